@@ -1,0 +1,420 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Each pin checks the oracle against a closed form, an invariant, brute force on a tiny
+input, a hand-derived special case or an independent library routine -- never against a
+retyped copy of its own formula.  The pins are plain functions raising AssertionError so
+that test_oracle_pins.py runs them and test_oracle_mutations.py checks that a planted
+mistake in the oracle makes at least one of them fail.
+
+Sources: "ScoutAttention: Efficient KV Cache Offloading via Layer-Ahead CPU Pre-computation
+for LLM Inference" (arXiv:2603.27138), HTML full text, cited as [HTML Sec. n]; Algorithm 1
+is the layer-ahead pre-computation listing of the paper (papercache.org summary, 三).
+"""
+
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+from oracle import scout_oracle as so
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert a.shape == b.shape and err <= tol, f"{what}: max abs err {err} > {tol}"
+
+
+# ---------------------------------------------------------------- storage rounding (R10)
+
+def pin_bf16_hand_cases():
+    """Round-to-nearest-even onto the bf16 grid, worked by hand (spacing 2^-7 on [1, 2))."""
+    cases = [
+        (1.0 + 2.0 ** -8, 1.0),                          # tie -> even significand
+        (1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -6),          # tie -> even (up)
+        (1.0 + 2.0 ** -8 + 2.0 ** -40, 1.0 + 2.0 ** -7),  # above the tie: ONE rounding
+        (-2.5, -2.5),
+        ((2 - 2.0 ** -7) * 2.0 ** 127, (2 - 2.0 ** -7) * 2.0 ** 127),  # largest finite
+        ((2 - 2.0 ** -8) * 2.0 ** 127, math.inf),        # tie above the largest -> inf
+        (2.0 ** -133, 2.0 ** -133),                      # smallest subnormal
+        (2.0 ** -134, 0.0),                              # tie to even (zero)
+        (3 * 2.0 ** -134, 2.0 ** -132),                  # tie to even (up)
+        (0.1, 0.10009765625),                            # 0.1 = 1.6 * 2^-4 -> 205/2048
+    ]
+    x = np.array([c[0] for c in cases])
+    want = np.array([c[1] for c in cases])
+    got = so.round_to_bf16(x)
+    assert np.array_equal(got, want), f"bf16 RNE: got {got}, want {want}"
+
+
+def pin_bf16_matches_library_on_float32():
+    """On float32 inputs a single RNE to bf16 is what torch's float32->bfloat16 cast does."""
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        rng.standard_normal(2000)]).astype(np.float32)
+    lib = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = so.round_to_bf16(x.astype(np.float64))
+    assert np.array_equal(got, lib), "bf16 RNE disagrees with torch's cast on float32 inputs"
+
+
+# ---------------------------------------------------------------- O1: Q_pred = W_Q X
+
+def pin_predict_query_hand():
+    """W_Q X for a column X is X W^T in row-major rows: a 2x3 by (2 features x 3) case
+    worked by hand, non-square so that a transposed operand cannot pass."""
+    X = np.array([[1.0, 2.0, 3.0], [4.0, 5.0, 6.0]])
+    W = np.array([[1.0, 1.0, 1.0], [1.0, 0.0, -1.0]])
+    want = np.array([[6.0, -2.0], [15.0, -2.0]])
+    assert np.array_equal(so.predict_query(X, W), want)
+    # a square case where W != W^T
+    X2 = np.array([[1.0, 0.0], [0.0, 1.0], [2.0, 3.0]])
+    W2 = np.array([[1.0, 2.0], [3.0, 4.0]])       # feature 0 = x0 + 2 x1; feature 1 = 3x0 + 4x1
+    want2 = np.array([[1.0, 3.0], [2.0, 4.0], [8.0, 18.0]])
+    assert np.array_equal(so.predict_query(X2, W2), want2)
+
+
+def pin_predict_query_one_hot():
+    """X = e_j picks input column j of W for every output feature."""
+    rng = np.random.default_rng(3)
+    W = rng.standard_normal((12, 7))
+    for j in range(7):
+        X = np.zeros((1, 7))
+        X[0, j] = 1.0
+        assert np.array_equal(so.predict_query(X, W)[0], W[:, j])
+
+
+# ---------------------------------------------------------------- O2/O3: blocks and digests
+
+def pin_blocks_hand():
+    assert so.num_blocks(1024, 16) == 64
+    assert so.num_blocks(33, 16) == 3
+    assert so.num_blocks(16, 16) == 1
+    assert so.num_blocks(1, 32) == 1
+    assert list(so.block_tokens(2, 33, 16)) == [32]
+    assert list(so.block_tokens(1, 33, 16)) == list(range(16, 32))
+
+
+def pin_digest_mean_closed_form():
+    """Keys that grow by one per token: the mean over [t0, t1) is (t0 + t1 - 1) / 2, also
+    for the partial last block (divided by its own token count, reading R9)."""
+    T, bs, d = 37, 8, 3
+    K = np.repeat(np.arange(T, dtype=np.float64)[:, None], d, axis=1)
+    K[:, 1] *= -2.0
+    K[:, 2] += 0.25
+    dig = so.digest_mean(K, T, bs, "f32")
+    for b in range(so.num_blocks(T, bs)):
+        t0, t1 = b * bs, min((b + 1) * bs, T)
+        mid = (t0 + t1 - 1) / 2.0
+        assert np.array_equal(dig[b], [mid, -2.0 * mid, mid + 0.25]), (b, dig[b])
+
+
+def pin_digest_mean_linearity():
+    """q . mean_b equals the mean over the block's tokens of q . K_t (before rounding);
+    dyadic values and a last block of 8 tokens keep every step exact."""
+    rng = np.random.default_rng(5)
+    T, bs, d = 40, 16, 8
+    K = rng.integers(-64, 64, size=(T, d)).astype(np.float64) / 16.0
+    q = rng.integers(-8, 8, size=d).astype(np.float64) / 4.0
+    dig = so.digest_mean(K, T, bs, "f32")
+    for b in range(so.num_blocks(T, bs)):
+        t = so.block_tokens(b, T, bs)
+        per_token = np.array([K[i] @ q for i in t])
+        assert abs(dig[b] @ q - per_token.mean()) < 1e-12
+
+
+def pin_digest_mean_single_rounding():
+    """A block whose float64 mean is exactly halfway between two bf16 values stores the
+    even one; one just above the tie stores the upper one."""
+    K = np.zeros((4, 2))
+    K[:, 0] = [1.0, 1.0, 1.0, 1.0 + 4 * 2.0 ** -8]          # mean 1 + 2^-8: tie -> 1.0
+    K[:, 1] = [1.0, 1.0, 1.0 + 2.0 ** -38, 1.0 + 4 * 2.0 ** -8]  # mean just above the tie
+    dig = so.digest_mean(K, 4, 4, "bf16")
+    assert dig[0, 0] == 1.0 and dig[0, 1] == 1.0 + 2.0 ** -7, dig
+
+
+def pin_digest_minmax_closed_form():
+    """K[t][c] = (t - c)^2 over block [t0, t1): max at an end, min 0 if c is inside."""
+    T, bs, d = 20, 8, 24
+    t = np.arange(T, dtype=np.float64)[:, None]
+    c = np.arange(d, dtype=np.float64)[None, :]
+    K = (t - c) ** 2
+    dig = so.digest_minmax(K, T, bs)
+    for b in range(so.num_blocks(T, bs)):
+        t0, t1 = b * bs, min((b + 1) * bs, T) - 1
+        for ch in range(d):
+            lo = 0.0 if t0 <= ch <= t1 else min((t0 - ch) ** 2, (t1 - ch) ** 2)
+            hi = max((t0 - ch) ** 2, (t1 - ch) ** 2)
+            assert dig[b, 0, ch] == lo and dig[b, 1, ch] == hi, (b, ch)
+
+
+# ---------------------------------------------------------------- O4: scores
+
+def pin_minmax_score_bounds_every_token():
+    """Quest's bound: for every block b, token t in b and query q,
+    q . K_t <= sum_c max(q_c min_bc, q_c max_bc); summed over a GQA group too."""
+    rng = np.random.default_rng(7)
+    T, bs, d, G = 203, 16, 32, 3
+    K = rng.standard_normal((T, d)) + rng.standard_normal((1, d))
+    qs = rng.standard_normal((G, d))
+    dig = so.digest_minmax(K, T, bs)
+    for g in range(G):
+        sig = so.score_minmax(qs[g:g + 1], dig)
+        for b in range(so.num_blocks(T, bs)):
+            for i in so.block_tokens(b, T, bs):
+                assert K[i] @ qs[g] <= sig[b] + 1e-12
+    sig_group = so.score_minmax(qs, dig)
+    for b in range(so.num_blocks(T, bs)):
+        for i in so.block_tokens(b, T, bs):
+            assert sum(K[i] @ qs[g] for g in range(G)) <= sig_group[b] + 1e-12
+
+
+def pin_scores_single_token_blocks():
+    """With one token per block both digests collapse onto the key, and both scores are
+    exactly the group's summed dot product with that key."""
+    rng = np.random.default_rng(8)
+    T, d, G = 9, 16, 4
+    K = rng.integers(-20, 20, size=(T, d)).astype(np.float64) / 4.0
+    qs = rng.integers(-20, 20, size=(G, d)).astype(np.float64) / 8.0
+    want = np.array([sum(K[t] @ qs[g] for g in range(G)) for t in range(T)])
+    assert np.array_equal(so.score_mean(qs, so.digest_mean(K, T, 1, "f32")), want)
+    assert np.array_equal(so.score_minmax(qs, so.digest_minmax(K, T, 1)), want)
+
+
+def pin_minmax_score_hand():
+    """Two channels, one block {(1, -2), (3, 4)}: min (1, -2), max (3, 4).
+    q = (1, -1): max(1, 3) + max(2, -4) = 5;  q = (-2, 0.5): max(-2, -6) + max(-1, 2) = 0."""
+    dig = so.digest_minmax(np.array([[1.0, -2.0], [3.0, 4.0]]), 2, 2)
+    assert so.score_minmax(np.array([[1.0, -1.0]]), dig)[0] == 5.0
+    assert so.score_minmax(np.array([[-2.0, 0.5]]), dig)[0] == 0.0
+    assert so.score_minmax(np.array([[1.0, -1.0], [-2.0, 0.5]]), dig)[0] == 5.0
+
+
+# ---------------------------------------------------------------- O5/O6: selection
+
+def _brute_topk(scores, k):
+    """Enumerate every k-subset; keep the largest total score; among equal totals the
+    lexicographically smallest sorted index tuple (lower index wins a tie)."""
+    n = len(scores)
+    best, best_key = None, None
+    for sub in itertools.combinations(range(n), min(k, n)):
+        key = (-sum(scores[i] for i in sub), sub)
+        if best_key is None or key < best_key:
+            best, best_key = sub, key
+    return np.array(best, dtype=np.int64)
+
+
+def pin_topk_brute_force():
+    """The selection equals brute force over all k-subsets on small inputs (integer scores,
+    so sums are exact and ties are frequent)."""
+    rng = np.random.default_rng(13)
+    for trial in range(300):
+        n = int(rng.integers(1, 13))
+        k = int(rng.integers(1, 6))
+        scores = rng.integers(-3, 4, size=n).astype(np.float64)
+        got = so.select_topk(scores, k)
+        want = _brute_topk(list(scores), k)
+        assert np.array_equal(got, want), (trial, scores, k, got, want)
+
+
+def pin_topk_special_cases():
+    s = np.array([0.5, 2.0, -1.0, 2.0, 3.0])
+    assert so.select_topk(s, 2).tolist() == [1, 4]          # tie at 2.0 -> lower index 1
+    assert so.select_topk(s, 10).tolist() == [0, 1, 2, 3, 4]  # k >= nb: all blocks
+    assert so.select_topk(np.zeros(6), 3).tolist() == [0, 1, 2]
+    assert so.select_topk(np.array([-0.0, 0.0, -0.0]), 1).tolist() == [0]
+
+
+def pin_split_hand():
+    sel = np.array([1, 4, 6, 9])
+    res = np.zeros(10, dtype=bool)
+    res[[0, 4, 9]] = True
+    g, c = so.split_resident(sel, res)
+    assert g.tolist() == [4, 9] and c.tolist() == [1, 6]
+
+
+# ---------------------------------------------------------------- O7/O8: attention, merge
+
+def pin_attention_closed_forms():
+    rng = np.random.default_rng(17)
+    d = 8
+    q = rng.standard_normal(d)
+    K1 = rng.standard_normal((1, d))
+    V1 = rng.standard_normal((1, d))
+    p = so.partial_attention(q, K1, V1, 0.5)        # one token: o = V, m = z, l = 1
+    assert np.array_equal(p.o, V1[0]) and p.l == 1.0 and abs(p.m - 0.5 * K1[0] @ q) < 1e-15
+    V = rng.standard_normal((5, d))                  # equal logits: o = mean V, l = T, m = 0
+    p = so.partial_attention(q, np.zeros((5, d)), V, 0.3)
+    _close(p.o, V.mean(axis=0), 1e-15, "equal logits")
+    assert p.m == 0.0 and p.l == 5.0
+    # two tokens with logits 0 and ln 3: weights 1/4, 3/4
+    q2 = np.array([1.0, 0.0])
+    K2 = np.array([[0.0, 0.0], [math.log(3.0), 0.0]])
+    V2 = np.array([[4.0, 0.0], [0.0, 8.0]])
+    p = so.partial_attention(q2, K2, V2, 1.0)
+    _close(p.o, [1.0, 6.0], 1e-14, "two tokens")
+    assert abs(p.m - math.log(3.0)) < 1e-15 and abs(p.l - 4.0 / 3.0) < 1e-14
+    e = so.partial_attention(q, np.zeros((0, d)), np.zeros((0, d)), 1.0)
+    assert e.m == -math.inf and e.l == 0.0 and not e.o.any()
+
+
+def pin_attention_matches_library():
+    """Dense attention equals torch's scaled_dot_product_attention in float64 (CPU)."""
+    rng = np.random.default_rng(19)
+    for T, d in ((1, 16), (37, 64), (300, 128)):
+        q = rng.standard_normal(d)
+        K = rng.standard_normal((T, d)) * 2.0
+        V = rng.standard_normal((T, d))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None, None, None, :], torch.from_numpy(K)[None, None],
+            torch.from_numpy(V)[None, None]).numpy()[0, 0, 0]
+        p = so.dense_attention(q, K, V, T, 1.0 / math.sqrt(d))
+        _close(p.o, ref, 1e-12, "dense vs SDPA")
+        z = K @ q / math.sqrt(d)
+        assert abs(p.lse - float(np.log(np.exp(z - z.max()).sum()) + z.max())) < 1e-12
+
+
+def pin_merge_union_invariant():
+    """Merging partials over disjoint token sets equals attention over their union
+    (online-softmax algebra the pages merge with); commutative, associative, and the
+    empty partial is the identity."""
+    rng = np.random.default_rng(23)
+    for trial in range(60):
+        T, d = int(rng.integers(2, 80)), int(rng.choice([4, 16, 64]))
+        q = rng.standard_normal(d) * 2.0
+        K = rng.standard_normal((T, d)) + rng.standard_normal((1, d)) * 3.0
+        V = rng.standard_normal((T, d))
+        cut = rng.permutation(T)
+        a, b, c = np.split(cut, sorted(rng.choice(np.arange(1, T), 2, replace=True)))
+        pa, pb, pc = (so.partial_attention(q, K[i], V[i], 0.7) for i in (a, b, c))
+        whole = so.partial_attention(q, K, V, 0.7)
+        for m in (so.merge(so.merge(pa, pb), pc), so.merge(pa, so.merge(pb, pc)),
+                  so.merge(pc, so.merge(pb, pa))):
+            _close(m.o, whole.o, 1e-12, "union o")
+            assert abs(m.lse - whole.lse) < 1e-12
+        e = so.empty_partial(d)
+        for m in (so.merge(pa, e), so.merge(e, pa)):
+            _close(m.o, pa.o, 0.0, "identity")
+            assert m.m == pa.m and m.l == pa.l
+    e = so.merge(so.empty_partial(4), so.empty_partial(4))
+    assert e.m == -math.inf and e.l == 0.0 and not e.o.any()
+
+
+# ---------------------------------------------------------------- O9: one layer, the step
+
+def _dense_ref_heads(qs, K, V, n, scale):
+    """Dense attention by the library routine for a group of query heads."""
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.asarray(qs))[None, :, None, :],
+        torch.from_numpy(K[:n])[None, None].expand(1, len(qs), n, K.shape[1]),
+        torch.from_numpy(V[:n])[None, None].expand(1, len(qs), n, V.shape[1]),
+        scale=scale).numpy()[0, :, 0]
+    return out
+
+
+def pin_full_budget_is_dense_attention():
+    """With k >= nb every block is selected, and GPU partial merged with the host partial
+    is plain softmax attention over the whole context, whatever is resident
+    (Transformer decode, [HTML Sec. 2.1]); both digest kinds, a ragged last block."""
+    rng = np.random.default_rng(29)
+    for kind in ("mean", "minmax"):
+        for T, bs, G in ((100, 16, 4), (64, 16, 1), (77, 32, 5)):
+            d = 32
+            offsets = 0.5 * rng.standard_normal((so.num_blocks(T, bs), d))
+            K = rng.standard_normal((T, d)) + np.repeat(offsets, bs, axis=0)[:T]
+            V = rng.standard_normal((T, d))
+            qs = rng.standard_normal((G, d))
+            nb = so.num_blocks(T, bs)
+            dig = so.digest_mean(K, T, bs, "f32") if kind == "mean" else so.digest_minmax(K, T, bs)
+            ref = _dense_ref_heads(qs, K, V, T, 1 / math.sqrt(d))
+            for res in (np.zeros(nb, bool), np.ones(nb, bool), rng.random(nb) < 0.5):
+                r = so.forward_pair(qs, qs, K, V, T, bs, dig, kind, nb + 3, res, 1 / math.sqrt(d))
+                assert r.selected.tolist() == list(range(nb))
+                for g in range(G):
+                    _close(r.out[g].o, ref[g], 1e-12, f"full budget {kind} T={T}")
+
+
+def pin_sparse_equals_attention_over_selection():
+    """With k < nb the merged output is attention over exactly the selected blocks' tokens
+    (GPU part over S and R, host part over S minus R): checked against the library routine
+    over the gathered tokens; unselected resident blocks must not contribute (R6)."""
+    rng = np.random.default_rng(31)
+    T, bs, d, G, k = 160, 16, 32, 2, 4
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    qs = rng.standard_normal((G, d))
+    dig = so.digest_mean(K, T, bs, "f32")
+    res = np.ones(so.num_blocks(T, bs), bool)       # everything resident, incl. fillers
+    r = so.forward_pair(qs, qs, K, V, T, bs, dig, "mean", k, res, 1 / math.sqrt(d))
+    idx = np.concatenate([np.arange(b * bs, (b + 1) * bs) for b in r.selected])
+    ref = _dense_ref_heads(qs, K[idx], V[idx], len(idx), 1 / math.sqrt(d))
+    for g in range(G):
+        _close(r.out[g].o, ref[g], 1e-12, "sparse = attention over selection")
+    assert len(r.cpu_blocks) == 0 and len(r.gpu_blocks) == k
+
+
+def pin_layer_ahead_selection_hand():
+    """Algorithm 1: layer 1 selects with Q_pred^1 = W_Q^1 X^0, not with its own Q^1, and
+    attends with Q^1; layer 0 selects with Q^0.  Hand case: hidden = d = 2, one head,
+    one token per block, W_Q^0 = W_Q^1 = I, X^0 = (1, 0), X^1 = (0, 1), k = 1."""
+    I = np.eye(2)
+    V = np.array([[5.0, 6.0], [7.0, 8.0]])
+    layers = [
+        dict(X=np.array([[1.0, 0.0]]), W=I, digest=np.array([[0.0, 1.0], [1.0, 0.0]]),
+             resident=np.array([True, True]), K=np.array([[0.0, 1.0], [1.0, 0.0]]), V=V,
+             seq_len=2, host=[so.empty_partial(2)]),
+        dict(X=np.array([[0.0, 1.0]]), W=I, digest=np.array([[1.0, 0.0], [0.0, 1.0]]),
+             resident=np.array([True, False]), K=np.array([[1.0, 0.0], [0.0, 1.0]]), V=V,
+             seq_len=2, host=[so.Partial(np.array([1.0, -1.0]), 3.0, 2.0)]),
+    ]
+    out = so.decode_step_pair(layers, 0, 0, 1, 2, 1, 1, 1.0)
+    # layer 0: Q^0 = (1, 0) scores blocks (0, 1) -> block 1 (key (1, 0)), resident
+    assert out[0].selected.tolist() == [1] and out[0].gpu_blocks.tolist() == [1]
+    # attention with Q^0 over the one token (1, 0): z = 1 -> o = V_1, m = 1, l = 1
+    assert np.array_equal(out[0].out[0].o, V[1]) and out[0].out[0].m == 1.0
+    # layer 1: Q_pred^1 = (1, 0) picks block 0 (its own Q^1 = (0, 1) would pick block 1)
+    assert out[1].selected.tolist() == [0] and out[1].gpu_blocks.tolist() == [0]
+    # attention with Q^1 = (0, 1) over key (1, 0): z = 0, o = V_0; nothing offloaded, so the
+    # host partial is not merged
+    assert np.array_equal(out[1].out[0].o, V[0]) and out[1].out[0].m == 0.0
+    assert out[1].out[0].l == 1.0
+    # make block 0 offloaded at layer 1: the output is the host partial alone
+    layers[1]["resident"] = np.array([False, True])
+    out = so.decode_step_pair(layers, 0, 0, 1, 2, 1, 1, 1.0)
+    assert out[1].cpu_blocks.tolist() == [0] and out[1].gpu_blocks.tolist() == []
+    assert np.array_equal(out[1].out[0].o, [1.0, -1.0]) and out[1].out[0].m == 3.0
+
+
+def pin_step_full_budget_is_dense():
+    """Every layer of the step with k >= nb and everything resident is dense attention
+    with the TRUE query Q^i = W_Q^i X^i (library routine), for any layer-ahead choice."""
+    rng = np.random.default_rng(37)
+    L, hidden, Hq, Hkv, d, T, bs = 3, 24, 4, 2, 8, 40, 8
+    G = Hq // Hkv
+    layers = []
+    for i in range(L):
+        layers.append(dict(
+            X=rng.standard_normal((2, hidden)), W=rng.standard_normal((Hq * d, hidden)) / 5,
+            K=rng.standard_normal((T, d)), V=rng.standard_normal((T, d)), seq_len=T,
+            resident=np.ones(so.num_blocks(T, bs), bool),
+            host=[so.empty_partial(d)] * G))
+        layers[-1]["digest"] = so.digest_mean(layers[-1]["K"], T, bs, "f32")
+    for s in range(2):
+        for h in range(Hkv):
+            out = so.decode_step_pair(layers, s, h, G, d, bs, 99, 1 / math.sqrt(d))
+            for i in range(L):
+                Q = layers[i]["X"][s] @ layers[i]["W"].T
+                qs = Q.reshape(Hq, d)[h * G:(h + 1) * G]
+                ref = _dense_ref_heads(qs, layers[i]["K"], layers[i]["V"], T, 1 / math.sqrt(d))
+                for g in range(G):
+                    _close(out[i].out[g].o, ref[g], 1e-12, f"step layer {i}")
+
+
+ALL_PINS = [v for k, v in dict(globals()).items() if k.startswith("pin_") and callable(v)]

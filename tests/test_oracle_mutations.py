@@ -1,0 +1,180 @@
+"""Planted mistakes in the oracle must each make at least one pin fail.
+
+Every mutation below is a plausible slip (a dropped term, a wrong sign or index, a
+transposed operand, a double rounding).  The mutation is planted in the oracle module on
+the CPU with monkeypatch; the pins are then run and at least one must raise.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle_pins
+from oracle import scout_oracle as so
+
+_orig = {name: getattr(so, name) for name in dir(so) if callable(getattr(so, name))}
+
+
+def _bf16_via_f32(x):
+    x = np.asarray(x, dtype=np.float64)
+    return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def _bf16_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    fin = np.isfinite(x) & (x != 0)
+    a = np.abs(x[fin])
+    _, e2 = np.frexp(a)
+    sp = np.ldexp(1.0, np.maximum(e2 - 1, -126) - 7)
+    out[fin] = np.copysign(np.floor(a / sp + 0.5) * sp, x[fin])
+    return out
+
+
+def _digest_mean_div_bs(K, seq_len, bs, kv_dtype):
+    K = np.asarray(K, dtype=np.float64)
+    nb = so.num_blocks(seq_len, bs)
+    out = np.array([K[b * bs:min((b + 1) * bs, seq_len)].sum(0) / bs for b in range(nb)])
+    return so.store_rounding(kv_dtype)(out)
+
+
+def _digest_mean_unrounded(K, seq_len, bs, kv_dtype):
+    K = np.asarray(K, dtype=np.float64)
+    nb = so.num_blocks(seq_len, bs)
+    return np.array([K[b * bs:min((b + 1) * bs, seq_len)].mean(0) for b in range(nb)])
+
+
+def _minmax_swapped(K, seq_len, bs):
+    return _orig["digest_minmax"](K, seq_len, bs)[:, ::-1, :]
+
+
+def _score_minmax_min(q_group, digest):
+    s = 0
+    for q in np.asarray(q_group):
+        s = s + np.minimum(q * digest[:, 0], q * digest[:, 1]).sum(1)
+    return s
+
+
+def _score_minmax_maxonly(q_group, digest):
+    return sum((digest[:, 1] @ q) for q in np.asarray(q_group))
+
+
+def _score_mean_first_head(q_group, digest):
+    return np.asarray(digest) @ np.asarray(q_group)[0]
+
+
+def _topk_ties_high(scores, k):
+    n = len(scores)
+    order = np.lexsort((-np.arange(n), -np.asarray(scores)))
+    return np.sort(order[:min(k, n)])
+
+
+def _topk_short(scores, k):
+    return _orig["select_topk"](scores, k)[:-1] if min(k, len(scores)) > 1 else \
+        _orig["select_topk"](scores, k)
+
+
+def _topk_ascending(scores, k):
+    n = len(scores)
+    order = np.lexsort((np.arange(n), np.asarray(scores)))
+    return np.sort(order[:min(k, n)])
+
+
+def _split_inverted(selected, resident):
+    g, c = _orig["split_resident"](selected, resident)
+    return c, g
+
+
+def _attn_no_scale(q, K, V, scale):
+    return _orig["partial_attention"](q, K, V, 1.0)
+
+
+def _attn_unnormalised(q, K, V, scale):
+    p = _orig["partial_attention"](q, K, V, scale)
+    return so.Partial(p.o * p.l, p.m, p.l)
+
+
+def _attn_min_shift(q, K, V, scale):
+    K = np.asarray(K, dtype=np.float64)
+    if K.shape[0] == 0:
+        return so.empty_partial(len(q))
+    z = (K @ np.asarray(q)) * scale
+    m = float(z.min())
+    p = np.exp(z - m)
+    return so.Partial((p @ np.asarray(V)) / p.sum(), m, float(p.sum()))
+
+
+def _merge_no_rescale(a, b):
+    if max(a.m, b.m) == -math.inf:
+        return so.empty_partial(a.o.shape[0])
+    l = a.l + b.l
+    return so.Partial((a.l * a.o + b.l * b.o) / l, max(a.m, b.m), l)
+
+
+def _merge_unnormalised(a, b):
+    r = _orig["merge"](a, b)
+    return so.Partial(r.o * r.l, r.m, r.l)
+
+
+def _qpred_transposed(X, W):
+    return np.asarray(X, dtype=np.float64) @ np.asarray(W, dtype=np.float64)
+
+
+def _block_tokens_shifted(b, seq_len, bs):
+    return range(b * bs + 1, min((b + 1) * bs + 1, seq_len))
+
+
+def _step_selects_with_own_query(layers, *a, **k):
+    return [_orig["decode_step_pair"]([L], *a, **k)[0] for L in layers]
+
+
+def _step_always_merges_host(layers, s, h, group, head_dim, *a, **k):
+    res = _orig["decode_step_pair"](layers, s, h, group, head_dim, *a, **k)
+    for i, r in enumerate(res):
+        r.out = [so.merge(r.gpu[j], layers[i]["host"][j]) for j in range(len(r.gpu))]
+    return res
+
+
+def _gqa_shifted(h, group):
+    return range(h * group + 1, (h + 1) * group + 1)
+
+
+MUTATIONS = {
+    "bf16 double rounding via f32": ("round_to_bf16", _bf16_via_f32),
+    "bf16 ties away from zero": ("round_to_bf16", _bf16_ties_away),
+    "Q_pred transposed operand": ("predict_query", _qpred_transposed),
+    "mean digest divides by bs": ("digest_mean", _digest_mean_div_bs),
+    "mean digest not rounded to the KV dtype": ("digest_mean", _digest_mean_unrounded),
+    "min/max rows swapped": ("digest_minmax", _minmax_swapped),
+    "min/max score takes the min": ("score_minmax", _score_minmax_min),
+    "min/max score uses max only": ("score_minmax", _score_minmax_maxonly),
+    "mean score drops the GQA sum": ("score_mean", _score_mean_first_head),
+    "top-k ties go to the higher index": ("select_topk", _topk_ties_high),
+    "top-k returns k-1 blocks": ("select_topk", _topk_short),
+    "top-k picks the smallest scores": ("select_topk", _topk_ascending),
+    "resident split inverted": ("split_resident", _split_inverted),
+    "attention without 1/sqrt(d)": ("partial_attention", _attn_no_scale),
+    "attention output not normalised": ("partial_attention", _attn_unnormalised),
+    "attention shifted by the min logit": ("partial_attention", _attn_min_shift),
+    "merge without exp rescale": ("merge", _merge_no_rescale),
+    "merge output not normalised": ("merge", _merge_unnormalised),
+    "block token range off by one": ("block_tokens", _block_tokens_shifted),
+    "layer selects with its own query": ("decode_step_pair", _step_selects_with_own_query),
+    "host partial merged when nothing offloaded": ("decode_step_pair", _step_always_merges_host),
+    "GQA group off by one head": ("gqa_group", _gqa_shifted),
+}
+
+
+@pytest.mark.parametrize("label", list(MUTATIONS))
+def test_planted_mistake_is_caught(label, monkeypatch):
+    name, fn = MUTATIONS[label]
+    monkeypatch.setattr(so, name, fn)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except Exception as e:  # noqa: BLE001 -- any failure of a pin counts
+            caught.append(f"{pin.__name__}: {type(e).__name__}")
+    assert caught, f"no pin caught the planted mistake: {label}"
