@@ -1,0 +1,264 @@
+"""ctypes binding of libscoutattn.so (C ABI in include/scoutattn.h).
+
+Argument marshalling only: every function takes torch tensors (device memory), checks
+their dtype / device / size against what the C call will read or write, and passes raw
+pointers and the current HIP stream.  All computation happens in the library's kernels.
+A failing call raises SaError with the library's message.  The library is loaded on first
+use; if it has not been built, that is an error (there is no fallback).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libscoutattn.so")
+
+SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = 0, -1, -2, -3, -4
+SA_F32, SA_BF16 = 0, 1
+SA_DIGEST_MEAN, SA_DIGEST_MINMAX = 0, 1
+ABI_VERSION = 1
+
+KIND = {"mean": SA_DIGEST_MEAN, "minmax": SA_DIGEST_MINMAX}
+
+
+class SaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{status}: {msg}")
+        self.status = status
+
+
+class sa_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+
+
+class sa_layer(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "x", "w_q", "digests", "block_table", "k_pool", "v_pool", "host_o", "host_m", "host_l",
+        "gpu_blocks", "n_gpu", "cpu_blocks", "n_cpu", "cpu_blocks_host", "n_cpu_host",
+        "out_o", "out_m", "out_l")]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+_Z = ctypes.c_size_t
+_D = ctypes.POINTER(sa_dims)
+
+SIGNATURES = {
+    "sa_abi_version": (ctypes.c_int, []),
+    "sa_last_error": (ctypes.c_char_p, []),
+    "sa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "sa_build_digests": (ctypes.c_int, [_D, ctypes.c_int, _P, _P, _P, _P, _P]),
+    "sa_predict_query_workspace_bytes": (_Z, [_I, _I, _I]),
+    "sa_predict_query": (ctypes.c_int, [_I, _I, _I, _P, _P, _P, _P, _Z, _P]),
+    "sa_workspace_bytes": (_Z, [_D, _I]),
+    "sa_select_blocks": (ctypes.c_int, [_D, ctypes.c_int, _P, _P, _P, _I, _P, _P, _P, _P, _P,
+                                        _P, _P, _Z, _P]),
+    "sa_sparse_decode": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _I, _F, _P, _P, _P,
+                                        _P, _Z, _P]),
+    "sa_merge": (ctypes.c_int, [_I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "sa_decode_attend_merge": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _I, _F, _P, _P,
+                                              _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "sa_step_workspace_bytes": (_Z, [_D, _I, _I]),
+    "sa_decode_step": (ctypes.c_int, [_D, ctypes.c_int, _I, _I, _F, _P, _I,
+                                      ctypes.POINTER(sa_layer), _P, _Z, _P, _P]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_attention_digest_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        if h.sa_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"libscoutattn ABI {h.sa_abi_version()} != {ABI_VERSION}")
+        _lib = h
+    return _lib
+
+
+def _check(status: int):
+    if status != SA_OK:
+        raise SaError(status, lib().sa_last_error().decode())
+
+
+def _ptr(t, dtype=None, numel=None, name="tensor", device=True):
+    """Device pointer of a contiguous tensor (None -> NULL), with marshalling checks."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name}: expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements < {numel} required")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream if hasattr(s, "cuda_stream") else int(s)
+
+
+@dataclass(frozen=True)
+class Dims:
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    max_blocks: int
+    num_pages: int
+    kv_dtype: int  # SA_F32 | SA_BF16
+
+    def c(self) -> sa_dims:
+        return sa_dims(self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim,
+                       self.block_size, self.max_blocks, self.num_pages, self.kv_dtype)
+
+    @property
+    def kv_torch(self):
+        return torch.bfloat16 if self.kv_dtype == SA_BF16 else torch.float32
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A device byte buffer of at least nbytes (at least 256 so it is never empty)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ---- calls (same names as the C ABI) -----------------------------------------------------
+
+def sa_abi_version() -> int:
+    return lib().sa_abi_version()
+
+
+def sa_workspace_bytes(dims: Dims, top_k: int) -> int:
+    return lib().sa_workspace_bytes(ctypes.byref(dims.c()), top_k)
+
+
+def sa_predict_query_workspace_bytes(m: int, n: int, k: int) -> int:
+    return lib().sa_predict_query_workspace_bytes(m, n, k)
+
+
+def sa_step_workspace_bytes(dims: Dims, hidden: int, top_k: int) -> int:
+    return lib().sa_step_workspace_bytes(ctypes.byref(dims.c()), hidden, top_k)
+
+
+def sa_build_digests(dims: Dims, kind: str, k_pool, block_table, seq_lens, digests,
+                     stream=None):
+    per = 2 if kind == "minmax" else 1
+    n_dig = dims.batch * dims.num_kv_heads * dims.max_blocks * per * dims.head_dim
+    _check(lib().sa_build_digests(
+        ctypes.byref(dims.c()), KIND[kind],
+        _ptr(k_pool, dims.kv_torch, dims.num_pages * dims.block_size * dims.head_dim, "k_pool"),
+        _ptr(block_table, torch.int32, dims.batch * dims.num_kv_heads * dims.max_blocks,
+             "block_table"),
+        _ptr(seq_lens, torch.int32, dims.batch, "seq_lens"),
+        _ptr(digests, dims.kv_torch, n_dig, "digests"), _stream(stream)))
+
+
+def sa_predict_query(x, w, q, ws=None, stream=None):
+    m, k = x.shape
+    n = w.shape[0]
+    if w.shape[1] != k or q.numel() != m * n:
+        raise ValueError("sa_predict_query: shapes x [m][k], w [n][k], q [m][n] expected")
+    _check(lib().sa_predict_query(
+        m, n, k, _ptr(x, torch.bfloat16, m * k, "x"), _ptr(w, torch.bfloat16, n * k, "w"),
+        _ptr(q, torch.float32, m * n, "q"), _ptr(ws, torch.uint8, name="ws"),
+        0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def sa_select_blocks(dims: Dims, kind: str, q, digests, seq_lens, top_k: int, block_table,
+                     gpu_blocks, n_gpu, cpu_blocks, n_cpu, scores=None, ws=None, stream=None):
+    pairs = dims.batch * dims.num_kv_heads
+    _check(lib().sa_select_blocks(
+        ctypes.byref(dims.c()), KIND[kind],
+        _ptr(q, torch.float32, dims.batch * dims.num_q_heads * dims.head_dim, "q"),
+        _ptr(digests, dims.kv_torch, name="digests"),
+        _ptr(seq_lens, torch.int32, dims.batch, "seq_lens"), top_k,
+        _ptr(block_table, torch.int32, pairs * dims.max_blocks, "block_table"),
+        _ptr(gpu_blocks, torch.int32, pairs * top_k, "gpu_blocks"),
+        _ptr(n_gpu, torch.int32, pairs, "n_gpu"),
+        _ptr(cpu_blocks, torch.int32, pairs * top_k, "cpu_blocks"),
+        _ptr(n_cpu, torch.int32, pairs, "n_cpu"),
+        _ptr(scores, torch.float32, pairs * dims.max_blocks, "scores"),
+        _ptr(ws, torch.uint8, name="ws"), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def sa_sparse_decode(dims: Dims, q, k_pool, v_pool, block_table, seq_lens, gpu_blocks, n_gpu,
+                     list_stride: int, scale: float, o, m=None, l=None, ws=None, stream=None):
+    rows = dims.batch * dims.num_q_heads
+    _check(lib().sa_sparse_decode(
+        ctypes.byref(dims.c()), _ptr(q, torch.float32, rows * dims.head_dim, "q"),
+        _ptr(k_pool, dims.kv_torch, name="k_pool"), _ptr(v_pool, dims.kv_torch, name="v_pool"),
+        _ptr(block_table, torch.int32, name="block_table"),
+        _ptr(seq_lens, torch.int32, dims.batch, "seq_lens"),
+        _ptr(gpu_blocks, torch.int32, name="gpu_blocks"), _ptr(n_gpu, torch.int32, name="n_gpu"),
+        list_stride, scale, _ptr(o, torch.float32, rows * dims.head_dim, "o"),
+        _ptr(m, torch.float32, rows, "m"), _ptr(l, torch.float32, rows, "l"),
+        _ptr(ws, torch.uint8, name="ws"), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def sa_decode_attend_merge(dims: Dims, q, k_pool, v_pool, block_table, seq_lens, gpu_blocks,
+                           n_gpu, list_stride: int, scale: float, host_o, host_m, host_l,
+                           n_cpu, o, m=None, l=None, ws=None, stream=None):
+    rows = dims.batch * dims.num_q_heads
+    _check(lib().sa_decode_attend_merge(
+        ctypes.byref(dims.c()), _ptr(q, torch.float32, rows * dims.head_dim, "q"),
+        _ptr(k_pool, dims.kv_torch, name="k_pool"), _ptr(v_pool, dims.kv_torch, name="v_pool"),
+        _ptr(block_table, torch.int32, name="block_table"),
+        _ptr(seq_lens, torch.int32, dims.batch, "seq_lens"),
+        _ptr(gpu_blocks, torch.int32, name="gpu_blocks"), _ptr(n_gpu, torch.int32, name="n_gpu"),
+        list_stride, scale, _ptr(host_o, torch.float32, rows * dims.head_dim, "host_o"),
+        _ptr(host_m, torch.float32, rows, "host_m"), _ptr(host_l, torch.float32, rows, "host_l"),
+        _ptr(n_cpu, torch.int32, name="n_cpu"),
+        _ptr(o, torch.float32, rows * dims.head_dim, "o"),
+        _ptr(m, torch.float32, rows, "m"), _ptr(l, torch.float32, rows, "l"),
+        _ptr(ws, torch.uint8, name="ws"), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def sa_merge(o_a, m_a, l_a, o_b, m_b, l_b, o, m, l, stream=None):
+    rows, d = o_a.shape[0], o_a.shape[-1]
+    rows = o_a.numel() // d
+    f = torch.float32
+    _check(lib().sa_merge(rows, d, _ptr(o_a, f, rows * d, "o_a"), _ptr(m_a, f, rows, "m_a"),
+                          _ptr(l_a, f, rows, "l_a"), _ptr(o_b, f, rows * d, "o_b"),
+                          _ptr(m_b, f, rows, "m_b"), _ptr(l_b, f, rows, "l_b"),
+                          _ptr(o, f, rows * d, "o"), _ptr(m, f, rows, "m"),
+                          _ptr(l, f, rows, "l"), _stream(stream)))
+
+
+def sa_decode_step(dims: Dims, kind: str, hidden: int, top_k: int, scale: float, seq_lens,
+                   layers: list, ws, stream=None, copy_stream=None):
+    """`layers` is a list of dicts with the sa_layer field names (tensors; the *_host ones
+    pinned CPU tensors or None)."""
+    arr = (sa_layer * len(layers))()
+    for i, L in enumerate(layers):
+        for name, _ in sa_layer._fields_:
+            t = L.get(name)
+            host = name.endswith("_host")
+            setattr(arr[i], name, _ptr(t, name=f"layers[{i}].{name}", device=not host))
+    _check(lib().sa_decode_step(
+        ctypes.byref(dims.c()), KIND[kind], hidden, top_k, scale,
+        _ptr(seq_lens, torch.int32, dims.batch, "seq_lens"), len(layers), arr,
+        _ptr(ws, torch.uint8, name="ws"), ws.numel(), _stream(stream),
+        None if copy_stream is None else _stream(copy_stream)))

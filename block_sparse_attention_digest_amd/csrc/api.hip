@@ -1,0 +1,446 @@
+// C ABI of libscoutattn: argument checks, workspace layout and kernel dispatch for the
+// GPU-side decode path of ScoutAttention [arXiv:2603.27138, HTML Sec. 3.2-3.3;
+// Algorithm 1].  Every argument is checked here, on the host, before anything is launched.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/scoutattn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+sa_status fail(sa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+sa_status ok() {
+  g_err.clear();
+  return SA_OK;
+}
+
+sa_status hip_fail(hipError_t e, const char* what) {
+  return fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxBlocks = 8192;  // LDS budget of the top-k workgroup
+
+sa_status check_dims(const sa_dims* d, sa::Shape* s) {
+  if (!d) return fail(SA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1 ||
+      d->block_size < 1 || d->max_blocks < 1 || d->num_pages < 1)
+    return fail(SA_ERR_INVALID_ARG,
+                "dims: batch, heads, head_dim, block_size, max_blocks, num_pages must be >= 1");
+  if (d->num_q_heads % d->num_kv_heads != 0)
+    return fail(SA_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                d->num_q_heads, d->num_kv_heads);
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (G > 8) return fail(SA_ERR_UNSUPPORTED, "query heads per KV head %d > 8", G);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(SA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", d->head_dim);
+  if (d->block_size != 16 && d->block_size != 32)
+    return fail(SA_ERR_UNSUPPORTED, "block_size %d not in {16, 32}", d->block_size);
+  if (d->max_blocks > kMaxBlocks)
+    return fail(SA_ERR_UNSUPPORTED, "max_blocks %d > %d", d->max_blocks, kMaxBlocks);
+  if (d->kv_dtype != SA_F32 && d->kv_dtype != SA_BF16)
+    return fail(SA_ERR_UNSUPPORTED, "kv_dtype %d is neither SA_F32 nor SA_BF16", (int)d->kv_dtype);
+  s->B = d->batch;
+  s->Hq = d->num_q_heads;
+  s->Hkv = d->num_kv_heads;
+  s->G = G;
+  s->d = d->head_dim;
+  s->bs = d->block_size;
+  s->max_blocks = d->max_blocks;
+  s->P = d->num_pages;
+  s->bf16 = d->kv_dtype == SA_BF16;
+  return SA_OK;
+}
+
+sa_status check_kind(sa_digest_kind k) {
+  if (k != SA_DIGEST_MEAN && k != SA_DIGEST_MINMAX)
+    return fail(SA_ERR_INVALID_ARG, "unknown digest kind %d", (int)k);
+  return SA_OK;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of selection + attention: scores, then chunk partials.
+struct Layout {
+  size_t scores, parts, total;
+  sa::AttnPlan plan;
+};
+Layout layout(const sa::Shape& s, int top_k) {
+  Layout L;
+  L.plan = sa::attn_plan(s, top_k);
+  L.scores = 0;
+  L.parts = align_up((size_t)s.B * s.Hkv * s.max_blocks * sizeof(float));
+  L.total = L.parts + align_up(L.plan.ws_bytes);
+  return L;
+}
+
+sa_status check_gemm_shape(int32_t m, int32_t n, int32_t k) {
+  if (m < 1 || n < 1 || k < 1) return fail(SA_ERR_INVALID_ARG, "GEMM sizes must be >= 1");
+  if (m > 256) return fail(SA_ERR_UNSUPPORTED, "GEMM m = %d > 256", m);
+  if (n % 64 != 0 || k % 64 != 0)
+    return fail(SA_ERR_UNSUPPORTED, "GEMM n (%d) and k (%d) must be multiples of 64", n, k);
+  return SA_OK;
+}
+
+#define SA_CHECK(expr)                \
+  do {                                \
+    sa_status st_ = (expr);           \
+    if (st_ != SA_OK) return st_;     \
+  } while (0)
+#define SA_NOT_NULL(p) \
+  do { if (!(p)) return fail(SA_ERR_INVALID_ARG, "%s is NULL", #p); } while (0)
+#define SA_HIP(expr, what)                       \
+  do {                                           \
+    hipError_t e_ = (expr);                      \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+sa_status check_scale(float scale) {
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(SA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  return SA_OK;
+}
+
+// selection of one layer: scores into ws (or `scores`), then top-k + split
+sa_status run_select(const sa::Shape& s, bool minmax, const float* q, const void* digests,
+                     const int32_t* seq_lens, int top_k, const int32_t* block_table,
+                     int32_t* gpu_blocks, int32_t* n_gpu, int32_t* cpu_blocks, int32_t* n_cpu,
+                     float* scores, hipStream_t stream) {
+  SA_HIP(sa::launch_score(s, minmax, q, digests, seq_lens, scores, stream), "score kernel");
+  SA_HIP(sa::launch_topk_split(s, scores, seq_lens, top_k, block_table, gpu_blocks, n_gpu,
+                               cpu_blocks, n_cpu, stream),
+         "top-k kernel");
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sa_abi_version(void) { return SA_ABI_VERSION; }
+
+const char* sa_last_error(void) { return g_err.c_str(); }
+
+const char* sa_status_string(sa_status status) {
+  switch (status) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_INVALID_ARG: return "SA_ERR_INVALID_ARG";
+    case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED";
+    case SA_ERR_WORKSPACE: return "SA_ERR_WORKSPACE";
+    case SA_ERR_HIP: return "SA_ERR_HIP";
+  }
+  return "unknown status";
+}
+
+sa_status sa_build_digests(const sa_dims* dims, sa_digest_kind kind, const void* k_pool,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           void* digests, hipStream_t stream) {
+  sa::Shape s;
+  SA_CHECK(check_dims(dims, &s));
+  SA_CHECK(check_kind(kind));
+  SA_NOT_NULL(k_pool);
+  SA_NOT_NULL(block_table);
+  SA_NOT_NULL(seq_lens);
+  SA_NOT_NULL(digests);
+  SA_HIP(sa::launch_build_digests(s, kind == SA_DIGEST_MINMAX, k_pool, block_table, seq_lens,
+                                  digests, stream),
+         "digest kernel");
+  return ok();
+}
+
+size_t sa_predict_query_workspace_bytes(int32_t m, int32_t n, int32_t k) {
+  if (check_gemm_shape(m, n, k) != SA_OK) return 0;
+  return sa::gemm_plan(m, n, k).ws_bytes;
+}
+
+sa_status sa_predict_query(int32_t m, int32_t n, int32_t k, const void* x, const void* w,
+                           float* q, void* ws, size_t ws_bytes, hipStream_t stream) {
+  SA_CHECK(check_gemm_shape(m, n, k));
+  SA_NOT_NULL(x);
+  SA_NOT_NULL(w);
+  SA_NOT_NULL(q);
+  const sa::GemmPlan plan = sa::gemm_plan(m, n, k);
+  if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes))
+    return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, plan.ws_bytes);
+  SA_HIP(sa::launch_gemm(m, n, k, x, 1, w, q, nullptr, nullptr, (float*)ws, plan, stream),
+         "GEMM kernel");
+  return ok();
+}
+
+size_t sa_workspace_bytes(const sa_dims* dims, int32_t top_k) {
+  sa::Shape s;
+  if (check_dims(dims, &s) != SA_OK) return 0;
+  if (top_k < 1 || top_k > s.max_blocks) {
+    fail(SA_ERR_INVALID_ARG, "top_k %d outside [1, max_blocks]", top_k);
+    return 0;
+  }
+  return layout(s, top_k).total;
+}
+
+sa_status sa_select_blocks(const sa_dims* dims, sa_digest_kind kind, const float* q,
+                           const void* digests, const int32_t* seq_lens, int32_t top_k,
+                           const int32_t* block_table, int32_t* gpu_blocks, int32_t* n_gpu,
+                           int32_t* cpu_blocks, int32_t* n_cpu, float* scores, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  sa::Shape s;
+  SA_CHECK(check_dims(dims, &s));
+  SA_CHECK(check_kind(kind));
+  SA_NOT_NULL(q);
+  SA_NOT_NULL(digests);
+  SA_NOT_NULL(seq_lens);
+  SA_NOT_NULL(block_table);
+  SA_NOT_NULL(gpu_blocks);
+  SA_NOT_NULL(n_gpu);
+  SA_NOT_NULL(cpu_blocks);
+  SA_NOT_NULL(n_cpu);
+  if (top_k < 1 || top_k > s.max_blocks)
+    return fail(SA_ERR_INVALID_ARG, "top_k %d outside [1, max_blocks = %d]", top_k, s.max_blocks);
+  const Layout L = layout(s, top_k);
+  if (!ws || ws_bytes < L.total)
+    return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, L.total);
+  float* sc = scores ? scores : (float*)((char*)ws + L.scores);
+  SA_CHECK(run_select(s, kind == SA_DIGEST_MINMAX, q, digests, seq_lens, top_k, block_table,
+                      gpu_blocks, n_gpu, cpu_blocks, n_cpu, sc, stream));
+  return ok();
+}
+
+static sa_status decode_common(const sa_dims* dims, const float* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* gpu_blocks,
+                               const int32_t* n_gpu, int32_t list_stride, float scale,
+                               const float* host_o, const float* host_m, const float* host_l,
+                               const int32_t* n_cpu, float* o, float* m, float* l, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  sa::Shape s;
+  SA_CHECK(check_dims(dims, &s));
+  SA_NOT_NULL(q);
+  SA_NOT_NULL(k_pool);
+  SA_NOT_NULL(v_pool);
+  SA_NOT_NULL(block_table);
+  SA_NOT_NULL(seq_lens);
+  SA_NOT_NULL(gpu_blocks);
+  SA_NOT_NULL(n_gpu);
+  SA_NOT_NULL(o);
+  SA_CHECK(check_scale(scale));
+  if (list_stride < 1 || list_stride > s.max_blocks)
+    return fail(SA_ERR_INVALID_ARG, "list_stride %d outside [1, max_blocks = %d]", list_stride,
+                s.max_blocks);
+  const Layout L = layout(s, list_stride);
+  if (!ws || ws_bytes < L.total)
+    return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, L.total);
+  float* parts = (float*)((char*)ws + L.parts);
+  SA_HIP(sa::launch_attention(s, L.plan, q, k_pool, v_pool, block_table, seq_lens, gpu_blocks,
+                              n_gpu, list_stride, scale, parts, stream),
+         "attention kernel");
+  SA_HIP(sa::launch_reduce(s, L.plan, n_gpu, parts, host_o, host_m, host_l, n_cpu, o, m, l,
+                           stream),
+         "reduce kernel");
+  return ok();
+}
+
+sa_status sa_sparse_decode(const sa_dims* dims, const float* q, const void* k_pool,
+                           const void* v_pool, const int32_t* block_table,
+                           const int32_t* seq_lens, const int32_t* gpu_blocks,
+                           const int32_t* n_gpu, int32_t list_stride, float scale, float* o,
+                           float* m, float* l, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_common(dims, q, k_pool, v_pool, block_table, seq_lens, gpu_blocks, n_gpu,
+                       list_stride, scale, nullptr, nullptr, nullptr, nullptr, o, m, l, ws,
+                       ws_bytes, stream);
+}
+
+sa_status sa_decode_attend_merge(const sa_dims* dims, const float* q, const void* k_pool,
+                                 const void* v_pool, const int32_t* block_table,
+                                 const int32_t* seq_lens, const int32_t* gpu_blocks,
+                                 const int32_t* n_gpu, int32_t list_stride, float scale,
+                                 const float* host_o, const float* host_m,
+                                 const float* host_l, const int32_t* n_cpu, float* o,
+                                 float* m, float* l, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  SA_NOT_NULL(host_o);
+  SA_NOT_NULL(host_m);
+  SA_NOT_NULL(host_l);
+  return decode_common(dims, q, k_pool, v_pool, block_table, seq_lens, gpu_blocks, n_gpu,
+                       list_stride, scale, host_o, host_m, host_l, n_cpu, o, m, l, ws,
+                       ws_bytes, stream);
+}
+
+sa_status sa_merge(int32_t rows, int32_t d, const float* o_a, const float* m_a,
+                   const float* l_a, const float* o_b, const float* m_b, const float* l_b,
+                   float* o, float* m, float* l, hipStream_t stream) {
+  if (rows < 1) return fail(SA_ERR_INVALID_ARG, "rows %d < 1", rows);
+  if (d < 1 || d > 1024) return fail(SA_ERR_INVALID_ARG, "d %d outside [1, 1024]", d);
+  SA_NOT_NULL(o_a);
+  SA_NOT_NULL(m_a);
+  SA_NOT_NULL(l_a);
+  SA_NOT_NULL(o_b);
+  SA_NOT_NULL(m_b);
+  SA_NOT_NULL(l_b);
+  SA_NOT_NULL(o);
+  SA_NOT_NULL(m);
+  SA_NOT_NULL(l);
+  SA_HIP(sa::launch_merge(rows, d, o_a, m_a, l_a, o_b, m_b, l_b, o, m, l, stream),
+         "merge kernel");
+  return ok();
+}
+
+// ---- the layer-ahead step -------------------------------------------------------------------
+
+namespace {
+struct StepLayout {
+  size_t q_true, q_pred, gemm, sel, total;
+  sa::GemmPlan plan_dual, plan_single;
+  Layout sel_layout;
+};
+StepLayout step_layout(const sa::Shape& s, int hidden, int top_k) {
+  StepLayout L;
+  const int n = s.Hq * s.d;
+  L.plan_dual = sa::gemm_plan(s.B, 2 * n, hidden);
+  L.plan_single = sa::gemm_plan(s.B, n, hidden);
+  const size_t qbytes = align_up((size_t)s.B * n * sizeof(float));
+  L.q_true = 0;
+  L.q_pred = qbytes;
+  L.gemm = 2 * qbytes;
+  const size_t gbytes = align_up(std::max(L.plan_dual.ws_bytes, L.plan_single.ws_bytes));
+  L.sel = L.gemm + gbytes;
+  L.sel_layout = layout(s, top_k);
+  L.total = L.sel + L.sel_layout.total;
+  return L;
+}
+}  // namespace
+
+size_t sa_step_workspace_bytes(const sa_dims* dims, int32_t hidden, int32_t top_k) {
+  sa::Shape s;
+  if (check_dims(dims, &s) != SA_OK) return 0;
+  if (check_gemm_shape(s.B, s.Hq * s.d, hidden) != SA_OK) return 0;
+  if (top_k < 1 || top_k > s.max_blocks) {
+    fail(SA_ERR_INVALID_ARG, "top_k %d outside [1, max_blocks]", top_k);
+    return 0;
+  }
+  return step_layout(s, hidden, top_k).total;
+}
+
+sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidden,
+                         int32_t top_k, float scale, const int32_t* seq_lens,
+                         int32_t num_layers, const sa_layer* layers, void* ws,
+                         size_t ws_bytes, hipStream_t stream, hipStream_t copy_stream) {
+  sa::Shape s;
+  SA_CHECK(check_dims(dims, &s));
+  SA_CHECK(check_kind(kind));
+  SA_CHECK(check_gemm_shape(s.B, s.Hq * s.d, hidden));
+  SA_CHECK(check_scale(scale));
+  SA_NOT_NULL(seq_lens);
+  SA_NOT_NULL(layers);
+  if (num_layers < 1) return fail(SA_ERR_INVALID_ARG, "num_layers %d < 1", num_layers);
+  if (top_k < 1 || top_k > s.max_blocks)
+    return fail(SA_ERR_INVALID_ARG, "top_k %d outside [1, max_blocks = %d]", top_k, s.max_blocks);
+  for (int i = 0; i < num_layers; ++i) {
+    const sa_layer& L = layers[i];
+    if (!L.x || !L.w_q || !L.digests || !L.block_table || !L.k_pool || !L.v_pool ||
+        !L.host_o || !L.host_m || !L.host_l || !L.gpu_blocks || !L.n_gpu || !L.cpu_blocks ||
+        !L.n_cpu || !L.out_o)
+      return fail(SA_ERR_INVALID_ARG, "layer %d: a required pointer is NULL", i);
+    if ((L.cpu_blocks_host == nullptr) != (L.n_cpu_host == nullptr))
+      return fail(SA_ERR_INVALID_ARG,
+                  "layer %d: cpu_blocks_host and n_cpu_host must both be set or both NULL", i);
+  }
+  const StepLayout SL = step_layout(s, hidden, top_k);
+  if (!ws || ws_bytes < SL.total)
+    return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, SL.total);
+
+  char* base = (char*)ws;
+  float* q_true = (float*)(base + SL.q_true);
+  float* q_pred = (float*)(base + SL.q_pred);
+  float* gemm_ws = (float*)(base + SL.gemm);
+  char* sel_base = base + SL.sel;
+  float* scores = (float*)(sel_base + SL.sel_layout.scores);
+  float* parts = (float*)(sel_base + SL.sel_layout.parts);
+  const bool minmax = kind == SA_DIGEST_MINMAX;
+  const int n = s.Hq * s.d;
+  const size_t list_bytes = (size_t)s.B * s.Hkv * top_k * sizeof(int32_t);
+  const size_t cnt_bytes = (size_t)s.B * s.Hkv * sizeof(int32_t);
+
+  std::vector<hipEvent_t> events;
+  auto cleanup = [&]() {
+    for (hipEvent_t e : events) (void)hipEventDestroy(e);
+  };
+  // hand-off of layer j's offloaded lists to the host (the "spawn" of the CPU attention)
+  auto handoff = [&](int j) -> sa_status {
+    const sa_layer& L = layers[j];
+    if (!copy_stream || !L.cpu_blocks_host) return SA_OK;
+    hipEvent_t ev;
+    SA_HIP(hipEventCreateWithFlags(&ev, hipEventDisableTiming), "hipEventCreate");
+    events.push_back(ev);
+    SA_HIP(hipEventRecord(ev, stream), "hipEventRecord");
+    SA_HIP(hipStreamWaitEvent(copy_stream, ev, 0), "hipStreamWaitEvent");
+    SA_HIP(hipMemcpyAsync(L.n_cpu_host, L.n_cpu, cnt_bytes, hipMemcpyDeviceToHost, copy_stream),
+           "hipMemcpyAsync n_cpu");
+    SA_HIP(hipMemcpyAsync(L.cpu_blocks_host, L.cpu_blocks, list_bytes, hipMemcpyDeviceToHost,
+                          copy_stream),
+           "hipMemcpyAsync cpu_blocks");
+    return SA_OK;
+  };
+
+  sa_status st = SA_OK;
+  for (int i = 0; i < num_layers && st == SA_OK; ++i) {
+    const sa_layer& L = layers[i];
+    const bool has_next = i + 1 < num_layers;
+    // 1. Q^i (and Q_pred^{i+1}) from X^i
+    hipError_t e = sa::launch_gemm(s.B, n, hidden, L.x, has_next ? 2 : 1, L.w_q, q_true,
+                                   has_next ? layers[i + 1].w_q : nullptr, q_pred, gemm_ws,
+                                   has_next ? SL.plan_dual : SL.plan_single, stream);
+    if (e != hipSuccess) { st = hip_fail(e, "GEMM kernel"); break; }
+    // 2. the first layer selects with its own query
+    if (i == 0) {
+      st = run_select(s, minmax, q_true, L.digests, seq_lens, top_k, L.block_table,
+                      L.gpu_blocks, L.n_gpu, L.cpu_blocks, L.n_cpu, scores, stream);
+      if (st == SA_OK) st = handoff(0);
+      if (st != SA_OK) break;
+    }
+    // 3. layer-ahead selection for layer i+1 and its hand-off
+    if (has_next) {
+      const sa_layer& N = layers[i + 1];
+      st = run_select(s, minmax, q_pred, N.digests, seq_lens, top_k, N.block_table,
+                      N.gpu_blocks, N.n_gpu, N.cpu_blocks, N.n_cpu, scores, stream);
+      if (st == SA_OK) st = handoff(i + 1);
+      if (st != SA_OK) break;
+    }
+    // 4. GPU attention of layer i, merged with its host partial
+    e = sa::launch_attention(s, SL.sel_layout.plan, q_true, L.k_pool, L.v_pool, L.block_table,
+                             seq_lens, L.gpu_blocks, L.n_gpu, top_k, scale, parts, stream);
+    if (e != hipSuccess) { st = hip_fail(e, "attention kernel"); break; }
+    e = sa::launch_reduce(s, SL.sel_layout.plan, L.n_gpu, parts, L.host_o, L.host_m, L.host_l,
+                          L.n_cpu, L.out_o, L.out_m, L.out_l, stream);
+    if (e != hipSuccess) { st = hip_fail(e, "reduce kernel"); break; }
+  }
+  // join the copy stream back into `stream`
+  if (!events.empty()) {
+    hipEvent_t done;
+    hipError_t e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+    if (e == hipSuccess) {
+      events.push_back(done);
+      e = hipEventRecord(done, copy_stream);
+      if (e == hipSuccess) e = hipStreamWaitEvent(stream, done, 0);
+    }
+    if (e != hipSuccess && st == SA_OK) st = hip_fail(e, "joining the copy stream");
+  }
+  cleanup();
+  return st == SA_OK ? ok() : st;
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Device helpers shared by the gfx950 kernels of libscoutattn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// ---- bfloat16 <-> float ------------------------------------------------------------------
+// A 32-bit word holds two bf16 values: element 0 in the low half, element 1 in the high half.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Eight bf16 values (one 16-byte vector) widened to float.
+__device__ __forceinline__ void bf16x8_to_f32(const uint4& v, float* f) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// double -> bf16 bits with ONE rounding, to nearest even, directly from the 53-bit
+// significand (going through float would round twice).  bf16 keeps 8 significant bits
+// and float's exponent range; below 2^-126 the spacing stays 2^-133.
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double x) {
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+  int exp = (int)((u >> 52) & 0x7ff);
+  uint64_t frac = u & ((1ull << 52) - 1);
+  if (exp == 0x7ff) return frac ? 0x7fc0u : (sign | 0x7f80u);   // NaN, +-inf
+  if (exp == 0) return sign;                                     // +-0 and f64 subnormals
+  int e = exp - 1023;                                           // unbiased exponent
+  uint64_t mant = frac | (1ull << 52);                          // 53-bit significand
+  if (e >= -126) {
+    uint32_t keep = (uint32_t)(mant >> 45);                      // 8 significant bits
+    uint64_t rem = mant & ((1ull << 45) - 1);
+    const uint64_t half = 1ull << 44;
+    if (rem > half || (rem == half && (keep & 1u))) keep += 1;
+    if (keep == 256u) { keep = 128u; e += 1; }
+    if (e > 127) return sign | 0x7f80u;                          // overflow to infinity
+    return sign | ((uint32_t)(e + 127) << 7) | (keep & 127u);
+  }
+  // subnormal range: value = n * 2^-133 with n = mant * 2^(e + 81)
+  int shift = -(e + 81);                                         // >= 46
+  if (shift > 60) return sign;                                   // < half of 2^-133
+  uint64_t n = mant >> shift;
+  uint64_t rem = mant & ((1ull << shift) - 1);
+  uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (n & 1ull))) n += 1;
+  return sign | (uint32_t)n;                                     // n == 128 is 2^-126
+}
+
+// ---- order-preserving keys -------------------------------------------------------------
+// Monotone map float -> uint32 (a < b  <=>  key(a) < key(b)); -0 and +0 map alike.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  f = f + 0.0f;  // -0 + 0 = +0 under round-to-nearest
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---- wavefront reductions ----------------------------------------------------------------
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {  // sum within aligned groups of W lanes
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace sa

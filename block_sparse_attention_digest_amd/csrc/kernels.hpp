@@ -1,0 +1,66 @@
+// Host-side launchers of the gfx950 kernels (one per kernel family), called by the C ABI
+// layer after it has validated every argument.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sa {
+
+// Validated problem shape, in plain ints.
+struct Shape {
+  int B, Hq, Hkv, G, d, bs, max_blocks, P;
+  bool bf16;  // KV dtype: bf16 (true) or float32 (false)
+};
+
+// ---- digests: one wave per block -----------------------------------------------------------
+hipError_t launch_build_digests(const Shape& s, bool minmax, const void* k_pool,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                void* digests, hipStream_t stream);
+
+// ---- skinny GEMM q[m][n] = x[m][k] . w[n][k]^T, for up to two weight matrices sharing x ---
+struct GemmPlan {
+  int ksplit;        // K slices, each a separate workgroup column
+  int kslice;        // columns of K per slice (multiple of 64)
+  size_t ws_bytes;   // float partials [ksplit][m][n_total] when ksplit > 1
+};
+GemmPlan gemm_plan(int m, int n_total, int k);
+hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void* w0,
+                       float* q0, const void* w1, float* q1, float* ws, const GemmPlan& plan,
+                       hipStream_t stream);
+
+// ---- selection: scores of every block, then top-k and the resident split per pair -------
+hipError_t launch_score(const Shape& s, bool minmax, const float* q, const void* digests,
+                        const int32_t* seq_lens, float* scores, hipStream_t stream);
+hipError_t launch_topk_split(const Shape& s, const float* scores, const int32_t* seq_lens,
+                             int top_k, const int32_t* block_table, int32_t* gpu_blocks,
+                             int32_t* n_gpu, int32_t* cpu_blocks, int32_t* n_cpu,
+                             hipStream_t stream);
+
+// ---- attention: chunk partials per (pair, chunk), then the reduction / merge per row -----
+struct AttnPlan {
+  int chunk_tokens;  // tokens of selected blocks handled by one workgroup
+  int chunk_blocks;  // = chunk_tokens / bs
+  int nchunks;       // ceil(list_stride / chunk_blocks)
+  size_t ws_bytes;   // partials: [B*Hkv][nchunks][G] x (d + 2) floats
+};
+AttnPlan attn_plan(const Shape& s, int list_stride);
+hipError_t launch_attention(const Shape& s, const AttnPlan& plan, const float* q,
+                            const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* gpu_blocks, const int32_t* n_gpu, int list_stride,
+                            float scale, float* partials, hipStream_t stream);
+// Combine the chunk partials of every (sequence, query head) row, optionally merged with a
+// host partial (gated by n_cpu when given); writes normalised o and natural-unit m, l.
+hipError_t launch_reduce(const Shape& s, const AttnPlan& plan, const int32_t* n_gpu,
+                         const float* partials, const float* host_o, const float* host_m,
+                         const float* host_l, const int32_t* n_cpu, float* o, float* m,
+                         float* l, hipStream_t stream);
+
+// ---- merge of two normalised partials ------------------------------------------------------
+hipError_t launch_merge(int rows, int d, const float* o_a, const float* m_a, const float* l_a,
+                        const float* o_b, const float* m_b, const float* l_b, float* o,
+                        float* m, float* l, hipStream_t stream);
+
+}  // namespace sa

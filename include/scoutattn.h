@@ -1,0 +1,235 @@
+/*
+ * scoutattn.h -- C ABI of libscoutattn.so, the MI355X (gfx950) GPU-side decode path of
+ * ScoutAttention's GPU-CPU collaborative block-sparse attention.
+ *
+ * Source of every operation (cited by page title and section):
+ *   "ScoutAttention: Efficient KV Cache Offloading via Layer-Ahead CPU Pre-computation for
+ *   LLM Inference", arXiv:2603.27138 -- HTML full text ("[HTML Sec. n]"), and the
+ *   papercache.org summary of the same paper, section 三, Algorithm 1 ("[Alg. 1]").
+ *
+ * Conventions shared by every call
+ *   - Pointers named *_host are host memory; every other pointer is device memory owned by
+ *     the caller.  The library keeps no pointer after a call returns and allocates no
+ *     device memory: scratch space comes from the caller's workspace (`ws`, `ws_bytes`),
+ *     whose required size the *_workspace_bytes() queries return.
+ *   - Work is enqueued on the caller's `stream` and the call returns without waiting.
+ *     Results are valid once the stream has reached that point.  Calls on different
+ *     streams may run concurrently if they share no output or workspace.
+ *   - Arguments are checked on the host before anything is launched: a failed check
+ *     returns SA_ERR_INVALID_ARG / SA_ERR_UNSUPPORTED / SA_ERR_WORKSPACE and enqueues
+ *     nothing.  A launch failure returns SA_ERR_HIP.  sa_last_error() then describes the
+ *     failure (thread-local, valid until the next call on the same thread).  No C++
+ *     exception crosses this interface.
+ *   - Contents of device buffers (block-table entries, list entries, sequence lengths) are
+ *     NOT checked on the host: they must satisfy the ranges stated below, otherwise the
+ *     kernels read out of bounds.
+ *   - Layouts are row-major, innermost index last.  "KV dtype" is sa_dims.kv_dtype:
+ *     SA_F32 (float) or SA_BF16 (bfloat16 bit patterns, uint16).
+ *
+ * Shapes: B sequences; Hq query heads; Hkv KV heads with G = Hq / Hkv query heads per KV
+ * head (query head g uses KV head g / G); head dimension d; block size bs; P pages in the
+ * paged K/V pool, one page holding bs tokens of one KV head: k_pool, v_pool [P][bs][d].
+ * block_table [B][Hkv][max_blocks] int32 maps block b of (sequence s, KV head h) to its
+ * page, or holds -1 when that block is not resident in GPU memory.  Block b of sequence s
+ * covers tokens [b*bs, min((b+1)*bs, seq_lens[s])); nb_s = ceil(seq_lens[s] / bs).
+ */
+#ifndef SCOUTATTN_H
+#define SCOUTATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_ABI_VERSION 1
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_INVALID_ARG = -1,  /* null pointer, inconsistent or out-of-range argument   */
+  SA_ERR_UNSUPPORTED = -2,  /* valid but not implemented: d, bs, dtype, G, GEMM shape */
+  SA_ERR_WORKSPACE = -3,    /* ws_bytes smaller than the matching *_workspace_bytes() */
+  SA_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed             */
+} sa_status;
+
+typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+
+/* Block digests [HTML Sec. 2.2]: MoBA-style mean pooling of K, or Quest-style channel-wise
+ * min/max pooling of K. */
+typedef enum { SA_DIGEST_MEAN = 0, SA_DIGEST_MINMAX = 1 } sa_digest_kind;
+
+/* Problem shape.  Supported: head_dim in {64, 128}; block_size in {16, 32};
+ * num_q_heads % num_kv_heads == 0 with G = num_q_heads / num_kv_heads in [1, 8];
+ * 1 <= max_blocks <= 16384; num_pages >= 1; kv_dtype SA_F32 or SA_BF16. */
+typedef struct {
+  int32_t batch;         /* B                                                     */
+  int32_t num_q_heads;   /* Hq                                                    */
+  int32_t num_kv_heads;  /* Hkv                                                   */
+  int32_t head_dim;      /* d                                                     */
+  int32_t block_size;    /* bs, tokens per block and per page                    */
+  int32_t max_blocks;    /* row length of block_table and of the digest arrays    */
+  int32_t num_pages;     /* P, pages in k_pool / v_pool; table entries are < P    */
+  sa_dtype kv_dtype;     /* dtype of k_pool, v_pool and the digests               */
+} sa_dims;
+
+/* ABI version of the loaded library (SA_ABI_VERSION when it matches this header). */
+int sa_abi_version(void);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char* sa_last_error(void);
+
+/* Name of a status code. */
+const char* sa_status_string(sa_status status);
+
+/* ---------------------------------------------------------------------------------------
+ * sa_build_digests -- digest of every resident block [HTML Sec. 2.2].
+ *   kind == SA_DIGEST_MEAN:   digests [B][Hkv][max_blocks][d]; entry b = mean of K over the
+ *       block's valid tokens, accumulated exactly (float64) and rounded once,
+ *       round-to-nearest-even, to the KV dtype.
+ *   kind == SA_DIGEST_MINMAX: digests [B][Hkv][max_blocks][2][d]; [..][0][c] = minimum and
+ *       [..][1][c] = maximum of K channel c over the block's valid tokens (exact).
+ *   k_pool [P][bs][d] (KV dtype); block_table [B][Hkv][max_blocks] (entries -1 or in
+ *   [0, P)); seq_lens [B] (1 <= seq_lens[s] <= max_blocks*bs).  Entries of blocks that are
+ *   not resident (table -1) or lie past the sequence end are left unchanged.
+ * ------------------------------------------------------------------------------------- */
+sa_status sa_build_digests(const sa_dims* dims, sa_digest_kind kind, const void* k_pool,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           void* digests, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * sa_predict_query -- the layer-ahead query prediction Q_pred^{i+1} = W_Q^{i+1} X^i
+ * ([Alg. 1]; [HTML Sec. 3.3]); the same call with W_Q^i gives the true query Q^i.
+ *   x [m][k] bf16 (one row per sequence), w [n][k] bf16 (row j = output feature j, the
+ *   linear-layer layout), q [m][n] float32 = x w^T (bf16 products, float32 accumulation, not
+ *   rounded further).  Supported: 1 <= m <= 256, n % 64 == 0, k % 64 == 0, n, k >= 64.
+ *   For attention, q is viewed as [m][Hq][d] (head j / d).
+ *   ws: sa_predict_query_workspace_bytes(m, n, k) bytes (may be 0 -> ws may be NULL).
+ * ------------------------------------------------------------------------------------- */
+size_t sa_predict_query_workspace_bytes(int32_t m, int32_t n, int32_t k);
+sa_status sa_predict_query(int32_t m, int32_t n, int32_t k, const void* x, const void* w,
+                           float* q, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Workspace of sa_select_blocks + sa_sparse_decode (+ sa_decode_attend_merge) for a shape
+ * and a top_k (a decode call uses list_stride == top_k).
+ * ------------------------------------------------------------------------------------- */
+size_t sa_workspace_bytes(const sa_dims* dims, int32_t top_k);
+
+/* ---------------------------------------------------------------------------------------
+ * sa_select_blocks -- B_pred = TopK(Q K_digest^T), B_cpu = B_pred \ B_gpu  ([Alg. 1];
+ * [HTML Sec. 3.2]), once per (sequence s, KV head h):
+ *   score sigma_b for every block b < nb_s, summed over the G query heads of the group:
+ *     mean:   sigma_b = sum_g q_g . digest_b
+ *     minmax: sigma_b = sum_g sum_c max(q_gc * min_bc, q_gc * max_bc)   (Quest's bound)
+ *   select the k_s = min(top_k, nb_s) largest scores (equal scores: lower block index
+ *   first), then split them by residency (block_table[s][h][b] >= 0).
+ *   q [B][Hq][d] float32; digests as written by sa_build_digests; seq_lens [B] in
+ *   [1, max_blocks*bs]; 1 <= top_k <= max_blocks.
+ *   Outputs: gpu_blocks, cpu_blocks [B][Hkv][top_k] int32 -- the resident / offloaded
+ *   selected block indices, ascending, padded with -1; n_gpu, n_cpu [B][Hkv] int32 (their
+ *   counts, n_gpu + n_cpu = k_s).  scores [B][Hkv][max_blocks] float32 may be NULL; when
+ *   given it receives sigma_b for b < nb_s.
+ * ------------------------------------------------------------------------------------- */
+sa_status sa_select_blocks(const sa_dims* dims, sa_digest_kind kind, const float* q,
+                           const void* digests, const int32_t* seq_lens, int32_t top_k,
+                           const int32_t* block_table, int32_t* gpu_blocks, int32_t* n_gpu,
+                           int32_t* cpu_blocks, int32_t* n_cpu, float* scores, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * sa_sparse_decode -- A_gpu = GPUATTN(Q, B_gpu) ([Alg. 1]; [HTML Sec. 3.2]): for every
+ * query head g of sequence s, softmax attention over the valid tokens of the blocks listed
+ * in gpu_blocks[s][g/G][0 .. n_gpu[s][g/G]) (each block read through block_table):
+ *   z_t = scale * q_g . K_t,  m = max z,  l = sum exp(z - m),  o = sum exp(z - m) V_t / l.
+ *   An empty list gives o = 0, m = -inf, l = 0.
+ *   q [B][Hq][d] float32; k_pool, v_pool [P][bs][d]; gpu_blocks [B][Hkv][list_stride] with
+ *   entries in [0, nb_s) whose table entry is a page in [0, P); 0 <= n_gpu <= list_stride.
+ *   Outputs o [B][Hq][d], m [B][Hq], l [B][Hq] float32 (m in natural-log units).
+ *   ws: sa_workspace_bytes(dims, list_stride).
+ * ------------------------------------------------------------------------------------- */
+sa_status sa_sparse_decode(const sa_dims* dims, const float* q, const void* k_pool,
+                           const void* v_pool, const int32_t* block_table,
+                           const int32_t* seq_lens, const int32_t* gpu_blocks,
+                           const int32_t* n_gpu, int32_t list_stride, float scale, float* o,
+                           float* m, float* l, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * sa_merge -- A = MERGE(A_a, A_b), the FlashAttention combination of two partials over
+ * disjoint token sets ([Alg. 1]; [HTML Sec. 3.2]), per row r < rows:
+ *   M = max(m_a, m_b); w_x = l_x exp(m_x - M) (0 if m_x = -inf); l = w_a + w_b;
+ *   o = (w_a o_a + w_b o_b) / l; m = M.  Two empty partials give (0, -inf, 0).
+ *   o_* [rows][d], m_*, l_* [rows] float32, o normalised.  The outputs may alias a.
+ *   Supported: rows >= 1, 1 <= d <= 1024.
+ * ------------------------------------------------------------------------------------- */
+sa_status sa_merge(int32_t rows, int32_t d, const float* o_a, const float* m_a,
+                   const float* l_a, const float* o_b, const float* m_b, const float* l_b,
+                   float* o, float* m, float* l, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * sa_decode_attend_merge -- GPUATTN followed by MERGE with the host partial in one
+ * enqueue ([Alg. 1], the attention and merge steps of layer i): the result equals
+ * sa_sparse_decode followed by sa_merge with (host_o, host_m, host_l) [B][Hq][d], [B][Hq],
+ * except that when n_cpu is not NULL the host partial of every head of (s, h) with
+ * n_cpu[s][h] == 0 is treated as empty (nothing was offloaded, so nothing came back).
+ * Arguments as for sa_sparse_decode; ws: sa_workspace_bytes(dims, list_stride).
+ * ------------------------------------------------------------------------------------- */
+sa_status sa_decode_attend_merge(const sa_dims* dims, const float* q, const void* k_pool,
+                                 const void* v_pool, const int32_t* block_table,
+                                 const int32_t* seq_lens, const int32_t* gpu_blocks,
+                                 const int32_t* n_gpu, int32_t list_stride, float scale,
+                                 const float* host_o, const float* host_m,
+                                 const float* host_l, const int32_t* n_cpu, float* o,
+                                 float* m, float* l, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * sa_decode_step -- one decode step over num_layers layers in the layer-ahead order of
+ * Algorithm 1 ([Alg. 1]; [HTML Sec. 3.3]).  For layer i:
+ *   1. Q^i = W_Q^i X^i and, for i < L-1, Q_pred^{i+1} = W_Q^{i+1} X^i (one GEMM launch);
+ *   2. (layer 0 only) select B^0 with Q^0 -- the first layer has no predecessor;
+ *   3. for i < L-1: select B_pred^{i+1} with Q_pred^{i+1} and layer i+1's digests and block
+ *      table, writing layer i+1's lists; then, when copy_stream is not NULL and the host
+ *      pointers are set, copy n_cpu and cpu_blocks of layer i+1 to the host on copy_stream
+ *      (the hand-off that spawns the CPU-side attention);
+ *   4. A_gpu^i over B_gpu^i with Q^i, merged with layer i's host partial (ignored for heads
+ *      whose n_cpu is 0) into out_o/out_m/out_l.
+ * All layers share dims, digest kind, hidden, top_k, scale and seq_lens.  `layers` is a host
+ * array of num_layers descriptors (read during the call only).  Before returning, `stream`
+ * waits for every copy issued on copy_stream, so a graph captured from `stream` is
+ * closed.  ws: sa_step_workspace_bytes(dims, hidden, top_k).
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+  const void* x;            /* X^i [B][hidden] bf16                                       */
+  const void* w_q;          /* W_Q^i [Hq*d][hidden] bf16                                  */
+  const void* digests;      /* layer digests, sa_build_digests layout for the kind        */
+  const int32_t* block_table; /* [B][Hkv][max_blocks]                                     */
+  const void* k_pool;       /* [P][bs][d] KV dtype (bf16)                                 */
+  const void* v_pool;       /* [P][bs][d]                                                 */
+  const float* host_o;      /* A_cpu^i: [B][Hq][d], normalised                            */
+  const float* host_m;      /* [B][Hq], natural-log units                                 */
+  const float* host_l;      /* [B][Hq]                                                    */
+  int32_t* gpu_blocks;      /* out: B_gpu^i list [B][Hkv][top_k]                          */
+  int32_t* n_gpu;           /* out: [B][Hkv]                                              */
+  int32_t* cpu_blocks;      /* out: B_cpu^i list [B][Hkv][top_k]                          */
+  int32_t* n_cpu;           /* out: [B][Hkv]                                              */
+  int32_t* cpu_blocks_host; /* optional pinned host copy of cpu_blocks (or NULL)          */
+  int32_t* n_cpu_host;      /* optional pinned host copy of n_cpu (or NULL)               */
+  float* out_o;             /* out: A^i [B][Hq][d]                                        */
+  float* out_m;             /* out: [B][Hq] (may be NULL)                                 */
+  float* out_l;             /* out: [B][Hq] (may be NULL)                                 */
+} sa_layer;
+
+size_t sa_step_workspace_bytes(const sa_dims* dims, int32_t hidden, int32_t top_k);
+sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidden,
+                         int32_t top_k, float scale, const int32_t* seq_lens,
+                         int32_t num_layers, const sa_layer* layers, void* ws,
+                         size_t ws_bytes, hipStream_t stream, hipStream_t copy_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SCOUTATTN_H */

@@ -141,6 +141,15 @@ def block_tokens(b: int, seq_len: int, block_size: int) -> range:
 # O3: digests  [HTML Sec. 2.2: MoBA mean pooling; Quest channel-wise min/max pooling]
 # ----------------------------------------------------------------------------------------
 
+def _block_view(K: np.ndarray, seq_len: int, block_size: int):
+    """The full blocks of K as [nb_full][bs][d], and the valid rows of a partial last block
+    (or None)."""
+    nfull = int(seq_len) // int(block_size)
+    full = K[:nfull * block_size].reshape(nfull, block_size, K.shape[1])
+    tail = K[nfull * block_size:seq_len] if seq_len % block_size else None
+    return full, tail
+
+
 def digest_mean(K: np.ndarray, seq_len: int, block_size: int, kv_dtype: str) -> np.ndarray:
     """Mean-pooled digest of every block of one (sequence, KV head).
 
@@ -149,12 +158,11 @@ def digest_mean(K: np.ndarray, seq_len: int, block_size: int, kv_dtype: str) -> 
     Returns [nb][d] (float64 holding stored values).
     """
     K = np.asarray(K, dtype=np.float64)
-    nb = num_blocks(seq_len, block_size)
-    out = np.empty((nb, K.shape[1]), dtype=np.float64)
-    for b in range(nb):
-        t = block_tokens(b, seq_len, block_size)
-        out[b] = K[t.start:t.stop].sum(axis=0) / len(t)
-    return store_rounding(kv_dtype)(out)
+    full, tail = _block_view(K, seq_len, block_size)
+    rows = [full.sum(axis=1) / block_size]
+    if tail is not None:
+        rows.append(tail.sum(axis=0, keepdims=True) / tail.shape[0])
+    return store_rounding(kv_dtype)(np.concatenate(rows, axis=0))
 
 
 def digest_minmax(K: np.ndarray, seq_len: int, block_size: int) -> np.ndarray:
@@ -164,13 +172,12 @@ def digest_minmax(K: np.ndarray, seq_len: int, block_size: int) -> np.ndarray:
     [b][1] the maximum.  Both are exact (they are stored key values).
     """
     K = np.asarray(K, dtype=np.float64)
-    nb = num_blocks(seq_len, block_size)
-    out = np.empty((nb, 2, K.shape[1]), dtype=np.float64)
-    for b in range(nb):
-        t = block_tokens(b, seq_len, block_size)
-        out[b, 0] = K[t.start:t.stop].min(axis=0)
-        out[b, 1] = K[t.start:t.stop].max(axis=0)
-    return out
+    full, tail = _block_view(K, seq_len, block_size)
+    lo, hi = [full.min(axis=1)], [full.max(axis=1)]
+    if tail is not None:
+        lo.append(tail.min(axis=0, keepdims=True))
+        hi.append(tail.max(axis=0, keepdims=True))
+    return np.stack([np.concatenate(lo, axis=0), np.concatenate(hi, axis=0)], axis=1)
 
 
 # ----------------------------------------------------------------------------------------
@@ -292,9 +299,12 @@ def merge(a: Partial, b: Partial) -> Partial:
 
 def gather_tokens(X: np.ndarray, blocks, seq_len: int, block_size: int) -> np.ndarray:
     """Rows of the logical sequence X [T][d] that belong to the given blocks' valid tokens."""
-    idx = [t for b in blocks for t in block_tokens(int(b), seq_len, block_size)]
-    return np.asarray(X, dtype=np.float64)[np.asarray(idx, dtype=np.int64)] if idx else \
-        np.zeros((0, np.asarray(X).shape[1]), dtype=np.float64)
+    X = np.asarray(X, dtype=np.float64)
+    parts = [np.arange(t.start, t.stop) for t in
+             (block_tokens(int(b), seq_len, block_size) for b in blocks)]
+    if not parts:
+        return np.zeros((0, X.shape[1]), dtype=np.float64)
+    return X[np.concatenate(parts)]
 
 
 def attend_blocks(q, K, V, blocks, seq_len: int, block_size: int, scale: float) -> Partial:
@@ -332,16 +342,16 @@ def select_pair(q_sel_group, digest, kind: str, top_k: int, resident):
     return sigma, sel, g_blocks, c_blocks
 
 
-def forward_pair(q_sel_group, q_att_group, K, V, seq_len: int, block_size: int, digest,
-                 kind: str, top_k: int, resident, scale: float, host=None) -> PairResult:
-    """Select with q_sel, attend with q_att, merge with the host partials.
+def attend_selection(q_att_group, K, V, seq_len: int, block_size: int, sigma, selected,
+                     resident, scale: float, host=None) -> PairResult:
+    """Split a selection by residency, attend the resident part with q_att, and merge.
 
     `host` is None to compute the host partials here as the attention of q_att over the
     offloaded selected blocks (what the CPU side computes), or a list of one Partial per
-    query head of the group to merge as given.  K/V need to hold valid rows only for the
-    blocks that are attended.
+    query head of the group to merge as given.  K/V need valid rows only for the blocks
+    that are attended.
     """
-    sigma, sel, g_blocks, c_blocks = select_pair(q_sel_group, digest, kind, top_k, resident)
+    g_blocks, c_blocks = split_resident(selected, resident)
     gpu, hst, out = [], [], []
     for j in range(len(q_att_group)):
         pg = attend_blocks(q_att_group[j], K, V, g_blocks, seq_len, block_size, scale)
@@ -352,7 +362,16 @@ def forward_pair(q_sel_group, q_att_group, K, V, seq_len: int, block_size: int, 
         gpu.append(pg)
         hst.append(ph)
         out.append(merge(pg, ph))
-    return PairResult(sigma, sel, g_blocks, c_blocks, gpu, hst, out)
+    return PairResult(sigma, np.asarray(selected), g_blocks, c_blocks, gpu, hst, out)
+
+
+def forward_pair(q_sel_group, q_att_group, K, V, seq_len: int, block_size: int, digest,
+                 kind: str, top_k: int, resident, scale: float, host=None) -> PairResult:
+    """One layer for one (sequence, KV head): select with q_sel, attend with q_att, merge
+    with the host partials (see attend_selection)."""
+    sigma, sel, _, _ = select_pair(q_sel_group, digest, kind, top_k, resident)
+    return attend_selection(q_att_group, K, V, seq_len, block_size, sigma, sel, resident,
+                            scale, host)
 
 
 # ----------------------------------------------------------------------------------------

@@ -1,0 +1,158 @@
+"""Parity harness for the layer-ahead decode step (Algorithm 1) over several layers.
+
+Inputs come from the generators; the resident pool of every layer is the top
+`pool_blocks` blocks under the true query Q^i = W_Q^i X^i on the drawn digests, chosen by
+the ORACLE (the stand-in for "important blocks found in earlier steps").  Pool-block
+digests are then recomputed from the pool keys on both sides.  The HIP step runs through
+sa_decode_step; the oracle runs decode_step_pair for the checked pairs.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import harness as H
+from block_sparse_attention_digest_amd import binding as B
+from block_sparse_attention_digest_amd import workloads as wk
+from oracle import scout_oracle as so
+
+
+def oracle_pool_sets(wl, X64, W64, dig64, kind="mean"):
+    """Top pool_blocks blocks per (seq, KV head) under the true query of one layer."""
+    Q = so.query_heads(so.predict_query(X64, W64), wl.num_q_heads, wl.head_dim)
+    G = wl.group
+    sets = []
+    for s in range(wl.batch):
+        row = []
+        for h in range(wl.num_kv_heads):
+            sig = so.score_blocks(Q[s, h * G:(h + 1) * G], dig64[s, h], kind)
+            row.append(so.select_topk(sig, wl.pool_blocks))
+        sets.append(row)
+    return sets
+
+
+def prepare_step(wl, gen_device, kind="mean"):
+    """Generate every layer and choose the pools with the oracle.  Returns (layers, oracle
+    layer dicts builder data)."""
+    dev = "cuda"
+    ins = wk.draw_layer_inputs(wl, gen_device)
+    layers = []
+    for i in range(wl.layers):
+        off = wk.layer_offsets(wl, i, gen_device)
+        dig = wk.draw_layer_digests(wl, i, off, gen_device)
+        if kind == "minmax":
+            # stand-in min/max digests around the drawn centre: centre -+ |N(0, 1)| spread
+            spread = torch.randn(dig.shape, generator=wk.generator(wl, f"spread{i}", gen_device),
+                                 device=gen_device).abs().to(dig.dtype)
+            dig = torch.stack([(dig.float() - spread.float()).to(dig.dtype),
+                               (dig.float() + spread.float()).to(dig.dtype)], dim=3)
+        X64, W64 = wk.f64(ins[i]["X"]), wk.f64(ins[i]["W"])
+        sets = oracle_pool_sets(wl, X64, W64, wk.f64(dig), kind)
+        pool = wk.draw_layer_pool(wl, i, off, sets)
+        hp = wk.draw_host_partials(wl, i, gen_device)
+        layers.append(dict(X=ins[i]["X"], W=ins[i]["W"], dig=dig, pool=pool, host=hp, sets=sets))
+    return layers
+
+
+def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs_to_check=None):
+    dev = "cuda"
+    B_, Hkv, Hq, G, d, bs, k = (wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.group,
+                                wl.head_dim, wl.block_size, wl.top_k)
+    L = wl.layers
+    data = prepare_step(wl, gen_device, kind)
+    lens = wk.seq_lens(wl)
+    lens_d = lens.to(dev)
+    P = data[0]["pool"]["K"].shape[0]
+    dims = H.dims_for(wl, P)
+    pairs = B_ * Hkv
+    i32, f32 = torch.int32, torch.float32
+
+    # ---------------- HIP path: pool digests rebuilt from the pool keys, then the step
+    dev_layers = []
+    pinned = []
+    for i, Ld in enumerate(data):
+        dig = Ld["dig"].to(dev).contiguous()
+        B.sa_build_digests(dims, kind, Ld["pool"]["K"].to(dev), Ld["pool"]["block_table"].to(dev),
+                           lens_d, dig)
+        e = dict(x=Ld["X"].to(dev), w_q=Ld["W"].to(dev), digests=dig,
+                 block_table=Ld["pool"]["block_table"].to(dev), k_pool=Ld["pool"]["K"].to(dev),
+                 v_pool=Ld["pool"]["V"].to(dev), host_o=Ld["host"]["o"].to(dev).contiguous(),
+                 host_m=Ld["host"]["m"].to(dev).contiguous(),
+                 host_l=Ld["host"]["l"].to(dev).contiguous(),
+                 gpu_blocks=torch.full((pairs, k), -7, dtype=i32, device=dev),
+                 n_gpu=torch.full((pairs,), -7, dtype=i32, device=dev),
+                 cpu_blocks=torch.full((pairs, k), -7, dtype=i32, device=dev),
+                 n_cpu=torch.full((pairs,), -7, dtype=i32, device=dev),
+                 out_o=torch.empty((B_, Hq, d), dtype=f32, device=dev),
+                 out_m=torch.empty((B_, Hq), dtype=f32, device=dev),
+                 out_l=torch.empty((B_, Hq), dtype=f32, device=dev))
+        if handoff:
+            e["cpu_blocks_host"] = torch.zeros((pairs, k), dtype=i32).pin_memory()
+            e["n_cpu_host"] = torch.zeros((pairs,), dtype=i32).pin_memory()
+        dev_layers.append(e)
+    ws = B.workspace(B.sa_step_workspace_bytes(dims, wl.hidden, k))
+    copy_stream = torch.cuda.Stream() if handoff else None
+    B.sa_decode_step(dims, kind, wl.hidden, k, wl.scale, lens_d, dev_layers, ws,
+                     copy_stream=copy_stream)
+    torch.cuda.synchronize()
+    H.log("  HIP step done")
+
+    # ---------------- oracle
+    check = range(pairs) if pairs_to_check is None else pairs_to_check
+    ties = 0
+    max_err = 0.0
+    for p in check:
+        s, h = divmod(p, Hkv)
+        n = int(lens[s])
+        nb = so.num_blocks(n, bs)
+        olayers = []
+        for i, Ld in enumerate(data):
+            bt = Ld["pool"]["block_table"][s, h].cpu()
+            resident = (bt[:nb] >= 0).numpy()
+            Kl = np.zeros((nb * bs, d))
+            Vl = np.zeros((nb * bs, d))
+            Kp, Vp = Ld["pool"]["K"], Ld["pool"]["V"]
+            for b in np.nonzero(resident)[0]:
+                Kl[b * bs:(b + 1) * bs] = wk.f64(Kp[int(bt[b])])
+                Vl[b * bs:(b + 1) * bs] = wk.f64(Vp[int(bt[b])])
+            dig = wk.f64(Ld["dig"][s, h, :nb])
+            res_blocks = np.nonzero(resident)[0]
+            if kind == "mean":
+                full = so.digest_mean(Kl, n, bs, wl.kv_dtype)
+            else:
+                full = so.digest_minmax(Kl, n, bs)
+            dig[res_blocks] = full[res_blocks]
+            host = [so.Partial(wk.f64(Ld["host"]["o"][s, h * G + j]),
+                               float(Ld["host"]["m"][s, h * G + j]),
+                               float(Ld["host"]["l"][s, h * G + j])) for j in range(G)]
+            olayers.append(dict(X=wk.f64(Ld["X"]), W=wk.f64(Ld["W"]), digest=dig,
+                                resident=resident, K=Kl, V=Vl, seq_len=n, host=host))
+        want = so.decode_step_pair(olayers, s, h, G, d, bs, k, wl.scale, kind)
+        for i in range(L):
+            e = dev_layers[i]
+            ng, nc = int(e["n_gpu"][p]), int(e["n_cpu"][p])
+            gbl = e["gpu_blocks"][p].cpu().numpy()
+            cbl = e["cpu_blocks"][p].cpu().numpy()
+            assert np.all(gbl[ng:] == -1) and np.all(cbl[nc:] == -1)
+            if handoff:
+                assert int(e["n_cpu_host"][p]) == nc
+                assert np.array_equal(e["cpu_blocks_host"][p].numpy(), cbl)
+            sel = np.sort(np.concatenate([gbl[:ng], cbl[:nc]]))
+            same = H.selection_matches(sel, want[i].selected, want[i].scores, min(k, nb))
+            if not same:
+                ties += 1
+                continue
+            assert np.array_equal(gbl[:ng], want[i].gpu_blocks)
+            o = e["out_o"][s, h * G:(h + 1) * G].cpu().double().numpy()
+            m = e["out_m"][s, h * G:(h + 1) * G].cpu().double().numpy()
+            l = e["out_l"][s, h * G:(h + 1) * G].cpu().double().numpy()
+            for j in range(G):
+                max_err = max(max_err, H.compare_partial(o[j], m[j], l[j], want[i].out[j],
+                                                         H.attn_tol(wl), f"layer {i} pair {p}"))
+    n_checked = len(list(check)) * L
+    assert ties <= max(1, n_checked // 100), f"too many tie-differing selections: {ties}"
+    cpu_ratio = np.mean([float(e["n_cpu"].sum()) * bs / (pairs * k * bs) for e in dev_layers])
+    H.log(f"  step {wl.name}: checked={n_checked} ties={ties} max_err={max_err:.2e} "
+          f"cpu_ratio={cpu_ratio:.3f}")
+    return dict(max_err=max_err, ties=ties, cpu_ratio=cpu_ratio)

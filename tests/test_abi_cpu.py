@@ -1,0 +1,167 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header declares,
+and rejects bad arguments on the host before launching anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from block_sparse_attention_digest_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "scoutattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from block_sparse_attention_digest_amd import build
+        build.build()
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_path(lib):
+    names = declared_functions()
+    for n in ("sa_build_digests", "sa_predict_query", "sa_select_blocks", "sa_sparse_decode",
+              "sa_merge", "sa_decode_attend_merge", "sa_decode_step"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(declared_functions()) <= set(B.SIGNATURES)
+
+
+def test_abi_version(lib):
+    assert lib.sa_abi_version() == B.ABI_VERSION == 1
+    assert lib.sa_status_string(B.SA_ERR_WORKSPACE) == b"SA_ERR_WORKSPACE"
+
+
+# The calls below must all fail validation; on a machine with a GPU they are skipped so
+# that a validation bug can never launch a kernel on dummy pointers.
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="host-only checks (no GPU)")
+FAKE = 0x1000
+
+
+def dims(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=32,
+                max_blocks=64, num_pages=128, kv_dtype=B.SA_BF16)
+    base.update(kw)
+    return B.sa_dims(**base)
+
+
+def select(lib, d, top_k=8, ws_bytes=1 << 30, q=FAKE, kind=0):
+    return lib.sa_select_blocks(ctypes.byref(d), kind, q, FAKE, FAKE, top_k, FAKE, FAKE, FAKE,
+                                FAKE, FAKE, None, FAKE, ws_bytes, None)
+
+
+@no_gpu
+def test_dims_validation(lib):
+    assert select(lib, dims(head_dim=96)) == B.SA_ERR_UNSUPPORTED
+    assert b"head_dim" in lib.sa_last_error()
+    assert select(lib, dims(block_size=8)) == B.SA_ERR_UNSUPPORTED
+    assert select(lib, dims(num_q_heads=7)) == B.SA_ERR_INVALID_ARG
+    assert select(lib, dims(num_q_heads=18, num_kv_heads=2)) == B.SA_ERR_UNSUPPORTED  # G = 9
+    assert select(lib, dims(kv_dtype=7)) == B.SA_ERR_UNSUPPORTED
+    assert select(lib, dims(batch=0)) == B.SA_ERR_INVALID_ARG
+    assert select(lib, dims(max_blocks=9000)) == B.SA_ERR_UNSUPPORTED
+    assert lib.sa_select_blocks(None, 0, FAKE, FAKE, FAKE, 8, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                None, FAKE, 1 << 30, None) == B.SA_ERR_INVALID_ARG
+
+
+@no_gpu
+def test_select_validation(lib):
+    d = dims()
+    assert select(lib, d, q=None) == B.SA_ERR_INVALID_ARG
+    assert b"q is NULL" in lib.sa_last_error()
+    assert select(lib, d, top_k=0) == B.SA_ERR_INVALID_ARG
+    assert select(lib, d, top_k=65) == B.SA_ERR_INVALID_ARG
+    assert select(lib, d, kind=5) == B.SA_ERR_INVALID_ARG
+    need = lib.sa_workspace_bytes(ctypes.byref(d), 8)
+    assert need > 0
+    assert select(lib, d, ws_bytes=need - 1) == B.SA_ERR_WORKSPACE
+    assert lib.sa_workspace_bytes(ctypes.byref(dims(head_dim=96)), 8) == 0
+
+
+@no_gpu
+def test_decode_and_merge_validation(lib):
+    d = dims()
+    ws = lib.sa_workspace_bytes(ctypes.byref(d), 8)
+    args = [ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 0.088, FAKE, FAKE,
+            FAKE, FAKE, ws, None]
+    bad_scale = list(args)
+    bad_scale[9] = float("nan")
+    assert lib.sa_sparse_decode(*bad_scale) == B.SA_ERR_INVALID_ARG
+    bad_scale[9] = 0.0
+    assert lib.sa_sparse_decode(*bad_scale) == B.SA_ERR_INVALID_ARG
+    bad = list(args)
+    bad[8] = 65
+    assert lib.sa_sparse_decode(*bad) == B.SA_ERR_INVALID_ARG
+    bad = list(args)
+    bad[14] = ws - 1
+    assert lib.sa_sparse_decode(*bad) == B.SA_ERR_WORKSPACE
+    bad = list(args)
+    bad[10] = None  # o
+    assert lib.sa_sparse_decode(*bad) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_decode_attend_merge(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      8, 0.088, None, FAKE, FAKE, None, FAKE, None, None, FAKE,
+                                      ws, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_merge(0, 128, *([FAKE] * 9), None) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_merge(4, 2000, *([FAKE] * 9), None) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_merge(4, 128, FAKE, None, *([FAKE] * 7), None) == B.SA_ERR_INVALID_ARG
+
+
+@no_gpu
+def test_gemm_validation(lib):
+    assert lib.sa_predict_query(0, 64, 64, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_predict_query(300, 64, 64, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == B.SA_ERR_UNSUPPORTED
+    assert lib.sa_predict_query(8, 100, 64, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == B.SA_ERR_UNSUPPORTED
+    assert lib.sa_predict_query(8, 64, 96, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == B.SA_ERR_UNSUPPORTED
+    assert lib.sa_predict_query(8, 64, 64, None, FAKE, FAKE, FAKE, 1 << 30, None) == B.SA_ERR_INVALID_ARG
+    need = lib.sa_predict_query_workspace_bytes(40, 5120, 5120)
+    assert need > 0
+    assert lib.sa_predict_query(40, 5120, 5120, FAKE, FAKE, FAKE, FAKE, need - 1,
+                                None) == B.SA_ERR_WORKSPACE
+    assert lib.sa_predict_query_workspace_bytes(40, 100, 5120) == 0
+
+
+@no_gpu
+def test_step_validation(lib):
+    d = dims()
+    ws = lib.sa_step_workspace_bytes(ctypes.byref(d), 1024, 8)
+    assert ws > 0
+    layers = (B.sa_layer * 2)()
+    for L in layers:
+        for name, _ in B.sa_layer._fields_:
+            setattr(L, name, FAKE)
+    layers[1].out_o = None
+    assert lib.sa_decode_step(ctypes.byref(d), 0, 1024, 8, 0.088, FAKE, 2, layers, FAKE, ws,
+                              None, None) == B.SA_ERR_INVALID_ARG
+    assert b"layer 1" in lib.sa_last_error()
+    layers[1].out_o = FAKE
+    layers[0].n_cpu_host = None
+    assert lib.sa_decode_step(ctypes.byref(d), 0, 1024, 8, 0.088, FAKE, 2, layers, FAKE, ws,
+                              None, None) == B.SA_ERR_INVALID_ARG
+    layers[0].n_cpu_host = FAKE
+    assert lib.sa_decode_step(ctypes.byref(d), 0, 1000, 8, 0.088, FAKE, 2, layers, FAKE, ws,
+                              None, None) == B.SA_ERR_UNSUPPORTED
+    assert lib.sa_decode_step(ctypes.byref(d), 0, 1024, 8, 0.088, FAKE, 0, layers, FAKE, ws,
+                              None, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_decode_step(ctypes.byref(d), 0, 1024, 8, 0.088, FAKE, 2, layers, FAKE,
+                              ws - 1, None, None) == B.SA_ERR_WORKSPACE
+
+
+def test_binding_requires_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()

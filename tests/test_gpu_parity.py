@@ -1,0 +1,145 @@
+"""HIP path against the CPU oracle, element by element, through the C ABI.
+
+Small and scaled workloads (several tiles, ragged tails) plus edge cases.  The full-size
+workloads live in test_gpu_fullsize.py.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import harness as H
+from block_sparse_attention_digest_amd import binding as B
+from block_sparse_attention_digest_amd import workloads as wk
+from oracle import scout_oracle as so
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+TINY = wk.TINY
+CFG2_S = wk.QWEN3_8B_LAYER.scaled(batch=2, context=4096 - 19)
+CFG3_S = wk.QWEN3_14B_LAYER.scaled(batch=2, context=8192 + 5)
+CFG5_S = wk.RAGGED.scaled(batch=4, ctx_min=1, ctx_max=5000, top_k=64)
+
+LAYER_CASES = [
+    ("cfg1-tiny-fp32", TINY, "mean", {}),
+    ("cfg1-tiny-minmax", TINY, "minmax", {}),
+    ("cfg1-full-budget", TINY, "mean", dict(top_k=64)),
+    ("cfg1-all-offloaded", TINY, "mean", dict(resident_override="none")),
+    ("cfg1-all-resident-k1", TINY, "mean", dict(resident_override="all", top_k=1)),
+    ("cfg2-scaled", CFG2_S, "mean", {}),
+    ("cfg3-scaled-minmax", CFG3_S, "minmax", {}),
+    ("cfg5-scaled-mean", CFG5_S, "mean", {}),
+    ("cfg5-scaled-minmax", CFG5_S, "minmax", {}),
+    ("bf16-g1-d64-bs16", wk.RAGGED.scaled(batch=2, num_q_heads=2, num_kv_heads=2, head_dim=64,
+                                          ctx_min=300, ctx_max=900, top_k=12), "mean", {}),
+    ("bf16-g8-d128-bs32", wk.QWEN3_14B_LAYER.scaled(batch=2, num_q_heads=16, num_kv_heads=2,
+                                                    context=2000, top_k=20,
+                                                    resident_frac=(0.5, 0.5)), "minmax", {}),
+    ("bf16-g3-d64-bs32-full", wk.QWEN3_14B_LAYER.scaled(batch=2, num_q_heads=6, num_kv_heads=2,
+                                                        head_dim=64, context=700, top_k=22),
+     "mean", dict(resident_override="all")),
+    ("f32-d128-bs32", wk.TINY.scaled(num_q_heads=10, num_kv_heads=2, head_dim=128,
+                                     block_size=32, context=1000, top_k=6), "minmax", {}),
+    ("bf16-short-seqs", wk.RAGGED.scaled(batch=5, ctx_min=1, ctx_max=40, top_k=3), "mean", {}),
+]
+
+
+@pytest.mark.parametrize("name,wl,kind,kw", LAYER_CASES, ids=[c[0] for c in LAYER_CASES])
+def test_layer_parity(name, wl, kind, kw):
+    H.log(f"[case] {name}")
+    H.run_layer(wl, kind, gen_device="cpu", **kw)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 64), (8, 4096, 4096), (40, 5120, 5120),
+                                   (65, 256, 320), (256, 128, 1024)])
+def test_predict_query_parity(m, n, k):
+    H.log(f"[case] gemm {m}x{n}x{k}")
+    g = torch.Generator().manual_seed(m * 7 + n + k)
+    X = torch.randn(m, k, generator=g).to(torch.bfloat16)
+    W = (torch.randn(n, k, generator=g) / math.sqrt(k)).to(torch.bfloat16)
+    want = so.predict_query(wk.f64(X), wk.f64(W))
+    q = torch.empty(m, n, dtype=torch.float32, device="cuda")
+    ws = B.workspace(B.sa_predict_query_workspace_bytes(m, n, k))
+    B.sa_predict_query(X.cuda(), W.cuda(), q, ws)
+    err = float(np.max(np.abs(q.cpu().double().numpy() - want)))
+    assert err <= H.TOL_GEMM, err
+
+
+def test_merge_parity_and_aliasing():
+    H.log("[case] merge")
+    rows, d = 37, 128
+    g = torch.Generator().manual_seed(5)
+    o_a = torch.randn(rows, d, generator=g)
+    o_b = torch.randn(rows, d, generator=g)
+    m_a = torch.randn(rows, generator=g) * 3
+    m_b = torch.randn(rows, generator=g) * 3
+    l_a = torch.rand(rows, generator=g) * 50 + 1
+    l_b = torch.rand(rows, generator=g) * 50 + 1
+    # empty partials on either side, and on both
+    for r, side in ((0, "a"), (1, "b"), (2, "ab")):
+        if "a" in side:
+            o_a[r], m_a[r], l_a[r] = 0, -math.inf, 0
+        if "b" in side:
+            o_b[r], m_b[r], l_b[r] = 0, -math.inf, 0
+    want = [so.merge(so.Partial(wk.f64(o_a[r]), float(m_a[r]), float(l_a[r])),
+                     so.Partial(wk.f64(o_b[r]), float(m_b[r]), float(l_b[r])))
+            for r in range(rows)]
+    dev = [t.cuda() for t in (o_a, m_a, l_a, o_b, m_b, l_b)]
+    out = [torch.empty_like(dev[0]), torch.empty_like(dev[1]), torch.empty_like(dev[2])]
+    B.sa_merge(*dev, *out)
+    B.sa_merge(*dev, dev[0], dev[1], dev[2])  # outputs aliasing input a
+    torch.cuda.synchronize()
+    for o, m, l in (out, dev[:3]):
+        o, m, l = o.cpu().double().numpy(), m.cpu().double().numpy(), l.cpu().double().numpy()
+        for r in range(rows):
+            H.compare_partial(o[r], m[r], l[r], want[r], 1e-5, f"merge row {r}")
+
+
+def test_selection_ties_go_to_lower_index():
+    """q = 0 makes every score 0 (+0 or -0): the lowest-indexed blocks are selected."""
+    H.log("[case] ties")
+    wl = wk.QWEN3_8B_LAYER.scaled(batch=2, context=1000, top_k=5)
+    dims = H.dims_for(wl, 4)
+    lens = torch.full((2,), 1000, dtype=torch.int32, device="cuda")
+    q = torch.zeros(2, wl.num_q_heads, wl.head_dim, device="cuda")
+    q[1, :, ::2] = -0.0
+    dig = torch.randn(2, wl.num_kv_heads, wl.max_blocks, wl.head_dim).to(torch.bfloat16).cuda()
+    bt = torch.full((2, wl.num_kv_heads, wl.max_blocks), -1, dtype=torch.int32, device="cuda")
+    bt[:, :, 2] = 0
+    pairs = 2 * wl.num_kv_heads
+    gb = torch.empty(pairs, 5, dtype=torch.int32, device="cuda")
+    cb, ng, nc = torch.empty_like(gb), torch.empty(pairs, dtype=torch.int32, device="cuda"), \
+        torch.empty(pairs, dtype=torch.int32, device="cuda")
+    ws = B.workspace(B.sa_workspace_bytes(dims, 5))
+    B.sa_select_blocks(dims, "mean", q, dig, lens, 5, bt, gb, ng, cb, nc, None, ws)
+    torch.cuda.synchronize()
+    for p in range(pairs):
+        assert gb[p].tolist() == [2, -1, -1, -1, -1] and ng[p] == 1
+        assert cb[p].tolist() == [0, 1, 3, 4, -1] and nc[p] == 4
+
+
+def test_step_parity():
+    H.log("[case] step")
+    import harness_step as HS
+    HS.run_step(wk.QWEN3_14B_STEP.scaled(batch=3, num_q_heads=10, num_kv_heads=2, context=2000,
+                                         layers=4, pool_blocks=16, hidden=512, top_k=8),
+                gen_device="cpu", handoff=True)
+
+
+def test_step_parity_minmax_no_handoff():
+    H.log("[case] step minmax")
+    import harness_step as HS
+    HS.run_step(wk.QWEN3_14B_STEP.scaled(batch=2, num_q_heads=8, num_kv_heads=2, context=1024,
+                                         layers=3, pool_blocks=8, hidden=256, top_k=4,
+                                         digest_kinds=("minmax",)),
+                gen_device="cpu", handoff=False, kind="minmax")
