@@ -1,0 +1,345 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the GPU-side ScoutAttention path on one MI355X.
+
+Workload: the Qwen3-14B-shaped 40-layer decode step, batch 40, context 65536 (2048 blocks
+of 32 per sequence and KV head), budget 2048 tokens (64 blocks), bf16 KV with mean
+digests, a resident pool of 128 blocks per (sequence, KV head) per layer.  One step runs
+Algorithm 1 over all 40 layers: Q^i and Q_pred^{i+1} GEMMs, digest scoring + top-k + split
+for layer i+1 (with the offloaded lists copied to pinned host memory on a copy stream),
+block-sparse attention over the resident blocks of layer i and the merge with layer i's
+host partial.  Inputs are synthetic (seeded) and resident in HBM before timing.
+
+Prints one JSON line: seq-layers/s (= batch * layers / step time), the attention
+kernel's achieved HBM bandwidth against the 8 TB/s peak (timed per launch with HIP
+events), and the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches")
+    ap.add_argument("--profile-steps", type=int, default=5,
+                    help="eager steps whose attention launches are timed with events")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------------------
+# workload setup (untimed)
+# ---------------------------------------------------------------------------------------
+
+def setup(wl, torch, B, wk):
+    dev = "cuda"
+    L, Bsz, Hkv, Hq, d, k = (wl.layers, wl.batch, wl.num_kv_heads, wl.num_q_heads,
+                             wl.head_dim, wl.top_k)
+    pairs = Bsz * Hkv
+    lens = wk.seq_lens(wl).to(dev)
+    P = pairs * wl.pool_blocks
+    dims = B.Dims(Bsz, Hq, Hkv, d, wl.block_size, wl.max_blocks, P, B.SA_BF16)
+    ins = wk.draw_layer_inputs(wl, dev)
+    # the pool of each layer: the top pool_blocks blocks under the layer's true query
+    # Q^i = W_Q^i X^i on the drawn digests (blocks found important in earlier steps)
+    table_none = torch.full((Bsz, Hkv, wl.max_blocks), -1, dtype=torch.int32, device=dev)
+    kp = wl.pool_blocks
+    sel_ws = B.workspace(B.sa_workspace_bytes(dims, kp))
+    gemm_ws = B.workspace(B.sa_predict_query_workspace_bytes(Bsz, Hq * d, wl.hidden))
+    q = torch.empty((Bsz, Hq * d), dtype=torch.float32, device=dev)
+    gb = torch.empty((pairs, kp), dtype=torch.int32, device=dev)
+    cb, ng, nc = torch.empty_like(gb), torch.empty(pairs, dtype=torch.int32, device=dev), \
+        torch.empty(pairs, dtype=torch.int32, device=dev)
+    layers = []
+    t0 = time.time()
+    for i in range(L):
+        off = wk.layer_offsets(wl, i, dev)
+        dig = wk.draw_layer_digests(wl, i, off, dev)
+        B.sa_predict_query(ins[i]["X"], ins[i]["W"], q, gemm_ws)
+        B.sa_select_blocks(dims, "mean", q, dig, lens, kp, table_none, gb, ng, cb, nc, None,
+                           sel_ws)
+        sets = [[None] * Hkv for _ in range(Bsz)]
+        cbh = cb.cpu().numpy()
+        for p in range(pairs):
+            sets[p // Hkv][p % Hkv] = cbh[p]
+        pool = wk.draw_layer_pool(wl, i, off, sets)
+        B.sa_build_digests(dims, "mean", pool["K"], pool["block_table"], lens, dig)
+        hp = wk.draw_host_partials(wl, i, dev)
+        del off
+        layers.append(dict(
+            x=ins[i]["X"], w_q=ins[i]["W"], digests=dig, block_table=pool["block_table"],
+            k_pool=pool["K"], v_pool=pool["V"], host_o=hp["o"], host_m=hp["m"],
+            host_l=hp["l"],
+            gpu_blocks=torch.empty((pairs, k), dtype=torch.int32, device=dev),
+            n_gpu=torch.empty(pairs, dtype=torch.int32, device=dev),
+            cpu_blocks=torch.empty((pairs, k), dtype=torch.int32, device=dev),
+            n_cpu=torch.empty(pairs, dtype=torch.int32, device=dev),
+            cpu_blocks_host=torch.empty((pairs, k), dtype=torch.int32).pin_memory(),
+            n_cpu_host=torch.empty(pairs, dtype=torch.int32).pin_memory(),
+            out_o=torch.empty((Bsz, Hq, d), dtype=torch.float32, device=dev),
+            out_m=torch.empty((Bsz, Hq), dtype=torch.float32, device=dev),
+            out_l=torch.empty((Bsz, Hq), dtype=torch.float32, device=dev)))
+        if i % 8 == 7 or i == L - 1:
+            torch.cuda.synchronize()
+            log(f"setup: {i + 1}/{L} layers ({time.time() - t0:.1f} s)")
+    ws = B.workspace(B.sa_step_workspace_bytes(dims, wl.hidden, k))
+    return dims, lens, layers, ws
+
+
+# ---------------------------------------------------------------------------------------
+# algorithmic bytes
+# ---------------------------------------------------------------------------------------
+
+def attention_bytes(wl, n_gpu_sum):
+    """GPUATTN of one layer: the selected resident K and V rows, q, and the (o, m, l) result."""
+    kv = n_gpu_sum * wl.block_size * wl.head_dim * 2 * 2
+    q = wl.batch * wl.num_q_heads * wl.head_dim * 4
+    out = wl.batch * wl.num_q_heads * (wl.head_dim + 2) * 4
+    return kv + q + out
+
+
+def step_bytes(wl, n_gpu_sums):
+    """Algorithmic bytes of one whole step (every stage of every layer)."""
+    Bsz, Hkv, Hq, d, k, L = (wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim,
+                             wl.top_k, wl.layers)
+    n, hid = Hq * d, wl.hidden
+    gemm = lambda: n * hid * 2 + Bsz * hid * 2 + Bsz * n * 4
+    score = Bsz * Hkv * wl.max_blocks * d * 2 + Bsz * Hq * d * 4 + Bsz * Hkv * (2 * k + 2) * 4
+    merge = 3 * Bsz * Hq * (d + 2) * 4
+    total = 0
+    for i in range(L):
+        total += gemm() * (2 if i + 1 < L else 1)
+        total += score * (2 if i == 0 else (1 if i + 1 < L else 0))
+        total += attention_bytes(wl, n_gpu_sums[i]) + merge
+    return total
+
+
+# ---------------------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------------------
+
+def cpu_baseline(wl_full, budget_s):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from block_sparse_attention_digest_amd import workloads as wk
+    from oracle import scout_oracle as so
+
+    nseq = 1
+    wl = wl_full.scaled(batch=nseq, layers=2)
+    ins = wk.draw_layer_inputs(wl, "cpu")
+    G, d, bs = wl.group, wl.head_dim, wl.block_size
+    nb = wl.max_blocks
+    olayers_by_pair = {(0, h): [] for h in range(wl.num_kv_heads)}
+    for i in range(wl.layers):
+        off = wk.layer_offsets(wl, i, "cpu")
+        dig = wk.draw_layer_digests(wl, i, off, "cpu")
+        X64 = ins[i]["X"].float().numpy().astype(np.float64)
+        W32 = ins[i]["W"].float().numpy()
+        Q = so.query_heads(so.predict_query(X64, W32), wl.num_q_heads, d)
+        dig64 = dig.float().numpy().astype(np.float64)
+        sets = [[so.select_topk(so.score_mean(Q[0, h * G:(h + 1) * G], dig64[0, h]),
+                                wl.pool_blocks) for h in range(wl.num_kv_heads)]]
+        pool = wk.draw_layer_pool(wl, i, off, sets)
+        hp = wk.draw_host_partials(wl, i, "cpu")
+        for h in range(wl.num_kv_heads):
+            bt = pool["block_table"][0, h]
+            resident = (bt >= 0).numpy()
+            Kl = np.zeros((nb * bs, d))
+            Vl = np.zeros((nb * bs, d))
+            for b in np.nonzero(resident)[0]:
+                Kl[b * bs:(b + 1) * bs] = pool["K"][int(bt[b])].float().numpy()
+                Vl[b * bs:(b + 1) * bs] = pool["V"][int(bt[b])].float().numpy()
+            digh = dig64[0, h].copy()
+            res_b = np.nonzero(resident)[0]
+            digh[res_b] = so.digest_mean(Kl, nb * bs, bs, "bf16")[res_b]
+            host = [so.Partial(hp["o"][0, h * G + j].double().numpy(), float(hp["m"][0, h * G + j]),
+                               float(hp["l"][0, h * G + j])) for j in range(G)]
+            olayers_by_pair[(0, h)].append(dict(X=X64, W=W32, digest=digh, resident=resident,
+                                                K=Kl, V=Vl, seq_len=nb * bs, host=host))
+    # time whole (sequence, layer) units: all KV heads of the sequence through one layer
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        for h in range(wl.num_kv_heads):
+            so.decode_step_pair(olayers_by_pair[(0, h)], 0, h, G, d, bs, wl.top_k, wl.scale)
+        done += wl.layers
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": done / el, "unit": "seq-layers/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} seq-layers: 1 sequence x {wl.layers} layers of the step "
+                      f"(all {wl.num_kv_heads} KV heads, Algorithm 1 end to end in float64), "
+                      f"repeated for {el:.1f} s; same shapes and recipe as the GPU workload"}
+
+
+# ---------------------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this decode path has no multi-GPU mode "
+              "(see DESIGN.md, 'How the path would shard').", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_sparse_attention_digest_amd import binding as B
+    from block_sparse_attention_digest_amd import workloads as wk
+    if not os.path.exists(B.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    B.lib()
+    torch.cuda.set_device(0)
+
+    wl = wk.QWEN3_14B_STEP
+    log(f"workload {wl.name}: setup")
+    dims, lens, layers, ws = setup(wl, torch, B, wk)
+    copy_stream = torch.cuda.Stream()
+    kind = "mean"
+
+    def step():
+        B.sa_decode_step(dims, kind, wl.hidden, wl.top_k, wl.scale, lens, layers, ws,
+                         copy_stream=copy_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ref_out = layers[-1]["out_o"].clone()
+    n_gpu_sums = [int(L["n_gpu"].sum()) for L in layers]
+    n_cpu_sums = [int(L["n_cpu"].sum()) for L in layers]
+    log("warmup done")
+
+    mode = "eager"
+    graph = None
+    if not args.no_graph:
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            torch.cuda.synchronize()
+            ok = True
+            for _ in range(3):  # every replay must reproduce the eager result
+                layers[-1]["out_o"].zero_()
+                graph.replay()
+                torch.cuda.synchronize()
+                ok &= bool(torch.equal(layers[-1]["out_o"], ref_out))
+            if ok:
+                mode = "hip-graph"
+            else:
+                log("graph replay differs from eager launches: timing eager launches")
+                graph = None
+        except Exception as e:  # noqa: BLE001
+            log(f"graph capture unavailable ({e}): timing eager launches")
+            graph = None
+
+    run = graph.replay if graph is not None else step
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"timed {args.steps} steps ({mode}): {ms_step:.3f} ms/step (wall {wall:.3f} s)")
+
+    # attention kernel timed per launch with HIP events (eager steps)
+    nprof = args.profile_steps * wl.layers
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(nprof)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(nprof)]
+    for e in starts + stops:
+        e.record()
+    torch.cuda.synchronize()
+    B.sa_profile_attention(starts, stops)
+    for _ in range(args.profile_steps):
+        step()
+    torch.cuda.synchronize()
+    B.sa_profile_attention([], [])
+    attn_ms = [starts[j].elapsed_time(stops[j]) for j in range(nprof)]
+    attn_avg_ms = sum(attn_ms) / len(attn_ms)
+    attn_bytes_avg = sum(attention_bytes(wl, n_gpu_sums[j % wl.layers])
+                         for j in range(nprof)) / nprof
+    achieved = attn_bytes_avg / (attn_avg_ms * 1e-3) / 1e9
+    total_bytes = step_bytes(wl, n_gpu_sums)
+    log(f"attention: {attn_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s algorithmic")
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "attention_traffic.json")
+    if os.path.exists(tpath):
+        t = json.load(open(tpath))
+        src = os.path.join(ROOT, "block_sparse_attention_digest_amd", "csrc", "attention.hip")
+        if t.get("attention_source_sha256_16") == source_hash(src):
+            traffic = t.get("hbm_bytes_per_launch")
+
+    value = wl.batch * wl.layers / (ms_step * 1e-3)
+    result = {
+        "metric": "decode-attn seq-layers/s + achieved HBM GB/s (%peak), Qwen3-14B shape 64K ctx",
+        "value": round(value, 1),
+        "unit": "seq-layers/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": wl.layers, "batch": wl.batch,
+                   "context": wl.context, "block_size": wl.block_size,
+                   "budget_tokens": wl.top_k * wl.block_size, "q_heads": wl.num_q_heads,
+                   "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "hidden": wl.hidden,
+                   "digest": kind, "resident_pool_blocks": wl.pool_blocks,
+                   "launch": mode, "parallelism": "single-gpu"},
+        "step_hbm_gbs": round(total_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_frac_of_peak": round(total_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "cpu_ratio": round(sum(n_cpu_sums) / (wl.layers * wl.batch * wl.num_kv_heads * wl.top_k), 4),
+        "roofline": {"kernel": "attn_bf16_kernel (GPUATTN)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "avg_launch_us": round(attn_avg_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": int(attn_bytes_avg)},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

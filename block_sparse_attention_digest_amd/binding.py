@@ -70,6 +70,7 @@ SIGNATURES = {
     "sa_step_workspace_bytes": (_Z, [_D, _I, _I]),
     "sa_decode_step": (ctypes.c_int, [_D, ctypes.c_int, _I, _I, _F, _P, _I,
                                       ctypes.POINTER(sa_layer), _P, _Z, _P, _P]),
+    "sa_profile_attention": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.POINTER(_P), _I]),
 }
 
 _lib = None
@@ -262,3 +263,13 @@ def sa_decode_step(dims: Dims, kind: str, hidden: int, top_k: int, scale: float,
         _ptr(seq_lens, torch.int32, dims.batch, "seq_lens"), len(layers), arr,
         _ptr(ws, torch.uint8, name="ws"), ws.numel(), _stream(stream),
         None if copy_stream is None else _stream(copy_stream)))
+
+
+def sa_profile_attention(starts, stops):
+    """Time the next len(starts) attention-kernel launches of this thread: `starts` and
+    `stops` are torch.cuda.Event(enable_timing=True) objects (already recorded once, so
+    that they exist).  Read durations with starts[i].elapsed_time(stops[i])."""
+    n = len(starts)
+    a = (_P * max(1, n))(*[e.cuda_event for e in starts])
+    b = (_P * max(1, n))(*[e.cuda_event for e in stops])
+    _check(lib().sa_profile_attention(a, b, n))

@@ -16,6 +16,22 @@ namespace {
 
 thread_local std::string g_err;
 
+// Attention-kernel profiling events of the calling thread (sa_profile_attention).
+struct ProfileEvents {
+  std::vector<hipEvent_t> start, stop;
+  size_t next = 0;
+};
+thread_local ProfileEvents g_prof;
+
+void next_profile_events(hipEvent_t* e0, hipEvent_t* e1) {
+  *e0 = *e1 = nullptr;
+  if (g_prof.next < g_prof.start.size()) {
+    *e0 = g_prof.start[g_prof.next];
+    *e1 = g_prof.stop[g_prof.next];
+    ++g_prof.next;
+  }
+}
+
 sa_status fail(sa_status st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -137,6 +153,21 @@ int sa_abi_version(void) { return SA_ABI_VERSION; }
 
 const char* sa_last_error(void) { return g_err.c_str(); }
 
+sa_status sa_profile_attention(const hipEvent_t* start, const hipEvent_t* stop, int32_t n) {
+  if (n < 0) return fail(SA_ERR_INVALID_ARG, "n %d < 0", n);
+  if (n > 0 && (!start || !stop)) return fail(SA_ERR_INVALID_ARG, "event arrays are NULL");
+  g_prof.start.assign(start, start + n);
+  g_prof.stop.assign(stop, stop + n);
+  g_prof.next = 0;
+  for (int32_t i = 0; i < n; ++i)
+    if (!g_prof.start[i] || !g_prof.stop[i]) {
+      g_prof.start.clear();
+      g_prof.stop.clear();
+      return fail(SA_ERR_INVALID_ARG, "event %d is NULL", i);
+    }
+  return ok();
+}
+
 const char* sa_status_string(sa_status status) {
   switch (status) {
     case SA_OK: return "SA_OK";
@@ -245,8 +276,10 @@ static sa_status decode_common(const sa_dims* dims, const float* q, const void* 
   if (!ws || ws_bytes < L.total)
     return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, L.total);
   float* parts = (float*)((char*)ws + L.parts);
+  hipEvent_t e0, e1;
+  next_profile_events(&e0, &e1);
   SA_HIP(sa::launch_attention(s, L.plan, q, k_pool, v_pool, block_table, seq_lens, gpu_blocks,
-                              n_gpu, list_stride, scale, parts, stream),
+                              n_gpu, list_stride, scale, parts, stream, e0, e1),
          "attention kernel");
   SA_HIP(sa::launch_reduce(s, L.plan, n_gpu, parts, host_o, host_m, host_l, n_cpu, o, m, l,
                            stream),
@@ -421,8 +454,11 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
       if (st != SA_OK) break;
     }
     // 4. GPU attention of layer i, merged with its host partial
+    hipEvent_t e0, e1;
+    next_profile_events(&e0, &e1);
     e = sa::launch_attention(s, SL.sel_layout.plan, q_true, L.k_pool, L.v_pool, L.block_table,
-                             seq_lens, L.gpu_blocks, L.n_gpu, top_k, scale, parts, stream);
+                             seq_lens, L.gpu_blocks, L.n_gpu, top_k, scale, parts, stream, e0,
+                             e1);
     if (e != hipSuccess) { st = hip_fail(e, "attention kernel"); break; }
     e = sa::launch_reduce(s, SL.sel_layout.plan, L.n_gpu, parts, L.host_o, L.host_m, L.host_l,
                           L.n_cpu, L.out_o, L.out_m, L.out_l, stream);

@@ -27,6 +27,8 @@
 //
 // Internal log2 domain: logits are scaled by scale * log2(e) and exponentiated with exp2;
 // m is reported in natural-log units.
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -466,14 +468,15 @@ template <int D, int BS>
 hipError_t attn_bf16_g(const Shape& s, const AttnPlan& p, const float* q, const void* k,
                        const void* v, const int32_t* t, const int32_t* lens,
                        const int32_t* gb, const int32_t* ng, int stride, float sl2,
-                       float* part, hipStream_t st) {
+                       float* part, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const dim3 grid(p.nchunks, s.B * s.Hkv), block(kAttnWaves * kWave);
   const int pairs = s.B * s.Hkv;
+  // hipExtLaunchKernelGGL records the (optional) events at the kernel's own start and end
 #define SA_ATTN_CASE(GG)                                                                    \
   case GG:                                                                                  \
-    hipLaunchKernelGGL((attn_bf16_kernel<D, BS, GG>), grid, block, 0, st, q,                \
-                       (const uint16_t*)k, (const uint16_t*)v, t, lens, gb, ng, stride,      \
-                       s.Hkv, s.max_blocks, sl2, p.chunk_blocks, p.nchunks, pairs, part);    \
+    hipExtLaunchKernelGGL((attn_bf16_kernel<D, BS, GG>), grid, block, 0, st, e0, e1, 0, q,  \
+                          (const uint16_t*)k, (const uint16_t*)v, t, lens, gb, ng, stride,   \
+                          s.Hkv, s.max_blocks, sl2, p.chunk_blocks, p.nchunks, pairs, part); \
     break;
   switch (s.G) {
     SA_ATTN_CASE(1) SA_ATTN_CASE(2) SA_ATTN_CASE(3) SA_ATTN_CASE(4)
@@ -487,11 +490,12 @@ hipError_t attn_bf16_g(const Shape& s, const AttnPlan& p, const float* q, const 
 template <int D, int BS>
 hipError_t attn_f32(const Shape& s, const AttnPlan& p, const float* q, const void* k,
                     const void* v, const int32_t* t, const int32_t* lens, const int32_t* gb,
-                    const int32_t* ng, int stride, float sl2, float* part, hipStream_t st) {
+                    const int32_t* ng, int stride, float sl2, float* part, hipStream_t st,
+                    hipEvent_t e0, hipEvent_t e1) {
   const dim3 grid(p.nchunks, s.B * s.Hkv);
-  hipLaunchKernelGGL((attn_f32_kernel<D, BS>), grid, dim3(kWave), 0, st, q, (const float*)k,
-                     (const float*)v, t, lens, gb, ng, stride, s.Hkv, s.G, s.max_blocks, sl2,
-                     p.chunk_blocks, p.nchunks, s.B * s.Hkv, part);
+  hipExtLaunchKernelGGL((attn_f32_kernel<D, BS>), grid, dim3(kWave), 0, st, e0, e1, 0, q,
+                        (const float*)k, (const float*)v, t, lens, gb, ng, stride, s.Hkv, s.G,
+                        s.max_blocks, sl2, p.chunk_blocks, p.nchunks, s.B * s.Hkv, part);
   return hipGetLastError();
 }
 
@@ -511,10 +515,11 @@ hipError_t launch_attention(const Shape& s, const AttnPlan& plan, const float* q
                             const void* k_pool, const void* v_pool,
                             const int32_t* block_table, const int32_t* seq_lens,
                             const int32_t* gpu_blocks, const int32_t* n_gpu, int list_stride,
-                            float scale, float* partials, hipStream_t stream) {
+                            float scale, float* partials, hipStream_t stream,
+                            hipEvent_t ev_start, hipEvent_t ev_stop) {
   const float sl2 = scale * kLog2e;
 #define SA_ARGS plan, q, k_pool, v_pool, block_table, seq_lens, gpu_blocks, n_gpu, \
-                list_stride, sl2, partials, stream
+                list_stride, sl2, partials, stream, ev_start, ev_stop
   if (s.bf16) {
     if (s.d == 128) return s.bs == 32 ? attn_bf16_g<128, 32>(s, SA_ARGS) : attn_bf16_g<128, 16>(s, SA_ARGS);
     return s.bs == 32 ? attn_bf16_g<64, 32>(s, SA_ARGS) : attn_bf16_g<64, 16>(s, SA_ARGS);

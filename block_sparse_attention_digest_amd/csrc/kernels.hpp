@@ -50,7 +50,8 @@ hipError_t launch_attention(const Shape& s, const AttnPlan& plan, const float* q
                             const void* k_pool, const void* v_pool,
                             const int32_t* block_table, const int32_t* seq_lens,
                             const int32_t* gpu_blocks, const int32_t* n_gpu, int list_stride,
-                            float scale, float* partials, hipStream_t stream);
+                            float scale, float* partials, hipStream_t stream,
+                            hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 // Combine the chunk partials of every (sequence, query head) row, optionally merged with a
 // host partial (gated by n_cpu when given); writes normalised o and natural-unit m, l.
 hipError_t launch_reduce(const Shape& s, const AttnPlan& plan, const int32_t* n_gpu,

@@ -63,7 +63,7 @@ typedef enum { SA_DIGEST_MEAN = 0, SA_DIGEST_MINMAX = 1 } sa_digest_kind;
 
 /* Problem shape.  Supported: head_dim in {64, 128}; block_size in {16, 32};
  * num_q_heads % num_kv_heads == 0 with G = num_q_heads / num_kv_heads in [1, 8];
- * 1 <= max_blocks <= 16384; num_pages >= 1; kv_dtype SA_F32 or SA_BF16. */
+ * 1 <= max_blocks <= 8192; num_pages >= 1; kv_dtype SA_F32 or SA_BF16. */
 typedef struct {
   int32_t batch;         /* B                                                     */
   int32_t num_q_heads;   /* Hq                                                    */
@@ -147,7 +147,8 @@ sa_status sa_select_blocks(const sa_dims* dims, sa_digest_kind kind, const float
  *   An empty list gives o = 0, m = -inf, l = 0.
  *   q [B][Hq][d] float32; k_pool, v_pool [P][bs][d]; gpu_blocks [B][Hkv][list_stride] with
  *   entries in [0, nb_s) whose table entry is a page in [0, P); 0 <= n_gpu <= list_stride.
- *   Outputs o [B][Hq][d], m [B][Hq], l [B][Hq] float32 (m in natural-log units).
+ *   Outputs o [B][Hq][d], m [B][Hq], l [B][Hq] float32 (m in natural-log units); m and l
+ *   may be NULL when not wanted.
  *   ws: sa_workspace_bytes(dims, list_stride).
  * ------------------------------------------------------------------------------------- */
 sa_status sa_sparse_decode(const sa_dims* dims, const float* q, const void* k_pool,
@@ -227,6 +228,17 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
                          int32_t top_k, float scale, const int32_t* seq_lens,
                          int32_t num_layers, const sa_layer* layers, void* ws,
                          size_t ws_bytes, hipStream_t stream, hipStream_t copy_stream);
+
+/* ---------------------------------------------------------------------------------------
+ * sa_profile_attention -- kernel timing of the attention stage (GPUATTN).  After this call
+ * the next n attention-kernel launches made by the calling thread (from sa_sparse_decode,
+ * sa_decode_attend_merge or sa_decode_step) record start[i] when the i-th launch begins
+ * executing and stop[i] when it ends, so hipEventElapsedTime(start[i], stop[i]) is that
+ * kernel's duration.  Events are created by the caller and must stay valid until those
+ * launches have completed; the handle arrays are copied.  Launches beyond n record
+ * nothing; n = 0 turns the hook off.  Not for use while a stream is being captured.
+ * ------------------------------------------------------------------------------------- */
+sa_status sa_profile_attention(const hipEvent_t* start, const hipEvent_t* stop, int32_t n);
 
 #ifdef __cplusplus
 }

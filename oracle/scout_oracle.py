@@ -398,8 +398,8 @@ def decode_step_pair(layers, s: int, h: int, group: int, head_dim: int, block_si
     rows = [slice(g * head_dim, (g + 1) * head_dim) for g in heads]
 
     def q_of(X, W):
-        x = np.asarray(X, dtype=np.float64)[s:s + 1]
-        Wg = np.concatenate([np.asarray(W, dtype=np.float64)[r] for r in rows], axis=0)
+        x = np.asarray(X[s:s + 1], dtype=np.float64)
+        Wg = np.concatenate([np.asarray(W[r], dtype=np.float64) for r in rows], axis=0)
         return predict_query(x, Wg).reshape(len(heads), head_dim)
 
     L = len(layers)
