@@ -52,6 +52,7 @@ sa_status hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int kMaxBlocks = 8192;  // LDS budget of the top-k workgroup
+constexpr int kMaxPairs = 8192;   // LDS budget of the attention workgroups' pair prefix
 
 sa_status check_dims(const sa_dims* d, sa::Shape* s) {
   if (!d) return fail(SA_ERR_INVALID_ARG, "dims is NULL");
@@ -70,6 +71,9 @@ sa_status check_dims(const sa_dims* d, sa::Shape* s) {
     return fail(SA_ERR_UNSUPPORTED, "block_size %d not in {16, 32}", d->block_size);
   if (d->max_blocks > kMaxBlocks)
     return fail(SA_ERR_UNSUPPORTED, "max_blocks %d > %d", d->max_blocks, kMaxBlocks);
+  if ((long)d->batch * d->num_kv_heads > kMaxPairs)
+    return fail(SA_ERR_UNSUPPORTED, "batch * num_kv_heads %ld > %d",
+                (long)d->batch * d->num_kv_heads, kMaxPairs);
   if (d->kv_dtype != SA_F32 && d->kv_dtype != SA_BF16)
     return fail(SA_ERR_UNSUPPORTED, "kv_dtype %d is neither SA_F32 nor SA_BF16", (int)d->kv_dtype);
   s->B = d->batch;

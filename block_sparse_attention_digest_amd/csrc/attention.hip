@@ -2,28 +2,34 @@
 // and its FlashAttention-style merge with the host partials, A = MERGE(A_gpu, A_cpu)
 // [ScoutAttention, arXiv:2603.27138, HTML Sec. 3.2; Algorithm 1].
 //
-// Work split.  A workgroup of 4 waves takes one (sequence, KV head) pair and a chunk of its
-// selected resident blocks; each wave walks its share of the chunk 32 tokens at a time (one
-// block of 32, or two blocks of 16) and keeps an online softmax for the G query heads of
-// the group.  The waves are combined in LDS and the workgroup writes one un-normalised
-// partial (o, m, l) per head; the reduce kernel combines a pair's chunk partials (and the
-// host partial) per query head.  Chunking gives thousands of workgroups even for a few
-// hundred pairs, which keeps all 256 CUs streaming.
+// Work split: balanced persistent waves.  The selected resident blocks of all (sequence,
+// KV head) pairs are laid end to end (an exclusive prefix sum of n_gpu over the pairs, T
+// blocks in all) and wave w of the W waves in the grid streams blocks
+// [floor(w T / W), floor((w+1) T / W)), crossing pair boundaries as it goes.  Every wave
+// gets the same number of blocks whatever the per-pair counts are, so the chip streams
+// until the end with no partial last round.  For each pair its range touches a wave keeps
+// one online softmax and writes one un-normalised partial (o, m, l) per query head; the
+// partial of wave w for pair p lives in slot w + p, which is unique because the waves'
+// ranges are ordered.  The reduce kernel combines a pair's partials (waves covering the
+// pair's block range) and, when given, the host partial.
 //
-// bf16 path, per 32-token step of a wave:
-//   * K (32 x d) is loaded straight into MFMA A-operand registers: lane l holds token
-//     l % 16 of a 16-token tile and 8 consecutive channels (16 bytes), so one load
-//     instruction reads 16 token rows of 64 contiguous bytes each.
+// bf16 path, per 16-token step of a wave (one MFMA tile: a block of 16, or half of 32):
+//   * the page and valid-token count of up to 64 upcoming blocks sit in lane registers,
+//     looked up in two dependent loads per window (list entry, then block table);
+//   * K (16 x d) is loaded straight into MFMA A-operand registers: lane l holds token
+//     l % 16 and 8 consecutive channels (16 bytes);
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16.  Q's columns are the G heads split into a
 //     bf16 high part (columns 0..7) and a bf16 low part q - hi (columns 8..15); adding the
 //     two results recovers q . k to about 2^-17 relative, so the float32 query keeps its
-//     precision while K stays bf16.
+//     precision while K stays bf16;
 //   * the softmax runs on the MFMA output layout (lane l: head l % 8, four tokens) with
-//     cross-lane shuffles; p is passed through a 1 KiB LDS slab to the PV layout.
-//   * O += P V on the vector ALU: lane l owns 8 channels of every 4th (d = 128) token row,
-//     V read with 16-byte loads that cover whole rows.
-// float32 path (small fp32 workloads): K and V staged through LDS, plain per-lane dot
-// products; same chunk partials.
+//     DPP / permlane exchanges; p goes through a 1 KiB LDS slab to the PV layout;
+//   * O += P V on the vector ALU: lane l owns 8 channels of every 4th (d = 128) token row;
+//   * steps are 16 tokens so that two of them (the one computed and the one in flight) fit
+//     the register budget of 2 waves per SIMD without spilling;
+//   * the next step's K and V are in flight while the current step is computed.
+// float32 path (small fp32 workloads): the same balanced ranges, one block at a time, K and
+// V staged through LDS and plain per-lane dot products.
 //
 // Internal log2 domain: logits are scaled by scale * log2(e) and exponentiated with exp2;
 // m is reported in natural-log units.
@@ -35,24 +41,80 @@
 namespace sa {
 namespace {
 
-constexpr int kAttnWaves = 4;
-constexpr int kStep = 32;  // tokens per wave step
+constexpr int kAttnWaves = 4;            // waves per workgroup (bf16 path)
+constexpr int kStep = 16;                // tokens per wave step (one MFMA tile)
+constexpr int kWavesPerCU = 8;           // resident waves per CU the grid is sized for
+constexpr int kMaxWaves = 256 * kWavesPerCU;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Partials of chunk c of pair p, head g: o at part_o[((p * nchunks + c) * G + g) * D],
-// (m_log2, l) at part_ml[((p * nchunks + c) * G + g) * 2].
-struct Partials {
+// Workspace: prefix [npairs + 1] ints, then per slot (W + npairs slots) and head: o [D]
+// floats, then (m_log2, l) pairs.
+struct PartialView {
+  int* pfx;
   float* o;
   float* ml;
 };
+__host__ __device__ inline size_t prefix_bytes(int npairs) {
+  return ((size_t)(npairs + 1) * sizeof(int) + 255) & ~(size_t)255;
+}
+__host__ __device__ inline PartialView partial_view(float* base, int npairs, int W, int G, int D) {
+  PartialView v;
+  v.pfx = reinterpret_cast<int*>(base);
+  v.o = reinterpret_cast<float*>(reinterpret_cast<char*>(base) + prefix_bytes(npairs));
+  v.ml = v.o + (size_t)(W + npairs) * G * D;
+  return v;
+}
 
-__device__ __forceinline__ Partials partial_ptrs(float* base, int pairs, int nchunks, int G,
-                                                 int D) {
-  Partials p;
-  p.o = base;
-  p.ml = base + (size_t)pairs * nchunks * G * D;
-  return p;
+// first global block of wave w, and the wave holding global block g
+__device__ __forceinline__ int wave_start(int w, int T, int W) {
+  return (int)((long long)w * T / W);
+}
+__device__ __forceinline__ int wave_of(int g, int T, int W) {
+  return (int)(((long long)(g + 1) * W + T - 1) / T) - 1;
+}
+
+// Exclusive prefix sum of n_gpu over the pairs into LDS pfx[0..npairs] (pfx[npairs] = T).
+// Every thread of the workgroup takes part; ends with a barrier.
+__device__ void pair_prefix(const int32_t* __restrict__ n_gpu, int npairs, int* pfx,
+                            int* wave_tot) {
+  const int nt = blockDim.x, tid = threadIdx.x;
+  const int lane = tid % kWave, wave = tid / kWave, nw = nt / kWave;
+  const int per = (npairs + nt - 1) / nt;
+  const int p0 = min(npairs, tid * per), p1 = min(npairs, p0 + per);
+  int local = 0;
+  for (int p = p0; p < p1; ++p) local += n_gpu[p];
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
+  }
+  if (lane == kWave - 1) wave_tot[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wave_tot[w];
+  int run = base + incl - local;
+  for (int p = p0; p < p1; ++p) {
+    pfx[p] = run;
+    run += n_gpu[p];
+  }
+  if (tid == nt - 1) {
+    int tot = 0;
+    for (int w = 0; w < nw; ++w) tot += wave_tot[w];
+    pfx[npairs] = tot;
+  }
+  __syncthreads();
+}
+
+// last pair p with pfx[p] <= g (the pair holding global block g when g < T)
+__device__ __forceinline__ int pair_of(const int* pfx, int npairs, int g) {
+  int lo = 0, hi = npairs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pfx[mid] <= g) lo = mid; else hi = mid - 1;
+  }
+  return lo;
 }
 
 template <int D, int BS, int G>
@@ -60,149 +122,151 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     const float* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ gpu_blocks,
-    const int32_t* __restrict__ n_gpu, int list_stride, int Hkv, int max_blocks,
-    float scale_log2, int chunk_blocks, int nchunks, int pairs, float* __restrict__ part_base) {
+    const int32_t* __restrict__ n_gpu, int list_stride, int Hkv, int max_blocks, int npairs,
+    int W, float scale_log2, float* __restrict__ ws) {
   constexpr int KS = D / 32;          // MFMA k-steps over the head dimension
-  constexpr int SPB = kStep / BS;     // blocks per step (1 or 2)
+  constexpr int HPB = BS / kStep;     // 16-token steps per block (1 or 2)
   constexpr int VLPR = D / 8;         // lanes per V row
   constexpr int VTPI = kWave / VLPR;  // V rows per load instruction
   constexpr int VJ = kStep / VTPI;    // V loads per lane per step
 
+  extern __shared__ int pfx[];        // [npairs + 1]
   __shared__ float p_lds[kAttnWaves][kStep][8];
   __shared__ float a_lds[kAttnWaves][8];
-  __shared__ float o_red[kAttnWaves][G][D];
-  __shared__ float ml_red[kAttnWaves][G][2];
+  __shared__ int wave_tot[kAttnWaves];
 
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int pair = blockIdx.y;
-  const int chunk = blockIdx.x;
-  const int ng = n_gpu[pair];
-  const int e_begin = chunk * chunk_blocks;
-  if (e_begin >= ng) return;  // the reduce kernel reads only non-empty chunks
-  const int e_end = min(ng, e_begin + chunk_blocks);
-  const int s = pair / Hkv, h = pair % Hkv;
-  const int len = seq_lens[s];
-  const int32_t* list = gpu_blocks + (size_t)pair * list_stride;
-  const int32_t* trow = table + (size_t)pair * max_blocks;
+  pair_prefix(n_gpu, npairs, pfx, wave_tot);
+  const PartialView part = partial_view(ws, npairs, W, G, D);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= npairs; i += blockDim.x) part.pfx[i] = pfx[i];
+  const int T = pfx[npairs];
+  const int gw = blockIdx.x * kAttnWaves + wave;
+  if (T == 0) return;
+  const int b0 = wave_start(gw, T, W), b1 = wave_start(gw + 1, T, W);
+  if (b0 >= b1) return;
 
-  const int c16 = lane % 16;   // MFMA column (head / hi-lo) and row-in-tile
+  const int c16 = lane % 16;   // MFMA column (head / hi-lo) and token row in the tile
   const int kq = lane / 16;    // MFMA k-group
   const int hcol = c16 & 7;    // head of this MFMA column
+  const int vcg = lane % VLPR, vts = lane / VLPR;
 
-  // Q^T as the MFMA B operand: column c < 8 = bf16(q_c), column c >= 8 = bf16(q_c - hi)
   bf16x8 qb[KS];
-  {
+  auto load_q = [&](int pair) {  // Q^T as the MFMA B operand (hi columns 0..7, lo 8..15)
+    const int s = pair / Hkv, h = pair % Hkv;
     const bool live = hcol < G;
     const float* qrow = q + ((size_t)s * Hkv * G + (size_t)h * G + (live ? hcol : 0)) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      float v[8];
+      *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(qrow + 32 * ks + 8 * kq);
+      *reinterpret_cast<float4*>(v + 4) =
+          *reinterpret_cast<const float4*>(qrow + 32 * ks + 8 * kq + 4);
       uint32_t w[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t half[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const float v = live ? qrow[32 * ks + 8 * kq + 2 * i + j] : 0.f;
-          const uint32_t hi = f32_to_bf16_rne(v);
-          half[j] = c16 < 8 ? hi : f32_to_bf16_rne(v - __uint_as_float(hi << 16));
+          const float x = live ? v[2 * i + j] : 0.f;
+          const uint32_t hi = f32_to_bf16_rne(x);
+          half[j] = c16 < 8 ? hi : f32_to_bf16_rne(x - __uint_as_float(hi << 16));
         }
         w[i] = half[0] | (half[1] << 16);
       }
       qb[ks] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
     }
-  }
+  };
 
   float m_run = -INFINITY;   // per head hcol (log2 units), uniform over the head's lanes
   float l_lane = 0.f;        // this lane's share of l for head hcol
   float o_acc[G][8];
+  auto reset = [&]() {
+    m_run = -INFINITY;
+    l_lane = 0.f;
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o_acc[g][i] = 0.f;
-
-  const int vcg = lane % VLPR, vts = lane / VLPR;
-  const int nsteps = (e_end - e_begin + SPB - 1) / SPB;
-  for (int step = wave; step < nsteps; step += kAttnWaves) {
-    // blocks of this step
-    int page[SPB], nval[SPB];
+      for (int i = 0; i < 8; ++i) o_acc[g][i] = 0.f;
+  };
+  auto finalize = [&](int pair) {  // write this wave's partial for `pair` to slot gw + pair
+    const float l_w = sum_xor32(sum_xor16(l_lane));
+    const size_t slot = (size_t)(gw + pair) * G;
 #pragma unroll
-    for (int j = 0; j < SPB; ++j) {
-      const int e = e_begin + step * SPB + j;
-      if (e < e_end) {
-        const int blk = list[e];
-        page[j] = trow[blk];
-        nval[j] = min(BS, len - blk * BS);
-      } else {
-        page[j] = -1;
-        nval[j] = 0;
+    for (int g = 0; g < G; ++g) {
+      float red[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float v = o_acc[g][i];
+        if (VLPR <= 8) v += xor8(v);
+        red[i] = sum_xor32(sum_xor16(v));
+      }
+      if (vts == 0) {
+        float* dst = part.o + (slot + g) * D + 8 * vcg;
+        *reinterpret_cast<float4*>(dst) = make_float4(red[0], red[1], red[2], red[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(red[4], red[5], red[6], red[7]);
       }
     }
-    // K into A-operand registers: tile tt covers step tokens 16tt .. 16tt+15
-    uint4 kr[2][KS];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int j = SPB == 1 ? 0 : tt;
-      const int tok = SPB == 1 ? 16 * tt + c16 : c16;
-      const bool ok = page[j] >= 0;
-      const uint16_t* src = k_pool + ((size_t)(ok ? page[j] : 0) * BS + tok) * D + 8 * kq;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kr[tt][ks] = ok ? *reinterpret_cast<const uint4*>(src + 32 * ks) : make_uint4(0, 0, 0, 0);
+    if (lane < G) {  // lane g: c16 = g, kq = 0
+      part.ml[(slot + lane) * 2 + 0] = m_run;
+      part.ml[(slot + lane) * 2 + 1] = l_w;
     }
-    // V rows for the PV product: step token t = jj * VTPI + vts
-    uint4 vr[VJ];
+  };
+
+  // one 16-token step in registers: a K tile as MFMA A operands, V rows for the PV product
+  struct StepRegs {
+    uint4 k[KS];
+    uint4 v[VJ];
+    int nval;
+  };
+  int w_pair = 0, w_page = -1, w_nval = 0;  // lane j: block (window start + j)
+  auto load_step = [&](int j, int hh, StepRegs& R) {
+    const int page = __builtin_amdgcn_readlane(w_page, j);
+    R.nval = __builtin_amdgcn_readlane(w_nval, j) - kStep * hh;  // valid tokens of the step
+    const size_t row0 = (size_t)page * BS + kStep * hh;
+    const uint16_t* src = k_pool + (row0 + c16) * D + 8 * kq;
 #pragma unroll
-    for (int jj = 0; jj < VJ; ++jj) {
+    for (int ks = 0; ks < KS; ++ks) R.k[ks] = *reinterpret_cast<const uint4*>(src + 32 * ks);
+#pragma unroll
+    for (int jj = 0; jj < VJ; ++jj) {  // step token t = jj * VTPI + vts
       const int t = jj * VTPI + vts;
-      const int j = t / BS;
-      const bool ok = (t % BS) < nval[j];  // masked rows are not read (p = 0 there)
-      vr[jj] = ok ? *reinterpret_cast<const uint4*>(
-                        v_pool + ((size_t)page[j] * BS + (t % BS)) * D + 8 * vcg)
-                  : make_uint4(0, 0, 0, 0);
+      R.v[jj] = t < R.nval ? *reinterpret_cast<const uint4*>(v_pool + (row0 + t) * D + 8 * vcg)
+                           : make_uint4(0, 0, 0, 0);  // masked rows are not read (p = 0)
     }
+  };
 
-    // S^T tiles: acc[tt][r] = logit of token 16tt + 4kq + r for MFMA column c16
-    float sc[2][4];
+  auto compute_step = [&](const StepRegs& R) {
+    // S^T tile: acc[r] = logit of token 4kq + r for MFMA column c16
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KS; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, R.k[ks]), qb[ks],
+                                                    acc, 0, 0, 0);
+    float sc[4];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[tt][ks]),
-                                                      qb[ks], acc, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float tot = acc[r] + __shfl_xor(acc[r], 8, kWave);  // hi + lo columns
-        const int j = SPB == 1 ? 0 : tt;
-        const int tin = SPB == 1 ? 16 * tt + 4 * kq + r : 4 * kq + r;  // token in block
-        sc[tt][r] = tin < nval[j] ? tot * scale_log2 : -INFINITY;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const float tot = acc[r] + xor8(acc[r]);  // hi + lo columns
+      sc[r] = 4 * kq + r < R.nval ? tot * scale_log2 : -INFINITY;
     }
     // online softmax for head hcol
-    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = max_xor32(max_xor16(mx));
     const float m_new = fmaxf(m_run, mx);
     const bool none = m_new == -INFINITY;
     const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
     float psum = 0.f;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = none ? 0.f : fast_exp2(sc[tt][r] - m_new);
-        sc[tt][r] = p;
-        psum += p;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const float p = none ? 0.f : fast_exp2(sc[r] - m_new);
+      sc[r] = p;
+      psum += p;
+    }
     l_lane = l_lane * alpha + psum;
     m_run = m_new;
     if (c16 < 8) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p_lds[wave][16 * tt + 4 * kq + r][c16] = sc[tt][r];
+      for (int r = 0; r < 4; ++r) p_lds[wave][4 * kq + r][c16] = sc[r];
       if (kq == 0) a_lds[wave][c16] = alpha;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -224,7 +288,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
       *reinterpret_cast<float4*>(pv) = *reinterpret_cast<const float4*>(&p_lds[wave][t][0]);
       *reinterpret_cast<float4*>(pv + 4) = *reinterpret_cast<const float4*>(&p_lds[wave][t][4]);
       float v[8];
-      bf16x8_to_f32(vr[jj], v);
+      bf16x8_to_f32(R.v[jj], v);
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -233,104 +297,130 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
+  };
 
-  // wave totals: l over the four k-groups, o over the VTPI token phases
-  float l_w = l_lane + __shfl_xor(l_lane, 16, kWave);
-  l_w += __shfl_xor(l_w, 32, kWave);
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float v = o_acc[g][i];
-#pragma unroll
-      for (int o = VLPR; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
-      o_acc[g][i] = v;
-    }
-  if (vts == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      *reinterpret_cast<float4*>(&o_red[wave][g][8 * vcg]) =
-          make_float4(o_acc[g][0], o_acc[g][1], o_acc[g][2], o_acc[g][3]);
-      *reinterpret_cast<float4*>(&o_red[wave][g][8 * vcg + 4]) =
-          make_float4(o_acc[g][4], o_acc[g][5], o_acc[g][6], o_acc[g][7]);
-    }
-  }
-  if (lane < G) {  // lane g: c16 = g, kq = 0
-    ml_red[wave][lane][0] = m_run;
-    ml_red[wave][lane][1] = l_w;
-  }
-  __syncthreads();
-
-  // combine the 4 waves and write this chunk's partial
-  const Partials part = partial_ptrs(part_base, pairs, nchunks, G, D);
-  const size_t slot = ((size_t)pair * nchunks + chunk) * G;
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-    const int g = idx / D, c = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, ml_red[w][g][0]);
-    float acc = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) {
-        const float mw = ml_red[w][g][0];
-        if (mw != -INFINITY) acc += fast_exp2(mw - M) * o_red[w][g][c];
+  int cur_pair = -1;
+  int start_pair = pair_of(pfx, npairs, b0);
+  reset();
+  for (int wb = b0; wb < b1; wb += kWave) {
+    // window: lane j looks up block wb + j (pair, list entry, page, valid tokens)
+    const int nw = min(kWave, b1 - wb);
+    {
+      const int g = wb + lane;
+      int p = start_pair;
+      if (lane < nw) {
+        while (pfx[p + 1] <= g) ++p;
+        const int pos = g - pfx[p];
+        const int blk = gpu_blocks[(size_t)p * list_stride + pos];
+        const int len = seq_lens[p / Hkv];
+        w_page = table[(size_t)p * max_blocks + blk];
+        w_nval = min(BS, len - blk * BS);
+      } else {
+        w_page = -1;
+        w_nval = 0;
       }
+      w_pair = p;
+      start_pair = __builtin_amdgcn_readlane(p, nw - 1);
     }
-    part.o[(slot + g) * D + c] = acc;
-  }
-  if (threadIdx.x < G) {
-    const int g = threadIdx.x;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, ml_red[w][g][0]);
-    float L = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) {
-        const float mw = ml_red[w][g][0];
-        if (mw != -INFINITY) L += fast_exp2(mw - M) * ml_red[w][g][1];
+    // steps of the window: (block j, half hh); a second half that holds no valid token of
+    // a partial last block is skipped
+    auto next = [&](int j, int hh, int& nj, int& nh) {
+      if (HPB == 2 && hh == 0 && __builtin_amdgcn_readlane(w_nval, j) > kStep) {
+        nj = j; nh = 1;
+      } else {
+        nj = j + 1; nh = 0;
       }
+    };
+    StepRegs ra, rb;
+    int ja = 0, ha = 0;
+    load_step(ja, ha, ra);
+    while (true) {
+      int jb, hb;
+      next(ja, ha, jb, hb);
+      if (jb < nw) load_step(jb, hb, rb);
+      const int pa = __builtin_amdgcn_readlane(w_pair, ja);
+      if (pa != cur_pair) {
+        if (cur_pair >= 0) { finalize(cur_pair); reset(); }
+        load_q(pa);
+        cur_pair = pa;
+      }
+      compute_step(ra);
+      if (jb >= nw) break;
+      next(jb, hb, ja, ha);
+      if (ja < nw) load_step(ja, ha, ra);
+      const int pb = __builtin_amdgcn_readlane(w_pair, jb);
+      if (pb != cur_pair) {
+        finalize(cur_pair);
+        reset();
+        load_q(pb);
+        cur_pair = pb;
+      }
+      compute_step(rb);
+      if (ja >= nw) break;
     }
-    part.ml[(slot + g) * 2 + 0] = M;
-    part.ml[(slot + g) * 2 + 1] = L;
   }
+  if (cur_pair >= 0) finalize(cur_pair);
 }
 
-// float32 KV: one wave per (pair, chunk); K and V blocks staged in LDS.
+// float32 KV: one wave per workgroup, the same balanced ranges, one block at a time.
 template <int D, int BS>
 __global__ __launch_bounds__(64) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k_pool,
     const float* __restrict__ v_pool, const int32_t* __restrict__ table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ gpu_blocks,
     const int32_t* __restrict__ n_gpu, int list_stride, int Hkv, int G, int max_blocks,
-    float scale_log2, int chunk_blocks, int nchunks, int pairs, float* __restrict__ part_base) {
+    int npairs, int W, float scale_log2, float* __restrict__ ws) {
   constexpr int CPL = D / kWave;  // channels per lane (1 or 2)
+  extern __shared__ int pfx[];    // [npairs + 1]
   __shared__ float qs[8][D];
   __shared__ float ks[BS][D + 1];
   __shared__ float vs[BS][D];
   __shared__ float sc[8][BS];
+  __shared__ int wave_tot[1];
   const int lane = threadIdx.x;
-  const int pair = blockIdx.y, chunk = blockIdx.x;
-  const int ng = n_gpu[pair];
-  const int e_begin = chunk * chunk_blocks;
-  if (e_begin >= ng) return;
-  const int e_end = min(ng, e_begin + chunk_blocks);
-  const int s = pair / Hkv, h = pair % Hkv;
-  const int len = seq_lens[s];
-  for (int i = lane; i < G * D; i += kWave)
-    qs[i / D][i % D] = q[((size_t)s * Hkv * G + (size_t)h * G) * D + i];
+  pair_prefix(n_gpu, npairs, pfx, wave_tot);
+  const PartialView part = partial_view(ws, npairs, W, G, D);
+  if (blockIdx.x == 0)
+    for (int i = lane; i <= npairs; i += kWave) part.pfx[i] = pfx[i];
+  const int T = pfx[npairs];
+  const int gw = blockIdx.x;
+  if (T == 0) return;
+  const int b0 = wave_start(gw, T, W), b1 = wave_start(gw + 1, T, W);
+  if (b0 >= b1) return;
   float m_run[8], l_run[8], o[8][CPL];
-  for (int g = 0; g < 8; ++g) {
-    m_run[g] = -INFINITY;
-    l_run[g] = 0.f;
-    for (int c = 0; c < CPL; ++c) o[g][c] = 0.f;
-  }
-  for (int e = e_begin; e < e_end; ++e) {
-    const int blk = gpu_blocks[(size_t)pair * list_stride + e];
-    const int page = table[(size_t)pair * max_blocks + blk];
-    const int nval = min(BS, len - blk * BS);
+  auto reset = [&]() {
+    for (int g = 0; g < 8; ++g) {
+      m_run[g] = -INFINITY;
+      l_run[g] = 0.f;
+      for (int c = 0; c < CPL; ++c) o[g][c] = 0.f;
+    }
+  };
+  auto finalize = [&](int pair) {
+    const size_t slot = (size_t)(gw + pair) * G;
+    for (int g = 0; g < G; ++g) {
+      for (int c = 0; c < CPL; ++c) part.o[(slot + g) * D + lane + kWave * c] = o[g][c];
+      if (lane == 0) {
+        part.ml[(slot + g) * 2 + 0] = m_run[g];
+        part.ml[(slot + g) * 2 + 1] = l_run[g];
+      }
+    }
+  };
+  reset();
+  int cur_pair = -1;
+  int p = pair_of(pfx, npairs, b0);
+  for (int g_blk = b0; g_blk < b1; ++g_blk) {
+    while (pfx[p + 1] <= g_blk) ++p;
+    if (p != cur_pair) {
+      if (cur_pair >= 0) { finalize(cur_pair); reset(); }
+      cur_pair = p;
+      const int s = p / Hkv, h = p % Hkv;
+      __syncthreads();
+      for (int i = lane; i < G * D; i += kWave)
+        qs[i / D][i % D] = q[((size_t)s * Hkv * G + (size_t)h * G) * D + i];
+    }
+    const int blk = gpu_blocks[(size_t)p * list_stride + (g_blk - pfx[p])];
+    const int page = table[(size_t)p * max_blocks + blk];
+    const int nval = min(BS, seq_lens[p / Hkv] - blk * BS);
     __syncthreads();
     for (int i = lane; i < BS * D; i += kWave) {
       ks[i / D][i % D] = k_pool[(size_t)page * BS * D + i];
@@ -347,38 +437,30 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
     for (int g = 0; g < G; ++g) {
       float mx = -INFINITY;
       for (int t = 0; t < BS; ++t) mx = fmaxf(mx, sc[g][t]);
-      const float m_new = fmaxf(m_run[g], mx);
-      const float alpha = fast_exp2(m_run[g] - m_new);  // m_new is finite: nval >= 1
+      const float m_new = fmaxf(m_run[g], mx);           // finite: nval >= 1
+      const float alpha = fast_exp2(m_run[g] - m_new);   // 0 on the first block
       float ps = 0.f;
       float acc[CPL];
       for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
       for (int t = 0; t < BS; ++t) {
-        const float p = fast_exp2(sc[g][t] - m_new);
-        ps += p;
-        for (int c = 0; c < CPL; ++c) acc[c] = fmaf(p, vs[t][lane + kWave * c], acc[c]);
+        const float pr = fast_exp2(sc[g][t] - m_new);
+        ps += pr;
+        for (int c = 0; c < CPL; ++c) acc[c] = fmaf(pr, vs[t][lane + kWave * c], acc[c]);
       }
       l_run[g] = l_run[g] * alpha + ps;
       for (int c = 0; c < CPL; ++c) o[g][c] = o[g][c] * alpha + acc[c];
       m_run[g] = m_new;
     }
   }
-  const Partials part = partial_ptrs(part_base, pairs, nchunks, G, D);
-  const size_t slot = ((size_t)pair * nchunks + chunk) * G;
-  for (int g = 0; g < G; ++g) {
-    for (int c = 0; c < CPL; ++c) part.o[(slot + g) * D + lane + kWave * c] = o[g][c];
-    if (lane == 0) {
-      part.ml[(slot + g) * 2 + 0] = m_run[g];
-      part.ml[(slot + g) * 2 + 1] = l_run[g];
-    }
-  }
+  if (cur_pair >= 0) finalize(cur_pair);
 }
 
-// One wave per (sequence, query head) row: combine the pair's chunk partials and, when
-// given, the host partial; write the normalised output.
+// One wave per (sequence, query head) row: combine the partials of the waves that covered
+// the pair's blocks and, when given, the host partial; write the normalised output.
 template <int D>
 __global__ __launch_bounds__(256) void reduce_kernel(
-    const float* __restrict__ part_base, int pairs, int nchunks, int chunk_blocks, int G,
-    int Hkv, int rows, const int32_t* __restrict__ n_gpu, const float* __restrict__ host_o,
+    const float* __restrict__ ws, int npairs, int W, int G, int Hkv, int rows,
+    const int32_t* __restrict__ n_gpu, const float* __restrict__ host_o,
     const float* __restrict__ host_m, const float* __restrict__ host_l,
     const int32_t* __restrict__ n_cpu, float* __restrict__ o, float* __restrict__ m,
     float* __restrict__ l) {
@@ -389,12 +471,20 @@ __global__ __launch_bounds__(256) void reduce_kernel(
   const int Hq = Hkv * G;
   const int s = row / Hq, qh = row % Hq;
   const int pair = s * Hkv + qh / G, g = qh % G;
-  const int nch = (n_gpu[pair] + chunk_blocks - 1) / chunk_blocks;
-  const Partials part = partial_ptrs(const_cast<float*>(part_base), pairs, nchunks, G, D);
-  const size_t slot0 = (size_t)pair * nchunks * G + g;
-
+  const PartialView part = partial_view(const_cast<float*>(ws), npairs, W, G, D);
+  const int ng = n_gpu[pair];
+  int w_lo = 0, w_hi = -1;
+  if (ng > 0) {
+    const int P = part.pfx[pair], Tn = part.pfx[npairs];
+    w_lo = wave_of(P, Tn, W);
+    w_hi = wave_of(P + ng - 1, Tn, W);
+  }
+  // waves with an empty range (possible when W > T) own no block and wrote no partial
+  const int T = part.pfx[npairs];
+  auto covers = [&](int w) { return wave_start(w, T, W) < wave_start(w + 1, T, W); };
   float M = -INFINITY;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, part.ml[(slot0 + (size_t)c * G) * 2]);
+  for (int w = w_lo; w <= w_hi; ++w)
+    if (covers(w)) M = fmaxf(M, part.ml[((size_t)(w + pair) * G + g) * 2]);
   bool use_host = host_o != nullptr && (n_cpu == nullptr || n_cpu[pair] > 0);
   float mh = -INFINITY, lh = 0.f;
   if (use_host) {
@@ -407,21 +497,22 @@ __global__ __launch_bounds__(256) void reduce_kernel(
 #pragma unroll
   for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
   if (M != -INFINITY) {
-    for (int c = 0; c < nch; ++c) {
-      const size_t sl = slot0 + (size_t)c * G;
+    for (int w = w_lo; w <= w_hi; ++w) {
+      if (!covers(w)) continue;
+      const size_t sl = (size_t)(w + pair) * G + g;
       const float mc = part.ml[sl * 2];
       if (mc == -INFINITY) continue;
-      const float w = fast_exp2(mc - M);
-      L += w * part.ml[sl * 2 + 1];
+      const float wt = fast_exp2(mc - M);
+      L += wt * part.ml[sl * 2 + 1];
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) acc[i] = fmaf(w, part.o[sl * D + lane + kWave * i], acc[i]);
+      for (int i = 0; i < CPL; ++i) acc[i] = fmaf(wt, part.o[sl * D + lane + kWave * i], acc[i]);
     }
     if (use_host) {
-      const float w = lh * fast_exp2(mh - M);
-      L += w;
+      const float wt = lh * fast_exp2(mh - M);
+      L += wt;
 #pragma unroll
       for (int i = 0; i < CPL; ++i)
-        acc[i] = fmaf(w, host_o[(size_t)row * D + lane + kWave * i], acc[i]);
+        acc[i] = fmaf(wt, host_o[(size_t)row * D + lane + kWave * i], acc[i]);
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -468,15 +559,16 @@ template <int D, int BS>
 hipError_t attn_bf16_g(const Shape& s, const AttnPlan& p, const float* q, const void* k,
                        const void* v, const int32_t* t, const int32_t* lens,
                        const int32_t* gb, const int32_t* ng, int stride, float sl2,
-                       float* part, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  const dim3 grid(p.nchunks, s.B * s.Hkv), block(kAttnWaves * kWave);
-  const int pairs = s.B * s.Hkv;
+                       float* ws, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  const int npairs = s.B * s.Hkv;
+  const dim3 grid(p.waves / kAttnWaves), block(kAttnWaves * kWave);
+  const size_t lds = (size_t)(npairs + 1) * sizeof(int);
   // hipExtLaunchKernelGGL records the (optional) events at the kernel's own start and end
-#define SA_ATTN_CASE(GG)                                                                    \
-  case GG:                                                                                  \
-    hipExtLaunchKernelGGL((attn_bf16_kernel<D, BS, GG>), grid, block, 0, st, e0, e1, 0, q,  \
-                          (const uint16_t*)k, (const uint16_t*)v, t, lens, gb, ng, stride,   \
-                          s.Hkv, s.max_blocks, sl2, p.chunk_blocks, p.nchunks, pairs, part); \
+#define SA_ATTN_CASE(GG)                                                                     \
+  case GG:                                                                                   \
+    hipExtLaunchKernelGGL((attn_bf16_kernel<D, BS, GG>), grid, block, lds, st, e0, e1, 0, q, \
+                          (const uint16_t*)k, (const uint16_t*)v, t, lens, gb, ng, stride,    \
+                          s.Hkv, s.max_blocks, npairs, p.waves, sl2, ws);                    \
     break;
   switch (s.G) {
     SA_ATTN_CASE(1) SA_ATTN_CASE(2) SA_ATTN_CASE(3) SA_ATTN_CASE(4)
@@ -490,12 +582,13 @@ hipError_t attn_bf16_g(const Shape& s, const AttnPlan& p, const float* q, const 
 template <int D, int BS>
 hipError_t attn_f32(const Shape& s, const AttnPlan& p, const float* q, const void* k,
                     const void* v, const int32_t* t, const int32_t* lens, const int32_t* gb,
-                    const int32_t* ng, int stride, float sl2, float* part, hipStream_t st,
+                    const int32_t* ng, int stride, float sl2, float* ws, hipStream_t st,
                     hipEvent_t e0, hipEvent_t e1) {
-  const dim3 grid(p.nchunks, s.B * s.Hkv);
-  hipExtLaunchKernelGGL((attn_f32_kernel<D, BS>), grid, dim3(kWave), 0, st, e0, e1, 0, q,
-                        (const float*)k, (const float*)v, t, lens, gb, ng, stride, s.Hkv, s.G,
-                        s.max_blocks, sl2, p.chunk_blocks, p.nchunks, s.B * s.Hkv, part);
+  const int npairs = s.B * s.Hkv;
+  const size_t lds = (size_t)(npairs + 1) * sizeof(int);
+  hipExtLaunchKernelGGL((attn_f32_kernel<D, BS>), dim3(p.waves), dim3(kWave), lds, st, e0, e1,
+                        0, q, (const float*)k, (const float*)v, t, lens, gb, ng, stride, s.Hkv,
+                        s.G, s.max_blocks, npairs, p.waves, sl2, ws);
   return hipGetLastError();
 }
 
@@ -503,11 +596,13 @@ hipError_t attn_f32(const Shape& s, const AttnPlan& p, const float* q, const voi
 
 AttnPlan attn_plan(const Shape& s, int list_stride) {
   AttnPlan p;
-  // bf16: 4 waves x 4 steps of 32 tokens; float32: a few blocks per single-wave group
-  p.chunk_tokens = s.bf16 ? kAttnWaves * 4 * kStep : 4 * s.bs;
-  p.chunk_blocks = p.chunk_tokens / s.bs;
-  p.nchunks = (list_stride + p.chunk_blocks - 1) / p.chunk_blocks;
-  p.ws_bytes = (size_t)s.B * s.Hkv * p.nchunks * s.G * (s.d + 2) * sizeof(float);
+  const int npairs = s.B * s.Hkv;
+  const long most = (long)npairs * list_stride;  // upper bound of the resident selected blocks
+  int w = (int)(most < kMaxWaves ? most : kMaxWaves);
+  if (s.bf16) w = (w + kAttnWaves - 1) / kAttnWaves * kAttnWaves;
+  p.waves = w < 1 ? 1 : w;
+  p.ws_bytes = prefix_bytes(npairs) +
+               (size_t)(p.waves + npairs) * s.G * (s.d + 2) * sizeof(float);
   return p;
 }
 
@@ -534,15 +629,15 @@ hipError_t launch_reduce(const Shape& s, const AttnPlan& plan, const int32_t* n_
                          const float* host_l, const int32_t* n_cpu, float* o, float* m,
                          float* l, hipStream_t stream) {
   const int rows = s.B * s.Hq;
+  const int npairs = s.B * s.Hkv;
   const dim3 grid((rows + 3) / 4), block(256);
   if (s.d == 128)
-    hipLaunchKernelGGL(reduce_kernel<128>, grid, block, 0, stream, partials, s.B * s.Hkv,
-                       plan.nchunks, plan.chunk_blocks, s.G, s.Hkv, rows, n_gpu, host_o,
-                       host_m, host_l, n_cpu, o, m, l);
+    hipLaunchKernelGGL(reduce_kernel<128>, grid, block, 0, stream, partials, npairs,
+                       plan.waves, s.G, s.Hkv, rows, n_gpu, host_o, host_m, host_l, n_cpu, o,
+                       m, l);
   else
-    hipLaunchKernelGGL(reduce_kernel<64>, grid, block, 0, stream, partials, s.B * s.Hkv,
-                       plan.nchunks, plan.chunk_blocks, s.G, s.Hkv, rows, n_gpu, host_o,
-                       host_m, host_l, n_cpu, o, m, l);
+    hipLaunchKernelGGL(reduce_kernel<64>, grid, block, 0, stream, partials, npairs, plan.waves,
+                       s.G, s.Hkv, rows, n_gpu, host_o, host_m, host_l, n_cpu, o, m, l);
   return hipGetLastError();
 }
 

@@ -70,11 +70,50 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// ---- wavefront reductions ----------------------------------------------------------------
+// ---- cross-lane exchange without LDS ------------------------------------------------------
+// DPP row permutations (within 16-lane rows) and the gfx950 permlane swaps (across rows).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within each 8
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within each 16
+constexpr int kDppRor8 = 0x128;       // lane i <- lane i^8 within each 16
+
+__device__ __forceinline__ float xor8(float v) { return dpp<kDppRor8>(v); }
+
+// {v of this lane, v of lane^16} summed / maxed, via v_permlane16_swap
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+// {v of this lane, v of lane^32}, via v_permlane32_swap
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+// Sum within aligned groups of W lanes (W a power of two <= 64); every lane gets its
+// group's sum.
 template <int W>
-__device__ __forceinline__ float group_sum(float v) {  // sum within aligned groups of W lanes
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+__device__ __forceinline__ float group_sum(float v) {
+  if (W >= 2) v += dpp<kDppXor1>(v);
+  if (W >= 4) v += dpp<kDppXor2>(v);
+  if (W >= 8) v += dpp<kDppHalfMirror>(v);
+  if (W >= 16) v += dpp<kDppMirror>(v);
+  if (W >= 32) v = sum_xor16(v);
+  if (W >= 64) v = sum_xor32(v);
   return v;
 }
 

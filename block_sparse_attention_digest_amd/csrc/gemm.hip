@@ -2,87 +2,103 @@
 // arXiv:2603.27138, HTML Sec. 3.3; Algorithm 1], and the true query Q^i = W_Q^i X^i, as a
 // skinny GEMM q[m][n] = x[m][k] . w[n][k]^T with bf16 operands and float32 accumulation.
 //
-// m is the batch (8..40 rows), so the product is bound by streaming W from HBM, not by
-// the matrix cores: each workgroup owns a 64-column tile of n (16 columns per wave) and a
-// slice of k, and computes every row of x against it with v_mfma_f32_16x16x32_bf16.  W is
-// read once, 16 contiguous bytes per lane per k-step, eight k-steps in flight per wave.
-// Several k-slices per tile give enough workgroups to cover the chip; their float32
-// partials are summed in a fixed order by a second kernel, so results are deterministic.
-// Two weight matrices that share x (Q^i and Q_pred^{i+1}) run as one launch.
+// m is the batch (8..40 rows), so the product is bound by streaming W from HBM, not by the
+// matrix cores.  A workgroup of 8 waves owns 128 columns of n (16 per wave) and one slice
+// of k.  The slice of x it needs (at most 64 rows) is staged once in LDS and shared by the
+// 8 waves, so HBM and L2 carry W once and x only once per workgroup.  Each wave streams its
+// W rows with 16-byte loads straight into v_mfma_f32_16x16x32_bf16 B operands, keeping the
+// next 8 k-steps of W in flight (double-buffered registers) while the current 8 are
+// multiplied.  Several k-slices per column tile give enough workgroups to cover the chip;
+// their float32 partials are summed in slice order by a second kernel, so results are
+// deterministic.  Two weight matrices that share x (Q^i and Q_pred^{i+1}) run as one launch.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace sa {
 namespace {
 
-constexpr int kTileN = 64;  // columns per workgroup (4 waves x 16)
-constexpr int kUnroll = 8;  // k-steps of 32 loaded ahead
+constexpr int kWaves = 8;
+constexpr int kTileN = 16 * kWaves;  // columns per workgroup
+constexpr int kGroup = 8;            // k-steps (of 32) per register buffer
+constexpr int kLdsBytes = 64 * 1024;
+constexpr int kPad = 8;              // bf16 elements of padding per LDS row
 
 template <int MT>
-__global__ __launch_bounds__(256) void gemm_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ x,
                                                    const uint16_t* __restrict__ w0,
                                                    const uint16_t* __restrict__ w1, int m,
                                                    int n, int k, int kslice, int n_total,
                                                    float* __restrict__ out0,
                                                    float* __restrict__ out1, int ksplit,
                                                    float* __restrict__ partials) {
+  extern __shared__ uint16_t xs[];  // [16*MT][kslice + kPad]
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int col_g = blockIdx.x * kTileN + wave * 16 + (lane % 16);  // in [0, n_total)
   const int prob = col_g >= n ? 1 : 0;
-  const int col = col_g - prob * n;
+  const int col = min(col_g - prob * n, n - 1);  // clamped for waves past n_total
   const uint16_t* w = prob ? w1 : w0;
   const int ks = blockIdx.y;
   const int k0 = ks * kslice;
   const int k1 = min(k, k0 + kslice);
+  const int klen = k1 - k0;
   const int row0 = blockIdx.z * 16 * MT;
-  const int kq = 8 * (lane / 16);  // this lane's 8 k-values within a 32-wide step
+  const int ldx = kslice + kPad;
 
-  const uint16_t* wrow = w + (size_t)col * k + kq;
-  const uint16_t* xrow[MT];
-  bool xvalid[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int r = row0 + 16 * t + (lane % 16);
-    xvalid[t] = r < m;
-    xrow[t] = x + (size_t)(xvalid[t] ? r : 0) * k + kq;
+  // stage x[row0 .. row0+16MT)[k0 .. k1) in LDS (rows past m are zero)
+  {
+    const int chunks_per_row = klen / 8;
+    const int total = 16 * MT * chunks_per_row;
+    for (int c = threadIdx.x; c < total; c += blockDim.x) {
+      const int r = c / chunks_per_row, q8 = c % chunks_per_row;
+      const int gr = row0 + r;
+      const uint4 v = gr < m ? *reinterpret_cast<const uint4*>(x + (size_t)gr * k + k0 + 8 * q8)
+                             : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(xs + r * ldx + 8 * q8) = v;
+    }
   }
+
+  const int kq = 8 * (lane / 16);  // this lane's 8 k-values within a 32-wide step
+  const uint16_t* wrow = w + (size_t)col * k + k0 + kq;
+  const int nsteps = klen / 32;
 
   floatx4 acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  int kk = k0;
-  for (; kk + 32 * kUnroll <= k1; kk += 32 * kUnroll) {
-    uint4 bw[kUnroll];
+  uint4 wa[kGroup], wb[kGroup];
+  auto load_group = [&](uint4* dst, int s0) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      bw[u] = *reinterpret_cast<const uint4*>(wrow + kk + 32 * u);
-    uint4 ax[kUnroll][MT];
+    for (int u = 0; u < kGroup; ++u)
+      dst[u] = s0 + u < nsteps ? *reinterpret_cast<const uint4*>(wrow + 32 * (s0 + u))
+                               : make_uint4(0, 0, 0, 0);
+  };
+  auto mma_group = [&](const uint4* src, int s0) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < kGroup; ++u) {
+      if (s0 + u < nsteps) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, src[u]);
 #pragma unroll
-      for (int t = 0; t < MT; ++t)
-        ax[u][t] = xvalid[t] ? *reinterpret_cast<const uint4*>(xrow[t] + kk + 32 * u)
-                             : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const bf16x8 b = __builtin_bit_cast(bf16x8, bw[u]);
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ax[u][t]),
-                                                         b, acc[t], 0, 0, 0);
+        for (int t = 0; t < MT; ++t) {
+          const uint4 a = *reinterpret_cast<const uint4*>(
+              xs + (16 * t + (lane % 16)) * ldx + 32 * (s0 + u) + kq);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b,
+                                                           acc[t], 0, 0, 0);
+        }
+      }
     }
-  }
-  for (; kk < k1; kk += 32) {
-    const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(wrow + kk));
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const uint4 a = xvalid[t] ? *reinterpret_cast<const uint4*>(xrow[t] + kk)
-                                : make_uint4(0, 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b,
-                                                       acc[t], 0, 0, 0);
-    }
+  };
+
+  // a wave whose 16 columns lie past n_total (last tile) only helps stage x
+  const bool live = blockIdx.x * kTileN + wave * 16 < n_total;
+  if (live) load_group(wa, 0);
+  __syncthreads();  // x slice staged
+  if (!live) return;
+  for (int s0 = 0; s0 < nsteps; s0 += 2 * kGroup) {
+    load_group(wb, s0 + kGroup);
+    mma_group(wa, s0);
+    if (s0 + 2 * kGroup < nsteps) load_group(wa, s0 + 2 * kGroup);
+    mma_group(wb, s0 + kGroup);
   }
 
   // acc[t][r] holds row row0 + 16t + 4*(lane/16) + r, column col_g
@@ -125,17 +141,22 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restric
   *reinterpret_cast<float4*>(out + (size_t)row * n + (col_g - prob * n)) = s;
 }
 
+int row_tiles(int m) { return m >= 64 ? 4 : (m + 15) / 16; }
+
 }  // namespace
 
 GemmPlan gemm_plan(int m, int n_total, int k) {
-  const int tiles = n_total / kTileN;
+  const int mt = row_tiles(m);
+  const int groups = (n_total + kTileN - 1) / kTileN;
   const int row_groups = (m + 63) / 64;
-  const int ksteps64 = k / 64;
-  int ksplit = (768 + tiles * row_groups - 1) / (tiles * row_groups);
+  // k-slice: a multiple of 64 whose x tile fits the LDS budget
+  const int max_slice = ((kLdsBytes / (16 * mt * 2) - kPad) / 64) * 64;
+  int ksplit = (640 + groups * row_groups - 1) / (groups * row_groups);  // ~640+ workgroups
   ksplit = ksplit < 1 ? 1 : ksplit;
-  const int max_split = ksteps64 / 4 > 0 ? ksteps64 / 4 : 1;  // slices of >= 256 columns
-  ksplit = ksplit > max_split ? max_split : ksplit;
-  const int kslice = 64 * ((ksteps64 + ksplit - 1) / ksplit);
+  const int ksteps64 = k / 64;
+  if (ksplit > ksteps64) ksplit = ksteps64;
+  int kslice = 64 * ((ksteps64 + ksplit - 1) / ksplit);
+  if (kslice > max_slice) kslice = max_slice;
   ksplit = (k + kslice - 1) / kslice;
   GemmPlan p;
   p.ksplit = ksplit;
@@ -148,21 +169,22 @@ hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void
                        float* q0, const void* w1, float* q1, float* ws, const GemmPlan& plan,
                        hipStream_t stream) {
   const int n_total = n * nprob;
-  const int mt = m >= 64 ? 4 : (m + 15) / 16;
-  const dim3 grid(n_total / kTileN, plan.ksplit, (m + 63) / 64);
-  const dim3 block(256);
+  const int mt = row_tiles(m);
+  const dim3 grid((n_total + kTileN - 1) / kTileN, plan.ksplit, (m + 63) / 64);
+  const dim3 block(kWaves * kWave);
+  const size_t lds = (size_t)16 * mt * (plan.kslice + kPad) * sizeof(uint16_t);
   const uint16_t* X = (const uint16_t*)x;
   const uint16_t* W0 = (const uint16_t*)w0;
   const uint16_t* W1 = (const uint16_t*)(nprob > 1 ? w1 : w0);
   float* Q1 = nprob > 1 ? q1 : q0;
   switch (mt) {
-    case 1: hipLaunchKernelGGL(gemm_kernel<1>, grid, block, 0, stream, X, W0, W1, m, n, k,
+    case 1: hipLaunchKernelGGL(gemm_kernel<1>, grid, block, lds, stream, X, W0, W1, m, n, k,
                                plan.kslice, n_total, q0, Q1, plan.ksplit, ws); break;
-    case 2: hipLaunchKernelGGL(gemm_kernel<2>, grid, block, 0, stream, X, W0, W1, m, n, k,
+    case 2: hipLaunchKernelGGL(gemm_kernel<2>, grid, block, lds, stream, X, W0, W1, m, n, k,
                                plan.kslice, n_total, q0, Q1, plan.ksplit, ws); break;
-    case 3: hipLaunchKernelGGL(gemm_kernel<3>, grid, block, 0, stream, X, W0, W1, m, n, k,
+    case 3: hipLaunchKernelGGL(gemm_kernel<3>, grid, block, lds, stream, X, W0, W1, m, n, k,
                                plan.kslice, n_total, q0, Q1, plan.ksplit, ws); break;
-    default: hipLaunchKernelGGL(gemm_kernel<4>, grid, block, 0, stream, X, W0, W1, m, n, k,
+    default: hipLaunchKernelGGL(gemm_kernel<4>, grid, block, lds, stream, X, W0, W1, m, n, k,
                                 plan.kslice, n_total, q0, Q1, plan.ksplit, ws); break;
   }
   hipError_t e = hipGetLastError();

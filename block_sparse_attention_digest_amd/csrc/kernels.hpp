@@ -38,12 +38,10 @@ hipError_t launch_topk_split(const Shape& s, const float* scores, const int32_t*
                              int32_t* n_gpu, int32_t* cpu_blocks, int32_t* n_cpu,
                              hipStream_t stream);
 
-// ---- attention: chunk partials per (pair, chunk), then the reduction / merge per row -----
+// ---- attention: balanced waves write partials, then the reduction / merge per row -------
 struct AttnPlan {
-  int chunk_tokens;  // tokens of selected blocks handled by one workgroup
-  int chunk_blocks;  // = chunk_tokens / bs
-  int nchunks;       // ceil(list_stride / chunk_blocks)
-  size_t ws_bytes;   // partials: [B*Hkv][nchunks][G] x (d + 2) floats
+  int waves;         // W: waves in the grid; the resident selected blocks are split evenly
+  size_t ws_bytes;   // pair prefix + one partial slot per (wave + pair) and head
 };
 AttnPlan attn_plan(const Shape& s, int list_stride);
 hipError_t launch_attention(const Shape& s, const AttnPlan& plan, const float* q,

@@ -7,37 +7,50 @@
 //     sum_g max(q_gc min_c, q_gc max_c) = (sum_g max(q_gc, 0)) max_c + (sum_g min(q_gc, 0)) min_c
 //   (exact, since max_c >= min_c) -- so each digest element costs one or two FMAs.  A digest
 //   row is read by 16-byte loads across LPR lanes and reduced across them with shuffles;
-//   four loads per lane are in flight.  HBM-bound: every digest byte is read once.
-// topk_split_kernel: one workgroup per (sequence, KV head).  The scores become
-//   order-preserving 32-bit keys in LDS; an MSB-first radix select (4 passes of 8 bits)
-//   finds the exact k-th largest key; selected blocks (ties at the threshold taken in index
-//   order) are compacted in ascending order and split by the block table into the resident
-//   and offloaded lists.
+//   every load of a wave (8-16 KiB) is issued before the first is used.  HBM-bound: every
+//   digest byte is read once.
+// topk_split_kernel: one workgroup per (sequence, KV head).  A histogram of the score values
+//   over 256 equal-width buckets locates the bucket holding the k-th largest score; the few
+//   scores in that bucket are ranked exactly by (score, lower index first).  Crowded
+//   buckets (e.g. all scores equal) fall back to an exact MSB-first radix select on
+//   order-preserving 32-bit keys.  The selected blocks are compacted in ascending order and
+//   split by the block table into the resident and offloaded lists.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace sa {
 namespace {
 
-constexpr int kScoreUnroll = 4;
-constexpr int kBlocksPerWG = 256;
+constexpr int kScoreWaves = 4;
 
+// digest rows per load instruction, loads in flight per lane, blocks per workgroup
+template <typename T, int D, bool MINMAX>
+struct ScoreShape;
 template <typename T>
 struct Digest;
 template <>
-struct Digest<uint16_t> {
+struct Digest<uint16_t> {  // eight bf16 per 16-byte vector
   static constexpr int N = 8;
-  __device__ static void load(const uint16_t* p, float* f) {
-    bf16x8_to_f32(*reinterpret_cast<const uint4*>(p), f);
-  }
+  __device__ static uint4 load(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void widen(const uint4& v, float* f) { bf16x8_to_f32(v, f); }
 };
 template <>
-struct Digest<float> {
+struct Digest<float> {  // four float per 16-byte vector
   static constexpr int N = 4;
-  __device__ static void load(const float* p, float* f) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
-    f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+  __device__ static uint4 load(const float* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void widen(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
   }
+};
+
+template <typename T, int D, bool MINMAX>
+struct ScoreShape {
+  static constexpr int VEC = Digest<T>::N;
+  static constexpr int LPR = D / VEC;       // lanes per digest row
+  static constexpr int BPI = kWave / LPR;   // blocks per load instruction
+  static constexpr int U = MINMAX ? 8 : 16; // block loads in flight per lane
+  static constexpr int BPW = kScoreWaves * U * BPI;  // blocks per workgroup
 };
 
 template <typename T, int D, bool MINMAX>
@@ -46,18 +59,31 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ q,
                                                     const int32_t* __restrict__ seq_lens,
                                                     float* __restrict__ scores, int Hkv, int G,
                                                     int bs, int max_blocks) {
-  constexpr int VEC = Digest<T>::N;
-  constexpr int LPR = D / VEC;       // lanes per digest row
-  constexpr int BPI = kWave / LPR;   // blocks per load instruction
+  using S = ScoreShape<T, D, MINMAX>;
+  constexpr int VEC = S::VEC, LPR = S::LPR, BPI = S::BPI, U = S::U;
   constexpr int ROW = MINMAX ? 2 * D : D;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int pair = blockIdx.y;
   const int s = pair / Hkv, h = pair % Hkv;
   const int nb = (seq_lens[s] + bs - 1) / bs;
-  const int wg_b0 = blockIdx.x * kBlocksPerWG;
+  const int wg_b0 = blockIdx.x * S::BPW;
   if (wg_b0 >= nb) return;
   const int cg = lane % LPR, bi = lane / LPR;
+
+  // block indices of this lane's loads; all of them are issued before any is used
+  int bidx[U];
+  uint4 raw[U][MINMAX ? 2 : 1];
+  const T* base = dig + (size_t)pair * max_blocks * ROW + cg * VEC;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int b = wg_b0 + (u * kScoreWaves + wave) * BPI + bi;
+    bidx[u] = b;
+    if (b < nb) {
+      raw[u][0] = Digest<T>::load(base + (size_t)b * ROW);
+      if (MINMAX) raw[u][MINMAX ? 1 : 0] = Digest<T>::load(base + (size_t)b * ROW + D);
+    }
+  }
 
   // per-channel coefficients of this lane's VEC channels
   float ca[VEC], cb[VEC];
@@ -73,39 +99,27 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ q,
     }
   }
 
-  const T* base = dig + (size_t)pair * max_blocks * ROW + cg * VEC;
   float* out = scores + (size_t)pair * max_blocks;
-  constexpr int kWaves = 4;
-  constexpr int kPerIter = kWaves * kScoreUnroll * BPI;
-  for (int it0 = wg_b0; it0 < min(nb, wg_b0 + kBlocksPerWG); it0 += kPerIter) {
-    float vals[kScoreUnroll][MINMAX ? 2 : 1][VEC];
-    int bidx[kScoreUnroll];
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-      const int b = it0 + (u * kWaves + wave) * BPI + bi;
-      bidx[u] = b;
-      if (b < nb) {
-        Digest<T>::load(base + (size_t)b * ROW, vals[u][0]);
-        if (MINMAX) Digest<T>::load(base + (size_t)b * ROW + D, vals[u][MINMAX ? 1 : 0]);
+  for (int u = 0; u < U; ++u) {
+    float acc = 0.f;
+    if (bidx[u] < nb) {
+      float lo_or_mean[VEC];
+      Digest<T>::widen(raw[u][0], lo_or_mean);
+      if (MINMAX) {  // digest row 0 = min, row 1 = max
+        float hi[VEC];
+        Digest<T>::widen(raw[u][MINMAX ? 1 : 0], hi);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc = fmaf(ca[i], hi[i], acc);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc = fmaf(cb[i], lo_or_mean[i], acc);
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc = fmaf(ca[i], lo_or_mean[i], acc);
       }
     }
-#pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-      float acc = 0.f;
-      if (bidx[u] < nb) {
-        if (MINMAX) {
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) acc = fmaf(ca[i], vals[u][MINMAX ? 1 : 0][i], acc);
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) acc = fmaf(cb[i], vals[u][0][i], acc);
-        } else {
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) acc = fmaf(ca[i], vals[u][0][i], acc);
-        }
-      }
-      acc = group_sum<LPR>(acc);
-      if (cg == 0 && bidx[u] < nb) out[bidx[u]] = acc;
-    }
+    acc = group_sum<LPR>(acc);
+    if (cg == 0 && bidx[u] < nb) out[bidx[u]] = acc;
   }
 }
 
@@ -125,69 +139,155 @@ __device__ __forceinline__ uint32_t block_scan_incl(uint32_t v, uint32_t* tmp) {
   return v + add;
 }
 
+constexpr int kMaxCand = 256;  // boundary-bucket candidates ranked directly
+constexpr uint8_t kSelected = 1, kResident = 2;  // per-block flag bits
+
 __global__ __launch_bounds__(256) void topk_split_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int bs,
     int max_blocks, int Hkv, int top_k, const int32_t* __restrict__ table,
     int32_t* __restrict__ gpu_blocks, int32_t* __restrict__ n_gpu,
     int32_t* __restrict__ cpu_blocks, int32_t* __restrict__ n_cpu) {
   extern __shared__ uint32_t smem[];
-  uint32_t* keys = smem;                                    // [max_blocks]
+  uint32_t* keys = smem;                                          // [max_blocks]
   uint8_t* flag = reinterpret_cast<uint8_t*>(smem + max_blocks);  // [max_blocks]
   __shared__ uint32_t hist[256];
   __shared__ uint32_t tmp[4];
-  __shared__ uint32_t sel_digit, sel_remaining, tot_res, tot_off;
+  __shared__ float red_lo[4], red_hi[4];
+  __shared__ uint32_t cand_key[kMaxCand];
+  __shared__ int cand_idx[kMaxCand];
+  __shared__ uint32_t sel_digit, sel_remaining, sel_count, ncand, tot_res, tot_off;
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int pair = blockIdx.x;
   const int s = pair / Hkv;
   const int nb = (seq_lens[s] + bs - 1) / bs;
-  const int ks = min(top_k, nb);
+  const uint32_t ks = (uint32_t)min(top_k, nb);
   const float* sc = scores + (size_t)pair * max_blocks;
-  for (int i = tid; i < nb; i += 256) keys[i] = order_key(sc[i]);
 
-  // radix select of the ks-th largest key
-  uint32_t prefix = 0, mask = 0, remaining = (uint32_t)ks;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
-    __syncthreads();
+  // keys and residency bits in LDS (scores and block table read together, coalesced), and
+  // the range of the scores
+  const int32_t* trow = table + (size_t)pair * max_blocks;
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll 8
+  for (int i = tid; i < nb; i += 256) {
+    const float v = sc[i];
+    const int32_t page = trow[i];
+    keys[i] = order_key(v);
+    flag[i] = page >= 0 ? kResident : 0;
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    lo = fminf(lo, __shfl_xor(lo, o, kWave));
+    hi = fmaxf(hi, __shfl_xor(hi, o, kWave));
+  }
+  if (lane == 0) { red_lo[wave] = lo; red_hi[wave] = hi; }
+  hist[tid] = 0;
+  if (tid == 0) ncand = 0;
+  __syncthreads();
+  lo = fminf(fminf(red_lo[0], red_lo[1]), fminf(red_lo[2], red_lo[3]));
+  hi = fmaxf(fmaxf(red_hi[0], red_hi[1]), fmaxf(red_hi[2], red_hi[3]));
+  const float span = hi - lo;
+  const bool bucketed = span > 0.f && span < INFINITY;
+  const float to_bucket = bucketed ? 256.f / span : 0.f;
+
+  // Fast path: a histogram of the score VALUE over 256 equal-width buckets.  The map
+  // v -> (v - lo) * 256 / span is monotone, so every block of a higher bucket outscores
+  // every block of a lower one; the k-th largest lies in the bucket B found by a suffix
+  // count, and only B's few members need an exact (score, index) ranking.
+  uint32_t B = 0, r = 0, cnt = 0xffffffffu;
+  if (bucketed) {
     for (int i = tid; i < nb; i += 256) {
-      const uint32_t kv = keys[i];
-      if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1u);
+      const int b = min(255, (int)((sc[i] - lo) * to_bucket));
+      atomicAdd(&hist[b], 1u);
     }
     __syncthreads();
-    const uint32_t c = hist[255 - tid];           // thread 0 holds the highest digit
-    const uint32_t cge = block_scan_incl(c, tmp);  // keys with digit >= 255 - tid
-    const uint32_t cgt = cge - c;                  // keys with digit >  255 - tid
-    if (cgt < remaining && cge >= remaining) {
+    const uint32_t c = hist[255 - tid];
+    const uint32_t cge = block_scan_incl(c, tmp);
+    const uint32_t cgt = cge - c;
+    if (cgt < ks && cge >= ks) {
       sel_digit = 255u - (uint32_t)tid;
-      sel_remaining = remaining - cgt;
+      sel_remaining = ks - cgt;
+      sel_count = c;
     }
     __syncthreads();
-    prefix |= sel_digit << shift;
-    mask |= 255u << shift;
-    remaining = sel_remaining;
+    B = sel_digit;
+    r = sel_remaining;
+    cnt = sel_count;
+  }
+  if (cnt <= (uint32_t)kMaxCand) {
+    for (int i = tid; i < nb; i += 256) {
+      const uint32_t b = (uint32_t)min(255, (int)((sc[i] - lo) * to_bucket));
+      if (b > B) flag[i] |= kSelected;
+      if (b == B) {
+        const uint32_t pos = atomicAdd(&ncand, 1u);
+        cand_key[pos] = keys[i];
+        cand_idx[pos] = i;
+      }
+    }
+    __syncthreads();
+    for (uint32_t c = tid; c < cnt; c += 256) {
+      const uint32_t key = cand_key[c];
+      const int idx = cand_idx[c];
+      uint32_t rank = 0;
+      for (uint32_t j = 0; j < cnt; ++j) {
+        const uint32_t kj = cand_key[j];
+        rank += kj > key || (kj == key && cand_idx[j] < idx);
+      }
+      if (rank < r) flag[idx] |= kSelected;
+    }
+    __syncthreads();
+  } else {
+    // General path (all scores equal, or a crowded bucket): exact radix select of the
+    // ks-th largest key, 8 bits per pass from the top.
+    uint32_t prefix = 0, mask = 0, remaining = ks;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      hist[tid] = 0;
+      __syncthreads();
+      for (int i = tid; i < nb; i += 256) {
+        const uint32_t kv = keys[i];
+        if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      const uint32_t c = hist[255 - tid];
+      const uint32_t cge = block_scan_incl(c, tmp);
+      const uint32_t cgt = cge - c;
+      if (cgt < remaining && cge >= remaining) {
+        sel_digit = 255u - (uint32_t)tid;
+        sel_remaining = remaining - cgt;
+      }
+      __syncthreads();
+      prefix |= sel_digit << shift;
+      mask |= 255u << shift;
+      remaining = sel_remaining;
+      __syncthreads();
+    }
+    const uint32_t thr = prefix;         // the ks-th largest key
+    const uint32_t take_eq = remaining;  // keys equal to thr that are selected
+    const int per = (nb + 255) / 256;
+    const int i0 = min(nb, tid * per), i1 = min(nb, i0 + per);
+    uint32_t ties = 0;
+    for (int i = i0; i < i1; ++i) ties += keys[i] == thr;
+    const uint32_t tie_base = block_scan_incl(ties, tmp) - ties;
+    uint32_t seen = 0;
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t kv = keys[i];
+      bool sel = kv > thr;
+      if (kv == thr) { sel = tie_base + seen < take_eq; ++seen; }
+      if (sel) flag[i] |= kSelected;
+    }
     __syncthreads();
   }
-  const uint32_t thr = prefix;   // the ks-th largest key
-  const uint32_t take_eq = remaining;  // how many keys equal to thr are selected
 
-  // contiguous index range of this thread
+  // ascending compaction of the selected blocks, split by residency
   const int per = (nb + 255) / 256;
   const int i0 = min(nb, tid * per), i1 = min(nb, i0 + per);
-  uint32_t ties = 0;
-  for (int i = i0; i < i1; ++i) ties += keys[i] == thr;
-  const uint32_t tie_base = block_scan_incl(ties, tmp) - ties;
-  uint32_t seen = 0, cnt_res = 0, cnt_off = 0;
-  const int32_t* trow = table + (size_t)pair * max_blocks;
+  uint32_t cnt_res = 0, cnt_off = 0;
   for (int i = i0; i < i1; ++i) {
-    const uint32_t kv = keys[i];
-    bool sel = kv > thr;
-    if (kv == thr) { sel = tie_base + seen < take_eq; ++seen; }
-    uint8_t f = 0;
-    if (sel) {
-      if (trow[i] >= 0) { f = 1; ++cnt_res; } else { f = 2; ++cnt_off; }
-    }
-    flag[i] = f;
+    const uint8_t f = flag[i];
+    cnt_res += f == (kSelected | kResident);
+    cnt_off += f == kSelected;
   }
   const uint32_t packed = cnt_res | (cnt_off << 16);
   const uint32_t incl = block_scan_incl(packed, tmp);
@@ -197,8 +297,8 @@ __global__ __launch_bounds__(256) void topk_split_kernel(
   int32_t* crow = cpu_blocks + (size_t)pair * top_k;
   for (int i = i0; i < i1; ++i) {
     const uint8_t f = flag[i];
-    if (f == 1) grow[pos_res++] = i;
-    else if (f == 2) crow[pos_off++] = i;
+    if (f == (kSelected | kResident)) grow[pos_res++] = i;
+    else if (f == kSelected) crow[pos_off++] = i;
   }
   __syncthreads();
   const int nr = (int)tot_res, no = (int)tot_off;
@@ -210,7 +310,9 @@ __global__ __launch_bounds__(256) void topk_split_kernel(
 template <typename T, int D>
 hipError_t score_typed(const Shape& s, bool minmax, const float* q, const void* dig,
                        const int32_t* lens, float* scores, hipStream_t st) {
-  const dim3 grid((s.max_blocks + kBlocksPerWG - 1) / kBlocksPerWG, s.B * s.Hkv);
+  const int bpw_mean = ScoreShape<T, D, false>::BPW, bpw_mm = ScoreShape<T, D, true>::BPW;
+  const int bpw = minmax ? bpw_mm : bpw_mean;
+  const dim3 grid((s.max_blocks + bpw - 1) / bpw, s.B * s.Hkv);
   if (minmax)
     hipLaunchKernelGGL((score_kernel<T, D, true>), grid, dim3(256), 0, st, q, (const T*)dig,
                        lens, scores, s.Hkv, s.G, s.bs, s.max_blocks);

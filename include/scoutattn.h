@@ -63,7 +63,8 @@ typedef enum { SA_DIGEST_MEAN = 0, SA_DIGEST_MINMAX = 1 } sa_digest_kind;
 
 /* Problem shape.  Supported: head_dim in {64, 128}; block_size in {16, 32};
  * num_q_heads % num_kv_heads == 0 with G = num_q_heads / num_kv_heads in [1, 8];
- * 1 <= max_blocks <= 8192; num_pages >= 1; kv_dtype SA_F32 or SA_BF16. */
+ * 1 <= max_blocks <= 8192; batch * num_kv_heads <= 8192; num_pages >= 1; kv_dtype SA_F32
+ * or SA_BF16. */
 typedef struct {
   int32_t batch;         /* B                                                     */
   int32_t num_q_heads;   /* Hq                                                    */
