@@ -96,17 +96,16 @@ sa_status check_kind(sa_digest_kind k) {
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace of selection + attention: scores, then chunk partials.
+// Workspace of selection + attention: the attention partials (selection needs none).
 struct Layout {
-  size_t scores, parts, total;
+  size_t parts, total;
   sa::AttnPlan plan;
 };
 Layout layout(const sa::Shape& s, int top_k) {
   Layout L;
   L.plan = sa::attn_plan(s, top_k);
-  L.scores = 0;
-  L.parts = align_up((size_t)s.B * s.Hkv * s.max_blocks * sizeof(float));
-  L.total = L.parts + align_up(L.plan.ws_bytes);
+  L.parts = 0;
+  L.total = align_up(L.plan.ws_bytes);
   return L;
 }
 
@@ -137,15 +136,15 @@ sa_status check_scale(float scale) {
   return SA_OK;
 }
 
-// selection of one layer: scores into ws (or `scores`), then top-k + split
+// selection of one layer: scores, top-k and split in one launch (scores written out only
+// when asked for)
 sa_status run_select(const sa::Shape& s, bool minmax, const float* q, const void* digests,
                      const int32_t* seq_lens, int top_k, const int32_t* block_table,
                      int32_t* gpu_blocks, int32_t* n_gpu, int32_t* cpu_blocks, int32_t* n_cpu,
                      float* scores, hipStream_t stream) {
-  SA_HIP(sa::launch_score(s, minmax, q, digests, seq_lens, scores, stream), "score kernel");
-  SA_HIP(sa::launch_topk_split(s, scores, seq_lens, top_k, block_table, gpu_blocks, n_gpu,
-                               cpu_blocks, n_cpu, stream),
-         "top-k kernel");
+  SA_HIP(sa::launch_select(s, minmax, q, digests, seq_lens, top_k, block_table, gpu_blocks,
+                           n_gpu, cpu_blocks, n_cpu, scores, stream),
+         "select kernel");
   return SA_OK;
 }
 
@@ -249,9 +248,8 @@ sa_status sa_select_blocks(const sa_dims* dims, sa_digest_kind kind, const float
   const Layout L = layout(s, top_k);
   if (!ws || ws_bytes < L.total)
     return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, L.total);
-  float* sc = scores ? scores : (float*)((char*)ws + L.scores);
   SA_CHECK(run_select(s, kind == SA_DIGEST_MINMAX, q, digests, seq_lens, top_k, block_table,
-                      gpu_blocks, n_gpu, cpu_blocks, n_cpu, sc, stream));
+                      gpu_blocks, n_gpu, cpu_blocks, n_cpu, scores, stream));
   return ok();
 }
 
@@ -405,7 +403,6 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
   float* q_pred = (float*)(base + SL.q_pred);
   float* gemm_ws = (float*)(base + SL.gemm);
   char* sel_base = base + SL.sel;
-  float* scores = (float*)(sel_base + SL.sel_layout.scores);
   float* parts = (float*)(sel_base + SL.sel_layout.parts);
   const bool minmax = kind == SA_DIGEST_MINMAX;
   const int n = s.Hq * s.d;
@@ -445,7 +442,7 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
     // 2. the first layer selects with its own query
     if (i == 0) {
       st = run_select(s, minmax, q_true, L.digests, seq_lens, top_k, L.block_table,
-                      L.gpu_blocks, L.n_gpu, L.cpu_blocks, L.n_cpu, scores, stream);
+                      L.gpu_blocks, L.n_gpu, L.cpu_blocks, L.n_cpu, nullptr, stream);
       if (st == SA_OK) st = handoff(0);
       if (st != SA_OK) break;
     }
@@ -453,7 +450,7 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
     if (has_next) {
       const sa_layer& N = layers[i + 1];
       st = run_select(s, minmax, q_pred, N.digests, seq_lens, top_k, N.block_table,
-                      N.gpu_blocks, N.n_gpu, N.cpu_blocks, N.n_cpu, scores, stream);
+                      N.gpu_blocks, N.n_gpu, N.cpu_blocks, N.n_cpu, nullptr, stream);
       if (st == SA_OK) st = handoff(i + 1);
       if (st != SA_OK) break;
     }

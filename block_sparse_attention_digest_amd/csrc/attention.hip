@@ -14,8 +14,8 @@
 // pair's block range) and, when given, the host partial.
 //
 // bf16 path, per 16-token step of a wave (one MFMA tile: a block of 16, or half of 32):
-//   * the page and valid-token count of up to 64 upcoming blocks sit in lane registers,
-//     looked up in two dependent loads per window (list entry, then block table);
+//   * the page and valid-token count of up to 64 upcoming blocks of one pair sit in lane
+//     registers, looked up in two dependent loads per window (list entry, block table);
 //   * K (16 x d) is loaded straight into MFMA A-operand registers: lane l holds token
 //     l % 16 and 8 consecutive channels (16 bytes);
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16.  Q's columns are the G heads split into a
@@ -27,7 +27,9 @@
 //   * O += P V on the vector ALU: lane l owns 8 channels of every 4th (d = 128) token row;
 //   * steps are 16 tokens so that two of them (the one computed and the one in flight) fit
 //     the register budget of 2 waves per SIMD without spilling;
-//   * the next step's K and V are in flight while the current step is computed.
+//   * the next step's K and V are in flight while the current step is computed; all of a
+//     step's loads are issued unconditionally (clamped to valid rows) so that the waits
+//     before a step cover that step only.
 // float32 path (small fp32 workloads): the same balanced ranges, one block at a time, K and
 // V staged through LDS and plain per-lane dot products.
 //
@@ -220,7 +222,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     uint4 v[VJ];
     int nval;
   };
-  int w_pair = 0, w_page = -1, w_nval = 0;  // lane j: block (window start + j)
+  int w_page = 0, w_nval = 0;  // lane j: page and valid tokens of block (window start + j)
+  // Every load is issued unconditionally (rows clamped into the page), so the number of
+  // loads in flight is the same on every path and the compiler waits only for the step
+  // being computed, never for the one in flight.
   auto load_step = [&](int j, int hh, StepRegs& R) {
     const int page = __builtin_amdgcn_readlane(w_page, j);
     R.nval = __builtin_amdgcn_readlane(w_nval, j) - kStep * hh;  // valid tokens of the step
@@ -229,10 +234,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) R.k[ks] = *reinterpret_cast<const uint4*>(src + 32 * ks);
 #pragma unroll
-    for (int jj = 0; jj < VJ; ++jj) {  // step token t = jj * VTPI + vts
-      const int t = jj * VTPI + vts;
-      R.v[jj] = t < R.nval ? *reinterpret_cast<const uint4*>(v_pool + (row0 + t) * D + 8 * vcg)
-                           : make_uint4(0, 0, 0, 0);  // masked rows are not read (p = 0)
+    for (int jj = 0; jj < VJ; ++jj) {  // step token t = jj * VTPI + vts; masked rows get p = 0
+      const int t = max(0, min(jj * VTPI + vts, R.nval - 1));
+      R.v[jj] = *reinterpret_cast<const uint4*>(v_pool + (row0 + t) * D + 8 * vcg);
     }
   };
 
@@ -299,67 +303,39 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  int cur_pair = -1;
-  int start_pair = pair_of(pfx, npairs, b0);
-  reset();
-  for (int wb = b0; wb < b1; wb += kWave) {
-    // window: lane j looks up block wb + j (pair, list entry, page, valid tokens)
-    const int nw = min(kWave, b1 - wb);
-    {
-      const int g = wb + lane;
-      int p = start_pair;
-      if (lane < nw) {
-        while (pfx[p + 1] <= g) ++p;
-        const int pos = g - pfx[p];
-        const int blk = gpu_blocks[(size_t)p * list_stride + pos];
+  // segments: the part of this wave's range that lies in one pair
+  int p = pair_of(pfx, npairs, b0);
+  for (int seg = b0; seg < b1;) {
+    while (pfx[p + 1] <= seg) ++p;
+    const int seg_end = min(b1, pfx[p + 1]);
+    load_q(p);
+    reset();
+    for (int wb = seg; wb < seg_end; wb += kWave) {
+      // window: lane j looks up block wb + j (list entry, then page and valid tokens)
+      const int nw = min(kWave, seg_end - wb);
+      {
+        const int jl = min(lane, nw - 1);
+        const int blk = gpu_blocks[(size_t)p * list_stride + (wb + jl - pfx[p])];
         const int len = seq_lens[p / Hkv];
         w_page = table[(size_t)p * max_blocks + blk];
         w_nval = min(BS, len - blk * BS);
-      } else {
-        w_page = -1;
-        w_nval = 0;
       }
-      w_pair = p;
-      start_pair = __builtin_amdgcn_readlane(p, nw - 1);
+      // HPB steps per block; a second half holding no valid token is fully masked
+      const int nst = nw * HPB;
+      StepRegs ra, rb;
+      load_step(0, 0, ra);
+      for (int st = 0; st < nst; st += 2) {
+        const int s1 = min(st + 1, nst - 1), s2 = min(st + 2, nst - 1);
+        load_step(s1 / HPB, s1 % HPB, rb);
+        compute_step(ra);
+        if (st + 1 >= nst) break;
+        load_step(s2 / HPB, s2 % HPB, ra);
+        compute_step(rb);
+      }
     }
-    // steps of the window: (block j, half hh); a second half that holds no valid token of
-    // a partial last block is skipped
-    auto next = [&](int j, int hh, int& nj, int& nh) {
-      if (HPB == 2 && hh == 0 && __builtin_amdgcn_readlane(w_nval, j) > kStep) {
-        nj = j; nh = 1;
-      } else {
-        nj = j + 1; nh = 0;
-      }
-    };
-    StepRegs ra, rb;
-    int ja = 0, ha = 0;
-    load_step(ja, ha, ra);
-    while (true) {
-      int jb, hb;
-      next(ja, ha, jb, hb);
-      if (jb < nw) load_step(jb, hb, rb);
-      const int pa = __builtin_amdgcn_readlane(w_pair, ja);
-      if (pa != cur_pair) {
-        if (cur_pair >= 0) { finalize(cur_pair); reset(); }
-        load_q(pa);
-        cur_pair = pa;
-      }
-      compute_step(ra);
-      if (jb >= nw) break;
-      next(jb, hb, ja, ha);
-      if (ja < nw) load_step(ja, ha, ra);
-      const int pb = __builtin_amdgcn_readlane(w_pair, jb);
-      if (pb != cur_pair) {
-        finalize(cur_pair);
-        reset();
-        load_q(pb);
-        cur_pair = pb;
-      }
-      compute_step(rb);
-      if (ja >= nw) break;
-    }
+    finalize(p);
+    seg = seg_end;
   }
-  if (cur_pair >= 0) finalize(cur_pair);
 }
 
 // float32 KV: one wave per workgroup, the same balanced ranges, one block at a time.
@@ -456,7 +432,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 }
 
 // One wave per (sequence, query head) row: combine the partials of the waves that covered
-// the pair's blocks and, when given, the host partial; write the normalised output.
+// the pair's blocks and, when given, the host partial; write the normalised output.  The
+// covering waves' (m, l) are read in parallel, one per lane; o is accumulated with
+// independent loads.
 template <int D>
 __global__ __launch_bounds__(256) void reduce_kernel(
     const float* __restrict__ ws, int npairs, int W, int G, int Hkv, int rows,
@@ -473,41 +451,59 @@ __global__ __launch_bounds__(256) void reduce_kernel(
   const int pair = s * Hkv + qh / G, g = qh % G;
   const PartialView part = partial_view(const_cast<float*>(ws), npairs, W, G, D);
   const int ng = n_gpu[pair];
-  int w_lo = 0, w_hi = -1;
-  if (ng > 0) {
-    const int P = part.pfx[pair], Tn = part.pfx[npairs];
-    w_lo = wave_of(P, Tn, W);
-    w_hi = wave_of(P + ng - 1, Tn, W);
-  }
-  // waves with an empty range (possible when W > T) own no block and wrote no partial
-  const int T = part.pfx[npairs];
-  auto covers = [&](int w) { return wave_start(w, T, W) < wave_start(w + 1, T, W); };
-  float M = -INFINITY;
-  for (int w = w_lo; w <= w_hi; ++w)
-    if (covers(w)) M = fmaxf(M, part.ml[((size_t)(w + pair) * G + g) * 2]);
-  bool use_host = host_o != nullptr && (n_cpu == nullptr || n_cpu[pair] > 0);
+  const bool host_given = host_o != nullptr && (n_cpu == nullptr || n_cpu[pair] > 0);
   float mh = -INFINITY, lh = 0.f;
-  if (use_host) {
+  if (host_given) {
     mh = host_m[row] * kLog2e;
     lh = host_l[row];
-    if (!(lh > 0.f) || mh == -INFINITY) use_host = false;
-    else M = fmaxf(M, mh);
+    if (!(lh > 0.f)) mh = -INFINITY;  // an empty host partial contributes nothing
   }
+  int w_lo = 0, nslot = 0, T = 0;
+  if (ng > 0) {
+    const int P = part.pfx[pair];
+    T = part.pfx[npairs];
+    w_lo = wave_of(P, T, W);
+    nslot = wave_of(P + ng - 1, T, W) - w_lo + 1;
+  }
+  // pass 1: the maximum over the covering waves (waves with an empty range, possible when
+  // W > T, own no block and wrote no partial)
+  float M = mh;
+  for (int j0 = 0; j0 < nslot; j0 += kWave) {
+    const int w = w_lo + j0 + lane;
+    float mw = -INFINITY;
+    if (j0 + lane < nslot && wave_start(w, T, W) < wave_start(w + 1, T, W))
+      mw = part.ml[((size_t)(w + pair) * G + g) * 2];
+    M = fmaxf(M, mw);
+  }
+  M = max_xor32(max_xor16(M));
+  M = fmaxf(M, dpp<kDppMirror>(M));
+  M = fmaxf(M, dpp<kDppHalfMirror>(M));
+  M = fmaxf(M, dpp<kDppXor2>(M));
+  M = fmaxf(M, dpp<kDppXor1>(M));
   float acc[CPL], L = 0.f;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
   if (M != -INFINITY) {
-    for (int w = w_lo; w <= w_hi; ++w) {
-      if (!covers(w)) continue;
-      const size_t sl = (size_t)(w + pair) * G + g;
-      const float mc = part.ml[sl * 2];
-      if (mc == -INFINITY) continue;
-      const float wt = fast_exp2(mc - M);
-      L += wt * part.ml[sl * 2 + 1];
+    // pass 2: weights per slot (lane j of each group of 64), then o with independent loads
+    for (int j0 = 0; j0 < nslot; j0 += kWave) {
+      const int w = w_lo + j0 + lane;
+      float wt = 0.f, lw = 0.f;
+      if (j0 + lane < nslot && wave_start(w, T, W) < wave_start(w + 1, T, W)) {
+        const float mw = part.ml[((size_t)(w + pair) * G + g) * 2];
+        lw = part.ml[((size_t)(w + pair) * G + g) * 2 + 1];
+        wt = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+      }
+      L += group_sum<kWave>(wt * lw);
+      const int cnt = min(kWave, nslot - j0);
+      for (int j = 0; j < cnt; ++j) {
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), j));
+        if (wj == 0.f) continue;
+        const size_t sl = (size_t)(w_lo + j0 + j + pair) * G + g;
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) acc[i] = fmaf(wt, part.o[sl * D + lane + kWave * i], acc[i]);
+        for (int i = 0; i < CPL; ++i) acc[i] = fmaf(wj, part.o[sl * D + lane + kWave * i], acc[i]);
+      }
     }
-    if (use_host) {
+    if (host_given && mh != -INFINITY) {
       const float wt = lh * fast_exp2(mh - M);
       L += wt;
 #pragma unroll

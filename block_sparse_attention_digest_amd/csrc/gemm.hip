@@ -66,25 +66,27 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ 
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // Loads are issued unconditionally (k-steps past the slice are clamped to its last
+  // step and their B operand zeroed), so every path has the same loads in flight and the
+  // compiler waits only for the group being multiplied.
   uint4 wa[kGroup], wb[kGroup];
   auto load_group = [&](uint4* dst, int s0) {
 #pragma unroll
     for (int u = 0; u < kGroup; ++u)
-      dst[u] = s0 + u < nsteps ? *reinterpret_cast<const uint4*>(wrow + 32 * (s0 + u))
-                               : make_uint4(0, 0, 0, 0);
+      dst[u] = *reinterpret_cast<const uint4*>(wrow + 32 * min(s0 + u, nsteps - 1));
   };
   auto mma_group = [&](const uint4* src, int s0) {
 #pragma unroll
     for (int u = 0; u < kGroup; ++u) {
-      if (s0 + u < nsteps) {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, src[u]);
+      const int st = min(s0 + u, nsteps - 1);
+      const uint4 bw = s0 + u < nsteps ? src[u] : make_uint4(0, 0, 0, 0);
+      const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const uint4 a = *reinterpret_cast<const uint4*>(
-              xs + (16 * t + (lane % 16)) * ldx + 32 * (s0 + u) + kq);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b,
-                                                           acc[t], 0, 0, 0);
-        }
+      for (int t = 0; t < MT; ++t) {
+        const uint4 a = *reinterpret_cast<const uint4*>(
+            xs + (16 * t + (lane % 16)) * ldx + 32 * st + kq);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b,
+                                                         acc[t], 0, 0, 0);
       }
     }
   };
@@ -97,7 +99,8 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ 
   for (int s0 = 0; s0 < nsteps; s0 += 2 * kGroup) {
     load_group(wb, s0 + kGroup);
     mma_group(wa, s0);
-    if (s0 + 2 * kGroup < nsteps) load_group(wa, s0 + 2 * kGroup);
+    if (s0 + kGroup >= nsteps) break;
+    load_group(wa, s0 + 2 * kGroup);
     mma_group(wb, s0 + kGroup);
   }
 

@@ -30,13 +30,11 @@ hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void
                        float* q0, const void* w1, float* q1, float* ws, const GemmPlan& plan,
                        hipStream_t stream);
 
-// ---- selection: scores of every block, then top-k and the resident split per pair -------
-hipError_t launch_score(const Shape& s, bool minmax, const float* q, const void* digests,
-                        const int32_t* seq_lens, float* scores, hipStream_t stream);
-hipError_t launch_topk_split(const Shape& s, const float* scores, const int32_t* seq_lens,
-                             int top_k, const int32_t* block_table, int32_t* gpu_blocks,
-                             int32_t* n_gpu, int32_t* cpu_blocks, int32_t* n_cpu,
-                             hipStream_t stream);
+// ---- selection: scores, top-k and the resident split, one workgroup per pair ----------------
+hipError_t launch_select(const Shape& s, bool minmax, const float* q, const void* digests,
+                         const int32_t* seq_lens, int top_k, const int32_t* block_table,
+                         int32_t* gpu_blocks, int32_t* n_gpu, int32_t* cpu_blocks,
+                         int32_t* n_cpu, float* scores_or_null, hipStream_t stream);
 
 // ---- attention: balanced waves write partials, then the reduction / merge per row -------
 struct AttnPlan {
