@@ -82,7 +82,8 @@ def setup(wl, torch, B, wk):
     for i in range(L):
         off = wk.layer_offsets(wl, i, dev)
         dig = wk.draw_layer_digests(wl, i, off, dev)
-        B.sa_predict_query(ins[i]["X"], ins[i]["W"], q, gemm_ws)
+        w_packed = B.pack_weight(ins[i]["W"])  # once, at weight load
+        B.sa_predict_query(ins[i]["X"], w_packed, q, gemm_ws)
         B.sa_select_blocks(dims, "mean", q, dig, lens, kp, table_none, gb, ng, cb, nc, None,
                            sel_ws)
         sets = [[None] * Hkv for _ in range(Bsz)]
@@ -90,12 +91,14 @@ def setup(wl, torch, B, wk):
         for p in range(pairs):
             sets[p // Hkv][p % Hkv] = cbh[p]
         pool = wk.draw_layer_pool(wl, i, off, sets)
-        B.sa_build_digests(dims, "mean", pool["K"], pool["block_table"], lens, dig)
+        k_pool = B.pack_k_pages(dims, pool["K"])  # K pages in the chunk-major layout
+        del pool["K"]
+        B.sa_build_digests(dims, "mean", k_pool, pool["block_table"], lens, dig)
         hp = wk.draw_host_partials(wl, i, dev)
         del off
         layers.append(dict(
-            x=ins[i]["X"], w_q=ins[i]["W"], digests=dig, block_table=pool["block_table"],
-            k_pool=pool["K"], v_pool=pool["V"], host_o=hp["o"], host_m=hp["m"],
+            x=ins[i]["X"], w_q=w_packed, digests=dig, block_table=pool["block_table"],
+            k_pool=k_pool, v_pool=pool["V"], host_o=hp["o"], host_m=hp["m"],
             host_l=hp["l"],
             gpu_blocks=torch.empty((pairs, k), dtype=torch.int32, device=dev),
             n_gpu=torch.empty(pairs, dtype=torch.int32, device=dev),

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libscoutattn.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = 0, -1, -2, -3, -4
 SA_F32, SA_BF16 = 0, 1
 SA_DIGEST_MEAN, SA_DIGEST_MINMAX = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 KIND = {"mean": SA_DIGEST_MEAN, "minmax": SA_DIGEST_MINMAX}
 
@@ -56,6 +56,8 @@ SIGNATURES = {
     "sa_abi_version": (ctypes.c_int, []),
     "sa_last_error": (ctypes.c_char_p, []),
     "sa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "sa_pack_k_pages": (ctypes.c_int, [_D, _P, _P, _P]),
+    "sa_pack_weight": (ctypes.c_int, [_I, _I, _P, _P, _P]),
     "sa_build_digests": (ctypes.c_int, [_D, ctypes.c_int, _P, _P, _P, _P, _P]),
     "sa_predict_query_workspace_bytes": (_Z, [_I, _I, _I]),
     "sa_predict_query": (ctypes.c_int, [_I, _I, _I, _P, _P, _P, _P, _Z, _P]),
@@ -164,6 +166,36 @@ def sa_step_workspace_bytes(dims: Dims, hidden: int, top_k: int) -> int:
     return lib().sa_step_workspace_bytes(ctypes.byref(dims.c()), hidden, top_k)
 
 
+def sa_pack_k_pages(dims: Dims, k_rows, k_pool, stream=None):
+    """k_rows [P][bs][d] token-row pages -> k_pool, the chunk-major K layout."""
+    n = dims.num_pages * dims.block_size * dims.head_dim
+    _check(lib().sa_pack_k_pages(
+        ctypes.byref(dims.c()), _ptr(k_rows, dims.kv_torch, n, "k_rows"),
+        _ptr(k_pool, dims.kv_torch, n, "k_pool"), _stream(stream)))
+
+
+def pack_k_pages(dims: Dims, k_rows, stream=None):
+    """Allocate a chunk-major K pool of k_rows' size and fill it with sa_pack_k_pages."""
+    out = torch.empty_like(k_rows)
+    sa_pack_k_pages(dims, k_rows, out, stream)
+    return out
+
+
+def sa_pack_weight(w, w_packed, stream=None):
+    """w [n][k] bf16 -> w_packed (n*k bf16), the order sa_predict_query streams."""
+    n, k = w.shape
+    _check(lib().sa_pack_weight(n, k, _ptr(w, torch.bfloat16, n * k, "w"),
+                                _ptr(w_packed, torch.bfloat16, n * k, "w_packed"),
+                                _stream(stream)))
+
+
+def pack_weight(w, stream=None):
+    """Allocate a packed copy of w [n][k] bf16 (same shape, packed order)."""
+    out = torch.empty_like(w)
+    sa_pack_weight(w, out, stream)
+    return out
+
+
 def sa_build_digests(dims: Dims, kind: str, k_pool, block_table, seq_lens, digests,
                      stream=None):
     per = 2 if kind == "minmax" else 1
@@ -177,13 +209,15 @@ def sa_build_digests(dims: Dims, kind: str, k_pool, block_table, seq_lens, diges
         _ptr(digests, dims.kv_torch, n_dig, "digests"), _stream(stream)))
 
 
-def sa_predict_query(x, w, q, ws=None, stream=None):
+def sa_predict_query(x, w_packed, q, ws=None, stream=None):
+    """q [m][n] = x [m][k] w^T, w given packed by sa_pack_weight (n*k elements)."""
     m, k = x.shape
-    n = w.shape[0]
-    if w.shape[1] != k or q.numel() != m * n:
-        raise ValueError("sa_predict_query: shapes x [m][k], w [n][k], q [m][n] expected")
+    n = q.numel() // m
+    if q.numel() != m * n or w_packed.numel() != n * k:
+        raise ValueError("sa_predict_query: shapes x [m][k], w_packed n*k, q [m][n] expected")
     _check(lib().sa_predict_query(
-        m, n, k, _ptr(x, torch.bfloat16, m * k, "x"), _ptr(w, torch.bfloat16, n * k, "w"),
+        m, n, k, _ptr(x, torch.bfloat16, m * k, "x"),
+        _ptr(w_packed, torch.bfloat16, n * k, "w_packed"),
         _ptr(q, torch.float32, m * n, "q"), _ptr(ws, torch.uint8, name="ws"),
         0 if ws is None else ws.numel(), _stream(stream)))
 

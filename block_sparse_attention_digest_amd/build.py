@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libscoutattn.so")
 
-SOURCES = ["api.hip", "digest.hip", "gemm.hip", "select.hip", "attention.hip"]
+SOURCES = ["api.hip", "layout.hip", "digest.hip", "gemm.hip", "select.hip", "attention.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -182,6 +182,35 @@ const char* sa_status_string(sa_status status) {
   return "unknown status";
 }
 
+sa_status sa_pack_k_pages(const sa_dims* dims, const void* k_rows, void* k_pool,
+                          hipStream_t stream) {
+  sa::Shape s;
+  SA_CHECK(check_dims(dims, &s));
+  SA_NOT_NULL(k_rows);
+  SA_NOT_NULL(k_pool);
+  const size_t bytes = (size_t)s.P * s.bs * s.d * (s.bf16 ? 2 : 4);
+  const char* a = (const char*)k_rows;
+  const char* b = (const char*)k_pool;
+  if (a < b + bytes && b < a + bytes) return fail(SA_ERR_INVALID_ARG, "k_rows and k_pool overlap");
+  SA_HIP(sa::launch_pack_k(s, k_rows, k_pool, stream), "K pack kernel");
+  return ok();
+}
+
+sa_status sa_pack_weight(int32_t n, int32_t k, const void* w, void* w_packed,
+                         hipStream_t stream) {
+  if (n < 32 || k < 32) return fail(SA_ERR_INVALID_ARG, "weight sizes n %d, k %d must be >= 32", n, k);
+  if (n % 16 != 0 || k % 32 != 0)
+    return fail(SA_ERR_UNSUPPORTED, "weight n (%d) must be a multiple of 16 and k (%d) of 32", n, k);
+  SA_NOT_NULL(w);
+  SA_NOT_NULL(w_packed);
+  const size_t bytes = (size_t)n * k * 2;
+  const char* a = (const char*)w;
+  const char* b = (const char*)w_packed;
+  if (a < b + bytes && b < a + bytes) return fail(SA_ERR_INVALID_ARG, "w and w_packed overlap");
+  SA_HIP(sa::launch_pack_w(n, k, w, w_packed, stream), "weight pack kernel");
+  return ok();
+}
+
 sa_status sa_build_digests(const sa_dims* dims, sa_digest_kind kind, const void* k_pool,
                            const int32_t* block_table, const int32_t* seq_lens,
                            void* digests, hipStream_t stream) {
@@ -203,11 +232,13 @@ size_t sa_predict_query_workspace_bytes(int32_t m, int32_t n, int32_t k) {
   return sa::gemm_plan(m, n, k).ws_bytes;
 }
 
-sa_status sa_predict_query(int32_t m, int32_t n, int32_t k, const void* x, const void* w,
-                           float* q, void* ws, size_t ws_bytes, hipStream_t stream) {
+sa_status sa_predict_query(int32_t m, int32_t n, int32_t k, const void* x,
+                           const void* w_packed, float* q, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
   SA_CHECK(check_gemm_shape(m, n, k));
   SA_NOT_NULL(x);
-  SA_NOT_NULL(w);
+  SA_NOT_NULL(w_packed);
+  const void* w = w_packed;
   SA_NOT_NULL(q);
   const sa::GemmPlan plan = sa::gemm_plan(m, n, k);
   if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes))

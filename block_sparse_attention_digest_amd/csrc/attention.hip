@@ -17,7 +17,9 @@
 //   * the page and valid-token count of up to 64 upcoming blocks of one pair sit in lane
 //     registers, looked up in two dependent loads per window (list entry, block table);
 //   * K (16 x d) is loaded straight into MFMA A-operand registers: lane l holds token
-//     l % 16 and 8 consecutive channels (16 bytes);
+//     l % 16 and 8 consecutive channels (16 bytes).  K pages are chunk-major (the bs
+//     tokens' values of 8 channels are 16 * bs contiguous bytes), so the 16 lanes that load
+//     one chunk for 16 tokens read 256 contiguous bytes -- whole cache lines;
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16.  Q's columns are the G heads split into a
 //     bf16 high part (columns 0..7) and a bf16 low part q - hi (columns 8..15); adding the
 //     two results recovers q . k to about 2^-17 relative, so the float32 query keeps its
@@ -30,8 +32,9 @@
 //   * the next step's K and V are in flight while the current step is computed; all of a
 //     step's loads are issued unconditionally (clamped to valid rows) so that the waits
 //     before a step cover that step only.
-// float32 path (small fp32 workloads): the same balanced ranges, one block at a time, K and
-// V staged through LDS and plain per-lane dot products.
+// float32 path (small fp32 workloads): the same balanced ranges, one block at a time, K
+// (chunk-major, four channels per chunk) and V staged through LDS and plain per-lane dot
+// products.
 //
 // Internal log2 domain: logits are scaled by scale * log2(e) and exponentiated with exp2;
 // m is reported in natural-log units.
@@ -138,12 +141,15 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   __shared__ int wave_tot[kAttnWaves];
 
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
+  // wave-uniform values are made explicitly scalar so that every loop below branches on
+  // scalars: a loop exit the compiler takes for lane-divergent ends in exec-masked flow
+  // blocks, where it drains all loads in flight (vmcnt(0)) at the loop header
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   pair_prefix(n_gpu, npairs, pfx, wave_tot);
   const PartialView part = partial_view(ws, npairs, W, G, D);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= npairs; i += blockDim.x) part.pfx[i] = pfx[i];
-  const int T = pfx[npairs];
+  const int T = __builtin_amdgcn_readfirstlane(pfx[npairs]);
   const int gw = blockIdx.x * kAttnWaves + wave;
   if (T == 0) return;
   const int b0 = wave_start(gw, T, W), b1 = wave_start(gw + 1, T, W);
@@ -230,9 +236,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     const int page = __builtin_amdgcn_readlane(w_page, j);
     R.nval = __builtin_amdgcn_readlane(w_nval, j) - kStep * hh;  // valid tokens of the step
     const size_t row0 = (size_t)page * BS + kStep * hh;
-    const uint16_t* src = k_pool + (row0 + c16) * D + 8 * kq;
+    // chunk 4 ks + kq (channels 32 ks + 8 kq .. + 7) of token kStep hh + c16
+    const uint16_t* src = k_pool + (size_t)page * BS * D + ((size_t)kq * BS + kStep * hh + c16) * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) R.k[ks] = *reinterpret_cast<const uint4*>(src + 32 * ks);
+    for (int ks = 0; ks < KS; ++ks)
+      R.k[ks] = *reinterpret_cast<const uint4*>(src + (size_t)ks * 4 * BS * 8);
 #pragma unroll
     for (int jj = 0; jj < VJ; ++jj) {  // step token t = jj * VTPI + vts; masked rows get p = 0
       const int t = max(0, min(jj * VTPI + vts, R.nval - 1));
@@ -304,10 +312,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   };
 
   // segments: the part of this wave's range that lies in one pair
-  int p = pair_of(pfx, npairs, b0);
+  int p = __builtin_amdgcn_readfirstlane(pair_of(pfx, npairs, b0));
   for (int seg = b0; seg < b1;) {
-    while (pfx[p + 1] <= seg) ++p;
-    const int seg_end = min(b1, pfx[p + 1]);
+    while (__builtin_amdgcn_readfirstlane(pfx[p + 1]) <= seg) ++p;
+    const int seg_end = min(b1, __builtin_amdgcn_readfirstlane(pfx[p + 1]));
+    const int pstart = __builtin_amdgcn_readfirstlane(pfx[p]);
     load_q(p);
     reset();
     for (int wb = seg; wb < seg_end; wb += kWave) {
@@ -315,22 +324,27 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
       const int nw = min(kWave, seg_end - wb);
       {
         const int jl = min(lane, nw - 1);
-        const int blk = gpu_blocks[(size_t)p * list_stride + (wb + jl - pfx[p])];
+        const int blk = gpu_blocks[(size_t)p * list_stride + (wb + jl - pstart)];
         const int len = seq_lens[p / Hkv];
         w_page = table[(size_t)p * max_blocks + blk];
         w_nval = min(BS, len - blk * BS);
       }
-      // HPB steps per block; a second half holding no valid token is fully masked
+      // HPB steps per block; a second half holding no valid token is fully masked.  Two
+      // steps per iteration, the next one's loads in flight while one is computed.  The
+      // loads are unconditional (steps past the end re-read the last step, lines that are
+      // still cached) so every path has the same loads in flight, and the scheduling
+      // barriers keep the compiler from sinking them to their use.
       const int nst = nw * HPB;
       StepRegs ra, rb;
       load_step(0, 0, ra);
       for (int st = 0; st < nst; st += 2) {
         const int s1 = min(st + 1, nst - 1), s2 = min(st + 2, nst - 1);
         load_step(s1 / HPB, s1 % HPB, rb);
+        __builtin_amdgcn_sched_barrier(0);
         compute_step(ra);
-        if (st + 1 >= nst) break;
         load_step(s2 / HPB, s2 % HPB, ra);
-        compute_step(rb);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + 1 < nst) compute_step(rb);
       }
     }
     finalize(p);
@@ -399,7 +413,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
     const int nval = min(BS, seq_lens[p / Hkv] - blk * BS);
     __syncthreads();
     for (int i = lane; i < BS * D; i += kWave) {
-      ks[i / D][i % D] = k_pool[(size_t)page * BS * D + i];
+      // K is chunk-major: element i is channel 4 (i / 4BS) + i % 4 of token (i / 4) % BS
+      ks[(i / 4) % BS][4 * (i / (4 * BS)) + i % 4] = k_pool[(size_t)page * BS * D + i];
       vs[i / D][i % D] = v_pool[(size_t)page * BS * D + i];
     }
     __syncthreads();

@@ -1,12 +1,14 @@
 // Block digests [ScoutAttention, arXiv:2603.27138, HTML Sec. 2.2]: the mean of K over a
 // block (MoBA-style) or the channel-wise min and max of K over a block (Quest-style).
 //
-// One wavefront per (sequence, KV head, block).  The block's page [bs][d] is read with
-// 16-byte loads: LPR lanes cover one token row and the wave covers TPI rows per load, so
-// every load instruction reads TPI*d*elem contiguous bytes.  The mean accumulates in
-// float64, where sums of bf16 keys are exact, and is rounded once to the stored dtype;
-// min/max are exact in any precision.  HBM-bound: the page is read once and d (or 2d)
-// values are written.
+// One wavefront per (sequence, KV head, block).  K pages are chunk-major ([d/x][bs][x], x
+// elements per 16-byte chunk), so one page is d/x chunk rows of bs tokens each.  Each load
+// instruction reads 8 chunks x 8 tokens: lane l takes chunk 8 cg + l / 8 and token
+// 8 tg + l % 8, so every group of 8 lanes reads one whole 128-byte line.  A lane keeps its
+// chunk's running sums (or min/max) over its tokens; the 8 lanes of a chunk then combine
+// theirs with cross-lane exchanges.  The mean accumulates in float64, where sums of bf16
+// keys are exact, and is rounded once to the stored dtype; min/max are exact in any
+// precision.  HBM-bound: the page is read once and d (or 2d) values are written.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -16,18 +18,16 @@ namespace {
 template <typename T>
 struct Vec;
 template <>
-struct Vec<uint16_t> {  // eight bf16
+struct Vec<uint16_t> {  // eight bf16 per 16-byte chunk
   static constexpr int N = 8;
-  __device__ static void load(const uint16_t* p, float* f) {
-    bf16x8_to_f32(*reinterpret_cast<const uint4*>(p), f);
-  }
+  __device__ static void widen(const uint4& v, float* f) { bf16x8_to_f32(v, f); }
 };
 template <>
-struct Vec<float> {  // four float
+struct Vec<float> {  // four float per 16-byte chunk
   static constexpr int N = 4;
-  __device__ static void load(const float* p, float* f) {
-    float4 v = *reinterpret_cast<const float4*>(p);
-    f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+  __device__ static void widen(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
   }
 };
 
@@ -58,10 +58,11 @@ __global__ __launch_bounds__(256) void digest_kernel(const T* __restrict__ k_poo
                                                      const int32_t* __restrict__ seq_lens,
                                                      T* __restrict__ dig, int Hkv,
                                                      int max_blocks, long total) {
-  constexpr int VEC = Vec<T>::N;
-  constexpr int LPR = D / VEC;        // lanes per token row
-  constexpr int TPI = kWave / LPR;    // token rows per load instruction
-  constexpr int ITERS = BS / TPI;
+  constexpr int VEC = Vec<T>::N;  // elements per 16-byte chunk
+  constexpr int NC = D / VEC;     // chunks per token
+  constexpr int CG = NC / 8;      // chunk groups: 8 chunks per load instruction
+  constexpr int TG = BS / 8;      // token groups: 8 tokens (one 128-byte line) per chunk
+  static_assert(NC % 8 == 0 && BS % 8 == 0, "page shape");
   const int lane = threadIdx.x % kWave;
   const long gw = (long)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (gw >= total) return;
@@ -72,60 +73,74 @@ __global__ __launch_bounds__(256) void digest_kernel(const T* __restrict__ k_poo
   const int page = table[gw];
   if (page < 0) return;
   const int nvalid = min(BS, len - b * BS);
-  const int cg = lane % LPR, ts = lane / LPR;
-  const T* src = k_pool + (size_t)page * BS * D + cg * VEC;
+  const T* src = k_pool + (size_t)page * BS * D;
+  const int cl = lane / 8, tl = lane % 8;  // chunk within the group, token within the group
+
+  // the whole page in flight at once (CG * TG <= 16 loads of 16 bytes per lane)
+  uint4 raw[CG][TG];
+#pragma unroll
+  for (int cg = 0; cg < CG; ++cg)
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg)
+      raw[cg][tg] = *reinterpret_cast<const uint4*>(
+          src + ((size_t)(8 * cg + cl) * BS + 8 * tg + tl) * VEC);
 
   if constexpr (MINMAX) {
-    float mn[VEC], mx[VEC];
+    float mn[CG][VEC], mx[CG][VEC];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) { mn[i] = INFINITY; mx[i] = -INFINITY; }
+    for (int cg = 0; cg < CG; ++cg) {
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int t = it * TPI + ts;
-      if (t < nvalid) {
-        float f[VEC];
-        Vec<T>::load(src + (size_t)t * D, f);
+      for (int i = 0; i < VEC; ++i) { mn[cg][i] = INFINITY; mx[cg][i] = -INFINITY; }
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) { mn[i] = fminf(mn[i], f[i]); mx[i] = fmaxf(mx[i], f[i]); }
+      for (int tg = 0; tg < TG; ++tg) {
+        if (8 * tg + tl < nvalid) {
+          float f[VEC];
+          Vec<T>::widen(raw[cg][tg], f);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) {
+            mn[cg][i] = fminf(mn[cg][i], f[i]);
+            mx[cg][i] = fmaxf(mx[cg][i], f[i]);
+          }
+        }
       }
-    }
 #pragma unroll
-    for (int o = LPR; o < kWave; o <<= 1) {
+      for (int o = 1; o < 8; o <<= 1)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        mn[i] = fminf(mn[i], __shfl_xor(mn[i], o, kWave));
-        mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], o, kWave));
+        for (int i = 0; i < VEC; ++i) {
+          mn[cg][i] = fminf(mn[cg][i], __shfl_xor(mn[cg][i], o, kWave));
+          mx[cg][i] = fmaxf(mx[cg][i], __shfl_xor(mx[cg][i], o, kWave));
+        }
+      if (tl == 0) {
+        T* dst = dig + (size_t)gw * 2 * D + (8 * cg + cl) * VEC;
+        store_vals(dst, mn[cg], VEC);
+        store_vals(dst + D, mx[cg], VEC);
       }
-    }
-    if (ts == 0) {
-      T* dst = dig + (size_t)gw * 2 * D + cg * VEC;
-      store_vals(dst, mn, VEC);
-      store_vals(dst + D, mx, VEC);
     }
   } else {
-    double acc[VEC];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[i] = 0.0;
+    for (int cg = 0; cg < CG; ++cg) {
+      double acc[VEC];
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int t = it * TPI + ts;
-      if (t < nvalid) {
-        float f[VEC];
-        Vec<T>::load(src + (size_t)t * D, f);
+      for (int i = 0; i < VEC; ++i) acc[i] = 0.0;
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) acc[i] += (double)f[i];
+      for (int tg = 0; tg < TG; ++tg) {
+        if (8 * tg + tl < nvalid) {
+          float f[VEC];
+          Vec<T>::widen(raw[cg][tg], f);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) acc[i] += (double)f[i];
+        }
       }
-    }
 #pragma unroll
-    for (int o = LPR; o < kWave; o <<= 1) {
+      for (int o = 1; o < 8; o <<= 1)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] += __shfl_xor(acc[i], o, kWave);
-    }
-    if (ts == 0) {
-      double v[VEC];
+        for (int i = 0; i < VEC; ++i) acc[i] += __shfl_xor(acc[i], o, kWave);
+      if (tl == 0) {
+        double v[VEC];
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) v[i] = acc[i] / (double)nvalid;
-      store_mean(dig + (size_t)gw * D + cg * VEC, v, VEC);
+        for (int i = 0; i < VEC; ++i) v[i] = acc[i] / (double)nvalid;
+        store_mean(dig + (size_t)gw * D + (8 * cg + cl) * VEC, v, VEC);
+      }
     }
   }
 }

@@ -5,10 +5,11 @@
 // m is the batch (8..40 rows), so the product is bound by streaming W from HBM, not by the
 // matrix cores.  A workgroup of 8 waves owns 128 columns of n (16 per wave) and one slice
 // of k.  The slice of x it needs (at most 64 rows) is staged once in LDS and shared by the
-// 8 waves, so HBM and L2 carry W once and x only once per workgroup.  Each wave streams its
-// W rows with 16-byte loads straight into v_mfma_f32_16x16x32_bf16 B operands, keeping the
-// next 8 k-steps of W in flight (double-buffered registers) while the current 8 are
-// multiplied.  Several k-slices per column tile give enough workgroups to cover the chip;
+// 8 waves, so HBM and L2 carry W once and x only once per workgroup.  W arrives packed
+// (launch_pack_w): the v_mfma_f32_16x16x32_bf16 B operand of one 16-column tile and one
+// 32-wide k-step is a contiguous kilobyte, so each wave streams its W with 16-byte loads
+// that cover whole cache lines, straight into B operands, keeping the next 8 k-steps in
+// flight (double-buffered registers) while the current 8 are multiplied.  Several k-slices per column tile give enough workgroups to cover the chip;
 // their float32 partials are summed in slice order by a second kernel, so results are
 // deterministic.  Two weight matrices that share x (Q^i and Q_pred^{i+1}) run as one launch.
 #include "common.hpp"
@@ -33,9 +34,9 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ 
                                                    float* __restrict__ partials) {
   extern __shared__ uint16_t xs[];  // [16*MT][kslice + kPad]
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // scalar branches
   const int col_g = blockIdx.x * kTileN + wave * 16 + (lane % 16);  // in [0, n_total)
-  const int prob = col_g >= n ? 1 : 0;
+  const int prob = col_g >= n ? 1 : 0;  // the same for the 16 columns of a wave (16 | n)
   const int col = min(col_g - prob * n, n - 1);  // clamped for waves past n_total
   const uint16_t* w = prob ? w1 : w0;
   const int ks = blockIdx.y;
@@ -59,7 +60,8 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ 
   }
 
   const int kq = 8 * (lane / 16);  // this lane's 8 k-values within a 32-wide step
-  const uint16_t* wrow = w + (size_t)col * k + k0 + kq;
+  // packed tile (col / 16, k-step): 512 elements, this lane's 8 at lane * 8
+  const uint16_t* wtile = w + ((size_t)(col / 16) * (k / 32) + k0 / 32) * 512 + lane * 8;
   const int nsteps = klen / 32;
 
   floatx4 acc[MT];
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ 
   auto load_group = [&](uint4* dst, int s0) {
 #pragma unroll
     for (int u = 0; u < kGroup; ++u)
-      dst[u] = *reinterpret_cast<const uint4*>(wrow + 32 * min(s0 + u, nsteps - 1));
+      dst[u] = *reinterpret_cast<const uint4*>(wtile + 512 * min(s0 + u, nsteps - 1));
   };
   auto mma_group = [&](const uint4* src, int s0) {
 #pragma unroll
@@ -96,11 +98,15 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ 
   if (live) load_group(wa, 0);
   __syncthreads();  // x slice staged
   if (!live) return;
+  // Both halves always run (a group past the slice multiplies zeros): with no early exit
+  // the compiler cannot sink a group's loads down to the block that uses them, and the
+  // scheduling barriers keep it from moving them within the iteration.
   for (int s0 = 0; s0 < nsteps; s0 += 2 * kGroup) {
     load_group(wb, s0 + kGroup);
+    __builtin_amdgcn_sched_barrier(0);
     mma_group(wa, s0);
-    if (s0 + kGroup >= nsteps) break;
     load_group(wa, s0 + 2 * kGroup);
+    __builtin_amdgcn_sched_barrier(0);
     mma_group(wb, s0 + kGroup);
   }
 

@@ -14,12 +14,19 @@ struct Shape {
   bool bf16;  // KV dtype: bf16 (true) or float32 (false)
 };
 
-// ---- digests: one wave per block -----------------------------------------------------------
+// ---- layout conversions (data movement only) ------------------------------------------------
+// K pages [P][bs][d] -> chunk-major [P][d/x][bs][x], x = 16 bytes of elements.
+hipError_t launch_pack_k(const Shape& s, const void* k_rows, void* k_pool, hipStream_t stream);
+// W [n][k] bf16 -> [n/16][k/32][64][8] (one MFMA B operand per KiB); n % 16 == 0, k % 32 == 0.
+hipError_t launch_pack_w(int n, int k, const void* w, void* w_packed, hipStream_t stream);
+
+// ---- digests: one wave per block (chunk-major K pages) ------------------------------------
 hipError_t launch_build_digests(const Shape& s, bool minmax, const void* k_pool,
                                 const int32_t* block_table, const int32_t* seq_lens,
                                 void* digests, hipStream_t stream);
 
 // ---- skinny GEMM q[m][n] = x[m][k] . w[n][k]^T, for up to two weight matrices sharing x ---
+// (weights in the launch_pack_w order)
 struct GemmPlan {
   int ksplit;        // K slices, each a separate workgroup column
   int kslice;        // columns of K per slice (multiple of 64)

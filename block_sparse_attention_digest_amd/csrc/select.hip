@@ -107,7 +107,8 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
   __shared__ int cand_idx[kMaxCand];
   __shared__ uint32_t sel_digit, sel_remaining, sel_count, ncand, tot_res, tot_off;
 
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // scalar loop bounds
   const int pair = blockIdx.x;
   const int s = pair / Hkv, h = pair % Hkv;
   const int nb = (seq_lens[s] + bs - 1) / bs;
@@ -184,12 +185,14 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
       }
     }
   };
+  // the scheduling barriers keep the compiler from sinking a batch's loads to their use
   for (int b = wb0; b < wb1; b += 2 * BPB) {
     load_batch(min(b + BPB, wb1 - 1), bufb);
+    __builtin_amdgcn_sched_barrier(0);
     score_batch(b, bufa);
-    if (b + BPB >= wb1) break;
     load_batch(min(b + 2 * BPB, wb1 - 1), bufa);
-    score_batch(b + BPB, bufb);
+    __builtin_amdgcn_sched_barrier(0);
+    if (b + BPB < wb1) score_batch(b + BPB, bufb);
   }
   lo = wave_min(lo);
   hi = wave_max(hi);

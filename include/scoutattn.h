@@ -28,10 +28,17 @@
  *
  * Shapes: B sequences; Hq query heads; Hkv KV heads with G = Hq / Hkv query heads per KV
  * head (query head g uses KV head g / G); head dimension d; block size bs; P pages in the
- * paged K/V pool, one page holding bs tokens of one KV head: k_pool, v_pool [P][bs][d].
+ * paged K/V pool, one page holding bs tokens of one KV head.
  * block_table [B][Hkv][max_blocks] int32 maps block b of (sequence s, KV head h) to its
  * page, or holds -1 when that block is not resident in GPU memory.  Block b of sequence s
  * covers tokens [b*bs, min((b+1)*bs, seq_lens[s])); nb_s = ceil(seq_lens[s] / bs).
+ *
+ * Page layouts.  v_pool is [P][bs][d] (token rows).  k_pool is chunk-major,
+ * [P][d/x][bs][x] with x = 16 / (bytes per element) -- 8 for bf16, 4 for float32: the head
+ * dimension is cut into 16-byte chunks and each chunk stores the page's bs tokens one after
+ * another.  A 16-token slice of one chunk is then 256 contiguous bytes, which lets the
+ * attention kernel load K straight into matrix-core operands with whole 128-byte cache
+ * lines.  sa_pack_k_pages converts token-row pages [P][bs][d] into this layout.
  */
 #ifndef SCOUTATTN_H
 #define SCOUTATTN_H
@@ -45,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 1
+#define SA_ABI_VERSION 2
 
 typedef enum {
   SA_OK = 0,
@@ -92,7 +99,7 @@ const char* sa_status_string(sa_status status);
  *       round-to-nearest-even, to the KV dtype.
  *   kind == SA_DIGEST_MINMAX: digests [B][Hkv][max_blocks][2][d]; [..][0][c] = minimum and
  *       [..][1][c] = maximum of K channel c over the block's valid tokens (exact).
- *   k_pool [P][bs][d] (KV dtype); block_table [B][Hkv][max_blocks] (entries -1 or in
+ *   k_pool chunk-major (KV dtype); block_table [B][Hkv][max_blocks] (entries -1 or in
  *   [0, P)); seq_lens [B] (1 <= seq_lens[s] <= max_blocks*bs).  Entries of blocks that are
  *   not resident (table -1) or lie past the sequence end are left unchanged.
  * ------------------------------------------------------------------------------------- */
@@ -101,17 +108,39 @@ sa_status sa_build_digests(const sa_dims* dims, sa_digest_kind kind, const void*
                            void* digests, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * sa_pack_k_pages -- layout conversion (no arithmetic): k_rows [P][bs][d] token-row pages
+ * of K in the KV dtype -> k_pool [P][d/x][bs][x], the chunk-major K layout that every call
+ * below reads (x = 16 / bytes per element).  Both device buffers hold P*bs*d elements and
+ * must not overlap.
+ * ------------------------------------------------------------------------------------- */
+sa_status sa_pack_k_pages(const sa_dims* dims, const void* k_rows, void* k_pool,
+                          hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * sa_pack_weight -- layout conversion (no arithmetic) of a query-projection weight, done
+ * once when the weights are loaded: w [n][k] bf16 (row j = output feature j, the
+ * linear-layer layout) -> w_packed [n/16][k/32][64][8] bf16, the order in which
+ * sa_predict_query streams it.  Tile (a, b) holds rows 16a..16a+15 and columns
+ * 32b..32b+31; its element [l][e] is w[16a + l % 16][32b + 8 (l / 16) + e].  Both buffers
+ * hold n*k elements and must not overlap.  Supported: n % 16 == 0, k % 32 == 0, n, k >= 32.
+ * ------------------------------------------------------------------------------------- */
+sa_status sa_pack_weight(int32_t n, int32_t k, const void* w, void* w_packed,
+                         hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * sa_predict_query -- the layer-ahead query prediction Q_pred^{i+1} = W_Q^{i+1} X^i
  * ([Alg. 1]; [HTML Sec. 3.3]); the same call with W_Q^i gives the true query Q^i.
- *   x [m][k] bf16 (one row per sequence), w [n][k] bf16 (row j = output feature j, the
- *   linear-layer layout), q [m][n] float32 = x w^T (bf16 products, float32 accumulation, not
- *   rounded further).  Supported: 1 <= m <= 256, n % 64 == 0, k % 64 == 0, n, k >= 64.
+ *   x [m][k] bf16 (one row per sequence); w_packed: the weight w [n][k] bf16 (row j =
+ *   output feature j) in the order written by sa_pack_weight; q [m][n] float32 = x w^T
+ *   (bf16 products, float32 accumulation, not rounded further).
+ *   Supported: 1 <= m <= 256, n % 64 == 0, k % 64 == 0, n, k >= 64.
  *   For attention, q is viewed as [m][Hq][d] (head j / d).
  *   ws: sa_predict_query_workspace_bytes(m, n, k) bytes (may be 0 -> ws may be NULL).
  * ------------------------------------------------------------------------------------- */
 size_t sa_predict_query_workspace_bytes(int32_t m, int32_t n, int32_t k);
-sa_status sa_predict_query(int32_t m, int32_t n, int32_t k, const void* x, const void* w,
-                           float* q, void* ws, size_t ws_bytes, hipStream_t stream);
+sa_status sa_predict_query(int32_t m, int32_t n, int32_t k, const void* x,
+                           const void* w_packed, float* q, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Workspace of sa_select_blocks + sa_sparse_decode (+ sa_decode_attend_merge) for a shape
@@ -146,7 +175,8 @@ sa_status sa_select_blocks(const sa_dims* dims, sa_digest_kind kind, const float
  * in gpu_blocks[s][g/G][0 .. n_gpu[s][g/G]) (each block read through block_table):
  *   z_t = scale * q_g . K_t,  m = max z,  l = sum exp(z - m),  o = sum exp(z - m) V_t / l.
  *   An empty list gives o = 0, m = -inf, l = 0.
- *   q [B][Hq][d] float32; k_pool, v_pool [P][bs][d]; gpu_blocks [B][Hkv][list_stride] with
+ *   q [B][Hq][d] float32; k_pool (chunk-major), v_pool [P][bs][d] in the KV dtype;
+ *   gpu_blocks [B][Hkv][list_stride] with
  *   entries in [0, nb_s) whose table entry is a page in [0, P); 0 <= n_gpu <= list_stride.
  *   Outputs o [B][Hq][d], m [B][Hq], l [B][Hq] float32 (m in natural-log units); m and l
  *   may be NULL when not wanted.
@@ -205,11 +235,11 @@ sa_status sa_decode_attend_merge(const sa_dims* dims, const float* q, const void
  * ------------------------------------------------------------------------------------- */
 typedef struct {
   const void* x;            /* X^i [B][hidden] bf16                                       */
-  const void* w_q;          /* W_Q^i [Hq*d][hidden] bf16                                  */
+  const void* w_q;          /* W_Q^i [Hq*d][hidden] bf16, packed by sa_pack_weight       */
   const void* digests;      /* layer digests, sa_build_digests layout for the kind        */
   const int32_t* block_table; /* [B][Hkv][max_blocks]                                     */
-  const void* k_pool;       /* [P][bs][d] KV dtype (bf16)                                 */
-  const void* v_pool;       /* [P][bs][d]                                                 */
+  const void* k_pool;       /* chunk-major K pages, bf16                                  */
+  const void* v_pool;       /* [P][bs][d] bf16                                            */
   const float* host_o;      /* A_cpu^i: [B][Hq][d], normalised                            */
   const float* host_m;      /* [B][Hq], natural-log units                                 */
   const float* host_l;      /* [B][Hq]                                                    */

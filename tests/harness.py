@@ -162,12 +162,14 @@ def run_layer(wl: wk.Workload, kind: str, gen_device: str = "cpu", top_k: int | 
         X, W = qin["X"].to(dev), qin["W"].to(dev)
         Qg = torch.empty((B_, wl.num_q_heads * d), dtype=f32, device=dev)
         gws = B.workspace(B.sa_predict_query_workspace_bytes(B_, W.shape[0], X.shape[1]))
-        B.sa_predict_query(X, W, Qg, gws)
+        B.sa_predict_query(X, B.pack_weight(W), Qg, gws)
         Qg = Qg.view(B_, wl.num_q_heads, d)
     dims_full = dims_for(wl, P_full)
     per = 2 if kind == "minmax" else 1
     dig_g = torch.zeros((B_, Hkv, wl.max_blocks, per, d), dtype=wl.torch_kv_dtype, device=dev)
-    B.sa_build_digests(dims_full, kind, kv["K"].to(dev), kv["table"].to(dev), lens_d, dig_g)
+    K_full = B.pack_k_pages(dims_full, kv["K"].to(dev))
+    B.sa_build_digests(dims_full, kind, K_full, kv["table"].to(dev), lens_d, dig_g)
+    del K_full
     dims = dims_for(wl, P_pool)
     pairs = B_ * Hkv
     gb = torch.empty((pairs, k), dtype=i32, device=dev)
@@ -178,7 +180,7 @@ def run_layer(wl: wk.Workload, kind: str, gen_device: str = "cpu", top_k: int | 
     ws = B.workspace(B.sa_workspace_bytes(dims, k))
     bt = pool["block_table"].to(dev)
     B.sa_select_blocks(dims, kind, Qg, dig_g, lens_d, k, bt, gb, ng, cb, nc, scores, ws)
-    Kp, Vp = pool["K"].to(dev), pool["V"].to(dev)
+    Kp, Vp = B.pack_k_pages(dims, pool["K"].to(dev)), pool["V"].to(dev)
     rows = B_ * wl.num_q_heads
     o_gpu = torch.empty((rows, d), dtype=f32, device=dev)
     m_gpu = torch.empty(rows, dtype=f32, device=dev)

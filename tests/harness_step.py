@@ -73,10 +73,10 @@ def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs
     pinned = []
     for i, Ld in enumerate(data):
         dig = Ld["dig"].to(dev).contiguous()
-        B.sa_build_digests(dims, kind, Ld["pool"]["K"].to(dev), Ld["pool"]["block_table"].to(dev),
-                           lens_d, dig)
-        e = dict(x=Ld["X"].to(dev), w_q=Ld["W"].to(dev), digests=dig,
-                 block_table=Ld["pool"]["block_table"].to(dev), k_pool=Ld["pool"]["K"].to(dev),
+        k_pool = B.pack_k_pages(dims, Ld["pool"]["K"].to(dev))
+        B.sa_build_digests(dims, kind, k_pool, Ld["pool"]["block_table"].to(dev), lens_d, dig)
+        e = dict(x=Ld["X"].to(dev), w_q=B.pack_weight(Ld["W"].to(dev)), digests=dig,
+                 block_table=Ld["pool"]["block_table"].to(dev), k_pool=k_pool,
                  v_pool=Ld["pool"]["V"].to(dev), host_o=Ld["host"]["o"].to(dev).contiguous(),
                  host_m=Ld["host"]["m"].to(dev).contiguous(),
                  host_l=Ld["host"]["l"].to(dev).contiguous(),

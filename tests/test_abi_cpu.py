@@ -30,8 +30,9 @@ def declared_functions():
 
 def test_header_declares_the_path(lib):
     names = declared_functions()
-    for n in ("sa_build_digests", "sa_predict_query", "sa_select_blocks", "sa_sparse_decode",
-              "sa_merge", "sa_decode_attend_merge", "sa_decode_step"):
+    for n in ("sa_pack_k_pages", "sa_pack_weight", "sa_build_digests", "sa_predict_query",
+              "sa_select_blocks", "sa_sparse_decode", "sa_merge", "sa_decode_attend_merge",
+              "sa_decode_step"):
         assert n in names
 
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.sa_abi_version() == B.ABI_VERSION == 1
+    assert lib.sa_abi_version() == B.ABI_VERSION == 2
     assert lib.sa_status_string(B.SA_ERR_WORKSPACE) == b"SA_ERR_WORKSPACE"
 
 
@@ -132,6 +133,24 @@ def test_gemm_validation(lib):
     assert lib.sa_predict_query(40, 5120, 5120, FAKE, FAKE, FAKE, FAKE, need - 1,
                                 None) == B.SA_ERR_WORKSPACE
     assert lib.sa_predict_query_workspace_bytes(40, 100, 5120) == 0
+
+
+@no_gpu
+def test_pack_validation(lib):
+    d = dims()
+    nbytes = 128 * 32 * 128 * 2
+    assert lib.sa_pack_k_pages(ctypes.byref(d), None, FAKE, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_pack_k_pages(ctypes.byref(d), FAKE, None, None) == B.SA_ERR_INVALID_ARG
+    # in-place or overlapping conversion is refused
+    assert lib.sa_pack_k_pages(ctypes.byref(d), FAKE, FAKE, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_pack_k_pages(ctypes.byref(d), FAKE, FAKE + nbytes - 16, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_pack_k_pages(ctypes.byref(dims(head_dim=96)), FAKE, FAKE + nbytes,
+                               None) == B.SA_ERR_UNSUPPORTED
+    assert lib.sa_pack_weight(16, 64, FAKE, FAKE + 4096, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_pack_weight(40, 64, FAKE, FAKE + 8192, None) == B.SA_ERR_UNSUPPORTED
+    assert lib.sa_pack_weight(64, 48, FAKE, FAKE + 8192, None) == B.SA_ERR_UNSUPPORTED
+    assert lib.sa_pack_weight(64, 64, FAKE, FAKE + 100, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_pack_weight(64, 64, None, FAKE, None) == B.SA_ERR_INVALID_ARG
 
 
 @no_gpu

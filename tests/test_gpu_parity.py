@@ -60,6 +60,36 @@ def test_layer_parity(name, wl, kind, kw):
     H.run_layer(wl, kind, gen_device="cpu", **kw)
 
 
+@pytest.mark.parametrize("kv,d,bs", [("bf16", 128, 32), ("bf16", 64, 16), ("f32", 128, 16),
+                                     ("f32", 64, 32)])
+def test_pack_k_pages_layout(kv, d, bs):
+    """The chunk-major K layout, bit for bit: [P][bs][d] viewed as [P][bs][d/x][x] with the
+    two middle axes swapped (x = 16 bytes of elements)."""
+    H.log(f"[case] pack K {kv} d{d} bs{bs}")
+    P = 37
+    g = torch.Generator().manual_seed(d + bs)
+    dt = torch.bfloat16 if kv == "bf16" else torch.float32
+    x = 8 if kv == "bf16" else 4
+    rows = torch.randn(P, bs, d, generator=g).to(dt)
+    want = rows.view(P, bs, d // x, x).permute(0, 2, 1, 3).contiguous()
+    dims = B.Dims(1, 1, 1, d, bs, 1, P, B.SA_BF16 if kv == "bf16" else B.SA_F32)
+    got = B.pack_k_pages(dims, rows.cuda()).cpu().view(P, d // x, bs, x)
+    iv = torch.int16 if kv == "bf16" else torch.int32
+    assert torch.equal(got.view(iv), want.view(iv))
+
+
+@pytest.mark.parametrize("n,k", [(64, 64), (48, 96), (5120, 5120)])
+def test_pack_weight_layout(n, k):
+    """The packed weight order, bit for bit: tile (a, b) = rows 16a.., columns 32b..; its
+    element [16 q + r][e] is w[16 a + r][32 b + 8 q + e]."""
+    H.log(f"[case] pack W {n}x{k}")
+    g = torch.Generator().manual_seed(n + 3 * k)
+    w = torch.randn(n, k, generator=g).to(torch.bfloat16)
+    want = w.view(n // 16, 16, k // 32, 4, 8).permute(0, 2, 3, 1, 4).contiguous()
+    got = B.pack_weight(w.cuda()).cpu()
+    assert torch.equal(got.view(torch.int16).flatten(), want.view(torch.int16).flatten())
+
+
 @pytest.mark.parametrize("m,n,k", [(1, 64, 64), (8, 4096, 4096), (40, 5120, 5120),
                                    (65, 256, 320), (256, 128, 1024)])
 def test_predict_query_parity(m, n, k):
@@ -70,7 +100,7 @@ def test_predict_query_parity(m, n, k):
     want = so.predict_query(wk.f64(X), wk.f64(W))
     q = torch.empty(m, n, dtype=torch.float32, device="cuda")
     ws = B.workspace(B.sa_predict_query_workspace_bytes(m, n, k))
-    B.sa_predict_query(X.cuda(), W.cuda(), q, ws)
+    B.sa_predict_query(X.cuda(), B.pack_weight(W.cuda()), q, ws)
     err = float(np.max(np.abs(q.cpu().double().numpy() - want)))
     assert err <= H.TOL_GEMM, err
 
