@@ -230,12 +230,12 @@ def main():
     wl = wk.QWEN3_14B_STEP
     log(f"workload {wl.name}: setup")
     dims, lens, layers, ws = setup(wl, torch, B, wk)
-    copy_stream = torch.cuda.Stream()
+    side_stream = torch.cuda.Stream()
     kind = "mean"
 
     def step():
         B.sa_decode_step(dims, kind, wl.hidden, wl.top_k, wl.scale, lens, layers, ws,
-                         copy_stream=copy_stream)
+                         side_stream=side_stream)
 
     for _ in range(args.warmup):
         step()

@@ -283,7 +283,7 @@ def sa_merge(o_a, m_a, l_a, o_b, m_b, l_b, o, m, l, stream=None):
 
 
 def sa_decode_step(dims: Dims, kind: str, hidden: int, top_k: int, scale: float, seq_lens,
-                   layers: list, ws, stream=None, copy_stream=None):
+                   layers: list, ws, stream=None, side_stream=None):
     """`layers` is a list of dicts with the sa_layer field names (tensors; the *_host ones
     pinned CPU tensors or None)."""
     arr = (sa_layer * len(layers))()
@@ -296,7 +296,7 @@ def sa_decode_step(dims: Dims, kind: str, hidden: int, top_k: int, scale: float,
         ctypes.byref(dims.c()), KIND[kind], hidden, top_k, scale,
         _ptr(seq_lens, torch.int32, dims.batch, "seq_lens"), len(layers), arr,
         _ptr(ws, torch.uint8, name="ws"), ws.numel(), _stream(stream),
-        None if copy_stream is None else _stream(copy_stream)))
+        None if side_stream is None else _stream(side_stream)))
 
 
 def sa_profile_attention(starts, stops):

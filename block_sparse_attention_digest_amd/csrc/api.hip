@@ -369,7 +369,7 @@ sa_status sa_merge(int32_t rows, int32_t d, const float* o_a, const float* m_a,
 
 namespace {
 struct StepLayout {
-  size_t q_true, q_pred, gemm, sel, total;
+  size_t q_true, q_pred[2], gemm, sel, total;
   sa::GemmPlan plan_dual, plan_single;
   Layout sel_layout;
 };
@@ -380,8 +380,9 @@ StepLayout step_layout(const sa::Shape& s, int hidden, int top_k) {
   L.plan_single = sa::gemm_plan(s.B, n, hidden);
   const size_t qbytes = align_up((size_t)s.B * n * sizeof(float));
   L.q_true = 0;
-  L.q_pred = qbytes;
-  L.gemm = 2 * qbytes;
+  L.q_pred[0] = qbytes;      // Q_pred of even target layers
+  L.q_pred[1] = 2 * qbytes;  // Q_pred of odd target layers
+  L.gemm = 3 * qbytes;
   const size_t gbytes = align_up(std::max(L.plan_dual.ws_bytes, L.plan_single.ws_bytes));
   L.sel = L.gemm + gbytes;
   L.sel_layout = layout(s, top_k);
@@ -404,7 +405,7 @@ size_t sa_step_workspace_bytes(const sa_dims* dims, int32_t hidden, int32_t top_
 sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidden,
                          int32_t top_k, float scale, const int32_t* seq_lens,
                          int32_t num_layers, const sa_layer* layers, void* ws,
-                         size_t ws_bytes, hipStream_t stream, hipStream_t copy_stream) {
+                         size_t ws_bytes, hipStream_t stream, hipStream_t side_stream) {
   sa::Shape s;
   SA_CHECK(check_dims(dims, &s));
   SA_CHECK(check_kind(kind));
@@ -425,13 +426,14 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
       return fail(SA_ERR_INVALID_ARG,
                   "layer %d: cpu_blocks_host and n_cpu_host must both be set or both NULL", i);
   }
+  if (side_stream == stream) side_stream = nullptr;
   const StepLayout SL = step_layout(s, hidden, top_k);
   if (!ws || ws_bytes < SL.total)
     return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, SL.total);
 
   char* base = (char*)ws;
   float* q_true = (float*)(base + SL.q_true);
-  float* q_pred = (float*)(base + SL.q_pred);
+  float* q_pred[2] = {(float*)(base + SL.q_pred[0]), (float*)(base + SL.q_pred[1])};
   float* gemm_ws = (float*)(base + SL.gemm);
   char* sel_base = base + SL.sel;
   float* parts = (float*)(sel_base + SL.sel_layout.parts);
@@ -439,53 +441,80 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
   const int n = s.Hq * s.d;
   const size_t list_bytes = (size_t)s.B * s.Hkv * top_k * sizeof(int32_t);
   const size_t cnt_bytes = (size_t)s.B * s.Hkv * sizeof(int32_t);
+  hipStream_t sel_stream = side_stream ? side_stream : stream;
 
   std::vector<hipEvent_t> events;
-  auto cleanup = [&]() {
-    for (hipEvent_t e : events) (void)hipEventDestroy(e);
+  auto new_event = [&](hipEvent_t* ev) -> sa_status {
+    SA_HIP(hipEventCreateWithFlags(ev, hipEventDisableTiming), "hipEventCreate");
+    events.push_back(*ev);
+    return SA_OK;
   };
-  // hand-off of layer j's offloaded lists to the host (the "spawn" of the CPU attention)
+  // `to` waits for the work enqueued so far on `from`
+  auto order = [&](hipStream_t from, hipStream_t to) -> sa_status {
+    if (from == to) return SA_OK;
+    hipEvent_t ev;
+    SA_CHECK(new_event(&ev));
+    SA_HIP(hipEventRecord(ev, from), "hipEventRecord");
+    SA_HIP(hipStreamWaitEvent(to, ev, 0), "hipStreamWaitEvent");
+    return SA_OK;
+  };
+  // hand-off of layer j's offloaded lists to the host (the "spawn" of the CPU attention),
+  // enqueued on the side stream right after layer j's selection
   auto handoff = [&](int j) -> sa_status {
     const sa_layer& L = layers[j];
-    if (!copy_stream || !L.cpu_blocks_host) return SA_OK;
-    hipEvent_t ev;
-    SA_HIP(hipEventCreateWithFlags(&ev, hipEventDisableTiming), "hipEventCreate");
-    events.push_back(ev);
-    SA_HIP(hipEventRecord(ev, stream), "hipEventRecord");
-    SA_HIP(hipStreamWaitEvent(copy_stream, ev, 0), "hipStreamWaitEvent");
-    SA_HIP(hipMemcpyAsync(L.n_cpu_host, L.n_cpu, cnt_bytes, hipMemcpyDeviceToHost, copy_stream),
+    if (!side_stream || !L.cpu_blocks_host) return SA_OK;
+    SA_HIP(hipMemcpyAsync(L.n_cpu_host, L.n_cpu, cnt_bytes, hipMemcpyDeviceToHost, side_stream),
            "hipMemcpyAsync n_cpu");
     SA_HIP(hipMemcpyAsync(L.cpu_blocks_host, L.cpu_blocks, list_bytes, hipMemcpyDeviceToHost,
-                          copy_stream),
+                          side_stream),
            "hipMemcpyAsync cpu_blocks");
     return SA_OK;
   };
 
   sa_status st = SA_OK;
+  hipEvent_t sel_done = nullptr;  // side stream: the selection of the coming layer is done
   for (int i = 0; i < num_layers && st == SA_OK; ++i) {
     const sa_layer& L = layers[i];
     const bool has_next = i + 1 < num_layers;
-    // 1. Q^i (and Q_pred^{i+1}) from X^i
+    // 1. Q^i (and Q_pred^{i+1}) from X^i.  Q_pred alternates between two buffers, so this
+    //    never overwrites the one a selection may still be reading.
+    float* qp = q_pred[(i + 1) & 1];
     hipError_t e = sa::launch_gemm(s.B, n, hidden, L.x, has_next ? 2 : 1, L.w_q, q_true,
-                                   has_next ? layers[i + 1].w_q : nullptr, q_pred, gemm_ws,
+                                   has_next ? layers[i + 1].w_q : nullptr, qp, gemm_ws,
                                    has_next ? SL.plan_dual : SL.plan_single, stream);
     if (e != hipSuccess) { st = hip_fail(e, "GEMM kernel"); break; }
-    // 2. the first layer selects with its own query
+    // 2. the first layer selects with its own query (on `stream`: its attention needs it)
     if (i == 0) {
       st = run_select(s, minmax, q_true, L.digests, seq_lens, top_k, L.block_table,
                       L.gpu_blocks, L.n_gpu, L.cpu_blocks, L.n_cpu, nullptr, stream);
-      if (st == SA_OK) st = handoff(0);
+      if (st == SA_OK && side_stream && L.cpu_blocks_host) {
+        st = order(stream, side_stream);
+        if (st == SA_OK) st = handoff(0);
+      }
       if (st != SA_OK) break;
     }
-    // 3. layer-ahead selection for layer i+1 and its hand-off
+    // 3. layer i's lists were selected on the side stream one layer earlier
+    if (i >= 1 && side_stream && hipStreamWaitEvent(stream, sel_done, 0) != hipSuccess) {
+      st = fail(SA_ERR_HIP, "hipStreamWaitEvent failed");
+      break;
+    }
+    // 4. layer-ahead selection for layer i+1 and its hand-off, on the side stream once
+    //    Q_pred^{i+1} exists; it runs while layer i's attention runs on `stream`
     if (has_next) {
       const sa_layer& N = layers[i + 1];
-      st = run_select(s, minmax, q_pred, N.digests, seq_lens, top_k, N.block_table,
-                      N.gpu_blocks, N.n_gpu, N.cpu_blocks, N.n_cpu, nullptr, stream);
+      st = order(stream, sel_stream);
+      if (st == SA_OK)
+        st = run_select(s, minmax, qp, N.digests, seq_lens, top_k, N.block_table,
+                        N.gpu_blocks, N.n_gpu, N.cpu_blocks, N.n_cpu, nullptr, sel_stream);
       if (st == SA_OK) st = handoff(i + 1);
+      if (st == SA_OK && side_stream) {
+        st = new_event(&sel_done);
+        if (st == SA_OK && hipEventRecord(sel_done, side_stream) != hipSuccess)
+          st = fail(SA_ERR_HIP, "hipEventRecord failed");
+      }
       if (st != SA_OK) break;
     }
-    // 4. GPU attention of layer i, merged with its host partial
+    // 5. GPU attention of layer i, merged with its host partial
     hipEvent_t e0, e1;
     next_profile_events(&e0, &e1);
     e = sa::launch_attention(s, SL.sel_layout.plan, q_true, L.k_pool, L.v_pool, L.block_table,
@@ -496,18 +525,12 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
                           L.n_cpu, L.out_o, L.out_m, L.out_l, stream);
     if (e != hipSuccess) { st = hip_fail(e, "reduce kernel"); break; }
   }
-  // join the copy stream back into `stream`
-  if (!events.empty()) {
-    hipEvent_t done;
-    hipError_t e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
-    if (e == hipSuccess) {
-      events.push_back(done);
-      e = hipEventRecord(done, copy_stream);
-      if (e == hipSuccess) e = hipStreamWaitEvent(stream, done, 0);
-    }
-    if (e != hipSuccess && st == SA_OK) st = hip_fail(e, "joining the copy stream");
+  // join the side stream back into `stream`
+  if (side_stream) {
+    sa_status j = order(side_stream, stream);
+    if (st == SA_OK) st = j;
   }
-  cleanup();
+  for (hipEvent_t ev : events) (void)hipEventDestroy(ev);
   return st == SA_OK ? ok() : st;
 }
 

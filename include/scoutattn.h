@@ -223,15 +223,19 @@ sa_status sa_decode_attend_merge(const sa_dims* dims, const float* q, const void
  *   1. Q^i = W_Q^i X^i and, for i < L-1, Q_pred^{i+1} = W_Q^{i+1} X^i (one GEMM launch);
  *   2. (layer 0 only) select B^0 with Q^0 -- the first layer has no predecessor;
  *   3. for i < L-1: select B_pred^{i+1} with Q_pred^{i+1} and layer i+1's digests and block
- *      table, writing layer i+1's lists; then, when copy_stream is not NULL and the host
- *      pointers are set, copy n_cpu and cpu_blocks of layer i+1 to the host on copy_stream
- *      (the hand-off that spawns the CPU-side attention);
+ *      table, writing layer i+1's lists; then, when side_stream is not NULL and the host
+ *      pointers are set, copy n_cpu and cpu_blocks of layer i+1 to the host (the hand-off
+ *      that spawns the CPU-side attention);
  *   4. A_gpu^i over B_gpu^i with Q^i, merged with layer i's host partial (ignored for heads
  *      whose n_cpu is 0) into out_o/out_m/out_l.
- * All layers share dims, digest kind, hidden, top_k, scale and seq_lens.  `layers` is a host
- * array of num_layers descriptors (read during the call only).  Before returning, `stream`
- * waits for every copy issued on copy_stream, so a graph captured from `stream` is
- * closed.  ws: sa_step_workspace_bytes(dims, hidden, top_k).
+ * With side_stream given, step 3 (the selection one layer ahead and its hand-off copies)
+ * runs on side_stream, concurrently with step 4 of layer i on `stream`; the two touch
+ * disjoint buffers, and layer i+1's attention waits for its selection.  With side_stream
+ * NULL (or equal to `stream`) every step runs in order on `stream` and no host copies are
+ * made.  All layers share dims, digest kind, hidden, top_k, scale and seq_lens.  `layers`
+ * is a host array of num_layers descriptors (read during the call only).  Before returning,
+ * `stream` waits for everything enqueued on side_stream, so a graph captured from `stream`
+ * is closed.  ws: sa_step_workspace_bytes(dims, hidden, top_k).
  * ------------------------------------------------------------------------------------- */
 typedef struct {
   const void* x;            /* X^i [B][hidden] bf16                                       */
@@ -258,7 +262,7 @@ size_t sa_step_workspace_bytes(const sa_dims* dims, int32_t hidden, int32_t top_
 sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidden,
                          int32_t top_k, float scale, const int32_t* seq_lens,
                          int32_t num_layers, const sa_layer* layers, void* ws,
-                         size_t ws_bytes, hipStream_t stream, hipStream_t copy_stream);
+                         size_t ws_bytes, hipStream_t stream, hipStream_t side_stream);
 
 /* ---------------------------------------------------------------------------------------
  * sa_profile_attention -- kernel timing of the attention stage (GPUATTN).  After this call

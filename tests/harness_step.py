@@ -92,9 +92,9 @@ def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs
             e["n_cpu_host"] = torch.zeros((pairs,), dtype=i32).pin_memory()
         dev_layers.append(e)
     ws = B.workspace(B.sa_step_workspace_bytes(dims, wl.hidden, k))
-    copy_stream = torch.cuda.Stream() if handoff else None
+    side_stream = torch.cuda.Stream() if handoff else None
     B.sa_decode_step(dims, kind, wl.hidden, k, wl.scale, lens_d, dev_layers, ws,
-                     copy_stream=copy_stream)
+                     side_stream=side_stream)
     torch.cuda.synchronize()
     H.log("  HIP step done")
 
