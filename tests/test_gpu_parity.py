@@ -1,7 +1,7 @@
 """HIP path against the CPU oracle, element by element, through the C ABI.
 
 Small and scaled workloads (several tiles, ragged tails) plus edge cases.  The full-size
-workloads live in test_gpu_fullsize.py.
+workloads live in test_gpu_parity_fullsize.py.
 """
 
 import math
