@@ -104,8 +104,8 @@ def setup(wl, torch, B, wk):
             n_gpu=torch.empty(pairs, dtype=torch.int32, device=dev),
             cpu_blocks=torch.empty((pairs, k), dtype=torch.int32, device=dev),
             n_cpu=torch.empty(pairs, dtype=torch.int32, device=dev),
-            cpu_blocks_host=torch.empty((pairs, k), dtype=torch.int32).pin_memory(),
-            n_cpu_host=torch.empty(pairs, dtype=torch.int32).pin_memory(),
+            cpu_blocks_host=B.pinned_empty((pairs, k)).zero_(),
+            n_cpu_host=B.pinned_empty((pairs,)).zero_(),
             out_o=torch.empty((Bsz, Hq, d), dtype=torch.float32, device=dev),
             out_m=torch.empty((Bsz, Hq), dtype=torch.float32, device=dev),
             out_l=torch.empty((Bsz, Hq), dtype=torch.float32, device=dev)))

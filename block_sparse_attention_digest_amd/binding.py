@@ -143,6 +143,35 @@ class Dims:
         return torch.bfloat16 if self.kv_dtype == SA_BF16 else torch.float32
 
 
+_hip = None
+_HOST_BUFFERS = []  # page-locked host buffers, kept until the process ends
+
+
+HIP_HOST_MALLOC_COHERENT = 0x40000000
+
+
+def pinned_empty(shape, dtype=torch.int32) -> torch.Tensor:
+    """A CPU tensor in coherent page-locked memory (hipHostMalloc with
+    hipHostMallocCoherent), for the host mirrors of the hand-off (cpu_blocks_host,
+    n_cpu_host), which the selection kernel writes directly."""
+    global _hip
+    if _hip is None:
+        lib()  # loads libamdhip64 as a dependency of the library
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t,
+                                       ctypes.c_uint]
+    n = 1
+    for v in (shape if isinstance(shape, (tuple, list)) else (shape,)):
+        n *= int(v)
+    nbytes = max(1, n) * torch.empty((), dtype=dtype).element_size()
+    ptr = ctypes.c_void_p()
+    if _hip.hipHostMalloc(ctypes.byref(ptr), nbytes, HIP_HOST_MALLOC_COHERENT) != 0 or not ptr.value:
+        raise RuntimeError(f"hipHostMalloc of {nbytes} bytes failed")
+    buf = (ctypes.c_char * nbytes).from_address(ptr.value)
+    _HOST_BUFFERS.append(buf)
+    return torch.frombuffer(buf, dtype=dtype, count=n).view(shape)
+
+
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     """A device byte buffer of at least nbytes (at least 256 so it is never empty)."""
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)

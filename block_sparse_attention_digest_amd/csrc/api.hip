@@ -23,6 +23,18 @@ struct ProfileEvents {
 };
 thread_local ProfileEvents g_prof;
 
+// Events that order the streams of sa_decode_step, created on first use and reused by
+// every later call on the same thread (re-recording an event does not affect waits
+// enqueued before it, so one event per fork/join point of a call is enough).  Creating
+// and destroying events on every call would block the host.  They live as long as the
+// thread: destroying them from a thread-exit destructor could run after the HIP runtime
+// itself has shut down.
+struct EventPool {
+  std::vector<hipEvent_t> ev;
+  size_t next = 0;
+};
+thread_local EventPool g_events;
+
 void next_profile_events(hipEvent_t* e0, hipEvent_t* e1) {
   *e0 = *e1 = nullptr;
   if (g_prof.next < g_prof.start.size()) {
@@ -141,9 +153,11 @@ sa_status check_scale(float scale) {
 sa_status run_select(const sa::Shape& s, bool minmax, const float* q, const void* digests,
                      const int32_t* seq_lens, int top_k, const int32_t* block_table,
                      int32_t* gpu_blocks, int32_t* n_gpu, int32_t* cpu_blocks, int32_t* n_cpu,
-                     float* scores, hipStream_t stream) {
+                     float* scores, int32_t* cpu_blocks_host, int32_t* n_cpu_host,
+                     hipStream_t stream) {
   SA_HIP(sa::launch_select(s, minmax, q, digests, seq_lens, top_k, block_table, gpu_blocks,
-                           n_gpu, cpu_blocks, n_cpu, scores, stream),
+                           n_gpu, cpu_blocks, n_cpu, scores, cpu_blocks_host, n_cpu_host,
+                           stream),
          "select kernel");
   return SA_OK;
 }
@@ -280,7 +294,7 @@ sa_status sa_select_blocks(const sa_dims* dims, sa_digest_kind kind, const float
   if (!ws || ws_bytes < L.total)
     return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, L.total);
   SA_CHECK(run_select(s, kind == SA_DIGEST_MINMAX, q, digests, seq_lens, top_k, block_table,
-                      gpu_blocks, n_gpu, cpu_blocks, n_cpu, scores, stream));
+                      gpu_blocks, n_gpu, cpu_blocks, n_cpu, scores, nullptr, nullptr, stream));
   return ok();
 }
 
@@ -369,7 +383,7 @@ sa_status sa_merge(int32_t rows, int32_t d, const float* o_a, const float* m_a,
 
 namespace {
 struct StepLayout {
-  size_t q_true, q_pred[2], gemm, sel, total;
+  size_t q_true, q_pred[2], gemm[2], sel, total;
   sa::GemmPlan plan_dual, plan_single;
   Layout sel_layout;
 };
@@ -382,9 +396,11 @@ StepLayout step_layout(const sa::Shape& s, int hidden, int top_k) {
   L.q_true = 0;
   L.q_pred[0] = qbytes;      // Q_pred of even target layers
   L.q_pred[1] = 2 * qbytes;  // Q_pred of odd target layers
-  L.gemm = 3 * qbytes;
+  // GEMM slice partials: one buffer for the main stream, one for the side stream
   const size_t gbytes = align_up(std::max(L.plan_dual.ws_bytes, L.plan_single.ws_bytes));
-  L.sel = L.gemm + gbytes;
+  L.gemm[0] = 3 * qbytes;
+  L.gemm[1] = L.gemm[0] + gbytes;
+  L.sel = L.gemm[1] + gbytes;
   L.sel_layout = layout(s, top_k);
   L.total = L.sel + L.sel_layout.total;
   return L;
@@ -434,19 +450,21 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
   char* base = (char*)ws;
   float* q_true = (float*)(base + SL.q_true);
   float* q_pred[2] = {(float*)(base + SL.q_pred[0]), (float*)(base + SL.q_pred[1])};
-  float* gemm_ws = (float*)(base + SL.gemm);
+  float* gemm_ws[2] = {(float*)(base + SL.gemm[0]), (float*)(base + SL.gemm[1])};
   char* sel_base = base + SL.sel;
   float* parts = (float*)(sel_base + SL.sel_layout.parts);
   const bool minmax = kind == SA_DIGEST_MINMAX;
   const int n = s.Hq * s.d;
-  const size_t list_bytes = (size_t)s.B * s.Hkv * top_k * sizeof(int32_t);
-  const size_t cnt_bytes = (size_t)s.B * s.Hkv * sizeof(int32_t);
   hipStream_t sel_stream = side_stream ? side_stream : stream;
 
-  std::vector<hipEvent_t> events;
+  g_events.next = 0;
   auto new_event = [&](hipEvent_t* ev) -> sa_status {
-    SA_HIP(hipEventCreateWithFlags(ev, hipEventDisableTiming), "hipEventCreate");
-    events.push_back(*ev);
+    if (g_events.next == g_events.ev.size()) {
+      hipEvent_t e;
+      SA_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming), "hipEventCreate");
+      g_events.ev.push_back(e);
+    }
+    *ev = g_events.ev[g_events.next++];
     return SA_OK;
   };
   // `to` waits for the work enqueued so far on `from`
@@ -458,60 +476,62 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
     SA_HIP(hipStreamWaitEvent(to, ev, 0), "hipStreamWaitEvent");
     return SA_OK;
   };
-  // hand-off of layer j's offloaded lists to the host (the "spawn" of the CPU attention),
-  // enqueued on the side stream right after layer j's selection
-  auto handoff = [&](int j) -> sa_status {
-    const sa_layer& L = layers[j];
-    if (!side_stream || !L.cpu_blocks_host) return SA_OK;
-    SA_HIP(hipMemcpyAsync(L.n_cpu_host, L.n_cpu, cnt_bytes, hipMemcpyDeviceToHost, side_stream),
-           "hipMemcpyAsync n_cpu");
-    SA_HIP(hipMemcpyAsync(L.cpu_blocks_host, L.cpu_blocks, list_bytes, hipMemcpyDeviceToHost,
-                          side_stream),
-           "hipMemcpyAsync cpu_blocks");
-    return SA_OK;
-  };
-
   sa_status st = SA_OK;
   hipEvent_t sel_done = nullptr;  // side stream: the selection of the coming layer is done
   for (int i = 0; i < num_layers && st == SA_OK; ++i) {
     const sa_layer& L = layers[i];
     const bool has_next = i + 1 < num_layers;
-    // 1. Q^i (and Q_pred^{i+1}) from X^i.  Q_pred alternates between two buffers, so this
-    //    never overwrites the one a selection may still be reading.
+    // Q_pred alternates between two buffers, so a prediction never overwrites the query a
+    // selection may still be reading.
     float* qp = q_pred[(i + 1) & 1];
-    hipError_t e = sa::launch_gemm(s.B, n, hidden, L.x, has_next ? 2 : 1, L.w_q, q_true,
-                                   has_next ? layers[i + 1].w_q : nullptr, qp, gemm_ws,
-                                   has_next ? SL.plan_dual : SL.plan_single, stream);
+    hipError_t e;
+    // 1. Q^i = W_Q^i X^i on `stream`.  Without a side stream, Q_pred^{i+1} = W_Q^{i+1} X^i
+    //    comes from the same launch (both weights share X^i).
+    if (side_stream || !has_next) {
+      e = sa::launch_gemm(s.B, n, hidden, L.x, 1, L.w_q, q_true, nullptr, nullptr, gemm_ws[0],
+                          SL.plan_single, stream);
+    } else {
+      e = sa::launch_gemm(s.B, n, hidden, L.x, 2, L.w_q, q_true, layers[i + 1].w_q, qp,
+                          gemm_ws[0], SL.plan_dual, stream);
+    }
     if (e != hipSuccess) { st = hip_fail(e, "GEMM kernel"); break; }
-    // 2. the first layer selects with its own query (on `stream`: its attention needs it)
+    // 2. the first layer selects with its own query (on `stream`: its attention needs it);
+    //    the selection kernels also write the offloaded lists into the host mirrors
     if (i == 0) {
       st = run_select(s, minmax, q_true, L.digests, seq_lens, top_k, L.block_table,
-                      L.gpu_blocks, L.n_gpu, L.cpu_blocks, L.n_cpu, nullptr, stream);
-      if (st == SA_OK && side_stream && L.cpu_blocks_host) {
-        st = order(stream, side_stream);
-        if (st == SA_OK) st = handoff(0);
-      }
+                      L.gpu_blocks, L.n_gpu, L.cpu_blocks, L.n_cpu, nullptr, L.cpu_blocks_host,
+                      L.n_cpu_host, stream);
+      if (st == SA_OK && side_stream) st = order(stream, side_stream);
       if (st != SA_OK) break;
     }
-    // 3. layer i's lists were selected on the side stream one layer earlier
+    // 3. layer-ahead work for layer i+1: with a side stream, the prediction GEMM (it needs
+    //    only X^i, ready once the previous layer is done), the selection and its hand-off
+    //    run there, concurrently with layer i's attention on `stream`
+    if (has_next) {
+      const sa_layer& N = layers[i + 1];
+      if (side_stream) {
+        if (i > 0) st = order(stream, side_stream);  // X^i exists; layer 0 forked above
+        if (st == SA_OK) {
+          e = sa::launch_gemm(s.B, n, hidden, L.x, 1, N.w_q, qp, nullptr, nullptr, gemm_ws[1],
+                              SL.plan_single, side_stream);
+          if (e != hipSuccess) st = hip_fail(e, "GEMM kernel");
+        }
+      }
+      if (st == SA_OK)
+        st = run_select(s, minmax, qp, N.digests, seq_lens, top_k, N.block_table,
+                        N.gpu_blocks, N.n_gpu, N.cpu_blocks, N.n_cpu, nullptr,
+                        N.cpu_blocks_host, N.n_cpu_host, sel_stream);
+      if (st != SA_OK) break;
+    }
+    // 4. layer i's lists were selected on the side stream one layer earlier
     if (i >= 1 && side_stream && hipStreamWaitEvent(stream, sel_done, 0) != hipSuccess) {
       st = fail(SA_ERR_HIP, "hipStreamWaitEvent failed");
       break;
     }
-    // 4. layer-ahead selection for layer i+1 and its hand-off, on the side stream once
-    //    Q_pred^{i+1} exists; it runs while layer i's attention runs on `stream`
-    if (has_next) {
-      const sa_layer& N = layers[i + 1];
-      st = order(stream, sel_stream);
-      if (st == SA_OK)
-        st = run_select(s, minmax, qp, N.digests, seq_lens, top_k, N.block_table,
-                        N.gpu_blocks, N.n_gpu, N.cpu_blocks, N.n_cpu, nullptr, sel_stream);
-      if (st == SA_OK) st = handoff(i + 1);
-      if (st == SA_OK && side_stream) {
-        st = new_event(&sel_done);
-        if (st == SA_OK && hipEventRecord(sel_done, side_stream) != hipSuccess)
-          st = fail(SA_ERR_HIP, "hipEventRecord failed");
-      }
+    if (has_next && side_stream) {
+      st = new_event(&sel_done);
+      if (st == SA_OK && hipEventRecord(sel_done, side_stream) != hipSuccess)
+        st = fail(SA_ERR_HIP, "hipEventRecord failed");
       if (st != SA_OK) break;
     }
     // 5. GPU attention of layer i, merged with its host partial
@@ -530,7 +550,6 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
     sa_status j = order(side_stream, stream);
     if (st == SA_OK) st = j;
   }
-  for (hipEvent_t ev : events) (void)hipEventDestroy(ev);
   return st == SA_OK ? ok() : st;
 }
 

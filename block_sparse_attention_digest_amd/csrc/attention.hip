@@ -448,8 +448,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 
 // One wave per (sequence, query head) row: combine the partials of the waves that covered
 // the pair's blocks and, when given, the host partial; write the normalised output.  The
-// covering waves' (m, l) are read in parallel, one per lane; o is accumulated with
-// independent loads.
+// loads come in two rounds: first the pair's count and prefix and the host partial, then
+// every covering wave's (m, l) (one per lane) together with the o vectors of the first
+// kPre of them; only pairs covered by more waves than that read further o vectors one by
+// one.
 template <int D>
 __global__ __launch_bounds__(256) void reduce_kernel(
     const float* __restrict__ ws, int npairs, int W, int G, int Hkv, int rows,
@@ -458,6 +460,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(
     const int32_t* __restrict__ n_cpu, float* __restrict__ o, float* __restrict__ m,
     float* __restrict__ l) {
   constexpr int CPL = D / kWave;
+  constexpr int kPre = 4;
   const int lane = threadIdx.x % kWave;
   const int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (row >= rows) return;
@@ -465,66 +468,92 @@ __global__ __launch_bounds__(256) void reduce_kernel(
   const int s = row / Hq, qh = row % Hq;
   const int pair = s * Hkv + qh / G, g = qh % G;
   const PartialView part = partial_view(const_cast<float*>(ws), npairs, W, G, D);
+
+  // round 1: the pair's block count and prefix, and the host partial
   const int ng = n_gpu[pair];
-  const bool host_given = host_o != nullptr && (n_cpu == nullptr || n_cpu[pair] > 0);
+  const int P = part.pfx[pair];
+  const int T = part.pfx[npairs];
+  const bool host_ptr = host_o != nullptr;
   float mh = -INFINITY, lh = 0.f;
-  if (host_given) {
+  float ho[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) ho[i] = 0.f;
+  int nc = 1;
+  if (host_ptr) {
     mh = host_m[row] * kLog2e;
     lh = host_l[row];
-    if (!(lh > 0.f)) mh = -INFINITY;  // an empty host partial contributes nothing
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) ho[i] = host_o[(size_t)row * D + lane + kWave * i];
+    if (n_cpu) nc = n_cpu[pair];
   }
-  int w_lo = 0, nslot = 0, T = 0;
+  // an empty host partial, or one for a pair with nothing offloaded, contributes nothing
+  if (!host_ptr || nc <= 0 || !(lh > 0.f)) mh = -INFINITY;
+
+  int w_lo = 0, nslot = 0;
   if (ng > 0) {
-    const int P = part.pfx[pair];
-    T = part.pfx[npairs];
     w_lo = wave_of(P, T, W);
     nslot = wave_of(P + ng - 1, T, W) - w_lo + 1;
   }
-  // pass 1: the maximum over the covering waves (waves with an empty range, possible when
-  // W > T, own no block and wrote no partial)
-  float M = mh;
-  for (int j0 = 0; j0 < nslot; j0 += kWave) {
-    const int w = w_lo + j0 + lane;
-    float mw = -INFINITY;
-    if (j0 + lane < nslot && wave_start(w, T, W) < wave_start(w + 1, T, W))
-      mw = part.ml[((size_t)(w + pair) * G + g) * 2];
-    M = fmaxf(M, mw);
-  }
-  M = max_xor32(max_xor16(M));
-  M = fmaxf(M, dpp<kDppMirror>(M));
-  M = fmaxf(M, dpp<kDppHalfMirror>(M));
-  M = fmaxf(M, dpp<kDppXor2>(M));
-  M = fmaxf(M, dpp<kDppXor1>(M));
-  float acc[CPL], L = 0.f;
+  // a covering wave with an empty range (possible when W > T) wrote no partial
+  auto slot_live = [&](int j) {
+    const int w = w_lo + j;
+    return j < nslot && wave_start(w, T, W) < wave_start(w + 1, T, W);
+  };
+  auto o_of = [&](int j, int i) {  // o of covering wave j (index clamped into the slots)
+    const size_t sl = (size_t)(w_lo + j + pair) * G + g;
+    return part.o[sl * D + lane + kWave * i];
+  };
+
+  // round 2: (m, l) of the covering waves, one per lane, and the first kPre o vectors
+  float M = mh, L = 0.f;
+  float acc[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
-  if (M != -INFINITY) {
-    // pass 2: weights per slot (lane j of each group of 64), then o with independent loads
-    for (int j0 = 0; j0 < nslot; j0 += kWave) {
-      const int w = w_lo + j0 + lane;
-      float wt = 0.f, lw = 0.f;
-      if (j0 + lane < nslot && wave_start(w, T, W) < wave_start(w + 1, T, W)) {
-        const float mw = part.ml[((size_t)(w + pair) * G + g) * 2];
-        lw = part.ml[((size_t)(w + pair) * G + g) * 2 + 1];
-        wt = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
-      }
+  float ob[kPre][CPL];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j)
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) ob[j][i] = o_of(max(0, min(j, nslot - 1)), i);
+  for (int j0 = 0; j0 < nslot; j0 += kWave) {
+    const bool live = slot_live(j0 + lane);
+    float mw = -INFINITY, lw = 0.f;
+    if (live) {
+      const size_t sl = (size_t)(w_lo + j0 + lane + pair) * G + g;
+      mw = part.ml[sl * 2];
+      lw = part.ml[sl * 2 + 1];
+    }
+    float mx = max_xor32(max_xor16(mw));
+    mx = fmaxf(mx, dpp<kDppMirror>(mx));
+    mx = fmaxf(mx, dpp<kDppHalfMirror>(mx));
+    mx = fmaxf(mx, dpp<kDppXor2>(mx));
+    mx = fmaxf(mx, dpp<kDppXor1>(mx));
+    // rescale what is accumulated so far to the new running maximum
+    const float Mn = fmaxf(M, mx);
+    if (Mn != -INFINITY) {
+      const float r = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+      L *= r;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) acc[i] *= r;
+      const float wt = mw == -INFINITY ? 0.f : fast_exp2(mw - Mn);
       L += group_sum<kWave>(wt * lw);
       const int cnt = min(kWave, nslot - j0);
       for (int j = 0; j < cnt; ++j) {
         const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), j));
-        if (wj == 0.f) continue;
-        const size_t sl = (size_t)(w_lo + j0 + j + pair) * G + g;
+        if (wj == 0.f) continue;  // (a stale slot may hold anything: skip, do not scale)
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) acc[i] = fmaf(wj, part.o[sl * D + lane + kWave * i], acc[i]);
+        for (int i = 0; i < CPL; ++i) {
+          const float v = j0 + j < kPre ? ob[min(j0 + j, kPre - 1)][i] : o_of(j0 + j, i);
+          acc[i] = fmaf(wj, v, acc[i]);
+        }
       }
     }
-    if (host_given && mh != -INFINITY) {
-      const float wt = lh * fast_exp2(mh - M);
-      L += wt;
+    M = Mn;
+  }
+  if (mh != -INFINITY) {  // the host partial, at the final maximum
+    const float wt = lh * fast_exp2(mh - M);
+    L += wt;
 #pragma unroll
-      for (int i = 0; i < CPL; ++i)
-        acc[i] = fmaf(wt, host_o[(size_t)row * D + lane + kWave * i], acc[i]);
-    }
+    for (int i = 0; i < CPL; ++i) acc[i] = fmaf(wt, ho[i], acc[i]);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll

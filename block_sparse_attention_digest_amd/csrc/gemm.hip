@@ -3,66 +3,62 @@
 // skinny GEMM q[m][n] = x[m][k] . w[n][k]^T with bf16 operands and float32 accumulation.
 //
 // m is the batch (8..40 rows), so the product is bound by streaming W from HBM, not by the
-// matrix cores.  A workgroup of 8 waves owns 128 columns of n (16 per wave) and one slice
-// of k.  The slice of x it needs (at most 64 rows) is staged once in LDS and shared by the
-// 8 waves, so HBM and L2 carry W once and x only once per workgroup.  W arrives packed
-// (launch_pack_w): the v_mfma_f32_16x16x32_bf16 B operand of one 16-column tile and one
-// 32-wide k-step is a contiguous kilobyte, so each wave streams its W with 16-byte loads
+// matrix cores.  The work is cut into units of one 16-column tile x one k-slice; each unit
+// belongs to one workgroup, where kpw waves split its k-slice (their sums are combined in
+// LDS at the end, in a fixed order).  A wave streams its W (packed by launch_pack_w: the v_mfma_f32_16x16x32_bf16 B
+// operand of one tile and one 32-wide k-step is a contiguous kilobyte) with 16-byte loads
 // that cover whole cache lines, straight into B operands, keeping the next 8 k-steps in
-// flight (double-buffered registers) while the current 8 are multiplied.  Several k-slices per column tile give enough workgroups to cover the chip;
-// their float32 partials are summed in slice order by a second kernel, so results are
-// deterministic.  Two weight matrices that share x (Q^i and Q_pred^{i+1}) run as one launch.
+// flight (double-buffered registers) while the current 8 are multiplied.  A workgroup's
+// waves own consecutive tiles of the same k-slice, so the slice of x they share (at most 64
+// rows) is staged once in LDS -- up to 160 KiB, so one k-slice can be long and the float32
+// partials of the slices (summed in slice order by a second kernel, so results are
+// deterministic) stay a small fraction of the W bytes.  The plan sizes the grid to about
+// one workgroup per CU, so the whole product is one round of long-lived waves.  Two weight
+// matrices that share x (Q^i and Q_pred^{i+1}) can run as one launch.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace sa {
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kTileN = 16 * kWaves;  // columns per workgroup
 constexpr int kGroup = 8;            // k-steps (of 32) per register buffer
-constexpr int kLdsBytes = 64 * 1024;
 constexpr int kPad = 8;              // bf16 elements of padding per LDS row
+constexpr int kMaxWpg = 10;          // waves per workgroup (640 threads: up to 168 VGPRs)
+constexpr int kTargetUnits = 1024;   // >= 4 long-lived waves per CU
+constexpr int kCUs = 256;
 
 template <int MT>
-__global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ x,
-                                                   const uint16_t* __restrict__ w0,
-                                                   const uint16_t* __restrict__ w1, int m,
-                                                   int n, int k, int kslice, int n_total,
-                                                   float* __restrict__ out0,
-                                                   float* __restrict__ out1, int ksplit,
-                                                   float* __restrict__ partials) {
-  extern __shared__ uint16_t xs[];  // [16*MT][kslice + kPad]
+__global__ __launch_bounds__(640) void gemm_kernel(const uint16_t* __restrict__ x,
+                                                    const uint16_t* __restrict__ w0,
+                                                    const uint16_t* __restrict__ w1, int m,
+                                                    int n, int k, int kslice, int n_total,
+                                                    int tiles, int tpw, float* __restrict__ out0,
+                                                    float* __restrict__ out1, int ksplit,
+                                                    float* __restrict__ partials) {
+  extern __shared__ uint16_t xs[];  // [16*MT][kslice + kPad]; later the kpw combine
   const int lane = threadIdx.x % kWave;
+  const int kpw = blockDim.x / kWave / tpw;  // waves per tile
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // scalar branches
-  const int col_g = blockIdx.x * kTileN + wave * 16 + (lane % 16);  // in [0, n_total)
-  const int prob = col_g >= n ? 1 : 0;  // the same for the 16 columns of a wave (16 | n)
-  const int col = min(col_g - prob * n, n - 1);  // clamped for waves past n_total
+  const int tw = wave % tpw, kpart = wave / tpw;
+  const int unit0 = blockIdx.x * tpw;  // units are (k-slice, tile), slice-major
+  const int ks = unit0 / tiles;        // one slice per workgroup (tiles % tpw == 0)
+  const int tile = unit0 % tiles + tw;
+  const int col_g = tile * 16 + (lane % 16);  // in [0, n_total)
+  const int prob = tile * 16 >= n ? 1 : 0;    // the same for the 16 columns (16 | n)
+  const int col = col_g - prob * n;
   const uint16_t* w = prob ? w1 : w0;
-  const int ks = blockIdx.y;
-  const int k0 = ks * kslice;
-  const int k1 = min(k, k0 + kslice);
-  const int klen = k1 - k0;
-  const int row0 = blockIdx.z * 16 * MT;
+  const int k0 = ks * kslice;                 // slices are full: k0 + kslice <= k
+  const int row0 = blockIdx.y * 16 * MT;
   const int ldx = kslice + kPad;
 
-  // stage x[row0 .. row0+16MT)[k0 .. k1) in LDS (rows past m are zero)
-  {
-    const int chunks_per_row = klen / 8;
-    const int total = 16 * MT * chunks_per_row;
-    for (int c = threadIdx.x; c < total; c += blockDim.x) {
-      const int r = c / chunks_per_row, q8 = c % chunks_per_row;
-      const int gr = row0 + r;
-      const uint4 v = gr < m ? *reinterpret_cast<const uint4*>(x + (size_t)gr * k + k0 + 8 * q8)
-                             : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(xs + r * ldx + 8 * q8) = v;
-    }
-  }
-
   const int kq = 8 * (lane / 16);  // this lane's 8 k-values within a 32-wide step
+  const int nsteps = kslice / 32 / kpw;  // this wave's k-steps: part kpart of the slice
+  const int step0 = kpart * nsteps;      // first k-step of the part within the slice
   // packed tile (col / 16, k-step): 512 elements, this lane's 8 at lane * 8
-  const uint16_t* wtile = w + ((size_t)(col / 16) * (k / 32) + k0 / 32) * 512 + lane * 8;
-  const int nsteps = klen / 32;
+  const uint16_t* wtile =
+      w + ((size_t)(col / 16) * (k / 32) + k0 / 32 + step0) * 512 + lane * 8;
 
   floatx4 acc[MT];
 #pragma unroll
@@ -86,28 +82,94 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ 
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         const uint4 a = *reinterpret_cast<const uint4*>(
-            xs + (16 * t + (lane % 16)) * ldx + 32 * st + kq);
+            xs + (16 * t + (lane % 16)) * ldx + 32 * (step0 + st) + kq);
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b,
                                                          acc[t], 0, 0, 0);
       }
     }
   };
 
-  // a wave whose 16 columns lie past n_total (last tile) only helps stage x
-  const bool live = blockIdx.x * kTileN + wave * 16 < n_total;
-  if (live) load_group(wa, 0);
-  __syncthreads();  // x slice staged
-  if (!live) return;
-  // Both halves always run (a group past the slice multiplies zeros): with no early exit
-  // the compiler cannot sink a group's loads down to the block that uses them, and the
-  // scheduling barriers keep it from moving them within the iteration.
-  for (int s0 = 0; s0 < nsteps; s0 += 2 * kGroup) {
-    load_group(wb, s0 + kGroup);
+  // Staging of the x slice overlaps the first two W groups: the slice's loads are issued
+  // first (up to 2 x kStage per thread; rows past m are not read), then the W groups, so
+  // the waits before the LDS stores cover the slice only (loads complete in issue order).
+  {
+    constexpr int kStage = 8;
+    const int nthr = blockDim.x;
+    const int chunks_per_row = kslice / 8;
+    const int mrows = min(16 * MT, m - row0);
+    const int total = mrows * chunks_per_row;
+    // chunk c of the slice (clamped to the last one: lanes past the end load and store
+    // that chunk's own value again, so there is no branch and the arrays stay in registers)
+    auto xload = [&](int c) -> uint4 {
+      c = min(c, total - 1);
+      const int r = c / chunks_per_row, q8 = c % chunks_per_row;
+      return *reinterpret_cast<const uint4*>(x + (size_t)(row0 + r) * k + k0 + 8 * q8);
+    };
+    auto xstore = [&](int c, uint4 v) {
+      c = min(c, total - 1);
+      const int r = c / chunks_per_row, q8 = c % chunks_per_row;
+      *reinterpret_cast<uint4*>(xs + r * ldx + 8 * q8) = v;
+    };
+    const int c0 = threadIdx.x;
+    uint4 va[kStage], vb[kStage];
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) va[j] = xload(c0 + j * nthr);
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) vb[j] = xload(c0 + (kStage + j) * nthr);
+    load_group(wa, 0);
+    load_group(wb, kGroup);
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) xstore(c0 + j * nthr, va[j]);
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) xstore(c0 + (kStage + j) * nthr, vb[j]);
+    // larger slices than one round of 2 x kStage per thread (not the usual shapes)
+    for (int c1 = c0 + 2 * kStage * nthr; c1 < total; c1 += kStage * nthr) {
+      uint4 vt[kStage];
+#pragma unroll
+      for (int j = 0; j < kStage; ++j) vt[j] = xload(c1 + j * nthr);
+#pragma unroll
+      for (int j = 0; j < kStage; ++j) xstore(c1 + j * nthr, vt[j]);
+    }
+    // padding rows of the last row tile are zero
+    for (int c = threadIdx.x; c < (16 * MT - mrows) * chunks_per_row; c += nthr) {
+      const int r = mrows + c / chunks_per_row, q8 = c % chunks_per_row;
+      *reinterpret_cast<uint4*>(xs + r * ldx + 8 * q8) = make_uint4(0, 0, 0, 0);
+    }
+  }
+  __syncthreads();  // x slice staged
+
+  // Both halves always run (a group past the part multiplies zeros): with no early exit
+  // the compiler cannot sink a group's loads down to the block that uses them, and the
+  // scheduling barriers keep it from moving them within the iteration.  Each group is
+  // loaded two groups ahead of its use.
+  for (int s0 = 0; s0 < nsteps; s0 += 2 * kGroup) {
     mma_group(wa, s0);
     load_group(wa, s0 + 2 * kGroup);
     __builtin_amdgcn_sched_barrier(0);
     mma_group(wb, s0 + kGroup);
+    load_group(wb, s0 + 3 * kGroup);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // combine the kpw parts of each tile in LDS (part order is fixed: deterministic)
+  if (kpw > 1) {
+    floatx4* red = reinterpret_cast<floatx4*>(xs);  // [tpw][kpw-1][MT][64]
+    __syncthreads();  // every wave is done with the x slice
+    if (kpart > 0) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        red[((tw * (kpw - 1) + kpart - 1) * MT + t) * kWave + lane] = acc[t];
+    }
+    __syncthreads();
+    if (kpart > 0) return;
+    for (int p = 1; p < kpw; ++p) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const floatx4 v = red[((tw * (kpw - 1) + p - 1) * MT + t) * kWave + lane];
+        acc[t] += v;
+      }
+    }
   }
 
   // acc[t][r] holds row row0 + 16t + 4*(lane/16) + r, column col_g
@@ -128,7 +190,10 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t* __restrict__ 
   }
 }
 
-// Sum of the k-slice partials in slice order; four consecutive columns per thread.
+// Sum of the k-slice partials in slice order; four consecutive columns per thread.  All
+// slices are loaded before the sum (up to kMaxSlices in flight), so the kernel waits for
+// memory once.
+constexpr int kMaxSlices = 8;
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ partials,
                                                           int m, int n, int n_total, int ksplit,
                                                           float* __restrict__ out0,
@@ -139,11 +204,19 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restric
   const long e = i4 * 4;
   const int row = (int)(e / n_total);
   const int col_g = (int)(e % n_total);
-  float4 s = *reinterpret_cast<const float4*>(partials + e);
-  for (int ks = 1; ks < ksplit; ++ks) {
-    const float4 v =
-        *reinterpret_cast<const float4*>(partials + (size_t)ks * m * n_total + e);
-    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  const size_t slice = (size_t)m * n_total;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = 0; k0 < ksplit; k0 += kMaxSlices) {
+    float4 v[kMaxSlices];
+#pragma unroll
+    for (int j = 0; j < kMaxSlices; ++j)
+      v[j] = *reinterpret_cast<const float4*>(partials + min(k0 + j, ksplit - 1) * slice + e);
+#pragma unroll
+    for (int j = 0; j < kMaxSlices; ++j) {
+      if (k0 + j < ksplit) {
+        s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w;
+      }
+    }
   }
   const int prob = col_g >= n ? 1 : 0;
   float* out = prob ? out1 : out0;
@@ -156,20 +229,35 @@ int row_tiles(int m) { return m >= 64 ? 4 : (m + 15) / 16; }
 
 GemmPlan gemm_plan(int m, int n_total, int k) {
   const int mt = row_tiles(m);
-  const int groups = (n_total + kTileN - 1) / kTileN;
-  const int row_groups = (m + 63) / 64;
-  // k-slice: a multiple of 64 whose x tile fits the LDS budget
-  const int max_slice = ((kLdsBytes / (16 * mt * 2) - kPad) / 64) * 64;
-  int ksplit = (640 + groups * row_groups - 1) / (groups * row_groups);  // ~640+ workgroups
-  ksplit = ksplit < 1 ? 1 : ksplit;
+  const int tiles = n_total / 16;
   const int ksteps64 = k / 64;
-  if (ksplit > ksteps64) ksplit = ksteps64;
-  int kslice = 64 * ((ksteps64 + ksplit - 1) / ksplit);
-  if (kslice > max_slice) kslice = max_slice;
-  ksplit = (k + kslice - 1) / kslice;
+  const size_t lds_max = 160 * 1024;
+  // fewest k-slices (a divisor of k/64, so slices are equal) that give enough units and
+  // whose x slice fits the LDS of one workgroup
+  int ksplit = 0;
+  for (int d = 1; d <= ksteps64; ++d) {
+    if (ksteps64 % d) continue;
+    const size_t lds = (size_t)16 * mt * (k / d + kPad) * sizeof(uint16_t);
+    if (lds > lds_max) continue;
+    ksplit = d;
+    if ((long)tiles * d >= kTargetUnits) break;
+  }
+  const int units = tiles * ksplit;
+  // tiles per workgroup: a divisor of the tile count (so a workgroup stays in one slice),
+  // as large as keeps about one workgroup per CU
+  int tpw = 1;
+  for (int v = 1; v <= kMaxWpg; ++v)
+    if (tiles % v == 0 && units / v >= kCUs) tpw = v;
+  // waves per tile: split the slice further while each part keeps two register groups
+  const int steps = k / ksplit / 32;
+  int kpw = 1;
+  for (int v = 2; v * tpw <= kMaxWpg; ++v)
+    if (steps % v == 0 && steps / v >= 2 * kGroup) kpw = v;
   GemmPlan p;
   p.ksplit = ksplit;
-  p.kslice = kslice;
+  p.kslice = k / ksplit;
+  p.tpw = tpw;
+  p.kpw = kpw;
   p.ws_bytes = ksplit > 1 ? (size_t)ksplit * m * n_total * sizeof(float) : 0;
   return p;
 }
@@ -179,23 +267,24 @@ hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void
                        hipStream_t stream) {
   const int n_total = n * nprob;
   const int mt = row_tiles(m);
-  const dim3 grid((n_total + kTileN - 1) / kTileN, plan.ksplit, (m + 63) / 64);
-  const dim3 block(kWaves * kWave);
-  const size_t lds = (size_t)16 * mt * (plan.kslice + kPad) * sizeof(uint16_t);
+  const int tiles = n_total / 16;
+  const dim3 grid(tiles * plan.ksplit / plan.tpw, (m + 63) / 64);
+  const dim3 block(plan.tpw * plan.kpw * kWave);
+  const size_t lds = std::max((size_t)16 * mt * (plan.kslice + kPad) * sizeof(uint16_t),
+                              (size_t)plan.tpw * (plan.kpw - 1) * mt * kWave * 16);
   const uint16_t* X = (const uint16_t*)x;
   const uint16_t* W0 = (const uint16_t*)w0;
   const uint16_t* W1 = (const uint16_t*)(nprob > 1 ? w1 : w0);
   float* Q1 = nprob > 1 ? q1 : q0;
+#define SA_GEMM_CASE(MT)                                                                    \
+  case MT:                                                                                  \
+    hipLaunchKernelGGL(gemm_kernel<MT>, grid, block, lds, stream, X, W0, W1, m, n, k,       \
+                       plan.kslice, n_total, tiles, plan.tpw, q0, Q1, plan.ksplit, ws);     \
+    break;
   switch (mt) {
-    case 1: hipLaunchKernelGGL(gemm_kernel<1>, grid, block, lds, stream, X, W0, W1, m, n, k,
-                               plan.kslice, n_total, q0, Q1, plan.ksplit, ws); break;
-    case 2: hipLaunchKernelGGL(gemm_kernel<2>, grid, block, lds, stream, X, W0, W1, m, n, k,
-                               plan.kslice, n_total, q0, Q1, plan.ksplit, ws); break;
-    case 3: hipLaunchKernelGGL(gemm_kernel<3>, grid, block, lds, stream, X, W0, W1, m, n, k,
-                               plan.kslice, n_total, q0, Q1, plan.ksplit, ws); break;
-    default: hipLaunchKernelGGL(gemm_kernel<4>, grid, block, lds, stream, X, W0, W1, m, n, k,
-                                plan.kslice, n_total, q0, Q1, plan.ksplit, ws); break;
+    SA_GEMM_CASE(1) SA_GEMM_CASE(2) SA_GEMM_CASE(3) default: SA_GEMM_CASE(4)
   }
+#undef SA_GEMM_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.ksplit == 1) return e;
   const long total4 = (long)m * n_total / 4;

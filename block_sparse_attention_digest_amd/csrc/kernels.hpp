@@ -28,8 +28,10 @@ hipError_t launch_build_digests(const Shape& s, bool minmax, const void* k_pool,
 // ---- skinny GEMM q[m][n] = x[m][k] . w[n][k]^T, for up to two weight matrices sharing x ---
 // (weights in the launch_pack_w order)
 struct GemmPlan {
-  int ksplit;        // K slices, each a separate workgroup column
-  int kslice;        // columns of K per slice (multiple of 64)
+  int ksplit;        // K slices (equal; k / ksplit is a multiple of 64)
+  int kslice;        // columns of K per slice
+  int tpw;           // 16-column tiles per workgroup (divides n_total / 16)
+  int kpw;           // waves per tile, each streaming 1/kpw of the k-slice
   size_t ws_bytes;   // float partials [ksplit][m][n_total] when ksplit > 1
 };
 GemmPlan gemm_plan(int m, int n_total, int k);
@@ -41,7 +43,8 @@ hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void
 hipError_t launch_select(const Shape& s, bool minmax, const float* q, const void* digests,
                          const int32_t* seq_lens, int top_k, const int32_t* block_table,
                          int32_t* gpu_blocks, int32_t* n_gpu, int32_t* cpu_blocks,
-                         int32_t* n_cpu, float* scores_or_null, hipStream_t stream);
+                         int32_t* n_cpu, float* scores_or_null,
+                         int32_t* cpu_blocks_host, int32_t* n_cpu_host, hipStream_t stream);
 
 // ---- attention: balanced waves write partials, then the reduction / merge per row -------
 struct AttnPlan {

@@ -15,7 +15,8 @@
 //      exactly by (score, lower index first).  Crowded buckets (e.g. all scores equal) fall
 //      back to an exact MSB-first radix select on order-preserving 32-bit keys.
 //   3. split: the selected blocks are compacted in ascending order and split by the block
-//      table (read during step 1) into the resident and offloaded lists.
+//      table (read during step 1) into the resident and offloaded lists; the offloaded list
+//      can also be written straight into a host mirror (the hand-off of Algorithm 1).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -90,7 +91,8 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
     int Hkv, int G, int bs, int max_blocks, int top_k, const int32_t* __restrict__ table,
     int32_t* __restrict__ gpu_blocks, int32_t* __restrict__ n_gpu,
     int32_t* __restrict__ cpu_blocks, int32_t* __restrict__ n_cpu,
-    float* __restrict__ scores_out) {
+    float* __restrict__ scores_out, int32_t* __restrict__ cpu_blocks_host,
+    int32_t* __restrict__ n_cpu_host) {
   constexpr int VEC = Digest<T>::N;
   constexpr int LPR = D / VEC;             // lanes per digest row
   constexpr int BPI = kWave / LPR;         // blocks per load instruction
@@ -286,7 +288,12 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
     __syncthreads();
   }
 
-  // ascending compaction of the selected blocks, split by residency
+  // ascending compaction of the selected blocks, split by residency.  The offloaded list
+  // is assembled in LDS (over the scores, no longer needed) and then written out with
+  // coalesced stores, to device memory and, when given, straight into the host mirror
+  // (coherent page-locked host memory, which the device writes through without caching,
+  // so the values are in host memory once the kernel has completed): the hand-off needs
+  // no copy.
   const int per = (nb + kSelThreads - 1) / kSelThreads;
   const int i0 = min(nb, tid * per), i1 = min(nb, i0 + per);
   uint32_t cnt_res = 0, cnt_off = 0;
@@ -300,34 +307,44 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
   uint32_t pos_res = (incl - packed) & 0xffffu, pos_off = (incl - packed) >> 16;
   if (tid == kSelThreads - 1) { tot_res = incl & 0xffffu; tot_off = incl >> 16; }
   int32_t* grow = gpu_blocks + (size_t)pair * top_k;
-  int32_t* crow = cpu_blocks + (size_t)pair * top_k;
+  int32_t* off_lds = reinterpret_cast<int32_t*>(sc);  // [top_k] <= [max_blocks]
   for (int i = i0; i < i1; ++i) {
     const uint8_t f = flag[i];
     if (f == (kSelected | kResident)) grow[pos_res++] = i;
-    else if (f == kSelected) crow[pos_off++] = i;
+    else if (f == kSelected) off_lds[pos_off++] = i;
   }
   __syncthreads();
   const int nr = (int)tot_res, no = (int)tot_off;
   for (int j = nr + tid; j < top_k; j += kSelThreads) grow[j] = -1;
-  for (int j = no + tid; j < top_k; j += kSelThreads) crow[j] = -1;
-  if (tid == 0) { n_gpu[pair] = nr; n_cpu[pair] = no; }
+  int32_t* crow = cpu_blocks + (size_t)pair * top_k;
+  int32_t* hrow = cpu_blocks_host ? cpu_blocks_host + (size_t)pair * top_k : nullptr;
+  for (int j = tid; j < top_k; j += kSelThreads) {
+    const int32_t v = j < no ? off_lds[j] : -1;
+    crow[j] = v;
+    if (hrow) hrow[j] = v;
+  }
+  if (tid == 0) {
+    n_gpu[pair] = nr;
+    n_cpu[pair] = no;
+    if (n_cpu_host) n_cpu_host[pair] = no;
+  }
 }
 
 template <typename T, int D>
 hipError_t select_typed(const Shape& s, bool minmax, const float* q, const void* dig,
                         const int32_t* lens, int top_k, const int32_t* table, int32_t* gb,
-                        int32_t* ng, int32_t* cb, int32_t* nc, float* scores,
-                        hipStream_t st) {
+                        int32_t* ng, int32_t* cb, int32_t* nc, float* scores, int32_t* cbh,
+                        int32_t* nch, hipStream_t st) {
   const size_t lds = (size_t)s.max_blocks * (sizeof(float) + 1);
   const dim3 grid(s.B * s.Hkv), block(kSelThreads);
   if (minmax)
     hipLaunchKernelGGL((select_kernel<T, D, true>), grid, block, lds, st, q, (const T*)dig,
                        lens, s.Hkv, s.G, s.bs, s.max_blocks, top_k, table, gb, ng, cb, nc,
-                       scores);
+                       scores, cbh, nch);
   else
     hipLaunchKernelGGL((select_kernel<T, D, false>), grid, block, lds, st, q, (const T*)dig,
                        lens, s.Hkv, s.G, s.bs, s.max_blocks, top_k, table, gb, ng, cb, nc,
-                       scores);
+                       scores, cbh, nch);
   return hipGetLastError();
 }
 
@@ -336,9 +353,10 @@ hipError_t select_typed(const Shape& s, bool minmax, const float* q, const void*
 hipError_t launch_select(const Shape& s, bool minmax, const float* q, const void* digests,
                          const int32_t* seq_lens, int top_k, const int32_t* block_table,
                          int32_t* gpu_blocks, int32_t* n_gpu, int32_t* cpu_blocks,
-                         int32_t* n_cpu, float* scores_or_null, hipStream_t stream) {
+                         int32_t* n_cpu, float* scores_or_null, int32_t* cpu_blocks_host,
+                         int32_t* n_cpu_host, hipStream_t stream) {
 #define SA_SEL_ARGS s, minmax, q, digests, seq_lens, top_k, block_table, gpu_blocks, n_gpu, \
-                    cpu_blocks, n_cpu, scores_or_null, stream
+                    cpu_blocks, n_cpu, scores_or_null, cpu_blocks_host, n_cpu_host, stream
   if (s.bf16)
     return s.d == 128 ? select_typed<uint16_t, 128>(SA_SEL_ARGS)
                       : select_typed<uint16_t, 64>(SA_SEL_ARGS);

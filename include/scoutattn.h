@@ -11,7 +11,8 @@
  *   - Pointers named *_host are host memory; every other pointer is device memory owned by
  *     the caller.  The library keeps no pointer after a call returns and allocates no
  *     device memory: scratch space comes from the caller's workspace (`ws`, `ws_bytes`),
- *     whose required size the *_workspace_bytes() queries return.
+ *     whose required size the *_workspace_bytes() queries return.  (sa_decode_step keeps
+ *     a per-thread pool of HIP events that order its two streams, reused across calls.)
  *   - Work is enqueued on the caller's `stream` and the call returns without waiting.
  *     Results are valid once the stream has reached that point.  Calls on different
  *     streams may run concurrently if they share no output or workspace.
@@ -223,16 +224,17 @@ sa_status sa_decode_attend_merge(const sa_dims* dims, const float* q, const void
  *   1. Q^i = W_Q^i X^i and, for i < L-1, Q_pred^{i+1} = W_Q^{i+1} X^i (one GEMM launch);
  *   2. (layer 0 only) select B^0 with Q^0 -- the first layer has no predecessor;
  *   3. for i < L-1: select B_pred^{i+1} with Q_pred^{i+1} and layer i+1's digests and block
- *      table, writing layer i+1's lists; then, when side_stream is not NULL and the host
- *      pointers are set, copy n_cpu and cpu_blocks of layer i+1 to the host (the hand-off
- *      that spawns the CPU-side attention);
+ *      table, writing layer i+1's lists; when a layer's host pointers are set, its selection
+ *      kernel also writes n_cpu and cpu_blocks straight into them (the hand-off that spawns
+ *      the CPU-side attention, with no copy).  They must be coherent page-locked host
+ *      memory the device can address (hipHostMalloc with hipHostMallocCoherent); the values
+ *      are complete once the stream that ran that selection has passed it;
  *   4. A_gpu^i over B_gpu^i with Q^i, merged with layer i's host partial (ignored for heads
  *      whose n_cpu is 0) into out_o/out_m/out_l.
- * With side_stream given, step 3 (the selection one layer ahead and its hand-off copies)
- * runs on side_stream, concurrently with step 4 of layer i on `stream`; the two touch
- * disjoint buffers, and layer i+1's attention waits for its selection.  With side_stream
- * NULL (or equal to `stream`) every step runs in order on `stream` and no host copies are
- * made.  All layers share dims, digest kind, hidden, top_k, scale and seq_lens.  `layers`
+ * With side_stream given, the prediction Q_pred^{i+1} and step 3 (the selection one layer
+ * ahead) run on side_stream, concurrently with step 4 of layer i on `stream`; the two
+ * touch disjoint buffers, and layer i+1's attention waits for its selection.  With
+ * side_stream NULL (or equal to `stream`) every step runs in order on `stream`.  All layers share dims, digest kind, hidden, top_k, scale and seq_lens.  `layers`
  * is a host array of num_layers descriptors (read during the call only).  Before returning,
  * `stream` waits for everything enqueued on side_stream, so a graph captured from `stream`
  * is closed.  ws: sa_step_workspace_bytes(dims, hidden, top_k).
@@ -251,8 +253,8 @@ typedef struct {
   int32_t* n_gpu;           /* out: [B][Hkv]                                              */
   int32_t* cpu_blocks;      /* out: B_cpu^i list [B][Hkv][top_k]                          */
   int32_t* n_cpu;           /* out: [B][Hkv]                                              */
-  int32_t* cpu_blocks_host; /* optional pinned host copy of cpu_blocks (or NULL)          */
-  int32_t* n_cpu_host;      /* optional pinned host copy of n_cpu (or NULL)               */
+  int32_t* cpu_blocks_host; /* optional host mirror of cpu_blocks (or NULL), coherent      */
+  int32_t* n_cpu_host;      /* optional host mirror of n_cpu (or NULL), coherent           */
   float* out_o;             /* out: A^i [B][Hq][d]                                        */
   float* out_m;             /* out: [B][Hq] (may be NULL)                                 */
   float* out_l;             /* out: [B][Hq] (may be NULL)                                 */

@@ -55,7 +55,10 @@ def prepare_step(wl, gen_device, kind="mean"):
     return layers
 
 
-def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs_to_check=None):
+def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs_to_check=None,
+             side=True):
+    """handoff: give every layer host mirrors of its offloaded lists; side: run the
+    layer-ahead work on a side stream."""
     dev = "cuda"
     B_, Hkv, Hq, G, d, bs, k = (wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.group,
                                 wl.head_dim, wl.block_size, wl.top_k)
@@ -88,11 +91,11 @@ def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs
                  out_m=torch.empty((B_, Hq), dtype=f32, device=dev),
                  out_l=torch.empty((B_, Hq), dtype=f32, device=dev))
         if handoff:
-            e["cpu_blocks_host"] = torch.zeros((pairs, k), dtype=i32).pin_memory()
-            e["n_cpu_host"] = torch.zeros((pairs,), dtype=i32).pin_memory()
+            e["cpu_blocks_host"] = B.pinned_empty((pairs, k)).zero_()
+            e["n_cpu_host"] = B.pinned_empty((pairs,)).zero_()
         dev_layers.append(e)
     ws = B.workspace(B.sa_step_workspace_bytes(dims, wl.hidden, k))
-    side_stream = torch.cuda.Stream() if handoff else None
+    side_stream = torch.cuda.Stream() if side else None
     B.sa_decode_step(dims, kind, wl.hidden, k, wl.scale, lens_d, dev_layers, ws,
                      side_stream=side_stream)
     torch.cuda.synchronize()

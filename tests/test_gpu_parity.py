@@ -159,11 +159,25 @@ def test_selection_ties_go_to_lower_index():
 
 
 def test_step_parity():
+    """Side stream and host hand-off; pools smaller than the budget, so every pair
+    offloads blocks and the host mirrors carry real lists."""
     H.log("[case] step")
     import harness_step as HS
-    HS.run_step(wk.QWEN3_14B_STEP.scaled(batch=3, num_q_heads=10, num_kv_heads=2, context=2000,
-                                         layers=4, pool_blocks=16, hidden=512, top_k=8),
-                gen_device="cpu", handoff=True)
+    r = HS.run_step(wk.QWEN3_14B_STEP.scaled(batch=3, num_q_heads=10, num_kv_heads=2,
+                                             context=2000, layers=4, pool_blocks=6, hidden=512,
+                                             top_k=8),
+                    gen_device="cpu", handoff=True, side=True)
+    assert r["cpu_ratio"] > 0.1
+
+
+def test_step_parity_handoff_one_stream():
+    H.log("[case] step hand-off, one stream")
+    import harness_step as HS
+    r = HS.run_step(wk.QWEN3_14B_STEP.scaled(batch=2, num_q_heads=8, num_kv_heads=2,
+                                             context=1500, layers=3, pool_blocks=5, hidden=256,
+                                             top_k=8),
+                    gen_device="cpu", handoff=True, side=False)
+    assert r["cpu_ratio"] > 0.1
 
 
 def test_step_parity_minmax_no_handoff():
@@ -172,4 +186,4 @@ def test_step_parity_minmax_no_handoff():
     HS.run_step(wk.QWEN3_14B_STEP.scaled(batch=2, num_q_heads=8, num_kv_heads=2, context=1024,
                                          layers=3, pool_blocks=8, hidden=256, top_k=4,
                                          digest_kinds=("minmax",)),
-                gen_device="cpu", handoff=False, kind="minmax")
+                gen_device="cpu", handoff=False, side=False, kind="minmax")
