@@ -485,6 +485,12 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
     // selection may still be reading.
     float* qp = q_pred[(i + 1) & 1];
     hipError_t e;
+    // 0. with a side stream, the layer-ahead work for layer i+1 (below) may start as soon
+    //    as X^i exists, i.e. once the previous layer is done on `stream`
+    if (side_stream && has_next && i > 0) {
+      st = order(stream, side_stream);
+      if (st != SA_OK) break;
+    }
     // 1. Q^i = W_Q^i X^i on `stream`.  Without a side stream, Q_pred^{i+1} = W_Q^{i+1} X^i
     //    comes from the same launch (both weights share X^i).
     if (side_stream || !has_next) {
@@ -505,17 +511,14 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
       if (st != SA_OK) break;
     }
     // 3. layer-ahead work for layer i+1: with a side stream, the prediction GEMM (it needs
-    //    only X^i, ready once the previous layer is done), the selection and its hand-off
-    //    run there, concurrently with layer i's attention on `stream`
+    //    only X^i), the selection and its hand-off run there, concurrently with layer i's
+    //    GEMM, attention and merge on `stream` (layer 0 forked after its own selection)
     if (has_next) {
       const sa_layer& N = layers[i + 1];
       if (side_stream) {
-        if (i > 0) st = order(stream, side_stream);  // X^i exists; layer 0 forked above
-        if (st == SA_OK) {
-          e = sa::launch_gemm(s.B, n, hidden, L.x, 1, N.w_q, qp, nullptr, nullptr, gemm_ws[1],
-                              SL.plan_single, side_stream);
-          if (e != hipSuccess) st = hip_fail(e, "GEMM kernel");
-        }
+        e = sa::launch_gemm(s.B, n, hidden, L.x, 1, N.w_q, qp, nullptr, nullptr, gemm_ws[1],
+                            SL.plan_single, side_stream);
+        if (e != hipSuccess) st = hip_fail(e, "GEMM kernel");
       }
       if (st == SA_OK)
         st = run_select(s, minmax, qp, N.digests, seq_lens, top_k, N.block_table,

@@ -160,17 +160,27 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   const int hcol = c16 & 7;    // head of this MFMA column
   const int vcg = lane % VLPR, vts = lane / VLPR;
 
+  // Q^T as the MFMA B operand (hi columns 0..7, lo 8..15): the float rows of a pair are
+  // fetched ahead (fetch_q, into qr) and converted when the pair's blocks begin
   bf16x8 qb[KS];
-  auto load_q = [&](int pair) {  // Q^T as the MFMA B operand (hi columns 0..7, lo 8..15)
+  float4 qr[KS][2];
+  auto fetch_q = [&](int pair) {
+    pair = min(pair, npairs - 1);
     const int s = pair / Hkv, h = pair % Hkv;
+    const float* qrow = q + ((size_t)s * Hkv * G + (size_t)h * G + (hcol < G ? hcol : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qr[ks][0] = *reinterpret_cast<const float4*>(qrow + 32 * ks + 8 * kq);
+      qr[ks][1] = *reinterpret_cast<const float4*>(qrow + 32 * ks + 8 * kq + 4);
+    }
+  };
+  auto convert_q = [&]() {
     const bool live = hcol < G;
-    const float* qrow = q + ((size_t)s * Hkv * G + (size_t)h * G + (live ? hcol : 0)) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       float v[8];
-      *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(qrow + 32 * ks + 8 * kq);
-      *reinterpret_cast<float4*>(v + 4) =
-          *reinterpret_cast<const float4*>(qrow + 32 * ks + 8 * kq + 4);
+      *reinterpret_cast<float4*>(v) = qr[ks][0];
+      *reinterpret_cast<float4*>(v + 4) = qr[ks][1];
       uint32_t w[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -311,45 +321,66 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // segments: the part of this wave's range that lies in one pair
+  // The wave's range is walked in windows of up to 64 blocks; a window may span several
+  // pairs.  Lane j looks up window block j in one pass (its pair by a short scan of the
+  // prefix, then list entry, page and valid tokens), so a pair change costs no new lookup.
+  // A segment is the part of a window in one pair; the next pair's query rows are fetched
+  // when a pair's blocks begin, so they have arrived by the time its successor starts.
+  // (The pair after p that holds blocks: the one holding block pfx[p + 1].)
+  auto next_pair = [&](int pp) {
+    const int end = __builtin_amdgcn_readfirstlane(pfx[pp + 1]);
+    while (pp < npairs - 1 && __builtin_amdgcn_readfirstlane(pfx[pp + 1]) <= end) ++pp;
+    return pp;
+  };
   int p = __builtin_amdgcn_readfirstlane(pair_of(pfx, npairs, b0));
-  for (int seg = b0; seg < b1;) {
-    while (__builtin_amdgcn_readfirstlane(pfx[p + 1]) <= seg) ++p;
-    const int seg_end = min(b1, __builtin_amdgcn_readfirstlane(pfx[p + 1]));
-    const int pstart = __builtin_amdgcn_readfirstlane(pfx[p]);
-    load_q(p);
-    reset();
-    for (int wb = seg; wb < seg_end; wb += kWave) {
-      // window: lane j looks up block wb + j (list entry, then page and valid tokens)
-      const int nw = min(kWave, seg_end - wb);
-      {
-        const int jl = min(lane, nw - 1);
-        const int blk = gpu_blocks[(size_t)p * list_stride + (wb + jl - pstart)];
-        const int len = seq_lens[p / Hkv];
-        w_page = table[(size_t)p * max_blocks + blk];
-        w_nval = min(BS, len - blk * BS);
+  fetch_q(p);
+  bool open = false;  // a partial of pair p is being accumulated
+  for (int wb = b0; wb < b1; wb += kWave) {
+    const int nw = min(kWave, b1 - wb);
+    {
+      const int g = wb + min(lane, nw - 1);
+      int pj = p;
+      while (pfx[pj + 1] <= g) ++pj;
+      const int blk = gpu_blocks[(size_t)pj * list_stride + (g - pfx[pj])];
+      const int len = seq_lens[pj / Hkv];
+      w_page = table[(size_t)pj * max_blocks + blk];
+      w_nval = min(BS, len - blk * BS);
+    }
+    for (int j = 0; j < nw;) {
+      if (!open) {
+        convert_q();
+        fetch_q(next_pair(p));
+        reset();
+        open = true;
       }
+      const int pend = __builtin_amdgcn_readfirstlane(pfx[p + 1]);
+      const int jend = min(nw, pend - wb);
       // HPB steps per block; a second half holding no valid token is fully masked.  Two
       // steps per iteration, the next one's loads in flight while one is computed.  The
       // loads are unconditional (steps past the end re-read the last step, lines that are
       // still cached) so every path has the same loads in flight, and the scheduling
       // barriers keep the compiler from sinking them to their use.
-      const int nst = nw * HPB;
+      const int nst = (jend - j) * HPB;
       StepRegs ra, rb;
-      load_step(0, 0, ra);
+      load_step(j, 0, ra);
       for (int st = 0; st < nst; st += 2) {
         const int s1 = min(st + 1, nst - 1), s2 = min(st + 2, nst - 1);
-        load_step(s1 / HPB, s1 % HPB, rb);
+        load_step(j + s1 / HPB, s1 % HPB, rb);
         __builtin_amdgcn_sched_barrier(0);
         compute_step(ra);
-        load_step(s2 / HPB, s2 % HPB, ra);
+        load_step(j + s2 / HPB, s2 % HPB, ra);
         __builtin_amdgcn_sched_barrier(0);
         if (st + 1 < nst) compute_step(rb);
       }
+      j = jend;
+      if (wb + jend == pend) {  // pair p ends here
+        finalize(p);
+        open = false;
+        p = next_pair(p);
+      }
     }
-    finalize(p);
-    seg = seg_end;
   }
+  if (open) finalize(p);  // the range ended inside pair p
 }
 
 // float32 KV: one wave per workgroup, the same balanced ranges, one block at a time.

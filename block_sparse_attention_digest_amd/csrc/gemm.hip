@@ -64,10 +64,10 @@ __global__ __launch_bounds__(640) void gemm_kernel(const uint16_t* __restrict__ 
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // Loads are issued unconditionally (k-steps past the slice are clamped to its last
-  // step and their B operand zeroed), so every path has the same loads in flight and the
+  // Loads are issued unconditionally (k-steps past the part are clamped to its last step
+  // and their B operand zeroed), so every path has the same loads in flight and the
   // compiler waits only for the group being multiplied.
-  uint4 wa[kGroup], wb[kGroup];
+  uint4 wa[kGroup], wb[kGroup], wc[kGroup];
   auto load_group = [&](uint4* dst, int s0) {
 #pragma unroll
     for (int u = 0; u < kGroup; ++u)
@@ -89,47 +89,58 @@ __global__ __launch_bounds__(640) void gemm_kernel(const uint16_t* __restrict__ 
     }
   };
 
-  // Staging of the x slice overlaps the first two W groups: the slice's loads are issued
-  // first (up to 2 x kStage per thread; rows past m are not read), then the W groups, so
-  // the waits before the LDS stores cover the slice only (loads complete in issue order).
+  // Staging of the x slice (up to 2 x kStage loads per thread in flight; rows past m are
+  // not read) comes before any W load: the barrier that ends it waits for every load the
+  // wave has in flight, and the slice's first touch on each XCD misses L2 and must not
+  // queue in HBM behind the W stream of the whole chip.
   {
     constexpr int kStage = 8;
     const int nthr = blockDim.x;
     const int chunks_per_row = kslice / 8;
     const int mrows = min(16 * MT, m - row0);
     const int total = mrows * chunks_per_row;
-    // chunk c of the slice (clamped to the last one: lanes past the end load and store
-    // that chunk's own value again, so there is no branch and the arrays stay in registers)
-    auto xload = [&](int c) -> uint4 {
-      c = min(c, total - 1);
-      const int r = c / chunks_per_row, q8 = c % chunks_per_row;
-      return *reinterpret_cast<const uint4*>(x + (size_t)(row0 + r) * k + k0 + 8 * q8);
-    };
-    auto xstore = [&](int c, uint4 v) {
-      c = min(c, total - 1);
-      const int r = c / chunks_per_row, q8 = c % chunks_per_row;
-      *reinterpret_cast<uint4*>(xs + r * ldx + 8 * q8) = v;
-    };
-    const int c0 = threadIdx.x;
+    // A thread's slots are c, c + nthr, c + 2 nthr, ...; their (row, chunk) positions are
+    // stepped incrementally (one division per thread: a division by a run-time value is a
+    // long instruction sequence).  Slots past the end clamp to the last chunk: those lanes
+    // load and store that chunk's own value again, so there is no branch and the arrays
+    // stay in registers.
+    const int dr = nthr / chunks_per_row, dq = nthr % chunks_per_row;
+    const int last_r = (total - 1) / chunks_per_row, last_q = (total - 1) % chunks_per_row;
+    int r = threadIdx.x / chunks_per_row, q = threadIdx.x % chunks_per_row;
+    // clamped (row, chunk) of each slot, chosen with integer selects: the staging is one
+    // basic block, so the compiler keeps every load ahead of the first store
+    int rs[2 * kStage], qs[2 * kStage];
+#pragma unroll
+    for (int j = 0; j < 2 * kStage; ++j) {
+      const bool past = (int)threadIdx.x + j * nthr >= total;
+      rs[j] = past ? last_r : r;
+      qs[j] = past ? last_q : q;
+      r += dr;
+      q += dq;
+      const bool wrap = q >= chunks_per_row;
+      q -= wrap ? chunks_per_row : 0;
+      r += wrap ? 1 : 0;
+    }
+    const uint16_t* xslice = x + (size_t)row0 * k + k0;
     uint4 va[kStage], vb[kStage];
 #pragma unroll
-    for (int j = 0; j < kStage; ++j) va[j] = xload(c0 + j * nthr);
+    for (int j = 0; j < kStage; ++j)
+      va[j] = *reinterpret_cast<const uint4*>(xslice + rs[j] * k + 8 * qs[j]);
 #pragma unroll
-    for (int j = 0; j < kStage; ++j) vb[j] = xload(c0 + (kStage + j) * nthr);
-    load_group(wa, 0);
-    load_group(wb, kGroup);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < kStage; ++j)
+      vb[j] = *reinterpret_cast<const uint4*>(xslice + rs[kStage + j] * k + 8 * qs[kStage + j]);
+    __builtin_amdgcn_sched_barrier(0);  // all of the slice's loads before the first store
 #pragma unroll
-    for (int j = 0; j < kStage; ++j) xstore(c0 + j * nthr, va[j]);
+    for (int j = 0; j < kStage; ++j)
+      *reinterpret_cast<uint4*>(xs + rs[j] * ldx + 8 * qs[j]) = va[j];
 #pragma unroll
-    for (int j = 0; j < kStage; ++j) xstore(c0 + (kStage + j) * nthr, vb[j]);
+    for (int j = 0; j < kStage; ++j)
+      *reinterpret_cast<uint4*>(xs + rs[kStage + j] * ldx + 8 * qs[kStage + j]) = vb[j];
     // larger slices than one round of 2 x kStage per thread (not the usual shapes)
-    for (int c1 = c0 + 2 * kStage * nthr; c1 < total; c1 += kStage * nthr) {
-      uint4 vt[kStage];
-#pragma unroll
-      for (int j = 0; j < kStage; ++j) vt[j] = xload(c1 + j * nthr);
-#pragma unroll
-      for (int j = 0; j < kStage; ++j) xstore(c1 + j * nthr, vt[j]);
+    for (int c1 = threadIdx.x + 2 * kStage * nthr; c1 < total; c1 += nthr) {
+      const int rr = c1 / chunks_per_row, qq = c1 % chunks_per_row;
+      *reinterpret_cast<uint4*>(xs + rr * ldx + 8 * qq) =
+          *reinterpret_cast<const uint4*>(x + (size_t)(row0 + rr) * k + k0 + 8 * qq);
     }
     // padding rows of the last row tile are zero
     for (int c = threadIdx.x; c < (16 * MT - mrows) * chunks_per_row; c += nthr) {
@@ -139,16 +150,25 @@ __global__ __launch_bounds__(640) void gemm_kernel(const uint16_t* __restrict__ 
   }
   __syncthreads();  // x slice staged
 
-  // Both halves always run (a group past the part multiplies zeros): with no early exit
-  // the compiler cannot sink a group's loads down to the block that uses them, and the
-  // scheduling barriers keep it from moving them within the iteration.  Each group is
-  // loaded two groups ahead of its use.
-  for (int s0 = 0; s0 < nsteps; s0 += 2 * kGroup) {
+  // W streams through three register groups (24 k-steps in flight: the whole part, for
+  // parts of up to 24 k-steps); each group is refilled right after it is multiplied.  All
+  // three thirds always run (a group past the part multiplies zeros and its refill re-reads
+  // the last step, a cached line): with no early exit the compiler cannot sink a group's
+  // loads down to the block that uses them, and the scheduling barriers keep it from
+  // moving them within the iteration.
+  load_group(wa, 0);
+  load_group(wb, kGroup);
+  load_group(wc, 2 * kGroup);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int s0 = 0; s0 < nsteps; s0 += 3 * kGroup) {
     mma_group(wa, s0);
-    load_group(wa, s0 + 2 * kGroup);
+    load_group(wa, s0 + 3 * kGroup);
     __builtin_amdgcn_sched_barrier(0);
     mma_group(wb, s0 + kGroup);
-    load_group(wb, s0 + 3 * kGroup);
+    load_group(wb, s0 + 4 * kGroup);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_group(wc, s0 + 2 * kGroup);
+    load_group(wc, s0 + 5 * kGroup);
     __builtin_amdgcn_sched_barrier(0);
   }
 
