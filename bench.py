@@ -4,16 +4,19 @@
 Workload: the Qwen3-14B-shaped 40-layer decode step, batch 40, context 65536 (2048 blocks
 of 32 per sequence and KV head), budget 2048 tokens (64 blocks), bf16 KV with mean
 digests, a resident pool of 128 blocks per (sequence, KV head) per layer.  One step runs
-Algorithm 1 over all 40 layers: Q^i and Q_pred^{i+1} GEMMs, digest scoring + top-k + split
-for layer i+1 (with the offloaded lists copied to pinned host memory on a copy stream),
-block-sparse attention over the resident blocks of layer i and the merge with layer i's
-host partial.  Inputs are synthetic (seeded) and resident in HBM before timing.
+Algorithm 1 over all 40 layers: the Q^i GEMM, and on a side stream the Q_pred^{i+1} GEMM
+with digest scoring + top-k + split for layer i+1 (the offloaded lists written straight
+into host mirrors), then block-sparse attention over the resident blocks of layer i and
+the merge with layer i's host partial.  Inputs are synthetic (seeded) and resident in HBM
+before timing.
 
-Prints one JSON line: seq-layers/s (= batch * layers / step time), the attention
-kernel's achieved HBM bandwidth against the 8 TB/s peak (timed per launch with HIP
-events), and the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line: seq-layers/s (= batch * layers / step time) over K replays of the
+step captured as a HIP graph; the attention kernel's achieved HBM bandwidth against the
+8 TB/s peak, from HIP events recorded at each attention launch's own start and end, both
+inside eager steps (sharing the GPU with the side stream) and launched alone; and the CPU
+oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-graph]
 """
 
 from __future__ import annotations
@@ -41,9 +44,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--no-graph", action="store_true", help="time eager launches")
-    ap.add_argument("--profile-steps", type=int, default=5,
-                    help="eager steps whose attention launches are timed with events")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager steps instead of replays of the step captured as a graph")
+    ap.add_argument("--profile-steps", type=int, default=3,
+                    help="eager steps after the timed region whose attention launches are "
+                         "timed with kernel-precise HIP events")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -245,29 +250,30 @@ def main():
     n_cpu_sums = [int(L["n_cpu"].sum()) for L in layers]
     log("warmup done")
 
-    mode = "eager"
-    graph = None
+    # The timed region: K replays of the step captured as a HIP graph (the way a serving
+    # loop runs it), each checked first to reproduce the eager result; eager steps if the
+    # capture is unavailable.
+    mode, graph = "eager", None
     if not args.no_graph:
         try:
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
                 step()
             torch.cuda.synchronize()
-            ok = True
-            for _ in range(3):  # every replay must reproduce the eager result
+            same = True
+            for _ in range(3):
                 layers[-1]["out_o"].zero_()
                 graph.replay()
                 torch.cuda.synchronize()
-                ok &= bool(torch.equal(layers[-1]["out_o"], ref_out))
-            if ok:
+                same &= bool(torch.equal(layers[-1]["out_o"], ref_out))
+            if same:
                 mode = "hip-graph"
             else:
-                log("graph replay differs from eager launches: timing eager launches")
+                log("graph replay differs from eager launches: timing eager steps")
                 graph = None
         except Exception as e:  # noqa: BLE001
-            log(f"graph capture unavailable ({e}): timing eager launches")
+            log(f"graph capture unavailable ({e}): timing eager steps")
             graph = None
-
     run = graph.replay if graph is not None else step
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -281,23 +287,47 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
     log(f"timed {args.steps} steps ({mode}): {ms_step:.3f} ms/step (wall {wall:.3f} s)")
 
-    # attention kernel timed per launch with HIP events (eager steps)
+    # Attention launches timed with HIP events recorded at the kernel's own start and end on
+    # its stream (sa_profile_attention; a graph cannot hold such events, and they slow the
+    # step down by about a tenth, so they are taken outside the timed region):
+    #  (1) inside eager steps, sharing the GPU with the side stream as in the step;
+    #  (2) alone: each layer's attention launched by itself, with the same lists.
+    def timed_launches(n, fn):
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        stops = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in starts + stops:
+            e.record()
+        torch.cuda.synchronize()
+        B.sa_profile_attention(starts, stops)
+        fn()
+        torch.cuda.synchronize()
+        B.sa_profile_attention([], [])
+        return [starts[j].elapsed_time(stops[j]) for j in range(n)]
+
     nprof = args.profile_steps * wl.layers
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(nprof)]
-    stops = [torch.cuda.Event(enable_timing=True) for _ in range(nprof)]
-    for e in starts + stops:
-        e.record()
-    torch.cuda.synchronize()
-    B.sa_profile_attention(starts, stops)
-    for _ in range(args.profile_steps):
-        step()
-    torch.cuda.synchronize()
-    B.sa_profile_attention([], [])
-    attn_ms = [starts[j].elapsed_time(stops[j]) for j in range(nprof)]
+    attn_ms = timed_launches(nprof, lambda: [step() for _ in range(args.profile_steps)])
     attn_avg_ms = sum(attn_ms) / len(attn_ms)
     attn_bytes_avg = sum(attention_bytes(wl, n_gpu_sums[j % wl.layers])
                          for j in range(nprof)) / nprof
     achieved = attn_bytes_avg / (attn_avg_ms * 1e-3) / 1e9
+    log(f"attention in the step: {attn_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s")
+
+    rows = wl.batch * wl.num_q_heads
+    o_iso = torch.empty((rows, wl.head_dim), dtype=torch.float32, device="cuda")
+    sel_ws = B.workspace(B.sa_workspace_bytes(dims, wl.top_k))
+    q_iso = torch.randn((wl.batch, wl.num_q_heads, wl.head_dim), device="cuda",
+                        generator=wk.generator(wl, "bench_q", "cuda"))
+
+    def alone():
+        for L in layers:
+            B.sa_sparse_decode(dims, q_iso, L["k_pool"], L["v_pool"], L["block_table"], lens,
+                               L["gpu_blocks"], L["n_gpu"], wl.top_k, wl.scale, o_iso, ws=sel_ws)
+    alone()
+    iso_ms = timed_launches(wl.layers, alone)
+    iso_avg_ms = sum(iso_ms) / len(iso_ms)
+    iso_bytes_avg = sum(attention_bytes(wl, n) for n in n_gpu_sums) / wl.layers
+    iso_achieved = iso_bytes_avg / (iso_avg_ms * 1e-3) / 1e9
+    log(f"attention alone: {iso_avg_ms * 1e3:.1f} us avg, {iso_achieved:.0f} GB/s")
     total_bytes = step_bytes(wl, n_gpu_sums)
     log(f"attention: {attn_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s algorithmic")
 
@@ -328,7 +358,7 @@ def main():
                    "budget_tokens": wl.top_k * wl.block_size, "q_heads": wl.num_q_heads,
                    "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "hidden": wl.hidden,
                    "digest": kind, "resident_pool_blocks": wl.pool_blocks,
-                   "launch": mode, "parallelism": "single-gpu"},
+                   "launch": mode + ", two streams", "parallelism": "single-gpu"},
         "step_hbm_gbs": round(total_bytes / (ms_step * 1e-3) / 1e9, 1),
         "step_frac_of_peak": round(total_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "cpu_ratio": round(sum(n_cpu_sums) / (wl.layers * wl.batch * wl.num_kv_heads * wl.top_k), 4),
@@ -336,7 +366,16 @@ def main():
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(attn_avg_ms * 1e3, 2),
-                     "algorithmic_bytes_per_launch": int(attn_bytes_avg)},
+                     "algorithmic_bytes_per_launch": int(attn_bytes_avg),
+                     "measured": f"{nprof} launches in {args.profile_steps} eager steps "
+                                 "after the timed region, HIP events at each kernel's start "
+                                 "and end"},
+        "roofline_isolated": {"kernel": "attn_bf16_kernel (GPUATTN), launched alone",
+                              "bound": "hbm", "achieved": round(iso_achieved, 1),
+                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": round(iso_achieved / PEAK_HBM_GBS, 4),
+                              "avg_launch_us": round(iso_avg_ms * 1e3, 2),
+                              "algorithmic_bytes_per_launch": int(iso_bytes_avg)},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
