@@ -150,14 +150,14 @@ sa_status check_scale(float scale) {
 
 // selection of one layer: scores, top-k and split in one launch (scores written out only
 // when asked for)
-sa_status run_select(const sa::Shape& s, bool minmax, const float* q, const void* digests,
+sa_status run_select(const sa::Shape& s, bool minmax, const sa::QParts& q, const void* digests,
                      const int32_t* seq_lens, int top_k, const int32_t* block_table,
                      int32_t* gpu_blocks, int32_t* n_gpu, int32_t* cpu_blocks, int32_t* n_cpu,
                      float* scores, int32_t* cpu_blocks_host, int32_t* n_cpu_host,
-                     hipStream_t stream) {
+                     int32_t* gpu_pages, hipStream_t stream) {
   SA_HIP(sa::launch_select(s, minmax, q, digests, seq_lens, top_k, block_table, gpu_blocks,
                            n_gpu, cpu_blocks, n_cpu, scores, cpu_blocks_host, n_cpu_host,
-                           stream),
+                           gpu_pages, stream),
          "select kernel");
   return SA_OK;
 }
@@ -293,8 +293,10 @@ sa_status sa_select_blocks(const sa_dims* dims, sa_digest_kind kind, const float
   const Layout L = layout(s, top_k);
   if (!ws || ws_bytes < L.total)
     return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, L.total);
-  SA_CHECK(run_select(s, kind == SA_DIGEST_MINMAX, q, digests, seq_lens, top_k, block_table,
-                      gpu_blocks, n_gpu, cpu_blocks, n_cpu, scores, nullptr, nullptr, stream));
+  SA_CHECK(run_select(s, kind == SA_DIGEST_MINMAX, sa::plain_query(q, s.Hq * s.d), digests,
+                      seq_lens, top_k, block_table,
+                      gpu_blocks, n_gpu, cpu_blocks, n_cpu, scores, nullptr, nullptr, nullptr,
+                      stream));
   return ok();
 }
 
@@ -325,8 +327,9 @@ static sa_status decode_common(const sa_dims* dims, const float* q, const void* 
   float* parts = (float*)((char*)ws + L.parts);
   hipEvent_t e0, e1;
   next_profile_events(&e0, &e1);
-  SA_HIP(sa::launch_attention(s, L.plan, q, k_pool, v_pool, block_table, seq_lens, gpu_blocks,
-                              n_gpu, list_stride, scale, parts, stream, e0, e1),
+  SA_HIP(sa::launch_attention(s, L.plan, sa::plain_query(q, s.Hq * s.d), k_pool, v_pool,
+                              block_table, seq_lens, gpu_blocks, nullptr, n_gpu, list_stride,
+                              scale, parts, stream, e0, e1),
          "attention kernel");
   SA_HIP(sa::launch_reduce(s, L.plan, n_gpu, parts, host_o, host_m, host_l, n_cpu, o, m, l,
                            stream),
@@ -383,7 +386,7 @@ sa_status sa_merge(int32_t rows, int32_t d, const float* o_a, const float* m_a,
 
 namespace {
 struct StepLayout {
-  size_t q_true, q_pred[2], gemm[2], sel, total;
+  size_t q_true, q_pred[2], gemm[2], pages[2], sel, total;
   sa::GemmPlan plan_dual, plan_single;
   Layout sel_layout;
 };
@@ -400,7 +403,12 @@ StepLayout step_layout(const sa::Shape& s, int hidden, int top_k) {
   const size_t gbytes = align_up(std::max(L.plan_dual.ws_bytes, L.plan_single.ws_bytes));
   L.gemm[0] = 3 * qbytes;
   L.gemm[1] = L.gemm[0] + gbytes;
-  L.sel = L.gemm[1] + gbytes;
+  // pages of the resident lists, written by the selection for the attention kernel; two
+  // buffers (by layer parity), as the next layer's selection runs during this attention
+  const size_t pbytes = align_up((size_t)s.B * s.Hkv * top_k * sizeof(int32_t));
+  L.pages[0] = L.gemm[1] + gbytes;
+  L.pages[1] = L.pages[0] + pbytes;
+  L.sel = L.pages[1] + pbytes;
   L.sel_layout = layout(s, top_k);
   L.total = L.sel + L.sel_layout.total;
   return L;
@@ -451,6 +459,7 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
   float* q_true = (float*)(base + SL.q_true);
   float* q_pred[2] = {(float*)(base + SL.q_pred[0]), (float*)(base + SL.q_pred[1])};
   float* gemm_ws[2] = {(float*)(base + SL.gemm[0]), (float*)(base + SL.gemm[1])};
+  int32_t* pages[2] = {(int32_t*)(base + SL.pages[0]), (int32_t*)(base + SL.pages[1])};
   char* sel_base = base + SL.sel;
   float* parts = (float*)(sel_base + SL.sel_layout.parts);
   const bool minmax = kind == SA_DIGEST_MINMAX;
@@ -492,21 +501,26 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
       if (st != SA_OK) break;
     }
     // 1. Q^i = W_Q^i X^i on `stream`.  Without a side stream, Q_pred^{i+1} = W_Q^{i+1} X^i
-    //    comes from the same launch (both weights share X^i).
+    //    comes from the same launch (both weights share X^i).  The GEMMs leave their k-slice
+    //    partials; the selection and attention kernels sum them as they read the query.
+    sa::QParts q_cur, q_next{};
     if (side_stream || !has_next) {
       e = sa::launch_gemm(s.B, n, hidden, L.x, 1, L.w_q, q_true, nullptr, nullptr, gemm_ws[0],
-                          SL.plan_single, stream);
+                          SL.plan_single, stream, false);
+      q_cur = sa::gemm_result(SL.plan_single, s.B, n, 1, 0, q_true, gemm_ws[0]);
     } else {
       e = sa::launch_gemm(s.B, n, hidden, L.x, 2, L.w_q, q_true, layers[i + 1].w_q, qp,
-                          gemm_ws[0], SL.plan_dual, stream);
+                          gemm_ws[0], SL.plan_dual, stream, false);
+      q_cur = sa::gemm_result(SL.plan_dual, s.B, n, 2, 0, q_true, gemm_ws[0]);
+      q_next = sa::gemm_result(SL.plan_dual, s.B, n, 2, 1, qp, gemm_ws[0]);
     }
     if (e != hipSuccess) { st = hip_fail(e, "GEMM kernel"); break; }
     // 2. the first layer selects with its own query (on `stream`: its attention needs it);
     //    the selection kernels also write the offloaded lists into the host mirrors
     if (i == 0) {
-      st = run_select(s, minmax, q_true, L.digests, seq_lens, top_k, L.block_table,
+      st = run_select(s, minmax, q_cur, L.digests, seq_lens, top_k, L.block_table,
                       L.gpu_blocks, L.n_gpu, L.cpu_blocks, L.n_cpu, nullptr, L.cpu_blocks_host,
-                      L.n_cpu_host, stream);
+                      L.n_cpu_host, pages[0], stream);
       if (st == SA_OK && side_stream) st = order(stream, side_stream);
       if (st != SA_OK) break;
     }
@@ -517,13 +531,14 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
       const sa_layer& N = layers[i + 1];
       if (side_stream) {
         e = sa::launch_gemm(s.B, n, hidden, L.x, 1, N.w_q, qp, nullptr, nullptr, gemm_ws[1],
-                            SL.plan_single, side_stream);
+                            SL.plan_single, side_stream, false);
         if (e != hipSuccess) st = hip_fail(e, "GEMM kernel");
+        q_next = sa::gemm_result(SL.plan_single, s.B, n, 1, 0, qp, gemm_ws[1]);
       }
       if (st == SA_OK)
-        st = run_select(s, minmax, qp, N.digests, seq_lens, top_k, N.block_table,
+        st = run_select(s, minmax, q_next, N.digests, seq_lens, top_k, N.block_table,
                         N.gpu_blocks, N.n_gpu, N.cpu_blocks, N.n_cpu, nullptr,
-                        N.cpu_blocks_host, N.n_cpu_host, sel_stream);
+                        N.cpu_blocks_host, N.n_cpu_host, pages[(i + 1) & 1], sel_stream);
       if (st != SA_OK) break;
     }
     // 4. layer i's lists were selected on the side stream one layer earlier
@@ -540,9 +555,9 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
     // 5. GPU attention of layer i, merged with its host partial
     hipEvent_t e0, e1;
     next_profile_events(&e0, &e1);
-    e = sa::launch_attention(s, SL.sel_layout.plan, q_true, L.k_pool, L.v_pool, L.block_table,
-                             seq_lens, L.gpu_blocks, L.n_gpu, top_k, scale, parts, stream, e0,
-                             e1);
+    e = sa::launch_attention(s, SL.sel_layout.plan, q_cur, L.k_pool, L.v_pool, L.block_table,
+                             seq_lens, L.gpu_blocks, pages[i & 1], L.n_gpu, top_k, scale,
+                             parts, stream, e0, e1);
     if (e != hipSuccess) { st = hip_fail(e, "attention kernel"); break; }
     e = sa::launch_reduce(s, SL.sel_layout.plan, L.n_gpu, parts, L.host_o, L.host_m, L.host_l,
                           L.n_cpu, L.out_o, L.out_m, L.out_l, stream);

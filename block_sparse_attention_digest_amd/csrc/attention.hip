@@ -47,6 +47,8 @@ namespace sa {
 namespace {
 
 constexpr int kAttnWaves = 4;            // waves per workgroup (bf16 path)
+constexpr int kQStage = 4;               // pairs whose summed queries a workgroup stages
+constexpr int kPartGroup = 4;            // query parts loaded together
 constexpr int kStep = 16;                // tokens per wave step (one MFMA tile)
 constexpr int kWavesPerCU = 8;           // resident waves per CU the grid is sized for
 constexpr int kMaxWaves = 256 * kWavesPerCU;
@@ -122,13 +124,56 @@ __device__ __forceinline__ int pair_of(const int* pfx, int npairs, int g) {
   return lo;
 }
 
+// The query rows of pairs [q_lo, q_lo + q_n) summed from their parts into LDS, in part
+// order: every thread of the workgroup takes part (all of its loads of a group of parts are
+// in flight together); ends with a barrier.
+template <int G, int D>
+__device__ void stage_queries(const QParts& q, int Hkv, int q_lo, int q_n, float* q_lds) {
+  constexpr int kPerPair = G * D / 4;  // float4 per pair
+  constexpr int kSlots = (kQStage * kPerPair + 255) / 256;
+  const int total = q_n * kPerPair;
+  const int nt = blockDim.x;
+  const float* src[kSlots];
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) {
+    const int i = min((int)threadIdx.x + j * nt, total - 1);  // past the end: a re-read
+    const int pair = q_lo + i / kPerPair, e = i % kPerPair;
+    src[j] = q.base + (size_t)(pair / Hkv) * q.row_stride + (size_t)(pair % Hkv) * G * D + 4 * e;
+  }
+  float4 acc[kSlots];
+  for (int p0 = 0; p0 < q.parts; p0 += kPartGroup) {
+    float4 t[kPartGroup][kSlots];
+#pragma unroll
+    for (int u = 0; u < kPartGroup; ++u)
+#pragma unroll
+      for (int j = 0; j < kSlots; ++j)
+        t[u][j] = *reinterpret_cast<const float4*>(src[j] + (size_t)min(p0 + u, q.parts - 1) *
+                                                               q.part_stride);
+#pragma unroll
+    for (int u = 0; u < kPartGroup; ++u)
+#pragma unroll
+      for (int j = 0; j < kSlots; ++j) {
+        if (p0 + u == 0) { acc[j] = t[u][j]; continue; }
+        if (p0 + u >= q.parts) continue;
+        acc[j].x += t[u][j].x; acc[j].y += t[u][j].y;
+        acc[j].z += t[u][j].z; acc[j].w += t[u][j].w;
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) {
+    const int i = (int)threadIdx.x + j * nt;
+    if (i < total) *reinterpret_cast<float4*>(q_lds + 4 * i) = acc[j];
+  }
+  __syncthreads();
+}
+
 template <int D, int BS, int G>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
-    const float* __restrict__ q, const uint16_t* __restrict__ k_pool,
+    const QParts q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ gpu_blocks,
-    const int32_t* __restrict__ n_gpu, int list_stride, int Hkv, int max_blocks, int npairs,
-    int W, float scale_log2, float* __restrict__ ws) {
+    const int32_t* __restrict__ gpu_pages, const int32_t* __restrict__ n_gpu, int list_stride,
+    int Hkv, int max_blocks, int npairs, int W, float scale_log2, float* __restrict__ ws) {
   constexpr int KS = D / 32;          // MFMA k-steps over the head dimension
   constexpr int HPB = BS / kStep;     // 16-token steps per block (1 or 2)
   constexpr int VLPR = D / 8;         // lanes per V row
@@ -136,6 +181,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   constexpr int VJ = kStep / VTPI;    // V loads per lane per step
 
   extern __shared__ int pfx[];        // [npairs + 1]
+  __shared__ float q_lds[kQStage * G * D];
   __shared__ float p_lds[kAttnWaves][kStep][8];
   __shared__ float a_lds[kAttnWaves][8];
   __shared__ int wave_tot[kAttnWaves];
@@ -152,7 +198,38 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   const int T = __builtin_amdgcn_readfirstlane(pfx[npairs]);
   const int gw = blockIdx.x * kAttnWaves + wave;
   if (T == 0) return;
+  // the queries of the first kQStage pairs the workgroup's block range touches
+  int q_lo = 0, q_n = 0;
+  {
+    const int lo = wave_start(blockIdx.x * kAttnWaves, T, W);
+    const int hi = wave_start((blockIdx.x + 1) * kAttnWaves, T, W);
+    if (lo < hi) {
+      q_lo = __builtin_amdgcn_readfirstlane(pair_of(pfx, npairs, lo));
+      q_n = min(kQStage, __builtin_amdgcn_readfirstlane(pair_of(pfx, npairs, hi - 1)) - q_lo + 1);
+    }
+  }
   const int b0 = wave_start(gw, T, W), b1 = wave_start(gw + 1, T, W);
+
+  // The wave's range is walked in windows of up to 64 blocks; a window may span several
+  // pairs.  Lane j looks up window block j in one pass (its pair by a short scan of the
+  // prefix, then list entry, valid tokens and page -- from the page list when one is
+  // given, else from the block table), so a pair change costs no new lookup.
+  int l_blk = 0, l_len = 0, l_page = 0;
+  auto lookup = [&](int wb, int nw, int pstart) {
+    const int g = wb + min(lane, nw - 1);
+    int pj = pstart;
+    while (pfx[pj + 1] <= g) ++pj;
+    const size_t idx = (size_t)pj * list_stride + (g - pfx[pj]);
+    l_blk = gpu_blocks[idx];
+    l_len = seq_lens[pj / Hkv];
+    l_page = gpu_pages ? gpu_pages[idx] : table[(size_t)pj * max_blocks + l_blk];
+  };
+  // The first window's lookup is issued before the query staging so that their loads are
+  // in flight together (a wave with no blocks looks up the last block, unused).
+  const int gfirst = min(b0, T - 1);
+  int p = __builtin_amdgcn_readfirstlane(pair_of(pfx, npairs, gfirst));
+  lookup(gfirst, b0 < b1 ? min(kWave, b1 - b0) : 1, p);
+  if (q_n > 0) stage_queries<G, D>(q, Hkv, q_lo, q_n, q_lds);
   if (b0 >= b1) return;
 
   const int c16 = lane % 16;   // MFMA column (head / hi-lo) and token row in the tile
@@ -161,17 +238,39 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   const int vcg = lane % VLPR, vts = lane / VLPR;
 
   // Q^T as the MFMA B operand (hi columns 0..7, lo 8..15): the float rows of a pair are
-  // fetched ahead (fetch_q, into qr) and converted when the pair's blocks begin
+  // fetched ahead (fetch_q, into qr) and converted when the pair's blocks begin.  Staged
+  // pairs come from LDS; any other pair (a workgroup range crossing more than kQStage
+  // pairs) is summed from its parts in global memory.
   bf16x8 qb[KS];
   float4 qr[KS][2];
   auto fetch_q = [&](int pair) {
     pair = min(pair, npairs - 1);
-    const int s = pair / Hkv, h = pair % Hkv;
-    const float* qrow = q + ((size_t)s * Hkv * G + (size_t)h * G + (hcol < G ? hcol : 0)) * D;
+    const int row = hcol < G ? hcol : 0;
+    if (pair - q_lo < q_n && pair >= q_lo) {
+      const float* qrow = q_lds + ((pair - q_lo) * G + row) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qr[ks][0] = *reinterpret_cast<const float4*>(qrow + 32 * ks + 8 * kq);
-      qr[ks][1] = *reinterpret_cast<const float4*>(qrow + 32 * ks + 8 * kq + 4);
+      for (int ks = 0; ks < KS; ++ks) {
+        qr[ks][0] = *reinterpret_cast<const float4*>(qrow + 32 * ks + 8 * kq);
+        qr[ks][1] = *reinterpret_cast<const float4*>(qrow + 32 * ks + 8 * kq + 4);
+      }
+    } else {
+      const float* qrow = q.base + (size_t)(pair / Hkv) * q.row_stride +
+                          ((size_t)(pair % Hkv) * G + row) * D;
+      for (int part = 0; part < q.parts; ++part) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const float4 v = *reinterpret_cast<const float4*>(
+                qrow + (size_t)part * q.part_stride + 32 * ks + 8 * kq + 4 * hh);
+            if (part == 0) {
+              qr[ks][hh] = v;
+            } else {
+              qr[ks][hh].x += v.x; qr[ks][hh].y += v.y;
+              qr[ks][hh].z += v.z; qr[ks][hh].w += v.w;
+            }
+          }
+      }
     }
   };
   auto convert_q = [&]() {
@@ -321,9 +420,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // The wave's range is walked in windows of up to 64 blocks; a window may span several
-  // pairs.  Lane j looks up window block j in one pass (its pair by a short scan of the
-  // prefix, then list entry, page and valid tokens), so a pair change costs no new lookup.
   // A segment is the part of a window in one pair; the next pair's query rows are fetched
   // when a pair's blocks begin, so they have arrived by the time its successor starts.
   // (The pair after p that holds blocks: the one holding block pfx[p + 1].)
@@ -332,20 +428,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     while (pp < npairs - 1 && __builtin_amdgcn_readfirstlane(pfx[pp + 1]) <= end) ++pp;
     return pp;
   };
-  int p = __builtin_amdgcn_readfirstlane(pair_of(pfx, npairs, b0));
   fetch_q(p);
   bool open = false;  // a partial of pair p is being accumulated
   for (int wb = b0; wb < b1; wb += kWave) {
     const int nw = min(kWave, b1 - wb);
-    {
-      const int g = wb + min(lane, nw - 1);
-      int pj = p;
-      while (pfx[pj + 1] <= g) ++pj;
-      const int blk = gpu_blocks[(size_t)pj * list_stride + (g - pfx[pj])];
-      const int len = seq_lens[pj / Hkv];
-      w_page = table[(size_t)pj * max_blocks + blk];
-      w_nval = min(BS, len - blk * BS);
-    }
+    if (wb != b0) lookup(wb, nw, p);
+    w_page = l_page;
+    w_nval = min(BS, l_len - l_blk * BS);
     for (int j = 0; j < nw;) {
       if (!open) {
         convert_q();
@@ -386,7 +475,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
 // float32 KV: one wave per workgroup, the same balanced ranges, one block at a time.
 template <int D, int BS>
 __global__ __launch_bounds__(64) void attn_f32_kernel(
-    const float* __restrict__ q, const float* __restrict__ k_pool,
+    const QParts q, const float* __restrict__ k_pool,
     const float* __restrict__ v_pool, const int32_t* __restrict__ table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ gpu_blocks,
     const int32_t* __restrict__ n_gpu, int list_stride, int Hkv, int G, int max_blocks,
@@ -436,8 +525,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
       cur_pair = p;
       const int s = p / Hkv, h = p % Hkv;
       __syncthreads();
-      for (int i = lane; i < G * D; i += kWave)
-        qs[i / D][i % D] = q[((size_t)s * Hkv * G + (size_t)h * G) * D + i];
+      const float* qrow = q.base + (size_t)s * q.row_stride + (size_t)h * G * D;
+      for (int i = lane; i < G * D; i += kWave) {
+        float v = qrow[i];
+        for (int part = 1; part < q.parts; ++part) v += qrow[(size_t)part * q.part_stride + i];
+        qs[i / D][i % D] = v;
+      }
     }
     const int blk = gpu_blocks[(size_t)p * list_stride + (g_blk - pfx[p])];
     const int page = table[(size_t)p * max_blocks + blk];
@@ -481,8 +574,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 // the pair's blocks and, when given, the host partial; write the normalised output.  The
 // loads come in two rounds: first the pair's count and prefix and the host partial, then
 // every covering wave's (m, l) (one per lane) together with the o vectors of the first
-// kPre of them; only pairs covered by more waves than that read further o vectors one by
-// one.
+// kPre of them (a pair usually spans fewer waves); only pairs covered by more waves than
+// that read further o vectors one by one.
 template <int D>
 __global__ __launch_bounds__(256) void reduce_kernel(
     const float* __restrict__ ws, int npairs, int W, int G, int Hkv, int rows,
@@ -491,7 +584,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(
     const int32_t* __restrict__ n_cpu, float* __restrict__ o, float* __restrict__ m,
     float* __restrict__ l) {
   constexpr int CPL = D / kWave;
-  constexpr int kPre = 4;
+  constexpr int kPre = 16;
   const int lane = threadIdx.x % kWave;
   const int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (row >= rows) return;
@@ -627,9 +720,10 @@ __global__ __launch_bounds__(256) void merge_kernel(int rows, int d, const float
 }
 
 template <int D, int BS>
-hipError_t attn_bf16_g(const Shape& s, const AttnPlan& p, const float* q, const void* k,
+hipError_t attn_bf16_g(const Shape& s, const AttnPlan& p, const QParts& q, const void* k,
                        const void* v, const int32_t* t, const int32_t* lens,
-                       const int32_t* gb, const int32_t* ng, int stride, float sl2,
+                       const int32_t* gb, const int32_t* gp, const int32_t* ng, int stride,
+                       float sl2,
                        float* ws, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const int npairs = s.B * s.Hkv;
   const dim3 grid(p.waves / kAttnWaves), block(kAttnWaves * kWave);
@@ -638,7 +732,7 @@ hipError_t attn_bf16_g(const Shape& s, const AttnPlan& p, const float* q, const 
 #define SA_ATTN_CASE(GG)                                                                     \
   case GG:                                                                                   \
     hipExtLaunchKernelGGL((attn_bf16_kernel<D, BS, GG>), grid, block, lds, st, e0, e1, 0, q, \
-                          (const uint16_t*)k, (const uint16_t*)v, t, lens, gb, ng, stride,    \
+                          (const uint16_t*)k, (const uint16_t*)v, t, lens, gb, gp, ng, stride,\
                           s.Hkv, s.max_blocks, npairs, p.waves, sl2, ws);                    \
     break;
   switch (s.G) {
@@ -651,9 +745,10 @@ hipError_t attn_bf16_g(const Shape& s, const AttnPlan& p, const float* q, const 
 }
 
 template <int D, int BS>
-hipError_t attn_f32(const Shape& s, const AttnPlan& p, const float* q, const void* k,
+hipError_t attn_f32(const Shape& s, const AttnPlan& p, const QParts& q, const void* k,
                     const void* v, const int32_t* t, const int32_t* lens, const int32_t* gb,
-                    const int32_t* ng, int stride, float sl2, float* ws, hipStream_t st,
+                    const int32_t*, const int32_t* ng, int stride, float sl2, float* ws,
+                    hipStream_t st,
                     hipEvent_t e0, hipEvent_t e1) {
   const int npairs = s.B * s.Hkv;
   const size_t lds = (size_t)(npairs + 1) * sizeof(int);
@@ -677,14 +772,15 @@ AttnPlan attn_plan(const Shape& s, int list_stride) {
   return p;
 }
 
-hipError_t launch_attention(const Shape& s, const AttnPlan& plan, const float* q,
+hipError_t launch_attention(const Shape& s, const AttnPlan& plan, const QParts& q,
                             const void* k_pool, const void* v_pool,
                             const int32_t* block_table, const int32_t* seq_lens,
-                            const int32_t* gpu_blocks, const int32_t* n_gpu, int list_stride,
-                            float scale, float* partials, hipStream_t stream,
-                            hipEvent_t ev_start, hipEvent_t ev_stop) {
+                            const int32_t* gpu_blocks, const int32_t* gpu_pages,
+                            const int32_t* n_gpu, int list_stride, float scale,
+                            float* partials, hipStream_t stream, hipEvent_t ev_start,
+                            hipEvent_t ev_stop) {
   const float sl2 = scale * kLog2e;
-#define SA_ARGS plan, q, k_pool, v_pool, block_table, seq_lens, gpu_blocks, n_gpu, \
+#define SA_ARGS plan, q, k_pool, v_pool, block_table, seq_lens, gpu_blocks, gpu_pages, n_gpu, \
                 list_stride, sl2, partials, stream, ev_start, ev_stop
   if (s.bf16) {
     if (s.d == 128) return s.bs == 32 ? attn_bf16_g<128, 32>(s, SA_ARGS) : attn_bf16_g<128, 16>(s, SA_ARGS);

@@ -284,7 +284,7 @@ GemmPlan gemm_plan(int m, int n_total, int k) {
 
 hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void* w0,
                        float* q0, const void* w1, float* q1, float* ws, const GemmPlan& plan,
-                       hipStream_t stream) {
+                       hipStream_t stream, bool sum_slices) {
   const int n_total = n * nprob;
   const int mt = row_tiles(m);
   const int tiles = n_total / 16;
@@ -306,11 +306,18 @@ hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void
   }
 #undef SA_GEMM_CASE
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || plan.ksplit == 1) return e;
+  if (e != hipSuccess || plan.ksplit == 1 || !sum_slices) return e;
   const long total4 = (long)m * n_total / 4;
   hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)((total4 + 255) / 256)), dim3(256), 0,
                      stream, ws, m, n, n_total, plan.ksplit, q0, Q1);
   return hipGetLastError();
+}
+
+QParts gemm_result(const GemmPlan& plan, int m, int n, int nprob, int prob, const float* q,
+                   const float* ws) {
+  if (plan.ksplit == 1) return plain_query(q, n);  // written straight to q
+  const size_t n_total = (size_t)n * nprob;
+  return QParts{ws + (size_t)prob * n, plan.ksplit, (size_t)m * n_total, n_total};
 }
 
 }  // namespace sa

@@ -25,6 +25,16 @@ hipError_t launch_build_digests(const Shape& s, bool minmax, const void* k_pool,
                                 const int32_t* block_table, const int32_t* seq_lens,
                                 void* digests, hipStream_t stream);
 
+// A float32 query [B][Hq][d] held as the sum of `parts` arrays (the k-slice partials of the
+// query GEMM, or one plain array), summed by its consumer in part order.
+struct QParts {
+  const float* base;   // part 0, element (row 0, column 0)
+  int parts;           // >= 1
+  size_t part_stride;  // floats from one part to the next
+  size_t row_stride;   // floats from one sequence row to the next (>= Hq * d)
+};
+inline QParts plain_query(const float* q, int n) { return QParts{q, 1, 0, (size_t)n}; }
+
 // ---- skinny GEMM q[m][n] = x[m][k] . w[n][k]^T, for up to two weight matrices sharing x ---
 // (weights in the launch_pack_w order)
 struct GemmPlan {
@@ -35,16 +45,22 @@ struct GemmPlan {
   size_t ws_bytes;   // float partials [ksplit][m][n_total] when ksplit > 1
 };
 GemmPlan gemm_plan(int m, int n_total, int k);
+// sum_slices: also launch the slice sum into q0 / q1 (when ksplit > 1).  Without it the
+// result of problem `prob` is left as gemm_result(...) describes, for a consumer to sum.
 hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void* w0,
                        float* q0, const void* w1, float* q1, float* ws, const GemmPlan& plan,
-                       hipStream_t stream);
+                       hipStream_t stream, bool sum_slices = true);
+QParts gemm_result(const GemmPlan& plan, int m, int n, int nprob, int prob, const float* q,
+                   const float* ws);
 
 // ---- selection: scores, top-k and the resident split, one workgroup per pair ----------------
-hipError_t launch_select(const Shape& s, bool minmax, const float* q, const void* digests,
+// gpu_pages (optional, [pairs][top_k]): the page of each resident list entry, -1 past n_gpu.
+hipError_t launch_select(const Shape& s, bool minmax, const QParts& q, const void* digests,
                          const int32_t* seq_lens, int top_k, const int32_t* block_table,
                          int32_t* gpu_blocks, int32_t* n_gpu, int32_t* cpu_blocks,
                          int32_t* n_cpu, float* scores_or_null,
-                         int32_t* cpu_blocks_host, int32_t* n_cpu_host, hipStream_t stream);
+                         int32_t* cpu_blocks_host, int32_t* n_cpu_host,
+                         int32_t* gpu_pages_or_null, hipStream_t stream);
 
 // ---- attention: balanced waves write partials, then the reduction / merge per row -------
 struct AttnPlan {
@@ -52,11 +68,12 @@ struct AttnPlan {
   size_t ws_bytes;   // pair prefix + one partial slot per (wave + pair) and head
 };
 AttnPlan attn_plan(const Shape& s, int list_stride);
-hipError_t launch_attention(const Shape& s, const AttnPlan& plan, const float* q,
+hipError_t launch_attention(const Shape& s, const AttnPlan& plan, const QParts& q,
                             const void* k_pool, const void* v_pool,
                             const int32_t* block_table, const int32_t* seq_lens,
-                            const int32_t* gpu_blocks, const int32_t* n_gpu, int list_stride,
-                            float scale, float* partials, hipStream_t stream,
+                            const int32_t* gpu_blocks, const int32_t* gpu_pages_or_null,
+                            const int32_t* n_gpu, int list_stride, float scale,
+                            float* partials, hipStream_t stream,
                             hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 // Combine the chunk partials of every (sequence, query head) row, optionally merged with a
 // host partial (gated by n_cpu when given); writes normalised o and natural-unit m, l.

@@ -16,7 +16,8 @@
 //      back to an exact MSB-first radix select on order-preserving 32-bit keys.
 //   3. split: the selected blocks are compacted in ascending order and split by the block
 //      table (read during step 1) into the resident and offloaded lists; the offloaded list
-//      can also be written straight into a host mirror (the hand-off of Algorithm 1).
+//      can also be written straight into a host mirror (the hand-off of Algorithm 1), and
+//      the pages of the resident list next to it (so attention skips the table lookup).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -87,12 +88,12 @@ __device__ __forceinline__ float wave_max(float v) {
 
 template <typename T, int D, bool MINMAX>
 __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
-    const float* __restrict__ q, const T* __restrict__ dig, const int32_t* __restrict__ seq_lens,
+    const QParts q, const T* __restrict__ dig, const int32_t* __restrict__ seq_lens,
     int Hkv, int G, int bs, int max_blocks, int top_k, const int32_t* __restrict__ table,
     int32_t* __restrict__ gpu_blocks, int32_t* __restrict__ n_gpu,
     int32_t* __restrict__ cpu_blocks, int32_t* __restrict__ n_cpu,
     float* __restrict__ scores_out, int32_t* __restrict__ cpu_blocks_host,
-    int32_t* __restrict__ n_cpu_host) {
+    int32_t* __restrict__ n_cpu_host, int32_t* __restrict__ gpu_pages) {
   constexpr int VEC = Digest<T>::N;
   constexpr int LPR = D / VEC;             // lanes per digest row
   constexpr int BPI = kWave / LPR;         // blocks per load instruction
@@ -102,6 +103,8 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
 
   extern __shared__ float sc[];                                 // [max_blocks] scores
   uint8_t* flag = reinterpret_cast<uint8_t*>(sc + max_blocks);  // [max_blocks]
+  // [max_blocks] block-table entries, kept only when the pages are written out
+  int32_t* pg = reinterpret_cast<int32_t*>(sc + max_blocks + (max_blocks + 3) / 4);
   __shared__ uint32_t hist[256];
   __shared__ uint32_t tmp[kSelWaves];
   __shared__ float red_lo[kSelWaves], red_hi[kSelWaves];
@@ -137,21 +140,37 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
 
   // residency of every block (block table read while the digests stream)
   const int32_t* trow = table + (size_t)pair * max_blocks;
-  for (int i = tid; i < nb; i += kSelThreads) flag[i] = trow[i] >= 0 ? kResident : 0;
+  for (int i = tid; i < nb; i += kSelThreads) {
+    const int32_t e = trow[i];
+    flag[i] = e >= 0 ? kResident : 0;
+    if (gpu_pages) pg[i] = e;
+  }
   if (tid < 256) hist[tid] = 0;
   if (tid == 0) ncand = 0;
 
-  // per-channel coefficients of this lane's VEC channels
+  // per-channel coefficients of this lane's VEC channels (each query element is the sum of
+  // its parts, taken in part order)
   float ca[VEC], cb[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) { ca[i] = 0.f; cb[i] = 0.f; }
-  const float* qg = q + ((size_t)s * Hkv * G + (size_t)h * G) * D + cg * VEC;
+  const float* qg = q.base + (size_t)s * q.row_stride + (size_t)h * G * D + cg * VEC;
   for (int g = 0; g < G; ++g) {
+    float v[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; i += 4)
+      *reinterpret_cast<float4*>(v + i) = *reinterpret_cast<const float4*>(qg + (size_t)g * D + i);
+    for (int part = 1; part < q.parts; ++part) {
+      const float* qp = qg + (size_t)part * q.part_stride + (size_t)g * D;
+#pragma unroll
+      for (int i = 0; i < VEC; i += 4) {
+        const float4 w = *reinterpret_cast<const float4*>(qp + i);
+        v[i] += w.x; v[i + 1] += w.y; v[i + 2] += w.z; v[i + 3] += w.w;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
-      const float v = qg[(size_t)g * D + i];
-      if (MINMAX) { ca[i] += fmaxf(v, 0.f); cb[i] += fminf(v, 0.f); }
-      else ca[i] += v;
+      if (MINMAX) { ca[i] += fmaxf(v[i], 0.f); cb[i] += fminf(v[i], 0.f); }
+      else ca[i] += v[i];
     }
   }
 
@@ -307,15 +326,24 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
   uint32_t pos_res = (incl - packed) & 0xffffu, pos_off = (incl - packed) >> 16;
   if (tid == kSelThreads - 1) { tot_res = incl & 0xffffu; tot_off = incl >> 16; }
   int32_t* grow = gpu_blocks + (size_t)pair * top_k;
+  int32_t* prow = gpu_pages ? gpu_pages + (size_t)pair * top_k : nullptr;
   int32_t* off_lds = reinterpret_cast<int32_t*>(sc);  // [top_k] <= [max_blocks]
   for (int i = i0; i < i1; ++i) {
     const uint8_t f = flag[i];
-    if (f == (kSelected | kResident)) grow[pos_res++] = i;
-    else if (f == kSelected) off_lds[pos_off++] = i;
+    if (f == (kSelected | kResident)) {
+      grow[pos_res] = i;
+      if (prow) prow[pos_res] = pg[i];
+      ++pos_res;
+    } else if (f == kSelected) {
+      off_lds[pos_off++] = i;
+    }
   }
   __syncthreads();
   const int nr = (int)tot_res, no = (int)tot_off;
-  for (int j = nr + tid; j < top_k; j += kSelThreads) grow[j] = -1;
+  for (int j = nr + tid; j < top_k; j += kSelThreads) {
+    grow[j] = -1;
+    if (prow) prow[j] = -1;
+  }
   int32_t* crow = cpu_blocks + (size_t)pair * top_k;
   int32_t* hrow = cpu_blocks_host ? cpu_blocks_host + (size_t)pair * top_k : nullptr;
   for (int j = tid; j < top_k; j += kSelThreads) {
@@ -331,32 +359,35 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
 }
 
 template <typename T, int D>
-hipError_t select_typed(const Shape& s, bool minmax, const float* q, const void* dig,
+hipError_t select_typed(const Shape& s, bool minmax, const QParts& q, const void* dig,
                         const int32_t* lens, int top_k, const int32_t* table, int32_t* gb,
                         int32_t* ng, int32_t* cb, int32_t* nc, float* scores, int32_t* cbh,
-                        int32_t* nch, hipStream_t st) {
-  const size_t lds = (size_t)s.max_blocks * (sizeof(float) + 1);
+                        int32_t* nch, int32_t* gp, hipStream_t st) {
+  // scores, flags (padded to a float boundary) and, when pages are written, table entries
+  const size_t lds = (size_t)(s.max_blocks + (s.max_blocks + 3) / 4) * sizeof(float) +
+                     (gp ? (size_t)s.max_blocks * sizeof(int32_t) : 0);
   const dim3 grid(s.B * s.Hkv), block(kSelThreads);
   if (minmax)
     hipLaunchKernelGGL((select_kernel<T, D, true>), grid, block, lds, st, q, (const T*)dig,
                        lens, s.Hkv, s.G, s.bs, s.max_blocks, top_k, table, gb, ng, cb, nc,
-                       scores, cbh, nch);
+                       scores, cbh, nch, gp);
   else
     hipLaunchKernelGGL((select_kernel<T, D, false>), grid, block, lds, st, q, (const T*)dig,
                        lens, s.Hkv, s.G, s.bs, s.max_blocks, top_k, table, gb, ng, cb, nc,
-                       scores, cbh, nch);
+                       scores, cbh, nch, gp);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_select(const Shape& s, bool minmax, const float* q, const void* digests,
+hipError_t launch_select(const Shape& s, bool minmax, const QParts& q, const void* digests,
                          const int32_t* seq_lens, int top_k, const int32_t* block_table,
                          int32_t* gpu_blocks, int32_t* n_gpu, int32_t* cpu_blocks,
                          int32_t* n_cpu, float* scores_or_null, int32_t* cpu_blocks_host,
-                         int32_t* n_cpu_host, hipStream_t stream) {
+                         int32_t* n_cpu_host, int32_t* gpu_pages, hipStream_t stream) {
 #define SA_SEL_ARGS s, minmax, q, digests, seq_lens, top_k, block_table, gpu_blocks, n_gpu, \
-                    cpu_blocks, n_cpu, scores_or_null, cpu_blocks_host, n_cpu_host, stream
+                    cpu_blocks, n_cpu, scores_or_null, cpu_blocks_host, n_cpu_host, gpu_pages, \
+                    stream
   if (s.bf16)
     return s.d == 128 ? select_typed<uint16_t, 128>(SA_SEL_ARGS)
                       : select_typed<uint16_t, 64>(SA_SEL_ARGS);
