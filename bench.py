@@ -97,13 +97,14 @@ def setup(wl, torch, B, wk):
             sets[p // Hkv][p % Hkv] = cbh[p]
         pool = wk.draw_layer_pool(wl, i, off, sets)
         k_pool = B.pack_k_pages(dims, pool["K"])  # K pages in the chunk-major layout
-        del pool["K"]
+        v_pool = B.pack_v_pages(dims, pool["V"])  # V pages as [P][bs/16][d][16]
+        del pool["K"], pool["V"]
         B.sa_build_digests(dims, "mean", k_pool, pool["block_table"], lens, dig)
         hp = wk.draw_host_partials(wl, i, dev)
         del off
         layers.append(dict(
             x=ins[i]["X"], w_q=w_packed, digests=dig, block_table=pool["block_table"],
-            k_pool=k_pool, v_pool=pool["V"], host_o=hp["o"], host_m=hp["m"],
+            k_pool=k_pool, v_pool=v_pool, host_o=hp["o"], host_m=hp["m"],
             host_l=hp["l"],
             gpu_blocks=torch.empty((pairs, k), dtype=torch.int32, device=dev),
             n_gpu=torch.empty(pairs, dtype=torch.int32, device=dev),

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libscoutattn.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = 0, -1, -2, -3, -4
 SA_F32, SA_BF16 = 0, 1
 SA_DIGEST_MEAN, SA_DIGEST_MINMAX = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 KIND = {"mean": SA_DIGEST_MEAN, "minmax": SA_DIGEST_MINMAX}
 
@@ -57,6 +57,7 @@ SIGNATURES = {
     "sa_last_error": (ctypes.c_char_p, []),
     "sa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "sa_pack_k_pages": (ctypes.c_int, [_D, _P, _P, _P]),
+    "sa_pack_v_pages": (ctypes.c_int, [_D, _P, _P, _P]),
     "sa_pack_weight": (ctypes.c_int, [_I, _I, _P, _P, _P]),
     "sa_build_digests": (ctypes.c_int, [_D, ctypes.c_int, _P, _P, _P, _P, _P]),
     "sa_predict_query_workspace_bytes": (_Z, [_I, _I, _I]),
@@ -207,6 +208,21 @@ def pack_k_pages(dims: Dims, k_rows, stream=None):
     """Allocate a chunk-major K pool of k_rows' size and fill it with sa_pack_k_pages."""
     out = torch.empty_like(k_rows)
     sa_pack_k_pages(dims, k_rows, out, stream)
+    return out
+
+
+def sa_pack_v_pages(dims: Dims, v_rows, v_pool, stream=None):
+    """v_rows [P][bs][d] token-row pages -> v_pool [P][bs/16][d][16]."""
+    n = dims.num_pages * dims.block_size * dims.head_dim
+    _check(lib().sa_pack_v_pages(
+        ctypes.byref(dims.c()), _ptr(v_rows, dims.kv_torch, n, "v_rows"),
+        _ptr(v_pool, dims.kv_torch, n, "v_pool"), _stream(stream)))
+
+
+def pack_v_pages(dims: Dims, v_rows, stream=None):
+    """Allocate a V pool of v_rows' size and fill it with sa_pack_v_pages."""
+    out = torch.empty_like(v_rows)
+    sa_pack_v_pages(dims, v_rows, out, stream)
     return out
 
 

@@ -210,6 +210,20 @@ sa_status sa_pack_k_pages(const sa_dims* dims, const void* k_rows, void* k_pool,
   return ok();
 }
 
+sa_status sa_pack_v_pages(const sa_dims* dims, const void* v_rows, void* v_pool,
+                          hipStream_t stream) {
+  sa::Shape s;
+  SA_CHECK(check_dims(dims, &s));
+  SA_NOT_NULL(v_rows);
+  SA_NOT_NULL(v_pool);
+  const size_t bytes = (size_t)s.P * s.bs * s.d * (s.bf16 ? 2 : 4);
+  const char* a = (const char*)v_rows;
+  const char* b = (const char*)v_pool;
+  if (a < b + bytes && b < a + bytes) return fail(SA_ERR_INVALID_ARG, "v_rows and v_pool overlap");
+  SA_HIP(sa::launch_pack_v(s, v_rows, v_pool, stream), "V pack kernel");
+  return ok();
+}
+
 sa_status sa_pack_weight(int32_t n, int32_t k, const void* w, void* w_packed,
                          hipStream_t stream) {
   if (n < 32 || k < 32) return fail(SA_ERR_INVALID_ARG, "weight sizes n %d, k %d must be >= 32", n, k);

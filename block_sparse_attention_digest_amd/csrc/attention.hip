@@ -174,16 +174,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ gpu_blocks,
     const int32_t* __restrict__ gpu_pages, const int32_t* __restrict__ n_gpu, int list_stride,
     int Hkv, int max_blocks, int npairs, int W, float scale_log2, float* __restrict__ ws) {
-  constexpr int KS = D / 32;          // MFMA k-steps over the head dimension
+  constexpr int KS = D / 32;          // MFMA k-steps over the head dimension (S = K Q^T)
+  constexpr int CG = D / 16;          // 16-channel groups of the output (O^T += V^T P)
   constexpr int HPB = BS / kStep;     // 16-token steps per block (1 or 2)
-  constexpr int VLPR = D / 8;         // lanes per V row
-  constexpr int VTPI = kWave / VLPR;  // V rows per load instruction
-  constexpr int VJ = kStep / VTPI;    // V loads per lane per step
 
   extern __shared__ int pfx[];        // [npairs + 1]
   __shared__ float q_lds[kQStage * G * D];
-  __shared__ float p_lds[kAttnWaves][kStep][8];
-  __shared__ float a_lds[kAttnWaves][8];
   __shared__ int wave_tot[kAttnWaves];
 
   const int lane = threadIdx.x % kWave;
@@ -235,17 +231,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   const int c16 = lane % 16;   // MFMA column (head / hi-lo) and token row in the tile
   const int kq = lane / 16;    // MFMA k-group
   const int hcol = c16 & 7;    // head of this MFMA column
-  const int vcg = lane % VLPR, vts = lane / VLPR;
 
-  // Q^T as the MFMA B operand (hi columns 0..7, lo 8..15): the float rows of a pair are
-  // fetched ahead (fetch_q, into qr) and converted when the pair's blocks begin.  Staged
-  // pairs come from LDS; any other pair (a workgroup range crossing more than kQStage
-  // pairs) is summed from its parts in global memory.
+  // Q^T as the MFMA B operand (hi columns 0..7, lo 8..15), set when a pair's blocks begin
+  // from its float rows: staged pairs from LDS; any other pair (a workgroup range crossing
+  // more than kQStage pairs) summed from its parts in global memory.
   bf16x8 qb[KS];
-  float4 qr[KS][2];
-  auto fetch_q = [&](int pair) {
-    pair = min(pair, npairs - 1);
+  auto set_q = [&](int pair) {
     const int row = hcol < G ? hcol : 0;
+    float4 qr[KS][2];
     if (pair - q_lo < q_n && pair >= q_lo) {
       const float* qrow = q_lds + ((pair - q_lo) * G + row) * D;
 #pragma unroll
@@ -272,8 +265,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
           }
       }
     }
-  };
-  auto convert_q = [&]() {
     const bool live = hcol < G;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -296,34 +287,30 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     }
   };
 
-  float m_run = -INFINITY;   // per head hcol (log2 units), uniform over the head's lanes
-  float l_lane = 0.f;        // this lane's share of l for head hcol
-  float o_acc[G][8];
+  // Online softmax state of MFMA column c16 (head hcol): m and this lane's share of l
+  // (its four tokens of every step), and O^T as CG MFMA accumulator tiles, o[cg][r] =
+  // O^T[channel 16 cg + 4 kq + r][column c16].  Columns 0..7 accumulate V^T P_hi and
+  // columns 8..15 V^T P_lo for the same heads; o = their sum.
+  float m_run = -INFINITY;   // log2 units, uniform over the column's lanes
+  float l_lane = 0.f;
+  floatx4 o[CG];
   auto reset = [&]() {
     m_run = -INFINITY;
     l_lane = 0.f;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o_acc[g][i] = 0.f;
+    for (int cg = 0; cg < CG; ++cg) o[cg] = floatx4{0.f, 0.f, 0.f, 0.f};
   };
   auto finalize = [&](int pair) {  // write this wave's partial for `pair` to slot gw + pair
-    const float l_w = sum_xor32(sum_xor16(l_lane));
+    const float l_w = sum_xor32(sum_xor16(l_lane));  // the column's four kq lanes
     const size_t slot = (size_t)(gw + pair) * G;
+    float* dst = part.o + (slot + (c16 < G ? c16 : 0)) * D + 4 * kq;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float red[8];
+    for (int cg = 0; cg < CG; ++cg) {
+      float v[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float v = o_acc[g][i];
-        if (VLPR <= 8) v += xor8(v);
-        red[i] = sum_xor32(sum_xor16(v));
-      }
-      if (vts == 0) {
-        float* dst = part.o + (slot + g) * D + 8 * vcg;
-        *reinterpret_cast<float4*>(dst) = make_float4(red[0], red[1], red[2], red[3]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(red[4], red[5], red[6], red[7]);
-      }
+      for (int r = 0; r < 4; ++r) v[r] = o[cg][r] + xor8(o[cg][r]);  // hi + lo columns
+      if (c16 < G)
+        *reinterpret_cast<float4*>(dst + 16 * cg) = make_float4(v[0], v[1], v[2], v[3]);
     }
     if (lane < G) {  // lane g: c16 = g, kq = 0
       part.ml[(slot + lane) * 2 + 0] = m_run;
@@ -331,10 +318,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     }
   };
 
-  // one 16-token step in registers: a K tile as MFMA A operands, V rows for the PV product
+  // One 16-token step in registers, both as MFMA A operands: the K tile (lane l: token
+  // l % 16, channels 32 ks + 8 kq .. + 7) and the V^T tiles (lane l: channel 16 cg + l % 16,
+  // tokens 4 kq .. + 3 of the step).
   struct StepRegs {
     uint4 k[KS];
-    uint4 v[VJ];
+    uint2 v[CG];
     int nval;
   };
   int w_page = 0, w_nval = 0;  // lane j: page and valid tokens of block (window start + j)
@@ -344,17 +333,17 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   auto load_step = [&](int j, int hh, StepRegs& R) {
     const int page = __builtin_amdgcn_readlane(w_page, j);
     R.nval = __builtin_amdgcn_readlane(w_nval, j) - kStep * hh;  // valid tokens of the step
-    const size_t row0 = (size_t)page * BS + kStep * hh;
     // chunk 4 ks + kq (channels 32 ks + 8 kq .. + 7) of token kStep hh + c16
     const uint16_t* src = k_pool + (size_t)page * BS * D + ((size_t)kq * BS + kStep * hh + c16) * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       R.k[ks] = *reinterpret_cast<const uint4*>(src + (size_t)ks * 4 * BS * 8);
+    // V half-page hh is [D][16]: channel 16 cg + c16, tokens 4 kq .. + 3 (8 bytes); the 64
+    // lanes of one tile read 512 contiguous bytes
+    const uint16_t* vsrc = v_pool + ((size_t)page * HPB + hh) * D * kStep + c16 * kStep + 4 * kq;
 #pragma unroll
-    for (int jj = 0; jj < VJ; ++jj) {  // step token t = jj * VTPI + vts; masked rows get p = 0
-      const int t = max(0, min(jj * VTPI + vts, R.nval - 1));
-      R.v[jj] = *reinterpret_cast<const uint4*>(v_pool + (row0 + t) * D + 8 * vcg);
-    }
+    for (int cg = 0; cg < CG; ++cg)
+      R.v[cg] = *reinterpret_cast<const uint2*>(vsrc + (size_t)cg * 16 * kStep);
   };
 
   auto compute_step = [&](const StepRegs& R) {
@@ -370,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
       const float tot = acc[r] + xor8(acc[r]);  // hi + lo columns
       sc[r] = 4 * kq + r < R.nval ? tot * scale_log2 : -INFINITY;
     }
-    // online softmax for head hcol
+    // online softmax for head hcol (the column's 16 tokens are on its four kq lanes)
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = max_xor32(max_xor16(mx));
     const float m_new = fmaxf(m_run, mx);
@@ -385,88 +374,105 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     }
     l_lane = l_lane * alpha + psum;
     m_run = m_new;
-    if (c16 < 8) {
+    // P as the B operand of O^T += V^T P, straight from this layout (lane l: column c16,
+    // tokens 4 kq .. + 3): bf16(p) in columns 0..7, the rounding remainder p - bf16(p) in
+    // columns 8..15, so the two column halves together carry p to about 2^-17
+    uint32_t pw[2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p_lds[wave][4 * kq + r][c16] = sc[r];
-      if (kq == 0) a_lds[wave][c16] = alpha;
+    for (int i = 0; i < 2; ++i) {
+      uint32_t half[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float x = sc[2 * i + j];
+        const uint32_t hi = f32_to_bf16_rne(x);
+        half[j] = c16 < 8 ? hi : f32_to_bf16_rne(x - __uint_as_float(hi << 16));
+      }
+      pw[i] = half[0] | (half[1] << 16);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // O = alpha O + P V
-    float al[8];
-    *reinterpret_cast<float4*>(al) = *reinterpret_cast<const float4*>(&a_lds[wave][0]);
-    *reinterpret_cast<float4*>(al + 4) = *reinterpret_cast<const float4*>(&a_lds[wave][4]);
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o_acc[g][i] *= al[g];
-#pragma unroll
-    for (int jj = 0; jj < VJ; ++jj) {
-      const int t = jj * VTPI + vts;
-      float pv[8];
-      *reinterpret_cast<float4*>(pv) = *reinterpret_cast<const float4*>(&p_lds[wave][t][0]);
-      *reinterpret_cast<float4*>(pv + 4) = *reinterpret_cast<const float4*>(&p_lds[wave][t][4]);
-      float v[8];
-      bf16x8_to_f32(R.v[jj], v);
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o_acc[g][i] = fmaf(pv[g], v[i], o_acc[g][i]);
+    const shortx4 pb = __builtin_bit_cast(shortx4, make_uint2(pw[0], pw[1]));
+    // tokens past the valid ones may hold anything (a partly filled page): their V is zeroed
+    // (their p is already 0), so no stale NaN reaches the sum
+    uint2 keep = make_uint2(~0u, ~0u);
+    if (R.nval < kStep) {
+      const int n = R.nval - 4 * kq;  // valid tokens among this lane's four
+      keep.x = n >= 2 ? ~0u : (n == 1 ? 0xffffu : 0u);
+      keep.y = n >= 4 ? ~0u : (n == 3 ? 0xffffu : 0u);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int cg = 0; cg < CG; ++cg) {
+      o[cg] *= alpha;
+      const uint2 v = make_uint2(R.v[cg].x & keep.x, R.v[cg].y & keep.y);
+      o[cg] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, v), pb,
+                                                        o[cg], 0, 0, 0);
+    }
   };
 
-  // A segment is the part of a window in one pair; the next pair's query rows are fetched
-  // when a pair's blocks begin, so they have arrived by the time its successor starts.
+  // The steps of a window run as one software pipeline across pair boundaries: before the
+  // first step of a pair's block is computed, the previous pair's partial is written and
+  // the new pair's query set, while that step's loads and the next ones are in flight.
   // (The pair after p that holds blocks: the one holding block pfx[p + 1].)
   auto next_pair = [&](int pp) {
     const int end = __builtin_amdgcn_readfirstlane(pfx[pp + 1]);
     while (pp < npairs - 1 && __builtin_amdgcn_readfirstlane(pfx[pp + 1]) <= end) ++pp;
     return pp;
   };
-  fetch_q(p);
   bool open = false;  // a partial of pair p is being accumulated
   for (int wb = b0; wb < b1; wb += kWave) {
     const int nw = min(kWave, b1 - wb);
     if (wb != b0) lookup(wb, nw, p);
     w_page = l_page;
     w_nval = min(BS, l_len - l_blk * BS);
-    for (int j = 0; j < nw;) {
-      if (!open) {
-        convert_q();
-        fetch_q(next_pair(p));
-        reset();
-        open = true;
-      }
-      const int pend = __builtin_amdgcn_readfirstlane(pfx[p + 1]);
-      const int jend = min(nw, pend - wb);
-      // HPB steps per block; a second half holding no valid token is fully masked.  Two
-      // steps per iteration, the next one's loads in flight while one is computed.  The
-      // loads are unconditional (steps past the end re-read the last step, lines that are
-      // still cached) so every path has the same loads in flight, and the scheduling
-      // barriers keep the compiler from sinking them to their use.
-      const int nst = (jend - j) * HPB;
-      StepRegs ra, rb;
-      load_step(j, 0, ra);
-      for (int st = 0; st < nst; st += 2) {
-        const int s1 = min(st + 1, nst - 1), s2 = min(st + 2, nst - 1);
-        load_step(j + s1 / HPB, s1 % HPB, rb);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_step(ra);
-        load_step(j + s2 / HPB, s2 % HPB, ra);
-        __builtin_amdgcn_sched_barrier(0);
-        if (st + 1 < nst) compute_step(rb);
-      }
-      j = jend;
-      if (wb + jend == pend) {  // pair p ends here
+    int bnd = __builtin_amdgcn_readfirstlane(pfx[p + 1]) - wb;  // first block of the next pair
+    // before step s (block s / HPB): switch pairs at a pair's first block
+    auto enter = [&](int s) {
+      if (s % HPB == 0 && s / HPB == bnd) {
         finalize(p);
         open = false;
         p = next_pair(p);
+        bnd = __builtin_amdgcn_readfirstlane(pfx[p + 1]) - wb;
       }
+      if (!open) {
+        set_q(p);
+        reset();
+        open = true;
+      }
+    };
+    // HPB steps per block; a second half holding no valid token is fully masked.  Three
+    // steps per iteration, the two after the one being computed in flight (so a wave keeps
+    // the memory busy on its own once its SIMD neighbour has finished).  The loads are
+    // unconditional (steps past the end re-read the last step, lines that are still
+    // cached) so every path has the same loads in flight, and the scheduling barriers keep
+    // the compiler from sinking them to their use.
+    const int nst = nw * HPB;
+    auto ld = [&](int st, StepRegs& R) {
+      const int sc = min(st, nst - 1);
+      load_step(sc / HPB, sc % HPB, R);
+    };
+    StepRegs ra, rb, rc;
+    ld(0, ra);
+    ld(1, rb);
+    for (int st = 0; st < nst; st += 3) {
+      ld(st + 2, rc);
+      __builtin_amdgcn_sched_barrier(0);
+      enter(st);
+      compute_step(ra);
+      ld(st + 3, ra);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + 1 < nst) {
+        enter(st + 1);
+        compute_step(rb);
+      }
+      ld(st + 4, rb);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + 2 < nst) {
+        enter(st + 2);
+        compute_step(rc);
+      }
+    }
+    if (nw == bnd) {  // pair p ends with the window
+      finalize(p);
+      open = false;
+      p = next_pair(p);
     }
   }
   if (open) finalize(p);  // the range ended inside pair p
@@ -537,9 +543,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
     const int nval = min(BS, seq_lens[p / Hkv] - blk * BS);
     __syncthreads();
     for (int i = lane; i < BS * D; i += kWave) {
-      // K is chunk-major: element i is channel 4 (i / 4BS) + i % 4 of token (i / 4) % BS
+      // K is chunk-major: element i is channel 4 (i / 4BS) + i % 4 of token (i / 4) % BS;
+      // V is [BS/16][D][16]: element i is channel (i / 16) % D of token 16 (i / 16D) + i % 16
       ks[(i / 4) % BS][4 * (i / (4 * BS)) + i % 4] = k_pool[(size_t)page * BS * D + i];
-      vs[i / D][i % D] = v_pool[(size_t)page * BS * D + i];
+      vs[16 * (i / (16 * D)) + i % 16][(i / 16) % D] = v_pool[(size_t)page * BS * D + i];
     }
     __syncthreads();
     for (int i = lane; i < G * BS; i += kWave) {

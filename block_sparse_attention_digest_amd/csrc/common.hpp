@@ -10,6 +10,7 @@ constexpr int kWave = 64;  // CDNA wavefront width
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));  // four bf16 MFMA operand
 
 // ---- bfloat16 <-> float ------------------------------------------------------------------
 // A 32-bit word holds two bf16 values: element 0 in the low half, element 1 in the high half.

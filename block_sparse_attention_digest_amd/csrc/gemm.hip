@@ -5,12 +5,13 @@
 // m is the batch (8..40 rows), so the product is bound by streaming W from HBM, not by the
 // matrix cores.  The work is cut into units of one 16-column tile x one k-slice; each unit
 // belongs to one workgroup, where kpw waves split its k-slice (their sums are combined in
-// LDS at the end, in a fixed order).  A wave streams its W (packed by launch_pack_w: the v_mfma_f32_16x16x32_bf16 B
-// operand of one tile and one 32-wide k-step is a contiguous kilobyte) with 16-byte loads
-// that cover whole cache lines, straight into B operands, keeping the next 8 k-steps in
-// flight (double-buffered registers) while the current 8 are multiplied.  A workgroup's
-// waves own consecutive tiles of the same k-slice, so the slice of x they share (at most 64
-// rows) is staged once in LDS -- up to 160 KiB, so one k-slice can be long and the float32
+// LDS at the end, in a fixed order).  A wave streams its W (packed by launch_pack_w: the
+// v_mfma_f32_16x16x32_bf16 B operand of one tile and one 32-wide k-step is a contiguous
+// kilobyte) with 16-byte loads that cover whole cache lines, straight into B operands,
+// with up to 24 k-steps in flight.  A workgroup's waves own consecutive tiles of the same
+// k-slice, so the slice of x they share (at most 64 rows) is staged once in LDS, by
+// global-to-LDS loads issued just ahead of the W stream (so the staging overlaps it) --
+// up to 160 KiB, so one k-slice can be long and the float32
 // partials of the slices (summed in slice order by a second kernel, so results are
 // deterministic) stay a small fraction of the W bytes.  The plan sizes the grid to about
 // one workgroup per CU, so the whole product is one round of long-lived waves.  Two weight
@@ -24,7 +25,6 @@ namespace sa {
 namespace {
 
 constexpr int kGroup = 8;            // k-steps (of 32) per register buffer
-constexpr int kPad = 8;              // bf16 elements of padding per LDS row
 constexpr int kMaxWpg = 10;          // waves per workgroup (640 threads: up to 168 VGPRs)
 constexpr int kTargetUnits = 1024;   // >= 4 long-lived waves per CU
 constexpr int kCUs = 256;
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(640) void gemm_kernel(const uint16_t* __restrict__ 
                                                     int tiles, int tpw, float* __restrict__ out0,
                                                     float* __restrict__ out1, int ksplit,
                                                     float* __restrict__ partials) {
-  extern __shared__ uint16_t xs[];  // [16*MT][kslice + kPad]; later the kpw combine
+  extern __shared__ uint16_t xs[];  // [kslice/32][MT][64 lanes][8]; later the kpw combine
   const int lane = threadIdx.x % kWave;
   const int kpw = blockDim.x / kWave / tpw;  // waves per tile
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // scalar branches
@@ -51,9 +51,7 @@ __global__ __launch_bounds__(640) void gemm_kernel(const uint16_t* __restrict__ 
   const uint16_t* w = prob ? w1 : w0;
   const int k0 = ks * kslice;                 // slices are full: k0 + kslice <= k
   const int row0 = blockIdx.y * 16 * MT;
-  const int ldx = kslice + kPad;
 
-  const int kq = 8 * (lane / 16);  // this lane's 8 k-values within a 32-wide step
   const int nsteps = kslice / 32 / kpw;  // this wave's k-steps: part kpart of the slice
   const int step0 = kpart * nsteps;      // first k-step of the part within the slice
   // packed tile (col / 16, k-step): 512 elements, this lane's 8 at lane * 8
@@ -64,9 +62,33 @@ __global__ __launch_bounds__(640) void gemm_kernel(const uint16_t* __restrict__ 
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // Loads are issued unconditionally (k-steps past the part are clamped to its last step
-  // and their B operand zeroed), so every path has the same loads in flight and the
-  // compiler waits only for the group being multiplied.
+  // 1. The x slice goes straight from global memory into LDS, in matrix-core operand order:
+  //    the A operand of row tile t and k-step s (rows 16t + l % 16, k-values 32s + 8(l / 16)
+  //    .. + 7 for lane l) is the kilobyte at xs + (s MT + t) 512, lane l's 16 bytes at
+  //    l * 8, so each load instruction fills one kilobyte and every later operand read is
+  //    lane-contiguous.  Rows past m read row m - 1: a row of A feeds only its own output
+  //    row, and those rows are not stored.  The waves of the workgroup share the chunks.
+  {
+    const int nst = kslice / 32;
+    const int waves = blockDim.x / kWave;
+    const int row = min(row0 + (lane % 16), m - 1) - row0;  // row within tile 0
+    const uint16_t* xl = x + (size_t)k0 + 8 * (lane / 16);
+    for (int j = wave; j < MT * nst; j += waves) {
+      const int st = j / MT, t = j % MT;
+      const int r = min(row0 + 16 * t + row, m - 1);
+      __builtin_amdgcn_global_load_lds(xl + (size_t)r * k + 32 * st, xs + (size_t)j * 512, 16,
+                                       0, 0);
+    }
+  }
+  // 2. W streams through three register groups (24 k-steps in flight: the whole part, for
+  //    parts of up to 24 k-steps), issued right behind the x slice so the slice's staging
+  //    overlaps the stream; each group is refilled right after it is multiplied.  All three
+  //    thirds always run (a group past the part multiplies zeros and its refill re-reads the
+  //    last step, a cached line): with no early exit the compiler cannot sink a group's loads
+  //    down to the block that uses them, and the scheduling barriers keep it from moving
+  //    them within the iteration.  Loads are unconditional (k-steps past the part clamp to
+  //    its last step and their B operand is zeroed), so every path has the same loads in
+  //    flight and the compiler waits only for the group being multiplied.
   uint4 wa[kGroup], wb[kGroup], wc[kGroup];
   auto load_group = [&](uint4* dst, int s0) {
 #pragma unroll
@@ -82,85 +104,22 @@ __global__ __launch_bounds__(640) void gemm_kernel(const uint16_t* __restrict__ 
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         const uint4 a = *reinterpret_cast<const uint4*>(
-            xs + (16 * t + (lane % 16)) * ldx + 32 * (step0 + st) + kq);
+            xs + ((size_t)(step0 + st) * MT + t) * 512 + lane * 8);
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b,
                                                          acc[t], 0, 0, 0);
       }
     }
   };
-
-  // Staging of the x slice (up to 2 x kStage loads per thread in flight; rows past m are
-  // not read) comes before any W load: the barrier that ends it waits for every load the
-  // wave has in flight, and the slice's first touch on each XCD misses L2 and must not
-  // queue in HBM behind the W stream of the whole chip.
-  {
-    constexpr int kStage = 8;
-    const int nthr = blockDim.x;
-    const int chunks_per_row = kslice / 8;
-    const int mrows = min(16 * MT, m - row0);
-    const int total = mrows * chunks_per_row;
-    // A thread's slots are c, c + nthr, c + 2 nthr, ...; their (row, chunk) positions are
-    // stepped incrementally (one division per thread: a division by a run-time value is a
-    // long instruction sequence).  Slots past the end clamp to the last chunk: those lanes
-    // load and store that chunk's own value again, so there is no branch and the arrays
-    // stay in registers.
-    const int dr = nthr / chunks_per_row, dq = nthr % chunks_per_row;
-    const int last_r = (total - 1) / chunks_per_row, last_q = (total - 1) % chunks_per_row;
-    int r = threadIdx.x / chunks_per_row, q = threadIdx.x % chunks_per_row;
-    // clamped (row, chunk) of each slot, chosen with integer selects: the staging is one
-    // basic block, so the compiler keeps every load ahead of the first store
-    int rs[2 * kStage], qs[2 * kStage];
-#pragma unroll
-    for (int j = 0; j < 2 * kStage; ++j) {
-      const bool past = (int)threadIdx.x + j * nthr >= total;
-      rs[j] = past ? last_r : r;
-      qs[j] = past ? last_q : q;
-      r += dr;
-      q += dq;
-      const bool wrap = q >= chunks_per_row;
-      q -= wrap ? chunks_per_row : 0;
-      r += wrap ? 1 : 0;
-    }
-    const uint16_t* xslice = x + (size_t)row0 * k + k0;
-    uint4 va[kStage], vb[kStage];
-#pragma unroll
-    for (int j = 0; j < kStage; ++j)
-      va[j] = *reinterpret_cast<const uint4*>(xslice + rs[j] * k + 8 * qs[j]);
-#pragma unroll
-    for (int j = 0; j < kStage; ++j)
-      vb[j] = *reinterpret_cast<const uint4*>(xslice + rs[kStage + j] * k + 8 * qs[kStage + j]);
-    __builtin_amdgcn_sched_barrier(0);  // all of the slice's loads before the first store
-#pragma unroll
-    for (int j = 0; j < kStage; ++j)
-      *reinterpret_cast<uint4*>(xs + rs[j] * ldx + 8 * qs[j]) = va[j];
-#pragma unroll
-    for (int j = 0; j < kStage; ++j)
-      *reinterpret_cast<uint4*>(xs + rs[kStage + j] * ldx + 8 * qs[kStage + j]) = vb[j];
-    // larger slices than one round of 2 x kStage per thread (not the usual shapes)
-    for (int c1 = threadIdx.x + 2 * kStage * nthr; c1 < total; c1 += nthr) {
-      const int rr = c1 / chunks_per_row, qq = c1 % chunks_per_row;
-      *reinterpret_cast<uint4*>(xs + rr * ldx + 8 * qq) =
-          *reinterpret_cast<const uint4*>(x + (size_t)(row0 + rr) * k + k0 + 8 * qq);
-    }
-    // padding rows of the last row tile are zero
-    for (int c = threadIdx.x; c < (16 * MT - mrows) * chunks_per_row; c += nthr) {
-      const int r = mrows + c / chunks_per_row, q8 = c % chunks_per_row;
-      *reinterpret_cast<uint4*>(xs + r * ldx + 8 * q8) = make_uint4(0, 0, 0, 0);
-    }
-  }
-  __syncthreads();  // x slice staged
-
-  // W streams through three register groups (24 k-steps in flight: the whole part, for
-  // parts of up to 24 k-steps); each group is refilled right after it is multiplied.  All
-  // three thirds always run (a group past the part multiplies zeros and its refill re-reads
-  // the last step, a cached line): with no early exit the compiler cannot sink a group's
-  // loads down to the block that uses them, and the scheduling barriers keep it from
-  // moving them within the iteration.
+  __builtin_amdgcn_sched_barrier(0);  // the x slice's loads go first
   load_group(wa, 0);
   load_group(wb, kGroup);
   load_group(wc, 2 * kGroup);
+  __syncthreads();  // x slice staged (waits for the W loads in flight too)
   __builtin_amdgcn_sched_barrier(0);
-  for (int s0 = 0; s0 < nsteps; s0 += 3 * kGroup) {
+  // (a do-while: nsteps >= 1, and a loop guard would let the compiler sink the loads above
+  // past it, below the barrier)
+  int s0 = 0;
+  do {
     mma_group(wa, s0);
     load_group(wa, s0 + 3 * kGroup);
     __builtin_amdgcn_sched_barrier(0);
@@ -170,7 +129,8 @@ __global__ __launch_bounds__(640) void gemm_kernel(const uint16_t* __restrict__ 
     mma_group(wc, s0 + 2 * kGroup);
     load_group(wc, s0 + 5 * kGroup);
     __builtin_amdgcn_sched_barrier(0);
-  }
+    s0 += 3 * kGroup;
+  } while (s0 < nsteps);
 
   // combine the kpw parts of each tile in LDS (part order is fixed: deterministic)
   if (kpw > 1) {
@@ -257,7 +217,7 @@ GemmPlan gemm_plan(int m, int n_total, int k) {
   int ksplit = 0;
   for (int d = 1; d <= ksteps64; ++d) {
     if (ksteps64 % d) continue;
-    const size_t lds = (size_t)16 * mt * (k / d + kPad) * sizeof(uint16_t);
+    const size_t lds = (size_t)16 * mt * (k / d) * sizeof(uint16_t);
     if (lds > lds_max) continue;
     ksplit = d;
     if ((long)tiles * d >= kTargetUnits) break;
@@ -290,7 +250,7 @@ hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void
   const int tiles = n_total / 16;
   const dim3 grid(tiles * plan.ksplit / plan.tpw, (m + 63) / 64);
   const dim3 block(plan.tpw * plan.kpw * kWave);
-  const size_t lds = std::max((size_t)16 * mt * (plan.kslice + kPad) * sizeof(uint16_t),
+  const size_t lds = std::max((size_t)16 * mt * plan.kslice * sizeof(uint16_t),
                               (size_t)plan.tpw * (plan.kpw - 1) * mt * kWave * 16);
   const uint16_t* X = (const uint16_t*)x;
   const uint16_t* W0 = (const uint16_t*)w0;

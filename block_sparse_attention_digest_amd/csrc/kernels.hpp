@@ -17,6 +17,8 @@ struct Shape {
 // ---- layout conversions (data movement only) ------------------------------------------------
 // K pages [P][bs][d] -> chunk-major [P][d/x][bs][x], x = 16 bytes of elements.
 hipError_t launch_pack_k(const Shape& s, const void* k_rows, void* k_pool, hipStream_t stream);
+// V pages [P][bs][d] -> [P][bs/16][d][16] (each 16-token half channel-major).
+hipError_t launch_pack_v(const Shape& s, const void* v_rows, void* v_pool, hipStream_t stream);
 // W [n][k] bf16 -> [n/16][k/32][64][8] (one MFMA B operand per KiB); n % 16 == 0, k % 32 == 0.
 hipError_t launch_pack_w(int n, int k, const void* w, void* w_packed, hipStream_t stream);
 

@@ -5,6 +5,9 @@
 //   K pages: token rows [P][bs][d] -> chunk-major [P][d/x][bs][x], x = 16 bytes of elements.
 //     A 16-token slice of one chunk is 256 contiguous bytes, so the attention kernel's
 //     matrix-core operand loads (16 tokens x 16 bytes per 16 lanes) read whole cache lines.
+//   V pages: token rows [P][bs][d] -> [P][bs/16][d][16]: each 16-token half of a page is
+//     channel-major with its 16 tokens contiguous, so a 16-channel x 16-token matrix-core
+//     operand tile of V^T is 512 contiguous bytes.
 //   W_Q: [n][k] -> [n/16][k/32][64][8], one v_mfma_f32_16x16x32_bf16 B operand (16 output
 //     features x 32 inputs, lane l holding feature l % 16 and inputs 8 (l / 16) .. + 7) per
 //     contiguous kilobyte, so one GEMM load instruction reads 1 KiB of consecutive bytes.
@@ -44,7 +47,34 @@ __global__ __launch_bounds__(256) void pack_w_kernel(const uint4* __restrict__ s
   dst[i] = src[(row * k + col) / 8];
 }
 
+// One thread per destination element (the source elements of 16 consecutive destinations
+// are one token row apart).
+template <typename T>
+__global__ __launch_bounds__(256) void pack_v_kernel(const T* __restrict__ src,
+                                                     T* __restrict__ dst, long total, int bs,
+                                                     int d) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const long per_page = (long)bs * d;
+  const long page = i / per_page;
+  const int r = (int)(i % per_page);
+  const int half = r / (16 * d), c = (r / 16) % d, t = 16 * half + r % 16;
+  dst[i] = src[page * per_page + (long)t * d + c];
+}
+
 }  // namespace
+
+hipError_t launch_pack_v(const Shape& s, const void* v_rows, void* v_pool, hipStream_t stream) {
+  const long total = (long)s.P * s.bs * s.d;
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  if (s.bf16)
+    hipLaunchKernelGGL(pack_v_kernel<uint16_t>, grid, block, 0, stream,
+                       (const uint16_t*)v_rows, (uint16_t*)v_pool, total, s.bs, s.d);
+  else
+    hipLaunchKernelGGL(pack_v_kernel<float>, grid, block, 0, stream, (const float*)v_rows,
+                       (float*)v_pool, total, s.bs, s.d);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack_k(const Shape& s, const void* k_rows, void* k_pool, hipStream_t stream) {
   const int nc = s.d * (s.bf16 ? 2 : 4) / 16;

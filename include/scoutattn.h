@@ -34,12 +34,15 @@
  * page, or holds -1 when that block is not resident in GPU memory.  Block b of sequence s
  * covers tokens [b*bs, min((b+1)*bs, seq_lens[s])); nb_s = ceil(seq_lens[s] / bs).
  *
- * Page layouts.  v_pool is [P][bs][d] (token rows).  k_pool is chunk-major,
+ * Page layouts.  k_pool is chunk-major,
  * [P][d/x][bs][x] with x = 16 / (bytes per element) -- 8 for bf16, 4 for float32: the head
  * dimension is cut into 16-byte chunks and each chunk stores the page's bs tokens one after
  * another.  A 16-token slice of one chunk is then 256 contiguous bytes, which lets the
  * attention kernel load K straight into matrix-core operands with whole 128-byte cache
- * lines.  sa_pack_k_pages converts token-row pages [P][bs][d] into this layout.
+ * lines.  v_pool is [P][bs/16][d][16]: each 16-token half of a page stores its d channels
+ * one after another, each channel's 16 tokens contiguous, so a 16-channel x 16-token tile
+ * of V^T (a matrix-core operand) is 16*16 contiguous elements.  sa_pack_k_pages and
+ * sa_pack_v_pages convert token-row pages [P][bs][d] into these layouts.
  */
 #ifndef SCOUTATTN_H
 #define SCOUTATTN_H
@@ -53,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 2
+#define SA_ABI_VERSION 3
 
 typedef enum {
   SA_OK = 0,
@@ -118,6 +121,15 @@ sa_status sa_pack_k_pages(const sa_dims* dims, const void* k_rows, void* k_pool,
                           hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * sa_pack_v_pages -- layout conversion (no arithmetic): v_rows [P][bs][d] token-row pages
+ * of V in the KV dtype -> v_pool [P][bs/16][d][16], the layout every call below reads:
+ * element (page, token t, channel c) goes to v_pool[page][t / 16][c][t % 16].  Both device
+ * buffers hold P*bs*d elements and must not overlap.
+ * ------------------------------------------------------------------------------------- */
+sa_status sa_pack_v_pages(const sa_dims* dims, const void* v_rows, void* v_pool,
+                          hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * sa_pack_weight -- layout conversion (no arithmetic) of a query-projection weight, done
  * once when the weights are loaded: w [n][k] bf16 (row j = output feature j, the
  * linear-layer layout) -> w_packed [n/16][k/32][64][8] bf16, the order in which
@@ -176,7 +188,7 @@ sa_status sa_select_blocks(const sa_dims* dims, sa_digest_kind kind, const float
  * in gpu_blocks[s][g/G][0 .. n_gpu[s][g/G]) (each block read through block_table):
  *   z_t = scale * q_g . K_t,  m = max z,  l = sum exp(z - m),  o = sum exp(z - m) V_t / l.
  *   An empty list gives o = 0, m = -inf, l = 0.
- *   q [B][Hq][d] float32; k_pool (chunk-major), v_pool [P][bs][d] in the KV dtype;
+ *   q [B][Hq][d] float32; k_pool (chunk-major), v_pool ([P][bs/16][d][16]) in the KV dtype;
  *   gpu_blocks [B][Hkv][list_stride] with
  *   entries in [0, nb_s) whose table entry is a page in [0, P); 0 <= n_gpu <= list_stride.
  *   Outputs o [B][Hq][d], m [B][Hq], l [B][Hq] float32 (m in natural-log units); m and l
@@ -245,7 +257,7 @@ typedef struct {
   const void* digests;      /* layer digests, sa_build_digests layout for the kind        */
   const int32_t* block_table; /* [B][Hkv][max_blocks]                                     */
   const void* k_pool;       /* chunk-major K pages, bf16                                  */
-  const void* v_pool;       /* [P][bs][d] bf16                                            */
+  const void* v_pool;       /* [P][bs/16][d][16] bf16 (sa_pack_v_pages)                   */
   const float* host_o;      /* A_cpu^i: [B][Hq][d], normalised                            */
   const float* host_m;      /* [B][Hq], natural-log units                                 */
   const float* host_l;      /* [B][Hq]                                                    */

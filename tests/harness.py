@@ -186,7 +186,7 @@ def run_layer(wl: wk.Workload, kind: str, gen_device: str = "cpu", top_k: int | 
     ws = B.workspace(B.sa_workspace_bytes(dims, k))
     bt = pool["block_table"].to(dev)
     B.sa_select_blocks(dims, kind, Qg, dig_g, lens_d, k, bt, gb, ng, cb, nc, scores, ws)
-    Kp, Vp = B.pack_k_pages(dims, pool["K"].to(dev)), pool["V"].to(dev)
+    Kp, Vp = B.pack_k_pages(dims, pool["K"].to(dev)), B.pack_v_pages(dims, pool["V"].to(dev))
     rows = B_ * wl.num_q_heads
     o_gpu = torch.empty((rows, d), dtype=f32, device=dev)
     m_gpu = torch.empty(rows, dtype=f32, device=dev)

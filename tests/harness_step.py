@@ -80,7 +80,8 @@ def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs
         B.sa_build_digests(dims, kind, k_pool, Ld["pool"]["block_table"].to(dev), lens_d, dig)
         e = dict(x=Ld["X"].to(dev), w_q=B.pack_weight(Ld["W"].to(dev)), digests=dig,
                  block_table=Ld["pool"]["block_table"].to(dev), k_pool=k_pool,
-                 v_pool=Ld["pool"]["V"].to(dev), host_o=Ld["host"]["o"].to(dev).contiguous(),
+                 v_pool=B.pack_v_pages(dims, Ld["pool"]["V"].to(dev)),
+                 host_o=Ld["host"]["o"].to(dev).contiguous(),
                  host_m=Ld["host"]["m"].to(dev).contiguous(),
                  host_l=Ld["host"]["l"].to(dev).contiguous(),
                  gpu_blocks=torch.full((pairs, k), -7, dtype=i32, device=dev),

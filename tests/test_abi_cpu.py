@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_path(lib):
     names = declared_functions()
-    for n in ("sa_pack_k_pages", "sa_pack_weight", "sa_build_digests", "sa_predict_query",
+    for n in ("sa_pack_k_pages", "sa_pack_v_pages", "sa_pack_weight", "sa_build_digests",
+              "sa_predict_query",
               "sa_select_blocks", "sa_sparse_decode", "sa_merge", "sa_decode_attend_merge",
               "sa_decode_step"):
         assert n in names
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.sa_abi_version() == B.ABI_VERSION == 2
+    assert lib.sa_abi_version() == B.ABI_VERSION == 3
     assert lib.sa_status_string(B.SA_ERR_WORKSPACE) == b"SA_ERR_WORKSPACE"
 
 
@@ -145,6 +146,11 @@ def test_pack_validation(lib):
     assert lib.sa_pack_k_pages(ctypes.byref(d), FAKE, FAKE, None) == B.SA_ERR_INVALID_ARG
     assert lib.sa_pack_k_pages(ctypes.byref(d), FAKE, FAKE + nbytes - 16, None) == B.SA_ERR_INVALID_ARG
     assert lib.sa_pack_k_pages(ctypes.byref(dims(head_dim=96)), FAKE, FAKE + nbytes,
+                               None) == B.SA_ERR_UNSUPPORTED
+    assert lib.sa_pack_v_pages(ctypes.byref(d), None, FAKE, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_pack_v_pages(ctypes.byref(d), FAKE, None, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_pack_v_pages(ctypes.byref(d), FAKE, FAKE + nbytes - 2, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_pack_v_pages(ctypes.byref(dims(head_dim=96)), FAKE, FAKE + nbytes,
                                None) == B.SA_ERR_UNSUPPORTED
     assert lib.sa_pack_weight(16, 64, FAKE, FAKE + 4096, None) == B.SA_ERR_INVALID_ARG
     assert lib.sa_pack_weight(40, 64, FAKE, FAKE + 8192, None) == B.SA_ERR_UNSUPPORTED

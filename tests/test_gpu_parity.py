@@ -62,6 +62,23 @@ def test_layer_parity(name, wl, kind, kw):
 
 @pytest.mark.parametrize("kv,d,bs", [("bf16", 128, 32), ("bf16", 64, 16), ("f32", 128, 16),
                                      ("f32", 64, 32)])
+def test_pack_v_pages_layout(kv, d, bs):
+    """The V page layout, bit for bit: [P][bs][d] viewed as [P][bs/16][16][d] with the two
+    inner axes swapped."""
+    H.log(f"[case] pack V {kv} d{d} bs{bs}")
+    P = 29
+    g = torch.Generator().manual_seed(3 * d + bs)
+    dt = torch.bfloat16 if kv == "bf16" else torch.float32
+    rows = torch.randn(P, bs, d, generator=g).to(dt)
+    want = rows.view(P, bs // 16, 16, d).permute(0, 1, 3, 2).contiguous()
+    dims = B.Dims(1, 1, 1, d, bs, 1, P, B.SA_BF16 if kv == "bf16" else B.SA_F32)
+    got = B.pack_v_pages(dims, rows.cuda()).cpu().view(P, bs // 16, d, 16)
+    iv = torch.int16 if kv == "bf16" else torch.int32
+    assert torch.equal(got.view(iv), want.view(iv))
+
+
+@pytest.mark.parametrize("kv,d,bs", [("bf16", 128, 32), ("bf16", 64, 16), ("f32", 128, 16),
+                                     ("f32", 64, 32)])
 def test_pack_k_pages_layout(kv, d, bs):
     """The chunk-major K layout, bit for bit: [P][bs][d] viewed as [P][bs][d/x][x] with the
     two middle axes swapped (x = 16 bytes of elements)."""
