@@ -1,14 +1,17 @@
 // Block digests [ScoutAttention, arXiv:2603.27138, HTML Sec. 2.2]: the mean of K over a
 // block (MoBA-style) or the channel-wise min and max of K over a block (Quest-style).
 //
-// One wavefront per (sequence, KV head, block).  K pages are chunk-major ([d/x][bs][x], x
-// elements per 16-byte chunk), so one page is d/x chunk rows of bs tokens each.  Each load
-// instruction reads 8 chunks x 8 tokens: lane l takes chunk 8 cg + l / 8 and token
-// 8 tg + l % 8, so every group of 8 lanes reads one whole 128-byte line.  A lane keeps its
-// chunk's running sums (or min/max) over its tokens; the 8 lanes of a chunk then combine
-// theirs with cross-lane exchanges.  The mean accumulates in float64, where sums of bf16
-// keys are exact, and is rounded once to the stored dtype; min/max are exact in any
-// precision.  HBM-bound: the page is read once and d (or 2d) values are written.
+// Persistent waves walk the (sequence, KV head, block) slots.  K pages are chunk-major
+// ([d/x][bs][x], x elements per 16-byte chunk), so one page is d/x chunk rows of bs tokens
+// each.  Each load instruction reads 8 chunks x 8 tokens: lane l takes chunk 8 cg + l / 8
+// and token 8 tg + l % 8, so every group of 8 lanes reads one whole 128-byte line.  A lane
+// keeps its chunk's running sums (or min/max) over its tokens; the 8 lanes of a chunk then
+// combine theirs with a reduce-scatter, after which each lane owns (and writes) one
+// channel.  The mean accumulates in float64, where sums of bf16 keys are exact, and is
+// rounded once to the stored dtype; min/max are exact in any precision.  HBM-bound: the
+// page is read once and d (or 2d) values are written.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -31,134 +34,211 @@ struct Vec<float> {  // four float per 16-byte chunk
   }
 };
 
-__device__ __forceinline__ void store_vals(uint16_t* dst, const float* f, int n) {
-  // values are exact bf16 (min/max of bf16 keys): take the high half of the float
-  uint32_t w[4];
-  for (int i = 0; i < n / 2; ++i)
-    w[i] = (__float_as_uint(f[2 * i]) >> 16) | (__float_as_uint(f[2 * i + 1]) & 0xffff0000u);
-  *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-}
-__device__ __forceinline__ void store_vals(float* dst, const float* f, int) {
-  *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
-}
-__device__ __forceinline__ void store_mean(uint16_t* dst, const double* v, int n) {
-  uint32_t w[4];
-  for (int i = 0; i < n / 2; ++i)
-    w[i] = f64_to_bf16_rne(v[2 * i]) | (f64_to_bf16_rne(v[2 * i + 1]) << 16);
-  *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-}
-__device__ __forceinline__ void store_mean(float* dst, const double* v, int) {
-  *reinterpret_cast<float4*>(dst) =
-      make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+// One exchange step: a lane keeps H of its 2H values (the upper half when `upper`) and adds
+// the partner's copy of them (lane ^ mask).
+template <int H, typename V, typename Op>
+__device__ __forceinline__ void halve(V* v, bool upper, int mask, Op op) {
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const V send = upper ? v[i] : v[H + i];
+    const V keep = upper ? v[H + i] : v[i];
+    v[i] = op(keep, __shfl_xor(send, mask, kWave));
+  }
 }
 
+// Reduce-scatter over the 8 lanes of a chunk (tl = lane % 8) of N = 8 or 4 values per lane:
+// each exchange halves what a lane keeps (the upper lane of a pair keeps the upper half);
+// once one value is left the last exchange adds it whole.  Lane tl ends with element
+// (tl * N) / 8 of the chunk, reduced over the 8 lanes.
+template <int N, typename V, typename Op>
+__device__ __forceinline__ V reduce_scatter8(V (&v)[N], int tl, Op op) {
+  static_assert(N == 8 || N == 4, "chunk width");
+  if constexpr (N == 8) {
+    halve<4>(v, tl & 4, 4, op);
+    halve<2>(v, tl & 2, 2, op);
+    halve<1>(v, tl & 1, 1, op);
+  } else {
+    halve<2>(v, tl & 4, 4, op);
+    halve<1>(v, tl & 2, 2, op);
+    v[0] = op(v[0], __shfl_xor(v[0], 1, kWave));
+  }
+  return v[0];
+}
+
+__device__ __forceinline__ void store_one(uint16_t* dst, float f) {
+  *dst = (uint16_t)(__float_as_uint(f) >> 16);  // exact bf16 (a min or max of bf16 keys)
+}
+__device__ __forceinline__ void store_one(float* dst, float f) { *dst = f; }
+__device__ __forceinline__ void store_mean1(uint16_t* dst, double v) {
+  *dst = (uint16_t)f64_to_bf16_rne(v);
+}
+__device__ __forceinline__ void store_mean1(float* dst, double v) { *dst = (float)v; }
+
+// One block's digest from its page, already in registers (raw), written to slot gidx.
+template <typename T, int D, int BS, bool MINMAX>
+__device__ __forceinline__ void digest_block(const uint4 (&raw)[D / Vec<T>::N / 8][BS / 8],
+                                             int nvalid, T* __restrict__ dig, long gidx,
+                                             int cl, int tl) {
+  constexpr int VEC = Vec<T>::N;
+  constexpr int CG = D / VEC / 8, TG = BS / 8;
+  const int e = tl * VEC / 8;                          // this lane's element of its chunk
+  const bool writer = (tl * VEC) % 8 == 0;             // one lane per element
+#pragma unroll
+  for (int cg = 0; cg < CG; ++cg) {
+    const int ch = (8 * cg + cl) * VEC + e;            // this lane's channel
+    if constexpr (MINMAX) {
+      float mn[VEC], mx[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) { mn[i] = INFINITY; mx[i] = -INFINITY; }
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg) {  // tokens past the valid ones are left out
+        const bool ok = 8 * tg + tl < nvalid;
+        float f[VEC];
+        Vec<T>::widen(raw[cg][tg], f);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          mn[i] = fminf(mn[i], ok ? f[i] : INFINITY);
+          mx[i] = fmaxf(mx[i], ok ? f[i] : -INFINITY);
+        }
+      }
+      const float lo = reduce_scatter8<VEC>(mn, tl, [](float a, float b) { return fminf(a, b); });
+      const float hi = reduce_scatter8<VEC>(mx, tl, [](float a, float b) { return fmaxf(a, b); });
+      if (writer) {
+        T* dst = dig + (size_t)gidx * 2 * D + ch;
+        store_one(dst, lo);
+        store_one(dst + D, hi);
+      }
+    } else {
+      double acc[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] = 0.0;
+      if (nvalid >= BS) {  // a full block (all but a sequence's last)
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) {
+          float f[VEC];
+          Vec<T>::widen(raw[cg][tg], f);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) acc[i] += (double)f[i];
+        }
+      } else {
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) {  // tokens past the valid ones add 0
+          const bool ok = 8 * tg + tl < nvalid;
+          float f[VEC];
+          Vec<T>::widen(raw[cg][tg], f);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) acc[i] += (double)(ok ? f[i] : 0.f);
+        }
+      }
+      const double sum = reduce_scatter8<VEC>(acc, tl, [](double a, double b) { return a + b; });
+      if (writer) store_mean1(dig + (size_t)gidx * D + ch, sum / (double)nvalid);
+    }
+  }
+}
+
+// Persistent waves over the (pair, block) slots: wave w owns slots [w per, (w + 1) per) and
+// walks them in windows of 64.  Lane j reads window slot j's table entry and its sequence
+// length (one coalesced round); the resident blocks of the window are then digested in
+// order, the next one's page loads in flight while the current one is reduced.  Slots that
+// are not resident or lie past their sequence are skipped (their digests are not written).
 template <typename T, int D, int BS, bool MINMAX>
 __global__ __launch_bounds__(256) void digest_kernel(const T* __restrict__ k_pool,
                                                      const int32_t* __restrict__ table,
                                                      const int32_t* __restrict__ seq_lens,
                                                      T* __restrict__ dig, int Hkv,
-                                                     int max_blocks, long total) {
+                                                     int max_blocks, long total, long per) {
   constexpr int VEC = Vec<T>::N;  // elements per 16-byte chunk
   constexpr int NC = D / VEC;     // chunks per token
   constexpr int CG = NC / 8;      // chunk groups: 8 chunks per load instruction
   constexpr int TG = BS / 8;      // token groups: 8 tokens (one 128-byte line) per chunk
   static_assert(NC % 8 == 0 && BS % 8 == 0, "page shape");
   const int lane = threadIdx.x % kWave;
-  const long gw = (long)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (gw >= total) return;
-  const int pair = (int)(gw / max_blocks);
-  const int b = (int)(gw % max_blocks);
-  const int len = seq_lens[pair / Hkv];
-  if (b * BS >= len) return;
-  const int page = table[gw];
-  if (page < 0) return;
-  const int nvalid = min(BS, len - b * BS);
-  const T* src = k_pool + (size_t)page * BS * D;
+  const long gw = (long)blockIdx.x * (blockDim.x / kWave) +
+                  __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const long i0 = gw * per, i1 = min(total, i0 + per);
   const int cl = lane / 8, tl = lane % 8;  // chunk within the group, token within the group
 
   // the whole page in flight at once (CG * TG <= 16 loads of 16 bytes per lane)
-  uint4 raw[CG][TG];
+  auto load_page = [&](int page, uint4 (&raw)[CG][TG]) {
+    const T* src = k_pool + (size_t)page * BS * D;
 #pragma unroll
-  for (int cg = 0; cg < CG; ++cg)
+    for (int cg = 0; cg < CG; ++cg)
 #pragma unroll
-    for (int tg = 0; tg < TG; ++tg)
-      raw[cg][tg] = *reinterpret_cast<const uint4*>(
-          src + ((size_t)(8 * cg + cl) * BS + 8 * tg + tl) * VEC);
+      for (int tg = 0; tg < TG; ++tg)
+        raw[cg][tg] = *reinterpret_cast<const uint4*>(
+            src + ((size_t)(8 * cg + cl) * BS + 8 * tg + tl) * VEC);
+  };
 
-  if constexpr (MINMAX) {
-    float mn[CG][VEC], mx[CG][VEC];
+  for (long w0 = i0; w0 < i1; w0 += kWave) {
+    const long idx = min(w0 + lane, i1 - 1);
+    const int page_l = table[idx];
+    const int pair = (int)(idx / max_blocks), b = (int)(idx % max_blocks);
+    const int len = seq_lens[pair / Hkv];
+    const bool live = w0 + lane < i1 && page_l >= 0 && b * BS < len;
+    const int nval_l = min(BS, len - b * BS);
+    uint64_t mask = __ballot(live);
+    if (mask == 0) continue;
+    // resident blocks of the window in order; the next one's page is loaded before the
+    // current one is reduced (past the last, the last is loaded again: cached lines)
+    int j = __builtin_ctzll(mask);
+    mask &= mask - 1;
+    uint4 cur[CG][TG], nxt[CG][TG];
+    load_page(__builtin_amdgcn_readlane(page_l, j), cur);
+    while (true) {
+      const int jn = mask ? __builtin_ctzll(mask) : j;
+      load_page(__builtin_amdgcn_readlane(page_l, jn), nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      digest_block<T, D, BS, MINMAX>(cur, __builtin_amdgcn_readlane(nval_l, j), dig, w0 + j,
+                                     cl, tl);
+      if (!mask) break;
+      mask &= mask - 1;
+      j = jn;
 #pragma unroll
-    for (int cg = 0; cg < CG; ++cg) {
+      for (int cg = 0; cg < CG; ++cg)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) { mn[cg][i] = INFINITY; mx[cg][i] = -INFINITY; }
-#pragma unroll
-      for (int tg = 0; tg < TG; ++tg) {
-        if (8 * tg + tl < nvalid) {
-          float f[VEC];
-          Vec<T>::widen(raw[cg][tg], f);
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) {
-            mn[cg][i] = fminf(mn[cg][i], f[i]);
-            mx[cg][i] = fmaxf(mx[cg][i], f[i]);
-          }
-        }
-      }
-#pragma unroll
-      for (int o = 1; o < 8; o <<= 1)
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          mn[cg][i] = fminf(mn[cg][i], __shfl_xor(mn[cg][i], o, kWave));
-          mx[cg][i] = fmaxf(mx[cg][i], __shfl_xor(mx[cg][i], o, kWave));
-        }
-      if (tl == 0) {
-        T* dst = dig + (size_t)gw * 2 * D + (8 * cg + cl) * VEC;
-        store_vals(dst, mn[cg], VEC);
-        store_vals(dst + D, mx[cg], VEC);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int cg = 0; cg < CG; ++cg) {
-      double acc[VEC];
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] = 0.0;
-#pragma unroll
-      for (int tg = 0; tg < TG; ++tg) {
-        if (8 * tg + tl < nvalid) {
-          float f[VEC];
-          Vec<T>::widen(raw[cg][tg], f);
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) acc[i] += (double)f[i];
-        }
-      }
-#pragma unroll
-      for (int o = 1; o < 8; o <<= 1)
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) acc[i] += __shfl_xor(acc[i], o, kWave);
-      if (tl == 0) {
-        double v[VEC];
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) v[i] = acc[i] / (double)nvalid;
-        store_mean(dig + (size_t)gw * D + (8 * cg + cl) * VEC, v, VEC);
-      }
+        for (int tg = 0; tg < TG; ++tg) cur[cg][tg] = nxt[cg][tg];
     }
   }
+}
+
+// Waves the device holds at once for this instantiation (all CUs at full occupancy), found
+// once per instantiation.
+template <typename K>
+long resident_waves(K kernel, int block) {
+  static const long n = [&] {
+    int per_cu = 0, cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess ||
+        per_cu < 1 || cus < 1)
+      return 2048L;  // the grid only has to cover the slots; this size always does
+    return (long)per_cu * cus * (block / kWave);
+  }();
+  return n;
+}
+
+template <typename T, int D, int BS, bool MINMAX>
+hipError_t launch_kind(const Shape& s, const void* k_pool, const int32_t* table,
+                       const int32_t* lens, void* dig, hipStream_t stream) {
+  const long total = (long)s.B * s.Hkv * s.max_blocks;
+  const int waves_per_wg = 4, block = waves_per_wg * kWave;
+  auto kernel = digest_kernel<T, D, BS, MINMAX>;
+  // every wave resident at once, each a contiguous share of the slots
+  const long waves =
+      std::max(1L, std::min((total + kWave - 1) / kWave, resident_waves(kernel, block)));
+  const long per = (total + waves - 1) / waves;
+  const long nw = (total + per - 1) / per;
+  const dim3 grid((unsigned)((nw + waves_per_wg - 1) / waves_per_wg));
+  hipLaunchKernelGGL(kernel, grid, dim3(block), 0, stream, (const T*)k_pool, table, lens,
+                     (T*)dig, s.Hkv, s.max_blocks, total, per);
+  return hipGetLastError();
 }
 
 template <typename T, int D, int BS>
 hipError_t launch_typed(const Shape& s, bool minmax, const void* k_pool, const int32_t* table,
                         const int32_t* lens, void* dig, hipStream_t stream) {
-  const long total = (long)s.B * s.Hkv * s.max_blocks;
-  const int waves_per_wg = 4;
-  const dim3 grid((unsigned)((total + waves_per_wg - 1) / waves_per_wg));
-  const dim3 block(waves_per_wg * kWave);
-  if (minmax)
-    hipLaunchKernelGGL((digest_kernel<T, D, BS, true>), grid, block, 0, stream,
-                       (const T*)k_pool, table, lens, (T*)dig, s.Hkv, s.max_blocks, total);
-  else
-    hipLaunchKernelGGL((digest_kernel<T, D, BS, false>), grid, block, 0, stream,
-                       (const T*)k_pool, table, lens, (T*)dig, s.Hkv, s.max_blocks, total);
-  return hipGetLastError();
+  return minmax ? launch_kind<T, D, BS, true>(s, k_pool, table, lens, dig, stream)
+                : launch_kind<T, D, BS, false>(s, k_pool, table, lens, dig, stream);
 }
 
 template <typename T>

@@ -47,32 +47,43 @@ __global__ __launch_bounds__(256) void pack_w_kernel(const uint4* __restrict__ s
   dst[i] = src[(row * k + col) / 8];
 }
 
-// One thread per destination element (the source elements of 16 consecutive destinations
-// are one token row apart).
+// One workgroup per 16-token half-page (16 x d elements): 16-byte reads of the token rows
+// into LDS, then 16-byte writes of the channel-major result, each gathering one channel's
+// consecutive tokens from LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void pack_v_kernel(const T* __restrict__ src,
-                                                     T* __restrict__ dst, long total, int bs,
-                                                     int d) {
-  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  const long per_page = (long)bs * d;
-  const long page = i / per_page;
-  const int r = (int)(i % per_page);
-  const int half = r / (16 * d), c = (r / 16) % d, t = 16 * half + r % 16;
-  dst[i] = src[page * per_page + (long)t * d + c];
+                                                     T* __restrict__ dst, int d) {
+  constexpr int E = 16 / sizeof(T);  // elements per 16-byte chunk
+  extern __shared__ uint4 tile[];   // [16][d] elements
+  const T* s = src + (size_t)blockIdx.x * 16 * d;
+  T* o = dst + (size_t)blockIdx.x * 16 * d;
+  const int chunks = 16 * d / E;
+  for (int c = threadIdx.x; c < chunks; c += blockDim.x)
+    tile[c] = *reinterpret_cast<const uint4*>(s + (size_t)c * E);
+  __syncthreads();
+  const T* t = reinterpret_cast<const T*>(tile);
+  for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
+    const int ch = c / (16 / E), t0 = (c % (16 / E)) * E;  // channel, first token
+    T v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = t[(t0 + e) * d + ch];
+    uint4 w;
+    __builtin_memcpy(&w, v, sizeof(w));
+    *reinterpret_cast<uint4*>(o + (size_t)c * E) = w;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_pack_v(const Shape& s, const void* v_rows, void* v_pool, hipStream_t stream) {
-  const long total = (long)s.P * s.bs * s.d;
-  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  const dim3 grid((unsigned)((long)s.P * (s.bs / 16))), block(256);
+  const size_t lds = (size_t)16 * s.d * (s.bf16 ? 2 : 4);
   if (s.bf16)
-    hipLaunchKernelGGL(pack_v_kernel<uint16_t>, grid, block, 0, stream,
-                       (const uint16_t*)v_rows, (uint16_t*)v_pool, total, s.bs, s.d);
+    hipLaunchKernelGGL(pack_v_kernel<uint16_t>, grid, block, lds, stream,
+                       (const uint16_t*)v_rows, (uint16_t*)v_pool, s.d);
   else
-    hipLaunchKernelGGL(pack_v_kernel<float>, grid, block, 0, stream, (const float*)v_rows,
-                       (float*)v_pool, total, s.bs, s.d);
+    hipLaunchKernelGGL(pack_v_kernel<float>, grid, block, lds, stream, (const float*)v_rows,
+                       (float*)v_pool, s.d);
   return hipGetLastError();
 }
 
