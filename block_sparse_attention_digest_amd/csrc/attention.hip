@@ -81,16 +81,19 @@ __device__ __forceinline__ int wave_of(int g, int T, int W) {
   return (int)(((long long)(g + 1) * W + T - 1) / T) - 1;
 }
 
-// Exclusive prefix sum of n_gpu over the pairs into LDS pfx[0..npairs] (pfx[npairs] = T).
-// Every thread of the workgroup takes part; ends with a barrier.
-__device__ void pair_prefix(const int32_t* __restrict__ n_gpu, int npairs, int* pfx,
+// Exclusive prefix sum of n_gpu over the pairs into LDS pfx[0..npairs] (pfx[npairs] = T);
+// counts are taken clamped into [0, cap] (cap = the list stride), so no count read from
+// memory can move an index past the lists.  Every thread of the workgroup takes part; ends
+// with a barrier.
+__device__ __forceinline__ int clamp_count(int n, int cap) { return min(max(n, 0), cap); }
+__device__ void pair_prefix(const int32_t* __restrict__ n_gpu, int npairs, int cap, int* pfx,
                             int* wave_tot) {
   const int nt = blockDim.x, tid = threadIdx.x;
   const int lane = tid % kWave, wave = tid / kWave, nw = nt / kWave;
   const int per = (npairs + nt - 1) / nt;
   const int p0 = min(npairs, tid * per), p1 = min(npairs, p0 + per);
   int local = 0;
-  for (int p = p0; p < p1; ++p) local += n_gpu[p];
+  for (int p = p0; p < p1; ++p) local += clamp_count(n_gpu[p], cap);
   int incl = local;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
@@ -104,7 +107,7 @@ __device__ void pair_prefix(const int32_t* __restrict__ n_gpu, int npairs, int* 
   int run = base + incl - local;
   for (int p = p0; p < p1; ++p) {
     pfx[p] = run;
-    run += n_gpu[p];
+    run += clamp_count(n_gpu[p], cap);
   }
   if (tid == nt - 1) {
     int tot = 0;
@@ -173,7 +176,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ gpu_blocks,
     const int32_t* __restrict__ gpu_pages, const int32_t* __restrict__ n_gpu, int list_stride,
-    int Hkv, int max_blocks, int npairs, int W, float scale_log2, float* __restrict__ ws) {
+    int Hkv, int max_blocks, int P, int npairs, int W, float scale_log2,
+    float* __restrict__ ws) {
   constexpr int KS = D / 32;          // MFMA k-steps over the head dimension (S = K Q^T)
   constexpr int CG = D / 16;          // 16-channel groups of the output (O^T += V^T P)
   constexpr int HPB = BS / kStep;     // 16-token steps per block (1 or 2)
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   // scalars: a loop exit the compiler takes for lane-divergent ends in exec-masked flow
   // blocks, where it drains all loads in flight (vmcnt(0)) at the loop header
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  pair_prefix(n_gpu, npairs, pfx, wave_tot);
+  pair_prefix(n_gpu, npairs, list_stride, pfx, wave_tot);
   const PartialView part = partial_view(ws, npairs, W, G, D);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= npairs; i += blockDim.x) part.pfx[i] = pfx[i];
@@ -216,9 +220,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     int pj = pstart;
     while (pfx[pj + 1] <= g) ++pj;
     const size_t idx = (size_t)pj * list_stride + (g - pfx[pj]);
-    l_blk = gpu_blocks[idx];
+    // entries are taken clamped into range: a bad list gives wrong numbers, never an access
+    // outside the pools
+    l_blk = min(max(gpu_blocks[idx], 0), max_blocks - 1);
     l_len = seq_lens[pj / Hkv];
     l_page = gpu_pages ? gpu_pages[idx] : table[(size_t)pj * max_blocks + l_blk];
+    l_page = min(max(l_page, 0), P - 1);
   };
   // The first window's lookup is issued before the query staging so that their loads are
   // in flight together (a wave with no blocks looks up the last block, unused).
@@ -485,7 +492,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
     const float* __restrict__ v_pool, const int32_t* __restrict__ table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ gpu_blocks,
     const int32_t* __restrict__ n_gpu, int list_stride, int Hkv, int G, int max_blocks,
-    int npairs, int W, float scale_log2, float* __restrict__ ws) {
+    int P, int npairs, int W, float scale_log2, float* __restrict__ ws) {
   constexpr int CPL = D / kWave;  // channels per lane (1 or 2)
   extern __shared__ int pfx[];    // [npairs + 1]
   __shared__ float qs[8][D];
@@ -494,7 +501,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
   __shared__ float sc[8][BS];
   __shared__ int wave_tot[1];
   const int lane = threadIdx.x;
-  pair_prefix(n_gpu, npairs, pfx, wave_tot);
+  pair_prefix(n_gpu, npairs, list_stride, pfx, wave_tot);
   const PartialView part = partial_view(ws, npairs, W, G, D);
   if (blockIdx.x == 0)
     for (int i = lane; i <= npairs; i += kWave) part.pfx[i] = pfx[i];
@@ -538,8 +545,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
         qs[i / D][i % D] = v;
       }
     }
-    const int blk = gpu_blocks[(size_t)p * list_stride + (g_blk - pfx[p])];
-    const int page = table[(size_t)p * max_blocks + blk];
+    const int blk = min(max(gpu_blocks[(size_t)p * list_stride + (g_blk - pfx[p])], 0),
+                        max_blocks - 1);
+    const int page = min(max(table[(size_t)p * max_blocks + blk], 0), P - 1);
     const int nval = min(BS, seq_lens[p / Hkv] - blk * BS);
     __syncthreads();
     for (int i = lane; i < BS * D; i += kWave) {
@@ -585,7 +593,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 // that read further o vectors one by one.
 template <int D>
 __global__ __launch_bounds__(256) void reduce_kernel(
-    const float* __restrict__ ws, int npairs, int W, int G, int Hkv, int rows,
+    const float* __restrict__ ws, int npairs, int W, int G, int Hkv, int rows, int cap,
     const int32_t* __restrict__ n_gpu, const float* __restrict__ host_o,
     const float* __restrict__ host_m, const float* __restrict__ host_l,
     const int32_t* __restrict__ n_cpu, float* __restrict__ o, float* __restrict__ m,
@@ -601,7 +609,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(
   const PartialView part = partial_view(const_cast<float*>(ws), npairs, W, G, D);
 
   // round 1: the pair's block count and prefix, and the host partial
-  const int ng = n_gpu[pair];
+  const int ng = clamp_count(n_gpu[pair], cap);
   const int P = part.pfx[pair];
   const int T = part.pfx[npairs];
   const bool host_ptr = host_o != nullptr;
@@ -740,7 +748,7 @@ hipError_t attn_bf16_g(const Shape& s, const AttnPlan& p, const QParts& q, const
   case GG:                                                                                   \
     hipExtLaunchKernelGGL((attn_bf16_kernel<D, BS, GG>), grid, block, lds, st, e0, e1, 0, q, \
                           (const uint16_t*)k, (const uint16_t*)v, t, lens, gb, gp, ng, stride,\
-                          s.Hkv, s.max_blocks, npairs, p.waves, sl2, ws);                    \
+                          s.Hkv, s.max_blocks, s.P, npairs, p.waves, sl2, ws);               \
     break;
   switch (s.G) {
     SA_ATTN_CASE(1) SA_ATTN_CASE(2) SA_ATTN_CASE(3) SA_ATTN_CASE(4)
@@ -761,7 +769,7 @@ hipError_t attn_f32(const Shape& s, const AttnPlan& p, const QParts& q, const vo
   const size_t lds = (size_t)(npairs + 1) * sizeof(int);
   hipExtLaunchKernelGGL((attn_f32_kernel<D, BS>), dim3(p.waves), dim3(kWave), lds, st, e0, e1,
                         0, q, (const float*)k, (const float*)v, t, lens, gb, ng, stride, s.Hkv,
-                        s.G, s.max_blocks, npairs, p.waves, sl2, ws);
+                        s.G, s.max_blocks, s.P, npairs, p.waves, sl2, ws);
   return hipGetLastError();
 }
 
@@ -774,6 +782,7 @@ AttnPlan attn_plan(const Shape& s, int list_stride) {
   int w = (int)(most < kMaxWaves ? most : kMaxWaves);
   if (s.bf16) w = (w + kAttnWaves - 1) / kAttnWaves * kAttnWaves;
   p.waves = w < 1 ? 1 : w;
+  p.list_stride = list_stride;
   p.ws_bytes = prefix_bytes(npairs) +
                (size_t)(p.waves + npairs) * s.G * (s.d + 2) * sizeof(float);
   return p;
@@ -807,11 +816,12 @@ hipError_t launch_reduce(const Shape& s, const AttnPlan& plan, const int32_t* n_
   const dim3 grid((rows + 3) / 4), block(256);
   if (s.d == 128)
     hipLaunchKernelGGL(reduce_kernel<128>, grid, block, 0, stream, partials, npairs,
-                       plan.waves, s.G, s.Hkv, rows, n_gpu, host_o, host_m, host_l, n_cpu, o,
-                       m, l);
+                       plan.waves, s.G, s.Hkv, rows, plan.list_stride, n_gpu, host_o, host_m,
+                       host_l, n_cpu, o, m, l);
   else
     hipLaunchKernelGGL(reduce_kernel<64>, grid, block, 0, stream, partials, npairs, plan.waves,
-                       s.G, s.Hkv, rows, n_gpu, host_o, host_m, host_l, n_cpu, o, m, l);
+                       s.G, s.Hkv, rows, plan.list_stride, n_gpu, host_o, host_m, host_l, n_cpu,
+                       o, m, l);
   return hipGetLastError();
 }
 

@@ -140,13 +140,15 @@ __device__ __forceinline__ void digest_block(const uint4 (&raw)[D / Vec<T>::N / 
 // walks them in windows of 64.  Lane j reads window slot j's table entry and its sequence
 // length (one coalesced round); the resident blocks of the window are then digested in
 // order, the next one's page loads in flight while the current one is reduced.  Slots that
-// are not resident or lie past their sequence are skipped (their digests are not written).
+// are not resident (or name a page outside the pool) or lie past their sequence are skipped
+// (their digests are not written).
 template <typename T, int D, int BS, bool MINMAX>
 __global__ __launch_bounds__(256) void digest_kernel(const T* __restrict__ k_pool,
                                                      const int32_t* __restrict__ table,
                                                      const int32_t* __restrict__ seq_lens,
                                                      T* __restrict__ dig, int Hkv,
-                                                     int max_blocks, long total, long per) {
+                                                     int max_blocks, int P, long total,
+                                                     long per) {
   constexpr int VEC = Vec<T>::N;  // elements per 16-byte chunk
   constexpr int NC = D / VEC;     // chunks per token
   constexpr int CG = NC / 8;      // chunk groups: 8 chunks per load instruction
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(256) void digest_kernel(const T* __restrict__ k_poo
     const int page_l = table[idx];
     const int pair = (int)(idx / max_blocks), b = (int)(idx % max_blocks);
     const int len = seq_lens[pair / Hkv];
-    const bool live = w0 + lane < i1 && page_l >= 0 && b * BS < len;
+    const bool live = w0 + lane < i1 && page_l >= 0 && page_l < P && b * BS < len;
     const int nval_l = min(BS, len - b * BS);
     uint64_t mask = __ballot(live);
     if (mask == 0) continue;
@@ -230,7 +232,7 @@ hipError_t launch_kind(const Shape& s, const void* k_pool, const int32_t* table,
   const long nw = (total + per - 1) / per;
   const dim3 grid((unsigned)((nw + waves_per_wg - 1) / waves_per_wg));
   hipLaunchKernelGGL(kernel, grid, dim3(block), 0, stream, (const T*)k_pool, table, lens,
-                     (T*)dig, s.Hkv, s.max_blocks, total, per);
+                     (T*)dig, s.Hkv, s.max_blocks, s.P, total, per);
   return hipGetLastError();
 }
 

@@ -67,6 +67,7 @@ hipError_t launch_select(const Shape& s, bool minmax, const QParts& q, const voi
 // ---- attention: balanced waves write partials, then the reduction / merge per row -------
 struct AttnPlan {
   int waves;         // W: waves in the grid; the resident selected blocks are split evenly
+  int list_stride;   // entries per pair in the lists (bound of every per-pair count)
   size_t ws_bytes;   // pair prefix + one partial slot per (wave + pair) and head
 };
 AttnPlan attn_plan(const Shape& s, int list_stride);

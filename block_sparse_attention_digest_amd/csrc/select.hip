@@ -116,7 +116,9 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // scalar loop bounds
   const int pair = blockIdx.x;
   const int s = pair / Hkv, h = pair % Hkv;
-  const int nb = (seq_lens[s] + bs - 1) / bs;
+  // blocks of the sequence, clamped to the table's span (a bad length cannot move a read
+  // past the pair's rows)
+  const int nb = min(max((seq_lens[s] + bs - 1) / bs, 0), max_blocks);
   const uint32_t ks = (uint32_t)min(top_k, nb);
   const int cg = lane % LPR, bi = lane / LPR;
 

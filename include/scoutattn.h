@@ -21,9 +21,11 @@
  *     nothing.  A launch failure returns SA_ERR_HIP.  sa_last_error() then describes the
  *     failure (thread-local, valid until the next call on the same thread).  No C++
  *     exception crosses this interface.
- *   - Contents of device buffers (block-table entries, list entries, sequence lengths) are
- *     NOT checked on the host: they must satisfy the ranges stated below, otherwise the
- *     kernels read out of bounds.
+ *   - Contents of device buffers (block-table entries, list entries and counts, sequence
+ *     lengths) are NOT checked on the host: they must satisfy the ranges stated below,
+ *     otherwise the results are unspecified.  The kernels clamp every index they take from
+ *     these buffers, so no value in them makes a kernel access memory outside the buffers
+ *     described here.
  *   - Layouts are row-major, innermost index last.  "KV dtype" is sa_dims.kv_dtype:
  *     SA_F32 (float) or SA_BF16 (bfloat16 bit patterns, uint16).
  *
