@@ -14,8 +14,9 @@
 // pair's block range) and, when given, the host partial.
 //
 // bf16 path, per 16-token step of a wave (one MFMA tile: a block of 16, or half of 32):
-//   * the page and valid-token count of up to 64 upcoming blocks of one pair sit in lane
-//     registers, looked up in two dependent loads per window (list entry, block table);
+//   * the page and valid-token count of up to 64 upcoming blocks (of one or more pairs) sit
+//     in lane registers, looked up in one round per window from the page list when the
+//     selection wrote one (else list entry, then block table);
 //   * K (16 x d) is loaded straight into MFMA A-operand registers: lane l holds token
 //     l % 16 and 8 consecutive channels (16 bytes).  K pages are chunk-major (the bs
 //     tokens' values of 8 channels are 16 * bs contiguous bytes), so the 16 lanes that load
@@ -24,14 +25,16 @@
 //     bf16 high part (columns 0..7) and a bf16 low part q - hi (columns 8..15); adding the
 //     two results recovers q . k to about 2^-17 relative, so the float32 query keeps its
 //     precision while K stays bf16;
-//   * the softmax runs on the MFMA output layout (lane l: head l % 8, four tokens) with
-//     DPP / permlane exchanges; p goes through a 1 KiB LDS slab to the PV layout;
-//   * O += P V on the vector ALU: lane l owns 8 channels of every 4th (d = 128) token row;
-//   * steps are 16 tokens so that two of them (the one computed and the one in flight) fit
-//     the register budget of 2 waves per SIMD without spilling;
-//   * the next step's K and V are in flight while the current step is computed; all of a
-//     step's loads are issued unconditionally (clamped to valid rows) so that the waits
-//     before a step cover that step only.
+//   * the softmax runs on the MFMA output layout (lane l: column l % 16, four tokens) with
+//     DPP / permlane exchanges;
+//   * O^T += V^T P on v_mfma_f32_16x16x16_bf16: V^T is the A operand (lane l: channel
+//     l % 16 of a 16-channel group, four tokens -- 8 contiguous bytes of a V page stored as
+//     [bs/16][d][16]), and P is the B operand straight from the softmax registers (its
+//     layout is the S^T layout), split like Q into bf16(p) (columns 0..7) and p - bf16(p)
+//     (columns 8..15);
+//   * the two steps after the one being computed are in flight; all of a step's loads are
+//     issued unconditionally (clamped to valid rows) so that the waits before a step cover
+//     that step only, and the pipeline runs on across pair boundaries.
 // float32 path (small fp32 workloads): the same balanced ranges, one block at a time, K
 // (chunk-major, four channels per chunk) and V staged through LDS and plain per-lane dot
 // products.

@@ -11,9 +11,10 @@
 // with up to 24 k-steps in flight.  A workgroup's waves own consecutive tiles of the same
 // k-slice, so the slice of x they share (at most 64 rows) is staged once in LDS, by
 // global-to-LDS loads issued just ahead of the W stream (so the staging overlaps it) --
-// up to 160 KiB, so one k-slice can be long and the float32
-// partials of the slices (summed in slice order by a second kernel, so results are
-// deterministic) stay a small fraction of the W bytes.  The plan sizes the grid to about
+// up to 160 KiB, so one k-slice can be long and the float32 partials of the slices stay a
+// small fraction of the W bytes.  The partials are summed in slice order -- by a second
+// kernel in the stand-alone call, by the kernels that read the query in the decode step --
+// so results are deterministic.  The plan sizes the grid to about
 // one workgroup per CU, so the whole product is one round of long-lived waves.  Two weight
 // matrices that share x (Q^i and Q_pred^{i+1}) can run as one launch.
 #include <algorithm>
