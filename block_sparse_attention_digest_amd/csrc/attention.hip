@@ -611,7 +611,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(
   const int pair = s * Hkv + qh / G, g = qh % G;
   const PartialView part = partial_view(const_cast<float*>(ws), npairs, W, G, D);
 
-  // round 1: the pair's block count and prefix, and the host partial
+  // first loads: the pair's block count and prefix, and the host partial
   const int ng = clamp_count(n_gpu[pair], cap);
   const int P = part.pfx[pair];
   const int T = part.pfx[npairs];
@@ -646,7 +646,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(
     return part.o[sl * D + lane + kWave * i];
   };
 
-  // round 2: (m, l) of the covering waves, one per lane, and the first kPre o vectors
+  // second loads: (m, l) of the covering waves, one per lane, and the first kPre o vectors
   float M = mh, L = 0.f;
   float acc[CPL];
 #pragma unroll
