@@ -120,6 +120,48 @@ __device__ void pair_prefix(const int32_t* __restrict__ n_gpu, int npairs, int c
   __syncthreads();
 }
 
+// The same prefix computed by each wave on its own, for npairs <= kWave * kPrefixRun: lane i
+// sums the counts of pairs [i r, i r + r) (r = ceil(npairs / kWave)) and one wave scan joins
+// the runs.  The waves of a workgroup all write the same values, and each reads the array
+// only after writing all of it itself, so no barrier is needed.  Returns T = pfx[npairs].
+constexpr int kPrefixRun = 8;
+__device__ int wave_prefix(const int32_t* __restrict__ n_gpu, int npairs, int cap, int* pfx) {
+  const int lane = threadIdx.x % kWave;
+  const int per = (npairs + kWave - 1) / kWave;
+  const int p0 = lane * per;
+  int v[kPrefixRun];
+  int local = 0;
+#pragma unroll
+  for (int u = 0; u < kPrefixRun; ++u) {  // loads unconditional, indexes clamped
+    const int c = n_gpu[min(p0 + u, npairs - 1)];
+    v[u] = u < per && p0 + u < npairs ? clamp_count(c, cap) : 0;
+    local += v[u];
+  }
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
+  }
+  int run = incl - local;
+#pragma unroll
+  for (int u = 0; u < kPrefixRun; ++u) {
+    if (u < per && p0 + u < npairs) pfx[p0 + u] = run;
+    run += v[u];
+  }
+  const int T = __builtin_amdgcn_readlane(incl, kWave - 1);
+  if (lane == 0) pfx[npairs] = T;
+  return T;
+}
+
+// Workgroup barrier that orders LDS accesses only: a wave waits for its own LDS writes, not
+// for its global loads in flight (which a __syncthreads would drain).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // last pair p with pfx[p] <= g (the pair holding global block g when g < T)
 __device__ __forceinline__ int pair_of(const int* pfx, int npairs, int g) {
   int lo = 0, hi = npairs - 1;
@@ -130,47 +172,78 @@ __device__ __forceinline__ int pair_of(const int* pfx, int npairs, int g) {
   return lo;
 }
 
-// The query rows of pairs [q_lo, q_lo + q_n) summed from their parts into LDS, in part
-// order: every thread of the workgroup takes part (all of its loads of a group of parts are
-// in flight together); ends with a barrier.
+// The query rows of pairs [q_lo, q_lo + q_n) summed from their parts, in part order, for
+// staging in LDS.  Every thread of the workgroup takes kSlots float4 of them.  stage_load
+// only issues the loads of the first kPartGroup parts (all in flight together), so the
+// caller can issue other loads before stage_store sums them (loading any further parts) and
+// writes the sums out.
 template <int G, int D>
-__device__ void stage_queries(const QParts& q, int Hkv, int q_lo, int q_n, float* q_lds) {
-  constexpr int kPerPair = G * D / 4;  // float4 per pair
-  constexpr int kSlots = (kQStage * kPerPair + 255) / 256;
-  const int total = q_n * kPerPair;
-  const int nt = blockDim.x;
+struct QStage {
+  static constexpr int kPerPair = G * D / 4;  // float4 per pair
+  static constexpr int kSlots = (kQStage * kPerPair + 255) / 256;
   const float* src[kSlots];
+  float4 t[kPartGroup][kSlots];
+};
+template <int G, int D>
+__device__ __forceinline__ void stage_load_group(const QParts& q, int p0, QStage<G, D>& st) {
 #pragma unroll
-  for (int j = 0; j < kSlots; ++j) {
-    const int i = min((int)threadIdx.x + j * nt, total - 1);  // past the end: a re-read
+  for (int u = 0; u < kPartGroup; ++u)
+#pragma unroll
+    for (int j = 0; j < QStage<G, D>::kSlots; ++j)
+      st.t[u][j] = *reinterpret_cast<const float4*>(
+          st.src[j] + (size_t)min(p0 + u, q.parts - 1) * q.part_stride);
+}
+template <int G, int D>
+__device__ __forceinline__ void stage_load(const QParts& q, int Hkv, int q_lo, int q_n,
+                                           QStage<G, D>& st) {
+  constexpr int kPerPair = QStage<G, D>::kPerPair;
+  const int total = max(q_n, 1) * kPerPair;  // q_n = 0: a re-read of pair q_lo, unused
+#pragma unroll
+  for (int j = 0; j < QStage<G, D>::kSlots; ++j) {
+    const int i = min((int)threadIdx.x + j * (int)blockDim.x, total - 1);  // past the end: a re-read
     const int pair = q_lo + i / kPerPair, e = i % kPerPair;
-    src[j] = q.base + (size_t)(pair / Hkv) * q.row_stride + (size_t)(pair % Hkv) * G * D + 4 * e;
+    st.src[j] = q.base + (size_t)(pair / Hkv) * q.row_stride + (size_t)(pair % Hkv) * G * D + 4 * e;
   }
+  stage_load_group(q, 0, st);
+}
+// adds parts p0 + u (u = u0 .. kPartGroup - 1) that exist; branch-free selects on the
+// uniform part count keep the waits on these loads exact
+template <int G, int D>
+__device__ __forceinline__ void stage_sum_group(const QParts& q, int p0, int u0,
+                                                const QStage<G, D>& st,
+                                                float4 (&acc)[QStage<G, D>::kSlots]) {
+#pragma unroll
+  for (int u = 0; u < kPartGroup; ++u) {
+    if (u < u0) continue;
+    const bool use = p0 + u < q.parts;
+#pragma unroll
+    for (int j = 0; j < QStage<G, D>::kSlots; ++j) {
+      const float4 t = st.t[u][j];
+      acc[j].x = use ? acc[j].x + t.x : acc[j].x;
+      acc[j].y = use ? acc[j].y + t.y : acc[j].y;
+      acc[j].z = use ? acc[j].z + t.z : acc[j].z;
+      acc[j].w = use ? acc[j].w + t.w : acc[j].w;
+    }
+  }
+}
+template <int G, int D>
+__device__ __forceinline__ void stage_store(const QParts& q, int q_n, QStage<G, D>& st,
+                                            float* q_lds) {
+  constexpr int kSlots = QStage<G, D>::kSlots;
   float4 acc[kSlots];
-  for (int p0 = 0; p0 < q.parts; p0 += kPartGroup) {
-    float4 t[kPartGroup][kSlots];
 #pragma unroll
-    for (int u = 0; u < kPartGroup; ++u)
-#pragma unroll
-      for (int j = 0; j < kSlots; ++j)
-        t[u][j] = *reinterpret_cast<const float4*>(src[j] + (size_t)min(p0 + u, q.parts - 1) *
-                                                               q.part_stride);
-#pragma unroll
-    for (int u = 0; u < kPartGroup; ++u)
-#pragma unroll
-      for (int j = 0; j < kSlots; ++j) {
-        if (p0 + u == 0) { acc[j] = t[u][j]; continue; }
-        if (p0 + u >= q.parts) continue;
-        acc[j].x += t[u][j].x; acc[j].y += t[u][j].y;
-        acc[j].z += t[u][j].z; acc[j].w += t[u][j].w;
-      }
+  for (int j = 0; j < kSlots; ++j) acc[j] = st.t[0][j];
+  stage_sum_group(q, 0, 1, st, acc);
+  for (int p0 = kPartGroup; p0 < q.parts; p0 += kPartGroup) {  // more parts: one group at a time
+    stage_load_group(q, p0, st);
+    stage_sum_group(q, p0, 0, st, acc);
   }
+  const int total = q_n * QStage<G, D>::kPerPair;
 #pragma unroll
   for (int j = 0; j < kSlots; ++j) {
-    const int i = (int)threadIdx.x + j * nt;
+    const int i = (int)threadIdx.x + j * (int)blockDim.x;
     if (i < total) *reinterpret_cast<float4*>(q_lds + 4 * i) = acc[j];
   }
-  __syncthreads();
 }
 
 template <int D, int BS, int G>
@@ -194,11 +267,17 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   // scalars: a loop exit the compiler takes for lane-divergent ends in exec-masked flow
   // blocks, where it drains all loads in flight (vmcnt(0)) at the loop header
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  pair_prefix(n_gpu, npairs, list_stride, pfx, wave_tot);
+  int T;
+  if (npairs <= kWave * kPrefixRun) {  // (uniform)
+    T = wave_prefix(n_gpu, npairs, list_stride, pfx);
+  } else {
+    pair_prefix(n_gpu, npairs, list_stride, pfx, wave_tot);
+    T = pfx[npairs];
+  }
+  T = __builtin_amdgcn_readfirstlane(T);
   const PartialView part = partial_view(ws, npairs, W, G, D);
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i <= npairs; i += blockDim.x) part.pfx[i] = pfx[i];
-  const int T = __builtin_amdgcn_readfirstlane(pfx[npairs]);
+  if (blockIdx.x == 0 && wave == 0)
+    for (int i = lane; i <= npairs; i += kWave) part.pfx[i] = pfx[i];
   const int gw = blockIdx.x * kAttnWaves + wave;
   if (T == 0) return;
   // the queries of the first kQStage pairs the workgroup's block range touches
@@ -230,13 +309,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     l_page = gpu_pages ? gpu_pages[idx] : table[(size_t)pj * max_blocks + l_blk];
     l_page = min(max(l_page, 0), P - 1);
   };
-  // The first window's lookup is issued before the query staging so that their loads are
-  // in flight together (a wave with no blocks looks up the last block, unused).
+  // The first window's lookup and the query staging loads are issued together (a wave with
+  // no blocks looks up the last block, unused).
   const int gfirst = min(b0, T - 1);
   int p = __builtin_amdgcn_readfirstlane(pair_of(pfx, npairs, gfirst));
   lookup(gfirst, b0 < b1 ? min(kWave, b1 - b0) : 1, p);
-  if (q_n > 0) stage_queries<G, D>(q, Hkv, q_lo, q_n, q_lds);
-  if (b0 >= b1) return;
+  QStage<G, D> qst;
+  stage_load<G, D>(q, Hkv, q_lo, q_n, qst);
+  __builtin_amdgcn_sched_barrier(0);  // issued here, ahead of the first window's K/V loads
 
   const int c16 = lane % 16;   // MFMA column (head / hi-lo) and token row in the tile
   const int kq = lane / 16;    // MFMA k-group
@@ -426,12 +506,39 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     while (pp < npairs - 1 && __builtin_amdgcn_readfirstlane(pfx[pp + 1]) <= end) ++pp;
     return pp;
   };
-  bool open = false;  // a partial of pair p is being accumulated
-  for (int wb = b0; wb < b1; wb += kWave) {
-    const int nw = min(kWave, b1 - wb);
-    if (wb != b0) lookup(wb, nw, p);
+  // A window's pages and valid-token counts go to lane registers and the loads of its first
+  // two steps are issued.  The steps past the window's end re-read its last step (lines that
+  // are still cached), so every path has the same loads in flight.
+  StepRegs ra, rb, rc;
+  int nw = 1, nst = 1;
+  auto ld = [&](int st, StepRegs& R) {
+    const int sc = min(st, nst - 1);
+    load_step(sc / HPB, sc % HPB, R);
+  };
+  auto open_window = [&](int wb) {
+    nw = max(1, min(kWave, b1 - wb));
     w_page = l_page;
     w_nval = min(BS, l_len - l_blk * BS);
+    nst = nw * HPB;
+    ld(0, ra);
+    ld(1, rb);
+  };
+  // The first window opens before the staged queries are written out, so its loads are in
+  // flight while the workgroup meets at the staging barrier (which orders LDS only).  A wave
+  // with no blocks has loaded its clamped lookup's page and stops there.
+  open_window(b0);
+  if (q_n > 0) {  // (uniform over the workgroup)
+    stage_store<G, D>(q, q_n, qst, q_lds);
+    lds_barrier();
+  }
+  if (b0 >= b1) return;
+
+  bool open = false;  // a partial of pair p is being accumulated
+  for (int wb = b0; wb < b1; wb += kWave) {
+    if (wb != b0) {
+      lookup(wb, min(kWave, b1 - wb), p);
+      open_window(wb);
+    }
     int bnd = __builtin_amdgcn_readfirstlane(pfx[p + 1]) - wb;  // first block of the next pair
     // before step s (block s / HPB): switch pairs at a pair's first block
     auto enter = [&](int s) {
@@ -449,18 +556,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     };
     // HPB steps per block; a second half holding no valid token is fully masked.  Three
     // steps per iteration, the two after the one being computed in flight (so a wave keeps
-    // the memory busy on its own once its SIMD neighbour has finished).  The loads are
-    // unconditional (steps past the end re-read the last step, lines that are still
-    // cached) so every path has the same loads in flight, and the scheduling barriers keep
-    // the compiler from sinking them to their use.
-    const int nst = nw * HPB;
-    auto ld = [&](int st, StepRegs& R) {
-      const int sc = min(st, nst - 1);
-      load_step(sc / HPB, sc % HPB, R);
-    };
-    StepRegs ra, rb, rc;
-    ld(0, ra);
-    ld(1, rb);
+    // the memory busy on its own once its SIMD neighbour has finished); the scheduling
+    // barriers keep the compiler from sinking the loads to their use.
     for (int st = 0; st < nst; st += 3) {
       ld(st + 2, rc);
       __builtin_amdgcn_sched_barrier(0);
