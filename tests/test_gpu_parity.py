@@ -51,6 +51,10 @@ LAYER_CASES = [
     ("f32-d128-bs32", wk.TINY.scaled(num_q_heads=10, num_kv_heads=2, head_dim=128,
                                      block_size=32, context=1000, top_k=6), "minmax", {}),
     ("bf16-short-seqs", wk.RAGGED.scaled(batch=5, ctx_min=1, ctx_max=40, top_k=3), "mean", {}),
+    # more than 512 (sequence, KV head) pairs: attention's workgroup-wide prefix scan, and
+    # workgroup ranges that cross more pairs than it stages queries for
+    ("bf16-many-pairs", wk.RAGGED.scaled(batch=72, ctx_min=1, ctx_max=300, top_k=4), "mean", {}),
+    ("bf16-512-pairs", wk.RAGGED.scaled(batch=64, ctx_min=1, ctx_max=300, top_k=4), "mean", {}),
 ]
 
 
