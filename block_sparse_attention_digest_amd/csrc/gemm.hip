@@ -26,12 +26,14 @@ namespace sa {
 namespace {
 
 constexpr int kGroup = 8;            // k-steps (of 32) per register buffer
-constexpr int kMaxWpg = 10;          // waves per workgroup (640 threads: up to 168 VGPRs)
+// waves per workgroup: small workgroups (about 122 VGPRs per wave, at most two waves on a
+// SIMD) leave room on every CU for an attention or selection workgroup running beside them
+constexpr int kMaxWpg = 5;
 constexpr int kTargetUnits = 1024;   // >= 4 long-lived waves per CU
 constexpr int kCUs = 256;
 
 template <int MT>
-__global__ __launch_bounds__(640) void gemm_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(kMaxWpg * kWave) void gemm_kernel(const uint16_t* __restrict__ x,
                                                     const uint16_t* __restrict__ w0,
                                                     const uint16_t* __restrict__ w1, int m,
                                                     int n, int k, int kslice, int n_total,
