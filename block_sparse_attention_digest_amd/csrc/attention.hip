@@ -154,14 +154,6 @@ __device__ int wave_prefix(const int32_t* __restrict__ n_gpu, int npairs, int ca
   return T;
 }
 
-// Workgroup barrier that orders LDS accesses only: a wave waits for its own LDS writes, not
-// for its global loads in flight (which a __syncthreads would drain).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // last pair p with pfx[p] <= g (the pair holding global block g when g < T)
 __device__ __forceinline__ int pair_of(const int* pfx, int npairs, int g) {
   int lo = 0, hi = npairs - 1;

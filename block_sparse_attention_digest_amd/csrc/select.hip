@@ -5,11 +5,15 @@
 //   1. scoring: the G query heads of the KV head are folded into per-channel coefficients
 //      -- the group sum sum_g q_g for mean digests, and for min/max digests
 //        sum_g max(q_gc min_c, q_gc max_c) = (sum_g max(q_gc, 0)) max_c + (sum_g min(q_gc, 0)) min_c
-//      (exact, since max_c >= min_c) -- so a digest element costs one or two FMAs.  Each
-//      wave streams a contiguous share of the pair's digest rows with 16-byte loads, the next
-//      batch of 8 loads in flight while the current one is reduced (DPP row sums; loads are
-//      unconditional so the waits cover one batch); the scores stay in LDS.  Every pair's workgroup is resident at once, so HBM bandwidth is
-//      shared evenly and the whole digest set streams in one pass.
+//      (exact, since max_c >= min_c) -- so a digest element costs one or two FMAs.  The
+//      query rows (all their parts), the first digest batch and the pair's block-table
+//      entries are requested together in one round: the workgroup sums the query parts into
+//      LDS and each lane reads its coefficients from there behind an LDS-only barrier, while
+//      the digests are already in flight.  Each wave streams a contiguous share of the
+//      pair's digest rows with 16-byte loads, the next batch of 8 loads in flight while the
+//      current one is reduced (DPP row sums; loads are unconditional so the waits cover one
+//      batch); the scores stay in LDS.  Every pair's workgroup is resident at once, so HBM
+//      bandwidth is shared evenly and the whole digest set streams in one pass.
 //   2. top-k: a histogram of the score values over 256 equal-width buckets locates the
 //      bucket holding the k-th largest score; the few scores in that bucket are ranked
 //      exactly by (score, lower index first).  Crowded buckets (e.g. all scores equal) fall
@@ -28,6 +32,9 @@ constexpr int kSelWaves = 8;
 constexpr int kSelThreads = kSelWaves * kWave;
 constexpr int kBatch = 8;        // 16-byte loads per lane per batch
 constexpr int kMaxCand = 256;    // boundary-bucket candidates ranked directly
+constexpr int kSelPartGroup = 4; // query parts loaded together
+constexpr int kTblRun = 8;       // block-table entries a thread holds in registers
+constexpr int kMaxGroup = 8;     // query heads per KV head
 constexpr uint8_t kSelected = 1, kResident = 2;  // per-block flag bits
 
 template <typename T>
@@ -111,11 +118,25 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
   __shared__ uint32_t cand_key[kMaxCand];
   __shared__ int cand_idx[kMaxCand];
   __shared__ uint32_t sel_digit, sel_remaining, sel_count, ncand, tot_res, tot_off;
+  __shared__ float4 q_sum[kMaxGroup * D / 4];  // the pair's G query rows, parts summed
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // scalar loop bounds
   const int pair = blockIdx.x;
   const int s = pair / Hkv, h = pair % Hkv;
+
+  // The pair's query rows come first, in one round: thread t loads float4 t of the G rows
+  // (G D / 4 <= kSelThreads), its first kSelPartGroup parts at once (indexes clamped, so every
+  // thread issues the same loads).
+  constexpr int kQ4 = D / 4;
+  const bool q_own = tid < G * kQ4;
+  const float* qsrc = q.base + (size_t)s * q.row_stride + (size_t)h * G * D +
+                      4 * (size_t)(q_own ? tid : 0);
+  float4 qp[kSelPartGroup];
+#pragma unroll
+  for (int u = 0; u < kSelPartGroup; ++u)
+    qp[u] = *reinterpret_cast<const float4*>(qsrc + (size_t)min(u, q.parts - 1) * q.part_stride);
+  __builtin_amdgcn_sched_barrier(0);  // issued ahead of the digest and table loads
   // blocks of the sequence, clamped to the table's span (a bad length cannot move a read
   // past the pair's rows)
   const int nb = min(max((seq_lens[s] + bs - 1) / bs, 0), max_blocks);
@@ -132,43 +153,54 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
   auto load_batch = [&](int b_first, uint4* buf) {
 #pragma unroll
     for (int u = 0; u < kBatch / LPB; ++u) {
-      const int b = min(b_first + u * BPI + bi, wb1 - 1);
+      const int b = max(min(b_first + u * BPI + bi, wb1 - 1), 0);
 #pragma unroll
       for (int r = 0; r < LPB; ++r)
         buf[u * LPB + r] = *reinterpret_cast<const uint4*>(base + (size_t)b * ROW + r * D);
     }
   };
-  if (wb0 < wb1) load_batch(wb0, bufa);
+  load_batch(wb0, bufa);  // (a wave with no rows re-reads a valid one, unused)
 
-  // residency of every block (block table read while the digests stream)
+  // residency of every block: the block table is read while the digests stream, into
+  // registers (kTblRun entries per thread) that are only consumed after the scoring
   const int32_t* trow = table + (size_t)pair * max_blocks;
-  for (int i = tid; i < nb; i += kSelThreads) {
-    const int32_t e = trow[i];
-    flag[i] = e >= 0 ? kResident : 0;
-    if (gpu_pages) pg[i] = e;
-  }
+  const bool tbl_regs = nb > 0 && nb <= kTblRun * kSelThreads;  // (uniform)
+  int32_t tbl[kTblRun];  // (loads unconditional, indexes clamped to a valid entry)
+#pragma unroll
+  for (int u = 0; u < kTblRun; ++u) tbl[u] = trow[max(min(tid + u * kSelThreads, nb - 1), 0)];
   if (tid < 256) hist[tid] = 0;
   if (tid == 0) ncand = 0;
 
-  // per-channel coefficients of this lane's VEC channels (each query element is the sum of
-  // its parts, taken in part order)
+  // each query element is the sum of its parts, taken in part order
+  {
+    float4 v = qp[0];
+    auto add = [&](const float4& w, bool use) {
+      v.x = use ? v.x + w.x : v.x; v.y = use ? v.y + w.y : v.y;
+      v.z = use ? v.z + w.z : v.z; v.w = use ? v.w + w.w : v.w;
+    };
+#pragma unroll
+    for (int u = 1; u < kSelPartGroup; ++u) add(qp[u], u < q.parts);
+    for (int p0 = kSelPartGroup; p0 < q.parts; p0 += kSelPartGroup) {  // more parts (rare)
+#pragma unroll
+      for (int u = 0; u < kSelPartGroup; ++u)
+        qp[u] = *reinterpret_cast<const float4*>(qsrc + (size_t)min(p0 + u, q.parts - 1) *
+                                                            q.part_stride);
+#pragma unroll
+      for (int u = 0; u < kSelPartGroup; ++u) add(qp[u], p0 + u < q.parts);
+    }
+    if (q_own) q_sum[tid] = v;
+  }
+  lds_barrier();  // the summed rows are visible; the digest loads stay in flight
+
+  // per-channel coefficients of this lane's VEC channels, summed over the heads in order
   float ca[VEC], cb[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) { ca[i] = 0.f; cb[i] = 0.f; }
-  const float* qg = q.base + (size_t)s * q.row_stride + (size_t)h * G * D + cg * VEC;
   for (int g = 0; g < G; ++g) {
     float v[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; i += 4)
-      *reinterpret_cast<float4*>(v + i) = *reinterpret_cast<const float4*>(qg + (size_t)g * D + i);
-    for (int part = 1; part < q.parts; ++part) {
-      const float* qp = qg + (size_t)part * q.part_stride + (size_t)g * D;
-#pragma unroll
-      for (int i = 0; i < VEC; i += 4) {
-        const float4 w = *reinterpret_cast<const float4*>(qp + i);
-        v[i] += w.x; v[i + 1] += w.y; v[i + 2] += w.z; v[i + 3] += w.w;
-      }
-    }
+      *reinterpret_cast<float4*>(v + i) = q_sum[g * kQ4 + (cg * VEC + i) / 4];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
       if (MINMAX) { ca[i] += fmaxf(v[i], 0.f); cb[i] += fminf(v[i], 0.f); }
@@ -216,6 +248,23 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
     load_batch(min(b + 2 * BPB, wb1 - 1), bufa);
     __builtin_amdgcn_sched_barrier(0);
     if (b + BPB < wb1) score_batch(b + BPB, bufb);
+  }
+  // the residency flags (and pages), from the table entries read at the start
+  if (tbl_regs) {
+#pragma unroll
+    for (int u = 0; u < kTblRun; ++u) {
+      const int i = tid + u * kSelThreads;
+      if (i < nb) {
+        flag[i] = tbl[u] >= 0 ? kResident : 0;
+        if (gpu_pages) pg[i] = tbl[u];
+      }
+    }
+  } else {
+    for (int i = tid; i < nb; i += kSelThreads) {
+      const int32_t e = trow[i];
+      flag[i] = e >= 0 ? kResident : 0;
+      if (gpu_pages) pg[i] = e;
+    }
   }
   lo = wave_min(lo);
   hi = wave_max(hi);
