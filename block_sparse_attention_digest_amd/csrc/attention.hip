@@ -726,9 +726,10 @@ __global__ __launch_bounds__(256) void reduce_kernel(
     nslot = wave_of(P + ng - 1, T, W) - w_lo + 1;
   }
   // a covering wave with an empty range (possible when W > T) wrote no partial
+  // (with no more waves than blocks every wave has a block)
   auto slot_live = [&](int j) {
     const int w = w_lo + j;
-    return j < nslot && wave_start(w, T, W) < wave_start(w + 1, T, W);
+    return j < nslot && (W <= T || wave_start(w, T, W) < wave_start(w + 1, T, W));
   };
   auto o_of = [&](int j, int i) {  // o of covering wave j (index clamped into the slots)
     const size_t sl = (size_t)(w_lo + j + pair) * G + g;
