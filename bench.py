@@ -370,7 +370,10 @@ def main():
                      "algorithmic_bytes_per_launch": int(attn_bytes_avg),
                      "measured": f"{nprof} launches in {args.profile_steps} eager steps "
                                  "after the timed region, HIP events at each kernel's start "
-                                 "and end"},
+                                 "and end",
+                     "shares_hbm_with": "the next layer's selection on the side stream, "
+                                        "which streams its digests during most of the "
+                                        "launch (step_hbm_gbs covers both)"},
         "roofline_isolated": {"kernel": "attn_bf16_kernel (GPUATTN), launched alone",
                               "bound": "hbm", "achieved": round(iso_achieved, 1),
                               "peak": PEAK_HBM_GBS, "unit": "GB/s",
