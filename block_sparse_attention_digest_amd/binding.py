@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libscoutattn.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = 0, -1, -2, -3, -4
 SA_F32, SA_BF16 = 0, 1
 SA_DIGEST_MEAN, SA_DIGEST_MINMAX = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 KIND = {"mean": SA_DIGEST_MEAN, "minmax": SA_DIGEST_MINMAX}
 
@@ -74,6 +74,8 @@ SIGNATURES = {
     "sa_decode_step": (ctypes.c_int, [_D, ctypes.c_int, _I, _I, _F, _P, _I,
                                       ctypes.POINTER(sa_layer), _P, _Z, _P, _P]),
     "sa_profile_attention": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.POINTER(_P), _I]),
+    "sa_host_partial_attention": (ctypes.c_int, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _I, _F,
+                                                 _P, _P, _P, _I]),
 }
 
 _lib = None
@@ -103,13 +105,16 @@ def _check(status: int):
 
 
 def _ptr(t, dtype=None, numel=None, name="tensor", device=True):
-    """Device pointer of a contiguous tensor (None -> NULL), with marshalling checks."""
+    """Pointer of a contiguous tensor (None -> NULL) on the GPU (device=True) or the host,
+    with marshalling checks."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name}: expected a torch.Tensor")
     if device and not t.is_cuda:
         raise ValueError(f"{name}: expected a GPU tensor")
+    if not device and t.is_cuda:
+        raise ValueError(f"{name}: expected a host (CPU) tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name}: expected a contiguous tensor")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
@@ -325,6 +330,27 @@ def sa_merge(o_a, m_a, l_a, o_b, m_b, l_b, o, m, l, stream=None):
                           _ptr(m_b, f, rows, "m_b"), _ptr(l_b, f, rows, "l_b"),
                           _ptr(o, f, rows * d, "o"), _ptr(m, f, rows, "m"),
                           _ptr(l, f, rows, "l"), _stream(stream)))
+
+
+def sa_host_partial_attention(dims: Dims, q, k_host, v_host, host_table, seq_lens, cpu_blocks,
+                              n_cpu, list_stride: int, scale: float, o, m, l, threads: int = 0):
+    """A_cpu on host threads: every argument is a CPU tensor (k_host, v_host [pages][bs][d])."""
+    rows = dims.batch * dims.num_q_heads
+    pairs = dims.batch * dims.num_kv_heads
+    pages = k_host.shape[0]
+    per_page = dims.block_size * dims.head_dim
+    i32, f32 = torch.int32, torch.float32
+    _check(lib().sa_host_partial_attention(
+        ctypes.byref(dims.c()), pages,
+        _ptr(q, f32, rows * dims.head_dim, "q", device=False),
+        _ptr(k_host, dims.kv_torch, pages * per_page, "k_host", device=False),
+        _ptr(v_host, dims.kv_torch, pages * per_page, "v_host", device=False),
+        _ptr(host_table, i32, pairs * dims.max_blocks, "host_table", device=False),
+        _ptr(seq_lens, i32, dims.batch, "seq_lens", device=False),
+        _ptr(cpu_blocks, i32, pairs * list_stride, "cpu_blocks", device=False),
+        _ptr(n_cpu, i32, pairs, "n_cpu", device=False), list_stride, scale,
+        _ptr(o, f32, rows * dims.head_dim, "o", device=False),
+        _ptr(m, f32, rows, "m", device=False), _ptr(l, f32, rows, "l", device=False), threads))
 
 
 def sa_decode_step(dims: Dims, kind: str, hidden: int, top_k: int, scale: float, seq_lens,

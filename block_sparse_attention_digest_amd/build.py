@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libscoutattn.so")
 
-SOURCES = ["api.hip", "layout.hip", "digest.hip", "gemm.hip", "select.hip", "attention.hip"]
+SOURCES = ["api.hip", "layout.hip", "digest.hip", "gemm.hip", "select.hip", "attention.hip",
+           "host_attention.cpp"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -54,7 +55,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     jobs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         jobs.append([cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))

@@ -10,6 +10,9 @@
 #include <vector>
 
 #include "../../include/scoutattn.h"
+#include <exception>
+
+#include "host.hpp"
 #include "kernels.hpp"
 
 namespace {
@@ -393,6 +396,63 @@ sa_status sa_merge(int32_t rows, int32_t d, const float* o_a, const float* m_a,
   SA_NOT_NULL(l);
   SA_HIP(sa::launch_merge(rows, d, o_a, m_a, l_a, o_b, m_b, l_b, o, m, l, stream),
          "merge kernel");
+  return ok();
+}
+
+// ---- the host side: partial attention over the offloaded blocks ------------------------------
+
+sa_status sa_host_partial_attention(const sa_dims* dims, int32_t host_pages,
+                                    const float* q_host, const void* k_host,
+                                    const void* v_host, const int32_t* host_table,
+                                    const int32_t* seq_lens_host,
+                                    const int32_t* cpu_blocks_host, const int32_t* n_cpu_host,
+                                    int32_t list_stride, float scale, float* o_host,
+                                    float* m_host, float* l_host, int32_t num_threads) {
+  sa::Shape s;
+  SA_CHECK(check_dims(dims, &s));
+  SA_CHECK(check_scale(scale));
+  if (host_pages < 1) return fail(SA_ERR_INVALID_ARG, "host_pages %d < 1", host_pages);
+  if (list_stride < 1 || list_stride > s.max_blocks)
+    return fail(SA_ERR_INVALID_ARG, "list_stride %d outside [1, max_blocks = %d]", list_stride,
+                s.max_blocks);
+  if (num_threads < 0) return fail(SA_ERR_INVALID_ARG, "num_threads %d < 0", num_threads);
+  SA_NOT_NULL(q_host);
+  SA_NOT_NULL(k_host);
+  SA_NOT_NULL(v_host);
+  SA_NOT_NULL(host_table);
+  SA_NOT_NULL(seq_lens_host);
+  SA_NOT_NULL(cpu_blocks_host);
+  SA_NOT_NULL(n_cpu_host);
+  SA_NOT_NULL(o_host);
+  SA_NOT_NULL(m_host);
+  SA_NOT_NULL(l_host);
+  sa::HostAttnArgs a;
+  a.B = s.B;
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.G = s.G;
+  a.d = s.d;
+  a.bs = s.bs;
+  a.max_blocks = s.max_blocks;
+  a.host_pages = host_pages;
+  a.list_stride = list_stride;
+  a.bf16 = s.bf16;
+  a.scale = scale;
+  a.q = q_host;
+  a.k_host = k_host;
+  a.v_host = v_host;
+  a.host_table = host_table;
+  a.seq_lens = seq_lens_host;
+  a.cpu_blocks = cpu_blocks_host;
+  a.n_cpu = n_cpu_host;
+  a.o = o_host;
+  a.m = m_host;
+  a.l = l_host;
+  try {
+    sa::host_partial_attention(a, sa::host_threads(num_threads));
+  } catch (const std::exception& e) {  // (thread creation; no exception crosses the ABI)
+    return fail(SA_ERR_INVALID_ARG, "host worker failed: %s", e.what());
+  }
   return ok();
 }
 

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 3
+#define SA_ABI_VERSION 4
 
 typedef enum {
   SA_OK = 0,
@@ -231,6 +231,37 @@ sa_status sa_decode_attend_merge(const sa_dims* dims, const float* q, const void
                                  const float* host_l, const int32_t* n_cpu, float* o,
                                  float* m, float* l, void* ws, size_t ws_bytes,
                                  hipStream_t stream);
+
+/*
+ * sa_host_partial_attention -- A_cpu, the CPU side of the collaborative attention
+ * ([Alg. 1]: the blocks of B_pred that are not resident on the GPU, B_cpu, are attended on
+ * the CPU from host memory; [HTML Sec. 3.2, 3.3]).  HOST memory and host threads only: no
+ * stream, no device pointer, and the call returns when the results are written.
+ *
+ * For every sequence s and query head qh (KV head h = qh / G): the partial (o, m, l) of
+ * q[s][qh] over the valid tokens of blocks cpu_blocks_host[s][h][0 .. n_cpu_host[s][h]),
+ * with scale `scale` (natural-log units: m is the largest scaled logit, l the sum of
+ * exp(logit - m), o the normalised weighted sum of V rows) -- the form sa_merge and
+ * sa_decode_attend_merge take as their host partial.  A pair with no block gives
+ * (o = 0, m = -inf, l = 0).
+ *
+ *   dims: as for the device calls (num_pages is not used here); host_pages: pages in the
+ *   host pool.  q_host [B][Hq][d] float32.  k_host, v_host [host_pages][bs][d], KV dtype,
+ *   token rows (the layout blocks are offloaded in).  host_table [B][Hkv][max_blocks]
+ *   int32: the host page of each block, or -1.  seq_lens_host [B].  cpu_blocks_host
+ *   [B][Hkv][list_stride], n_cpu_host [B][Hkv]: the offloaded lists, as sa_select_blocks
+ *   or sa_decode_step hand them over.  o_host [B][Hq][d], m_host, l_host [B][Hq] float32.
+ *   num_threads: worker threads (0: the machine's hardware threads).
+ * List entries outside [0, max_blocks), blocks without a host page and blocks past their
+ * sequence are skipped.  The result does not depend on num_threads.
+ */
+sa_status sa_host_partial_attention(const sa_dims* dims, int32_t host_pages,
+                                    const float* q_host, const void* k_host,
+                                    const void* v_host, const int32_t* host_table,
+                                    const int32_t* seq_lens_host,
+                                    const int32_t* cpu_blocks_host, const int32_t* n_cpu_host,
+                                    int32_t list_stride, float scale, float* o_host,
+                                    float* m_host, float* l_host, int32_t num_threads);
 
 /* ---------------------------------------------------------------------------------------
  * sa_decode_step -- one decode step over num_layers layers in the layer-ahead order of

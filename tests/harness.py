@@ -88,11 +88,14 @@ def oracle_query(wl, qin):
 
 
 def run_layer(wl: wk.Workload, kind: str, gen_device: str = "cpu", top_k: int | None = None,
-              resident_override=None, pairs_to_check=None) -> LayerRun:
+              resident_override=None, pairs_to_check=None, host_worker=False) -> LayerRun:
     """Run one single-layer workload (configs 1, 2, 3, 5 and their scaled variants).
 
     resident_override: None (the workload recipe), "all" or "none".
     pairs_to_check: None (all pairs) or a list of pair indices for the output comparison.
+    host_worker: the host partial comes from the library's host worker over the GPU's own
+    offloaded lists and the token-row pages in host memory (Algorithm 1 end to end), instead
+    of from the oracle.
     """
     dev = "cuda"
     res = LayerRun()
@@ -192,9 +195,21 @@ def run_layer(wl: wk.Workload, kind: str, gen_device: str = "cpu", top_k: int | 
     m_gpu = torch.empty(rows, dtype=f32, device=dev)
     l_gpu = torch.empty(rows, dtype=f32, device=dev)
     B.sa_sparse_decode(dims, Qg, Kp, Vp, bt, lens_d, gb, ng, k, wl.scale, o_gpu, m_gpu, l_gpu, ws)
-    hto = torch.from_numpy(host_o).to(f32).to(dev).contiguous()
-    htm = torch.from_numpy(host_m).to(f32).to(dev).contiguous()
-    htl = torch.from_numpy(host_l).to(f32).to(dev).contiguous()
+    if host_worker:  # A_cpu on host threads, from the hand-off lists and host pages
+        torch.cuda.synchronize()
+        ho = torch.empty((rows, d), dtype=f32)
+        hm = torch.empty(rows, dtype=f32)
+        hl = torch.empty(rows, dtype=f32)
+        B.sa_host_partial_attention(dims_full, Qg.cpu().contiguous(), kv["K"].cpu().contiguous(),
+                                    kv["V"].cpu().contiguous(),
+                                    kv["table"].cpu().to(i32).contiguous(), lens.cpu().to(i32),
+                                    cb.cpu(), nc.cpu(), k, wl.scale, ho, hm, hl, 8)
+        hto, htm, htl = ho.to(dev), hm.to(dev), hl.to(dev)
+        log("  host worker done")
+    else:
+        hto = torch.from_numpy(host_o).to(f32).to(dev).contiguous()
+        htm = torch.from_numpy(host_m).to(f32).to(dev).contiguous()
+        htl = torch.from_numpy(host_l).to(f32).to(dev).contiguous()
     o_fin = torch.empty_like(o_gpu)
     m_fin = torch.empty_like(m_gpu)
     l_fin = torch.empty_like(l_gpu)

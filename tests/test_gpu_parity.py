@@ -59,6 +59,11 @@ LAYER_CASES = [
     # cross more pairs than they stage queries for (those are summed from global memory)
     ("bf16-one-block-pairs", wk.RAGGED.scaled(batch=300, ctx_min=1, ctx_max=16, top_k=1), "mean",
      dict(resident_override="all")),
+    # Algorithm 1 end to end: the host partial from the host worker over the GPU's hand-off
+    # lists and host pages, merged on the GPU
+    ("cfg1-host-worker", TINY, "mean", dict(host_worker=True)),
+    ("cfg3-scaled-minmax-host-worker", CFG3_S, "minmax", dict(host_worker=True)),
+    ("cfg5-scaled-mean-host-worker", CFG5_S, "mean", dict(host_worker=True)),
 ]
 
 
