@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libscoutattn.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = 0, -1, -2, -3, -4
 SA_F32, SA_BF16 = 0, 1
 SA_DIGEST_MEAN, SA_DIGEST_MINMAX = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 KIND = {"mean": SA_DIGEST_MEAN, "minmax": SA_DIGEST_MINMAX}
 
@@ -60,6 +60,7 @@ SIGNATURES = {
     "sa_pack_v_pages": (ctypes.c_int, [_D, _P, _P, _P]),
     "sa_pack_weight": (ctypes.c_int, [_I, _I, _P, _P, _P]),
     "sa_build_digests": (ctypes.c_int, [_D, ctypes.c_int, _P, _P, _P, _P, _P]),
+    "sa_refresh_last_digests": (ctypes.c_int, [_D, ctypes.c_int, _P, _P, _P, _P, _P]),
     "sa_predict_query_workspace_bytes": (_Z, [_I, _I, _I]),
     "sa_predict_query": (ctypes.c_int, [_I, _I, _I, _P, _P, _P, _P, _Z, _P]),
     "sa_workspace_bytes": (_Z, [_D, _I]),
@@ -251,6 +252,19 @@ def sa_build_digests(dims: Dims, kind: str, k_pool, block_table, seq_lens, diges
     per = 2 if kind == "minmax" else 1
     n_dig = dims.batch * dims.num_kv_heads * dims.max_blocks * per * dims.head_dim
     _check(lib().sa_build_digests(
+        ctypes.byref(dims.c()), KIND[kind],
+        _ptr(k_pool, dims.kv_torch, dims.num_pages * dims.block_size * dims.head_dim, "k_pool"),
+        _ptr(block_table, torch.int32, dims.batch * dims.num_kv_heads * dims.max_blocks,
+             "block_table"),
+        _ptr(seq_lens, torch.int32, dims.batch, "seq_lens"),
+        _ptr(digests, dims.kv_torch, n_dig, "digests"), _stream(stream)))
+
+
+def sa_refresh_last_digests(dims: Dims, kind: str, k_pool, block_table, seq_lens, digests,
+                            stream=None):
+    per = 2 if kind == "minmax" else 1
+    n_dig = dims.batch * dims.num_kv_heads * dims.max_blocks * per * dims.head_dim
+    _check(lib().sa_refresh_last_digests(
         ctypes.byref(dims.c()), KIND[kind],
         _ptr(k_pool, dims.kv_torch, dims.num_pages * dims.block_size * dims.head_dim, "k_pool"),
         _ptr(block_table, torch.int32, dims.batch * dims.num_kv_heads * dims.max_blocks,

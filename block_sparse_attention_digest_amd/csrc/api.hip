@@ -258,6 +258,22 @@ sa_status sa_build_digests(const sa_dims* dims, sa_digest_kind kind, const void*
   return ok();
 }
 
+sa_status sa_refresh_last_digests(const sa_dims* dims, sa_digest_kind kind,
+                                  const void* k_pool, const int32_t* block_table,
+                                  const int32_t* seq_lens, void* digests, hipStream_t stream) {
+  sa::Shape s;
+  SA_CHECK(check_dims(dims, &s));
+  SA_CHECK(check_kind(kind));
+  SA_NOT_NULL(k_pool);
+  SA_NOT_NULL(block_table);
+  SA_NOT_NULL(seq_lens);
+  SA_NOT_NULL(digests);
+  SA_HIP(sa::launch_refresh_digests(s, kind == SA_DIGEST_MINMAX, k_pool, block_table,
+                                    seq_lens, digests, stream),
+         "digest refresh kernel");
+  return ok();
+}
+
 size_t sa_predict_query_workspace_bytes(int32_t m, int32_t n, int32_t k) {
   if (check_gemm_shape(m, n, k) != SA_OK) return 0;
   return sa::gemm_plan(m, n, k).ws_bytes;

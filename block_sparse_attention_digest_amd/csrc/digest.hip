@@ -203,6 +203,39 @@ __global__ __launch_bounds__(256) void digest_kernel(const T* __restrict__ k_poo
   }
 }
 
+// Digest maintenance during decode: one wave per (sequence, KV head) recomputes the digest of
+// the block that holds the sequence's last token, from its page, with the same arithmetic
+// as the full build (so the entry is bit-identical to what digest_kernel writes).  A pair
+// whose last block is not resident (or names a page outside the pool) is left unchanged.
+template <typename T, int D, int BS, bool MINMAX>
+__global__ __launch_bounds__(256) void refresh_kernel(const T* __restrict__ k_pool,
+                                                      const int32_t* __restrict__ table,
+                                                      const int32_t* __restrict__ seq_lens,
+                                                      T* __restrict__ dig, int Hkv, int npairs,
+                                                      int max_blocks, int P) {
+  constexpr int VEC = Vec<T>::N;
+  constexpr int CG = D / VEC / 8, TG = BS / 8;
+  const int lane = threadIdx.x % kWave;
+  const int pair = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (pair >= npairs) return;
+  const int len = seq_lens[pair / Hkv];
+  if (len < 1) return;
+  const int b = min((len - 1) / BS, max_blocks - 1);
+  const int page = table[(size_t)pair * max_blocks + b];
+  if (page < 0 || page >= P) return;
+  const int cl = lane / 8, tl = lane % 8;
+  uint4 raw[CG][TG];
+  const T* src = k_pool + (size_t)page * BS * D;
+#pragma unroll
+  for (int cg = 0; cg < CG; ++cg)
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg)
+      raw[cg][tg] = *reinterpret_cast<const uint4*>(
+          src + ((size_t)(8 * cg + cl) * BS + 8 * tg + tl) * VEC);
+  digest_block<T, D, BS, MINMAX>(raw, min(BS, len - b * BS), dig,
+                                 (long)pair * max_blocks + b, cl, tl);
+}
+
 // Waves the device holds at once for this instantiation (all CUs at full occupancy), found
 // once per instantiation.
 template <typename K>
@@ -253,7 +286,39 @@ hipError_t launch_dtype(const Shape& s, bool minmax, const void* k, const int32_
                     : launch_typed<T, 64, 16>(s, minmax, k, t, l, dig, st);
 }
 
+template <typename T, int D, int BS>
+hipError_t refresh_typed(const Shape& s, bool minmax, const void* k, const int32_t* t,
+                         const int32_t* l, void* dig, hipStream_t st) {
+  const int npairs = s.B * s.Hkv;
+  const dim3 grid((npairs + 3) / 4), block(256);
+  if (minmax)
+    hipLaunchKernelGGL((refresh_kernel<T, D, BS, true>), grid, block, 0, st, (const T*)k, t, l,
+                       (T*)dig, s.Hkv, npairs, s.max_blocks, s.P);
+  else
+    hipLaunchKernelGGL((refresh_kernel<T, D, BS, false>), grid, block, 0, st, (const T*)k, t, l,
+                       (T*)dig, s.Hkv, npairs, s.max_blocks, s.P);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t refresh_dtype(const Shape& s, bool minmax, const void* k, const int32_t* t,
+                         const int32_t* l, void* dig, hipStream_t st) {
+  if (s.d == 128)
+    return s.bs == 32 ? refresh_typed<T, 128, 32>(s, minmax, k, t, l, dig, st)
+                      : refresh_typed<T, 128, 16>(s, minmax, k, t, l, dig, st);
+  return s.bs == 32 ? refresh_typed<T, 64, 32>(s, minmax, k, t, l, dig, st)
+                    : refresh_typed<T, 64, 16>(s, minmax, k, t, l, dig, st);
+}
+
 }  // namespace
+
+hipError_t launch_refresh_digests(const Shape& s, bool minmax, const void* k_pool,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  void* digests, hipStream_t stream) {
+  if (s.bf16)
+    return refresh_dtype<uint16_t>(s, minmax, k_pool, block_table, seq_lens, digests, stream);
+  return refresh_dtype<float>(s, minmax, k_pool, block_table, seq_lens, digests, stream);
+}
 
 hipError_t launch_build_digests(const Shape& s, bool minmax, const void* k_pool,
                                 const int32_t* block_table, const int32_t* seq_lens,

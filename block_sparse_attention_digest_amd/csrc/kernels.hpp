@@ -26,6 +26,11 @@ hipError_t launch_pack_w(int n, int k, const void* w, void* w_packed, hipStream_
 hipError_t launch_build_digests(const Shape& s, bool minmax, const void* k_pool,
                                 const int32_t* block_table, const int32_t* seq_lens,
                                 void* digests, hipStream_t stream);
+// the digest of each (sequence, KV head)'s last block only, from its page (decode-time
+// maintenance after a token append); bit-identical to launch_build_digests for that block
+hipError_t launch_refresh_digests(const Shape& s, bool minmax, const void* k_pool,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  void* digests, hipStream_t stream);
 
 // A float32 query [B][Hq][d] held as the sum of `parts` arrays (the k-slice partials of the
 // query GEMM, or one plain array), summed by its consumer in part order.

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 4
+#define SA_ABI_VERSION 5
 
 typedef enum {
   SA_OK = 0,
@@ -112,6 +112,20 @@ const char* sa_status_string(sa_status status);
 sa_status sa_build_digests(const sa_dims* dims, sa_digest_kind kind, const void* k_pool,
                            const int32_t* block_table, const int32_t* seq_lens,
                            void* digests, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * sa_refresh_last_digests -- digest maintenance during decode [HTML Sec. 2.2]: after the
+ * token at position seq_lens[s] - 1 has been written into its page, the digest of the
+ * block that holds it changes (its mean or min/max gains one token; a token that opens a
+ * new block gives that block its first digest).  This recomputes, for every (sequence s,
+ * KV head h), only the entry of block (seq_lens[s] - 1) / bs, from its page, with the same
+ * arithmetic as sa_build_digests, so the entry is bit-identical to what a full rebuild
+ * writes.  Arguments and layouts as for sa_build_digests; a pair whose last block is not
+ * resident (table -1) is left unchanged.
+ * ------------------------------------------------------------------------------------- */
+sa_status sa_refresh_last_digests(const sa_dims* dims, sa_digest_kind kind,
+                                  const void* k_pool, const int32_t* block_table,
+                                  const int32_t* seq_lens, void* digests, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * sa_pack_k_pages -- layout conversion (no arithmetic): k_rows [P][bs][d] token-row pages

@@ -33,7 +33,7 @@ def test_header_declares_the_path(lib):
     for n in ("sa_pack_k_pages", "sa_pack_v_pages", "sa_pack_weight", "sa_build_digests",
               "sa_predict_query",
               "sa_select_blocks", "sa_sparse_decode", "sa_merge", "sa_decode_attend_merge",
-              "sa_decode_step", "sa_host_partial_attention"):
+              "sa_decode_step", "sa_host_partial_attention", "sa_refresh_last_digests"):
         assert n in names
 
 
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.sa_abi_version() == B.ABI_VERSION == 4
+    assert lib.sa_abi_version() == B.ABI_VERSION == 5
     assert lib.sa_status_string(B.SA_ERR_WORKSPACE) == b"SA_ERR_WORKSPACE"
 
 

@@ -135,6 +135,47 @@ def test_predict_query_parity(m, n, k):
     assert err <= H.TOL_GEMM, err
 
 
+@pytest.mark.parametrize("kind,kv,d,bs", [("mean", "bf16", 128, 32), ("minmax", "bf16", 64, 16),
+                                          ("mean", "f32", 64, 16), ("minmax", "f32", 128, 32)])
+def test_refresh_last_digests(kind, kv, d, bs):
+    """Decode-time digest maintenance: after one more token per sequence, refreshing the
+    last blocks gives exactly what a full rebuild gives (and what the oracle gives), for a
+    partly filled block, a block that becomes full and a token that opens a new block."""
+    H.log(f"[case] refresh digests {kind} {kv} d{d} bs{bs}")
+    B_, Hq, Hkv, mb = 6, 4, 2, 5
+    g = torch.Generator().manual_seed(d + bs + (kind == "minmax"))
+    dt = torch.bfloat16 if kv == "bf16" else torch.float32
+    P = B_ * Hkv * mb
+    rows = torch.randn(P, bs, d, generator=g).to(dt)  # every block of every pair has a page
+    table = torch.randperm(P, generator=g).to(torch.int32).view(B_, Hkv, mb)
+    lens0 = torch.tensor([1, bs - 1, bs, bs + 1, 2 * bs - 1, 3 * bs], dtype=torch.int32)
+    lens1 = lens0 + 1
+    dims = B.Dims(B_, Hq, Hkv, d, bs, mb, P, B.SA_BF16 if kv == "bf16" else B.SA_F32)
+    per = 2 if kind == "minmax" else 1
+    kp = B.pack_k_pages(dims, rows.cuda())
+    bt = table.cuda()
+    def build(lens):
+        dig = torch.zeros((B_, Hkv, mb, per, d), dtype=dt, device="cuda")
+        B.sa_build_digests(dims, kind, kp, bt, lens.cuda(), dig)
+        return dig
+    dig = build(lens0)
+    B.sa_refresh_last_digests(dims, kind, kp, bt, lens1.cuda(), dig)
+    want = build(lens1)
+    torch.cuda.synchronize()
+    iv = torch.int16 if kv == "bf16" else torch.int32
+    assert torch.equal(dig.cpu().view(iv), want.cpu().view(iv))
+    # and the refreshed entries against the oracle
+    for s in range(B_):
+        n = int(lens1[s])
+        b = (n - 1) // bs
+        for h in range(Hkv):
+            K = wk.f64(wk.logical_rows(rows, table[s, h], n))
+            ref = (so.digest_mean(K, n, bs, kv) if kind == "mean" else
+                   so.digest_minmax(K, n, bs))[b].reshape(per, d)
+            got = wk.f64(dig[s, h, b].cpu())
+            assert np.array_equal(got, ref), (s, h)
+
+
 def test_merge_parity_and_aliasing():
     H.log("[case] merge")
     rows, d = 37, 128
