@@ -1,5 +1,8 @@
 """Build libscoutattn.so for gfx950 with hipcc (objects in parallel, then one link).
 
+The HIP sources go through hipcc; the host-only C++ source (the CPU partial attention) goes
+through the host C++ compiler, which can give it per-CPU clones.
+
     python -m block_sparse_attention_digest_amd.build
 
 The library lands next to this file; objects go to _build/ (not committed).
@@ -32,6 +35,18 @@ FLAGS = [
 ]
 
 
+# -Wno-psabi: the 32-byte vector helpers are internal, so their calling convention never
+# crosses an interface
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-psabi", "-pthread", f"-I{INCLUDE}"]
+
+
+def host_cxx() -> str:
+    for c in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("no host C++ compiler found (g++ is required to build libscoutattn)")
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -57,14 +72,17 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        jobs.append([cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        if src.endswith(".hip"):
+            jobs.append([cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        else:
+            jobs.append([host_cxx(), *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
     with ThreadPoolExecutor(max_workers=workers) as ex:
         for msg in ex.map(_run, jobs):
             if msg.strip() and verbose:
                 print(msg, file=sys.stderr)
     tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp, *objs])
     os.replace(tmp, LIB)
     return LIB
 

@@ -7,7 +7,8 @@
 // One task per (sequence, KV head): the G query heads that share the KV head walk the pair's
 // offloaded blocks together, so each key and value row is read from memory once per pair.
 // Each head keeps an online softmax in float32 (running maximum m, sum l, and the unscaled
-// output row); the result is the normalised partial (o, m, l) with m in natural-log units,
+// output row), updated once per block; the result is the normalised partial (o, m, l) with m
+// in natural-log units,
 // the form the GPU merge takes.  Tasks go to worker threads through an atomic counter, so
 // pairs with many offloaded blocks do not hold the others up; a pair is always computed by
 // one thread in one order, so the result does not depend on the thread count.
@@ -33,17 +34,111 @@ inline float to_f32(uint16_t v) {  // bfloat16 bit pattern
   return f;
 }
 
-// dot product with eight independent partial sums (so the compiler can keep them in SIMD
-// lanes); d is a multiple of 8
-inline float dot(const float* a, const float* b, int d) {
-  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < d; c += 8)
-    for (int i = 0; i < 8; ++i) s[i] += a[c + i] * b[c + i];
-  return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+// eight floats as one vector value (two SSE registers, or one AVX register where the build has it)
+typedef float v8f __attribute__((vector_size(32)));
+
+inline v8f load8(const float* p) {
+  v8f v;
+  std::memcpy(&v, p, sizeof v);
+  return v;
+}
+inline void store8(float* p, v8f v) { std::memcpy(p, &v, sizeof v); }
+
+// One block of one pair for the G query heads, on float rows already converted: the block's
+// G x nval logits first (each key row read once for all heads), then one online-softmax update
+// per head (one rescale of the running output per block, not per token), then P V with a
+// 16-column strip of the G output rows held in registers across the block's tokens.  The head
+// dimension is a multiple of 16.  z holds G rows of zs logits.
+template <int G>
+inline __attribute__((always_inline)) void block_body(const float* q, const float* kf,
+                                                      const float* vf, int nval, int D,
+                                                      float scale, float* m, float* l,
+                                                      float* acc, float* z, int zs) {
+  for (int t = 0; t < nval; ++t) {
+    const float* kr = kf + (size_t)t * D;
+    v8f s[G];
+    for (int g = 0; g < G; ++g) s[g] = v8f{};
+    for (int c = 0; c < D; c += 8) {
+      const v8f k = load8(kr + c);
+      for (int g = 0; g < G; ++g) s[g] += load8(q + (size_t)g * D + c) * k;
+    }
+    for (int g = 0; g < G; ++g)
+      z[g * zs + t] = (((s[g][0] + s[g][1]) + (s[g][2] + s[g][3])) +
+                       ((s[g][4] + s[g][5]) + (s[g][6] + s[g][7]))) * scale;
+  }
+  float alpha[G];
+  for (int g = 0; g < G; ++g) {
+    float* zg = z + g * zs;
+    float mb = zg[0];
+    for (int t = 1; t < nval; ++t) mb = std::max(mb, zg[t]);
+    const float m_new = std::max(m[g], mb);
+    alpha[g] = std::exp(m[g] - m_new);  // 0 for the first block (m = -inf)
+    float psum = 0.f;
+    for (int t = 0; t < nval; ++t) {
+      zg[t] = std::exp(zg[t] - m_new);
+      psum += zg[t];
+    }
+    l[g] = l[g] * alpha[g] + psum;
+    m[g] = m_new;
+  }
+  for (int c0 = 0; c0 < D; c0 += 16) {
+    v8f o[G][2];
+    for (int g = 0; g < G; ++g) {
+      float* ag = acc + (size_t)g * D + c0;
+      o[g][0] = load8(ag) * alpha[g];
+      o[g][1] = load8(ag + 8) * alpha[g];
+    }
+    for (int t = 0; t < nval; ++t) {
+      const float* vr = vf + (size_t)t * D + c0;
+      const v8f v0 = load8(vr), v1 = load8(vr + 8);
+      for (int g = 0; g < G; ++g) {
+        const float p = z[g * zs + t];
+        o[g][0] += p * v0;
+        o[g][1] += p * v1;
+      }
+    }
+    for (int g = 0; g < G; ++g) {
+      float* ag = acc + (size_t)g * D + c0;
+      store8(ag, o[g][0]);
+      store8(ag + 8, o[g][1]);
+    }
+  }
+}
+
+template <int G>
+__attribute__((target("avx2,fma"))) void block_avx2(const float* q, const float* kf,
+                                                    const float* vf, int nval, int D,
+                                                    float scale, float* m, float* l,
+                                                    float* acc, float* z, int zs) {
+  block_body<G>(q, kf, vf, nval, D, scale, m, l, acc, z, zs);
+}
+
+template <int G>
+void block_base(const float* q, const float* kf, const float* vf, int nval, int D, float scale,
+                float* m, float* l, float* acc, float* z, int zs) {
+  block_body<G>(q, kf, vf, nval, D, scale, m, l, acc, z, zs);
+}
+
+using BlockFn = void (*)(const float*, const float*, const float*, int, int, float, float*,
+                         float*, float*, float*, int);
+
+// the block routine for a group size, the AVX2+FMA build where the CPU has both
+BlockFn pick_block(int G) {
+  static const bool avx2 = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma");
+  switch (G) {
+#define SA_HOST_G(n) \
+  case n:            \
+    return avx2 ? block_avx2<n> : block_base<n>;
+    SA_HOST_G(1) SA_HOST_G(2) SA_HOST_G(3) SA_HOST_G(4)
+    SA_HOST_G(5) SA_HOST_G(6) SA_HOST_G(7) SA_HOST_G(8)
+#undef SA_HOST_G
+  }
+  return nullptr;
 }
 
 template <typename T>
-void attend_pair(const HostAttnArgs& a, int pair, float* kf, float* vf, float* acc) {
+void attend_pair(const HostAttnArgs& a, BlockFn block, int pair, float* kf, float* vf,
+                 float* acc, float* z) {
   const int G = a.G, D = a.d, BS = a.bs;
   const int s = pair / a.Hkv, h = pair % a.Hkv;
   const int len = a.seq_lens[s];
@@ -64,28 +159,14 @@ void attend_pair(const HostAttnArgs& a, int pair, float* kf, float* vf, float* a
     const int page = a.host_table[(size_t)pair * a.max_blocks + b];
     if (page < 0 || page >= a.host_pages) continue;
     const int nval = std::min(BS, len - b * BS);
-    for (int t = 0; t < nval; ++t) {
-      const T* kr = K + ((size_t)page * BS + t) * D;
-      const T* vr = V + ((size_t)page * BS + t) * D;
-      for (int c = 0; c < D; ++c) {
-        kf[c] = to_f32(kr[c]);
-        vf[c] = to_f32(vr[c]);
-      }
-      for (int g = 0; g < G; ++g) {
-        const float z = dot(q + (size_t)g * D, kf, D) * a.scale;
-        float* o = acc + (size_t)g * D;
-        if (z > m[g]) {  // a new maximum: rescale what is accumulated so far
-          const float alpha = std::exp(m[g] - z);  // 0 for the first token (m = -inf)
-          l[g] = l[g] * alpha + 1.f;
-          for (int c = 0; c < D; ++c) o[c] = o[c] * alpha + vf[c];
-          m[g] = z;
-        } else {
-          const float p = std::exp(z - m[g]);
-          l[g] += p;
-          for (int c = 0; c < D; ++c) o[c] += p * vf[c];
-        }
-      }
+    if (nval <= 0) continue;
+    const T* kr = K + (size_t)page * BS * D;
+    const T* vr = V + (size_t)page * BS * D;
+    for (size_t i = 0; i < (size_t)nval * D; ++i) {
+      kf[i] = to_f32(kr[i]);
+      vf[i] = to_f32(vr[i]);
     }
+    block(q, kf, vf, nval, D, a.scale, m, l, acc, z, BS);
   }
   for (int g = 0; g < G; ++g) {
     const size_t row = (size_t)s * a.Hq + (size_t)h * G + g;
@@ -106,11 +187,18 @@ void attend_pair(const HostAttnArgs& a, int pair, float* kf, float* vf, float* a
 template <typename T>
 void run(const HostAttnArgs& a, int threads) {
   const int npairs = a.B * a.Hkv;
+  const BlockFn block = pick_block(a.G);
   std::atomic<int> next{0};
   auto worker = [&]() {
-    std::vector<float> buf((size_t)(2 + a.G) * a.d);
+    // per thread: one block of K and V as float, the G output rows, the G x bs logits
+    const size_t blk = (size_t)a.bs * a.d;
+    std::vector<float> buf(2 * blk + (size_t)a.G * a.d + (size_t)a.G * a.bs);
+    float* kf = buf.data();
+    float* vf = kf + blk;
+    float* acc = vf + blk;
+    float* z = acc + (size_t)a.G * a.d;
     for (int p = next.fetch_add(1); p < npairs; p = next.fetch_add(1))
-      attend_pair<T>(a, p, buf.data(), buf.data() + a.d, buf.data() + 2 * a.d);
+      attend_pair<T>(a, block, p, kf, vf, acc, z);
   };
   threads = std::max(1, std::min(threads, npairs));
   std::vector<std::thread> pool;
