@@ -23,6 +23,8 @@ written out in float64, with no blocking, fusion or reordering beyond it):
     merge of the partials                             [HTML Sec. 3.2; Algorithm 1]
   * the layer-ahead order: layer i predicts and selects for layer i+1, then attends and
     merges layer i                                    [Algorithm 1; HTML Sec. 3.3]
+  * the CPU side's partial over B_cpu, spawned one layer ahead and so computed with the
+    predicted query                                   [Algorithm 1; HTML Sec. 3.3, 4]
 
 Readings taken where the pages are silent (each also listed in the design doc):
   R1 min/max score = sum_c max(q_c*min_c, q_c*max_c), Quest's upper bound on q.k.
@@ -389,7 +391,15 @@ def decode_step_pair(layers, s: int, h: int, group: int, head_dim: int, block_si
       resident  bool [nb]   B_gpu membership of (s, h) at layer i
       K, V   [T][d] logical keys/values of (s, h) at layer i (rows of resident blocks)
       seq_len  int
-      host   list of Partial per query head of the group, merged when S_cpu is not empty
+      host   list of Partial per query head of the group, merged when S_cpu is not empty;
+             or, in place of `host`,
+      K_host, V_host  [T][d] logical keys/values of (s, h) at layer i as the host holds
+             them (rows of the offloaded blocks): the host partial is then computed here,
+             as the CPU side does it, over S_cpu with the query the CPU has when layer i's
+             work is spawned one layer ahead -- Q_pred^i (Q^0 for layer 0)
+             [Algorithm 1: CPUAttn(B_cpu^{i+1}) is spawned while layer i runs, before Q^{i+1}
+             exists; HTML Sec. 3.3 and the accuracy discussion of Sec. 4: the CPU side
+             attends with the predicted query]
     Layer i selects for layer i+1 with Q_pred^{i+1} = W_Q^{i+1} X^i; layer 0 has no
     predecessor and selects with its own Q^0.  Layer i attends with Q^i = W_Q^i X^i.
     Returns a list of PairResult, one per layer.
@@ -417,7 +427,13 @@ def decode_step_pair(layers, s: int, h: int, group: int, head_dim: int, block_si
         for j in range(len(heads)):
             pg = attend_blocks(q_true[j], Li["K"], Li["V"], g_blocks, Li["seq_len"],
                                block_size, scale)
-            ph = Li["host"][j] if len(c_blocks) > 0 else empty_partial(head_dim)
+            if len(c_blocks) == 0:
+                ph = empty_partial(head_dim)
+            elif "K_host" in Li:
+                ph = attend_blocks(q_sel[i][j], Li["K_host"], Li["V_host"], c_blocks,
+                                   Li["seq_len"], block_size, scale)
+            else:
+                ph = Li["host"][j]
             gpu.append(pg)
             hst.append(ph)
             out.append(merge(pg, ph))

@@ -417,4 +417,74 @@ def pin_step_full_budget_is_dense():
                     _close(out[i].out[g].o, ref[g], 1e-12, f"step layer {i}")
 
 
+def pin_step_host_side_uses_predicted_query_hand():
+    """Algorithm 1: the CPU side of layer i is spawned one layer ahead, so it attends the
+    offloaded blocks with Q_pred^i (Q^0 at layer 0), read from the host's copy of the KV.
+    Hand case of pin_layer_ahead_selection_hand with both layers' selections offloaded;
+    the GPU-side rows of offloaded blocks are NaN, so reading them would show."""
+    I = np.eye(2)
+    V = np.array([[5.0, 6.0], [7.0, 8.0]])
+    nan = np.full((2, 2), np.nan)
+    layers = [
+        dict(X=np.array([[1.0, 0.0]]), W=I, digest=np.array([[0.0, 1.0], [1.0, 0.0]]),
+             resident=np.array([True, False]), K=nan, V=nan,
+             K_host=np.array([[0.0, 1.0], [1.0, 0.0]]), V_host=V, seq_len=2),
+        dict(X=np.array([[0.0, 1.0]]), W=I, digest=np.array([[1.0, 0.0], [0.0, 1.0]]),
+             resident=np.array([False, True]), K=nan, V=nan,
+             K_host=np.array([[1.0, 0.0], [0.0, 1.0]]), V_host=V, seq_len=2),
+    ]
+    out = so.decode_step_pair(layers, 0, 0, 1, 2, 1, 1, 1.0)
+    # layer 0 selects block 1 (offloaded) with Q^0 = (1, 0); the CPU attends it with Q^0:
+    # z = (1, 0).(1, 0) = 1, so (o, m, l) = (V_1, 1, 1) and the output is that partial
+    assert out[0].cpu_blocks.tolist() == [1] and out[0].gpu_blocks.tolist() == []
+    assert np.array_equal(out[0].host[0].o, V[1]) and out[0].host[0].m == 1.0
+    assert np.array_equal(out[0].out[0].o, V[1]) and out[0].out[0].m == 1.0
+    # layer 1 selects block 0 with Q_pred^1 = (1, 0); the CPU attends it with Q_pred^1, not
+    # with Q^1 = (0, 1): z = 1 (Q^1 would give z = 0)
+    assert out[1].cpu_blocks.tolist() == [0]
+    assert out[1].host[0].m == 1.0 and out[1].host[0].l == 1.0
+    assert np.array_equal(out[1].out[0].o, V[0]) and out[1].out[0].m == 1.0
+
+
+def pin_step_host_side_merges_to_attention_over_selection():
+    """With Q_pred^i = Q^i (every layer has the same X and W_Q), GPU partial over the
+    resident selected blocks merged with the host's partial over the offloaded ones is
+    plain softmax attention over the tokens of the whole selection (library routine), for
+    any residency; a ragged last block.  Rows the other side holds are NaN on each side."""
+    rng = np.random.default_rng(43)
+    L, hidden, Hq, Hkv, d, T, bs, k = 3, 16, 4, 2, 8, 45, 8, 4
+    G = Hq // Hkv
+    nb = so.num_blocks(T, bs)
+    X = rng.standard_normal((2, hidden))
+    W = rng.standard_normal((Hq * d, hidden)) / 4
+    layers = []
+    for i in range(L):
+        K = rng.standard_normal((T, d)) + rng.standard_normal(d)
+        Vv = rng.standard_normal((T, d))
+        res = rng.random(nb) < 0.5
+        res[i % nb] = not res[i % nb]
+        tok_res = np.repeat(res, bs)[:T]
+        Kg, Vg, Kh, Vh = K.copy(), Vv.copy(), K.copy(), Vv.copy()
+        Kg[~tok_res] = np.nan
+        Vg[~tok_res] = np.nan
+        Kh[tok_res] = np.nan
+        Vh[tok_res] = np.nan
+        layers.append(dict(X=X, W=W, digest=so.digest_mean(K, T, bs, "f32"), resident=res,
+                           K=Kg, V=Vg, K_host=Kh, V_host=Vh, seq_len=T, Kfull=K, Vfull=Vv))
+    scale = 1 / math.sqrt(d)
+    for s in range(2):
+        Q = (X[s] @ W.T).reshape(Hq, d)
+        for h in range(Hkv):
+            out = so.decode_step_pair(layers, s, h, G, d, bs, k, scale)
+            for i in range(L):
+                r = out[i]
+                assert len(r.cpu_blocks) + len(r.gpu_blocks) == k
+                rows = np.concatenate([np.arange(b * bs, min((b + 1) * bs, T))
+                                       for b in r.selected])
+                Ks, Vs = layers[i]["Kfull"][rows], layers[i]["Vfull"][rows]
+                ref = _dense_ref_heads(Q[h * G:(h + 1) * G], Ks, Vs, len(rows), scale)
+                for g in range(G):
+                    _close(r.out[g].o, ref[g], 1e-12, f"host-side step layer {i}")
+
+
 ALL_PINS = [v for k, v in dict(globals()).items() if k.startswith("pin_") and callable(v)]

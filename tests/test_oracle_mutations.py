@@ -137,6 +137,29 @@ def _step_always_merges_host(layers, s, h, group, head_dim, *a, **k):
     return res
 
 
+def _step_host_with_true_query(layers, s, h, group, head_dim, block_size, top_k, scale,
+                               kind="mean"):
+    """The CPU side attends with the layer's own Q^i instead of the query it has when its
+    work is spawned (Q_pred^i)."""
+    first = _orig["decode_step_pair"](layers, s, h, group, head_dim, block_size, top_k, scale,
+                                      kind)
+    heads = list(so.gqa_group(h, group))
+    fixed = []
+    for i, L in enumerate(layers):
+        if "K_host" not in L:
+            fixed.append(L)
+            continue
+        Q = np.asarray(L["X"][s], dtype=np.float64) @ np.asarray(L["W"], dtype=np.float64).T
+        Q = Q.reshape(-1, head_dim)
+        host = [so.attend_blocks(Q[g], L["K_host"], L["V_host"], first[i].cpu_blocks,
+                                 L["seq_len"], block_size, scale) for g in heads]
+        M = {key: v for key, v in L.items() if key not in ("K_host", "V_host")}
+        M["host"] = host
+        fixed.append(M)
+    return _orig["decode_step_pair"](fixed, s, h, group, head_dim, block_size, top_k, scale,
+                                     kind)
+
+
 def _gqa_shifted(h, group):
     return range(h * group + 1, (h + 1) * group + 1)
 
@@ -164,6 +187,7 @@ MUTATIONS = {
     "layer selects with its own query": ("decode_step_pair", _step_selects_with_own_query),
     "host partial merged when nothing offloaded": ("decode_step_pair", _step_always_merges_host),
     "GQA group off by one head": ("gqa_group", _gqa_shifted),
+    "host side attends with the true query": ("decode_step_pair", _step_host_with_true_query),
 }
 
 
