@@ -14,9 +14,12 @@ Prints one JSON line: seq-layers/s (= batch * layers / step time) over K replays
 step captured as a HIP graph; the attention kernel's achieved HBM bandwidth against the
 8 TB/s peak, from HIP events recorded at each attention launch's own start and end, both
 inside eager steps (sharing the GPU with the side stream) and launched alone; and the CPU
-oracle timed on a bounded sample of the same workload.
+oracle timed on a bounded sample of the same workload.  In the timed step the host partials
+are given (seeded); with --offload the line also carries "offload": the same step with
+its CPU side computed by host threads one layer ahead (sa_decode_step_offload) from an
+aliased host KV store, and the share of that step the GPU spends waiting for it.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-graph]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-graph] [--offload]
 """
 
 from __future__ import annotations
@@ -52,6 +55,14 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--offload", action="store_true",
+                    help="after the GPU path, also time the step with its CPU side computed "
+                         "by host tasks (sa_decode_step_offload), reported as \"offload\"")
+    ap.add_argument("--offload-steps", type=int, default=5)
+    ap.add_argument("--host-threads", type=int, default=16,
+                    help="host worker threads of the offload step (at most the CPUs present)")
+    ap.add_argument("--host-pages", type=int, default=32768,
+                    help="pages of the aliased host KV store of the offload step")
     return ap.parse_args()
 
 
@@ -211,6 +222,83 @@ def cpu_baseline(wl_full, budget_s):
 
 
 # ---------------------------------------------------------------------------------------
+
+def offload_measure(wl, dims, lens, layers, ws, side_stream, ms_gpu, args, torch, B, wk):
+    """The same step with its CPU side computed, not given: sa_decode_step_offload runs each
+    layer's host partial on host threads one layer ahead (Algorithm 1) and makes the merge
+    wait for it.  The host KV is an aliased store (draw_host_store_aliased): the 64K-token
+    offloaded KV of 40 layers would not fit in host memory, so every block maps into one
+    pool of host pages.  Not the headline figure: the GPU path is."""
+    Bsz, Hq, Hkv, d, k = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.top_k
+    pairs = Bsz * Hkv
+    f32 = torch.float32
+    threads = max(1, min(args.host_threads, os.cpu_count() or 1))
+    t0 = time.time()
+    store = wk.draw_host_store_aliased(wl, args.host_pages)
+    hls = [dict(k_host=store["K"], v_host=store["V"], host_table=store["table"],
+                q_host=B.pinned_empty((Bsz, Hq, d), f32),
+                cpu_blocks_host=B.pinned_empty((pairs, k)), n_cpu_host=B.pinned_empty((pairs,)),
+                o_host=B.pinned_empty((Bsz, Hq, d), f32), m_host=B.pinned_empty((Bsz, Hq), f32),
+                l_host=B.pinned_empty((Bsz, Hq), f32)) for _ in range(wl.layers)]
+    plan = B.HostPlan(dims, k, wl.scale, lens.cpu().contiguous(), hls, threads=threads)
+    host_stream = torch.cuda.Stream()
+    log(f"offload: host store of {args.host_pages} pages ready ({time.time() - t0:.1f} s), "
+        f"{threads} host threads")
+
+    def step():
+        B.sa_decode_step_offload(dims, "mean", wl.hidden, k, wl.scale, lens, layers, ws, plan,
+                                 host_stream, side_stream=side_stream)
+
+    def timed(run, n):
+        torch.cuda.synchronize()
+        n0, b0 = plan.stats()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        n1, b1 = plan.stats()
+        return e0.elapsed_time(e1) / n, (b1 - b0) / max(1, n1 - n0) * 1e3
+
+    out = {}
+    try:
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        ms_eager, host_ms = timed(step, args.offload_steps)
+        log(f"offload step (eager): {ms_eager:.2f} ms/step, host {host_ms:.3f} ms per layer")
+        out = {"ms_per_step_eager": round(ms_eager, 3)}
+        ms_off, mode = ms_eager, "eager"
+        graph = None
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            torch.cuda.synchronize()
+            ms_graph, host_ms = timed(graph.replay, args.offload_steps)
+            log(f"offload step (hip-graph): {ms_graph:.2f} ms/step")
+            out["ms_per_step_graph"] = round(ms_graph, 3)
+            if ms_graph < ms_off:
+                ms_off, mode = ms_graph, "hip-graph"
+        except Exception as e:  # noqa: BLE001
+            log(f"offload step: graph capture unavailable ({e})")
+        torch.cuda.synchronize()
+        del graph
+        out.update({
+            "ms_per_step": round(ms_off, 3), "launch": mode,
+            "seq_layers_per_s": round(wl.batch * wl.layers / (ms_off * 1e-3), 1),
+            "gpu_only_ms_per_step": round(ms_gpu, 4),
+            "gpu_wait_frac": round(max(0.0, 1.0 - ms_gpu / ms_off), 4),
+            "host_ms_per_layer": round(host_ms, 3), "host_threads": threads,
+            "host_store": f"aliased pool of {args.host_pages} pages ({wl.kv_dtype})",
+            "note": "gpu_wait_frac = 1 - (step time without the CPU side) / (step time with "
+                    "it): the share of the step the GPU spends waiting for host partials"})
+    finally:
+        torch.cuda.synchronize()
+        plan.close()
+    return out
+
 
 def main():
     args = parse()
@@ -381,6 +469,9 @@ def main():
                               "avg_launch_us": round(iso_avg_ms * 1e3, 2),
                               "algorithmic_bytes_per_launch": int(iso_bytes_avg)},
     }
+    if args.offload:
+        result["offload"] = offload_measure(wl, dims, lens, layers, ws, side_stream, ms_step,
+                                            args, torch, B, wk)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

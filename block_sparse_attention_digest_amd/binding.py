@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libscoutattn.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = 0, -1, -2, -3, -4
 SA_F32, SA_BF16 = 0, 1
 SA_DIGEST_MEAN, SA_DIGEST_MINMAX = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 KIND = {"mean": SA_DIGEST_MEAN, "minmax": SA_DIGEST_MINMAX}
 
@@ -44,6 +44,13 @@ class sa_layer(ctypes.Structure):
         "x", "w_q", "digests", "block_table", "k_pool", "v_pool", "host_o", "host_m", "host_l",
         "gpu_blocks", "n_gpu", "cpu_blocks", "n_cpu", "cpu_blocks_host", "n_cpu_host",
         "out_o", "out_m", "out_l")]
+
+
+class sa_host_layer(ctypes.Structure):
+    _fields_ = [("k_host", ctypes.c_void_p), ("v_host", ctypes.c_void_p),
+                ("host_table", ctypes.c_void_p), ("host_pages", ctypes.c_int32)] + [
+        (n, ctypes.c_void_p) for n in ("q_host", "cpu_blocks_host", "n_cpu_host", "o_host",
+                                       "m_host", "l_host")]
 
 
 _P = ctypes.c_void_p
@@ -75,6 +82,13 @@ SIGNATURES = {
     "sa_decode_step": (ctypes.c_int, [_D, ctypes.c_int, _I, _I, _F, _P, _I,
                                       ctypes.POINTER(sa_layer), _P, _Z, _P, _P]),
     "sa_profile_attention": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.POINTER(_P), _I]),
+    "sa_host_plan_create": (ctypes.c_int, [_D, _I, _F, _P, _I, ctypes.POINTER(sa_host_layer), _I,
+                                           ctypes.POINTER(_P)]),
+    "sa_host_plan_destroy": (ctypes.c_int, [_P]),
+    "sa_host_plan_stats": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_double)]),
+    "sa_decode_step_offload": (ctypes.c_int, [_D, ctypes.c_int, _I, _I, _F, _P, _I,
+                                              ctypes.POINTER(sa_layer), _P, _Z, _P, _P, _P, _P]),
     "sa_host_partial_attention": (ctypes.c_int, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _I, _F,
                                                  _P, _P, _P, _I]),
 }
@@ -382,6 +396,77 @@ def sa_decode_step(dims: Dims, kind: str, hidden: int, top_k: int, scale: float,
         _ptr(seq_lens, torch.int32, dims.batch, "seq_lens"), len(layers), arr,
         _ptr(ws, torch.uint8, name="ws"), ws.numel(), _stream(stream),
         None if side_stream is None else _stream(side_stream)))
+
+
+class HostPlan:
+    """The host side of sa_decode_step_offload (sa_host_plan_create): per layer a dict with
+    k_host, v_host [pages][bs][d] and host_table [B][Hkv][max_blocks] (CPU tensors), and the
+    pinned buffers (pinned_empty) q_host [B][Hq][d], cpu_blocks_host [B][Hkv][top_k],
+    n_cpu_host [B][Hkv], o_host [B][Hq][d], m_host, l_host [B][Hq].  Keeps the tensors alive;
+    close() stops the workers (not while enqueued work or a captured graph may still use
+    the plan)."""
+
+    def __init__(self, dims: Dims, top_k: int, scale: float, seq_lens_host, layers: list,
+                 threads: int = 0):
+        i32, f32 = torch.int32, torch.float32
+        B, Hq, Hkv, d = dims.batch, dims.num_q_heads, dims.num_kv_heads, dims.head_dim
+        per_page = dims.block_size * d
+        arr = (sa_host_layer * len(layers))()
+        for i, L in enumerate(layers):
+            pages = L["k_host"].shape[0]
+            if L["v_host"].shape[0] != pages:
+                raise ValueError(f"layers[{i}]: k_host and v_host differ in pages")
+            a = arr[i]
+            a.k_host = _ptr(L["k_host"], dims.kv_torch, pages * per_page, f"[{i}].k_host", False)
+            a.v_host = _ptr(L["v_host"], dims.kv_torch, pages * per_page, f"[{i}].v_host", False)
+            a.host_table = _ptr(L["host_table"], i32, B * Hkv * dims.max_blocks,
+                                f"[{i}].host_table", False)
+            a.host_pages = pages
+            a.q_host = _ptr(L["q_host"], f32, B * Hq * d, f"[{i}].q_host", False)
+            a.cpu_blocks_host = _ptr(L["cpu_blocks_host"], i32, B * Hkv * top_k,
+                                     f"[{i}].cpu_blocks_host", False)
+            a.n_cpu_host = _ptr(L["n_cpu_host"], i32, B * Hkv, f"[{i}].n_cpu_host", False)
+            a.o_host = _ptr(L["o_host"], f32, B * Hq * d, f"[{i}].o_host", False)
+            a.m_host = _ptr(L["m_host"], f32, B * Hq, f"[{i}].m_host", False)
+            a.l_host = _ptr(L["l_host"], f32, B * Hq, f"[{i}].l_host", False)
+        self.layers = layers
+        self.seq_lens = seq_lens_host
+        self.handle = _P()
+        _check(lib().sa_host_plan_create(
+            ctypes.byref(dims.c()), top_k, scale,
+            _ptr(seq_lens_host, i32, B, "seq_lens_host", device=False), len(layers), arr,
+            threads, ctypes.byref(self.handle)))
+
+    def stats(self):
+        """(host tasks run, seconds they took)."""
+        n = ctypes.c_int64()
+        t = ctypes.c_double()
+        _check(lib().sa_host_plan_stats(self.handle, ctypes.byref(n), ctypes.byref(t)))
+        return n.value, t.value
+
+    def close(self):
+        if self.handle:
+            _check(lib().sa_host_plan_destroy(self.handle))
+            self.handle = _P()
+
+
+def sa_decode_step_offload(dims: Dims, kind: str, hidden: int, top_k: int, scale: float,
+                           seq_lens, layers: list, ws, plan: HostPlan, host_stream,
+                           stream=None, side_stream=None):
+    """sa_decode_step with the CPU side computed by `plan` on `host_stream` (a stream of its
+    own); host_o/m/l and the host mirrors of `layers` are not used."""
+    arr = (sa_layer * len(layers))()
+    for i, L in enumerate(layers):
+        for name, _ in sa_layer._fields_:
+            if name.endswith("_host") or name in ("host_o", "host_m", "host_l"):
+                continue
+            setattr(arr[i], name, _ptr(L.get(name), name=f"layers[{i}].{name}"))
+    _check(lib().sa_decode_step_offload(
+        ctypes.byref(dims.c()), KIND[kind], hidden, top_k, scale,
+        _ptr(seq_lens, torch.int32, dims.batch, "seq_lens"), len(layers), arr,
+        _ptr(ws, torch.uint8, name="ws"), ws.numel(), _stream(stream),
+        None if side_stream is None else _stream(side_stream), plan.handle,
+        _stream(host_stream)))
 
 
 def sa_profile_attention(starts, stops):

@@ -3,9 +3,13 @@
 // Algorithm 1].  Every argument is checked here, on the host, before anything is launched.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <memory>
 #include <string>
 #include <vector>
 
@@ -417,6 +421,36 @@ sa_status sa_merge(int32_t rows, int32_t d, const float* o_a, const float* m_a,
 
 // ---- the host side: partial attention over the offloaded blocks ------------------------------
 
+static sa::HostAttnArgs host_args(const sa::Shape& s, int host_pages, int list_stride,
+                                  float scale, const float* q, const void* k_host,
+                                  const void* v_host, const int32_t* host_table,
+                                  const int32_t* seq_lens, const int32_t* cpu_blocks,
+                                  const int32_t* n_cpu, float* o, float* m, float* l) {
+  sa::HostAttnArgs a;
+  a.B = s.B;
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.G = s.G;
+  a.d = s.d;
+  a.bs = s.bs;
+  a.max_blocks = s.max_blocks;
+  a.host_pages = host_pages;
+  a.list_stride = list_stride;
+  a.bf16 = s.bf16;
+  a.scale = scale;
+  a.q = q;
+  a.k_host = k_host;
+  a.v_host = v_host;
+  a.host_table = host_table;
+  a.seq_lens = seq_lens;
+  a.cpu_blocks = cpu_blocks;
+  a.n_cpu = n_cpu;
+  a.o = o;
+  a.m = m;
+  a.l = l;
+  return a;
+}
+
 sa_status sa_host_partial_attention(const sa_dims* dims, int32_t host_pages,
                                     const float* q_host, const void* k_host,
                                     const void* v_host, const int32_t* host_table,
@@ -442,33 +476,109 @@ sa_status sa_host_partial_attention(const sa_dims* dims, int32_t host_pages,
   SA_NOT_NULL(o_host);
   SA_NOT_NULL(m_host);
   SA_NOT_NULL(l_host);
-  sa::HostAttnArgs a;
-  a.B = s.B;
-  a.Hq = s.Hq;
-  a.Hkv = s.Hkv;
-  a.G = s.G;
-  a.d = s.d;
-  a.bs = s.bs;
-  a.max_blocks = s.max_blocks;
-  a.host_pages = host_pages;
-  a.list_stride = list_stride;
-  a.bf16 = s.bf16;
-  a.scale = scale;
-  a.q = q_host;
-  a.k_host = k_host;
-  a.v_host = v_host;
-  a.host_table = host_table;
-  a.seq_lens = seq_lens_host;
-  a.cpu_blocks = cpu_blocks_host;
-  a.n_cpu = n_cpu_host;
-  a.o = o_host;
-  a.m = m_host;
-  a.l = l_host;
+  const sa::HostAttnArgs a =
+      host_args(s, host_pages, list_stride, scale, q_host, k_host, v_host, host_table,
+                seq_lens_host, cpu_blocks_host, n_cpu_host, o_host, m_host, l_host);
   try {
     sa::host_partial_attention(a, sa::host_threads(num_threads));
   } catch (const std::exception& e) {  // (thread creation; no exception crosses the ABI)
     return fail(SA_ERR_INVALID_ARG, "host worker failed: %s", e.what());
   }
+  return ok();
+}
+
+// ---- the host plan: the CPU side of the step, as HIP host tasks ------------------------------
+
+struct sa_host_plan {
+  struct Task {
+    sa_host_plan* plan;
+    int layer;
+  };
+  sa::Shape s;
+  int top_k = 0;
+  float scale = 0.f;
+  const int32_t* seq_lens = nullptr;
+  std::vector<sa_host_layer> layers;
+  std::vector<Task> tasks;  // the host functions' arguments (stable addresses)
+  std::unique_ptr<sa::HostPool> pool;
+  std::atomic<int64_t> runs{0}, busy_ns{0};
+  std::atomic<bool> failed{false};
+};
+
+// A HIP host function (it runs on the runtime's callback thread and holds its stream until
+// it returns; it makes no HIP call): A_cpu of one layer on the plan's workers.
+static void run_host_task(void* arg) {
+  const auto* t = static_cast<const sa_host_plan::Task*>(arg);
+  sa_host_plan& P = *t->plan;
+  const sa_host_layer& H = P.layers[t->layer];
+  const auto t0 = std::chrono::steady_clock::now();
+  const sa::HostAttnArgs a =
+      host_args(P.s, H.host_pages, P.top_k, P.scale, H.q_host, H.k_host, H.v_host,
+                H.host_table, P.seq_lens, H.cpu_blocks_host, H.n_cpu_host, H.o_host, H.m_host,
+                H.l_host);
+  if (!P.pool->run(a)) {  // no worker could run: leave the empty partial, report it later
+    P.failed = true;
+    const size_t rows = (size_t)P.s.B * P.s.Hq;
+    std::fill(H.o_host, H.o_host + rows * P.s.d, 0.f);
+    std::fill(H.m_host, H.m_host + rows, -INFINITY);
+    std::fill(H.l_host, H.l_host + rows, 0.f);
+  }
+  const auto dt = std::chrono::steady_clock::now() - t0;
+  P.busy_ns += std::chrono::duration_cast<std::chrono::nanoseconds>(dt).count();
+  ++P.runs;
+}
+
+sa_status sa_host_plan_create(const sa_dims* dims, int32_t top_k, float scale,
+                              const int32_t* seq_lens_host, int32_t num_layers,
+                              const sa_host_layer* layers, int32_t num_threads,
+                              sa_host_plan** plan) {
+  SA_NOT_NULL(plan);
+  *plan = nullptr;
+  sa::Shape s;
+  SA_CHECK(check_dims(dims, &s));
+  SA_CHECK(check_scale(scale));
+  if (top_k < 1 || top_k > s.max_blocks)
+    return fail(SA_ERR_INVALID_ARG, "top_k %d outside [1, max_blocks = %d]", top_k, s.max_blocks);
+  SA_NOT_NULL(seq_lens_host);
+  SA_NOT_NULL(layers);
+  if (num_layers < 1) return fail(SA_ERR_INVALID_ARG, "num_layers %d < 1", num_layers);
+  if (num_threads < 0) return fail(SA_ERR_INVALID_ARG, "num_threads %d < 0", num_threads);
+  for (int i = 0; i < num_layers; ++i) {
+    const sa_host_layer& H = layers[i];
+    if (!H.k_host || !H.v_host || !H.host_table || !H.q_host || !H.cpu_blocks_host ||
+        !H.n_cpu_host || !H.o_host || !H.m_host || !H.l_host)
+      return fail(SA_ERR_INVALID_ARG, "host layer %d: a pointer is NULL", i);
+    if (H.host_pages < 1)
+      return fail(SA_ERR_INVALID_ARG, "host layer %d: host_pages %d < 1", i, H.host_pages);
+  }
+  try {
+    auto P = std::make_unique<sa_host_plan>();
+    P->s = s;
+    P->top_k = top_k;
+    P->scale = scale;
+    P->seq_lens = seq_lens_host;
+    P->layers.assign(layers, layers + num_layers);
+    P->tasks.resize(num_layers);
+    for (int i = 0; i < num_layers; ++i) P->tasks[i] = {P.get(), i};
+    P->pool = std::make_unique<sa::HostPool>(sa::host_threads(num_threads));
+    *plan = P.release();
+  } catch (const std::exception& e) {  // allocation or thread creation
+    return fail(SA_ERR_INVALID_ARG, "host plan: %s", e.what());
+  }
+  return ok();
+}
+
+sa_status sa_host_plan_destroy(sa_host_plan* plan) {
+  delete plan;  // joins the workers
+  return ok();
+}
+
+sa_status sa_host_plan_stats(const sa_host_plan* plan, int64_t* tasks, double* busy_seconds) {
+  SA_NOT_NULL(plan);
+  if (tasks) *tasks = plan->runs.load();
+  if (busy_seconds) *busy_seconds = 1e-9 * (double)plan->busy_ns.load();
+  if (plan->failed.load())
+    return fail(SA_ERR_HIP, "a host task could not run (out of memory); its partial is empty");
   return ok();
 }
 
@@ -516,10 +626,13 @@ size_t sa_step_workspace_bytes(const sa_dims* dims, int32_t hidden, int32_t top_
   return step_layout(s, hidden, top_k).total;
 }
 
-sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidden,
-                         int32_t top_k, float scale, const int32_t* seq_lens,
-                         int32_t num_layers, const sa_layer* layers, void* ws,
-                         size_t ws_bytes, hipStream_t stream, hipStream_t side_stream) {
+// The step, with its CPU side given (plan NULL: each layer's host_o/m/l) or computed by the
+// plan's host tasks on host_stream.
+static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hidden,
+                           int32_t top_k, float scale, const int32_t* seq_lens,
+                           int32_t num_layers, const sa_layer* layers, void* ws,
+                           size_t ws_bytes, hipStream_t stream, hipStream_t side_stream,
+                           sa_host_plan* plan, hipStream_t host_stream) {
   sa::Shape s;
   SA_CHECK(check_dims(dims, &s));
   SA_CHECK(check_kind(kind));
@@ -533,14 +646,28 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
   for (int i = 0; i < num_layers; ++i) {
     const sa_layer& L = layers[i];
     if (!L.x || !L.w_q || !L.digests || !L.block_table || !L.k_pool || !L.v_pool ||
-        !L.host_o || !L.host_m || !L.host_l || !L.gpu_blocks || !L.n_gpu || !L.cpu_blocks ||
-        !L.n_cpu || !L.out_o)
+        !L.gpu_blocks || !L.n_gpu || !L.cpu_blocks || !L.n_cpu || !L.out_o)
       return fail(SA_ERR_INVALID_ARG, "layer %d: a required pointer is NULL", i);
+    if (plan) continue;  // the plan's host buffers take the place of the rest
+    if (!L.host_o || !L.host_m || !L.host_l)
+      return fail(SA_ERR_INVALID_ARG, "layer %d: a host partial pointer is NULL", i);
     if ((L.cpu_blocks_host == nullptr) != (L.n_cpu_host == nullptr))
       return fail(SA_ERR_INVALID_ARG,
                   "layer %d: cpu_blocks_host and n_cpu_host must both be set or both NULL", i);
   }
   if (side_stream == stream) side_stream = nullptr;
+  if (plan) {
+    const sa::Shape& p = plan->s;
+    if (p.B != s.B || p.Hq != s.Hq || p.Hkv != s.Hkv || p.d != s.d || p.bs != s.bs ||
+        p.max_blocks != s.max_blocks || p.bf16 != s.bf16)
+      return fail(SA_ERR_INVALID_ARG, "the host plan was made for other dims");
+    if (plan->top_k != top_k || plan->scale != scale ||
+        (int)plan->layers.size() != num_layers)
+      return fail(SA_ERR_INVALID_ARG,
+                  "the host plan was made for another top_k, scale or number of layers");
+    if (!host_stream || host_stream == stream || host_stream == side_stream)
+      return fail(SA_ERR_INVALID_ARG, "host_stream must be a stream of its own");
+  }
   const StepLayout SL = step_layout(s, hidden, top_k);
   if (!ws || ws_bytes < SL.total)
     return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, SL.total);
@@ -575,6 +702,23 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
     SA_HIP(hipStreamWaitEvent(to, ev, 0), "hipStreamWaitEvent");
     return SA_OK;
   };
+  // the CPU side of layer j, once its lists are selected on `from`: the query it attends
+  // with goes to the plan's host buffer, then a host task on host_stream computes A_cpu^j
+  std::vector<hipEvent_t> host_done(plan ? num_layers : 0, nullptr);
+  auto spawn_host = [&](int j, const sa::QParts& q, hipStream_t from) -> sa_status {
+    const sa_host_layer& H = plan->layers[j];
+    SA_HIP(sa::launch_gather_query(q, s.B, n, H.q_host, from), "query gather kernel");
+    SA_CHECK(order(from, host_stream));
+    SA_HIP(hipLaunchHostFunc(host_stream, run_host_task, &plan->tasks[j]), "hipLaunchHostFunc");
+    SA_CHECK(new_event(&host_done[j]));
+    SA_HIP(hipEventRecord(host_done[j], host_stream), "hipEventRecord");
+    return SA_OK;
+  };
+  // where the selection of layer j hands its offloaded lists over
+  auto mirror_blocks = [&](int j) {
+    return plan ? plan->layers[j].cpu_blocks_host : layers[j].cpu_blocks_host;
+  };
+  auto mirror_n = [&](int j) { return plan ? plan->layers[j].n_cpu_host : layers[j].n_cpu_host; };
   sa_status st = SA_OK;
   hipEvent_t sel_done = nullptr;  // side stream: the selection of the coming layer is done
   for (int i = 0; i < num_layers && st == SA_OK; ++i) {
@@ -609,8 +753,9 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
     //    the selection kernels also write the offloaded lists into the host mirrors
     if (i == 0) {
       st = run_select(s, minmax, q_cur, L.digests, seq_lens, top_k, L.block_table,
-                      L.gpu_blocks, L.n_gpu, L.cpu_blocks, L.n_cpu, nullptr, L.cpu_blocks_host,
-                      L.n_cpu_host, pages[0], stream);
+                      L.gpu_blocks, L.n_gpu, L.cpu_blocks, L.n_cpu, nullptr, mirror_blocks(0),
+                      mirror_n(0), pages[0], stream);
+      if (st == SA_OK && plan) st = spawn_host(0, q_cur, stream);
       if (st == SA_OK && side_stream) st = order(stream, side_stream);
       if (st != SA_OK) break;
     }
@@ -628,7 +773,8 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
       if (st == SA_OK)
         st = run_select(s, minmax, q_next, N.digests, seq_lens, top_k, N.block_table,
                         N.gpu_blocks, N.n_gpu, N.cpu_blocks, N.n_cpu, nullptr,
-                        N.cpu_blocks_host, N.n_cpu_host, pages[(i + 1) & 1], sel_stream);
+                        mirror_blocks(i + 1), mirror_n(i + 1), pages[(i + 1) & 1], sel_stream);
+      if (st == SA_OK && plan) st = spawn_host(i + 1, q_next, sel_stream);
       if (st != SA_OK) break;
     }
     // 4. layer i's lists were selected on the side stream one layer earlier
@@ -649,16 +795,50 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
                              seq_lens, L.gpu_blocks, pages[i & 1], L.n_gpu, top_k, scale,
                              parts, stream, e0, e1);
     if (e != hipSuccess) { st = hip_fail(e, "attention kernel"); break; }
-    e = sa::launch_reduce(s, SL.sel_layout.plan, L.n_gpu, parts, L.host_o, L.host_m, L.host_l,
-                          L.n_cpu, L.out_o, L.out_m, L.out_l, stream);
+    const float* ho = L.host_o;
+    const float* hm = L.host_m;
+    const float* hl = L.host_l;
+    if (plan) {  // layer i's CPU side, spawned one layer earlier (layer 0: just now)
+      if (hipStreamWaitEvent(stream, host_done[i], 0) != hipSuccess) {
+        st = fail(SA_ERR_HIP, "hipStreamWaitEvent failed");
+        break;
+      }
+      ho = plan->layers[i].o_host;
+      hm = plan->layers[i].m_host;
+      hl = plan->layers[i].l_host;
+    }
+    e = sa::launch_reduce(s, SL.sel_layout.plan, L.n_gpu, parts, ho, hm, hl, L.n_cpu, L.out_o,
+                          L.out_m, L.out_l, stream);
     if (e != hipSuccess) { st = hip_fail(e, "reduce kernel"); break; }
   }
-  // join the side stream back into `stream`
+  // join the side stream and the host tasks back into `stream`
   if (side_stream) {
     sa_status j = order(side_stream, stream);
     if (st == SA_OK) st = j;
   }
+  if (plan) {
+    sa_status j = order(host_stream, stream);
+    if (st == SA_OK) st = j;
+  }
   return st == SA_OK ? ok() : st;
+}
+
+sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidden,
+                         int32_t top_k, float scale, const int32_t* seq_lens,
+                         int32_t num_layers, const sa_layer* layers, void* ws,
+                         size_t ws_bytes, hipStream_t stream, hipStream_t side_stream) {
+  return step_impl(dims, kind, hidden, top_k, scale, seq_lens, num_layers, layers, ws, ws_bytes,
+                   stream, side_stream, nullptr, nullptr);
+}
+
+sa_status sa_decode_step_offload(const sa_dims* dims, sa_digest_kind kind, int32_t hidden,
+                                 int32_t top_k, float scale, const int32_t* seq_lens,
+                                 int32_t num_layers, const sa_layer* layers, void* ws,
+                                 size_t ws_bytes, hipStream_t stream, hipStream_t side_stream,
+                                 sa_host_plan* plan, hipStream_t host_stream) {
+  SA_NOT_NULL(plan);
+  return step_impl(dims, kind, hidden, top_k, scale, seq_lens, num_layers, layers, ws, ws_bytes,
+                   stream, side_stream, plan, host_stream);
 }
 
 }  // extern "C"

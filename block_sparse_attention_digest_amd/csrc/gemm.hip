@@ -276,6 +276,32 @@ hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void
   return hipGetLastError();
 }
 
+// One float4 of one row per thread: the k-slice partials summed in slice order.  `out` may be
+// page-locked host memory the device addresses (the query handed to the CPU side).
+__global__ __launch_bounds__(256) void gather_query_kernel(QParts q, int rows, int n,
+                                                           float* __restrict__ out) {
+  const long i4 = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int n4 = n / 4;
+  if (i4 >= (long)rows * n4) return;
+  const int row = (int)(i4 / n4);
+  const int col = (int)(i4 % n4) * 4;
+  const float* src = q.base + (size_t)row * q.row_stride + col;
+  float4 s = *reinterpret_cast<const float4*>(src);
+  for (int p = 1; p < q.parts; ++p) {
+    const float4 v = *reinterpret_cast<const float4*>(src + (size_t)p * q.part_stride);
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  *reinterpret_cast<float4*>(out + (size_t)row * n + col) = s;
+}
+
+hipError_t launch_gather_query(const QParts& q, int rows, int n, float* out, hipStream_t stream) {
+  const long total4 = (long)rows * (n / 4);
+  if (total4 == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_query_kernel, dim3((unsigned)((total4 + 255) / 256)), dim3(256), 0,
+                     stream, q, rows, n, out);
+  return hipGetLastError();
+}
+
 QParts gemm_result(const GemmPlan& plan, int m, int n, int nprob, int prob, const float* q,
                    const float* ws) {
   if (plan.ksplit == 1) return plain_query(q, n);  // written straight to q

@@ -1,8 +1,13 @@
 // Host-side (CPU) part of the library: the partial attention over offloaded blocks.
 #pragma once
 
+#include <atomic>
+#include <condition_variable>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
+#include <thread>
+#include <vector>
 
 namespace sa {
 
@@ -25,7 +30,34 @@ struct HostAttnArgs {
 
 // worker threads for a request (<= 0: the machine's hardware threads)
 int host_threads(int requested);
-// computes every (sequence, query head) partial; blocks until done
+// computes every (sequence, query head) partial; blocks until done; throws if no thread could
+// run
 void host_partial_attention(const HostAttnArgs& args, int threads);
+
+// A fixed set of worker threads for repeated host partials (one per decode layer): threads-1
+// workers wait between jobs, and the thread that calls run() works beside them.  run() is not
+// reentrant: one job at a time.
+class HostPool {
+ public:
+  explicit HostPool(int threads);
+  ~HostPool();
+  HostPool(const HostPool&) = delete;
+  HostPool& operator=(const HostPool&) = delete;
+  // computes every (sequence, query head) partial of `args`; blocks until done; false if no
+  // thread could run (out of memory)
+  bool run(const HostAttnArgs& args);
+  int threads() const { return (int)workers_.size() + 1; }
+
+ private:
+  void loop();
+  std::mutex mu_;
+  std::condition_variable start_, done_;
+  const HostAttnArgs* job_ = nullptr;
+  uint64_t gen_ = 0;
+  int busy_ = 0;
+  bool stop_ = false;
+  std::atomic<int> next_{0};
+  std::vector<std::thread> workers_;
+};
 
 }  // namespace sa

@@ -15,7 +15,10 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <condition_variable>
 #include <cstring>
+#include <mutex>
+#include <stdexcept>
 #include <thread>
 #include <vector>
 
@@ -184,28 +187,34 @@ void attend_pair(const HostAttnArgs& a, BlockFn block, int pair, float* kf, floa
   }
 }
 
+// Takes pairs from `next` until none is left, with this thread's own block buffers: one
+// block of K and V as float, the G output rows, the G x bs logits.
 template <typename T>
-void run(const HostAttnArgs& a, int threads) {
-  const int npairs = a.B * a.Hkv;
+void work(const HostAttnArgs& a, std::atomic<int>& next) {
   const BlockFn block = pick_block(a.G);
-  std::atomic<int> next{0};
-  auto worker = [&]() {
-    // per thread: one block of K and V as float, the G output rows, the G x bs logits
-    const size_t blk = (size_t)a.bs * a.d;
-    std::vector<float> buf(2 * blk + (size_t)a.G * a.d + (size_t)a.G * a.bs);
-    float* kf = buf.data();
-    float* vf = kf + blk;
-    float* acc = vf + blk;
-    float* z = acc + (size_t)a.G * a.d;
-    for (int p = next.fetch_add(1); p < npairs; p = next.fetch_add(1))
-      attend_pair<T>(a, block, p, kf, vf, acc, z);
-  };
-  threads = std::max(1, std::min(threads, npairs));
-  std::vector<std::thread> pool;
-  pool.reserve(threads - 1);
-  for (int t = 1; t < threads; ++t) pool.emplace_back(worker);
-  worker();  // the calling thread works too
-  for (auto& th : pool) th.join();
+  const int npairs = a.B * a.Hkv;
+  const size_t blk = (size_t)a.bs * a.d;
+  std::vector<float> buf(2 * blk + (size_t)a.G * a.d + (size_t)a.G * a.bs);
+  float* kf = buf.data();
+  float* vf = kf + blk;
+  float* acc = vf + blk;
+  float* z = acc + (size_t)a.G * a.d;
+  for (int p = next.fetch_add(1); p < npairs; p = next.fetch_add(1))
+    attend_pair<T>(a, block, p, kf, vf, acc, z);
+}
+
+// false if this thread could not take part (its buffers could not be allocated); the pairs
+// it would have taken are then left to the other threads
+bool work_any(const HostAttnArgs& a, std::atomic<int>& next) noexcept {
+  try {
+    if (a.bf16)
+      work<uint16_t>(a, next);
+    else
+      work<float>(a, next);
+    return true;
+  } catch (...) {
+    return false;
+  }
 }
 
 }  // namespace
@@ -217,10 +226,76 @@ int host_threads(int requested) {
 }
 
 void host_partial_attention(const HostAttnArgs& a, int threads) {
-  if (a.bf16)
-    run<uint16_t>(a, threads);
-  else
-    run<float>(a, threads);
+  std::atomic<int> next{0};
+  std::atomic<bool> ok{true};
+  threads = std::max(1, std::min(threads, a.B * a.Hkv));
+  std::vector<std::thread> pool;
+  pool.reserve(threads - 1);
+  for (int t = 1; t < threads; ++t)
+    pool.emplace_back([&] {
+      if (!work_any(a, next)) ok = false;
+    });
+  if (!work_any(a, next)) ok = false;  // the calling thread works too
+  for (auto& th : pool) th.join();
+  // a thread that failed took no pair, so a pair is left only if every thread failed
+  if (next.load() < a.B * a.Hkv) throw std::runtime_error("no worker thread could run");
+}
+
+// ---- persistent workers ----------------------------------------------------------------------
+// run() publishes one job under the mutex and bumps the generation; every worker takes part in
+// each generation exactly once (run() returns only when all of them have reported back), so a
+// job's arguments stay valid for as long as any worker reads them.
+
+HostPool::HostPool(int threads) {
+  threads = std::max(1, threads);
+  workers_.reserve(threads - 1);
+  for (int t = 1; t < threads; ++t) workers_.emplace_back([this] { loop(); });
+}
+
+HostPool::~HostPool() {
+  {
+    std::lock_guard<std::mutex> lk(mu_);
+    stop_ = true;
+  }
+  start_.notify_all();
+  for (auto& th : workers_) th.join();
+}
+
+void HostPool::loop() {
+  uint64_t seen = 0;
+  for (;;) {
+    const HostAttnArgs* job;
+    {
+      std::unique_lock<std::mutex> lk(mu_);
+      start_.wait(lk, [&] { return stop_ || gen_ != seen; });
+      if (stop_) return;
+      seen = gen_;
+      job = job_;
+    }
+    work_any(*job, next_);  // a thread that fails leaves its pairs to the others
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      if (--busy_ == 0) done_.notify_one();
+    }
+  }
+}
+
+bool HostPool::run(const HostAttnArgs& a) {
+  {
+    std::lock_guard<std::mutex> lk(mu_);
+    job_ = &a;
+    next_.store(0);
+    busy_ = (int)workers_.size();
+    ++gen_;
+  }
+  start_.notify_all();
+  work_any(a, next_);  // the calling thread works too
+  std::unique_lock<std::mutex> lk(mu_);
+  done_.wait(lk, [&] { return busy_ == 0; });
+  job_ = nullptr;
+  // a thread that failed took no pair, and a pair taken is always finished: the job is
+  // whole unless every thread failed
+  return next_.load() >= a.B * a.Hkv;
 }
 
 }  // namespace sa

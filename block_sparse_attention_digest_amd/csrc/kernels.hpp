@@ -59,6 +59,9 @@ hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void
                        hipStream_t stream, bool sum_slices = true);
 QParts gemm_result(const GemmPlan& plan, int m, int n, int nprob, int prob, const float* q,
                    const float* ws);
+// q_out[r][c] = the sum of the parts of q, for rows r < rows and columns c < n (n a multiple of
+// 4); q_out may be device-addressable host memory
+hipError_t launch_gather_query(const QParts& q, int rows, int n, float* q_out, hipStream_t stream);
 
 // ---- selection: scores, top-k and the resident split, one workgroup per pair ----------------
 // gpu_pages (optional, [pairs][top_k]): the page of each resident list entry, -1 past n_gpu.

@@ -320,6 +320,45 @@ def draw_layer_pool(wl: Workload, layer: int, offsets: torch.Tensor, pool_sets) 
             "block_table": table.to(torch.int32).to(dev)}
 
 
+def draw_host_store(wl: Workload, layer: int, offsets: torch.Tensor) -> dict:
+    """The host's copy of one layer's KV, from which the CPU side reads offloaded blocks:
+    every block of every (sequence, KV head) has a host page (a seeded permutation); keys are
+    offset + N(0, 1) per token, values N(0, 1), in the KV dtype, on the CPU.  Returns
+    {"K", "V" [P][bs][d], "table" [B][Hkv][max_blocks] int32}."""
+    B, H, bs, d, mb = wl.batch, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.max_blocks
+    P = B * H * mb
+    perm = torch.randperm(P, generator=generator(wl, f"host_perm{layer}", "cpu"))
+    table = perm.to(torch.int32).view(B, H, mb).clone()
+    noise = _normal((P, bs, d), generator(wl, f"host_k{layer}", "cpu"), "cpu")
+    k_log = offsets.cpu().reshape(P, 1, d) + noise      # logical order (s, h, b)
+    v_log = _normal((P, bs, d), generator(wl, f"host_v{layer}", "cpu"), "cpu")
+    K = torch.empty_like(k_log)
+    V = torch.empty_like(v_log)
+    K[perm] = k_log
+    V[perm] = v_log
+    return {"K": K.to(wl.torch_kv_dtype), "V": V.to(wl.torch_kv_dtype), "table": table}
+
+
+def draw_host_store_aliased(wl: Workload, host_pages: int) -> dict:
+    """A host store for shapes whose whole offloaded KV would not fit in host memory: a pool
+    of host_pages pages (keys and values N(0, 1) in the KV dtype) that every (sequence, KV
+    head, block) maps into through a seeded random table, so any selection reads the bytes a
+    distinct-page store would.  Returns {"K", "V" [host_pages][bs][d], "table" [B][Hkv]
+    [max_blocks] int32}, on the CPU."""
+    bs, d = wl.block_size, wl.head_dim
+    g = generator(wl, "host_alias", "cpu")
+    K = torch.empty((host_pages, bs, d), dtype=wl.torch_kv_dtype)
+    V = torch.empty_like(K)
+    step = max(1, (1 << 22) // (bs * d))  # pages per chunk: 4M values at a time
+    for p0 in range(0, host_pages, step):
+        p1 = min(host_pages, p0 + step)
+        K[p0:p1] = torch.randn((p1 - p0, bs, d), generator=g).to(wl.torch_kv_dtype)
+        V[p0:p1] = torch.randn((p1 - p0, bs, d), generator=g).to(wl.torch_kv_dtype)
+    table = torch.randint(0, host_pages, (wl.batch, wl.num_kv_heads, wl.max_blocks),
+                          generator=g, dtype=torch.int32)
+    return {"K": K, "V": V, "table": table}
+
+
 def draw_host_partials(wl: Workload, layer: int, device) -> dict:
     """Stand-in partials of the offloaded blocks (what the CPU side returns): o ~ N(0, 1)^d,
     m ~ N(0, 1), l ~ U[1, bs * k].  float32, [B][Hq][d] and [B][Hq]."""

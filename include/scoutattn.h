@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 5
+#define SA_ABI_VERSION 6
 
 typedef enum {
   SA_OK = 0,
@@ -324,6 +324,69 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
                          int32_t top_k, float scale, const int32_t* seq_lens,
                          int32_t num_layers, const sa_layer* layers, void* ws,
                          size_t ws_bytes, hipStream_t stream, hipStream_t side_stream);
+
+/* ---------------------------------------------------------------------------------------
+ * The CPU side of the step, run one layer ahead ([Alg. 1]: CPUAttn(B_cpu^{i+1}) is spawned
+ * while layer i runs, and its result A_cpu^{i+1} is merged at layer i+1; [HTML Sec. 3.3]:
+ * the CPU's window is the GPU's layer i).
+ *
+ * sa_host_layer -- one layer's host side.  The first three members may be ordinary host
+ * memory (only host threads read them); the rest must be coherent page-locked host memory
+ * the device can address (hipHostMalloc with hipHostMallocCoherent), as the device writes or
+ * reads them.  All are owned by the caller and must stay valid while a plan that names
+ * them exists.
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+  const void* k_host;        /* the layer's offloaded keys [host_pages][bs][d], KV dtype,
+                                token rows (the layout of sa_host_partial_attention)       */
+  const void* v_host;        /* values, same layout                                         */
+  const int32_t* host_table; /* [B][Hkv][max_blocks]: host page of each block, or -1        */
+  int32_t host_pages;        /* pages in k_host / v_host                                    */
+  float* q_host;             /* [B][Hq][d] float32, written by the step: the query the CPU
+                                attends with (Q_pred^i; Q^0 for layer 0)                    */
+  int32_t* cpu_blocks_host;  /* [B][Hkv][top_k], written by the step's selection: B_cpu^i   */
+  int32_t* n_cpu_host;       /* [B][Hkv], written by the step's selection                   */
+  float* o_host;             /* [B][Hq][d] float32: A_cpu^i, written by the host workers and
+                                read by the step's merge of layer i                          */
+  float* m_host;             /* [B][Hq], natural-log units                                  */
+  float* l_host;             /* [B][Hq]                                                     */
+} sa_host_layer;
+
+/* sa_host_plan -- the host side of sa_decode_step_offload: the layers' host buffers, the
+ * shape, and a pool of num_threads persistent worker threads (0: the machine's hardware
+ * threads).  Creating it touches no device.  seq_lens_host [B] is read by the host work every
+ * time it runs (not copied).  *plan receives the handle, or NULL on error.
+ * sa_host_plan_destroy stops the workers; it must not be called while enqueued work (or a
+ * HIP graph captured from sa_decode_step_offload) that uses the plan can still run.
+ * sa_host_plan_stats: the number of layer tasks run so far and the host time they took
+ * (seconds, wall clock inside the tasks); SA_ERR_HIP if a task failed (its partial is then
+ * left as the empty partial).  Either output pointer may be NULL. */
+typedef struct sa_host_plan sa_host_plan;
+sa_status sa_host_plan_create(const sa_dims* dims, int32_t top_k, float scale,
+                              const int32_t* seq_lens_host, int32_t num_layers,
+                              const sa_host_layer* layers, int32_t num_threads,
+                              sa_host_plan** plan);
+sa_status sa_host_plan_destroy(sa_host_plan* plan);
+sa_status sa_host_plan_stats(const sa_host_plan* plan, int64_t* tasks, double* busy_seconds);
+
+/* sa_decode_step_offload -- sa_decode_step with the CPU side computed, not given.  The
+ * arguments are those of sa_decode_step, with the plan's shape, top_k, scale and num_layers;
+ * in `layers`, host_o/host_m/host_l and the host mirrors are not used (the plan's buffers
+ * take their place).  For each layer i, once B^i is selected (layer 0 on `stream`, the
+ * others one layer ahead on side_stream), the step writes the query the CPU attends with
+ * into q_host and the lists into the plan's mirrors, then enqueues on host_stream a host
+ * task that computes A_cpu^i with the plan's workers (as sa_host_partial_attention does)
+ * into o_host/m_host/l_host; layer i's merge on `stream` waits for that task.  host_stream
+ * must be a stream of its own (not `stream`, not side_stream): each task holds it while it
+ * runs.  Layer 0 has no layer before it, so its merge waits for its own CPU side.  Before
+ * returning, `stream` waits for host_stream and side_stream.  A HIP graph may be captured
+ * from `stream`; its host tasks then run with the plan's buffers at every replay.
+ * ------------------------------------------------------------------------------------- */
+sa_status sa_decode_step_offload(const sa_dims* dims, sa_digest_kind kind, int32_t hidden,
+                                 int32_t top_k, float scale, const int32_t* seq_lens,
+                                 int32_t num_layers, const sa_layer* layers, void* ws,
+                                 size_t ws_bytes, hipStream_t stream, hipStream_t side_stream,
+                                 sa_host_plan* plan, hipStream_t host_stream);
 
 /* ---------------------------------------------------------------------------------------
  * sa_profile_attention -- kernel timing of the attention stage (GPUATTN).  After this call

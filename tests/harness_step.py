@@ -51,14 +51,17 @@ def prepare_step(wl, gen_device, kind="mean"):
         sets = oracle_pool_sets(wl, X64, W64, wk.f64(dig), kind)
         pool = wk.draw_layer_pool(wl, i, off, sets)
         hp = wk.draw_host_partials(wl, i, gen_device)
-        layers.append(dict(X=ins[i]["X"], W=ins[i]["W"], dig=dig, pool=pool, host=hp, sets=sets))
+        layers.append(dict(X=ins[i]["X"], W=ins[i]["W"], dig=dig, pool=pool, host=hp, sets=sets,
+                           off=off))
     return layers
 
 
 def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs_to_check=None,
-             side=True):
+             side=True, offload=False, host_threads=4):
     """handoff: give every layer host mirrors of its offloaded lists; side: run the
-    layer-ahead work on a side stream."""
+    layer-ahead work on a side stream; offload: compute the CPU side with host tasks
+    (sa_decode_step_offload) from a host store of every block, instead of merging the
+    drawn host partials."""
     dev = "cuda"
     B_, Hkv, Hq, G, d, bs, k = (wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.group,
                                 wl.head_dim, wl.block_size, wl.top_k)
@@ -97,10 +100,33 @@ def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs
         dev_layers.append(e)
     ws = B.workspace(B.sa_step_workspace_bytes(dims, wl.hidden, k))
     side_stream = torch.cuda.Stream() if side else None
-    B.sa_decode_step(dims, kind, wl.hidden, k, wl.scale, lens_d, dev_layers, ws,
-                     side_stream=side_stream)
-    torch.cuda.synchronize()
-    H.log("  HIP step done")
+    stores = host_layers = None
+    if offload:
+        stores = [wk.draw_host_store(wl, i, Ld["off"]) for i, Ld in enumerate(data)]
+        host_layers = []
+        for st in stores:
+            host_layers.append(dict(
+                k_host=st["K"], v_host=st["V"], host_table=st["table"],
+                q_host=B.pinned_empty((B_, Hq, d), f32).fill_(float("nan")),
+                cpu_blocks_host=B.pinned_empty((pairs, k)).fill_(-7),
+                n_cpu_host=B.pinned_empty((pairs,)).fill_(-7),
+                o_host=B.pinned_empty((B_, Hq, d), f32).fill_(float("nan")),
+                m_host=B.pinned_empty((B_, Hq), f32).fill_(float("nan")),
+                l_host=B.pinned_empty((B_, Hq), f32).fill_(float("nan"))))
+        plan = B.HostPlan(dims, k, wl.scale, lens.clone(), host_layers, threads=host_threads)
+        host_stream = torch.cuda.Stream()
+        B.sa_decode_step_offload(dims, kind, wl.hidden, k, wl.scale, lens_d, dev_layers, ws,
+                                 plan, host_stream, side_stream=side_stream)
+        torch.cuda.synchronize()
+        tasks, secs = plan.stats()
+        plan.close()
+        assert tasks == L, (tasks, L)
+        H.log(f"  HIP step with host tasks done ({tasks} tasks, {secs * 1e3:.2f} ms on the host)")
+    else:
+        B.sa_decode_step(dims, kind, wl.hidden, k, wl.scale, lens_d, dev_layers, ws,
+                         side_stream=side_stream)
+        torch.cuda.synchronize()
+        H.log("  HIP step done")
 
     # ---------------- oracle
     check = range(pairs) if pairs_to_check is None else pairs_to_check
@@ -127,11 +153,19 @@ def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs
             else:
                 full = so.digest_minmax(Kl, n, bs)
             dig[res_blocks] = full[res_blocks]
-            host = [so.Partial(wk.f64(Ld["host"]["o"][s, h * G + j]),
-                               float(Ld["host"]["m"][s, h * G + j]),
-                               float(Ld["host"]["l"][s, h * G + j])) for j in range(G)]
-            olayers.append(dict(X=wk.f64(Ld["X"]), W=wk.f64(Ld["W"]), digest=dig,
-                                resident=resident, K=Kl, V=Vl, seq_len=n, host=host))
+            OL = dict(X=wk.f64(Ld["X"]), W=wk.f64(Ld["W"]), digest=dig, resident=resident,
+                      K=Kl, V=Vl, seq_len=n)
+            if offload:  # the host's copy of every block; the oracle attends the offloaded ones
+                st = stores[i]
+                pg = st["table"][s, h, :nb].long()
+                OL["K_host"] = wk.f64(st["K"][pg]).reshape(nb * bs, d)
+                OL["V_host"] = wk.f64(st["V"][pg]).reshape(nb * bs, d)
+            else:
+                OL["host"] = [so.Partial(wk.f64(Ld["host"]["o"][s, h * G + j]),
+                                         float(Ld["host"]["m"][s, h * G + j]),
+                                         float(Ld["host"]["l"][s, h * G + j]))
+                              for j in range(G)]
+            olayers.append(OL)
         want = so.decode_step_pair(olayers, s, h, G, d, bs, k, wl.scale, kind)
         for i in range(L):
             e = dev_layers[i]
@@ -139,7 +173,11 @@ def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs
             gbl = e["gpu_blocks"][p].cpu().numpy()
             cbl = e["cpu_blocks"][p].cpu().numpy()
             assert np.all(gbl[ng:] == -1) and np.all(cbl[nc:] == -1)
-            if handoff:
+            if offload:
+                hl_ = host_layers[i]
+                assert int(hl_["n_cpu_host"][p]) == nc
+                assert np.array_equal(hl_["cpu_blocks_host"][p].numpy(), cbl)
+            elif handoff:
                 assert int(e["n_cpu_host"][p]) == nc
                 assert np.array_equal(e["cpu_blocks_host"][p].numpy(), cbl)
             sel = np.sort(np.concatenate([gbl[:ng], cbl[:nc]]))
@@ -148,6 +186,19 @@ def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs
                 ties += 1
                 continue
             assert np.array_equal(gbl[:ng], want[i].gpu_blocks)
+            if offload:
+                # the query handed to the CPU (Q_pred^i; Q^0 at layer 0) and the CPU's partial
+                X64 = wk.f64(data[i - 1]["X"] if i > 0 else data[0]["X"])[s:s + 1]
+                W64 = wk.f64(data[i]["W"])[h * G * d:(h + 1) * G * d]
+                q_want = so.predict_query(X64, W64).reshape(G, d)
+                q_got = host_layers[i]["q_host"][s, h * G:(h + 1) * G].double().numpy()
+                assert np.max(np.abs(q_got - q_want)) <= 1e-3 * max(1.0, np.max(np.abs(q_want)))
+                hl_ = host_layers[i]
+                for j in range(G):  # (the empty partial where nothing is offloaded)
+                    max_err = max(max_err, H.compare_partial(
+                        hl_["o_host"][s, h * G + j].double().numpy(),
+                        float(hl_["m_host"][s, h * G + j]), float(hl_["l_host"][s, h * G + j]),
+                        want[i].host[j], H.attn_tol(wl), f"host partial layer {i} pair {p}"))
             o = e["out_o"][s, h * G:(h + 1) * G].cpu().double().numpy()
             m = e["out_m"][s, h * G:(h + 1) * G].cpu().double().numpy()
             l = e["out_l"][s, h * G:(h + 1) * G].cpu().double().numpy()

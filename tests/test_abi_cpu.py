@@ -33,7 +33,9 @@ def test_header_declares_the_path(lib):
     for n in ("sa_pack_k_pages", "sa_pack_v_pages", "sa_pack_weight", "sa_build_digests",
               "sa_predict_query",
               "sa_select_blocks", "sa_sparse_decode", "sa_merge", "sa_decode_attend_merge",
-              "sa_decode_step", "sa_host_partial_attention", "sa_refresh_last_digests"):
+              "sa_decode_step", "sa_host_partial_attention", "sa_refresh_last_digests",
+              "sa_host_plan_create", "sa_host_plan_destroy", "sa_host_plan_stats",
+              "sa_decode_step_offload"):
         assert n in names
 
 
@@ -44,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.sa_abi_version() == B.ABI_VERSION == 5
+    assert lib.sa_abi_version() == B.ABI_VERSION == 6
     assert lib.sa_status_string(B.SA_ERR_WORKSPACE) == b"SA_ERR_WORKSPACE"
 
 
@@ -183,6 +185,90 @@ def test_step_validation(lib):
                               None, None) == B.SA_ERR_INVALID_ARG
     assert lib.sa_decode_step(ctypes.byref(d), 0, 1024, 8, 0.088, FAKE, 2, layers, FAKE,
                               ws - 1, None, None) == B.SA_ERR_WORKSPACE
+
+
+def host_layers(n):
+    arr = (B.sa_host_layer * n)()
+    for L in arr:
+        for name, _ in B.sa_host_layer._fields_:
+            setattr(L, name, 4 if name == "host_pages" else FAKE)
+    return arr
+
+
+def test_host_plan_lifecycle(lib):
+    """Creating a plan starts its workers and touches no device; nothing runs until a step
+    enqueues its tasks, so the fake pointers are never read."""
+    d = dims()
+    plan = ctypes.c_void_p()
+    assert lib.sa_host_plan_create(ctypes.byref(d), 8, 0.088, FAKE, 3, host_layers(3), 4,
+                                   ctypes.byref(plan)) == B.SA_OK
+    assert plan.value
+    n, t = ctypes.c_int64(-1), ctypes.c_double(-1.0)
+    assert lib.sa_host_plan_stats(plan, ctypes.byref(n), ctypes.byref(t)) == B.SA_OK
+    assert n.value == 0 and t.value == 0.0
+    assert lib.sa_host_plan_destroy(plan) == B.SA_OK
+    assert lib.sa_host_plan_destroy(None) == B.SA_OK  # like free(NULL)
+
+
+def test_host_plan_rejects_bad_arguments(lib):
+    d = dims()
+    plan = ctypes.c_void_p(FAKE)
+
+    def create(top_k=8, scale=0.088, lens=FAKE, n=2, layers=None, threads=0, out=True):
+        layers = host_layers(max(n, 1)) if layers is None else layers
+        return lib.sa_host_plan_create(ctypes.byref(d), top_k, scale, lens, n, layers, threads,
+                                       ctypes.byref(plan) if out else None)
+
+    assert create(top_k=0) == B.SA_ERR_INVALID_ARG and plan.value is None
+    assert create(top_k=65) == B.SA_ERR_INVALID_ARG
+    assert create(scale=0.0) == B.SA_ERR_INVALID_ARG
+    assert create(lens=None) == B.SA_ERR_INVALID_ARG
+    assert create(n=0) == B.SA_ERR_INVALID_ARG
+    assert create(threads=-1) == B.SA_ERR_INVALID_ARG
+    assert create(out=False) == B.SA_ERR_INVALID_ARG
+    bad = host_layers(2)
+    bad[1].host_pages = 0
+    assert create(layers=bad) == B.SA_ERR_INVALID_ARG and b"host layer 1" in lib.sa_last_error()
+    bad = host_layers(2)
+    bad[0].o_host = None
+    assert create(layers=bad) == B.SA_ERR_INVALID_ARG and b"host layer 0" in lib.sa_last_error()
+
+
+@no_gpu
+def test_offload_step_validation(lib):
+    """The plan must match the step's dims, top_k, scale and layer count, and host_stream
+    must be a stream of its own; all checked before anything is enqueued."""
+    d = dims()
+    plan = ctypes.c_void_p()
+    assert lib.sa_host_plan_create(ctypes.byref(d), 8, 0.088, FAKE, 2, host_layers(2), 2,
+                                   ctypes.byref(plan)) == B.SA_OK
+    try:
+        ws = lib.sa_step_workspace_bytes(ctypes.byref(d), 1024, 8)
+        layers = (B.sa_layer * 2)()
+        for L in layers:
+            for name, _ in B.sa_layer._fields_:
+                setattr(L, name, FAKE)
+            L.host_o = L.host_m = L.host_l = L.cpu_blocks_host = L.n_cpu_host = None
+
+        def step(dd=d, top_k=8, scale=0.088, n=2, p=plan, host=FAKE + 3, side=FAKE + 2):
+            return lib.sa_decode_step_offload(ctypes.byref(dd), 0, 1024, top_k, scale, FAKE, n,
+                                              layers, FAKE, ws, FAKE + 1, side, p, host)
+
+        assert step(p=None) == B.SA_ERR_INVALID_ARG
+        assert step(dd=dims(batch=3)) == B.SA_ERR_INVALID_ARG
+        assert b"other dims" in lib.sa_last_error()
+        assert step(top_k=4) == B.SA_ERR_INVALID_ARG
+        assert step(scale=0.1) == B.SA_ERR_INVALID_ARG
+        assert step(n=1) == B.SA_ERR_INVALID_ARG
+        assert step(host=None) == B.SA_ERR_INVALID_ARG
+        assert step(host=FAKE + 1) == B.SA_ERR_INVALID_ARG  # the main stream
+        assert step(host=FAKE + 2) == B.SA_ERR_INVALID_ARG  # the side stream
+        assert b"stream of its own" in lib.sa_last_error()
+        # without a plan the same layers lack their host partials
+        assert lib.sa_decode_step(ctypes.byref(d), 0, 1024, 8, 0.088, FAKE, 2, layers, FAKE,
+                                  ws, None, None) == B.SA_ERR_INVALID_ARG
+    finally:
+        assert lib.sa_host_plan_destroy(plan) == B.SA_OK
 
 
 def test_binding_requires_the_library(monkeypatch, tmp_path):

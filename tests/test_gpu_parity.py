@@ -251,6 +251,29 @@ def test_step_parity_handoff_one_stream():
     assert r["cpu_ratio"] > 0.1
 
 
+def test_step_offload_parity():
+    """The CPU side computed by host tasks one layer ahead (sa_decode_step_offload): the
+    handed-over query, the host partials and the merged outputs against the oracle, which
+    attends the offloaded blocks with Q_pred^i (Q^0 at layer 0)."""
+    H.log("[case] step offload, side stream")
+    import harness_step as HS
+    r = HS.run_step(wk.QWEN3_14B_STEP.scaled(batch=3, num_q_heads=10, num_kv_heads=2,
+                                             context=2000, layers=4, pool_blocks=6, hidden=512,
+                                             top_k=8),
+                    gen_device="cpu", side=True, offload=True)
+    assert r["cpu_ratio"] > 0.1
+
+
+def test_step_offload_parity_one_stream_one_thread():
+    H.log("[case] step offload, one stream, one host thread")
+    import harness_step as HS
+    r = HS.run_step(wk.QWEN3_14B_STEP.scaled(batch=2, num_q_heads=8, num_kv_heads=2,
+                                             context=1500, layers=3, pool_blocks=5, hidden=256,
+                                             top_k=8),
+                    gen_device="cpu", side=False, offload=True, host_threads=1)
+    assert r["cpu_ratio"] > 0.1
+
+
 def test_step_parity_minmax_no_handoff():
     H.log("[case] step minmax")
     import harness_step as HS
