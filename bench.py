@@ -63,6 +63,9 @@ def parse():
                     help="host worker threads of the offload step (at most the CPUs present)")
     ap.add_argument("--host-pages", type=int, default=32768,
                     help="pages of the aliased host KV store of the offload step")
+    ap.add_argument("--pool-blocks", type=int, default=None,
+                    help="resident pool blocks per (sequence, KV head) instead of the "
+                         "workload's 128 (a study of the CPU share; not the headline workload)")
     return ap.parse_args()
 
 
@@ -322,6 +325,8 @@ def main():
     torch.cuda.set_device(0)
 
     wl = wk.QWEN3_14B_STEP
+    if args.pool_blocks is not None:
+        wl = wl.scaled(pool_blocks=args.pool_blocks)
     log(f"workload {wl.name}: setup")
     dims, lens, layers, ws = setup(wl, torch, B, wk)
     side_stream = torch.cuda.Stream()

@@ -85,6 +85,7 @@ SIGNATURES = {
     "sa_host_plan_create": (ctypes.c_int, [_D, _I, _F, _P, _I, ctypes.POINTER(sa_host_layer), _I,
                                            ctypes.POINTER(_P)]),
     "sa_host_plan_destroy": (ctypes.c_int, [_P]),
+    "sa_host_plan_run": (ctypes.c_int, [_P, _I]),
     "sa_host_plan_stats": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int64),
                                           ctypes.POINTER(ctypes.c_double)]),
     "sa_decode_step_offload": (ctypes.c_int, [_D, ctypes.c_int, _I, _I, _F, _P, _I,
@@ -443,6 +444,10 @@ class HostPlan:
         t = ctypes.c_double()
         _check(lib().sa_host_plan_stats(self.handle, ctypes.byref(n), ctypes.byref(t)))
         return n.value, t.value
+
+    def run(self, layer: int):
+        """Layer `layer`'s host task now, on this thread and the plan's workers."""
+        _check(lib().sa_host_plan_run(self.handle, layer))
 
     def close(self):
         if self.handle:

@@ -505,18 +505,18 @@ struct sa_host_plan {
   std::atomic<bool> failed{false};
 };
 
-// A HIP host function (it runs on the runtime's callback thread and holds its stream until
-// it returns; it makes no HIP call): A_cpu of one layer on the plan's workers.
-static void run_host_task(void* arg) {
-  const auto* t = static_cast<const sa_host_plan::Task*>(arg);
-  sa_host_plan& P = *t->plan;
-  const sa_host_layer& H = P.layers[t->layer];
+// A layer's host task: A_cpu on the plan's workers; false if no worker could run (the
+// partial is then the empty one).
+static bool host_task(const sa_host_plan::Task& t) {
+  sa_host_plan& P = *t.plan;
+  const sa_host_layer& H = P.layers[t.layer];
   const auto t0 = std::chrono::steady_clock::now();
   const sa::HostAttnArgs a =
       host_args(P.s, H.host_pages, P.top_k, P.scale, H.q_host, H.k_host, H.v_host,
                 H.host_table, P.seq_lens, H.cpu_blocks_host, H.n_cpu_host, H.o_host, H.m_host,
                 H.l_host);
-  if (!P.pool->run(a)) {  // no worker could run: leave the empty partial, report it later
+  const bool done = P.pool->run(a);
+  if (!done) {
     P.failed = true;
     const size_t rows = (size_t)P.s.B * P.s.Hq;
     std::fill(H.o_host, H.o_host + rows * P.s.d, 0.f);
@@ -526,7 +526,12 @@ static void run_host_task(void* arg) {
   const auto dt = std::chrono::steady_clock::now() - t0;
   P.busy_ns += std::chrono::duration_cast<std::chrono::nanoseconds>(dt).count();
   ++P.runs;
+  return done;
 }
+
+// The host task as a HIP host function: it runs on the runtime's callback thread and holds
+// its stream until it returns; it makes no HIP call.  A failure shows in sa_host_plan_stats.
+static void run_host_task(void* arg) { host_task(*static_cast<const sa_host_plan::Task*>(arg)); }
 
 sa_status sa_host_plan_create(const sa_dims* dims, int32_t top_k, float scale,
                               const int32_t* seq_lens_host, int32_t num_layers,
@@ -565,6 +570,15 @@ sa_status sa_host_plan_create(const sa_dims* dims, int32_t top_k, float scale,
   } catch (const std::exception& e) {  // allocation or thread creation
     return fail(SA_ERR_INVALID_ARG, "host plan: %s", e.what());
   }
+  return ok();
+}
+
+sa_status sa_host_plan_run(sa_host_plan* plan, int32_t layer) {
+  SA_NOT_NULL(plan);
+  if (layer < 0 || layer >= (int)plan->layers.size())
+    return fail(SA_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, (int)plan->layers.size());
+  if (!host_task(plan->tasks[layer]))
+    return fail(SA_ERR_HIP, "the host task could not run (out of memory)");
   return ok();
 }
 

@@ -52,11 +52,12 @@ class HostPool {
   void loop();
   std::mutex mu_;
   std::condition_variable start_, done_;
-  const HostAttnArgs* job_ = nullptr;
-  uint64_t gen_ = 0;
-  int busy_ = 0;
-  bool stop_ = false;
+  std::atomic<const HostAttnArgs*> job_{nullptr};
+  std::atomic<uint64_t> gen_{0};
+  std::atomic<int> busy_{0};
+  std::atomic<bool> stop_{false};
   std::atomic<int> next_{0};
+  std::vector<float> own_buf_;  // the block buffers of the thread that calls run()
   std::vector<std::thread> workers_;
 };
 

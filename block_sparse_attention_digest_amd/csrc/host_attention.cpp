@@ -14,6 +14,7 @@
 // one thread in one order, so the result does not depend on the thread count.
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <condition_variable>
 #include <cstring>
@@ -187,14 +188,14 @@ void attend_pair(const HostAttnArgs& a, BlockFn block, int pair, float* kf, floa
   }
 }
 
-// Takes pairs from `next` until none is left, with this thread's own block buffers: one
-// block of K and V as float, the G output rows, the G x bs logits.
+// Takes pairs from `next` until none is left, with this thread's own block buffers in `buf`:
+// one block of K and V as float, the G output rows, the G x bs logits.
 template <typename T>
-void work(const HostAttnArgs& a, std::atomic<int>& next) {
+void work(const HostAttnArgs& a, std::atomic<int>& next, std::vector<float>& buf) {
   const BlockFn block = pick_block(a.G);
   const int npairs = a.B * a.Hkv;
   const size_t blk = (size_t)a.bs * a.d;
-  std::vector<float> buf(2 * blk + (size_t)a.G * a.d + (size_t)a.G * a.bs);
+  buf.resize(2 * blk + (size_t)a.G * a.d + (size_t)a.G * a.bs);
   float* kf = buf.data();
   float* vf = kf + blk;
   float* acc = vf + blk;
@@ -205,17 +206,34 @@ void work(const HostAttnArgs& a, std::atomic<int>& next) {
 
 // false if this thread could not take part (its buffers could not be allocated); the pairs
 // it would have taken are then left to the other threads
-bool work_any(const HostAttnArgs& a, std::atomic<int>& next) noexcept {
+bool work_any(const HostAttnArgs& a, std::atomic<int>& next, std::vector<float>& buf) noexcept {
   try {
     if (a.bf16)
-      work<uint16_t>(a, next);
+      work<uint16_t>(a, next, buf);
     else
-      work<float>(a, next);
+      work<float>(a, next, buf);
     return true;
   } catch (...) {
     return false;
   }
 }
+
+// Spins until pred() holds or `us` microseconds have passed; returns pred().  Waking a thread
+// that sleeps on a condition variable costs tens of microseconds, which a layer's host task
+// (well under a millisecond when little is offloaded) would pay twice.  The spin yields rather
+// than pausing: with as many workers as CPUs, a spinning worker must give way to the runtime's
+// own threads (the one that starts the next host task among them).
+template <class Pred>
+bool spin_until(Pred pred, int us) {
+  const auto end = std::chrono::steady_clock::now() + std::chrono::microseconds(us);
+  for (unsigned i = 0;; ++i) {
+    if (pred()) return true;
+    std::this_thread::yield();
+    if ((i & 63) == 63 && std::chrono::steady_clock::now() > end) return pred();
+  }
+}
+
+constexpr int kSpinUs = 300;  // about two GPU layers of the 40-layer decode step
 
 }  // namespace
 
@@ -233,18 +251,22 @@ void host_partial_attention(const HostAttnArgs& a, int threads) {
   pool.reserve(threads - 1);
   for (int t = 1; t < threads; ++t)
     pool.emplace_back([&] {
-      if (!work_any(a, next)) ok = false;
+      std::vector<float> buf;
+      if (!work_any(a, next, buf)) ok = false;
     });
-  if (!work_any(a, next)) ok = false;  // the calling thread works too
+  std::vector<float> buf;
+  if (!work_any(a, next, buf)) ok = false;  // the calling thread works too
   for (auto& th : pool) th.join();
   // a thread that failed took no pair, so a pair is left only if every thread failed
   if (next.load() < a.B * a.Hkv) throw std::runtime_error("no worker thread could run");
 }
 
 // ---- persistent workers ----------------------------------------------------------------------
-// run() publishes one job under the mutex and bumps the generation; every worker takes part in
-// each generation exactly once (run() returns only when all of them have reported back), so a
-// job's arguments stay valid for as long as any worker reads them.
+// run() publishes one job and bumps the generation (under the mutex, so a sleeping worker cannot
+// miss it); every worker takes part in each generation exactly once (run() returns only when
+// all of them have reported back), so a job's arguments stay valid while any worker reads them.
+// Between jobs a worker spins for a short while before it sleeps, and so does run() while it
+// waits for the last worker.
 
 HostPool::HostPool(int threads) {
   threads = std::max(1, threads);
@@ -255,7 +277,7 @@ HostPool::HostPool(int threads) {
 HostPool::~HostPool() {
   {
     std::lock_guard<std::mutex> lk(mu_);
-    stop_ = true;
+    stop_.store(true);
   }
   start_.notify_all();
   for (auto& th : workers_) th.join();
@@ -263,36 +285,41 @@ HostPool::~HostPool() {
 
 void HostPool::loop() {
   uint64_t seen = 0;
+  std::vector<float> buf;  // this worker's block buffers, kept across jobs
+  auto ready = [&] { return stop_.load(std::memory_order_acquire) ||
+                            gen_.load(std::memory_order_acquire) != seen; };
   for (;;) {
-    const HostAttnArgs* job;
-    {
+    if (!spin_until(ready, kSpinUs)) {
       std::unique_lock<std::mutex> lk(mu_);
-      start_.wait(lk, [&] { return stop_ || gen_ != seen; });
-      if (stop_) return;
-      seen = gen_;
-      job = job_;
+      start_.wait(lk, ready);
     }
-    work_any(*job, next_);  // a thread that fails leaves its pairs to the others
-    {
+    if (stop_.load(std::memory_order_acquire)) return;
+    seen = gen_.load(std::memory_order_acquire);
+    work_any(*job_.load(std::memory_order_acquire), next_, buf);  // a failure leaves its
+                                                                  // pairs to the others
+    if (busy_.fetch_sub(1, std::memory_order_acq_rel) == 1) {
       std::lock_guard<std::mutex> lk(mu_);
-      if (--busy_ == 0) done_.notify_one();
+      done_.notify_one();
     }
   }
 }
 
 bool HostPool::run(const HostAttnArgs& a) {
+  job_.store(&a, std::memory_order_relaxed);
+  next_.store(0, std::memory_order_relaxed);
+  busy_.store((int)workers_.size(), std::memory_order_relaxed);
   {
     std::lock_guard<std::mutex> lk(mu_);
-    job_ = &a;
-    next_.store(0);
-    busy_ = (int)workers_.size();
-    ++gen_;
+    gen_.fetch_add(1, std::memory_order_release);
   }
   start_.notify_all();
-  work_any(a, next_);  // the calling thread works too
-  std::unique_lock<std::mutex> lk(mu_);
-  done_.wait(lk, [&] { return busy_ == 0; });
-  job_ = nullptr;
+  work_any(a, next_, own_buf_);  // the calling thread works too
+  auto finished = [&] { return busy_.load(std::memory_order_acquire) == 0; };
+  if (!spin_until(finished, kSpinUs)) {
+    std::unique_lock<std::mutex> lk(mu_);
+    done_.wait(lk, finished);
+  }
+  job_.store(nullptr, std::memory_order_relaxed);
   // a thread that failed took no pair, and a pair taken is always finished: the job is
   // whole unless every thread failed
   return next_.load() >= a.B * a.Hkv;

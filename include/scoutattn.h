@@ -360,12 +360,17 @@ typedef struct {
  * HIP graph captured from sa_decode_step_offload) that uses the plan can still run.
  * sa_host_plan_stats: the number of layer tasks run so far and the host time they took
  * (seconds, wall clock inside the tasks); SA_ERR_HIP if a task failed (its partial is then
- * left as the empty partial).  Either output pointer may be NULL. */
+ * left as the empty partial).  Either output pointer may be NULL.
+ * sa_host_plan_run: runs layer `layer`'s host task now, on the calling thread and the plan's
+ * workers (what the step enqueues as a host function), from the layer's q_host and hand-off
+ * lists as they are; returns when o_host/m_host/l_host are written.  For callers that drive
+ * the CPU side themselves.  Not while the plan's tasks may run from a stream. */
 typedef struct sa_host_plan sa_host_plan;
 sa_status sa_host_plan_create(const sa_dims* dims, int32_t top_k, float scale,
                               const int32_t* seq_lens_host, int32_t num_layers,
                               const sa_host_layer* layers, int32_t num_threads,
                               sa_host_plan** plan);
+sa_status sa_host_plan_run(sa_host_plan* plan, int32_t layer);
 sa_status sa_host_plan_destroy(sa_host_plan* plan);
 sa_status sa_host_plan_stats(const sa_host_plan* plan, int64_t* tasks, double* busy_seconds);
 

@@ -35,6 +35,7 @@ def test_header_declares_the_path(lib):
               "sa_select_blocks", "sa_sparse_decode", "sa_merge", "sa_decode_attend_merge",
               "sa_decode_step", "sa_host_partial_attention", "sa_refresh_last_digests",
               "sa_host_plan_create", "sa_host_plan_destroy", "sa_host_plan_stats",
+              "sa_host_plan_run",
               "sa_decode_step_offload"):
         assert n in names
 

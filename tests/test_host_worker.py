@@ -163,3 +163,46 @@ def test_host_partial_rejects_bad_arguments(lib):
 def ctypes_dims(dims):
     import ctypes
     return ctypes.byref(dims.c())
+
+
+def plan_layer(P):
+    """A host-plan layer over a make_problem instance (plain CPU tensors: nothing on the
+    device reads them here)."""
+    dims = P["dims"]
+    rows = dims.batch * dims.num_q_heads
+    return dict(k_host=P["k_host"], v_host=P["v_host"], host_table=P["table"],
+                q_host=P["q"].clone(), cpu_blocks_host=P["cpu"].clone(),
+                n_cpu_host=P["n_cpu"].clone(),
+                o_host=torch.full((rows, dims.head_dim), float("nan")),
+                m_host=torch.full((rows,), float("nan")), l_host=torch.full((rows,), float("nan")))
+
+
+@pytest.mark.parametrize("threads", [1, 3])
+def test_host_plan_run_matches_the_worker(lib, threads):
+    """A plan's layer task (persistent workers that spin, then sleep, between jobs) gives
+    exactly what sa_host_partial_attention gives for the same layer, run after run."""
+    import time
+    Ps = [make_problem("bf16", seed=51), make_problem("bf16", seed=52)]
+    for P in Ps[1:]:  # one shape for the plan: same dims, lengths and list stride
+        P["lens"] = Ps[0]["lens"]
+    layers = [plan_layer(P) for P in Ps]
+    dims = Ps[0]["dims"]
+    plan = B.HostPlan(dims, Ps[0]["top"], Ps[0]["scale"], Ps[0]["lens"], layers, threads=threads)
+    try:
+        for rep in range(3):
+            for i in (1, 0):
+                layers[i]["o_host"].fill_(float("nan"))
+                plan.run(i)
+                want = run_worker(Ps[i], threads=2)
+                got = (layers[i]["o_host"].numpy().astype(np.float64),
+                       layers[i]["m_host"].numpy().astype(np.float64),
+                       layers[i]["l_host"].numpy().astype(np.float64))
+                for a, b in zip(got, want):
+                    assert np.array_equal(a, b, equal_nan=True), (rep, i)
+            time.sleep(0.002 * rep)  # past the spin: the workers sleep and are woken
+        n, secs = plan.stats()
+        assert n == 6 and secs > 0
+        with pytest.raises(B.SaError):
+            plan.run(2)
+    finally:
+        plan.close()
