@@ -25,6 +25,8 @@ written out in float64, with no blocking, fusion or reordering beyond it):
     merges layer i                                    [Algorithm 1; HTML Sec. 3.3]
   * the CPU side's partial over B_cpu, spawned one layer ahead and so computed with the
     predicted query                                   [Algorithm 1; HTML Sec. 3.3, 4]
+  * periodic recall: offloaded selected blocks move into the pages of resident blocks
+    that are no longer selected                       [HTML Sec. 3.4; DIGEST 三]
 
 Readings taken where the pages are silent (each also listed in the design doc):
   R1 min/max score = sum_c max(q_c*min_c, q_c*max_c), Quest's upper bound on q.k.
@@ -244,6 +246,37 @@ def split_resident(selected: np.ndarray, resident: np.ndarray):
     selected = np.asarray(selected, dtype=np.int64)
     res = np.asarray(resident, dtype=bool)[selected]
     return selected[res], selected[~res]
+
+
+def recall_pair(table_row, seq_len: int, block_size: int, gpu_blocks, cpu_blocks,
+                host_pages_row, max_recall: int):
+    """Periodic KV recall for one (sequence, KV head) [HTML Sec. 3.4; DIGEST 三, the
+    asynchronous periodic recall]: blocks the CPU attends are brought back into GPU memory,
+    refreshing the resident set towards the blocks that are important now.
+
+    Readings (the pages name neither which blocks come back nor which make room):
+      * recalled: the layer's current B_cpu in list order (ascending), skipping entries that
+        are outside the sequence, already resident, or without a host page;
+      * evicted: the resident blocks that are not in the current selection
+        (B_gpu and B_cpu), in ascending block order; a recalled block takes the page of the
+        evicted block paired with it;
+      * n = min(#recalled candidates, #evictable, max_recall) blocks move.
+    Returns (new table row, [(recalled block, page, host page), ...]).
+    """
+    table = np.array(table_row, dtype=np.int64)
+    nb = min(num_blocks(seq_len, block_size), len(table))
+    selected = set(int(b) for b in gpu_blocks) | set(int(b) for b in cpu_blocks)
+    cands = [int(b) for b in cpu_blocks
+             if 0 <= b < nb and table[b] < 0 and host_pages_row[b] >= 0]
+    victims = [b for b in range(nb) if table[b] >= 0 and b not in selected]
+    n = min(len(cands), len(victims), max_recall)
+    moves = []
+    for t in range(n):
+        page = int(table[victims[t]])
+        table[victims[t]] = -1
+        table[cands[t]] = page
+        moves.append((cands[t], page, int(host_pages_row[cands[t]])))
+    return table, moves
 
 
 # ----------------------------------------------------------------------------------------

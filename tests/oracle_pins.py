@@ -487,4 +487,57 @@ def pin_step_host_side_merges_to_attention_over_selection():
                     _close(r.out[g].o, ref[g], 1e-12, f"host-side step layer {i}")
 
 
+def pin_recall_hand():
+    """Periodic recall, worked by hand: 8 blocks of 4 tokens (30 tokens: block 7 holds 2),
+    resident {0: page 10, 2: 11, 5: 12, 6: 13}, selection B_gpu = {2}, B_cpu = {1, 3, 7};
+    block 4 has no host page.  Evictable (resident, not selected, ascending): 0, 5, 6.
+    With max_recall 2: block 1 takes block 0's page 10, block 3 takes block 5's page 12."""
+    table = [10, -1, 11, -1, -1, 12, 13, -1]
+    host = [50, 51, 52, 53, -1, 55, 56, 57]
+    new, moves = so.recall_pair(table, 30, 4, [2], [1, 3, 7], host, 2)
+    assert new.tolist() == [-1, 10, 11, 12, -1, -1, 13, -1]
+    assert moves == [(1, 10, 51), (3, 12, 53)]
+    # unlimited: block 7 takes block 6's page 13 as well
+    new, moves = so.recall_pair(table, 30, 4, [2], [1, 3, 7], host, 99)
+    assert new.tolist() == [-1, 10, 11, 12, -1, -1, -1, 13] and len(moves) == 3
+    # a listed block that is already resident, past the sequence, or without a host page is
+    # skipped; nothing to evict means nothing moves
+    new, moves = so.recall_pair(table, 30, 4, [2], [0, 4, 9], host, 9)
+    assert new.tolist() == table and moves == []
+    new, moves = so.recall_pair(table, 30, 4, [0, 2, 5, 6], [1], host, 9)
+    assert new.tolist() == table and moves == []
+
+
+def pin_recall_invariants():
+    """On random tables and selections: the set of pages in use is unchanged, the number of
+    resident blocks is unchanged, no selected resident block loses its page, every moved
+    block was offloaded and selected and is resident afterwards, and the moves are as many
+    as the smallest of candidates, evictable blocks and the limit (brute force)."""
+    rng = np.random.default_rng(61)
+    for trial in range(200):
+        nb_max = int(rng.integers(1, 40))
+        bs = int(rng.integers(1, 9))
+        seq_len = int(rng.integers(1, nb_max * bs + 1))
+        nb = so.num_blocks(seq_len, bs)
+        res = rng.random(nb_max) < rng.random()
+        pages = rng.permutation(1000)[:nb_max]
+        table = np.where(res, pages, -1)
+        table[nb:] = -1
+        host = np.where(rng.random(nb_max) < 0.9, rng.permutation(nb_max), -1)
+        k = int(rng.integers(1, nb + 1))
+        sel = np.sort(rng.permutation(nb)[:k])
+        g, c = so.split_resident(sel, table[:nb] >= 0)
+        lim = int(rng.integers(0, k + 2))
+        new, moves = so.recall_pair(table, seq_len, bs, g, c, host, lim)
+        used0 = sorted(int(p) for p in table if p >= 0)
+        used1 = sorted(int(p) for p in new if p >= 0)
+        assert used0 == used1, trial
+        assert all(new[b] == table[b] for b in g), trial
+        cands = [b for b in c if host[b] >= 0]
+        evictable = [b for b in range(nb) if table[b] >= 0 and b not in set(sel.tolist())]
+        assert len(moves) == min(len(cands), len(evictable), lim), trial
+        for b, p, hp in moves:
+            assert table[b] < 0 and b in set(c.tolist()) and new[b] == p and hp == host[b]
+
+
 ALL_PINS = [v for k, v in dict(globals()).items() if k.startswith("pin_") and callable(v)]

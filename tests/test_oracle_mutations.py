@@ -160,6 +160,30 @@ def _step_host_with_true_query(layers, s, h, group, head_dim, block_size, top_k,
                                      kind)
 
 
+def _recall_evicts_descending(table_row, seq_len, block_size, gpu_blocks, cpu_blocks,
+                              host_pages_row, max_recall):
+    """Evicts the highest-indexed evictable blocks first."""
+    table = np.array(table_row, dtype=np.int64)
+    nb = min(so.num_blocks(seq_len, block_size), len(table))
+    selected = set(int(b) for b in gpu_blocks) | set(int(b) for b in cpu_blocks)
+    cands = [int(b) for b in cpu_blocks if 0 <= b < nb and table[b] < 0 and host_pages_row[b] >= 0]
+    victims = [b for b in range(nb) if table[b] >= 0 and b not in selected][::-1]
+    moves = []
+    for t in range(min(len(cands), len(victims), max_recall)):
+        page = int(table[victims[t]])
+        table[victims[t]] = -1
+        table[cands[t]] = page
+        moves.append((cands[t], page, int(host_pages_row[cands[t]])))
+    return table, moves
+
+
+def _recall_evicts_selected(table_row, seq_len, block_size, gpu_blocks, cpu_blocks,
+                            host_pages_row, max_recall):
+    """Forgets B_gpu when choosing whom to evict."""
+    return _orig["recall_pair"](table_row, seq_len, block_size, [], cpu_blocks, host_pages_row,
+                                max_recall)
+
+
 def _gqa_shifted(h, group):
     return range(h * group + 1, (h + 1) * group + 1)
 
@@ -188,6 +212,8 @@ MUTATIONS = {
     "host partial merged when nothing offloaded": ("decode_step_pair", _step_always_merges_host),
     "GQA group off by one head": ("gqa_group", _gqa_shifted),
     "host side attends with the true query": ("decode_step_pair", _step_host_with_true_query),
+    "recall evicts the highest blocks first": ("recall_pair", _recall_evicts_descending),
+    "recall may evict selected resident blocks": ("recall_pair", _recall_evicts_selected),
 }
 
 
