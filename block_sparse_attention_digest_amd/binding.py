@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libscoutattn.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = 0, -1, -2, -3, -4
 SA_F32, SA_BF16 = 0, 1
 SA_DIGEST_MEAN, SA_DIGEST_MINMAX = 0, 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 KIND = {"mean": SA_DIGEST_MEAN, "minmax": SA_DIGEST_MINMAX}
 
@@ -82,6 +82,9 @@ SIGNATURES = {
     "sa_decode_step": (ctypes.c_int, [_D, ctypes.c_int, _I, _I, _F, _P, _I,
                                       ctypes.POINTER(sa_layer), _P, _Z, _P, _P]),
     "sa_profile_attention": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.POINTER(_P), _I]),
+    "sa_recall_workspace_bytes": (_Z, [_D, _I]),
+    "sa_recall_blocks": (ctypes.c_int, [_D, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P,
+                                        _P, _P, _P, _Z, _P]),
     "sa_host_plan_create": (ctypes.c_int, [_D, _I, _F, _P, _I, ctypes.POINTER(sa_host_layer), _I,
                                            ctypes.POINTER(_P)]),
     "sa_host_plan_destroy": (ctypes.c_int, [_P]),
@@ -397,6 +400,38 @@ def sa_decode_step(dims: Dims, kind: str, hidden: int, top_k: int, scale: float,
         _ptr(seq_lens, torch.int32, dims.batch, "seq_lens"), len(layers), arr,
         _ptr(ws, torch.uint8, name="ws"), ws.numel(), _stream(stream),
         None if side_stream is None else _stream(side_stream)))
+
+
+def sa_recall_blocks(dims: Dims, list_stride: int, max_recall: int, seq_lens, block_table,
+                     gpu_blocks, n_gpu, cpu_blocks, n_cpu, k_host, v_host, host_table,
+                     k_pool, v_pool, n_recalled, ws=None, stream=None):
+    """Periodic recall for one layer.  k_host, v_host: pinned CPU tensors (pinned_empty)
+    [pages][bs][d]; host_table: a GPU tensor or a pinned CPU tensor; the rest GPU tensors.
+    block_table, k_pool, v_pool and n_recalled are written."""
+    i32 = torch.int32
+    B_, Hkv, mb = dims.batch, dims.num_kv_heads, dims.max_blocks
+    pairs = B_ * Hkv
+    pages = k_host.shape[0]
+    per_page = dims.block_size * dims.head_dim
+    if ws is None:
+        ws = workspace(sa_recall_workspace_bytes(dims, max_recall))
+    _check(lib().sa_recall_blocks(
+        ctypes.byref(dims.c()), list_stride, max_recall,
+        _ptr(seq_lens, i32, B_, "seq_lens"), _ptr(block_table, i32, pairs * mb, "block_table"),
+        _ptr(gpu_blocks, i32, pairs * list_stride, "gpu_blocks"),
+        _ptr(n_gpu, i32, pairs, "n_gpu"), _ptr(cpu_blocks, i32, pairs * list_stride, "cpu_blocks"),
+        _ptr(n_cpu, i32, pairs, "n_cpu"),
+        _ptr(k_host, dims.kv_torch, pages * per_page, "k_host", device=False),
+        _ptr(v_host, dims.kv_torch, pages * per_page, "v_host", device=False),
+        _ptr(host_table, i32, pairs * mb, "host_table", device=host_table.is_cuda), pages,
+        _ptr(k_pool, dims.kv_torch, dims.num_pages * per_page, "k_pool"),
+        _ptr(v_pool, dims.kv_torch, dims.num_pages * per_page, "v_pool"),
+        _ptr(n_recalled, i32, pairs, "n_recalled"), _ptr(ws, torch.uint8, name="ws"),
+        ws.numel(), _stream(stream)))
+
+
+def sa_recall_workspace_bytes(dims: Dims, max_recall: int) -> int:
+    return lib().sa_recall_workspace_bytes(ctypes.byref(dims.c()), max_recall)
 
 
 class HostPlan:

@@ -419,6 +419,60 @@ sa_status sa_merge(int32_t rows, int32_t d, const float* o_a, const float* m_a,
   return ok();
 }
 
+// ---- periodic recall -------------------------------------------------------------------------
+
+static constexpr int kMaxRecall = 4096;
+
+size_t sa_recall_workspace_bytes(const sa_dims* dims, int32_t max_recall) {
+  sa::Shape s;
+  if (check_dims(dims, &s) != SA_OK) return 0;
+  if (max_recall < 1 || max_recall > kMaxRecall) {
+    fail(SA_ERR_INVALID_ARG, "max_recall %d outside [1, %d]", max_recall, kMaxRecall);
+    return 0;
+  }
+  return align_up((size_t)s.B * s.Hkv * max_recall * 2 * sizeof(int32_t));
+}
+
+sa_status sa_recall_blocks(const sa_dims* dims, int32_t list_stride, int32_t max_recall,
+                           const int32_t* seq_lens, int32_t* block_table,
+                           const int32_t* gpu_blocks, const int32_t* n_gpu,
+                           const int32_t* cpu_blocks, const int32_t* n_cpu, const void* k_host,
+                           const void* v_host, const int32_t* host_table, int32_t host_pages,
+                           void* k_pool, void* v_pool, int32_t* n_recalled, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  sa::Shape s;
+  SA_CHECK(check_dims(dims, &s));
+  if (list_stride < 1 || list_stride > s.max_blocks)
+    return fail(SA_ERR_INVALID_ARG, "list_stride %d outside [1, max_blocks = %d]", list_stride,
+                s.max_blocks);
+  if (max_recall < 1 || max_recall > kMaxRecall)
+    return fail(SA_ERR_INVALID_ARG, "max_recall %d outside [1, %d]", max_recall, kMaxRecall);
+  if (sa::recall_plan_lds_bytes(s, max_recall) > 64 * 1024)
+    return fail(SA_ERR_UNSUPPORTED, "max_blocks %d with max_recall %d exceeds the plan's LDS",
+                s.max_blocks, max_recall);
+  if (host_pages < 1) return fail(SA_ERR_INVALID_ARG, "host_pages %d < 1", host_pages);
+  SA_NOT_NULL(seq_lens);
+  SA_NOT_NULL(block_table);
+  SA_NOT_NULL(gpu_blocks);
+  SA_NOT_NULL(n_gpu);
+  SA_NOT_NULL(cpu_blocks);
+  SA_NOT_NULL(n_cpu);
+  SA_NOT_NULL(k_host);
+  SA_NOT_NULL(v_host);
+  SA_NOT_NULL(host_table);
+  SA_NOT_NULL(k_pool);
+  SA_NOT_NULL(v_pool);
+  SA_NOT_NULL(n_recalled);
+  const size_t need = sa_recall_workspace_bytes(dims, max_recall);
+  if (!ws || ws_bytes < need)
+    return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
+  SA_HIP(sa::launch_recall(s, list_stride, max_recall, seq_lens, block_table, gpu_blocks, n_gpu,
+                           cpu_blocks, n_cpu, k_host, v_host, host_table, host_pages, k_pool,
+                           v_pool, n_recalled, ws, stream),
+         "recall kernels");
+  return ok();
+}
+
 // ---- the host side: partial attention over the offloaded blocks ------------------------------
 
 static sa::HostAttnArgs host_args(const sa::Shape& s, int host_pages, int list_stride,

@@ -59,6 +59,16 @@ hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void
                        hipStream_t stream, bool sum_slices = true);
 QParts gemm_result(const GemmPlan& plan, int m, int n, int nprob, int prob, const float* q,
                    const float* ws);
+// ---- periodic recall: the plan (one wave per pair), then one workgroup per copied block -----
+// copies: [pairs][max_recall] int2 (pool page, host page); k_host/v_host device-addressable
+size_t recall_plan_lds_bytes(const Shape& s, int max_recall);
+hipError_t launch_recall(const Shape& s, int list_stride, int max_recall, const int* seq_lens,
+                         int* block_table, const int* gpu_blocks, const int* n_gpu,
+                         const int* cpu_blocks, const int* n_cpu, const void* k_host,
+                         const void* v_host, const int* host_table, int host_pages,
+                         void* k_pool, void* v_pool, int* n_recalled, void* copies,
+                         hipStream_t stream);
+
 // q_out[r][c] = the sum of the parts of q, for rows r < rows and columns c < n (n a multiple of
 // 4); q_out may be device-addressable host memory
 hipError_t launch_gather_query(const QParts& q, int rows, int n, float* q_out, hipStream_t stream);

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 6
+#define SA_ABI_VERSION 7
 
 typedef enum {
   SA_OK = 0,
@@ -392,6 +392,43 @@ sa_status sa_decode_step_offload(const sa_dims* dims, sa_digest_kind kind, int32
                                  int32_t num_layers, const sa_layer* layers, void* ws,
                                  size_t ws_bytes, hipStream_t stream, hipStream_t side_stream,
                                  sa_host_plan* plan, hipStream_t host_stream);
+
+/* ---------------------------------------------------------------------------------------
+ * sa_recall_blocks -- asynchronous periodic KV recall ([HTML Sec. 3.4]: at intervals,
+ * important blocks are brought back from host memory into GPU memory, so that the share of
+ * the budget the CPU attends stays below a threshold; the copy is issued after the layer's
+ * attention and is needed only at the same layer of the next decode step).
+ *
+ * For every (sequence s, KV head h), from one layer's current selection lists:
+ *   candidates: cpu_blocks[s][h][0 .. n_cpu) in list order, skipping entries outside the
+ *     sequence, already resident (block_table >= 0) or without a host page;
+ *   evictable: the resident blocks of the sequence (a page in [0, num_pages)) that are in
+ *     neither gpu_blocks[s][h][0 .. n_gpu) nor the cpu list, in ascending block order;
+ *   n = min(#candidates, #evictable, max_recall) blocks move: candidate t takes the page of
+ *     evictable block t (block_table: evicted -> -1, candidate -> the page), and its keys and
+ *     values are copied from the host store into that page, in the pool layouts
+ *     (sa_pack_k_pages / sa_pack_v_pages).  n_recalled[s][h] = n.
+ * Digests are not touched (a block's digest does not depend on where the block is held).
+ *
+ *   list_stride: the lists' row length (the selection's top_k).  seq_lens [B], block_table
+ *   [B][Hkv][max_blocks] (updated in place), the lists, k_pool, v_pool, n_recalled [B][Hkv]:
+ *   device memory.  k_host, v_host [host_pages][bs][d], KV dtype, token rows: page-locked
+ *   host memory the device reads (hipHostMalloc).  host_table [B][Hkv][max_blocks]: host
+ *   page of each block, or -1; device memory or page-locked host memory.
+ *   ws: sa_recall_workspace_bytes(dims, max_recall) (the copy list).
+ * Runs on `stream` (two launches); nothing else may read or write the layer's block table
+ * or pool pages meanwhile -- issue it on the stream of the layer's attention, after it, or
+ * order another stream after that attention and order the next use of the layer after it.
+ * max_recall in [1, 4096].
+ * ------------------------------------------------------------------------------------- */
+size_t sa_recall_workspace_bytes(const sa_dims* dims, int32_t max_recall);
+sa_status sa_recall_blocks(const sa_dims* dims, int32_t list_stride, int32_t max_recall,
+                           const int32_t* seq_lens, int32_t* block_table,
+                           const int32_t* gpu_blocks, const int32_t* n_gpu,
+                           const int32_t* cpu_blocks, const int32_t* n_cpu, const void* k_host,
+                           const void* v_host, const int32_t* host_table, int32_t host_pages,
+                           void* k_pool, void* v_pool, int32_t* n_recalled, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * sa_profile_attention -- kernel timing of the attention stage (GPUATTN).  After this call

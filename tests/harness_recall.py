@@ -1,0 +1,178 @@
+"""Parity harness for periodic recall (sa_recall_blocks) inside a multi-layer step.
+
+A step runs once (sa_decode_step, host partials given); its selection lists drive the
+recall of every layer.  The recall is checked against the oracle's recall_pair, bit for
+bit: the new block tables, the number of blocks moved, the recalled pages' keys and values
+(unpacked from the pool layouts in numpy and compared with the host store they were drawn
+into), and every page that did not move.  The step then runs again: its CPU share must
+fall, and its outputs must match the oracle's step over the new residency, whose keys and
+values come from the generators (the host store for recalled blocks, the pool draw for the
+rest), never from the device.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import harness as H
+import harness_step as HS
+from block_sparse_attention_digest_amd import binding as B
+from block_sparse_attention_digest_amd import workloads as wk
+from oracle import scout_oracle as so
+
+
+def unpack_k(pool_page: torch.Tensor, bs: int, d: int) -> torch.Tensor:
+    """Chunk-major [d/x][bs][x] -> token rows [bs][d] (x = 16 bytes of elements)."""
+    x = 16 // pool_page.element_size()
+    return pool_page.reshape(d // x, bs, x).permute(1, 0, 2).reshape(bs, d)
+
+
+def unpack_v(pool_page: torch.Tensor, bs: int, d: int) -> torch.Tensor:
+    """[bs/16][d][16] -> token rows [bs][d]."""
+    return pool_page.reshape(bs // 16, d, 16).permute(0, 2, 1).reshape(bs, d)
+
+
+def run_recall(wl: wk.Workload, max_recall: int):
+    dev = "cuda"
+    B_, Hkv, Hq, G, d, bs, k = (wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.group,
+                                wl.head_dim, wl.block_size, wl.top_k)
+    pairs = B_ * Hkv
+    i32, f32 = torch.int32, torch.float32
+    data = HS.prepare_step(wl, "cpu")
+    lens = wk.seq_lens(wl)
+    lens_d = lens.to(dev)
+    P = data[0]["pool"]["K"].shape[0]
+    dims = H.dims_for(wl, P)
+    dev_layers, stores = [], []
+    for i, Ld in enumerate(data):
+        dig = Ld["dig"].to(dev).contiguous()
+        k_pool = B.pack_k_pages(dims, Ld["pool"]["K"].to(dev))
+        B.sa_build_digests(dims, "mean", k_pool, Ld["pool"]["block_table"].to(dev), lens_d, dig)
+        dev_layers.append(dict(
+            x=Ld["X"].to(dev), w_q=B.pack_weight(Ld["W"].to(dev)), digests=dig,
+            block_table=Ld["pool"]["block_table"].to(dev).to(i32).contiguous(), k_pool=k_pool,
+            v_pool=B.pack_v_pages(dims, Ld["pool"]["V"].to(dev)),
+            host_o=Ld["host"]["o"].to(dev).contiguous(), host_m=Ld["host"]["m"].to(dev).contiguous(),
+            host_l=Ld["host"]["l"].to(dev).contiguous(),
+            gpu_blocks=torch.full((pairs, k), -7, dtype=i32, device=dev),
+            n_gpu=torch.full((pairs,), -7, dtype=i32, device=dev),
+            cpu_blocks=torch.full((pairs, k), -7, dtype=i32, device=dev),
+            n_cpu=torch.full((pairs,), -7, dtype=i32, device=dev),
+            out_o=torch.empty((B_, Hq, d), dtype=f32, device=dev),
+            out_m=torch.empty((B_, Hq), dtype=f32, device=dev),
+            out_l=torch.empty((B_, Hq), dtype=f32, device=dev)))
+        st = wk.draw_host_store(wl, i, Ld["off"])
+        kh = B.pinned_empty(tuple(st["K"].shape), st["K"].dtype)
+        vh = B.pinned_empty(tuple(st["V"].shape), st["V"].dtype)
+        kh.copy_(st["K"])
+        vh.copy_(st["V"])
+        stores.append(dict(K=kh, V=vh, table=st["table"], table_d=st["table"].to(dev)))
+    ws = B.workspace(B.sa_step_workspace_bytes(dims, wl.hidden, k))
+    side = torch.cuda.Stream()
+    B.sa_decode_step(dims, "mean", wl.hidden, k, wl.scale, lens_d, dev_layers, ws, side_stream=side)
+    torch.cuda.synchronize()
+    H.log("  first step done")
+    n_cpu_before = sum(int(e["n_cpu"].sum()) for e in dev_layers)
+
+    # ---------------- recall every layer, then check it against the oracle
+    tables_before = [e["block_table"].cpu().clone() for e in dev_layers]
+    kp_before = [e["k_pool"].cpu().clone() for e in dev_layers]
+    vp_before = [e["v_pool"].cpu().clone() for e in dev_layers]
+    rws = B.workspace(B.sa_recall_workspace_bytes(dims, max_recall))
+    moved_total = 0
+    new_tables = []
+    for i, e in enumerate(dev_layers):
+        n_rec = torch.full((pairs,), -7, dtype=i32, device=dev)
+        B.sa_recall_blocks(dims, k, max_recall, lens_d, e["block_table"], e["gpu_blocks"],
+                           e["n_gpu"], e["cpu_blocks"], e["n_cpu"], stores[i]["K"],
+                           stores[i]["V"], stores[i]["table_d"], e["k_pool"], e["v_pool"],
+                           n_rec, rws)
+        torch.cuda.synchronize()
+        tab = e["block_table"].cpu().view(pairs, -1)
+        tb0 = tables_before[i].view(pairs, -1)
+        kp, vp = e["k_pool"].cpu(), e["v_pool"].cpu()
+        moved_pages = set()
+        oracle_tab = torch.empty_like(tb0)
+        gl, cl = e["gpu_blocks"].cpu(), e["cpu_blocks"].cpu()
+        ngl, ncl = e["n_gpu"].cpu(), e["n_cpu"].cpu()
+        for p in range(pairs):
+            s, h = divmod(p, Hkv)
+            want_tab, moves = so.recall_pair(
+                tb0[p].numpy(), int(lens[s]), bs, gl[p, :int(ngl[p])].numpy(),
+                cl[p, :int(ncl[p])].numpy(), stores[i]["table"][s, h].numpy(), max_recall)
+            assert np.array_equal(tab[p].numpy(), want_tab), f"layer {i} pair {p}: table"
+            oracle_tab[p] = torch.from_numpy(want_tab.astype(np.int32))
+            assert int(n_rec[p]) == len(moves), f"layer {i} pair {p}: n_recalled"
+            for b, page, hp in moves:
+                assert torch.equal(unpack_k(kp[page], bs, d), stores[i]["K"][hp]), (i, p, b)
+                assert torch.equal(unpack_v(vp[page], bs, d), stores[i]["V"][hp]), (i, p, b)
+                moved_pages.add(page)
+            moved_total += len(moves)
+        keep = torch.tensor([pg not in moved_pages for pg in range(P)])
+        assert torch.equal(kp[keep], kp_before[i][keep]) and torch.equal(vp[keep], vp_before[i][keep])
+        new_tables.append(oracle_tab.view(B_, Hkv, -1))  # (equal to the device's, checked)
+    H.log(f"  recall: {moved_total} blocks moved, tables and pages match the oracle")
+
+    # ---------------- the step again, over the new residency
+    B.sa_decode_step(dims, "mean", wl.hidden, k, wl.scale, lens_d, dev_layers, ws, side_stream=side)
+    torch.cuda.synchronize()
+    n_cpu_after = sum(int(e["n_cpu"].sum()) for e in dev_layers)
+    H.log(f"  second step: offloaded selected blocks {n_cpu_before} -> {n_cpu_after}")
+    # the inputs are unchanged, so the selection is too: every recalled block is now a
+    # resident selected block, and no evicted block was selected
+    assert n_cpu_after == n_cpu_before - moved_total
+
+    max_err, ties = 0.0, 0
+    for p in range(pairs):
+        s, h = divmod(p, Hkv)
+        n = int(lens[s])
+        nb = so.num_blocks(n, bs)
+        olayers = []
+        for i, Ld in enumerate(data):
+            bt0 = tables_before[i].view(B_, Hkv, -1)[s, h]
+            bt1 = new_tables[i][s, h]
+            resident = (bt1[:nb] >= 0).numpy()
+            Kl = np.zeros((nb * bs, d))
+            Vl = np.zeros((nb * bs, d))
+            for b in np.nonzero(resident)[0]:
+                if int(bt0[b]) == int(bt1[b]):  # stayed: the pool draw
+                    Kl[b * bs:(b + 1) * bs] = wk.f64(Ld["pool"]["K"][int(bt0[b])])
+                    Vl[b * bs:(b + 1) * bs] = wk.f64(Ld["pool"]["V"][int(bt0[b])])
+                else:                            # recalled: the host store's copy
+                    hp = int(stores[i]["table"][s, h, b])
+                    Kl[b * bs:(b + 1) * bs] = wk.f64(stores[i]["K"][hp])
+                    Vl[b * bs:(b + 1) * bs] = wk.f64(stores[i]["V"][hp])
+            # digests: the pool blocks' digests were rebuilt from the pool keys before the
+            # recall and the recall does not touch them
+            dig = wk.f64(Ld["dig"][s, h, :nb])
+            res0 = (bt0[:nb] >= 0).numpy()
+            K0 = np.zeros((nb * bs, d))
+            for b in np.nonzero(res0)[0]:
+                K0[b * bs:(b + 1) * bs] = wk.f64(Ld["pool"]["K"][int(bt0[b])])
+            full = so.digest_mean(K0, n, bs, wl.kv_dtype)
+            dig[np.nonzero(res0)[0]] = full[np.nonzero(res0)[0]]
+            host = [so.Partial(wk.f64(Ld["host"]["o"][s, h * G + j]),
+                               float(Ld["host"]["m"][s, h * G + j]),
+                               float(Ld["host"]["l"][s, h * G + j])) for j in range(G)]
+            olayers.append(dict(X=wk.f64(Ld["X"]), W=wk.f64(Ld["W"]), digest=dig,
+                                resident=resident, K=Kl, V=Vl, seq_len=n, host=host))
+        want = so.decode_step_pair(olayers, s, h, G, d, bs, k, wl.scale, "mean")
+        for i, e in enumerate(dev_layers):
+            ng, nc = int(e["n_gpu"][p]), int(e["n_cpu"][p])
+            gbl = e["gpu_blocks"][p].cpu().numpy()
+            cbl = e["cpu_blocks"][p].cpu().numpy()
+            sel = np.sort(np.concatenate([gbl[:ng], cbl[:nc]]))
+            if not H.selection_matches(sel, want[i].selected, want[i].scores, min(k, nb)):
+                ties += 1
+                continue
+            assert np.array_equal(gbl[:ng], want[i].gpu_blocks)
+            o = e["out_o"][s, h * G:(h + 1) * G].cpu().double().numpy()
+            m = e["out_m"][s, h * G:(h + 1) * G].cpu().double().numpy()
+            l = e["out_l"][s, h * G:(h + 1) * G].cpu().double().numpy()
+            for j in range(G):
+                max_err = max(max_err, H.compare_partial(o[j], m[j], l[j], want[i].out[j],
+                                                         H.attn_tol(wl), f"layer {i} pair {p}"))
+    assert ties <= max(1, pairs * len(data) // 100)
+    H.log(f"  second step matches the oracle: max_err={max_err:.2e} ties={ties}")
+    return dict(moved=moved_total, n_cpu_before=n_cpu_before, n_cpu_after=n_cpu_after)

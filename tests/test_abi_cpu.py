@@ -35,7 +35,7 @@ def test_header_declares_the_path(lib):
               "sa_select_blocks", "sa_sparse_decode", "sa_merge", "sa_decode_attend_merge",
               "sa_decode_step", "sa_host_partial_attention", "sa_refresh_last_digests",
               "sa_host_plan_create", "sa_host_plan_destroy", "sa_host_plan_stats",
-              "sa_host_plan_run",
+              "sa_host_plan_run", "sa_recall_blocks", "sa_recall_workspace_bytes",
               "sa_decode_step_offload"):
         assert n in names
 
@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.sa_abi_version() == B.ABI_VERSION == 6
+    assert lib.sa_abi_version() == B.ABI_VERSION == 7
     assert lib.sa_status_string(B.SA_ERR_WORKSPACE) == b"SA_ERR_WORKSPACE"
 
 
@@ -270,6 +270,36 @@ def test_offload_step_validation(lib):
                                   ws, None, None) == B.SA_ERR_INVALID_ARG
     finally:
         assert lib.sa_host_plan_destroy(plan) == B.SA_OK
+
+
+@no_gpu
+def test_recall_validation(lib):
+    d = dims()
+    ws = lib.sa_recall_workspace_bytes(ctypes.byref(d), 8)
+    assert ws >= 2 * 2 * 8 * 4
+    assert lib.sa_recall_workspace_bytes(ctypes.byref(d), 0) == 0
+    assert lib.sa_recall_workspace_bytes(ctypes.byref(d), 5000) == 0
+
+    def call(stride=8, maxr=8, hp=16, ws_=ws, **null):
+        args = dict(seq_lens=FAKE, block_table=FAKE, gpu_blocks=FAKE, n_gpu=FAKE,
+                    cpu_blocks=FAKE, n_cpu=FAKE, k_host=FAKE, v_host=FAKE, host_table=FAKE,
+                    k_pool=FAKE, v_pool=FAKE, n_recalled=FAKE)
+        args.update(null)
+        a = args
+        return lib.sa_recall_blocks(ctypes.byref(d), stride, maxr, a["seq_lens"],
+                                    a["block_table"], a["gpu_blocks"], a["n_gpu"],
+                                    a["cpu_blocks"], a["n_cpu"], a["k_host"], a["v_host"],
+                                    a["host_table"], hp, a["k_pool"], a["v_pool"],
+                                    a["n_recalled"], FAKE, ws_, None)
+
+    assert call(stride=0) == B.SA_ERR_INVALID_ARG
+    assert call(stride=65) == B.SA_ERR_INVALID_ARG
+    assert call(maxr=0) == B.SA_ERR_INVALID_ARG
+    assert call(hp=0) == B.SA_ERR_INVALID_ARG
+    assert call(ws_=ws - 1) == B.SA_ERR_WORKSPACE
+    for name in ("seq_lens", "block_table", "cpu_blocks", "k_host", "host_table", "v_pool",
+                 "n_recalled"):
+        assert call(**{name: None}) == B.SA_ERR_INVALID_ARG, name
 
 
 def test_binding_requires_the_library(monkeypatch, tmp_path):

@@ -274,6 +274,18 @@ def test_step_offload_parity_one_stream_one_thread():
     assert r["cpu_ratio"] > 0.1
 
 
+@pytest.mark.parametrize("pool,max_recall", [(6, 64), (12, 2), (12, 64)])
+def test_recall_parity(pool, max_recall):
+    """Periodic recall of every layer after a step: tables, moved pages and untouched pages
+    against the oracle bit for bit, then the next step over the new residency."""
+    H.log(f"[case] recall pool={pool} max_recall={max_recall}")
+    import harness_recall as HR
+    r = HR.run_recall(wk.QWEN3_14B_STEP.scaled(batch=3, num_q_heads=10, num_kv_heads=2,
+                                                context=2000, layers=2, pool_blocks=pool,
+                                                hidden=512, top_k=8), max_recall)
+    assert r["moved"] > 0
+
+
 def test_step_parity_minmax_no_handoff():
     H.log("[case] step minmax")
     import harness_step as HS
