@@ -17,9 +17,11 @@ inside eager steps (sharing the GPU with the side stream) and launched alone; an
 oracle timed on a bounded sample of the same workload.  In the timed step the host partials
 are given (seeded); with --offload the line also carries "offload": the same step with
 its CPU side computed by host threads one layer ahead (sa_decode_step_offload) from an
-aliased host KV store, and the share of that step the GPU spends waiting for it.
+aliased host KV store, and the share of that step the GPU spends waiting for it; with
+--recall, "recall": one periodic recall of every layer (sa_recall_blocks) over the host
+link, the CPU share before and after, and (with --offload) the offload step again.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-graph] [--offload]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-graph] [--offload] [--recall]
 """
 
 from __future__ import annotations
@@ -63,6 +65,10 @@ def parse():
                     help="host worker threads of the offload step (at most the CPUs present)")
     ap.add_argument("--host-pages", type=int, default=32768,
                     help="pages of the aliased host KV store of the offload step")
+    ap.add_argument("--recall", action="store_true",
+                    help="after the GPU path (and --offload), recall every layer's offloaded "
+                         "selected blocks from the host store (sa_recall_blocks), reported as "
+                         "\"recall\"; with --offload the offload step is timed again after it")
     ap.add_argument("--pool-blocks", type=int, default=None,
                     help="resident pool blocks per (sequence, KV head) instead of the "
                          "workload's 128 (a study of the CPU share; not the headline workload)")
@@ -226,7 +232,55 @@ def cpu_baseline(wl_full, budget_s):
 
 # ---------------------------------------------------------------------------------------
 
-def offload_measure(wl, dims, lens, layers, ws, side_stream, ms_gpu, args, torch, B, wk):
+def host_store(wl, args, B, wk):
+    """The aliased host KV store (draw_host_store_aliased) in page-locked memory, which the
+    host workers read and the recall kernels read over the host link."""
+    t0 = time.time()
+    st = wk.draw_host_store_aliased(wl, args.host_pages)
+    K = B.pinned_empty(tuple(st["K"].shape), st["K"].dtype)
+    V = B.pinned_empty(tuple(st["V"].shape), st["V"].dtype)
+    K.copy_(st["K"])
+    V.copy_(st["V"])
+    log(f"host store of {args.host_pages} pages ready ({time.time() - t0:.1f} s)")
+    return {"K": K, "V": V, "table": st["table"]}
+
+
+def recall_measure(wl, dims, lens, layers, store, torch, B):
+    """Periodic recall (sa_recall_blocks) of every layer, from the lists of the last step:
+    each layer's offloaded selected blocks move into pages of resident blocks no longer
+    selected, read from the page-locked host store over the host link.  Timed per layer with
+    HIP events; then one step shows the CPU share that is left."""
+    Bsz, Hkv, bs, d, k = wl.batch, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.top_k
+    pairs = Bsz * Hkv
+    table_d = store["table"].to("cuda")
+    rws = B.workspace(B.sa_recall_workspace_bytes(dims, k))
+    n_rec = torch.empty(pairs, dtype=torch.int32, device="cuda")
+    share0 = sum(int(L["n_cpu"].sum()) for L in layers) / (wl.layers * pairs * k)
+    torch.cuda.synchronize()
+    ms, moved = [], 0
+    for L in layers:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        B.sa_recall_blocks(dims, k, k, lens, L["block_table"], L["gpu_blocks"], L["n_gpu"],
+                           L["cpu_blocks"], L["n_cpu"], store["K"], store["V"], table_d,
+                           L["k_pool"], L["v_pool"], n_rec, rws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+        moved += int(n_rec.sum())
+    el = 2 if wl.kv_dtype == "bf16" else 4
+    nbytes = moved * 2 * bs * d * el
+    total_ms = sum(ms)
+    log(f"recall: {moved} blocks, {nbytes / 1e6:.1f} MB in {total_ms:.2f} ms "
+        f"({nbytes / (total_ms * 1e-3) / 1e9:.1f} GB/s)")
+    return {"blocks_moved": moved, "bytes_moved": nbytes,
+            "ms_per_layer": round(total_ms / len(ms), 4),
+            "host_link_gbs": round(nbytes / (total_ms * 1e-3) / 1e9, 2),
+            "cpu_share_before": round(share0, 4)}
+
+
+def offload_measure(wl, dims, lens, layers, ws, side_stream, ms_gpu, args, torch, B, wk,
+                    store=None):
     """The same step with its CPU side computed, not given: sa_decode_step_offload runs each
     layer's host partial on host threads one layer ahead (Algorithm 1) and makes the merge
     wait for it.  The host KV is an aliased store (draw_host_store_aliased): the 64K-token
@@ -237,7 +291,8 @@ def offload_measure(wl, dims, lens, layers, ws, side_stream, ms_gpu, args, torch
     f32 = torch.float32
     threads = max(1, min(args.host_threads, os.cpu_count() or 1))
     t0 = time.time()
-    store = wk.draw_host_store_aliased(wl, args.host_pages)
+    if store is None:
+        store = wk.draw_host_store_aliased(wl, args.host_pages)
     hls = [dict(k_host=store["K"], v_host=store["V"], host_table=store["table"],
                 q_host=B.pinned_empty((Bsz, Hq, d), f32),
                 cpu_blocks_host=B.pinned_empty((pairs, k)), n_cpu_host=B.pinned_empty((pairs,)),
@@ -474,9 +529,33 @@ def main():
                               "avg_launch_us": round(iso_avg_ms * 1e3, 2),
                               "algorithmic_bytes_per_launch": int(iso_bytes_avg)},
     }
+    store = host_store(wl, args, B, wk) if args.recall else None
     if args.offload:
         result["offload"] = offload_measure(wl, dims, lens, layers, ws, side_stream, ms_step,
-                                            args, torch, B, wk)
+                                            args, torch, B, wk, store)
+    if args.recall:
+        rec = recall_measure(wl, dims, lens, layers, store, torch, B)
+        step()  # the next step over the new residency
+        torch.cuda.synchronize()
+        rec["cpu_share_after"] = round(
+            sum(int(L["n_cpu"].sum()) for L in layers) / (wl.layers * wl.batch * wl.num_kv_heads
+                                                          * wl.top_k), 4)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        rec["gpu_only_ms_per_step_after"] = round(e0.elapsed_time(e1) / args.steps, 4)
+        rec["after_launch"] = "eager"
+        rec["note"] = ("one recall of every layer from the last step's lists; the inputs do "
+                       "not change between steps here, so the selection does not drift and "
+                       "the CPU share after the recall is what the pool's free pages allow")
+        if args.offload:
+            ms_after = rec["gpu_only_ms_per_step_after"]
+            rec["offload_after"] = offload_measure(wl, dims, lens, layers, ws, side_stream,
+                                                   ms_after, args, torch, B, wk, store)
+        result["recall"] = rec
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
