@@ -19,9 +19,11 @@ are given (seeded); with --offload the line also carries "offload": the same ste
 its CPU side computed by host threads one layer ahead (sa_decode_step_offload) from an
 aliased host KV store, and the share of that step the GPU spends waiting for it; with
 --recall, "recall": one periodic recall of every layer (sa_recall_blocks) over the host
-link, the CPU share before and after, and (with --offload) the offload step again.
+link, the CPU share before and after, and (with --offload) the offload step again; with
+--dense, "dense": FullKV attention over one layer's whole 64K context (sa_dense_decode).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-graph] [--offload] [--recall]
+                    [--dense]
 """
 
 from __future__ import annotations
@@ -69,6 +71,9 @@ def parse():
                     help="after the GPU path (and --offload), recall every layer's offloaded "
                          "selected blocks from the host store (sa_recall_blocks), reported as "
                          "\"recall\"; with --offload the offload step is timed again after it")
+    ap.add_argument("--dense", action="store_true",
+                    help="also time dense (FullKV) attention over one layer of the workload's "
+                         "whole context (sa_dense_decode), reported as \"dense\"")
     ap.add_argument("--pool-blocks", type=int, default=None,
                     help="resident pool blocks per (sequence, KV head) instead of the "
                          "workload's 128 (a study of the CPU share; not the headline workload)")
@@ -277,6 +282,71 @@ def recall_measure(wl, dims, lens, layers, store, torch, B):
             "ms_per_layer": round(total_ms / len(ms), 4),
             "host_link_gbs": round(nbytes / (total_ms * 1e-3) / 1e9, 2),
             "cpu_share_before": round(share0, 4)}
+
+
+def dense_measure(wl, args, torch, B, wk, sparse_us):
+    """FullKV attention of one layer of the workload (every block of the 64K context
+    resident, 10.7 GB of K and V) with sa_dense_decode, next to the sparse path's attention
+    of the same layer.  Keys and values are drawn on the device (N(0, 1), bf16)."""
+    dev = "cuda"
+    Bsz, Hq, Hkv, d, bs = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+    nb = wl.max_blocks
+    P = Bsz * Hkv * nb
+    dims = B.Dims(Bsz, Hq, Hkv, d, bs, nb, P, B.SA_BF16)
+    g = torch.Generator(device=dev)
+    g.manual_seed(20240)
+    t0 = time.time()
+
+    def pool(pack):
+        rows = torch.empty((P, bs, d), dtype=torch.bfloat16, device=dev)
+        step = 1 << 15
+        for p0 in range(0, P, step):
+            p1 = min(P, p0 + step)
+            rows[p0:p1] = torch.randn((p1 - p0, bs, d), generator=g, device=dev).to(torch.bfloat16)
+        out = pack(dims, rows)
+        del rows
+        return out
+
+    k_pool = pool(B.pack_k_pages)
+    v_pool = pool(B.pack_v_pages)
+    perm = torch.randperm(P, generator=g, device=dev).to(torch.int32)
+    table = perm.view(Bsz, Hkv, nb).contiguous()
+    lens = torch.full((Bsz,), wl.context, dtype=torch.int32, device=dev)
+    q = torch.randn((Bsz, Hq, d), generator=g, device=dev)
+    o = torch.empty((Bsz, Hq, d), device=dev)
+    m = torch.empty((Bsz, Hq), device=dev)
+    l = torch.empty_like(m)
+    ws = B.workspace(B.sa_dense_workspace_bytes(dims))
+    torch.cuda.synchronize()
+    log(f"dense: one layer's full KV ready ({time.time() - t0:.1f} s)")
+
+    def run():
+        B.sa_dense_decode(dims, q, k_pool, v_pool, table, lens, wl.scale, o, m, l, ws)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    n = max(3, args.steps // 2)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    kv_bytes = 2 * Bsz * Hkv * wl.context * d * 2
+    io_bytes = Bsz * Hq * d * 4 + Bsz * Hq * (d + 2) * 4
+    gbs = (kv_bytes + io_bytes) / (ms * 1e-3) / 1e9
+    log(f"dense: {ms:.3f} ms per layer, {gbs:.0f} GB/s")
+    out = {"ms_per_layer": round(ms, 4), "hbm_gbs": round(gbs, 1),
+           "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "kv_bytes": kv_bytes,
+           "sparse_attention_us_alone": round(sparse_us, 2),
+           "dense_over_sparse_attention": round(ms * 1e3 / sparse_us, 1),
+           "note": "one layer, 40 sequences x 65536 tokens, every block resident; the "
+                   "sparse figure is the same layer's block-sparse attention launched alone"}
+    del k_pool, v_pool
+    torch.cuda.empty_cache()
+    return out
 
 
 def offload_measure(wl, dims, lens, layers, ws, side_stream, ms_gpu, args, torch, B, wk,
@@ -529,6 +599,8 @@ def main():
                               "avg_launch_us": round(iso_avg_ms * 1e3, 2),
                               "algorithmic_bytes_per_launch": int(iso_bytes_avg)},
     }
+    if args.dense:
+        result["dense"] = dense_measure(wl, args, torch, B, wk, iso_avg_ms * 1e3)
     store = host_store(wl, args, B, wk) if args.recall else None
     if args.offload:
         result["offload"] = offload_measure(wl, dims, lens, layers, ws, side_stream, ms_step,

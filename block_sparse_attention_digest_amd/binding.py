@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libscoutattn.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = 0, -1, -2, -3, -4
 SA_F32, SA_BF16 = 0, 1
 SA_DIGEST_MEAN, SA_DIGEST_MINMAX = 0, 1
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 KIND = {"mean": SA_DIGEST_MEAN, "minmax": SA_DIGEST_MINMAX}
 
@@ -82,6 +82,8 @@ SIGNATURES = {
     "sa_decode_step": (ctypes.c_int, [_D, ctypes.c_int, _I, _I, _F, _P, _I,
                                       ctypes.POINTER(sa_layer), _P, _Z, _P, _P]),
     "sa_profile_attention": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.POINTER(_P), _I]),
+    "sa_dense_workspace_bytes": (_Z, [_D]),
+    "sa_dense_decode": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _F, _P, _P, _P, _P, _Z, _P]),
     "sa_recall_workspace_bytes": (_Z, [_D, _I]),
     "sa_recall_blocks": (ctypes.c_int, [_D, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P,
                                         _P, _P, _P, _Z, _P]),
@@ -400,6 +402,27 @@ def sa_decode_step(dims: Dims, kind: str, hidden: int, top_k: int, scale: float,
         _ptr(seq_lens, torch.int32, dims.batch, "seq_lens"), len(layers), arr,
         _ptr(ws, torch.uint8, name="ws"), ws.numel(), _stream(stream),
         None if side_stream is None else _stream(side_stream)))
+
+
+def sa_dense_workspace_bytes(dims: Dims) -> int:
+    return lib().sa_dense_workspace_bytes(ctypes.byref(dims.c()))
+
+
+def sa_dense_decode(dims: Dims, q, k_pool, v_pool, block_table, seq_lens, scale: float, o,
+                    m=None, l=None, ws=None, stream=None):
+    """FullKV attention over every resident block (GPU tensors)."""
+    B_, Hq, Hkv, d = dims.batch, dims.num_q_heads, dims.num_kv_heads, dims.head_dim
+    f32, i32 = torch.float32, torch.int32
+    n = dims.num_pages * dims.block_size * d
+    if ws is None:
+        ws = workspace(sa_dense_workspace_bytes(dims))
+    _check(lib().sa_dense_decode(
+        ctypes.byref(dims.c()), _ptr(q, f32, B_ * Hq * d, "q"),
+        _ptr(k_pool, dims.kv_torch, n, "k_pool"), _ptr(v_pool, dims.kv_torch, n, "v_pool"),
+        _ptr(block_table, i32, B_ * Hkv * dims.max_blocks, "block_table"),
+        _ptr(seq_lens, i32, B_, "seq_lens"), scale, _ptr(o, f32, B_ * Hq * d, "o"),
+        _ptr(m, f32, B_ * Hq, "m"), _ptr(l, f32, B_ * Hq, "l"), _ptr(ws, torch.uint8, name="ws"),
+        ws.numel(), _stream(stream)))
 
 
 def sa_recall_blocks(dims: Dims, list_stride: int, max_recall: int, seq_lens, block_table,

@@ -419,6 +419,53 @@ sa_status sa_merge(int32_t rows, int32_t d, const float* o_a, const float* m_a,
   return ok();
 }
 
+// ---- dense (FullKV) attention -----------------------------------------------------------------
+
+// workspace: the lists [pairs][max_blocks], the counts [pairs], then the attention partials
+static size_t dense_lists_bytes(const sa::Shape& s) {
+  return align_up((size_t)s.B * s.Hkv * (s.max_blocks + 1) * sizeof(int32_t));
+}
+
+size_t sa_dense_workspace_bytes(const sa_dims* dims) {
+  sa::Shape s;
+  if (check_dims(dims, &s) != SA_OK) return 0;
+  return dense_lists_bytes(s) + layout(s, s.max_blocks).total;
+}
+
+sa_status sa_dense_decode(const sa_dims* dims, const float* q, const void* k_pool,
+                          const void* v_pool, const int32_t* block_table,
+                          const int32_t* seq_lens, float scale, float* o, float* m, float* l,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  sa::Shape s;
+  SA_CHECK(check_dims(dims, &s));
+  SA_CHECK(check_scale(scale));
+  SA_NOT_NULL(q);
+  SA_NOT_NULL(k_pool);
+  SA_NOT_NULL(v_pool);
+  SA_NOT_NULL(block_table);
+  SA_NOT_NULL(seq_lens);
+  SA_NOT_NULL(o);
+  const size_t need = sa_dense_workspace_bytes(dims);
+  if (!ws || ws_bytes < need)
+    return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
+  int32_t* lists = (int32_t*)ws;
+  int32_t* counts = lists + (size_t)s.B * s.Hkv * s.max_blocks;
+  float* parts = (float*)((char*)ws + dense_lists_bytes(s));
+  const Layout L = layout(s, s.max_blocks);
+  SA_HIP(sa::launch_dense_lists(s, seq_lens, block_table, lists, counts, stream),
+         "dense list kernel");
+  hipEvent_t e0, e1;
+  next_profile_events(&e0, &e1);
+  SA_HIP(sa::launch_attention(s, L.plan, sa::plain_query(q, s.Hq * s.d), k_pool, v_pool,
+                              block_table, seq_lens, lists, nullptr, counts, s.max_blocks, scale,
+                              parts, stream, e0, e1),
+         "attention kernel");
+  SA_HIP(sa::launch_reduce(s, L.plan, counts, parts, nullptr, nullptr, nullptr, nullptr, o, m, l,
+                           stream),
+         "reduce kernel");
+  return ok();
+}
+
 // ---- periodic recall -------------------------------------------------------------------------
 
 static constexpr int kMaxRecall = 4096;

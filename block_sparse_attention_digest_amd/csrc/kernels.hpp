@@ -59,6 +59,11 @@ hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void
                        hipStream_t stream, bool sum_slices = true);
 QParts gemm_result(const GemmPlan& plan, int m, int n, int nprob, int prob, const float* q,
                    const float* ws);
+// ---- dense attention: the list of every resident block per pair ---------------------------
+// lists [pairs][max_blocks] (ascending, unused entries untouched), counts [pairs]
+hipError_t launch_dense_lists(const Shape& s, const int* seq_lens, const int* block_table,
+                              int* lists, int* counts, hipStream_t stream);
+
 // ---- periodic recall: the plan (one wave per pair), then one workgroup per copied block -----
 // copies: [pairs][max_recall] int2 (pool page, host page); k_host/v_host device-addressable
 size_t recall_plan_lds_bytes(const Shape& s, int max_recall);

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 7
+#define SA_ABI_VERSION 8
 
 typedef enum {
   SA_OK = 0,
@@ -392,6 +392,22 @@ sa_status sa_decode_step_offload(const sa_dims* dims, sa_digest_kind kind, int32
                                  int32_t num_layers, const sa_layer* layers, void* ws,
                                  size_t ws_bytes, hipStream_t stream, hipStream_t side_stream,
                                  sa_host_plan* plan, hipStream_t host_stream);
+
+/* ---------------------------------------------------------------------------------------
+ * sa_dense_decode -- dense paged decode attention (FullKV, the pages' uncompressed baseline
+ * [HTML Sec. 4]): for every query head g of sequence s, softmax attention over the valid
+ * tokens of every block b < nb_s whose block_table entry is a page in [0, num_pages), in the
+ * form of sa_sparse_decode's result (o normalised, m natural-log units, l; no block gives
+ * o = 0, m = -inf, l = 0).  With every block resident this is plain attention over the whole
+ * context.  Arguments as for sa_sparse_decode, with no lists; m and l may be NULL.
+ * ws: sa_dense_workspace_bytes(dims) (the lists of every resident block, then the attention
+ * partials).
+ * ------------------------------------------------------------------------------------- */
+size_t sa_dense_workspace_bytes(const sa_dims* dims);
+sa_status sa_dense_decode(const sa_dims* dims, const float* q, const void* k_pool,
+                          const void* v_pool, const int32_t* block_table,
+                          const int32_t* seq_lens, float scale, float* o, float* m, float* l,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * sa_recall_blocks -- asynchronous periodic KV recall ([HTML Sec. 3.4]: at intervals,

@@ -36,6 +36,7 @@ def test_header_declares_the_path(lib):
               "sa_decode_step", "sa_host_partial_attention", "sa_refresh_last_digests",
               "sa_host_plan_create", "sa_host_plan_destroy", "sa_host_plan_stats",
               "sa_host_plan_run", "sa_recall_blocks", "sa_recall_workspace_bytes",
+              "sa_dense_decode", "sa_dense_workspace_bytes",
               "sa_decode_step_offload"):
         assert n in names
 
@@ -47,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.sa_abi_version() == B.ABI_VERSION == 7
+    assert lib.sa_abi_version() == B.ABI_VERSION == 8
     assert lib.sa_status_string(B.SA_ERR_WORKSPACE) == b"SA_ERR_WORKSPACE"
 
 

@@ -293,3 +293,54 @@ def test_step_parity_minmax_no_handoff():
                                          layers=3, pool_blocks=8, hidden=256, top_k=4,
                                          digest_kinds=("minmax",)),
                 gen_device="cpu", handoff=False, side=False, kind="minmax")
+
+
+@pytest.mark.parametrize("name,wl,drop", [
+    ("f32-tiny", wk.TINY, 0.0),
+    ("bf16-ragged-bs16", wk.RAGGED.scaled(batch=6, ctx_min=1, ctx_max=2500), 0.0),
+    ("bf16-ragged-bs32", wk.RAGGED.scaled(batch=4, ctx_min=40, ctx_max=3000, block_size=32,
+                                          top_k=64), 0.0),
+    ("bf16-some-blocks-without-page", wk.RAGGED.scaled(batch=5, ctx_min=1, ctx_max=1500), 0.3),
+])
+def test_dense_parity(name, wl, drop):
+    """FullKV (sa_dense_decode) against the oracle's dense attention over the whole context;
+    with blocks left without a page, against attention over the blocks that have one."""
+    H.log(f"[case] dense {name}")
+    lens = wk.seq_lens(wl)
+    kv = wk.draw_kv_pages(wl, lens, "cpu")
+    table = kv["table"].clone()
+    if drop:
+        g = wk.generator(wl, "dense_drop", "cpu")
+        gone = (torch.rand(table.shape, generator=g) < drop) & (table >= 0)
+        table[gone] = -1
+        table[0, 0, :] = -1  # one pair with nothing: the empty partial
+    q = wk.draw_queries(wl, "cpu")["Q"]
+    P = kv["K"].shape[0]
+    dims = H.dims_for(wl, P)
+    dev = "cuda"
+    o = torch.full((wl.batch, wl.num_q_heads, wl.head_dim), float("nan"), device=dev)
+    m = torch.full((wl.batch, wl.num_q_heads), float("nan"), device=dev)
+    l = torch.full_like(m, float("nan"))
+    B.sa_dense_decode(dims, q.to(dev), B.pack_k_pages(dims, kv["K"].to(dev)),
+                      B.pack_v_pages(dims, kv["V"].to(dev)), table.to(dev), lens.to(dev),
+                      wl.scale, o, m, l)
+    torch.cuda.synchronize()
+    o, m, l = o.cpu().double().numpy(), m.cpu().double().numpy(), l.cpu().double().numpy()
+    G, bs = wl.group, wl.block_size
+    max_err = 0.0
+    for s in range(wl.batch):
+        n = int(lens[s])
+        for h in range(wl.num_kv_heads):
+            K = wk.f64(wk.logical_rows(kv["K"], kv["table"][s, h], n))
+            V = wk.f64(wk.logical_rows(kv["V"], kv["table"][s, h], n))
+            blocks = [b for b in range(so.num_blocks(n, bs)) if int(table[s, h, b]) >= 0]
+            for j in range(G):
+                qh = h * G + j
+                qv = q[s, qh].double().numpy()
+                if drop:
+                    want = so.attend_blocks(qv, K, V, blocks, n, bs, wl.scale)
+                else:
+                    want = so.dense_attention(qv, K, V, n, wl.scale)
+                max_err = max(max_err, H.compare_partial(o[s, qh], m[s, qh], l[s, qh], want,
+                                                         H.attn_tol(wl), f"seq {s} head {qh}"))
+    H.log(f"  dense {name}: max_err={max_err:.2e}")
