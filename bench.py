@@ -74,6 +74,10 @@ def parse():
     ap.add_argument("--dense", action="store_true",
                     help="also time dense (FullKV) attention over one layer of the workload's "
                          "whole context (sa_dense_decode), reported as \"dense\"")
+    ap.add_argument("--block-size", type=int, default=None, choices=(16, 32),
+                    help="KV block size instead of the workload's 32, with the token budget "
+                         "and the resident pool kept in tokens (a study of the digest "
+                         "granularity; not the headline workload)")
     ap.add_argument("--pool-blocks", type=int, default=None,
                     help="resident pool blocks per (sequence, KV head) instead of the "
                          "workload's 128 (a study of the CPU share; not the headline workload)")
@@ -452,6 +456,10 @@ def main():
     wl = wk.QWEN3_14B_STEP
     if args.pool_blocks is not None:
         wl = wl.scaled(pool_blocks=args.pool_blocks)
+    if args.block_size is not None and args.block_size != wl.block_size:
+        f = wl.block_size // args.block_size  # budget and pool kept in tokens
+        wl = wl.scaled(block_size=args.block_size, top_k=wl.top_k * f,
+                       pool_blocks=wl.pool_blocks * f)
     log(f"workload {wl.name}: setup")
     dims, lens, layers, ws = setup(wl, torch, B, wk)
     side_stream = torch.cuda.Stream()
