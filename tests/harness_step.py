@@ -57,11 +57,13 @@ def prepare_step(wl, gen_device, kind="mean"):
 
 
 def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs_to_check=None,
-             side=True, offload=False, host_threads=4):
+             side=True, offload=False, host_threads=4, store="full", host_pages=32768):
     """handoff: give every layer host mirrors of its offloaded lists; side: run the
     layer-ahead work on a side stream; offload: compute the CPU side with host tasks
     (sa_decode_step_offload) from a host store of every block, instead of merging the
-    drawn host partials."""
+    drawn host partials.  store: "full" gives every block its own host page
+    (draw_host_store); "aliased" maps every block into one pool of host_pages pages shared by
+    all layers (draw_host_store_aliased), for shapes whose offloaded KV would not fit."""
     dev = "cuda"
     B_, Hkv, Hq, G, d, bs, k = (wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.group,
                                 wl.head_dim, wl.block_size, wl.top_k)
@@ -102,7 +104,11 @@ def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs
     side_stream = torch.cuda.Stream() if side else None
     stores = host_layers = None
     if offload:
-        stores = [wk.draw_host_store(wl, i, Ld["off"]) for i, Ld in enumerate(data)]
+        if store == "aliased":
+            shared = wk.draw_host_store_aliased(wl, host_pages)
+            stores = [shared] * len(data)
+        else:
+            stores = [wk.draw_host_store(wl, i, Ld["off"]) for i, Ld in enumerate(data)]
         host_layers = []
         for st in stores:
             host_layers.append(dict(
@@ -155,11 +161,20 @@ def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs
             dig[res_blocks] = full[res_blocks]
             OL = dict(X=wk.f64(Ld["X"]), W=wk.f64(Ld["W"]), digest=dig, resident=resident,
                       K=Kl, V=Vl, seq_len=n)
-            if offload:  # the host's copy of every block; the oracle attends the offloaded ones
+            if offload:  # the host's copy of the blocks; the oracle attends the offloaded ones
                 st = stores[i]
-                pg = st["table"][s, h, :nb].long()
-                OL["K_host"] = wk.f64(st["K"][pg]).reshape(nb * bs, d)
-                OL["V_host"] = wk.f64(st["V"][pg]).reshape(nb * bs, d)
+                Kh = np.zeros((nb * bs, d))
+                Vh = np.zeros((nb * bs, d))
+                # rows of the blocks the step handed to the CPU (a selection the oracle makes
+                # differently is a tie and skipped below); the rest are never read
+                e = dev_layers[i]
+                nc_ = int(e["n_cpu"][p])
+                for b in e["cpu_blocks"][p, :nc_].cpu().tolist():
+                    hp = int(st["table"][s, h, b])
+                    Kh[b * bs:(b + 1) * bs] = wk.f64(st["K"][hp])
+                    Vh[b * bs:(b + 1) * bs] = wk.f64(st["V"][hp])
+                OL["K_host"] = Kh
+                OL["V_host"] = Vh
             else:
                 OL["host"] = [so.Partial(wk.f64(Ld["host"]["o"][s, h * G + j]),
                                          float(Ld["host"]["m"][s, h * G + j]),

@@ -56,3 +56,52 @@ def test_step_fullsize():
     import harness_step as HS
     r = HS.run_step(wl, gen_device="cuda", handoff=True, pairs_to_check=sample_pairs(wl, 6, 5))
     assert 0.0 < r["cpu_ratio"] < 0.5
+
+
+def test_step_offload_fullsize():
+    """The benchmark's step with its CPU side computed by host tasks one layer ahead, from an
+    aliased host store (as bench.py --offload), sampled pairs through every layer: the query
+    handed over, the host partials and the merged outputs."""
+    wl = wk.QWEN3_14B_STEP
+    H.log(f"[case] full size offload step {wl.name}")
+    import harness_step as HS
+    r = HS.run_step(wl, gen_device="cuda", offload=True, store="aliased", host_threads=16,
+                    pairs_to_check=sample_pairs(wl, 3, 9))
+    assert 0.0 < r["cpu_ratio"] < 0.5
+
+
+def test_dense_fullsize():
+    """FullKV over one layer of the benchmark shape (40 sequences x 65536 tokens, every block
+    resident, as bench.py --dense): sampled (sequence, query head) rows against the oracle's
+    dense attention over the whole context."""
+    from oracle import scout_oracle as so
+    wl = wk.QWEN3_14B_STEP.scaled(layers=1)
+    H.log(f"[case] full size dense {wl.name}")
+    dev = "cuda"
+    lens = wk.seq_lens(wl)
+    kv = wk.draw_kv_pages(wl, lens, dev)
+    P = kv["K"].shape[0]
+    dims = H.dims_for(wl, P)
+    q = wk.draw_queries(wl.scaled(hidden=0), dev)["Q"]
+    k_pool = B.pack_k_pages(dims, kv["K"])
+    v_pool = B.pack_v_pages(dims, kv["V"])
+    o = torch.full((wl.batch, wl.num_q_heads, wl.head_dim), float("nan"), device=dev)
+    m = torch.full((wl.batch, wl.num_q_heads), float("nan"), device=dev)
+    l = torch.full_like(m, float("nan"))
+    B.sa_dense_decode(dims, q, k_pool, v_pool, kv["table"], lens.to(dev), wl.scale, o, m, l)
+    torch.cuda.synchronize()
+    del k_pool, v_pool
+    G = wl.group
+    max_err = 0.0
+    for p in sample_pairs(wl, 4, 13):
+        s, h = divmod(p, wl.num_kv_heads)
+        n = int(lens[s])
+        K = wk.f64(wk.logical_rows(kv["K"], kv["table"][s, h], n))
+        V = wk.f64(wk.logical_rows(kv["V"], kv["table"][s, h], n))
+        for j in range(G):
+            qh = h * G + j
+            want = so.dense_attention(q[s, qh].double().cpu().numpy(), K, V, n, wl.scale)
+            max_err = max(max_err, H.compare_partial(
+                o[s, qh].double().cpu().numpy(), float(m[s, qh]), float(l[s, qh]), want,
+                H.attn_tol(wl), f"seq {s} head {qh}"))
+    H.log(f"  dense full size: max_err={max_err:.2e}")
