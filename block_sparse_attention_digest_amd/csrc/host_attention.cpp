@@ -17,10 +17,12 @@
 #include <chrono>
 #include <cmath>
 #include <condition_variable>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <stdexcept>
 #include <thread>
+#include <type_traits>
 #include <vector>
 
 #include "host.hpp"
@@ -38,37 +40,67 @@ inline float to_f32(uint16_t v) {  // bfloat16 bit pattern
   return f;
 }
 
-// eight floats as one vector value (two SSE registers, or one AVX register where the build has it)
-typedef float v8f __attribute__((vector_size(32)));
+// W floats as one vector value (W = 8: two SSE registers or one AVX register; W = 16: one
+// AVX-512 register where the build has it)
+template <int W>
+struct VecT {
+  typedef float type __attribute__((vector_size(W * sizeof(float))));
+};
+template <int W>
+using vecf = typename VecT<W>::type;
 
-inline v8f load8(const float* p) {
-  v8f v;
+template <int W>
+inline __attribute__((always_inline)) vecf<W> loadv(const float* p) {
+  vecf<W> v;
   std::memcpy(&v, p, sizeof v);
   return v;
 }
-inline void store8(float* p, v8f v) { std::memcpy(p, &v, sizeof v); }
+template <int W>
+inline __attribute__((always_inline)) void storev(float* p, vecf<W> v) {
+  std::memcpy(p, &v, sizeof v);
+}
+template <int W>
+inline __attribute__((always_inline)) float hsum(vecf<W> s) {
+  float t = 0.f;
+  for (int i = 0; i < W; ++i) t += s[i];
+  return t;
+}
 
-// One block of one pair for the G query heads, on float rows already converted: the block's
-// G x nval logits first (each key row read once for all heads), then one online-softmax update
-// per head (one rescale of the running output per block, not per token), then P V with a
-// 16-column strip of the G output rows held in registers across the block's tokens.  The head
-// dimension is a multiple of 16.  z holds G rows of zs logits.
-template <int G>
-inline __attribute__((always_inline)) void block_body(const float* q, const float* kf,
-                                                      const float* vf, int nval, int D,
-                                                      float scale, float* m, float* l,
-                                                      float* acc, float* z, int zs) {
-  for (int t = 0; t < nval; ++t) {
-    const float* kr = kf + (size_t)t * D;
-    v8f s[G];
-    for (int g = 0; g < G; ++g) s[g] = v8f{};
-    for (int c = 0; c < D; c += 8) {
-      const v8f k = load8(kr + c);
-      for (int g = 0; g < G; ++g) s[g] += load8(q + (size_t)g * D + c) * k;
+// One block of one pair for the G query heads: the block's rows converted to float (bf16
+// keys and values), the block's G x nval logits (each key row read once for all heads), one
+// online-softmax update per head (one rescale of the running output per block, not per
+// token), then P V with a 2W-column strip of the G output rows held in registers across the
+// block's tokens.  The head dimension is a multiple of 2W.  z holds G rows of zs logits.
+template <typename T, int G, int W>
+inline __attribute__((always_inline)) void block_body(const float* q, const void* k_rows,
+                                                      const void* v_rows, float* kf, float* vf,
+                                                      int nval, int D, float scale, float* m,
+                                                      float* l, float* acc, float* z, int zs) {
+  const float* K;
+  const float* V;
+  if constexpr (std::is_same<T, float>::value) {
+    K = static_cast<const float*>(k_rows);
+    V = static_cast<const float*>(v_rows);
+  } else {
+    const T* kr = static_cast<const T*>(k_rows);
+    const T* vr = static_cast<const T*>(v_rows);
+    const size_t n = (size_t)nval * D;
+    for (size_t i = 0; i < n; ++i) {
+      kf[i] = to_f32(kr[i]);
+      vf[i] = to_f32(vr[i]);
     }
-    for (int g = 0; g < G; ++g)
-      z[g * zs + t] = (((s[g][0] + s[g][1]) + (s[g][2] + s[g][3])) +
-                       ((s[g][4] + s[g][5]) + (s[g][6] + s[g][7]))) * scale;
+    K = kf;
+    V = vf;
+  }
+  for (int t = 0; t < nval; ++t) {
+    const float* kt = K + (size_t)t * D;
+    vecf<W> s[G];
+    for (int g = 0; g < G; ++g) s[g] = vecf<W>{};
+    for (int c = 0; c < D; c += W) {
+      const vecf<W> k = loadv<W>(kt + c);
+      for (int g = 0; g < G; ++g) s[g] += loadv<W>(q + (size_t)g * D + c) * k;
+    }
+    for (int g = 0; g < G; ++g) z[g * zs + t] = hsum<W>(s[g]) * scale;
   }
   float alpha[G];
   for (int g = 0; g < G; ++g) {
@@ -85,16 +117,16 @@ inline __attribute__((always_inline)) void block_body(const float* q, const floa
     l[g] = l[g] * alpha[g] + psum;
     m[g] = m_new;
   }
-  for (int c0 = 0; c0 < D; c0 += 16) {
-    v8f o[G][2];
+  for (int c0 = 0; c0 < D; c0 += 2 * W) {
+    vecf<W> o[G][2];
     for (int g = 0; g < G; ++g) {
       float* ag = acc + (size_t)g * D + c0;
-      o[g][0] = load8(ag) * alpha[g];
-      o[g][1] = load8(ag + 8) * alpha[g];
+      o[g][0] = loadv<W>(ag) * alpha[g];
+      o[g][1] = loadv<W>(ag + W) * alpha[g];
     }
     for (int t = 0; t < nval; ++t) {
-      const float* vr = vf + (size_t)t * D + c0;
-      const v8f v0 = load8(vr), v1 = load8(vr + 8);
+      const float* vt = V + (size_t)t * D + c0;
+      const vecf<W> v0 = loadv<W>(vt), v1 = loadv<W>(vt + W);
       for (int g = 0; g < G; ++g) {
         const float p = z[g * zs + t];
         o[g][0] += p * v0;
@@ -103,36 +135,68 @@ inline __attribute__((always_inline)) void block_body(const float* q, const floa
     }
     for (int g = 0; g < G; ++g) {
       float* ag = acc + (size_t)g * D + c0;
-      store8(ag, o[g][0]);
-      store8(ag + 8, o[g][1]);
+      storev<W>(ag, o[g][0]);
+      storev<W>(ag + W, o[g][1]);
     }
   }
 }
 
-template <int G>
-__attribute__((target("avx2,fma"))) void block_avx2(const float* q, const float* kf,
-                                                    const float* vf, int nval, int D,
-                                                    float scale, float* m, float* l,
-                                                    float* acc, float* z, int zs) {
-  block_body<G>(q, kf, vf, nval, D, scale, m, l, acc, z, zs);
+#define SA_BLOCK_ARGS                                                                       \
+  const float *q, const void *k_rows, const void *v_rows, float *kf, float *vf, int nval,  \
+      int D, float scale, float *m, float *l, float *acc, float *z, int zs
+#define SA_BLOCK_PASS q, k_rows, v_rows, kf, vf, nval, D, scale, m, l, acc, z, zs
+
+template <typename T, int G>
+__attribute__((target("avx512f,avx512bw,avx512vl,avx512dq,fma"))) void block_avx512(
+    SA_BLOCK_ARGS) {
+  block_body<T, G, 16>(SA_BLOCK_PASS);
 }
 
-template <int G>
-void block_base(const float* q, const float* kf, const float* vf, int nval, int D, float scale,
-                float* m, float* l, float* acc, float* z, int zs) {
-  block_body<G>(q, kf, vf, nval, D, scale, m, l, acc, z, zs);
+template <typename T, int G>
+__attribute__((target("avx2,fma"))) void block_avx2(SA_BLOCK_ARGS) {
+  block_body<T, G, 8>(SA_BLOCK_PASS);
 }
 
-using BlockFn = void (*)(const float*, const float*, const float*, int, int, float, float*,
-                         float*, float*, float*, int);
+template <typename T, int G>
+void block_base(SA_BLOCK_ARGS) {
+  block_body<T, G, 8>(SA_BLOCK_PASS);
+}
 
-// the block routine for a group size, the AVX2+FMA build where the CPU has both
+using BlockFn = void (*)(SA_BLOCK_ARGS);
+#undef SA_BLOCK_ARGS
+#undef SA_BLOCK_PASS
+
+enum class Isa { base, avx2, avx512 };
+
+// The widest build the CPU runs, or a narrower one named by SCOUTATTN_HOST_ISA ("base",
+// "avx2"; read once), so that every build can be checked on one machine.
+Isa host_isa() {
+  static const Isa isa = [] {
+    Isa best = Isa::base;
+    if (__builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+        __builtin_cpu_supports("avx512vl") && __builtin_cpu_supports("avx512dq") &&
+        __builtin_cpu_supports("fma"))
+      best = Isa::avx512;
+    else if (__builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma"))
+      best = Isa::avx2;
+    const char* want = std::getenv("SCOUTATTN_HOST_ISA");
+    if (want && std::strcmp(want, "base") == 0) return Isa::base;
+    if (want && std::strcmp(want, "avx2") == 0 && best != Isa::base) return Isa::avx2;
+    return best;
+  }();
+  return isa;
+}
+
+// the block routine for a KV type and group size, in the widest build the CPU runs
+template <typename T>
 BlockFn pick_block(int G) {
-  static const bool avx2 = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma");
+  const Isa isa = host_isa();
   switch (G) {
-#define SA_HOST_G(n) \
-  case n:            \
-    return avx2 ? block_avx2<n> : block_base<n>;
+#define SA_HOST_G(n)                                    \
+  case n:                                               \
+    return isa == Isa::avx512 ? block_avx512<T, n>      \
+           : isa == Isa::avx2 ? block_avx2<T, n>        \
+                              : block_base<T, n>;
     SA_HOST_G(1) SA_HOST_G(2) SA_HOST_G(3) SA_HOST_G(4)
     SA_HOST_G(5) SA_HOST_G(6) SA_HOST_G(7) SA_HOST_G(8)
 #undef SA_HOST_G
@@ -164,13 +228,8 @@ void attend_pair(const HostAttnArgs& a, BlockFn block, int pair, float* kf, floa
     if (page < 0 || page >= a.host_pages) continue;
     const int nval = std::min(BS, len - b * BS);
     if (nval <= 0) continue;
-    const T* kr = K + (size_t)page * BS * D;
-    const T* vr = V + (size_t)page * BS * D;
-    for (size_t i = 0; i < (size_t)nval * D; ++i) {
-      kf[i] = to_f32(kr[i]);
-      vf[i] = to_f32(vr[i]);
-    }
-    block(q, kf, vf, nval, D, a.scale, m, l, acc, z, BS);
+    block(q, K + (size_t)page * BS * D, V + (size_t)page * BS * D, kf, vf, nval, D, a.scale, m,
+          l, acc, z, BS);
   }
   for (int g = 0; g < G; ++g) {
     const size_t row = (size_t)s * a.Hq + (size_t)h * G + g;
@@ -192,7 +251,7 @@ void attend_pair(const HostAttnArgs& a, BlockFn block, int pair, float* kf, floa
 // one block of K and V as float, the G output rows, the G x bs logits.
 template <typename T>
 void work(const HostAttnArgs& a, std::atomic<int>& next, std::vector<float>& buf) {
-  const BlockFn block = pick_block(a.G);
+  const BlockFn block = pick_block<T>(a.G);
   const int npairs = a.B * a.Hkv;
   const size_t blk = (size_t)a.bs * a.d;
   buf.resize(2 * blk + (size_t)a.G * a.d + (size_t)a.G * a.bs);

@@ -206,3 +206,30 @@ def test_host_plan_run_matches_the_worker(lib, threads):
             plan.run(2)
     finally:
         plan.close()
+
+
+@pytest.mark.parametrize("isa", ["base", "avx2"])
+def test_host_partial_narrower_builds(isa, tmp_path):
+    """The SSE and AVX2 builds of the block routine (the widest one the CPU runs is what the
+    other tests see) against the oracle and against the widest build, in a fresh process
+    with SCOUTATTN_HOST_ISA set (it is read once per process)."""
+    import subprocess
+    import sys
+    code = (
+        "import sys, numpy as np; sys.path.insert(0, 'tests'); "
+        "import test_host_worker as T; from block_sparse_attention_digest_amd import binding as B; "
+        "B.lib(); P = T.make_problem('bf16', seed=12); o, m, l = T.run_worker(P, threads=2); "
+        "np.save(sys.argv[1], np.concatenate([o.ravel(), m.ravel(), l.ravel()]))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    outs = {}
+    for name, env_isa in (("narrow", isa), ("widest", "")):
+        path = str(tmp_path / f"{name}.npy")
+        env = dict(os.environ, SCOUTATTN_HOST_ISA=env_isa)
+        r = subprocess.run([sys.executable, "-c", code, path], cwd=root, env=env,
+                           capture_output=True, text=True, timeout=300)
+        assert r.returncode == 0, r.stderr
+        outs[name] = np.load(path)
+    a, b = outs["narrow"], outs["widest"]
+    fin = np.isfinite(b)
+    assert np.array_equal(np.isfinite(a), fin)
+    assert np.max(np.abs(a[fin] - b[fin])) <= 1e-5 * max(1.0, float(np.max(np.abs(b[fin]))))
