@@ -264,6 +264,16 @@ def test_step_offload_parity():
     assert r["cpu_ratio"] > 0.1
 
 
+def test_step_offload_parity_ragged():
+    """Ragged lengths down to one token (k_s = min(k, nb_s)), bf16, bs 32."""
+    H.log("[case] step offload, ragged")
+    import harness_step as HS
+    HS.run_step(wk.QWEN3_14B_STEP.scaled(batch=4, num_q_heads=10, num_kv_heads=2, context=0,
+                                         ctx_min=1, ctx_max=2000, layers=3, pool_blocks=5,
+                                         hidden=256, top_k=8),
+                gen_device="cpu", side=True, offload=True, host_threads=3)
+
+
 def test_step_offload_parity_one_stream_one_thread():
     H.log("[case] step offload, one stream, one host thread")
     import harness_step as HS
@@ -274,15 +284,18 @@ def test_step_offload_parity_one_stream_one_thread():
     assert r["cpu_ratio"] > 0.1
 
 
-@pytest.mark.parametrize("pool,max_recall", [(6, 64), (12, 2), (12, 64)])
-def test_recall_parity(pool, max_recall):
+@pytest.mark.parametrize("pool,max_recall,ragged", [(6, 64, False), (12, 2, False),
+                                                     (12, 64, False), (6, 64, True)])
+def test_recall_parity(pool, max_recall, ragged):
     """Periodic recall of every layer after a step: tables, moved pages and untouched pages
     against the oracle bit for bit, then the next step over the new residency."""
-    H.log(f"[case] recall pool={pool} max_recall={max_recall}")
+    H.log(f"[case] recall pool={pool} max_recall={max_recall} ragged={ragged}")
     import harness_recall as HR
-    r = HR.run_recall(wk.QWEN3_14B_STEP.scaled(batch=3, num_q_heads=10, num_kv_heads=2,
-                                                context=2000, layers=2, pool_blocks=pool,
-                                                hidden=512, top_k=8), max_recall)
+    wl = wk.QWEN3_14B_STEP.scaled(batch=3, num_q_heads=10, num_kv_heads=2, context=2000,
+                                  layers=2, pool_blocks=pool, hidden=512, top_k=8)
+    if ragged:
+        wl = wl.scaled(batch=4, context=0, ctx_min=1, ctx_max=2000)
+    r = HR.run_recall(wl, max_recall)
     assert r["moved"] > 0
 
 
