@@ -23,7 +23,7 @@ link, the CPU share before and after, and (with --offload) the offload step agai
 --dense, "dense": FullKV attention over one layer's whole 64K context (sa_dense_decode).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-graph] [--offload] [--recall]
-                    [--dense]
+                    [--dense] [--drift-steps S]
 """
 
 from __future__ import annotations
@@ -74,6 +74,13 @@ def parse():
     ap.add_argument("--dense", action="store_true",
                     help="also time dense (FullKV) attention over one layer of the workload's "
                          "whole context (sa_dense_decode), reported as \"dense\"")
+    ap.add_argument("--drift-steps", type=int, default=0,
+                    help="decode steps of a drift study: each step's layer inputs move "
+                         "(X <- rho X + sqrt(1 - rho^2) Z), once without recall and once "
+                         "recalling every layer whose CPU share exceeds --beta, reported as "
+                         "\"drift\"")
+    ap.add_argument("--drift-rho", type=float, default=0.97)
+    ap.add_argument("--beta", type=float, default=0.12)
     ap.add_argument("--block-size", type=int, default=None, choices=(16, 32),
                     help="KV block size instead of the workload's 32, with the token budget "
                          "and the resident pool kept in tokens (a study of the digest "
@@ -353,6 +360,73 @@ def dense_measure(wl, args, torch, B, wk, sparse_us):
     return out
 
 
+def drift_measure(wl, dims, lens, layers, ws, side_stream, store, args, torch, B):
+    """The CPU share over decode steps whose inputs drift, without and with periodic recall.
+
+    Each step moves every layer's input, X^i <- rho X^i + sqrt(1 - rho^2) Z (Z ~ N(0, 1),
+    seeded per step), so the queries, and with them the selections, drift away from the
+    resident pools, which were chosen for the first step's queries.  Run once without recall
+    and once with it; in the second run a layer whose CPU share (offloaded selected blocks
+    over the budget) exceeds beta after a step is recalled from that step's lists
+    (sa_recall_blocks) before the next step -- an online stand-in for the pages' per-layer
+    intervals chosen offline to keep the share under beta.  The pools change in the second
+    run only, so it goes last."""
+    import math as _m
+    Bsz, Hkv, k = wl.batch, wl.num_kv_heads, wl.top_k
+    pairs = Bsz * Hkv
+    x0 = [L["x"].clone() for L in layers]
+    table_d = store["table"].to("cuda")
+    rws = B.workspace(B.sa_recall_workspace_bytes(dims, k))
+    n_rec = torch.empty(pairs, dtype=torch.int32, device="cuda")
+    c = _m.sqrt(1.0 - args.drift_rho ** 2)
+
+    def run(recall):
+        for L, x in zip(layers, x0):
+            L["x"].copy_(x)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(4242)
+        shares, recalls, moved, rec_ms = [], 0, 0, 0.0
+        for _ in range(args.drift_steps):
+            for L in layers:
+                z = torch.randn(L["x"].shape, generator=g, device="cuda")
+                L["x"].copy_((args.drift_rho * L["x"].float() + c * z).to(torch.bfloat16))
+            B.sa_decode_step(dims, "mean", wl.hidden, k, wl.scale, lens, layers, ws,
+                             side_stream=side_stream)
+            torch.cuda.synchronize()
+            per_layer = [int(L["n_cpu"].sum()) / (pairs * k) for L in layers]
+            shares.append(round(sum(per_layer) / len(per_layer), 4))
+            if recall:
+                for L, sh in zip(layers, per_layer):
+                    if sh <= args.beta:
+                        continue
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    B.sa_recall_blocks(dims, k, k, lens, L["block_table"], L["gpu_blocks"],
+                                       L["n_gpu"], L["cpu_blocks"], L["n_cpu"], store["K"],
+                                       store["V"], table_d, L["k_pool"], L["v_pool"], n_rec, rws)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    rec_ms += e0.elapsed_time(e1)
+                    recalls += 1
+                    moved += int(n_rec.sum())
+        return shares, recalls, moved, rec_ms
+
+    t0 = time.time()
+    s0, _, _, _ = run(False)
+    s1, recalls, moved, rec_ms = run(True)
+    log(f"drift: {args.drift_steps} steps in {time.time() - t0:.1f} s; mean CPU share "
+        f"{sum(s0) / len(s0):.3f} without recall, {sum(s1) / len(s1):.3f} with "
+        f"({recalls} layer recalls)")
+    return {"steps": args.drift_steps, "rho": args.drift_rho, "beta": args.beta,
+            "cpu_share_no_recall": s0, "cpu_share_with_recall": s1,
+            "mean_no_recall": round(sum(s0) / len(s0), 4),
+            "mean_with_recall": round(sum(s1) / len(s1), 4),
+            "layer_recalls": recalls, "layers": wl.layers, "blocks_moved": moved,
+            "recall_ms_total": round(rec_ms, 2),
+            "note": "CPU share = offloaded selected blocks / budget, averaged over the layers "
+                    "after each step; a layer is recalled when its share exceeds beta"}
+
+
 def offload_measure(wl, dims, lens, layers, ws, side_stream, ms_gpu, args, torch, B, wk,
                     store=None):
     """The same step with its CPU side computed, not given: sa_decode_step_offload runs each
@@ -609,7 +683,7 @@ def main():
     }
     if args.dense:
         result["dense"] = dense_measure(wl, args, torch, B, wk, iso_avg_ms * 1e3)
-    store = host_store(wl, args, B, wk) if args.recall else None
+    store = host_store(wl, args, B, wk) if (args.recall or args.drift_steps) else None
     if args.offload:
         result["offload"] = offload_measure(wl, dims, lens, layers, ws, side_stream, ms_step,
                                             args, torch, B, wk, store)
@@ -636,6 +710,9 @@ def main():
             rec["offload_after"] = offload_measure(wl, dims, lens, layers, ws, side_stream,
                                                    ms_after, args, torch, B, wk, store)
         result["recall"] = rec
+    if args.drift_steps:
+        result["drift"] = drift_measure(wl, dims, lens, layers, ws, side_stream, store, args,
+                                        torch, B)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
