@@ -510,8 +510,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: this decode path has no multi-GPU mode "
-              "(see DESIGN.md, 'How the path would shard').", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: this decode path has no multi-GPU mode; "
+              "it would shard over sequences or KV heads with no exchange on the path.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

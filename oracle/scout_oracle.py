@@ -28,7 +28,7 @@ written out in float64, with no blocking, fusion or reordering beyond it):
   * periodic recall: offloaded selected blocks move into the pages of resident blocks
     that are no longer selected                       [HTML Sec. 3.4; DIGEST 三]
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   R1 min/max score = sum_c max(q_c*min_c, q_c*max_c), Quest's upper bound on q.k.
   R2 one selection per (sequence, KV head): the scores of the G query heads that share
      the KV head are summed.
