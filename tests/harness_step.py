@@ -56,6 +56,61 @@ def prepare_step(wl, gen_device, kind="mean"):
     return layers
 
 
+def device_layers(wl, data, dims, lens_d, kind="mean", handoff=True):
+    """The step's per-layer device buffers (sa_layer fields): pool pages packed, pool-block
+    digests rebuilt from the pool keys, lists and outputs allocated (lists poisoned with -7)."""
+    dev = "cuda"
+    B_, Hkv, Hq, d, k = wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim, wl.top_k
+    pairs = B_ * Hkv
+    i32, f32 = torch.int32, torch.float32
+    out = []
+    for Ld in data:
+        dig = Ld["dig"].to(dev).contiguous()
+        k_pool = B.pack_k_pages(dims, Ld["pool"]["K"].to(dev))
+        B.sa_build_digests(dims, kind, k_pool, Ld["pool"]["block_table"].to(dev), lens_d, dig)
+        e = dict(x=Ld["X"].to(dev), w_q=B.pack_weight(Ld["W"].to(dev)), digests=dig,
+                 block_table=Ld["pool"]["block_table"].to(dev), k_pool=k_pool,
+                 v_pool=B.pack_v_pages(dims, Ld["pool"]["V"].to(dev)),
+                 host_o=Ld["host"]["o"].to(dev).contiguous(),
+                 host_m=Ld["host"]["m"].to(dev).contiguous(),
+                 host_l=Ld["host"]["l"].to(dev).contiguous(),
+                 gpu_blocks=torch.full((pairs, k), -7, dtype=i32, device=dev),
+                 n_gpu=torch.full((pairs,), -7, dtype=i32, device=dev),
+                 cpu_blocks=torch.full((pairs, k), -7, dtype=i32, device=dev),
+                 n_cpu=torch.full((pairs,), -7, dtype=i32, device=dev),
+                 out_o=torch.empty((B_, Hq, d), dtype=f32, device=dev),
+                 out_m=torch.empty((B_, Hq), dtype=f32, device=dev),
+                 out_l=torch.empty((B_, Hq), dtype=f32, device=dev))
+        if handoff:
+            e["cpu_blocks_host"] = B.pinned_empty((pairs, k)).zero_()
+            e["n_cpu_host"] = B.pinned_empty((pairs,)).zero_()
+        out.append(e)
+    return out
+
+
+def host_side(wl, data, store="full", host_pages=32768):
+    """Host stores and the host-plan layers (pinned hand-off buffers, poisoned)."""
+    B_, Hkv, Hq, d, k = wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim, wl.top_k
+    pairs = B_ * Hkv
+    f32 = torch.float32
+    if store == "aliased":
+        shared = wk.draw_host_store_aliased(wl, host_pages)
+        stores = [shared] * len(data)
+    else:
+        stores = [wk.draw_host_store(wl, i, Ld["off"]) for i, Ld in enumerate(data)]
+    host_layers = []
+    for st in stores:
+        host_layers.append(dict(
+            k_host=st["K"], v_host=st["V"], host_table=st["table"],
+            q_host=B.pinned_empty((B_, Hq, d), f32).fill_(float("nan")),
+            cpu_blocks_host=B.pinned_empty((pairs, k)).fill_(-7),
+            n_cpu_host=B.pinned_empty((pairs,)).fill_(-7),
+            o_host=B.pinned_empty((B_, Hq, d), f32).fill_(float("nan")),
+            m_host=B.pinned_empty((B_, Hq), f32).fill_(float("nan")),
+            l_host=B.pinned_empty((B_, Hq), f32).fill_(float("nan"))))
+    return stores, host_layers
+
+
 def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs_to_check=None,
              side=True, offload=False, host_threads=4, store="full", host_pages=32768):
     """handoff: give every layer host mirrors of its offloaded lists; side: run the
@@ -77,48 +132,12 @@ def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs
     i32, f32 = torch.int32, torch.float32
 
     # ---------------- HIP path: pool digests rebuilt from the pool keys, then the step
-    dev_layers = []
-    pinned = []
-    for i, Ld in enumerate(data):
-        dig = Ld["dig"].to(dev).contiguous()
-        k_pool = B.pack_k_pages(dims, Ld["pool"]["K"].to(dev))
-        B.sa_build_digests(dims, kind, k_pool, Ld["pool"]["block_table"].to(dev), lens_d, dig)
-        e = dict(x=Ld["X"].to(dev), w_q=B.pack_weight(Ld["W"].to(dev)), digests=dig,
-                 block_table=Ld["pool"]["block_table"].to(dev), k_pool=k_pool,
-                 v_pool=B.pack_v_pages(dims, Ld["pool"]["V"].to(dev)),
-                 host_o=Ld["host"]["o"].to(dev).contiguous(),
-                 host_m=Ld["host"]["m"].to(dev).contiguous(),
-                 host_l=Ld["host"]["l"].to(dev).contiguous(),
-                 gpu_blocks=torch.full((pairs, k), -7, dtype=i32, device=dev),
-                 n_gpu=torch.full((pairs,), -7, dtype=i32, device=dev),
-                 cpu_blocks=torch.full((pairs, k), -7, dtype=i32, device=dev),
-                 n_cpu=torch.full((pairs,), -7, dtype=i32, device=dev),
-                 out_o=torch.empty((B_, Hq, d), dtype=f32, device=dev),
-                 out_m=torch.empty((B_, Hq), dtype=f32, device=dev),
-                 out_l=torch.empty((B_, Hq), dtype=f32, device=dev))
-        if handoff:
-            e["cpu_blocks_host"] = B.pinned_empty((pairs, k)).zero_()
-            e["n_cpu_host"] = B.pinned_empty((pairs,)).zero_()
-        dev_layers.append(e)
+    dev_layers = device_layers(wl, data, dims, lens_d, kind, handoff)
     ws = B.workspace(B.sa_step_workspace_bytes(dims, wl.hidden, k))
     side_stream = torch.cuda.Stream() if side else None
     stores = host_layers = None
     if offload:
-        if store == "aliased":
-            shared = wk.draw_host_store_aliased(wl, host_pages)
-            stores = [shared] * len(data)
-        else:
-            stores = [wk.draw_host_store(wl, i, Ld["off"]) for i, Ld in enumerate(data)]
-        host_layers = []
-        for st in stores:
-            host_layers.append(dict(
-                k_host=st["K"], v_host=st["V"], host_table=st["table"],
-                q_host=B.pinned_empty((B_, Hq, d), f32).fill_(float("nan")),
-                cpu_blocks_host=B.pinned_empty((pairs, k)).fill_(-7),
-                n_cpu_host=B.pinned_empty((pairs,)).fill_(-7),
-                o_host=B.pinned_empty((B_, Hq, d), f32).fill_(float("nan")),
-                m_host=B.pinned_empty((B_, Hq), f32).fill_(float("nan")),
-                l_host=B.pinned_empty((B_, Hq), f32).fill_(float("nan"))))
+        stores, host_layers = host_side(wl, data, store, host_pages)
         plan = B.HostPlan(dims, k, wl.scale, lens.clone(), host_layers, threads=host_threads)
         host_stream = torch.cuda.Stream()
         B.sa_decode_step_offload(dims, kind, wl.hidden, k, wl.scale, lens_d, dev_layers, ws,

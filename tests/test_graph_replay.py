@@ -1,0 +1,107 @@
+"""HIP graphs of the decode step.
+
+The step, and the step with its CPU side as host tasks, are each captured once and replayed
+several times.  Between replays the outputs are poisoned and an eager step runs.  Every
+replay and every eager step must reproduce the first eager result bit for bit: the same
+kernels and the same host tasks run on the same inputs.
+"""
+
+import pytest
+import torch
+
+import harness as H
+import harness_step as HS
+from block_sparse_attention_digest_amd import binding as B
+from block_sparse_attention_digest_amd import workloads as wk
+
+pytestmark = pytest.mark.gpu
+
+WL = wk.QWEN3_14B_STEP.scaled(batch=3, num_q_heads=10, num_kv_heads=2, context=2000, layers=4,
+                              pool_blocks=6, hidden=512, top_k=8)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def snapshot(layers, host_layers):
+    out = []
+    for L in layers:
+        out += [L[n].clone() for n in ("out_o", "out_m", "out_l", "gpu_blocks", "n_gpu",
+                                       "cpu_blocks", "n_cpu")]
+    for h in host_layers or []:
+        out += [h[n].clone() for n in ("q_host", "o_host", "m_host", "l_host", "n_cpu_host",
+                                       "cpu_blocks_host")]
+    return out
+
+
+def poison(layers, host_layers):
+    for L in layers:
+        for n in ("out_o", "out_m", "out_l"):
+            L[n].fill_(float("nan"))
+        for n in ("gpu_blocks", "n_gpu", "cpu_blocks", "n_cpu"):
+            L[n].fill_(-7)
+    for h in host_layers or []:
+        for n in ("q_host", "o_host", "m_host", "l_host"):
+            h[n].fill_(float("nan"))
+
+
+def same(a, b):
+    return all(torch.equal(x, y) for x, y in zip(a, b)) and len(a) == len(b)
+
+
+@pytest.mark.parametrize("offload", [False, True], ids=["step", "step-with-host-tasks"])
+def test_step_graph_replays_match_eager(offload):
+    H.log(f"[case] graph replay, offload={offload}")
+    data = HS.prepare_step(WL, "cpu")
+    lens = wk.seq_lens(WL)
+    lens_d = lens.to("cuda")
+    dims = H.dims_for(WL, data[0]["pool"]["K"].shape[0])
+    layers = HS.device_layers(WL, data, dims, lens_d, "mean", handoff=not offload)
+    ws = B.workspace(B.sa_step_workspace_bytes(dims, WL.hidden, WL.top_k))
+    side = torch.cuda.Stream()
+    host_layers = plan = None
+    if offload:
+        _, host_layers = HS.host_side(WL, data)
+        plan = B.HostPlan(dims, WL.top_k, WL.scale, lens.clone(), host_layers, threads=3)
+        host_stream = torch.cuda.Stream()
+
+    def step():
+        if offload:
+            B.sa_decode_step_offload(dims, "mean", WL.hidden, WL.top_k, WL.scale, lens_d, layers,
+                                     ws, plan, host_stream, side_stream=side)
+        else:
+            B.sa_decode_step(dims, "mean", WL.hidden, WL.top_k, WL.scale, lens_d, layers, ws,
+                             side_stream=side)
+
+    try:
+        step()
+        torch.cuda.synchronize()
+        ref = snapshot(layers, host_layers)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for rep in range(3):
+            poison(layers, host_layers)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert same(snapshot(layers, host_layers), ref), f"replay {rep}"
+            poison(layers, host_layers)
+            step()  # eager work between the replays
+            torch.cuda.synchronize()
+            assert same(snapshot(layers, host_layers), ref), f"eager step after replay {rep}"
+        del graph
+        torch.cuda.synchronize()
+        if offload:
+            tasks, _ = plan.stats()
+            # the capture enqueues no task; each eager step and each replay runs one per layer
+            assert tasks == WL.layers * 7, tasks
+    finally:
+        if plan is not None:
+            torch.cuda.synchronize()
+            plan.close()
