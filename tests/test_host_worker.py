@@ -233,3 +233,27 @@ def test_host_partial_narrower_builds(isa, tmp_path):
     fin = np.isfinite(b)
     assert np.array_equal(np.isfinite(a), fin)
     assert np.max(np.abs(a[fin] - b[fin])) <= 1e-5 * max(1.0, float(np.max(np.abs(b[fin]))))
+
+
+def test_host_plan_many_jobs_with_random_pauses(lib):
+    """200 jobs on one plan, with pauses from none to well past the workers' spin (so they are
+    caught spinning, falling asleep and asleep): every result is identical to the first."""
+    import time
+    P = make_problem("f32", seed=71)
+    layers = [plan_layer(P)]
+    plan = B.HostPlan(P["dims"], P["top"], P["scale"], P["lens"], layers, threads=4)
+    rng = np.random.default_rng(5)
+    try:
+        plan.run(0)
+        ref = [layers[0][n].clone() for n in ("o_host", "m_host", "l_host")]
+        for it in range(200):
+            pause = float(rng.choice([0.0, 0.0001, 0.0003, 0.002]))
+            if pause:
+                time.sleep(pause)
+            layers[0]["o_host"].fill_(float("nan"))
+            plan.run(0)
+            for r, n in zip(ref, ("o_host", "m_host", "l_host")):
+                assert torch.equal(layers[0][n], r), (it, n)
+        assert plan.stats()[0] == 201
+    finally:
+        plan.close()
