@@ -279,6 +279,15 @@ def recall_pair(table_row, seq_len: int, block_size: int, gpu_blocks, cpu_blocks
     return table, moves
 
 
+def recall_due(n_cpu_per_pair, top_k: int, beta: float) -> bool:
+    """Whether a layer is recalled [HTML Sec. 3.4]: its CPU compute ratio -- the share of the
+    budget the CPU attends -- is above the threshold beta.  Reading: the ratio is counted in
+    blocks, sum over pairs of |B_cpu| / (pairs * top_k), and tested after each selection (the
+    pages set per-layer intervals offline so that the measured ratio stays under beta)."""
+    n = np.asarray(n_cpu_per_pair, dtype=np.int64)
+    return float(n.sum()) / (len(n) * top_k) > beta
+
+
 # ----------------------------------------------------------------------------------------
 # O7/O8: partial attention and the merge  [HTML Sec. 3.2: partials merged with the
 #        FlashAttention algorithm; Algorithm 1: A_gpu = GPUATTN(Q, B_gpu),

@@ -540,4 +540,15 @@ def pin_recall_invariants():
             assert table[b] < 0 and b in set(c.tolist()) and new[b] == p and hp == host[b]
 
 
+def pin_recall_due_hand():
+    """The recall trigger by hand: 4 pairs, k = 8 (a budget of 32 blocks), beta = 0.12.
+    3 offloaded blocks are 0.09375 (no), 4 are 0.125 (yes); the boundary 0.125 itself is not
+    above beta = 0.125."""
+    assert not so.recall_due([1, 1, 1, 0], 8, 0.12)
+    assert so.recall_due([1, 1, 1, 1], 8, 0.12)
+    assert not so.recall_due([1, 1, 1, 1], 8, 0.125)
+    assert so.recall_due([0, 0, 0, 1], 8, 0.0)
+    assert not so.recall_due([0, 0, 0, 0], 8, 0.0)
+
+
 ALL_PINS = [v for k, v in dict(globals()).items() if k.startswith("pin_") and callable(v)]
