@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libscoutattn.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = 0, -1, -2, -3, -4
 SA_F32, SA_BF16 = 0, 1
 SA_DIGEST_MEAN, SA_DIGEST_MINMAX = 0, 1
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 KIND = {"mean": SA_DIGEST_MEAN, "minmax": SA_DIGEST_MINMAX}
 
@@ -51,6 +51,10 @@ class sa_host_layer(ctypes.Structure):
                 ("host_table", ctypes.c_void_p), ("host_pages", ctypes.c_int32)] + [
         (n, ctypes.c_void_p) for n in ("q_host", "cpu_blocks_host", "n_cpu_host", "o_host",
                                        "m_host", "l_host")]
+
+
+class sa_recall_layer(ctypes.Structure):
+    _fields_ = [("host_table_dev", ctypes.c_void_p), ("n_recalled", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -94,7 +98,10 @@ SIGNATURES = {
     "sa_host_plan_stats": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int64),
                                           ctypes.POINTER(ctypes.c_double)]),
     "sa_decode_step_offload": (ctypes.c_int, [_D, ctypes.c_int, _I, _I, _F, _P, _I,
-                                              ctypes.POINTER(sa_layer), _P, _Z, _P, _P, _P, _P]),
+                                              ctypes.POINTER(sa_layer), _P, _Z, _P, _P, _P, _P,
+                                              _P]),
+    "sa_host_plan_set_recall": (ctypes.c_int, [_P, _I, _F, ctypes.POINTER(sa_recall_layer), _P,
+                                               _Z]),
     "sa_host_partial_attention": (ctypes.c_int, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _I, _F,
                                                  _P, _P, _P, _I]),
 }
@@ -503,6 +510,27 @@ class HostPlan:
         _check(lib().sa_host_plan_stats(self.handle, ctypes.byref(n), ctypes.byref(t)))
         return n.value, t.value
 
+    def set_recall(self, dims: Dims, max_recall: int, beta: float, layers, ws=None):
+        """Periodic recall inside the offload step (sa_host_plan_set_recall): `layers` is a
+        list of dicts with host_table_dev (GPU int32 [B][Hkv][max_blocks], or None) and
+        n_recalled (GPU int32 [B][Hkv]); None turns recall off."""
+        if layers is None:
+            _check(lib().sa_host_plan_set_recall(self.handle, 0, 0.0, None, None, 0))
+            self._recall = None
+            return
+        pairs = dims.batch * dims.num_kv_heads
+        if ws is None:
+            ws = workspace(sa_recall_workspace_bytes(dims, max_recall))
+        arr = (sa_recall_layer * len(layers))()
+        for i, L in enumerate(layers):
+            arr[i].host_table_dev = _ptr(L.get("host_table_dev"), torch.int32,
+                                         pairs * dims.max_blocks, f"[{i}].host_table_dev")
+            arr[i].n_recalled = _ptr(L.get("n_recalled"), torch.int32, pairs,
+                                     f"[{i}].n_recalled")
+        self._recall = (layers, ws)
+        _check(lib().sa_host_plan_set_recall(self.handle, max_recall, beta, arr,
+                                             _ptr(ws, torch.uint8, name="ws"), ws.numel()))
+
     def run(self, layer: int):
         """Layer `layer`'s host task now, on this thread and the plan's workers."""
         _check(lib().sa_host_plan_run(self.handle, layer))
@@ -515,7 +543,7 @@ class HostPlan:
 
 def sa_decode_step_offload(dims: Dims, kind: str, hidden: int, top_k: int, scale: float,
                            seq_lens, layers: list, ws, plan: HostPlan, host_stream,
-                           stream=None, side_stream=None):
+                           stream=None, side_stream=None, recall_stream=None):
     """sa_decode_step with the CPU side computed by `plan` on `host_stream` (a stream of its
     own); host_o/m/l and the host mirrors of `layers` are not used."""
     arr = (sa_layer * len(layers))()
@@ -529,7 +557,7 @@ def sa_decode_step_offload(dims: Dims, kind: str, hidden: int, top_k: int, scale
         _ptr(seq_lens, torch.int32, dims.batch, "seq_lens"), len(layers), arr,
         _ptr(ws, torch.uint8, name="ws"), ws.numel(), _stream(stream),
         None if side_stream is None else _stream(side_stream), plan.handle,
-        _stream(host_stream)))
+        _stream(host_stream), None if recall_stream is None else _stream(recall_stream)))
 
 
 def sa_profile_attention(starts, stops):

@@ -468,7 +468,7 @@ sa_status sa_dense_decode(const sa_dims* dims, const float* q, const void* k_poo
 
 // ---- periodic recall -------------------------------------------------------------------------
 
-static constexpr int kMaxRecall = 4096;
+static constexpr int kMaxRecall = 4096;  // blocks moved per pair by one recall, at most
 
 size_t sa_recall_workspace_bytes(const sa_dims* dims, int32_t max_recall) {
   sa::Shape s;
@@ -515,7 +515,7 @@ sa_status sa_recall_blocks(const sa_dims* dims, int32_t list_stride, int32_t max
     return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
   SA_HIP(sa::launch_recall(s, list_stride, max_recall, seq_lens, block_table, gpu_blocks, n_gpu,
                            cpu_blocks, n_cpu, k_host, v_host, host_table, host_pages, k_pool,
-                           v_pool, n_recalled, ws, stream),
+                           v_pool, n_recalled, ws, -1, stream),
          "recall kernels");
   return ok();
 }
@@ -590,6 +590,7 @@ sa_status sa_host_partial_attention(const sa_dims* dims, int32_t host_pages,
 
 // ---- the host plan: the CPU side of the step, as HIP host tasks ------------------------------
 
+
 struct sa_host_plan {
   struct Task {
     sa_host_plan* plan;
@@ -604,6 +605,11 @@ struct sa_host_plan {
   std::unique_ptr<sa::HostPool> pool;
   std::atomic<int64_t> runs{0}, busy_ns{0};
   std::atomic<bool> failed{false};
+  // periodic recall inside the step (sa_host_plan_set_recall); off while `recall` is empty
+  std::vector<sa_recall_layer> recall;
+  int max_recall = 0;
+  long recall_threshold = 0;  // the layer recalls when its offloaded selected blocks exceed it
+  void* recall_ws = nullptr;
 };
 
 // A layer's host task: A_cpu on the plan's workers; false if no worker could run (the
@@ -683,6 +689,39 @@ sa_status sa_host_plan_run(sa_host_plan* plan, int32_t layer) {
   return ok();
 }
 
+sa_status sa_host_plan_set_recall(sa_host_plan* plan, int32_t max_recall, float beta,
+                                  const sa_recall_layer* layers, void* ws, size_t ws_bytes) {
+  SA_NOT_NULL(plan);
+  if (!layers) {
+    plan->recall.clear();
+    return ok();
+  }
+  if (max_recall < 1 || max_recall > kMaxRecall)
+    return fail(SA_ERR_INVALID_ARG, "max_recall %d outside [1, %d]", max_recall, kMaxRecall);
+  if (!(beta >= 0.f)) return fail(SA_ERR_INVALID_ARG, "beta must be >= 0");
+  if (sa::recall_plan_lds_bytes(plan->s, max_recall) > 64 * 1024)
+    return fail(SA_ERR_UNSUPPORTED, "max_blocks %d with max_recall %d exceeds the plan's LDS",
+                plan->s.max_blocks, max_recall);
+  const size_t need = align_up((size_t)plan->s.B * plan->s.Hkv * max_recall * 2 * sizeof(int32_t));
+  if (!ws || ws_bytes < need)
+    return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
+  const int L = (int)plan->layers.size();
+  for (int i = 0; i < L; ++i)
+    if (layers[i].host_table_dev && !layers[i].n_recalled)
+      return fail(SA_ERR_INVALID_ARG, "recall layer %d: n_recalled is NULL", i);
+  try {
+    plan->recall.assign(layers, layers + L);
+  } catch (const std::exception& e) {
+    return fail(SA_ERR_INVALID_ARG, "recall layers: %s", e.what());
+  }
+  plan->max_recall = max_recall;
+  // ratio > beta  <=>  total > beta * pairs * top_k  <=>  total > floor(beta * pairs * top_k)
+  plan->recall_threshold =
+      (long)std::floor((double)beta * (double)plan->s.B * plan->s.Hkv * plan->top_k);
+  plan->recall_ws = ws;
+  return ok();
+}
+
 sa_status sa_host_plan_destroy(sa_host_plan* plan) {
   delete plan;  // joins the workers
   return ok();
@@ -747,7 +786,8 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
                            int32_t top_k, float scale, const int32_t* seq_lens,
                            int32_t num_layers, const sa_layer* layers, void* ws,
                            size_t ws_bytes, hipStream_t stream, hipStream_t side_stream,
-                           sa_host_plan* plan, hipStream_t host_stream) {
+                           sa_host_plan* plan, hipStream_t host_stream,
+                           hipStream_t recall_stream) {
   sa::Shape s;
   SA_CHECK(check_dims(dims, &s));
   SA_CHECK(check_kind(kind));
@@ -782,7 +822,13 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
                   "the host plan was made for another top_k, scale or number of layers");
     if (!host_stream || host_stream == stream || host_stream == side_stream)
       return fail(SA_ERR_INVALID_ARG, "host_stream must be a stream of its own");
+    if (!plan->recall.empty() &&
+        (!recall_stream || recall_stream == stream || recall_stream == side_stream ||
+         recall_stream == host_stream))
+      return fail(SA_ERR_INVALID_ARG,
+                  "the plan recalls: recall_stream must be a stream of its own");
   }
+  const bool recalls = plan && !plan->recall.empty();
   const StepLayout SL = step_layout(s, hidden, top_k);
   if (!ws || ws_bytes < SL.total)
     return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, SL.total);
@@ -925,6 +971,22 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
     e = sa::launch_reduce(s, SL.sel_layout.plan, L.n_gpu, parts, ho, hm, hl, L.n_cpu, L.out_o,
                           L.out_m, L.out_l, stream);
     if (e != hipSuccess) { st = hip_fail(e, "reduce kernel"); break; }
+    // 6. periodic recall of layer i, off the critical path: nothing in this step reads layer
+    //    i's table or pages any more, and the next step's use of them follows the final join.
+    //    The layer's buffers are the caller's, writable when it has the plan recall.
+    if (recalls && plan->recall[i].host_table_dev) {
+      st = order(stream, recall_stream);
+      if (st != SA_OK) break;
+      const sa_host_layer& H = plan->layers[i];
+      e = sa::launch_recall(s, top_k, plan->max_recall, seq_lens,
+                            const_cast<int32_t*>(L.block_table), L.gpu_blocks, L.n_gpu,
+                            L.cpu_blocks, L.n_cpu, H.k_host, H.v_host,
+                            plan->recall[i].host_table_dev, H.host_pages,
+                            const_cast<void*>(L.k_pool), const_cast<void*>(L.v_pool),
+                            plan->recall[i].n_recalled, plan->recall_ws,
+                            plan->recall_threshold, recall_stream);
+      if (e != hipSuccess) { st = hip_fail(e, "recall kernels"); break; }
+    }
   }
   // join the side stream and the host tasks back into `stream`
   if (side_stream) {
@@ -935,6 +997,10 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
     sa_status j = order(host_stream, stream);
     if (st == SA_OK) st = j;
   }
+  if (recalls) {
+    sa_status j = order(recall_stream, stream);
+    if (st == SA_OK) st = j;
+  }
   return st == SA_OK ? ok() : st;
 }
 
@@ -943,17 +1009,18 @@ sa_status sa_decode_step(const sa_dims* dims, sa_digest_kind kind, int32_t hidde
                          int32_t num_layers, const sa_layer* layers, void* ws,
                          size_t ws_bytes, hipStream_t stream, hipStream_t side_stream) {
   return step_impl(dims, kind, hidden, top_k, scale, seq_lens, num_layers, layers, ws, ws_bytes,
-                   stream, side_stream, nullptr, nullptr);
+                   stream, side_stream, nullptr, nullptr, nullptr);
 }
 
 sa_status sa_decode_step_offload(const sa_dims* dims, sa_digest_kind kind, int32_t hidden,
                                  int32_t top_k, float scale, const int32_t* seq_lens,
                                  int32_t num_layers, const sa_layer* layers, void* ws,
                                  size_t ws_bytes, hipStream_t stream, hipStream_t side_stream,
-                                 sa_host_plan* plan, hipStream_t host_stream) {
+                                 sa_host_plan* plan, hipStream_t host_stream,
+                                 hipStream_t recall_stream) {
   SA_NOT_NULL(plan);
   return step_impl(dims, kind, hidden, top_k, scale, seq_lens, num_layers, layers, ws, ws_bytes,
-                   stream, side_stream, plan, host_stream);
+                   stream, side_stream, plan, host_stream, recall_stream);
 }
 
 }  // extern "C"

@@ -65,14 +65,15 @@ hipError_t launch_dense_lists(const Shape& s, const int* seq_lens, const int* bl
                               int* lists, int* counts, hipStream_t stream);
 
 // ---- periodic recall: the plan (one wave per pair), then one workgroup per copied block -----
-// copies: [pairs][max_recall] int2 (pool page, host page); k_host/v_host device-addressable
+// copies: [pairs][max_recall] int2 (pool page, host page); k_host/v_host device-addressable;
+// threshold >= 0: nothing moves unless the layer's offloaded selected blocks exceed it
 size_t recall_plan_lds_bytes(const Shape& s, int max_recall);
 hipError_t launch_recall(const Shape& s, int list_stride, int max_recall, const int* seq_lens,
                          int* block_table, const int* gpu_blocks, const int* n_gpu,
                          const int* cpu_blocks, const int* n_cpu, const void* k_host,
                          const void* v_host, const int* host_table, int host_pages,
                          void* k_pool, void* v_pool, int* n_recalled, void* copies,
-                         hipStream_t stream);
+                         long threshold, hipStream_t stream);
 
 // q_out[r][c] = the sum of the parts of q, for rows r < rows and columns c < n (n a multiple of
 // 4); q_out may be device-addressable host memory

@@ -1,7 +1,8 @@
 // Periodic KV recall [arXiv:2603.27138, HTML Sec. 3.4]: offloaded blocks that the current
 // selection needs come back from host memory into GPU pages, so the share of the budget the
 // CPU attends stays small.  Two launches:
-//   recall_plan_kernel -- one wave per (sequence, KV head): which blocks move where.  The
+//   recall_plan_kernel -- one wave per (sequence, KV head): which blocks move where, if the
+//     layer is due (optionally: its offloaded selected blocks above a threshold).  The
 //     candidates are the pair's offloaded selected blocks (cpu list order) that lie inside the
 //     sequence, are not resident and have a host page; the evicted blocks are the resident
 //     blocks outside the current selection, in ascending order; candidate t takes the page of
@@ -22,7 +23,8 @@ __global__ __launch_bounds__(kWave) void recall_plan_kernel(
     int* __restrict__ block_table, const int* __restrict__ gpu_blocks,
     const int* __restrict__ n_gpu, const int* __restrict__ cpu_blocks,
     const int* __restrict__ n_cpu, int list_stride, const int* __restrict__ host_table,
-    int host_pages, int max_recall, int2* __restrict__ copies, int* __restrict__ n_recalled) {
+    int host_pages, int max_recall, long threshold, int2* __restrict__ copies,
+    int* __restrict__ n_recalled) {
   extern __shared__ int lds[];
   const int words = (max_blocks + 31) / 32;
   unsigned* sel = reinterpret_cast<unsigned*>(lds);  // selection bitmap over the blocks
@@ -39,6 +41,18 @@ __global__ __launch_bounds__(kWave) void recall_plan_kernel(
   const int ng = min(max(n_gpu[pair], 0), list_stride);
   const int nc = min(max(n_cpu[pair], 0), list_stride);
 
+  // the trigger (threshold >= 0): the layer's offloaded selected blocks, over all pairs, must
+  // exceed it, or nothing moves; every workgroup counts them itself
+  if (threshold >= 0) {
+    long total = 0;
+    const int pairs = gridDim.x;
+    for (int p = lane; p < pairs; p += kWave) total += min(max(n_cpu[p], 0), list_stride);
+    for (int off = kWave / 2; off > 0; off >>= 1) total += __shfl_xor(total, off);
+    if (total <= threshold) {
+      if (lane == 0) n_recalled[pair] = 0;
+      return;
+    }
+  }
   for (int w = lane; w < words; w += kWave) sel[w] = 0u;
   __syncthreads();
   for (int j = lane; j < ng + nc; j += kWave) {
@@ -139,13 +153,14 @@ hipError_t launch_recall(const Shape& s, int list_stride, int max_recall, const 
                          const int* cpu_blocks, const int* n_cpu, const void* k_host,
                          const void* v_host, const int* host_table, int host_pages,
                          void* k_pool, void* v_pool, int* n_recalled, void* copies,
-                         hipStream_t stream) {
+                         long threshold, hipStream_t stream) {
   const int pairs = s.B * s.Hkv;
   int2* cp = static_cast<int2*>(copies);
   hipLaunchKernelGGL(recall_plan_kernel, dim3(pairs), dim3(kWave),
                      recall_plan_lds_bytes(s, max_recall), stream, seq_lens, s.Hkv, s.bs,
                      s.max_blocks, s.P, block_table, gpu_blocks, n_gpu, cpu_blocks, n_cpu,
-                     list_stride, host_table, host_pages, max_recall, cp, n_recalled);
+                     list_stride, host_table, host_pages, max_recall, threshold, cp,
+                     n_recalled);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(max_recall, pairs), block(kCopyThreads);

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 8
+#define SA_ABI_VERSION 9
 
 typedef enum {
   SA_OK = 0,
@@ -371,6 +371,27 @@ sa_status sa_host_plan_create(const sa_dims* dims, int32_t top_k, float scale,
                               const sa_host_layer* layers, int32_t num_threads,
                               sa_host_plan** plan);
 sa_status sa_host_plan_run(sa_host_plan* plan, int32_t layer);
+
+/* sa_host_plan_set_recall -- periodic recall inside the offload step ([HTML Sec. 3.4]: the
+ * recall is issued after the layer's attention, off the critical path, and is needed only
+ * at the same layer of the next step).  With it set, sa_decode_step_offload enqueues, after
+ * each layer's merge, sa_recall_blocks for that layer on recall_stream, gated on the device:
+ * nothing moves unless the layer's CPU compute ratio, sum of n_cpu over pairs / (pairs *
+ * top_k), is above beta.  The plan's k_host / v_host must then be page-locked memory the
+ * device reads (hipHostMalloc), and each layer's block_table, k_pool and v_pool in the
+ * step's sa_layer are written (the step's own selection and attention of that layer are
+ * over by then).  layers: num_layers entries (host array, copied): host_table_dev, the
+ * layer's host_table in device memory (NULL: the layer is never recalled), and n_recalled
+ * [B][Hkv] device int32, the blocks moved per pair at the layer's last step (0 when not
+ * due).  ws: sa_recall_workspace_bytes(dims, max_recall) device bytes, used by one layer at a
+ * time (the recalls run in order on recall_stream); it and the arrays must outlive the plan's
+ * use.  max_recall in [1, 4096], beta >= 0.  layers == NULL turns recall off again. */
+typedef struct {
+  const int32_t* host_table_dev;
+  int32_t* n_recalled;
+} sa_recall_layer;
+sa_status sa_host_plan_set_recall(sa_host_plan* plan, int32_t max_recall, float beta,
+                                  const sa_recall_layer* layers, void* ws, size_t ws_bytes);
 sa_status sa_host_plan_destroy(sa_host_plan* plan);
 sa_status sa_host_plan_stats(const sa_host_plan* plan, int64_t* tasks, double* busy_seconds);
 
@@ -384,14 +405,17 @@ sa_status sa_host_plan_stats(const sa_host_plan* plan, int64_t* tasks, double* b
  * into o_host/m_host/l_host; layer i's merge on `stream` waits for that task.  host_stream
  * must be a stream of its own (not `stream`, not side_stream): each task holds it while it
  * runs.  Layer 0 has no layer before it, so its merge waits for its own CPU side.  Before
- * returning, `stream` waits for host_stream and side_stream.  A HIP graph may be captured
- * from `stream`; its host tasks then run with the plan's buffers at every replay.
+ * returning, `stream` waits for host_stream, side_stream and recall_stream.  recall_stream
+ * (a stream of its own, or NULL) carries the recalls when the plan has them set
+ * (sa_host_plan_set_recall); it is required then.  A HIP graph may be captured from
+ * `stream`; its host tasks then run with the plan's buffers at every replay.
  * ------------------------------------------------------------------------------------- */
 sa_status sa_decode_step_offload(const sa_dims* dims, sa_digest_kind kind, int32_t hidden,
                                  int32_t top_k, float scale, const int32_t* seq_lens,
                                  int32_t num_layers, const sa_layer* layers, void* ws,
                                  size_t ws_bytes, hipStream_t stream, hipStream_t side_stream,
-                                 sa_host_plan* plan, hipStream_t host_stream);
+                                 sa_host_plan* plan, hipStream_t host_stream,
+                                 hipStream_t recall_stream);
 
 /* ---------------------------------------------------------------------------------------
  * sa_dense_decode -- dense paged decode attention (FullKV, the pages' uncompressed baseline

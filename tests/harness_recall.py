@@ -176,3 +176,78 @@ def run_recall(wl: wk.Workload, max_recall: int):
     assert ties <= max(1, pairs * len(data) // 100)
     H.log(f"  second step matches the oracle: max_err={max_err:.2e} ties={ties}")
     return dict(moved=moved_total, n_cpu_before=n_cpu_before, n_cpu_after=n_cpu_after)
+
+
+def run_step_with_recall(wl: wk.Workload, beta: float, max_recall: int):
+    """The offload step with periodic recall inside it (sa_host_plan_set_recall): after each
+    layer's merge the step recalls that layer on a fourth stream when its CPU share (in
+    blocks) is above beta.  Checked against the oracle's recall_due and recall_pair on the
+    step's own lists, bit for bit (tables, counts, moved pages); layers not due must be
+    untouched.  Then the next step's CPU share must not be higher."""
+    dev = "cuda"
+    B_, Hkv, d, bs, k = wl.batch, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k
+    pairs = B_ * Hkv
+    data = HS.prepare_step(wl, "cpu")
+    lens = wk.seq_lens(wl)
+    lens_d = lens.to(dev)
+    P = data[0]["pool"]["K"].shape[0]
+    dims = H.dims_for(wl, P)
+    layers = HS.device_layers(wl, data, dims, lens_d, "mean", handoff=False)
+    stores, host_layers = HS.host_side(wl, data)
+    for h in host_layers:  # the recall reads the host store from the device: page-locked
+        for n in ("k_host", "v_host"):
+            pinned = B.pinned_empty(tuple(h[n].shape), h[n].dtype)
+            pinned.copy_(h[n])
+            h[n] = pinned
+    plan = B.HostPlan(dims, k, wl.scale, lens.clone(), host_layers, threads=3)
+    rec = [dict(host_table_dev=st["table"].to(dev),
+                n_recalled=torch.full((pairs,), -7, dtype=torch.int32, device=dev))
+           for st in stores]
+    plan.set_recall(dims, max_recall, beta, rec)
+    ws = B.workspace(B.sa_step_workspace_bytes(dims, wl.hidden, k))
+    side, host, recall = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    tables0 = [L["block_table"].cpu().clone() for L in layers]
+    kp0 = [L["k_pool"].cpu().clone() for L in layers]
+    try:
+        B.sa_decode_step_offload(dims, "mean", wl.hidden, k, wl.scale, lens_d, layers, ws, plan,
+                                 host, side_stream=side, recall_stream=recall)
+        torch.cuda.synchronize()
+        due_layers, moved = 0, 0
+        share0 = sum(int(L["n_cpu"].sum()) for L in layers)
+        for i, L in enumerate(layers):
+            ncl = L["n_cpu"].cpu()
+            due = so.recall_due(ncl.numpy(), k, beta)
+            tab = L["block_table"].cpu().view(pairs, -1)
+            nrec = rec[i]["n_recalled"].cpu()
+            if not due:
+                assert torch.equal(tab, tables0[i].view(pairs, -1)), f"layer {i} not due, changed"
+                assert torch.equal(L["k_pool"].cpu(), kp0[i]), f"layer {i} not due, pages changed"
+                assert int(nrec.abs().sum()) == 0, f"layer {i}: n_recalled {nrec.tolist()}"
+                continue
+            due_layers += 1
+            gl, cl, ngl = L["gpu_blocks"].cpu(), L["cpu_blocks"].cpu(), L["n_gpu"].cpu()
+            kp, vp = L["k_pool"].cpu(), L["v_pool"].cpu()
+            for p in range(pairs):
+                s, h = divmod(p, Hkv)
+                want, moves = so.recall_pair(
+                    tables0[i].view(pairs, -1)[p].numpy(), int(lens[s]), bs,
+                    gl[p, :int(ngl[p])].numpy(), cl[p, :int(ncl[p])].numpy(),
+                    stores[i]["table"][s, h].numpy(), max_recall)
+                assert np.array_equal(tab[p].numpy(), want), f"layer {i} pair {p}: table"
+                assert int(nrec[p]) == len(moves), f"layer {i} pair {p}: n_recalled"
+                for b, page, hp in moves:
+                    assert torch.equal(unpack_k(kp[page], bs, d), stores[i]["K"][hp])
+                    assert torch.equal(unpack_v(vp[page], bs, d), stores[i]["V"][hp])
+                moved += len(moves)
+        # the next step, over the new residency
+        B.sa_decode_step_offload(dims, "mean", wl.hidden, k, wl.scale, lens_d, layers, ws, plan,
+                                 host, side_stream=side, recall_stream=recall)
+        torch.cuda.synchronize()
+        share1 = sum(int(L["n_cpu"].sum()) for L in layers)
+    finally:
+        torch.cuda.synchronize()
+        plan.close()
+    assert share1 <= share0 - moved, (share0, share1, moved)
+    H.log(f"  in-step recall beta={beta}: {due_layers}/{len(layers)} layers due, {moved} blocks "
+          f"moved, offloaded selected blocks {share0} -> {share1}")
+    return dict(due=due_layers, moved=moved, share0=share0, share1=share1)

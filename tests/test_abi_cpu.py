@@ -37,7 +37,7 @@ def test_header_declares_the_path(lib):
               "sa_host_plan_create", "sa_host_plan_destroy", "sa_host_plan_stats",
               "sa_host_plan_run", "sa_recall_blocks", "sa_recall_workspace_bytes",
               "sa_dense_decode", "sa_dense_workspace_bytes",
-              "sa_decode_step_offload"):
+              "sa_decode_step_offload", "sa_host_plan_set_recall"):
         assert n in names
 
 
@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.sa_abi_version() == B.ABI_VERSION == 8
+    assert lib.sa_abi_version() == B.ABI_VERSION == 9
     assert lib.sa_status_string(B.SA_ERR_WORKSPACE) == b"SA_ERR_WORKSPACE"
 
 
@@ -252,9 +252,10 @@ def test_offload_step_validation(lib):
                 setattr(L, name, FAKE)
             L.host_o = L.host_m = L.host_l = L.cpu_blocks_host = L.n_cpu_host = None
 
-        def step(dd=d, top_k=8, scale=0.088, n=2, p=plan, host=FAKE + 3, side=FAKE + 2):
+        def step(dd=d, top_k=8, scale=0.088, n=2, p=plan, host=FAKE + 3, side=FAKE + 2,
+                 rec=None):
             return lib.sa_decode_step_offload(ctypes.byref(dd), 0, 1024, top_k, scale, FAKE, n,
-                                              layers, FAKE, ws, FAKE + 1, side, p, host)
+                                              layers, FAKE, ws, FAKE + 1, side, p, host, rec)
 
         assert step(p=None) == B.SA_ERR_INVALID_ARG
         assert step(dd=dims(batch=3)) == B.SA_ERR_INVALID_ARG
@@ -266,6 +267,22 @@ def test_offload_step_validation(lib):
         assert step(host=FAKE + 1) == B.SA_ERR_INVALID_ARG  # the main stream
         assert step(host=FAKE + 2) == B.SA_ERR_INVALID_ARG  # the side stream
         assert b"stream of its own" in lib.sa_last_error()
+        # with recall set, a recall stream of its own is required
+        rl = (B.sa_recall_layer * 2)()
+        for r in rl:
+            r.host_table_dev, r.n_recalled = FAKE, FAKE
+        rws = lib.sa_recall_workspace_bytes(ctypes.byref(d), 8)
+        assert lib.sa_host_plan_set_recall(plan, 8, 0.12, rl, FAKE, rws - 1) == B.SA_ERR_WORKSPACE
+        assert lib.sa_host_plan_set_recall(plan, 0, 0.12, rl, FAKE, rws) == B.SA_ERR_INVALID_ARG
+        assert lib.sa_host_plan_set_recall(plan, 8, -1.0, rl, FAKE, rws) == B.SA_ERR_INVALID_ARG
+        rl[1].n_recalled = None
+        assert lib.sa_host_plan_set_recall(plan, 8, 0.12, rl, FAKE, rws) == B.SA_ERR_INVALID_ARG
+        rl[1].n_recalled = FAKE
+        assert lib.sa_host_plan_set_recall(plan, 8, 0.12, rl, FAKE, rws) == B.SA_OK
+        assert step(rec=None) == B.SA_ERR_INVALID_ARG
+        assert step(rec=FAKE + 3) == B.SA_ERR_INVALID_ARG  # the host stream
+        assert b"recall_stream" in lib.sa_last_error()
+        assert lib.sa_host_plan_set_recall(plan, 0, 0.0, None, None, 0) == B.SA_OK  # off
         # without a plan the same layers lack their host partials
         assert lib.sa_decode_step(ctypes.byref(d), 0, 1024, 8, 0.088, FAKE, 2, layers, FAKE,
                                   ws, None, None) == B.SA_ERR_INVALID_ARG

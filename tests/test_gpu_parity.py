@@ -299,6 +299,22 @@ def test_recall_parity(pool, max_recall, ragged):
     assert r["moved"] > 0
 
 
+@pytest.mark.parametrize("beta", [0.0, 0.12, 1.0])
+def test_step_with_recall_parity(beta):
+    """Periodic recall inside the offload step, gated on the device by the CPU share against
+    beta: due layers match the oracle's recall bit for bit, the others are untouched."""
+    H.log(f"[case] step with in-step recall, beta={beta}")
+    import harness_recall as HR
+    r = HR.run_step_with_recall(wk.QWEN3_14B_STEP.scaled(batch=3, num_q_heads=10,
+                                                         num_kv_heads=2, context=2000, layers=4,
+                                                         pool_blocks=12, hidden=512, top_k=8),
+                                beta, 64)
+    if beta >= 1.0:
+        assert r["due"] == 0 and r["moved"] == 0
+    if beta == 0.0:
+        assert r["moved"] > 0
+
+
 def test_step_parity_minmax_no_handoff():
     H.log("[case] step minmax")
     import harness_step as HS
