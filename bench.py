@@ -360,7 +360,7 @@ def dense_measure(wl, args, torch, B, wk, sparse_us):
     return out
 
 
-def drift_measure(wl, dims, lens, layers, ws, side_stream, store, args, torch, B):
+def drift_measure(wl, dims, lens, layers, ws, side_stream, store, args, torch, B):  # noqa: C901
     """The CPU share over decode steps whose inputs drift, without and with periodic recall.
 
     Each step moves every layer's input, X^i <- rho X^i + sqrt(1 - rho^2) Z (Z ~ N(0, 1),
@@ -411,20 +411,82 @@ def drift_measure(wl, dims, lens, layers, ws, side_stream, store, args, torch, B
                     moved += int(n_rec.sum())
         return shares, recalls, moved, rec_ms
 
+    def run_offload(recall):
+        """The whole system: the CPU side as host tasks one layer ahead, and (recall) periodic
+        recall inside the step, gated on the device by beta; per-step time and share."""
+        for L, x in zip(layers, x0):
+            L["x"].copy_(x)
+        f32 = torch.float32
+        hls = [dict(k_host=store["K"], v_host=store["V"], host_table=store["table"],
+                    q_host=B.pinned_empty((Bsz, wl.num_q_heads, wl.head_dim), f32),
+                    cpu_blocks_host=B.pinned_empty((pairs, k)),
+                    n_cpu_host=B.pinned_empty((pairs,)),
+                    o_host=B.pinned_empty((Bsz, wl.num_q_heads, wl.head_dim), f32),
+                    m_host=B.pinned_empty((Bsz, wl.num_q_heads), f32),
+                    l_host=B.pinned_empty((Bsz, wl.num_q_heads), f32)) for _ in layers]
+        threads = max(1, min(args.host_threads, os.cpu_count() or 1))
+        plan = B.HostPlan(dims, k, wl.scale, lens.cpu().contiguous(), hls, threads=threads)
+        host_stream, recall_stream = torch.cuda.Stream(), torch.cuda.Stream()
+        nrec = [torch.zeros(pairs, dtype=torch.int32, device="cuda") for _ in layers]
+        if recall:
+            plan.set_recall(dims, k, args.beta,
+                            [dict(host_table_dev=table_d, n_recalled=n) for n in nrec], rws)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(4242)
+        shares, ms, moved = [], [], 0
+        try:
+            for _ in range(args.drift_steps):
+                for L in layers:
+                    z = torch.randn(L["x"].shape, generator=g, device="cuda")
+                    L["x"].copy_((args.drift_rho * L["x"].float() + c * z).to(torch.bfloat16))
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                B.sa_decode_step_offload(dims, "mean", wl.hidden, k, wl.scale, lens, layers, ws,
+                                         plan, host_stream, side_stream=side_stream,
+                                         recall_stream=recall_stream if recall else None)
+                e1.record()
+                torch.cuda.synchronize()
+                ms.append(round(e0.elapsed_time(e1), 3))
+                shares.append(round(sum(int(L["n_cpu"].sum()) for L in layers)
+                                    / (len(layers) * pairs * k), 4))
+                moved += sum(int(n.sum()) for n in nrec) if recall else 0
+        finally:
+            torch.cuda.synchronize()
+            plan.close()
+        return shares, ms, moved
+
     t0 = time.time()
     s0, _, _, _ = run(False)
-    s1, recalls, moved, rec_ms = run(True)
-    log(f"drift: {args.drift_steps} steps in {time.time() - t0:.1f} s; mean CPU share "
-        f"{sum(s0) / len(s0):.3f} without recall, {sum(s1) / len(s1):.3f} with "
-        f"({recalls} layer recalls)")
-    return {"steps": args.drift_steps, "rho": args.drift_rho, "beta": args.beta,
-            "cpu_share_no_recall": s0, "cpu_share_with_recall": s1,
-            "mean_no_recall": round(sum(s0) / len(s0), 4),
-            "mean_with_recall": round(sum(s1) / len(s1), 4),
-            "layer_recalls": recalls, "layers": wl.layers, "blocks_moved": moved,
-            "recall_ms_total": round(rec_ms, 2),
-            "note": "CPU share = offloaded selected blocks / budget, averaged over the layers "
-                    "after each step; a layer is recalled when its share exceeds beta"}
+    out = {"steps": args.drift_steps, "rho": args.drift_rho, "beta": args.beta,
+           "cpu_share_no_recall": s0, "mean_no_recall": round(sum(s0) / len(s0), 4),
+           "layers": wl.layers,
+           "note": "CPU share = offloaded selected blocks / budget, averaged over the layers "
+                   "after each step; a layer is recalled when its share exceeds beta"}
+    if args.offload:
+        # the whole system; the run with recall changes the pools, so it goes last
+        so0, ms0, _ = run_offload(False)
+        so1, ms1, moved = run_offload(True)
+        assert so0 == s0, "the offload step selects as the GPU-only step does"
+        out.update({"cpu_share_with_recall": so1, "mean_with_recall": round(sum(so1) / len(so1), 4),
+                    "blocks_moved": moved, "recall": "inside the offload step (4th stream)",
+                    "offload_ms_per_step_no_recall": ms0,
+                    "offload_ms_per_step_with_recall": ms1,
+                    "mean_offload_ms_no_recall": round(sum(ms0) / len(ms0), 3),
+                    "mean_offload_ms_with_recall": round(sum(ms1) / len(ms1), 3),
+                    "launch": "eager"})
+        log(f"drift: offload step {out['mean_offload_ms_no_recall']} ms without recall, "
+            f"{out['mean_offload_ms_with_recall']} ms with in-step recall; mean CPU share "
+            f"{out['mean_no_recall']} -> {out['mean_with_recall']}")
+    else:
+        s1, recalls, moved, rec_ms = run(True)
+        out.update({"cpu_share_with_recall": s1, "mean_with_recall": round(sum(s1) / len(s1), 4),
+                    "layer_recalls": recalls, "blocks_moved": moved,
+                    "recall_ms_total": round(rec_ms, 2), "recall": "between steps"})
+        log(f"drift: mean CPU share {out['mean_no_recall']:.3f} without recall, "
+            f"{out['mean_with_recall']:.3f} with ({recalls} layer recalls)")
+    log(f"drift: done in {time.time() - t0:.1f} s")
+    return out
 
 
 def offload_measure(wl, dims, lens, layers, ws, side_stream, ms_gpu, args, torch, B, wk,
