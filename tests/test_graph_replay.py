@@ -53,9 +53,13 @@ def same(a, b):
     return all(torch.equal(x, y) for x, y in zip(a, b)) and len(a) == len(b)
 
 
-@pytest.mark.parametrize("offload", [False, True], ids=["step", "step-with-host-tasks"])
-def test_step_graph_replays_match_eager(offload):
-    H.log(f"[case] graph replay, offload={offload}")
+@pytest.mark.parametrize("offload,recall", [(False, False), (True, False), (True, True)],
+                         ids=["step", "step-with-host-tasks", "step-with-host-tasks-and-recall"])
+def test_step_graph_replays_match_eager(offload, recall):
+    """With recall (beta 0), the first eager step recalls every offloaded selected block it
+    can, and the state is then stable: later steps find nothing due, on the device, inside
+    the graph as well."""
+    H.log(f"[case] graph replay, offload={offload} recall={recall}")
     data = HS.prepare_step(WL, "cpu")
     lens = wk.seq_lens(WL)
     lens_d = lens.to("cuda")
@@ -64,15 +68,30 @@ def test_step_graph_replays_match_eager(offload):
     ws = B.workspace(B.sa_step_workspace_bytes(dims, WL.hidden, WL.top_k))
     side = torch.cuda.Stream()
     host_layers = plan = None
+    recall_stream = None
     if offload:
-        _, host_layers = HS.host_side(WL, data)
+        stores, host_layers = HS.host_side(WL, data)
+        if recall:  # the recall reads the host store from the device: page-locked
+            for h in host_layers:
+                for n in ("k_host", "v_host"):
+                    pinned = B.pinned_empty(tuple(h[n].shape), h[n].dtype)
+                    pinned.copy_(h[n])
+                    h[n] = pinned
         plan = B.HostPlan(dims, WL.top_k, WL.scale, lens.clone(), host_layers, threads=3)
         host_stream = torch.cuda.Stream()
+        if recall:
+            pairs = WL.batch * WL.num_kv_heads
+            plan.set_recall(dims, 64, 0.0, [
+                dict(host_table_dev=st["table"].to("cuda"),
+                     n_recalled=torch.zeros(pairs, dtype=torch.int32, device="cuda"))
+                for st in stores])
+            recall_stream = torch.cuda.Stream()
 
     def step():
         if offload:
             B.sa_decode_step_offload(dims, "mean", WL.hidden, WL.top_k, WL.scale, lens_d, layers,
-                                     ws, plan, host_stream, side_stream=side)
+                                     ws, plan, host_stream, side_stream=side,
+                                     recall_stream=recall_stream)
         else:
             B.sa_decode_step(dims, "mean", WL.hidden, WL.top_k, WL.scale, lens_d, layers, ws,
                              side_stream=side)
@@ -80,7 +99,14 @@ def test_step_graph_replays_match_eager(offload):
     try:
         step()
         torch.cuda.synchronize()
+        if recall:  # the first step recalled; from here on the state is stable
+            moved = sum(int(L["n_cpu"].sum()) for L in layers)
+            step()
+            torch.cuda.synchronize()
+            assert sum(int(L["n_cpu"].sum()) for L in layers) < moved
         ref = snapshot(layers, host_layers)
+        if recall:
+            ref += [L["block_table"].clone() for L in layers]
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             step()
@@ -90,17 +116,23 @@ def test_step_graph_replays_match_eager(offload):
             torch.cuda.synchronize()
             graph.replay()
             torch.cuda.synchronize()
-            assert same(snapshot(layers, host_layers), ref), f"replay {rep}"
+            got = snapshot(layers, host_layers)
+            if recall:
+                got += [L["block_table"].clone() for L in layers]
+            assert same(got, ref), f"replay {rep}"
             poison(layers, host_layers)
             step()  # eager work between the replays
             torch.cuda.synchronize()
-            assert same(snapshot(layers, host_layers), ref), f"eager step after replay {rep}"
+            got = snapshot(layers, host_layers)
+            if recall:
+                got += [L["block_table"].clone() for L in layers]
+            assert same(got, ref), f"eager step after replay {rep}"
         del graph
         torch.cuda.synchronize()
         if offload:
             tasks, _ = plan.stats()
             # the capture enqueues no task; each eager step and each replay runs one per layer
-            assert tasks == WL.layers * 7, tasks
+            assert tasks == WL.layers * (8 if recall else 7), tasks
     finally:
         if plan is not None:
             torch.cuda.synchronize()
