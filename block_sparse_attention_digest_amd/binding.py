@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libscoutattn.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = 0, -1, -2, -3, -4
 SA_F32, SA_BF16 = 0, 1
 SA_DIGEST_MEAN, SA_DIGEST_MINMAX = 0, 1
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 KIND = {"mean": SA_DIGEST_MEAN, "minmax": SA_DIGEST_MINMAX}
 
@@ -101,7 +101,7 @@ SIGNATURES = {
                                               ctypes.POINTER(sa_layer), _P, _Z, _P, _P, _P, _P,
                                               _P]),
     "sa_host_plan_set_recall": (ctypes.c_int, [_P, _I, _F, ctypes.POINTER(sa_recall_layer), _P,
-                                               _Z]),
+                                               _Z, _I]),
     "sa_host_partial_attention": (ctypes.c_int, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _I, _F,
                                                  _P, _P, _P, _I]),
 }
@@ -510,12 +510,13 @@ class HostPlan:
         _check(lib().sa_host_plan_stats(self.handle, ctypes.byref(n), ctypes.byref(t)))
         return n.value, t.value
 
-    def set_recall(self, dims: Dims, max_recall: int, beta: float, layers, ws=None):
+    def set_recall(self, dims: Dims, max_recall: int, beta: float, layers, ws=None,
+                   overlap: bool = False):
         """Periodic recall inside the offload step (sa_host_plan_set_recall): `layers` is a
         list of dicts with host_table_dev (GPU int32 [B][Hkv][max_blocks], or None) and
         n_recalled (GPU int32 [B][Hkv]); None turns recall off."""
         if layers is None:
-            _check(lib().sa_host_plan_set_recall(self.handle, 0, 0.0, None, None, 0))
+            _check(lib().sa_host_plan_set_recall(self.handle, 0, 0.0, None, None, 0, 0))
             self._recall = None
             return
         pairs = dims.batch * dims.num_kv_heads
@@ -529,7 +530,8 @@ class HostPlan:
                                      f"[{i}].n_recalled")
         self._recall = (layers, ws)
         _check(lib().sa_host_plan_set_recall(self.handle, max_recall, beta, arr,
-                                             _ptr(ws, torch.uint8, name="ws"), ws.numel()))
+                                             _ptr(ws, torch.uint8, name="ws"), ws.numel(),
+                                             1 if overlap else 0))
 
     def run(self, layer: int):
         """Layer `layer`'s host task now, on this thread and the plan's workers."""

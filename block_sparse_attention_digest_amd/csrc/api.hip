@@ -610,6 +610,14 @@ struct sa_host_plan {
   int max_recall = 0;
   long recall_threshold = 0;  // the layer recalls when its offloaded selected blocks exceed it
   void* recall_ws = nullptr;
+  // overlap mode: a step leaves its recalls running; layer i's event, recorded after its
+  // recall, is waited for by the next step's selection of layer i
+  bool recall_overlap = false;
+  std::vector<hipEvent_t> recall_done;
+  std::vector<char> recall_pending;
+  ~sa_host_plan() {
+    for (hipEvent_t e : recall_done) hipEventDestroy(e);
+  }
 };
 
 // A layer's host task: A_cpu on the plan's workers; false if no worker could run (the
@@ -690,10 +698,15 @@ sa_status sa_host_plan_run(sa_host_plan* plan, int32_t layer) {
 }
 
 sa_status sa_host_plan_set_recall(sa_host_plan* plan, int32_t max_recall, float beta,
-                                  const sa_recall_layer* layers, void* ws, size_t ws_bytes) {
+                                  const sa_recall_layer* layers, void* ws, size_t ws_bytes,
+                                  int32_t overlap) {
   SA_NOT_NULL(plan);
+  for (hipEvent_t e : plan->recall_done)  // a step may still be recalling: let it finish
+    if (hipEventSynchronize(e) != hipSuccess) return fail(SA_ERR_HIP, "hipEventSynchronize");
+  std::fill(plan->recall_pending.begin(), plan->recall_pending.end(), 0);
   if (!layers) {
     plan->recall.clear();
+    plan->recall_overlap = false;
     return ok();
   }
   if (max_recall < 1 || max_recall > kMaxRecall)
@@ -719,6 +732,15 @@ sa_status sa_host_plan_set_recall(sa_host_plan* plan, int32_t max_recall, float 
   plan->recall_threshold =
       (long)std::floor((double)beta * (double)plan->s.B * plan->s.Hkv * plan->top_k);
   plan->recall_ws = ws;
+  plan->recall_overlap = overlap != 0;
+  if (plan->recall_overlap && plan->recall_done.empty()) {
+    for (int i = 0; i < L; ++i) {
+      hipEvent_t e;
+      SA_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming), "hipEventCreate");
+      plan->recall_done.push_back(e);
+    }
+    plan->recall_pending.assign(L, 0);
+  }
   return ok();
 }
 
@@ -829,6 +851,14 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
                   "the plan recalls: recall_stream must be a stream of its own");
   }
   const bool recalls = plan && !plan->recall.empty();
+  const bool overlap = recalls && plan->recall_overlap;
+  if (overlap) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    SA_HIP(hipStreamIsCapturing(stream, &cs), "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+      return fail(SA_ERR_INVALID_ARG,
+                  "recalls that overlap the next step cannot be captured (set overlap 0)");
+  }
   const StepLayout SL = step_layout(s, hidden, top_k);
   if (!ws || ws_bytes < SL.total)
     return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, SL.total);
@@ -880,6 +910,14 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
     return plan ? plan->layers[j].cpu_blocks_host : layers[j].cpu_blocks_host;
   };
   auto mirror_n = [&](int j) { return plan ? plan->layers[j].n_cpu_host : layers[j].n_cpu_host; };
+  // overlap mode: the selection of layer j (which rewrites the lists layer j's pending recall
+  // reads, and reads the table it writes) waits for that recall first
+  auto after_recall = [&](int j, hipStream_t on) -> sa_status {
+    if (!overlap || !plan->recall_pending[j]) return SA_OK;
+    SA_HIP(hipStreamWaitEvent(on, plan->recall_done[j], 0), "hipStreamWaitEvent");
+    plan->recall_pending[j] = 0;
+    return SA_OK;
+  };
   sa_status st = SA_OK;
   hipEvent_t sel_done = nullptr;  // side stream: the selection of the coming layer is done
   for (int i = 0; i < num_layers && st == SA_OK; ++i) {
@@ -913,7 +951,9 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
     // 2. the first layer selects with its own query (on `stream`: its attention needs it);
     //    the selection kernels also write the offloaded lists into the host mirrors
     if (i == 0) {
-      st = run_select(s, minmax, q_cur, L.digests, seq_lens, top_k, L.block_table,
+      st = after_recall(0, stream);
+      if (st == SA_OK)
+        st = run_select(s, minmax, q_cur, L.digests, seq_lens, top_k, L.block_table,
                       L.gpu_blocks, L.n_gpu, L.cpu_blocks, L.n_cpu, nullptr, mirror_blocks(0),
                       mirror_n(0), pages[0], stream);
       if (st == SA_OK && plan) st = spawn_host(0, q_cur, stream);
@@ -931,6 +971,7 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
         if (e != hipSuccess) st = hip_fail(e, "GEMM kernel");
         q_next = sa::gemm_result(SL.plan_single, s.B, n, 1, 0, qp, gemm_ws[1]);
       }
+      if (st == SA_OK) st = after_recall(i + 1, sel_stream);
       if (st == SA_OK)
         st = run_select(s, minmax, q_next, N.digests, seq_lens, top_k, N.block_table,
                         N.gpu_blocks, N.n_gpu, N.cpu_blocks, N.n_cpu, nullptr,
@@ -986,6 +1027,13 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
                             plan->recall[i].n_recalled, plan->recall_ws,
                             plan->recall_threshold, recall_stream);
       if (e != hipSuccess) { st = hip_fail(e, "recall kernels"); break; }
+      if (overlap) {
+        if (hipEventRecord(plan->recall_done[i], recall_stream) != hipSuccess) {
+          st = fail(SA_ERR_HIP, "hipEventRecord failed");
+          break;
+        }
+        plan->recall_pending[i] = 1;
+      }
     }
   }
   // join the side stream and the host tasks back into `stream`
@@ -997,7 +1045,7 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
     sa_status j = order(host_stream, stream);
     if (st == SA_OK) st = j;
   }
-  if (recalls) {
+  if (recalls && !overlap) {
     sa_status j = order(recall_stream, stream);
     if (st == SA_OK) st = j;
   }

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 9
+#define SA_ABI_VERSION 10
 
 typedef enum {
   SA_OK = 0,
@@ -385,13 +385,20 @@ sa_status sa_host_plan_run(sa_host_plan* plan, int32_t layer);
  * [B][Hkv] device int32, the blocks moved per pair at the layer's last step (0 when not
  * due).  ws: sa_recall_workspace_bytes(dims, max_recall) device bytes, used by one layer at a
  * time (the recalls run in order on recall_stream); it and the arrays must outlive the plan's
- * use.  max_recall in [1, 4096], beta >= 0.  layers == NULL turns recall off again. */
+ * use.  max_recall in [1, 4096], beta >= 0.  layers == NULL turns recall off again.
+ * overlap = 0: each step waits for its recalls before it returns.  overlap != 0: as in the
+ * pages, a step leaves its recalls running and the next step's selection of layer i waits
+ * for layer i's recall only; the caller synchronises recall_stream before it reads or writes
+ * a layer's block table, pages or n_recalled itself, and such steps cannot be captured in a
+ * graph (SA_ERR_INVALID_ARG).  The call waits for recalls still running, and creates the
+ * events it needs on the current device. */
 typedef struct {
   const int32_t* host_table_dev;
   int32_t* n_recalled;
 } sa_recall_layer;
 sa_status sa_host_plan_set_recall(sa_host_plan* plan, int32_t max_recall, float beta,
-                                  const sa_recall_layer* layers, void* ws, size_t ws_bytes);
+                                  const sa_recall_layer* layers, void* ws, size_t ws_bytes,
+                                  int32_t overlap);
 sa_status sa_host_plan_destroy(sa_host_plan* plan);
 sa_status sa_host_plan_stats(const sa_host_plan* plan, int64_t* tasks, double* busy_seconds);
 
@@ -405,7 +412,8 @@ sa_status sa_host_plan_stats(const sa_host_plan* plan, int64_t* tasks, double* b
  * into o_host/m_host/l_host; layer i's merge on `stream` waits for that task.  host_stream
  * must be a stream of its own (not `stream`, not side_stream): each task holds it while it
  * runs.  Layer 0 has no layer before it, so its merge waits for its own CPU side.  Before
- * returning, `stream` waits for host_stream, side_stream and recall_stream.  recall_stream
+ * returning, `stream` waits for host_stream, side_stream and (unless the plan's recalls
+ * overlap the next step) recall_stream.  recall_stream
  * (a stream of its own, or NULL) carries the recalls when the plan has them set
  * (sa_host_plan_set_recall); it is required then.  A HIP graph may be captured from
  * `stream`; its host tasks then run with the plan's buffers at every replay.

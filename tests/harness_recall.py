@@ -251,3 +251,77 @@ def run_step_with_recall(wl: wk.Workload, beta: float, max_recall: int):
     H.log(f"  in-step recall beta={beta}: {due_layers}/{len(layers)} layers due, {moved} blocks "
           f"moved, offloaded selected blocks {share0} -> {share1}")
     return dict(due=due_layers, moved=moved, share0=share0, share1=share1)
+
+
+def _offload_setup(wl, beta, overlap, max_recall=64):
+    dev = "cuda"
+    pairs = wl.batch * wl.num_kv_heads
+    data = HS.prepare_step(wl, "cpu")
+    lens = wk.seq_lens(wl)
+    lens_d = lens.to(dev)
+    dims = H.dims_for(wl, data[0]["pool"]["K"].shape[0])
+    layers = HS.device_layers(wl, data, dims, lens_d, "mean", handoff=False)
+    stores, host_layers = HS.host_side(wl, data)
+    for h in host_layers:
+        for n in ("k_host", "v_host"):
+            pinned = B.pinned_empty(tuple(h[n].shape), h[n].dtype)
+            pinned.copy_(h[n])
+            h[n] = pinned
+    plan = B.HostPlan(dims, wl.top_k, wl.scale, lens.clone(), host_layers, threads=2)
+    rec = [dict(host_table_dev=st["table"].to(dev),
+                n_recalled=torch.full((pairs,), -7, dtype=torch.int32, device=dev))
+           for st in stores]
+    plan.set_recall(dims, max_recall, beta, rec, overlap=overlap)
+    ws = B.workspace(B.sa_step_workspace_bytes(dims, wl.hidden, wl.top_k))
+    streams = dict(side_stream=torch.cuda.Stream(), recall_stream=torch.cuda.Stream())
+    host = torch.cuda.Stream()
+
+    def step():
+        B.sa_decode_step_offload(dims, "mean", wl.hidden, wl.top_k, wl.scale, lens_d, layers, ws,
+                                 plan, host, **streams)
+
+    return dict(layers=layers, rec=rec, plan=plan, step=step, host_layers=host_layers)
+
+
+def state(S):
+    out = []
+    for L in S["layers"]:
+        out += [L[n].clone() for n in ("out_o", "out_m", "out_l", "gpu_blocks", "n_gpu",
+                                       "cpu_blocks", "n_cpu", "block_table", "k_pool", "v_pool")]
+    out += [r["n_recalled"].clone() for r in S["rec"]]
+    return out
+
+
+def run_overlap_vs_join(wl, beta, steps=3):
+    """Steps whose recalls overlap the next step against steps that join their recalls: the
+    same computations in another order, so every output, list, table and page must be the
+    same bit for bit after each step.  Also: an overlapping step refuses graph capture."""
+    A = _offload_setup(wl, beta, overlap=False)
+    Bv = _offload_setup(wl, beta, overlap=True)
+    moved = 0
+    try:
+        for t in range(steps):
+            A["step"]()
+            Bv["step"]()
+            torch.cuda.synchronize()
+            sa, sb = state(A), state(Bv)
+            assert all(torch.equal(x, y) for x, y in zip(sa, sb)), f"step {t}"
+            moved += sum(int(r["n_recalled"].sum()) for r in A["rec"])
+        g = torch.cuda.CUDAGraph()
+        refused = False
+        try:
+            with torch.cuda.graph(g):
+                try:
+                    Bv["step"]()
+                except B.SaError:
+                    refused = True
+        except Exception:  # noqa: BLE001 -- an empty capture may itself complain
+            pass
+        assert refused, "an overlapping step was captured"
+        torch.cuda.synchronize()
+    finally:
+        torch.cuda.synchronize()
+        A["plan"].close()
+        Bv["plan"].close()
+    H.log(f"  overlap vs join: {steps} steps identical, {moved} blocks moved")
+    return moved

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.sa_abi_version() == B.ABI_VERSION == 9
+    assert lib.sa_abi_version() == B.ABI_VERSION == 10
     assert lib.sa_status_string(B.SA_ERR_WORKSPACE) == b"SA_ERR_WORKSPACE"
 
 
@@ -272,17 +272,17 @@ def test_offload_step_validation(lib):
         for r in rl:
             r.host_table_dev, r.n_recalled = FAKE, FAKE
         rws = lib.sa_recall_workspace_bytes(ctypes.byref(d), 8)
-        assert lib.sa_host_plan_set_recall(plan, 8, 0.12, rl, FAKE, rws - 1) == B.SA_ERR_WORKSPACE
-        assert lib.sa_host_plan_set_recall(plan, 0, 0.12, rl, FAKE, rws) == B.SA_ERR_INVALID_ARG
-        assert lib.sa_host_plan_set_recall(plan, 8, -1.0, rl, FAKE, rws) == B.SA_ERR_INVALID_ARG
+        assert lib.sa_host_plan_set_recall(plan, 8, 0.12, rl, FAKE, rws - 1, 0) == B.SA_ERR_WORKSPACE
+        assert lib.sa_host_plan_set_recall(plan, 0, 0.12, rl, FAKE, rws, 0) == B.SA_ERR_INVALID_ARG
+        assert lib.sa_host_plan_set_recall(plan, 8, -1.0, rl, FAKE, rws, 0) == B.SA_ERR_INVALID_ARG
         rl[1].n_recalled = None
-        assert lib.sa_host_plan_set_recall(plan, 8, 0.12, rl, FAKE, rws) == B.SA_ERR_INVALID_ARG
+        assert lib.sa_host_plan_set_recall(plan, 8, 0.12, rl, FAKE, rws, 0) == B.SA_ERR_INVALID_ARG
         rl[1].n_recalled = FAKE
-        assert lib.sa_host_plan_set_recall(plan, 8, 0.12, rl, FAKE, rws) == B.SA_OK
+        assert lib.sa_host_plan_set_recall(plan, 8, 0.12, rl, FAKE, rws, 0) == B.SA_OK
         assert step(rec=None) == B.SA_ERR_INVALID_ARG
         assert step(rec=FAKE + 3) == B.SA_ERR_INVALID_ARG  # the host stream
         assert b"recall_stream" in lib.sa_last_error()
-        assert lib.sa_host_plan_set_recall(plan, 0, 0.0, None, None, 0) == B.SA_OK  # off
+        assert lib.sa_host_plan_set_recall(plan, 0, 0.0, None, None, 0, 0) == B.SA_OK  # off
         # without a plan the same layers lack their host partials
         assert lib.sa_decode_step(ctypes.byref(d), 0, 1024, 8, 0.088, FAKE, 2, layers, FAKE,
                                   ws, None, None) == B.SA_ERR_INVALID_ARG

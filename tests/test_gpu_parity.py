@@ -315,6 +315,18 @@ def test_step_with_recall_parity(beta):
         assert r["moved"] > 0
 
 
+def test_step_recall_overlap_matches_join():
+    """Recalls left running into the next step (the next selection of a layer waits for that
+    layer's recall only) give the same results as recalls joined at the end of their step."""
+    H.log("[case] in-step recall, overlap vs join")
+    import harness_recall as HR
+    moved = HR.run_overlap_vs_join(wk.QWEN3_14B_STEP.scaled(batch=3, num_q_heads=10,
+                                                            num_kv_heads=2, context=2000,
+                                                            layers=4, pool_blocks=12, hidden=512,
+                                                            top_k=8), 0.0)
+    assert moved > 0
+
+
 def test_step_parity_minmax_no_handoff():
     H.log("[case] step minmax")
     import harness_step as HS
