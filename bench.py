@@ -428,9 +428,10 @@ def drift_measure(wl, dims, lens, layers, ws, side_stream, store, args, torch, B
         plan = B.HostPlan(dims, k, wl.scale, lens.cpu().contiguous(), hls, threads=threads)
         host_stream, recall_stream = torch.cuda.Stream(), torch.cuda.Stream()
         nrec = [torch.zeros(pairs, dtype=torch.int32, device="cuda") for _ in layers]
-        if recall:
+        if recall:  # recalls overlap the next step, as in the pages
             plan.set_recall(dims, k, args.beta,
-                            [dict(host_table_dev=table_d, n_recalled=n) for n in nrec], rws)
+                            [dict(host_table_dev=table_d, n_recalled=n) for n in nrec], rws,
+                            overlap=True)
         g = torch.Generator(device="cuda")
         g.manual_seed(4242)
         shares, ms, moved = [], [], 0
@@ -446,11 +447,13 @@ def drift_measure(wl, dims, lens, layers, ws, side_stream, store, args, torch, B
                                          plan, host_stream, side_stream=side_stream,
                                          recall_stream=recall_stream if recall else None)
                 e1.record()
-                torch.cuda.synchronize()
+                e1.synchronize()  # the step's own streams; a recall may still be running
                 ms.append(round(e0.elapsed_time(e1), 3))
                 shares.append(round(sum(int(L["n_cpu"].sum()) for L in layers)
                                     / (len(layers) * pairs * k), 4))
-                moved += sum(int(n.sum()) for n in nrec) if recall else 0
+            torch.cuda.synchronize()
+            if recall:
+                moved = sum(int(n.sum()) for n in nrec)  # (the last step's recalls)
         finally:
             torch.cuda.synchronize()
             plan.close()
@@ -469,7 +472,8 @@ def drift_measure(wl, dims, lens, layers, ws, side_stream, store, args, torch, B
         so1, ms1, moved = run_offload(True)
         assert so0 == s0, "the offload step selects as the GPU-only step does"
         out.update({"cpu_share_with_recall": so1, "mean_with_recall": round(sum(so1) / len(so1), 4),
-                    "blocks_moved": moved, "recall": "inside the offload step (4th stream)",
+                    "blocks_moved_last_step": moved,
+                    "recall": "inside the offload step (4th stream), overlapping the next step",
                     "offload_ms_per_step_no_recall": ms0,
                     "offload_ms_per_step_with_recall": ms1,
                     "mean_offload_ms_no_recall": round(sum(ms0) / len(ms0), 3),
