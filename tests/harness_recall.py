@@ -307,16 +307,19 @@ def run_overlap_vs_join(wl, beta, steps=3):
             sa, sb = state(A), state(Bv)
             assert all(torch.equal(x, y) for x, y in zip(sa, sb)), f"step {t}"
             moved += sum(int(r["n_recalled"].sum()) for r in A["rec"])
+        import warnings
         g = torch.cuda.CUDAGraph()
         refused = False
-        try:
-            with torch.cuda.graph(g):
-                try:
-                    Bv["step"]()
-                except B.SaError:
-                    refused = True
-        except Exception:  # noqa: BLE001 -- an empty capture may itself complain
-            pass
+        with warnings.catch_warnings():
+            warnings.simplefilter("ignore")  # the refused capture leaves the graph empty
+            try:
+                with torch.cuda.graph(g):
+                    try:
+                        Bv["step"]()
+                    except B.SaError:
+                        refused = True
+            except Exception:  # noqa: BLE001 -- an empty capture may itself complain
+                pass
         assert refused, "an overlapping step was captured"
         torch.cuda.synchronize()
     finally:
