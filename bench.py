@@ -40,6 +40,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA
 
 
 def log(msg):
@@ -293,6 +294,37 @@ def recall_measure(wl, dims, lens, layers, store, torch, B):
             "ms_per_layer": round(total_ms / len(ms), 4),
             "host_link_gbs": round(nbytes / (total_ms * 1e-3) / 1e9, 2),
             "cpu_share_before": round(share0, 4)}
+
+
+def gemm_measure(wl, layers, torch, B, n=20):
+    """The query GEMM (a1) alone: Q = X W^T for one layer (M = batch rows, N = Hq * d, K =
+    hidden), the stand-alone call with its slice sum, timed with HIP events over n launches.
+    Its flops per byte of W are M, so at the HBM peak it could reach M * 8 TB/s of flops, a
+    small share of the bf16 MFMA peak; both fractions are reported."""
+    M, N, K = wl.batch, wl.num_q_heads * wl.head_dim, wl.hidden
+    x, w = layers[0]["x"], layers[1]["w_q"]
+    q = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    gws = B.workspace(B.sa_predict_query_workspace_bytes(M, N, K))
+    for _ in range(3):
+        B.sa_predict_query(x, w, q, gws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        B.sa_predict_query(x, w, q, gws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    flops = 2.0 * M * N * K
+    tflops = flops / (us * 1e-6) / 1e12
+    ceiling = M * PEAK_HBM_GBS / 1e3  # TFLOP/s at the HBM peak (M flops per W byte)
+    w_gbs = N * K * 2 / (us * 1e-6) / 1e9
+    log(f"query GEMM alone: {us:.1f} us, {tflops:.0f} TFLOP/s, W at {w_gbs:.0f} GB/s")
+    return {"kernel": "gemm_kernel (Q_pred / Q, with its slice sum)", "m": M, "n": N, "k": K,
+            "avg_call_us": round(us, 2), "achieved": round(tflops, 1), "unit": "TFLOP/s",
+            "peak": PEAK_BF16_TFLOPS, "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "hbm_ceiling": round(ceiling, 1), "frac_of_hbm_ceiling": round(tflops / ceiling, 4),
+            "w_stream_gbs": round(w_gbs, 1)}
 
 
 def dense_measure(wl, args, torch, B, wk, sparse_us):
@@ -748,6 +780,7 @@ def main():
                               "avg_launch_us": round(iso_avg_ms * 1e3, 2),
                               "algorithmic_bytes_per_launch": int(iso_bytes_avg)},
     }
+    result["gemm"] = gemm_measure(wl, layers, torch, B)
     if args.dense:
         result["dense"] = dense_measure(wl, args, torch, B, wk, iso_avg_ms * 1e3)
     store = host_store(wl, args, B, wk) if (args.recall or args.drift_steps) else None
