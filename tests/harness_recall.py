@@ -216,7 +216,8 @@ def run_step_with_recall(wl: wk.Workload, beta: float, max_recall: int):
         share0 = sum(int(L["n_cpu"].sum()) for L in layers)
         for i, L in enumerate(layers):
             ncl = L["n_cpu"].cpu()
-            due = so.recall_due(ncl.numpy(), k, beta)
+            # beta crosses the C ABI as a float32: the oracle takes the same value
+            due = so.recall_due(ncl.numpy(), k, float(np.float32(beta)))
             tab = L["block_table"].cpu().view(pairs, -1)
             nrec = rec[i]["n_recalled"].cpu()
             if not due:
