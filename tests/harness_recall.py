@@ -329,3 +329,54 @@ def run_overlap_vs_join(wl, beta, steps=3):
         Bv["plan"].close()
     H.log(f"  overlap vs join: {steps} steps identical, {moved} blocks moved")
     return moved
+
+
+def run_recall_fullsize(wl, pairs_to_check, host_pages=32768, max_recall=64):
+    """The benchmark-sized step, then one recall of every layer from an aliased page-locked
+    host store (as bench.py --recall), checked on sampled pairs against the oracle's
+    recall_pair bit for bit: tables, counts and the moved pages."""
+    dev = "cuda"
+    Hkv, d, bs, k = wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k
+    pairs = wl.batch * Hkv
+    data = HS.prepare_step(wl, dev)
+    lens = wk.seq_lens(wl)
+    lens_d = lens.to(dev)
+    dims = H.dims_for(wl, data[0]["pool"]["K"].shape[0])
+    layers = HS.device_layers(wl, data, dims, lens_d, "mean", handoff=False)
+    del data
+    ws = B.workspace(B.sa_step_workspace_bytes(dims, wl.hidden, k))
+    B.sa_decode_step(dims, "mean", wl.hidden, k, wl.scale, lens_d, layers, ws,
+                     side_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    st = wk.draw_host_store_aliased(wl, host_pages)
+    K = B.pinned_empty(tuple(st["K"].shape), st["K"].dtype)
+    V = B.pinned_empty(tuple(st["V"].shape), st["V"].dtype)
+    K.copy_(st["K"])
+    V.copy_(st["V"])
+    table_d = st["table"].to(dev)
+    rws = B.workspace(B.sa_recall_workspace_bytes(dims, max_recall))
+    moved = 0
+    for i, L in enumerate(layers):
+        t0 = L["block_table"].view(pairs, -1)[pairs_to_check].cpu()
+        lists = {n: L[n].cpu() for n in ("gpu_blocks", "n_gpu", "cpu_blocks", "n_cpu")}
+        n_rec = torch.full((pairs,), -7, dtype=torch.int32, device=dev)
+        B.sa_recall_blocks(dims, k, max_recall, lens_d, L["block_table"], L["gpu_blocks"],
+                           L["n_gpu"], L["cpu_blocks"], L["n_cpu"], K, V, table_d, L["k_pool"],
+                           L["v_pool"], n_rec, rws)
+        torch.cuda.synchronize()
+        tab = L["block_table"].view(pairs, -1)
+        for j, p in enumerate(pairs_to_check):
+            s, h = divmod(p, Hkv)
+            gl = lists["gpu_blocks"][p, :int(lists["n_gpu"][p])].numpy()
+            cl = lists["cpu_blocks"][p, :int(lists["n_cpu"][p])].numpy()
+            want, moves = so.recall_pair(t0[j].numpy(), int(lens[s]), bs, gl, cl,
+                                         st["table"][s, h].numpy(), max_recall)
+            assert np.array_equal(tab[p].cpu().numpy(), want), f"layer {i} pair {p}: table"
+            assert int(n_rec[p]) == len(moves), f"layer {i} pair {p}: n_recalled"
+            for b, page, hp in moves:
+                assert torch.equal(unpack_k(L["k_pool"][page].cpu(), bs, d), st["K"][hp])
+                assert torch.equal(unpack_v(L["v_pool"][page].cpu(), bs, d), st["V"][hp])
+            moved += len(moves)
+    H.log(f"  full-size recall: {moved} blocks moved on {len(pairs_to_check)} sampled pairs x "
+          f"{len(layers)} layers, all matching the oracle")
+    return moved

@@ -105,3 +105,13 @@ def test_dense_fullsize():
                 o[s, qh].double().cpu().numpy(), float(m[s, qh]), float(l[s, qh]), want,
                 H.attn_tol(wl), f"seq {s} head {qh}"))
     H.log(f"  dense full size: max_err={max_err:.2e}")
+
+
+def test_recall_fullsize():
+    """One periodic recall of every layer after the benchmark's step (as bench.py --recall),
+    sampled pairs bit for bit against the oracle's recall."""
+    wl = wk.QWEN3_14B_STEP
+    H.log(f"[case] full size recall {wl.name}")
+    import harness_recall as HR
+    moved = HR.run_recall_fullsize(wl, sample_pairs(wl, 6, 17))
+    assert moved > 0
