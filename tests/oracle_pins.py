@@ -55,6 +55,31 @@ def pin_bf16_hand_cases():
     assert np.array_equal(got, want), f"bf16 RNE: got {got}, want {want}"
 
 
+def pin_f32_hand_cases():
+    """Round-to-nearest-even onto the float32 grid, worked by hand (spacing 2^-23 on [1, 2),
+    so the ties sit at odd multiples of 2^-24)."""
+    cases = [
+        (1.0 + 2.0 ** -24, 1.0),                              # tie -> even significand
+        (1.0 + 3 * 2.0 ** -24, 1.0 + 2.0 ** -22),             # tie -> even (up)
+        (1.0 + 2.0 ** -24 + 2.0 ** -50, 1.0 + 2.0 ** -23),    # just above the tie: up
+        (1.0 + 2.0 ** -24 - 2.0 ** -50, 1.0),                 # just below the tie: down
+        (1.0 + 2.0 ** -22, 1.0 + 2.0 ** -22),                 # on the grid, not on bf16's
+        (-3.0, -3.0),
+        ((2 - 2.0 ** -23) * 2.0 ** 127, (2 - 2.0 ** -23) * 2.0 ** 127),  # largest finite
+        ((2 - 2.0 ** -24) * 2.0 ** 127, math.inf),            # tie above the largest -> inf
+        (2.0 ** -149, 2.0 ** -149),                           # smallest subnormal
+        (2.0 ** -150, 0.0),                                   # tie to even (zero)
+        (3 * 2.0 ** -150, 2.0 ** -148),                       # tie to even (up)
+        # 0.1 = 1.6 * 2^-4: 1.6 * 2^23 = 13421772.8 rounds to 13421773
+        (0.1, 13421773 * 2.0 ** -27),
+    ]
+    x = np.array([c[0] for c in cases])
+    want = np.array([c[1] for c in cases])
+    with np.errstate(over="ignore"):        # the overflow case is meant to overflow
+        got = so.round_to_f32(x)
+    assert np.array_equal(got, want), f"f32 RNE: got {got.tolist()}, want {want.tolist()}"
+
+
 def pin_bf16_matches_library_on_float32():
     """On float32 inputs a single RNE to bf16 is what torch's float32->bfloat16 cast does."""
     rng = np.random.default_rng(11)
@@ -79,6 +104,27 @@ def pin_predict_query_hand():
     W2 = np.array([[1.0, 2.0], [3.0, 4.0]])       # feature 0 = x0 + 2 x1; feature 1 = 3x0 + 4x1
     want2 = np.array([[1.0, 3.0], [2.0, 4.0], [8.0, 18.0]])
     assert np.array_equal(so.predict_query(X2, W2), want2)
+
+
+def pin_query_heads_layout():
+    """The projection output [M][Hq*d] viewed per head: element n of a row belongs to head
+    n div d, channel n mod d.  A non-square case (Hq = 3, d = 4) worked by hand, so that a
+    channel-major reading (head n mod Hq) cannot pass."""
+    M, Hq, d = 2, 3, 4
+    rows = np.arange(M * Hq * d, dtype=np.float64).reshape(M, Hq * d)
+    heads = so.query_heads(rows, Hq, d)
+    assert heads.shape == (M, Hq, d)
+    assert heads[1].tolist() == [[12.0, 13.0, 14.0, 15.0], [16.0, 17.0, 18.0, 19.0],
+                                 [20.0, 21.0, 22.0, 23.0]], heads[1]
+    for m in range(M):
+        for n in range(Hq * d):
+            assert heads[m, n // d, n % d] == rows[m, n]
+    try:
+        so.query_heads(rows, Hq + 1, d)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("query_heads accepted a width that is not Hq*d")
 
 
 def pin_predict_query_one_hot():
@@ -138,6 +184,25 @@ def pin_digest_mean_single_rounding():
     K[:, 1] = [1.0, 1.0, 1.0 + 2.0 ** -38, 1.0 + 4 * 2.0 ** -8]  # mean just above the tie
     dig = so.digest_mean(K, 4, 4, "bf16")
     assert dig[0, 0] == 1.0 and dig[0, 1] == 1.0 + 2.0 ** -7, dig
+
+
+def pin_digest_mean_f32_single_rounding():
+    """Float32 KV: the float64 mean of a block is rounded once to float32 -- not left
+    unrounded, and not rounded onto a coarser grid (bf16, fp16).  One block of four tokens,
+    one channel per case (float32 spacing 2^-23 on [1, 2)):
+      mean 1 + 2^-22            on the float32 grid, not on bf16's or fp16's: kept;
+      mean 1 + 2^-24 + 2^-30    just above a float32 tie: rounds up to 1 + 2^-23;
+      mean 1 + 2^-24            a float32 tie: rounds to the even value 1;
+    and a partial last block of two tokens whose mean 1 + 3 * 2^-24 is a tie rounding up to
+    1 + 2^-22 (it divides by its own count, reading R9)."""
+    K = np.ones((6, 3))
+    K[3, 0] = 1.0 + 2.0 ** -20
+    K[3, 1] = 1.0 + 2.0 ** -22 + 2.0 ** -28
+    K[3, 2] = 1.0 + 2.0 ** -22
+    K[5, :] = 1.0 + 3 * 2.0 ** -23
+    dig = so.digest_mean(K, 6, 4, "f32")
+    assert dig[0].tolist() == [1.0 + 2.0 ** -22, 1.0 + 2.0 ** -23, 1.0], dig[0]
+    assert dig[1].tolist() == [1.0 + 2.0 ** -22] * 3, dig[1]
 
 
 def pin_digest_minmax_closed_form():
@@ -230,6 +295,92 @@ def pin_topk_special_cases():
     assert so.select_topk(s, 10).tolist() == [0, 1, 2, 3, 4]  # k >= nb: all blocks
     assert so.select_topk(np.zeros(6), 3).tolist() == [0, 1, 2]
     assert so.select_topk(np.array([-0.0, 0.0, -0.0]), 1).tolist() == [0]
+
+
+def _box_corner_score(q, K_block):
+    """Largest q . c over the corners c of the channel-wise bounding box of a block's keys,
+    by enumeration.  A linear function is largest over a box at one of its corners, so this
+    is the smallest upper bound of q . K_t that sees only the box [HTML Sec. 2.2, Quest]."""
+    d = K_block.shape[1]
+    lo = [min(float(K_block[t, c]) for t in range(K_block.shape[0])) for c in range(d)]
+    hi = [max(float(K_block[t, c]) for t in range(K_block.shape[0])) for c in range(d)]
+    best = -math.inf
+    for corner in itertools.product(*zip(lo, hi)):
+        best = max(best, sum(float(q[c]) * corner[c] for c in range(d)))
+    return best
+
+
+def pin_minmax_selection_below_budget_brute_force():
+    """Min/max digests with k below the block count: the selection of select_pair (and of
+    forward_pair, with its split and attention) equals brute force -- each block scored as
+    the sum over the group's heads of the largest q_g . c over its box corners, then the
+    best k-subset by enumeration (lower index first on ties).  Dyadic keys and queries keep
+    every score exact.  The cases are drawn so that mean digests select differently in
+    some of them, which a pin that only sees k >= nb cannot tell apart."""
+    rng = np.random.default_rng(47)
+    differs = 0
+    for trial in range(40):
+        d, bs, G = int(rng.integers(2, 5)), int(rng.integers(1, 5)), int(rng.integers(1, 4))
+        nb = int(rng.integers(3, 9))
+        T = nb * bs - int(rng.integers(0, bs))          # a ragged last block
+        k = int(rng.integers(1, nb))
+        K = rng.integers(-12, 13, size=(T, d)).astype(np.float64) / 4.0
+        V = rng.standard_normal((T, d))
+        qs = rng.integers(-6, 7, size=(G, d)).astype(np.float64) / 2.0
+        want_sig = []
+        for b in range(nb):
+            rows = K[b * bs:min((b + 1) * bs, T)]
+            want_sig.append(sum(_box_corner_score(qs[g], rows) for g in range(G)))
+        want = _brute_topk(want_sig, k)
+        resident = rng.random(nb) < 0.5
+        dig = so.digest_minmax(K, T, bs)
+        sig, sel, g_blocks, c_blocks = so.select_pair(qs, dig, "minmax", k, resident)
+        assert np.array_equal(sig, want_sig), (trial, sig, want_sig)
+        assert sel.tolist() == want.tolist(), (trial, sel, want)
+        assert g_blocks.tolist() == [b for b in want if resident[b]]
+        assert c_blocks.tolist() == [b for b in want if not resident[b]]
+        r = so.forward_pair(qs, qs, K, V, T, bs, dig, "minmax", k, resident, 0.5)
+        assert r.selected.tolist() == want.tolist()
+        rows = np.concatenate([np.arange(b * bs, min((b + 1) * bs, T)) for b in want])
+        ref = _dense_ref_heads(qs, K[rows], V[rows], len(rows), 0.5)
+        for g in range(G):
+            _close(r.out[g].o, ref[g], 1e-12, f"min/max forward trial {trial}")
+        mean_sel = _brute_topk([float(sum(qs[g] @ K[b * bs:min((b + 1) * bs, T)].mean(0)
+                                          for g in range(G))) for b in range(nb)], k)
+        differs += mean_sel.tolist() != want.tolist()
+    assert differs >= 5, f"only {differs} cases tell min/max from mean selection"
+
+
+def pin_step_minmax_hand():
+    """Algorithm 1 with min/max digests, worked by hand: d = 2, blocks of 2 tokens, one
+    head, W_Q^0 = I, W_Q^1 = the swap [[0, 1], [1, 0]], X^0 = (1, 0), X^1 = (0, 2), k = 1.
+    Layer 0 selects with Q^0 = (1, 0): block 0 = {(1, 0), (-1, 0)} has box corners up to
+    q.c = 1, block 1 = {(0.5, 0), (0.5, 0)} scores 0.5, so block 0 wins (its mean (0, 0)
+    would lose to 0.5).  Its attention with Q^0 over block 0: logits (1, -1), so with
+    V = e_0, e_1 the output is (1, e^-2) / (1 + e^-2), m = 1, l = 1 + e^-2.  Layer 1 selects
+    with Q_pred^1 = W_Q^1 X^0 = (0, 1): block 0 = {(0, -2), (0, 1)} scores max(-2, 1) = 1,
+    block 1 = {(0, 0.8), (0, 0.8)} scores 0.8 (block 0's mean (0, -0.5) would lose).  It
+    attends with Q^1 = W_Q^1 X^1 = (2, 0): logits (0, 0), o = (V_0 + V_1) / 2, m = 0, l = 2."""
+    I = np.eye(2)
+    S = np.array([[0.0, 1.0], [1.0, 0.0]])
+    V = np.array([[1.0, 0.0], [0.0, 1.0], [3.0, 3.0], [3.0, 3.0]])
+    K0 = np.array([[1.0, 0.0], [-1.0, 0.0], [0.5, 0.0], [0.5, 0.0]])
+    K1 = np.array([[0.0, -2.0], [0.0, 1.0], [0.0, 0.8], [0.0, 0.8]])
+    dig0 = np.array([[[-1.0, 0.0], [1.0, 0.0]], [[0.5, 0.0], [0.5, 0.0]]])
+    dig1 = np.array([[[0.0, -2.0], [0.0, 1.0]], [[0.0, 0.8], [0.0, 0.8]]])
+    res = np.array([True, True])
+    layers = [dict(X=np.array([[1.0, 0.0]]), W=I, digest=dig0, resident=res, K=K0, V=V,
+                   seq_len=4, host=[so.empty_partial(2)]),
+              dict(X=np.array([[0.0, 2.0]]), W=S, digest=dig1, resident=res, K=K1, V=V,
+                   seq_len=4, host=[so.empty_partial(2)])]
+    out = so.decode_step_pair(layers, 0, 0, 1, 2, 2, 1, 1.0, kind="minmax")
+    assert out[0].scores.tolist() == [1.0, 0.5] and out[0].selected.tolist() == [0]
+    e2 = math.exp(-2.0)
+    _close(out[0].out[0].o, [1 / (1 + e2), e2 / (1 + e2)], 1e-15, "layer 0 output")
+    assert out[0].out[0].m == 1.0 and abs(out[0].out[0].l - (1 + e2)) < 1e-15
+    assert out[1].scores.tolist() == [1.0, 0.8] and out[1].selected.tolist() == [0]
+    _close(out[1].out[0].o, [0.5, 0.5], 1e-15, "layer 1 output")
+    assert out[1].out[0].m == 0.0 and out[1].out[0].l == 2.0
 
 
 def pin_split_hand():

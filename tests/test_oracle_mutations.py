@@ -188,6 +188,36 @@ def _gqa_shifted(h, group):
     return range(h * group + 1, (h + 1) * group + 1)
 
 
+def _f32_noop(x):
+    return np.asarray(x, dtype=np.float64).copy()
+
+
+def _f32_via_fp16(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def _store_rounding_bf16_for_f32(kv_dtype):
+    return _orig["round_to_bf16"] if kv_dtype in ("bf16", "f32") else _orig["store_rounding"](kv_dtype)
+
+
+def _query_heads_channel_major(Q_rows, num_q_heads, head_dim):
+    M, N = Q_rows.shape
+    if N != num_q_heads * head_dim:
+        raise ValueError("query_heads: width is not Hq*d")
+    return np.ascontiguousarray(Q_rows.reshape(M, head_dim, num_q_heads).transpose(0, 2, 1))
+
+
+def _score_blocks_minmax_as_mean_of_max(q_group, digest, kind):
+    if kind == "minmax":
+        return _orig["score_mean"](q_group, np.asarray(digest)[:, 1, :])
+    return _orig["score_blocks"](q_group, digest, kind)
+
+
+def _step_always_mean(layers, s, h, group, head_dim, block_size, top_k, scale, kind="mean"):
+    return _orig["decode_step_pair"](layers, s, h, group, head_dim, block_size, top_k, scale,
+                                     "mean")
+
+
 MUTATIONS = {
     "bf16 double rounding via f32": ("round_to_bf16", _bf16_via_f32),
     "bf16 ties away from zero": ("round_to_bf16", _bf16_ties_away),
@@ -214,6 +244,13 @@ MUTATIONS = {
     "host side attends with the true query": ("decode_step_pair", _step_host_with_true_query),
     "recall evicts the highest blocks first": ("recall_pair", _recall_evicts_descending),
     "recall may evict selected resident blocks": ("recall_pair", _recall_evicts_selected),
+    "f32 rounding is a no-op": ("round_to_f32", _f32_noop),
+    "f32 rounding onto the fp16 grid": ("round_to_f32", _f32_via_fp16),
+    "f32 digests stored with the bf16 rounding": ("store_rounding", _store_rounding_bf16_for_f32),
+    "query heads read channel-major": ("query_heads", _query_heads_channel_major),
+    "min/max dispatch scores the max row as a mean digest":
+        ("score_blocks", _score_blocks_minmax_as_mean_of_max),
+    "step ignores the digest kind": ("decode_step_pair", _step_always_mean),
 }
 
 
