@@ -664,7 +664,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
       float ps = 0.f;
       float acc[CPL];
       for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
-      for (int t = 0; t < BS; ++t) {
+      // only the valid tokens: the rest of a partly filled page may hold anything, and a
+      // zero weight times a stale NaN or infinity would still poison the sum
+      for (int t = 0; t < nval; ++t) {
         const float pr = fast_exp2(sc[g][t] - m_new);
         ps += pr;
         for (int c = 0; c < CPL; ++c) acc[c] = fmaf(pr, vs[t][lane + kWave * c], acc[c]);
