@@ -64,6 +64,19 @@ LAYER_CASES = [
     ("cfg1-host-worker", TINY, "mean", dict(host_worker=True)),
     ("cfg3-scaled-minmax-host-worker", CFG3_S, "minmax", dict(host_worker=True)),
     ("cfg5-scaled-mean-host-worker", CFG5_S, "mean", dict(host_worker=True)),
+    # the unused rows of partly filled last pages hold NaN and infinities: no kernel (fp32 or
+    # bf16 attention, digests, the host worker) may let them into a result.  Full budgets so
+    # that every partly filled block is attended.
+    ("f32-poisoned-tails", TINY.scaled(context=1000), "mean",
+     dict(poison_tails=True, resident_override="all", top_k=63)),
+    ("f32-poisoned-tails-sparse", TINY.scaled(context=1000), "minmax", dict(poison_tails=True)),
+    ("f32-poisoned-tails-host-worker", TINY.scaled(context=1000), "mean",
+     dict(poison_tails=True, resident_override="none", top_k=63, host_worker=True)),
+    ("bf16-poisoned-tails", wk.RAGGED.scaled(batch=3, ctx_min=100, ctx_max=700, top_k=44),
+     "minmax", dict(poison_tails=True, resident_override="all")),
+    ("bf16-poisoned-tails-host-worker",
+     wk.RAGGED.scaled(batch=3, ctx_min=100, ctx_max=700, top_k=44), "mean",
+     dict(poison_tails=True, resident_override="none", host_worker=True)),
 ]
 
 
