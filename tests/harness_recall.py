@@ -1,7 +1,8 @@
 """Parity harness for periodic recall (sa_recall_blocks) inside a multi-layer step.
 
-A step runs once (sa_decode_step, host partials given); its selection lists drive the
-recall of every layer.  The recall is checked against the oracle's recall_pair, bit for
+A step runs once (sa_decode_step, host partials given); its selection lists and outputs are
+first checked against the oracle's Algorithm 1, and only then drive the recall of every
+layer.  The recall is checked against the oracle's recall_pair, bit for
 bit: the new block tables, the number of blocks moved, the recalled pages' keys and values
 (unpacked from the pool layouts in numpy and compared with the host store they were drawn
 into), and every page that did not move.  The step then runs again: its CPU share must
@@ -72,7 +73,8 @@ def run_recall(wl: wk.Workload, max_recall: int):
     side = torch.cuda.Stream()
     B.sa_decode_step(dims, "mean", wl.hidden, k, wl.scale, lens_d, dev_layers, ws, side_stream=side)
     torch.cuda.synchronize()
-    H.log("  first step done")
+    first = HS.check_step(wl, data, dev_layers, lens)
+    H.log(f"  first step done, lists and outputs match the oracle (ties {first['ties']})")
     n_cpu_before = sum(int(e["n_cpu"].sum()) for e in dev_layers)
 
     # ---------------- recall every layer, then check it against the oracle
@@ -212,6 +214,9 @@ def run_step_with_recall(wl: wk.Workload, beta: float, max_recall: int):
         B.sa_decode_step_offload(dims, "mean", wl.hidden, k, wl.scale, lens_d, layers, ws, plan,
                                  host, side_stream=side, recall_stream=recall)
         torch.cuda.synchronize()
+        # the lists the recall reads are the step's: checked against the oracle first
+        HS.check_step(wl, data, layers, lens, None, "mean", offload=True, stores=stores,
+                      host_layers=host_layers)
         due_layers, moved = 0, 0
         share0 = sum(int(L["n_cpu"].sum()) for L in layers)
         for i, L in enumerate(layers):
@@ -343,11 +348,13 @@ def run_recall_fullsize(wl, pairs_to_check, host_pages=32768, max_recall=64):
     lens_d = lens.to(dev)
     dims = H.dims_for(wl, data[0]["pool"]["K"].shape[0])
     layers = HS.device_layers(wl, data, dims, lens_d, "mean", handoff=False)
-    del data
     ws = B.workspace(B.sa_step_workspace_bytes(dims, wl.hidden, k))
     B.sa_decode_step(dims, "mean", wl.hidden, k, wl.scale, lens_d, layers, ws,
                      side_stream=torch.cuda.Stream())
     torch.cuda.synchronize()
+    # the sampled pairs' lists (which the recall reads) against the oracle first
+    HS.check_step(wl, data, layers, lens, pairs_to_check)
+    del data
     st = wk.draw_host_store_aliased(wl, host_pages)
     K = B.pinned_empty(tuple(st["K"].shape), st["K"].dtype)
     V = B.pinned_empty(tuple(st["V"].shape), st["V"].dtype)

@@ -153,7 +153,48 @@ def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs
         torch.cuda.synchronize()
         H.log("  HIP step done")
 
-    # ---------------- oracle
+    r = check_step(wl, data, dev_layers, lens, pairs_to_check, kind, offload, stores,
+                   host_layers, handoff)
+    cpu_ratio = np.mean([float(e["n_cpu"].sum()) * bs / (pairs * k * bs) for e in dev_layers])
+    H.log(f"  step {wl.name}: checked={r['checked']} ties={r['ties']} max_err={r['max_err']:.2e} "
+          f"cpu_ratio={cpu_ratio:.3f}")
+    return dict(max_err=r["max_err"], ties=r["ties"], cpu_ratio=cpu_ratio)
+
+
+def _oracle_layer(wl, data, i, s, h, OL, offload, sel=None):
+    """The oracle's layer i for pair (s, h) over a given selection (a valid tie-alternative
+    the GPU made): GPU part with Q^i over the resident selected blocks, host part over the
+    offloaded ones (with Q_pred^i, Q^0 at layer 0, from the host's copy when computed; as
+    given otherwise; empty when nothing is offloaded), merged."""
+    G, d, bs = wl.group, wl.head_dim, wl.block_size
+    n = OL["seq_len"]
+    rows = slice(h * G * d, (h + 1) * G * d)
+    x = wk.f64(data[i]["X"])[s:s + 1]
+    q_true = so.predict_query(x, wk.f64(data[i]["W"])[rows]).reshape(G, d)
+    _, c_blocks = so.split_resident(sel, OL["resident"])
+    if len(c_blocks) == 0:
+        host = [so.empty_partial(d)] * G
+    elif offload:
+        xs = wk.f64(data[i - 1]["X"] if i > 0 else data[0]["X"])[s:s + 1]
+        q_sel = so.predict_query(xs, wk.f64(data[i]["W"])[rows]).reshape(G, d)
+        host = [so.attend_blocks(q_sel[j], OL["K_host"], OL["V_host"], c_blocks, n, bs, wl.scale)
+                for j in range(G)]
+    else:
+        host = OL["host"]
+    return so.attend_selection(q_true, OL["K"], OL["V"], n, bs, None, sel, OL["resident"],
+                               wl.scale, host)
+
+
+def check_step(wl, data, dev_layers, lens, pairs_to_check=None, kind="mean", offload=False,
+               stores=None, host_layers=None, handoff=False):
+    """The step's lists and outputs (dev_layers, after the step ran) against the oracle's
+    Algorithm 1 for the checked pairs: selections identical up to ties; outputs (and, with
+    offload, the handed-over query and the host partials) within the attention tolerance of
+    the oracle over the GPU's selection.  Returns {max_err, ties, checked}."""
+    B_, Hkv, G, d, bs, k = (wl.batch, wl.num_kv_heads, wl.group, wl.head_dim, wl.block_size,
+                            wl.top_k)
+    L = len(data)
+    pairs = B_ * Hkv
     check = range(pairs) if pairs_to_check is None else pairs_to_check
     ties = 0
     max_err = 0.0
@@ -184,8 +225,8 @@ def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs
                 st = stores[i]
                 Kh = np.zeros((nb * bs, d))
                 Vh = np.zeros((nb * bs, d))
-                # rows of the blocks the step handed to the CPU (a selection the oracle makes
-                # differently is a tie and skipped below); the rest are never read
+                # rows of the blocks the step handed to the CPU (the oracle's own offloaded
+                # blocks differ from these only on a tie, and then the GPU's are attended)
                 e = dev_layers[i]
                 nc_ = int(e["n_cpu"][p])
                 for b in e["cpu_blocks"][p, :nc_].cpu().tolist():
@@ -216,10 +257,14 @@ def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs
                 assert np.array_equal(e["cpu_blocks_host"][p].numpy(), cbl)
             sel = np.sort(np.concatenate([gbl[:ng], cbl[:nc]]))
             same = H.selection_matches(sel, want[i].selected, want[i].scores, min(k, nb))
-            if not same:
+            r = want[i]
+            if same:
+                assert np.array_equal(gbl[:ng], r.gpu_blocks)
+            else:
                 ties += 1
-                continue
-            assert np.array_equal(gbl[:ng], want[i].gpu_blocks)
+                resident = olayers[i]["resident"]
+                assert np.all(resident[gbl[:ng]]) and not np.any(resident[cbl[:nc]])
+                r = _oracle_layer(wl, data, i, s, h, olayers[i], offload, sel)
             if offload:
                 # the query handed to the CPU (Q_pred^i; Q^0 at layer 0) and the CPU's partial
                 X64 = wk.f64(data[i - 1]["X"] if i > 0 else data[0]["X"])[s:s + 1]
@@ -232,16 +277,13 @@ def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs
                     max_err = max(max_err, H.compare_partial(
                         hl_["o_host"][s, h * G + j].double().numpy(),
                         float(hl_["m_host"][s, h * G + j]), float(hl_["l_host"][s, h * G + j]),
-                        want[i].host[j], H.attn_tol(wl), f"host partial layer {i} pair {p}"))
+                        r.host[j], H.attn_tol(wl), f"host partial layer {i} pair {p}"))
             o = e["out_o"][s, h * G:(h + 1) * G].cpu().double().numpy()
             m = e["out_m"][s, h * G:(h + 1) * G].cpu().double().numpy()
             l = e["out_l"][s, h * G:(h + 1) * G].cpu().double().numpy()
             for j in range(G):
-                max_err = max(max_err, H.compare_partial(o[j], m[j], l[j], want[i].out[j],
+                max_err = max(max_err, H.compare_partial(o[j], m[j], l[j], r.out[j],
                                                          H.attn_tol(wl), f"layer {i} pair {p}"))
     n_checked = len(list(check)) * L
     assert ties <= max(1, n_checked // 100), f"too many tie-differing selections: {ties}"
-    cpu_ratio = np.mean([float(e["n_cpu"].sum()) * bs / (pairs * k * bs) for e in dev_layers])
-    H.log(f"  step {wl.name}: checked={n_checked} ties={ties} max_err={max_err:.2e} "
-          f"cpu_ratio={cpu_ratio:.3f}")
-    return dict(max_err=max_err, ties=ties, cpu_ratio=cpu_ratio)
+    return dict(max_err=max_err, ties=ties, checked=n_checked)
