@@ -10,6 +10,7 @@ use; if it has not been built, that is an error (there is no fallback).
 from __future__ import annotations
 
 import ctypes
+import weakref
 import os
 from dataclasses import dataclass
 
@@ -178,7 +179,10 @@ class Dims:
 
 
 _hip = None
-_HOST_BUFFERS = []  # page-locked host buffers, kept until the process ends
+# Page-locked buffers whose tensors have died.  They are released (hipHostFree, which waits
+# for the device) at the next pinned_empty call or by release_pinned(), never from inside a
+# garbage-collection pass, which could land in the middle of a stream capture.
+_PENDING_FREE = []
 
 
 HIP_HOST_MALLOC_COHERENT = 0x40000000
@@ -194,6 +198,8 @@ def pinned_empty(shape, dtype=torch.int32) -> torch.Tensor:
         _hip = ctypes.CDLL("libamdhip64.so")
         _hip.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t,
                                        ctypes.c_uint]
+        _hip.hipHostFree.argtypes = [ctypes.c_void_p]
+    release_pinned()
     n = 1
     for v in (shape if isinstance(shape, (tuple, list)) else (shape,)):
         n *= int(v)
@@ -202,8 +208,23 @@ def pinned_empty(shape, dtype=torch.int32) -> torch.Tensor:
     if _hip.hipHostMalloc(ctypes.byref(ptr), nbytes, HIP_HOST_MALLOC_COHERENT) != 0 or not ptr.value:
         raise RuntimeError(f"hipHostMalloc of {nbytes} bytes failed")
     buf = (ctypes.c_char * nbytes).from_address(ptr.value)
-    _HOST_BUFFERS.append(buf)
+    # the tensor (and every view of it) holds buf; once the last one dies, the memory is
+    # queued for release
+    weakref.finalize(buf, _PENDING_FREE.append, ptr.value)
     return torch.frombuffer(buf, dtype=dtype, count=n).view(shape)
+
+
+def release_pinned() -> int:
+    """Free the page-locked buffers whose tensors have died; returns how many.  Not to be
+    called while a stream is being captured (hipHostFree waits for the device)."""
+    freed = 0
+    if _PENDING_FREE and torch.cuda.is_initialized():
+        torch.cuda.synchronize()  # no queued work may still read or write them
+    while _PENDING_FREE:
+        if _hip.hipHostFree(ctypes.c_void_p(_PENDING_FREE.pop())) != 0:
+            raise RuntimeError("hipHostFree failed")
+        freed += 1
+    return freed
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
