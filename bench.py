@@ -171,6 +171,34 @@ def attention_bytes(wl, n_gpu_sum):
     return kv + q + out
 
 
+def select_bytes(wl, kind="mean", lens=None):
+    """Scoring + top-k + split of one layer: every valid digest row, the query, the block
+    table entries of the valid blocks, and the two lists with their counts."""
+    import math as _m
+    Bsz, Hkv, Hq, d, k, bs = (wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim,
+                              wl.top_k, wl.block_size)
+    el = 2 if wl.kv_dtype == "bf16" else 4
+    per = 2 if kind == "minmax" else 1
+    nbs = ([_m.ceil(int(n) / bs) for n in lens] if lens is not None
+           else [wl.max_blocks] * Bsz)
+    rows = Hkv * sum(nbs)
+    return rows * (per * d * el + 4) + Bsz * Hq * d * 4 + Bsz * Hkv * 2 * (k + 1) * 4
+
+
+def gemm_bytes(m, n, k):
+    """Q = X W^T: W and X read once, Q written once (float32)."""
+    return n * k * 2 + m * k * 2 + m * n * 4
+
+
+def spread(ms):
+    """Median, p10, p90 and mean of a list of kernel times (ms), in microseconds."""
+    v = sorted(ms)
+    q = lambda f: v[min(len(v) - 1, max(0, int(round(f * (len(v) - 1)))))]
+    return {"median_us": round(q(0.5) * 1e3, 2), "p10_us": round(q(0.1) * 1e3, 2),
+            "p90_us": round(q(0.9) * 1e3, 2), "mean_us": round(sum(v) / len(v) * 1e3, 2),
+            "launches": len(v)}
+
+
 def step_bytes(wl, n_gpu_sums):
     """Algorithmic bytes of one whole step (every stage of every layer)."""
     Bsz, Hkv, Hq, d, k, L = (wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim,
@@ -296,35 +324,41 @@ def recall_measure(wl, dims, lens, layers, store, torch, B):
             "cpu_share_before": round(share0, 4)}
 
 
-def gemm_measure(wl, layers, torch, B, n=20):
+def gemm_measure(wl, layers, torch, B, n=40):
     """The query GEMM (a1) alone: Q = X W^T for one layer (M = batch rows, N = Hq * d, K =
     hidden), the stand-alone call with its slice sum, timed with HIP events over n launches.
     Its flops per byte of W are M, so at the HBM peak it could reach M * 8 TB/s of flops, a
     small share of the bf16 MFMA peak; both fractions are reported."""
     M, N, K = wl.batch, wl.num_q_heads * wl.head_dim, wl.hidden
-    x, w = layers[0]["x"], layers[1]["w_q"]
     q = torch.empty((M, N), dtype=torch.float32, device="cuda")
     gws = B.workspace(B.sa_predict_query_workspace_bytes(M, N, K))
-    for _ in range(3):
-        B.sa_predict_query(x, w, q, gws)
+    L = len(layers)
+
+    def calls():  # each layer's own W once per pass (no W stays cached)
+        for i in range(n):
+            B.sa_predict_query(layers[i % L]["x"], layers[i % L]["w_q"], q, gws)
+    calls()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(n):
-        B.sa_predict_query(x, w, q, gws)
+    calls()
     e1.record()
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / n * 1e3
+    call_us = e0.elapsed_time(e1) / n * 1e3
+    kern = spread(timed_multi(torch, B, {"gemm": n}, calls)["gemm"])
+    us = kern["median_us"]
     flops = 2.0 * M * N * K
     tflops = flops / (us * 1e-6) / 1e12
     ceiling = M * PEAK_HBM_GBS / 1e3  # TFLOP/s at the HBM peak (M flops per W byte)
-    w_gbs = N * K * 2 / (us * 1e-6) / 1e9
-    log(f"query GEMM alone: {us:.1f} us, {tflops:.0f} TFLOP/s, W at {w_gbs:.0f} GB/s")
-    return {"kernel": "gemm_kernel (Q_pred / Q, with its slice sum)", "m": M, "n": N, "k": K,
-            "avg_call_us": round(us, 2), "achieved": round(tflops, 1), "unit": "TFLOP/s",
+    gbs = gemm_bytes(M, N, K) / (us * 1e-6) / 1e9
+    log(f"query GEMM alone: kernel {us:.1f} us median ({tflops:.0f} TFLOP/s, {gbs:.0f} GB/s); "
+        f"call with its slice sum {call_us:.1f} us")
+    return {"kernel": "gemm_kernel (Q_pred / Q)", "m": M, "n": N, "k": K,
+            "kernel_time": kern, "achieved": round(tflops, 1), "unit": "TFLOP/s",
             "peak": PEAK_BF16_TFLOPS, "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "hbm_ceiling": round(ceiling, 1), "frac_of_hbm_ceiling": round(tflops / ceiling, 4),
-            "w_stream_gbs": round(w_gbs, 1)}
+            "hbm_gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "avg_call_us_with_slice_sum": round(call_us, 2)}
 
 
 def dense_measure(wl, args, torch, B, wk, sparse_us):
@@ -604,6 +638,60 @@ def offload_measure(wl, dims, lens, layers, ws, side_stream, ms_gpu, args, torch
     return out
 
 
+def timed_multi(torch, B, counts, fn):
+    """Run fn() with the next counts[stage] launches of each stage's kernel timed from the
+    kernel's own start to its end (sa_profile_kernels); returns {stage: [ms, ...]}."""
+    ev = {}
+    for stage, n in counts.items():
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        stops = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in starts + stops:
+            e.record()
+        ev[stage] = (starts, stops)
+    torch.cuda.synchronize()
+    for stage, (starts, stops) in ev.items():
+        B.sa_profile_kernels(stage, starts, stops)
+    fn()
+    torch.cuda.synchronize()
+    for stage in ev:
+        B.sa_profile_kernels(stage, [], [])
+    return {stage: [a.elapsed_time(b) for a, b in zip(*ev[stage])] for stage in ev}
+
+
+def select_alone(wl, dims, lens, layers, kind, torch, B, passes=2):
+    """The selection kernel (scoring + top-k + split) launched by itself for every layer,
+    each with the query the step selects it with (Q_pred^i = W_Q^i X^{i-1}; Q^0 for layer
+    0), so each launch reads that layer's own digests (about 168 MB, and 40 layers' worth
+    between two reads of the same ones: nothing stays in the 256 MB last-level cache)."""
+    Bsz, Hq, Hkv, d, k = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.top_k
+    n, pairs = Hq * d, Bsz * Hkv
+    gws = B.workspace(B.sa_predict_query_workspace_bytes(Bsz, n, wl.hidden))
+    qs = []
+    for i, L in enumerate(layers):
+        q = torch.empty((Bsz, n), dtype=torch.float32, device="cuda")
+        B.sa_predict_query(layers[max(i - 1, 0)]["x"], L["w_q"], q, gws)
+        qs.append(q)
+    ws = B.workspace(B.sa_workspace_bytes(dims, k))
+    gb = torch.empty((pairs, k), dtype=torch.int32, device="cuda")
+    cb = torch.empty_like(gb)
+    ng = torch.empty(pairs, dtype=torch.int32, device="cuda")
+    nc = torch.empty_like(ng)
+
+    def run():
+        for i, L in enumerate(layers):
+            B.sa_select_blocks(dims, kind, qs[i], L["digests"], lens, k, L["block_table"], gb,
+                               ng, cb, nc, None, ws)
+    run()
+    ms = timed_multi(torch, B, {"select": passes * len(layers)},
+                     lambda: [run() for _ in range(passes)])["select"]
+    st = spread(ms)
+    nbytes = select_bytes(wl, kind)
+    gbs = nbytes / (st["median_us"] * 1e-6) / 1e9
+    log(f"selection alone: {st['median_us']:.1f} us median (p10 {st['p10_us']:.1f}, p90 "
+        f"{st['p90_us']:.1f}), {gbs:.0f} GB/s")
+    return dict(st, achieved=round(gbs, 1), bytes=nbytes)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -687,30 +775,28 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
     log(f"timed {args.steps} steps ({mode}): {ms_step:.3f} ms/step (wall {wall:.3f} s)")
 
-    # Attention launches timed with HIP events recorded at the kernel's own start and end on
-    # its stream (sa_profile_attention; a graph cannot hold such events, and they slow the
-    # step down by about a tenth, so they are taken outside the timed region):
-    #  (1) inside eager steps, sharing the GPU with the side stream as in the step;
-    #  (2) alone: each layer's attention launched by itself, with the same lists.
-    def timed_launches(n, fn):
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        stops = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        for e in starts + stops:
-            e.record()
-        torch.cuda.synchronize()
-        B.sa_profile_attention(starts, stops)
-        fn()
-        torch.cuda.synchronize()
-        B.sa_profile_attention([], [])
-        return [starts[j].elapsed_time(stops[j]) for j in range(n)]
-
-    nprof = args.profile_steps * wl.layers
-    attn_ms = timed_launches(nprof, lambda: [step() for _ in range(args.profile_steps)])
+    # Kernel launches timed with HIP events recorded at the kernel's own start and end on
+    # its stream (sa_profile_kernels; a graph cannot hold such events, and they slow the step
+    # down by about a tenth, so they are taken outside the timed region):
+    #  (1) inside eager steps, sharing the GPU with the other stream as in the step: every
+    #      attention, selection and query-GEMM launch of those steps;
+    #  (2) alone: each layer's attention and selection launched by themselves.
+    L_ = wl.layers
+    nprof = args.profile_steps * L_
+    n_sel, n_gemm = nprof, args.profile_steps * (2 * L_ - 1)
+    in_step = timed_multi(torch, B, {"attention": nprof, "select": n_sel, "gemm": n_gemm},
+                          lambda: [step() for _ in range(args.profile_steps)])
+    attn_ms = in_step["attention"]
     attn_avg_ms = sum(attn_ms) / len(attn_ms)
     attn_bytes_avg = sum(attention_bytes(wl, n_gpu_sums[j % wl.layers])
                          for j in range(nprof)) / nprof
     achieved = attn_bytes_avg / (attn_avg_ms * 1e-3) / 1e9
     log(f"attention in the step: {attn_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s")
+    sbytes = select_bytes(wl, kind)
+    sel_step = spread(in_step["select"])
+    gemm_step = spread(in_step["gemm"])
+    log(f"selection in the step: {sel_step['median_us']:.1f} us median; query GEMM in the step: "
+        f"{gemm_step['median_us']:.1f} us median")
 
     rows = wl.batch * wl.num_q_heads
     o_iso = torch.empty((rows, wl.head_dim), dtype=torch.float32, device="cuda")
@@ -723,11 +809,13 @@ def main():
             B.sa_sparse_decode(dims, q_iso, L["k_pool"], L["v_pool"], L["block_table"], lens,
                                L["gpu_blocks"], L["n_gpu"], wl.top_k, wl.scale, o_iso, ws=sel_ws)
     alone()
-    iso_ms = timed_launches(wl.layers, alone)
+    iso_ms = timed_multi(torch, B, {"attention": 2 * wl.layers},
+                         lambda: [alone() for _ in range(2)])["attention"]
     iso_avg_ms = sum(iso_ms) / len(iso_ms)
     iso_bytes_avg = sum(attention_bytes(wl, n) for n in n_gpu_sums) / wl.layers
     iso_achieved = iso_bytes_avg / (iso_avg_ms * 1e-3) / 1e9
     log(f"attention alone: {iso_avg_ms * 1e3:.1f} us avg, {iso_achieved:.0f} GB/s")
+    sel_alone = select_alone(wl, dims, lens, layers, kind, torch, B)
     total_bytes = step_bytes(wl, n_gpu_sums)
     log(f"attention: {attn_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s algorithmic")
 
@@ -778,9 +866,28 @@ def main():
                               "peak": PEAK_HBM_GBS, "unit": "GB/s",
                               "frac": round(iso_achieved / PEAK_HBM_GBS, 4),
                               "avg_launch_us": round(iso_avg_ms * 1e3, 2),
+                              "time": spread(iso_ms),
                               "algorithmic_bytes_per_launch": int(iso_bytes_avg)},
+        "roofline_select": {
+            "kernel": "select_kernel (digest scoring + top-k + resident split), in the step",
+            "bound": "hbm",
+            "achieved": round(sbytes / (sel_step["median_us"] * 1e-6) / 1e9, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(sbytes / (sel_step["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "traffic": None, "time": sel_step, "algorithmic_bytes_per_launch": sbytes,
+            "measured": f"{n_sel} launches in {args.profile_steps} eager steps, HIP events at "
+                        "each kernel's start and end; median",
+            "shares_hbm_with": "the previous layer's attention on the main stream"},
+        "roofline_select_isolated": {
+            "kernel": "select_kernel, launched alone (each layer's digests once per pass)",
+            "bound": "hbm", "achieved": sel_alone["achieved"], "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(sel_alone["achieved"] / PEAK_HBM_GBS, 4),
+            "time": {k_: v for k_, v in sel_alone.items() if k_ not in ("achieved", "bytes")},
+            "algorithmic_bytes_per_launch": sbytes},
+        "attention_in_step_time": spread(attn_ms),
     }
     result["gemm"] = gemm_measure(wl, layers, torch, B)
+    result["gemm"]["in_step_kernel"] = gemm_step
     if args.dense:
         result["dense"] = dense_measure(wl, args, torch, B, wk, iso_avg_ms * 1e3)
     store = host_store(wl, args, B, wk) if (args.recall or args.drift_steps) else None

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libscoutattn.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = 0, -1, -2, -3, -4
 SA_F32, SA_BF16 = 0, 1
 SA_DIGEST_MEAN, SA_DIGEST_MINMAX = 0, 1
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 KIND = {"mean": SA_DIGEST_MEAN, "minmax": SA_DIGEST_MINMAX}
 
@@ -87,6 +87,8 @@ SIGNATURES = {
     "sa_decode_step": (ctypes.c_int, [_D, ctypes.c_int, _I, _I, _F, _P, _I,
                                       ctypes.POINTER(sa_layer), _P, _Z, _P, _P]),
     "sa_profile_attention": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.POINTER(_P), _I]),
+    "sa_profile_kernels": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(_P), ctypes.POINTER(_P),
+                                          _I]),
     "sa_dense_workspace_bytes": (_Z, [_D]),
     "sa_dense_decode": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _F, _P, _P, _P, _P, _Z, _P]),
     "sa_recall_workspace_bytes": (_Z, [_D, _I]),
@@ -228,8 +230,10 @@ def release_pinned() -> int:
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """A device byte buffer of at least nbytes (at least 256 so it is never empty)."""
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    """A zero-filled device byte buffer of at least nbytes (at least 256 so it is never
+    empty).  Zero is what the selection's arrival counters must hold before their first
+    use; the calls leave them zero again."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 # ---- calls (same names as the C ABI) -----------------------------------------------------
@@ -581,6 +585,20 @@ def sa_decode_step_offload(dims: Dims, kind: str, hidden: int, top_k: int, scale
         _ptr(ws, torch.uint8, name="ws"), ws.numel(), _stream(stream),
         None if side_stream is None else _stream(side_stream), plan.handle,
         _stream(host_stream), None if recall_stream is None else _stream(recall_stream)))
+
+
+PROFILE_STAGE = {"attention": 0, "select": 1, "gemm": 2}
+
+
+def sa_profile_kernels(stage: str, starts, stops):
+    """Time the next len(starts) launches of one stage's kernel ("attention", "select" or
+    "gemm") on this thread: `starts` and `stops` are torch.cuda.Event(enable_timing=True)
+    objects (already recorded once, so that they exist).  Read durations with
+    starts[i].elapsed_time(stops[i])."""
+    n = len(starts)
+    a = (_P * max(1, n))(*[e.cuda_event for e in starts])
+    b = (_P * max(1, n))(*[e.cuda_event for e in stops])
+    _check(lib().sa_profile_kernels(PROFILE_STAGE[stage], a, b, n))
 
 
 def sa_profile_attention(starts, stops):

@@ -23,12 +23,12 @@ namespace {
 
 thread_local std::string g_err;
 
-// Attention-kernel profiling events of the calling thread (sa_profile_attention).
+// Kernel profiling events of the calling thread, per stage (sa_profile_kernels).
 struct ProfileEvents {
   std::vector<hipEvent_t> start, stop;
   size_t next = 0;
 };
-thread_local ProfileEvents g_prof;
+thread_local ProfileEvents g_prof[SA_PROFILE_STAGES];
 
 // Events that order the streams of sa_decode_step, created on first use and reused by
 // every later call on the same thread (re-recording an event does not affect waits
@@ -42,12 +42,14 @@ struct EventPool {
 };
 thread_local EventPool g_events;
 
-void next_profile_events(hipEvent_t* e0, hipEvent_t* e1) {
+void next_profile_events(hipEvent_t* e0, hipEvent_t* e1,
+                         sa_profile_stage stage = SA_PROFILE_ATTENTION) {
+  ProfileEvents& P = g_prof[stage];
   *e0 = *e1 = nullptr;
-  if (g_prof.next < g_prof.start.size()) {
-    *e0 = g_prof.start[g_prof.next];
-    *e1 = g_prof.stop[g_prof.next];
-    ++g_prof.next;
+  if (P.next < P.start.size()) {
+    *e0 = P.start[P.next];
+    *e1 = P.stop[P.next];
+    ++P.next;
   }
 }
 
@@ -115,16 +117,22 @@ sa_status check_kind(sa_digest_kind k) {
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace of selection + attention: the attention partials (selection needs none).
+// Workspace of selection + attention: first the selection's hand-over buffers (their
+// counters stay zero between calls), then the attention partials.  The selection region is
+// sized for the larger of the two digest kinds, so one workspace serves both.
 struct Layout {
-  size_t parts, total;
+  size_t sel, parts, total;
   sa::AttnPlan plan;
 };
+size_t select_ws_bytes(const sa::Shape& s) {
+  return align_up(std::max(sa::select_plan(s, false).ws_bytes, sa::select_plan(s, true).ws_bytes));
+}
 Layout layout(const sa::Shape& s, int top_k) {
   Layout L;
   L.plan = sa::attn_plan(s, top_k);
-  L.parts = 0;
-  L.total = align_up(L.plan.ws_bytes);
+  L.sel = 0;
+  L.parts = select_ws_bytes(s);
+  L.total = L.parts + align_up(L.plan.ws_bytes);
   return L;
 }
 
@@ -156,15 +164,17 @@ sa_status check_scale(float scale) {
 }
 
 // selection of one layer: scores, top-k and split in one launch (scores written out only
-// when asked for)
+// when asked for); sel_ws is the selection region of a Layout
 sa_status run_select(const sa::Shape& s, bool minmax, const sa::QParts& q, const void* digests,
                      const int32_t* seq_lens, int top_k, const int32_t* block_table,
                      int32_t* gpu_blocks, int32_t* n_gpu, int32_t* cpu_blocks, int32_t* n_cpu,
                      float* scores, int32_t* cpu_blocks_host, int32_t* n_cpu_host,
-                     int32_t* gpu_pages, hipStream_t stream) {
-  SA_HIP(sa::launch_select(s, minmax, q, digests, seq_lens, top_k, block_table, gpu_blocks,
-                           n_gpu, cpu_blocks, n_cpu, scores, cpu_blocks_host, n_cpu_host,
-                           gpu_pages, stream),
+                     int32_t* gpu_pages, void* sel_ws, hipStream_t stream) {
+  hipEvent_t e0, e1;
+  next_profile_events(&e0, &e1, SA_PROFILE_SELECT);
+  SA_HIP(sa::launch_select(s, sa::select_plan(s, minmax), minmax, q, digests, seq_lens, top_k,
+                           block_table, gpu_blocks, n_gpu, cpu_blocks, n_cpu, scores,
+                           cpu_blocks_host, n_cpu_host, gpu_pages, sel_ws, stream, e0, e1),
          "select kernel");
   return SA_OK;
 }
@@ -177,19 +187,27 @@ int sa_abi_version(void) { return SA_ABI_VERSION; }
 
 const char* sa_last_error(void) { return g_err.c_str(); }
 
-sa_status sa_profile_attention(const hipEvent_t* start, const hipEvent_t* stop, int32_t n) {
+sa_status sa_profile_kernels(sa_profile_stage stage, const hipEvent_t* start,
+                             const hipEvent_t* stop, int32_t n) {
+  if ((int)stage < 0 || (int)stage >= SA_PROFILE_STAGES)
+    return fail(SA_ERR_INVALID_ARG, "unknown profile stage %d", (int)stage);
   if (n < 0) return fail(SA_ERR_INVALID_ARG, "n %d < 0", n);
   if (n > 0 && (!start || !stop)) return fail(SA_ERR_INVALID_ARG, "event arrays are NULL");
-  g_prof.start.assign(start, start + n);
-  g_prof.stop.assign(stop, stop + n);
-  g_prof.next = 0;
+  ProfileEvents& P = g_prof[stage];
+  P.start.assign(start, start + n);
+  P.stop.assign(stop, stop + n);
+  P.next = 0;
   for (int32_t i = 0; i < n; ++i)
-    if (!g_prof.start[i] || !g_prof.stop[i]) {
-      g_prof.start.clear();
-      g_prof.stop.clear();
+    if (!P.start[i] || !P.stop[i]) {
+      P.start.clear();
+      P.stop.clear();
       return fail(SA_ERR_INVALID_ARG, "event %d is NULL", i);
     }
   return ok();
+}
+
+sa_status sa_profile_attention(const hipEvent_t* start, const hipEvent_t* stop, int32_t n) {
+  return sa_profile_kernels(SA_PROFILE_ATTENTION, start, stop, n);
 }
 
 const char* sa_status_string(sa_status status) {
@@ -294,7 +312,10 @@ sa_status sa_predict_query(int32_t m, int32_t n, int32_t k, const void* x,
   const sa::GemmPlan plan = sa::gemm_plan(m, n, k);
   if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes))
     return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, plan.ws_bytes);
-  SA_HIP(sa::launch_gemm(m, n, k, x, 1, w, q, nullptr, nullptr, (float*)ws, plan, stream),
+  hipEvent_t e0, e1;
+  next_profile_events(&e0, &e1, SA_PROFILE_GEMM);
+  SA_HIP(sa::launch_gemm(m, n, k, x, 1, w, q, nullptr, nullptr, (float*)ws, plan, stream, true,
+                         e0, e1),
          "GEMM kernel");
   return ok();
 }
@@ -333,7 +354,7 @@ sa_status sa_select_blocks(const sa_dims* dims, sa_digest_kind kind, const float
   SA_CHECK(run_select(s, kind == SA_DIGEST_MINMAX, sa::plain_query(q, s.Hq * s.d), digests,
                       seq_lens, top_k, block_table,
                       gpu_blocks, n_gpu, cpu_blocks, n_cpu, scores, nullptr, nullptr, nullptr,
-                      stream));
+                      (char*)ws + L.sel, stream));
   return ok();
 }
 
@@ -870,6 +891,9 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
   int32_t* pages[2] = {(int32_t*)(base + SL.pages[0]), (int32_t*)(base + SL.pages[1])};
   char* sel_base = base + SL.sel;
   float* parts = (float*)(sel_base + SL.sel_layout.parts);
+  // the selections of the step run one after another (each stream is in order, and the
+  // side stream's selection of layer i+1 starts after layer i's), so they share one region
+  void* sel_ws = sel_base + SL.sel_layout.sel;
   const bool minmax = kind == SA_DIGEST_MINMAX;
   const int n = s.Hq * s.d;
   hipStream_t sel_stream = side_stream ? side_stream : stream;
@@ -937,13 +961,15 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
     //    comes from the same launch (both weights share X^i).  The GEMMs leave their k-slice
     //    partials; the selection and attention kernels sum them as they read the query.
     sa::QParts q_cur, q_next{};
+    hipEvent_t g0, g1;
+    next_profile_events(&g0, &g1, SA_PROFILE_GEMM);
     if (side_stream || !has_next) {
       e = sa::launch_gemm(s.B, n, hidden, L.x, 1, L.w_q, q_true, nullptr, nullptr, gemm_ws[0],
-                          SL.plan_single, stream, false);
+                          SL.plan_single, stream, false, g0, g1);
       q_cur = sa::gemm_result(SL.plan_single, s.B, n, 1, 0, q_true, gemm_ws[0]);
     } else {
       e = sa::launch_gemm(s.B, n, hidden, L.x, 2, L.w_q, q_true, layers[i + 1].w_q, qp,
-                          gemm_ws[0], SL.plan_dual, stream, false);
+                          gemm_ws[0], SL.plan_dual, stream, false, g0, g1);
       q_cur = sa::gemm_result(SL.plan_dual, s.B, n, 2, 0, q_true, gemm_ws[0]);
       q_next = sa::gemm_result(SL.plan_dual, s.B, n, 2, 1, qp, gemm_ws[0]);
     }
@@ -955,7 +981,7 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
       if (st == SA_OK)
         st = run_select(s, minmax, q_cur, L.digests, seq_lens, top_k, L.block_table,
                       L.gpu_blocks, L.n_gpu, L.cpu_blocks, L.n_cpu, nullptr, mirror_blocks(0),
-                      mirror_n(0), pages[0], stream);
+                      mirror_n(0), pages[0], sel_ws, stream);
       if (st == SA_OK && plan) st = spawn_host(0, q_cur, stream);
       if (st == SA_OK && side_stream) st = order(stream, side_stream);
       if (st != SA_OK) break;
@@ -966,8 +992,9 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
     if (has_next) {
       const sa_layer& N = layers[i + 1];
       if (side_stream) {
+        next_profile_events(&g0, &g1, SA_PROFILE_GEMM);
         e = sa::launch_gemm(s.B, n, hidden, L.x, 1, N.w_q, qp, nullptr, nullptr, gemm_ws[1],
-                            SL.plan_single, side_stream, false);
+                            SL.plan_single, side_stream, false, g0, g1);
         if (e != hipSuccess) st = hip_fail(e, "GEMM kernel");
         q_next = sa::gemm_result(SL.plan_single, s.B, n, 1, 0, qp, gemm_ws[1]);
       }
@@ -975,7 +1002,8 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
       if (st == SA_OK)
         st = run_select(s, minmax, q_next, N.digests, seq_lens, top_k, N.block_table,
                         N.gpu_blocks, N.n_gpu, N.cpu_blocks, N.n_cpu, nullptr,
-                        mirror_blocks(i + 1), mirror_n(i + 1), pages[(i + 1) & 1], sel_stream);
+                        mirror_blocks(i + 1), mirror_n(i + 1), pages[(i + 1) & 1], sel_ws,
+                        sel_stream);
       if (st == SA_OK && plan) st = spawn_host(i + 1, q_next, sel_stream);
       if (st != SA_OK) break;
     }

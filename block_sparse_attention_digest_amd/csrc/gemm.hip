@@ -17,6 +17,8 @@
 // so results are deterministic.  The plan sizes the grid to about
 // one workgroup per CU, so the whole product is one round of long-lived waves.  Two weight
 // matrices that share x (Q^i and Q_pred^{i+1}) can run as one launch.
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 
 #include "common.hpp"
@@ -247,7 +249,8 @@ GemmPlan gemm_plan(int m, int n_total, int k) {
 
 hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void* w0,
                        float* q0, const void* w1, float* q1, float* ws, const GemmPlan& plan,
-                       hipStream_t stream, bool sum_slices) {
+                       hipStream_t stream, bool sum_slices, hipEvent_t ev_start,
+                       hipEvent_t ev_stop) {
   const int n_total = n * nprob;
   const int mt = row_tiles(m);
   const int tiles = n_total / 16;
@@ -259,10 +262,12 @@ hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void
   const uint16_t* W0 = (const uint16_t*)w0;
   const uint16_t* W1 = (const uint16_t*)(nprob > 1 ? w1 : w0);
   float* Q1 = nprob > 1 ? q1 : q0;
+  // hipExtLaunchKernelGGL records the (optional) events at the kernel's own start and end
 #define SA_GEMM_CASE(MT)                                                                    \
   case MT:                                                                                  \
-    hipLaunchKernelGGL(gemm_kernel<MT>, grid, block, lds, stream, X, W0, W1, m, n, k,       \
-                       plan.kslice, n_total, tiles, plan.tpw, q0, Q1, plan.ksplit, ws);     \
+    hipExtLaunchKernelGGL(gemm_kernel<MT>, grid, block, lds, stream, ev_start, ev_stop, 0,  \
+                          X, W0, W1, m, n, k, plan.kslice, n_total, tiles, plan.tpw, q0,    \
+                          Q1, plan.ksplit, ws);                                             \
     break;
   switch (mt) {
     SA_GEMM_CASE(1) SA_GEMM_CASE(2) SA_GEMM_CASE(3) default: SA_GEMM_CASE(4)

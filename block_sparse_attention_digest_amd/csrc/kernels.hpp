@@ -56,7 +56,8 @@ GemmPlan gemm_plan(int m, int n_total, int k);
 // result of problem `prob` is left as gemm_result(...) describes, for a consumer to sum.
 hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void* w0,
                        float* q0, const void* w1, float* q1, float* ws, const GemmPlan& plan,
-                       hipStream_t stream, bool sum_slices = true);
+                       hipStream_t stream, bool sum_slices = true,
+                       hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 QParts gemm_result(const GemmPlan& plan, int m, int n, int nprob, int prob, const float* q,
                    const float* ws);
 // ---- dense attention: the list of every resident block per pair ---------------------------
@@ -79,14 +80,27 @@ hipError_t launch_recall(const Shape& s, int list_stride, int max_recall, const 
 // 4); q_out may be device-addressable host memory
 hipError_t launch_gather_query(const QParts& q, int rows, int n, float* q_out, hipStream_t stream);
 
-// ---- selection: scores, top-k and the resident split, one workgroup per pair ----------------
+// ---- selection: scores, top-k and the resident split --------------------------------------
+// Pairs [0, whole) get one workgroup each; the other `split` pairs are cut into nchunk
+// chunks of `chunk` rows, one workgroup each, which hand their scores over through ws_bytes
+// of workspace whose arrival counters must be zero before the first launch (every launch
+// leaves them zero again).
+struct SelectPlan {
+  int whole;        // pairs of one workgroup each (full rounds of one per CU)
+  int split;        // pairs cut into chunks (the rest)
+  int chunk;        // rows per chunk workgroup
+  int nchunk;       // chunks per split pair (of max_blocks rows)
+  size_t ws_bytes;  // hand-over buffers; 0 when no pair is split
+};
+SelectPlan select_plan(const Shape& s, bool minmax);
 // gpu_pages (optional, [pairs][top_k]): the page of each resident list entry, -1 past n_gpu.
-hipError_t launch_select(const Shape& s, bool minmax, const QParts& q, const void* digests,
-                         const int32_t* seq_lens, int top_k, const int32_t* block_table,
-                         int32_t* gpu_blocks, int32_t* n_gpu, int32_t* cpu_blocks,
-                         int32_t* n_cpu, float* scores_or_null,
+hipError_t launch_select(const Shape& s, const SelectPlan& plan, bool minmax, const QParts& q,
+                         const void* digests, const int32_t* seq_lens, int top_k,
+                         const int32_t* block_table, int32_t* gpu_blocks, int32_t* n_gpu,
+                         int32_t* cpu_blocks, int32_t* n_cpu, float* scores_or_null,
                          int32_t* cpu_blocks_host, int32_t* n_cpu_host,
-                         int32_t* gpu_pages_or_null, hipStream_t stream);
+                         int32_t* gpu_pages_or_null, void* ws, hipStream_t stream,
+                         hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // ---- attention: balanced waves write partials, then the reduction / merge per row -------
 struct AttnPlan {

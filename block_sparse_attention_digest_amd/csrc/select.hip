@@ -1,27 +1,49 @@
 // Block selection of ScoutAttention [arXiv:2603.27138, HTML Sec. 2.2 and 3.2; Algorithm 1]:
 //   B_pred = TopK(Q K_digest^T) per (sequence, KV head), then B_cpu = B_pred \ B_gpu.
 //
-// One workgroup of 8 waves per (sequence, KV head) does the whole selection:
+// Work split: whole (sequence, KV head) pairs go one to an 8-wave workgroup, in as many
+// full rounds of one per CU as the pairs fill; the pairs left over are cut into pieces,
+// about one per CU in all, one workgroup each.  So every CU streams about the same digest
+// bytes (at the 40-layer decode shape: 320 pairs on 256 CUs, each CU one whole pair plus a
+// quarter of one of the 64 others), where one workgroup per pair would put two pairs on a
+// quarter of the CUs and end with them.  The pieces come first in the grid and are short,
+// so their hand-over (step 3) is over while the whole pairs still stream.
 //   1. scoring: the G query heads of the KV head are folded into per-channel coefficients
 //      -- the group sum sum_g q_g for mean digests, and for min/max digests
 //        sum_g max(q_gc min_c, q_gc max_c) = (sum_g max(q_gc, 0)) max_c + (sum_g min(q_gc, 0)) min_c
 //      (exact, since max_c >= min_c) -- so a digest element costs one or two FMAs.  The
-//      query rows (all their parts), the first digest batch and the pair's block-table
+//      query rows (all their parts), the first digest batch and the item's block-table
 //      entries are requested together in one round: the workgroup sums the query parts into
 //      LDS and each lane reads its coefficients from there behind an LDS-only barrier, while
-//      the digests are already in flight.  Each wave streams a contiguous share of the
-//      pair's digest rows with 16-byte loads, the next batch of 8 loads in flight while the
-//      current one is reduced (DPP row sums; loads are unconditional so the waits cover one
-//      batch); the scores stay in LDS.  Every pair's workgroup is resident at once, so HBM
-//      bandwidth is shared evenly and the whole digest set streams in one pass.
+//      the digests are already in flight.  The waves stream the item's rows in batches of
+//      8 coalesced 16-byte loads per lane, the next batch in flight while the current one is
+//      reduced (DPP row sums; loads are unconditional so the waits cover one batch); after
+//      its first two batches a wave takes each next batch from a counter in LDS, so the
+//      waves of a workgroup run out of rows together rather than each at the end of a
+//      fixed share (under load, one wave's latency differs from another's by microseconds).
+//      The scores stay in LDS.
 //   2. top-k: a histogram of the score values over 256 equal-width buckets locates the
 //      bucket holding the k-th largest score; the few scores in that bucket are ranked
-//      exactly by (score, lower index first).  Crowded buckets (e.g. all scores equal) fall
-//      back to an exact MSB-first radix select on order-preserving 32-bit keys.
-//   3. split: the selected blocks are compacted in ascending order and split by the block
-//      table (read during step 1) into the resident and offloaded lists; the offloaded list
-//      can also be written straight into a host mirror (the hand-off of Algorithm 1), and
-//      the pages of the resident list next to it (so attention skips the table lookup).
+//      exactly by (score, lower position first).  A crowded bucket (e.g. all scores equal)
+//      falls back to an exact MSB-first radix select on order-preserving 32-bit keys.
+//   3. hand-over (pieces only): each piece selects its own top min(k, rows) -- every block
+//      of the pair's selection that lies in the piece is among them -- and writes them, in
+//      ascending block order with their scores and block-table entries, to the workspace
+//      with device-scope stores (written through to the memory all XCDs share); it waits
+//      until they have completed and only then counts itself in on the pair's arrival
+//      counter (a device-scope atomic add).  The piece that counts last has therefore every
+//      other piece's candidates in memory: it reads them back with device-scope loads (in
+//      piece order, so still ascending by block), resets the counter to zero for the next
+//      launch, and selects the pair's top-k among them (step 2 again).  No workgroup ever
+//      waits for another.
+//   4. split: the selected blocks are compacted in ascending order and split by the block
+//      table into the resident and offloaded lists; the offloaded list can also be written
+//      straight into a host mirror (the hand-off of Algorithm 1), and the pages of the
+//      resident list next to it (so attention skips the table lookup).
+#include <hip/hip_ext.h>
+
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -30,11 +52,17 @@ namespace {
 
 constexpr int kSelWaves = 8;
 constexpr int kSelThreads = kSelWaves * kWave;
+static_assert(kSelThreads >= 256, "a thread per histogram bucket");
 constexpr int kBatch = 8;        // 16-byte loads per lane per batch
 constexpr int kMaxCand = 256;    // boundary-bucket candidates ranked directly
 constexpr int kSelPartGroup = 4; // query parts loaded together
 constexpr int kTblRun = 8;       // block-table entries a thread holds in registers
+constexpr int kMaxRows = kTblRun * kSelThreads;  // rows of one item: its entries fit them
+constexpr int kMinChunkRows = 64;
+constexpr int kCUs = 256;        // compute units of the chip (one round of whole pairs)
 constexpr int kMaxGroup = 8;     // query heads per KV head
+// two workgroups per CU at once (a whole pair's beside a piece's): 4 waves per SIMD
+constexpr int kSelWavesPerSimd = 4;
 constexpr uint8_t kSelected = 1, kResident = 2;  // per-block flag bits
 
 template <typename T>
@@ -53,6 +81,15 @@ struct Digest<float> {  // four float per 16-byte vector
   }
 };
 
+// Device-scope accesses of the chunks' hand-over: stores written through to (and loads
+// served from) the memory every XCD shares, so no L2 cache holds a stale copy.
+__device__ __forceinline__ void store_device(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_device(uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Inclusive prefix sum over all threads of the workgroup.
 __device__ __forceinline__ uint32_t block_scan_incl(uint32_t v, uint32_t* tmp) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -68,6 +105,7 @@ __device__ __forceinline__ uint32_t block_scan_incl(uint32_t v, uint32_t* tmp) {
   __syncthreads();
   return v + add;
 }
+
 
 // The bucket (0..255) of score v when [lo, hi] is split into 256 equal-width buckets.  The
 // map is monotone in v, so a higher bucket means a strictly larger score.
@@ -93,14 +131,26 @@ __device__ __forceinline__ float wave_max(float v) {
   return max_xor32(max_xor16(v));
 }
 
+// The hand-over buffers in the workspace: per pair and block, a piece's candidates at
+// the piece's own rows (score, block-table entry, block index), the candidate count of every
+// (pair, piece), then the arrival counters [pairs] (zero between launches).
+struct Handover {
+  uint32_t* score;  // [pairs][max_blocks]
+  uint32_t* page;   // [pairs][max_blocks]
+  uint32_t* blk;    // [pairs][max_blocks]
+  uint32_t* n;      // [pairs][nchunk]
+  uint32_t* count;  // [pairs]
+};
+
 template <typename T, int D, bool MINMAX>
-__global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
+__global__ __launch_bounds__(kSelThreads, kSelWavesPerSimd) void select_kernel(
     const QParts q, const T* __restrict__ dig, const int32_t* __restrict__ seq_lens,
-    int Hkv, int G, int bs, int max_blocks, int top_k, const int32_t* __restrict__ table,
-    int32_t* __restrict__ gpu_blocks, int32_t* __restrict__ n_gpu,
-    int32_t* __restrict__ cpu_blocks, int32_t* __restrict__ n_cpu,
-    float* __restrict__ scores_out, int32_t* __restrict__ cpu_blocks_host,
-    int32_t* __restrict__ n_cpu_host, int32_t* __restrict__ gpu_pages) {
+    int Hkv, int G, int bs, int max_blocks, int top_k, int whole, int split, int chunk,
+    int nchunk, const int32_t* __restrict__ table, int32_t* __restrict__ gpu_blocks,
+    int32_t* __restrict__ n_gpu, int32_t* __restrict__ cpu_blocks,
+    int32_t* __restrict__ n_cpu, float* __restrict__ scores_out,
+    int32_t* __restrict__ cpu_blocks_host, int32_t* __restrict__ n_cpu_host,
+    int32_t* __restrict__ gpu_pages, Handover xs) {
   constexpr int VEC = Digest<T>::N;
   constexpr int LPR = D / VEC;             // lanes per digest row
   constexpr int BPI = kWave / LPR;         // blocks per load instruction
@@ -108,22 +158,39 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
   constexpr int BPB = kBatch / LPB * BPI;  // blocks per batch (per wave)
   constexpr int ROW = LPB * D;
 
-  extern __shared__ float sc[];                                 // [max_blocks] scores
-  uint8_t* flag = reinterpret_cast<uint8_t*>(sc + max_blocks);  // [max_blocks]
-  // [max_blocks] block-table entries, kept only when the pages are written out
-  int32_t* pg = reinterpret_cast<int32_t*>(sc + max_blocks + (max_blocks + 3) / 4);
+  // per position j < max_blocks: score, block-table entry, block index (the last piece's
+  // candidates; elsewhere the position is the block) and flags
+  extern __shared__ float sc[];
+  int32_t* pg = reinterpret_cast<int32_t*>(sc + max_blocks);
+  uint16_t* bk = reinterpret_cast<uint16_t*>(pg + max_blocks);
+  uint8_t* flag = reinterpret_cast<uint8_t*>(bk + max_blocks);
   __shared__ uint32_t hist[256];
   __shared__ uint32_t tmp[kSelWaves];
   __shared__ float red_lo[kSelWaves], red_hi[kSelWaves];
   __shared__ uint32_t cand_key[kMaxCand];
   __shared__ int cand_idx[kMaxCand];
-  __shared__ uint32_t sel_digit, sel_remaining, sel_count, ncand, tot_res, tot_off;
-  __shared__ float4 q_sum[kMaxGroup * D / 4];  // the pair's G query rows, parts summed
+  __shared__ uint32_t sel_digit, sel_remaining, sel_count, ncand, tot_a, tot_b, arrived;
+  __shared__ uint32_t next_row;                 // the next unscored batch of the item
+  __shared__ float4 q_sum[kMaxGroup * D / 4];   // the pair's G query rows, parts summed
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // scalar loop bounds
-  const int pair = blockIdx.x;
+  // work item: the first split * nchunk workgroups take the pieces of pairs [whole, whole +
+  // split), the rest one whole pair each (pairs [0, whole))
+  const bool whole_item = (int)blockIdx.x >= split * nchunk;
+  const int pair = whole_item ? (int)blockIdx.x - split * nchunk : whole + (int)blockIdx.x / nchunk;
+  const int ck = whole_item ? 0 : (int)blockIdx.x % nchunk;
   const int s = pair / Hkv, h = pair % Hkv;
+
+  // blocks of the sequence, clamped to the table's span (a bad length cannot move a read
+  // past the pair's rows), and the pieces that hold them (at least one, which also handles
+  // a pair without blocks)
+  const int nb = min(max((seq_lens[s] + bs - 1) / bs, 0), max_blocks);
+  const int live = whole_item ? 1 : max(1, (nb + chunk - 1) / chunk);
+  if (ck >= live) return;  // (uniform) a piece past the sequence's blocks
+  const bool alone = live == 1;
+  const int r0 = ck * chunk, r1 = alone ? nb : min(nb, r0 + chunk);  // this item's rows
+  const uint32_t ks = (uint32_t)min(top_k, nb);
 
   // The pair's query rows come first, in one round: thread t loads float4 t of the G rows
   // (G D / 4 <= kSelThreads), its first kSelPartGroup parts at once (indexes clamped, so every
@@ -137,39 +204,33 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
   for (int u = 0; u < kSelPartGroup; ++u)
     qp[u] = *reinterpret_cast<const float4*>(qsrc + (size_t)min(u, q.parts - 1) * q.part_stride);
   __builtin_amdgcn_sched_barrier(0);  // issued ahead of the digest and table loads
-  // blocks of the sequence, clamped to the table's span (a bad length cannot move a read
-  // past the pair's rows)
-  const int nb = min(max((seq_lens[s] + bs - 1) / bs, 0), max_blocks);
-  const uint32_t ks = (uint32_t)min(top_k, nb);
   const int cg = lane % LPR, bi = lane / LPR;
 
-  // this wave's contiguous share of the pair's blocks
-  const int per_wave = (nb + kSelWaves - 1) / kSelWaves;
-  const int wb0 = min(nb, wave * per_wave), wb1 = min(nb, wb0 + per_wave);
   const T* base = dig + (size_t)pair * max_blocks * ROW + cg * VEC;
   uint4 bufa[kBatch], bufb[kBatch];
-  // Loads are issued unconditionally (rows past the range clamped to its last row, their
-  // scores discarded), so the waits before a batch cover that batch only.
+  // Batch [b, b + BPB) of the item's rows.  Loads are issued unconditionally (rows past the
+  // item clamped to its last row, their scores discarded), so the waits before a batch cover
+  // that batch only.
   auto load_batch = [&](int b_first, uint4* buf) {
 #pragma unroll
     for (int u = 0; u < kBatch / LPB; ++u) {
-      const int b = max(min(b_first + u * BPI + bi, wb1 - 1), 0);
+      const int b = max(min(b_first + u * BPI + bi, r1 - 1), 0);
 #pragma unroll
       for (int r = 0; r < LPB; ++r)
         buf[u * LPB + r] = *reinterpret_cast<const uint4*>(base + (size_t)b * ROW + r * D);
     }
   };
-  load_batch(wb0, bufa);  // (a wave with no rows re-reads a valid one, unused)
+  // the first two batches of a wave are fixed; later ones come from next_row
+  int cur = r0 + wave * BPB, nxt = r0 + (kSelWaves + wave) * BPB;
+  load_batch(cur, bufa);  // (a wave with no rows re-reads a valid one, unused)
 
-  // residency of every block: the block table is read while the digests stream, into
-  // registers (kTblRun entries per thread) that are only consumed after the scoring
+  // the item's block-table entries are read while the digests stream, into registers
+  // (row r0 + tid + u * kSelThreads in entry u) that are only consumed after the scoring
   const int32_t* trow = table + (size_t)pair * max_blocks;
-  const bool tbl_regs = nb > 0 && nb <= kTblRun * kSelThreads;  // (uniform)
   int32_t tbl[kTblRun];  // (loads unconditional, indexes clamped to a valid entry)
 #pragma unroll
-  for (int u = 0; u < kTblRun; ++u) tbl[u] = trow[max(min(tid + u * kSelThreads, nb - 1), 0)];
-  if (tid < 256) hist[tid] = 0;
-  if (tid == 0) ncand = 0;
+  for (int u = 0; u < kTblRun; ++u) tbl[u] = trow[max(min(r0 + tid + u * kSelThreads, r1 - 1), 0)];
+  if (tid == 0) next_row = (uint32_t)(r0 + 2 * kSelWaves * BPB);
 
   // each query element is the sum of its parts, taken in part order
   {
@@ -190,7 +251,7 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
     }
     if (q_own) q_sum[tid] = v;
   }
-  lds_barrier();  // the summed rows are visible; the digest loads stay in flight
+  lds_barrier();  // the summed rows and next_row are visible; the digest loads stay in flight
 
   // per-channel coefficients of this lane's VEC channels, summed over the heads in order
   float ca[VEC], cb[VEC];
@@ -230,7 +291,7 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
         }
       }
       acc = group_sum<LPR>(acc);
-      if (b < wb1) {
+      if (b < r1) {
         lo = fminf(lo, acc);
         hi = fmaxf(hi, acc);
         if (cg == 0) {
@@ -240,132 +301,215 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
       }
     }
   };
+  // a batch from the counter: lane 0 asks, and the answer is read (made scalar) only when
+  // it is needed, two batches later
+  auto take = [&]() {
+    uint32_t v = 0;
+    if (lane == 0) v = atomicAdd(&next_row, (uint32_t)BPB);
+    return v;
+  };
+  auto scalar = [](uint32_t v) { return (int)__builtin_amdgcn_readfirstlane(v); };
   // the scheduling barriers keep the compiler from sinking a batch's loads to their use
-  for (int b = wb0; b < wb1; b += 2 * BPB) {
-    load_batch(min(b + BPB, wb1 - 1), bufb);
+  while (cur < r1) {
+    load_batch(nxt, bufb);
+    const uint32_t t1 = take();
     __builtin_amdgcn_sched_barrier(0);
-    score_batch(b, bufa);
-    load_batch(min(b + 2 * BPB, wb1 - 1), bufa);
+    score_batch(cur, bufa);
+    if (nxt >= r1) break;
+    const int after = scalar(t1);
+    load_batch(after, bufa);
+    const uint32_t t2 = take();
     __builtin_amdgcn_sched_barrier(0);
-    if (b + BPB < wb1) score_batch(b + BPB, bufb);
+    score_batch(nxt, bufb);
+    cur = after;
+    nxt = scalar(t2);
   }
-  // the residency flags (and pages), from the table entries read at the start
-  if (tbl_regs) {
+
+  // flags (and pages) of the item's rows, from the table entries read at the start
 #pragma unroll
-    for (int u = 0; u < kTblRun; ++u) {
-      const int i = tid + u * kSelThreads;
-      if (i < nb) {
-        flag[i] = tbl[u] >= 0 ? kResident : 0;
-        if (gpu_pages) pg[i] = tbl[u];
-      }
-    }
-  } else {
-    for (int i = tid; i < nb; i += kSelThreads) {
-      const int32_t e = trow[i];
-      flag[i] = e >= 0 ? kResident : 0;
-      if (gpu_pages) pg[i] = e;
+  for (int u = 0; u < kTblRun; ++u) {
+    const int i = r0 + tid + u * kSelThreads;
+    if (i < r1) {
+      flag[i] = tbl[u] >= 0 ? kResident : 0;
+      pg[i] = tbl[u];
     }
   }
   lo = wave_min(lo);
   hi = wave_max(hi);
   if (lane == 0) { red_lo[wave] = lo; red_hi[wave] = hi; }
-  __syncthreads();  // scores, flags, histogram reset and the per-wave ranges are visible
+  __syncthreads();  // scores, flags and the per-wave ranges are visible
   lo = red_lo[0];
   hi = red_hi[0];
   for (int w = 1; w < kSelWaves; ++w) { lo = fminf(lo, red_lo[w]); hi = fmaxf(hi, red_hi[w]); }
-  const float span = hi - lo;
-  const bool bucketed = span > 0.f && span < INFINITY;
-  const float to_bucket = bucketed ? 256.f / span : 0.f;
 
-  // top-k, fast path: histogram of score values, exact ranking inside the boundary bucket
-  uint32_t B = 0, r = 0, cnt = 0xffffffffu;
-  if (bucketed) {
-    for (int i = tid; i < nb; i += kSelThreads) atomicAdd(&hist[bucket_of(sc[i], lo, to_bucket)], 1u);
-    __syncthreads();
-    const uint32_t c = tid < 256 ? hist[255 - tid] : 0u;  // thread 0: the highest bucket
-    const uint32_t cge = block_scan_incl(c, tmp);
-    const uint32_t cgt = cge - c;
-    if (tid < 256 && cgt < ks && cge >= ks) {
-      sel_digit = 255u - (uint32_t)tid;
-      sel_remaining = ks - cgt;
-      sel_count = c;
-    }
-    __syncthreads();
-    B = sel_digit;
-    r = sel_remaining;
-    cnt = sel_count;
-  }
-  if (cnt <= (uint32_t)kMaxCand) {
-    for (int i = tid; i < nb; i += kSelThreads) {
-      const uint32_t b = (uint32_t)bucket_of(sc[i], lo, to_bucket);
-      if (b > B) flag[i] |= kSelected;
-      if (b == B) {
-        const uint32_t pos = atomicAdd(&ncand, 1u);
-        cand_key[pos] = order_key(sc[i]);
-        cand_idx[pos] = i;
-      }
-    }
-    __syncthreads();
-    for (uint32_t c = tid; c < cnt; c += kSelThreads) {
-      const uint32_t key = cand_key[c];
-      const int idx = cand_idx[c];
-      uint32_t rank = 0;
-      for (uint32_t j = 0; j < cnt; ++j) {
-        const uint32_t kj = cand_key[j];
-        rank += kj > key || (kj == key && cand_idx[j] < idx);
-      }
-      if (rank < r) flag[idx] |= kSelected;
-    }
-    __syncthreads();
-  } else {
-    // General path: exact radix select of the ks-th largest key, 8 bits per pass.
-    uint32_t prefix = 0, mask = 0, remaining = ks;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      if (tid < 256) hist[tid] = 0;
+  // Marks, in flag, the kk largest of sc[b0 .. b0 + n) (equal scores: the lower position
+  // first), whose minimum and maximum are lo and hi.  Every thread calls it.
+  auto topk = [&](int b0, int n, uint32_t kk, float lo, float hi) {
+    if (kk >= (uint32_t)n) {  // all of them (also none)
+      for (int i = tid; i < n; i += kSelThreads) flag[b0 + i] |= kSelected;
       __syncthreads();
-      for (int i = tid; i < nb; i += kSelThreads) {
-        const uint32_t kv = order_key(sc[i]);
-        if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1u);
-      }
+      return;
+    }
+    if (tid < 256) hist[tid] = 0;
+    if (tid == 0) ncand = 0;
+    __syncthreads();
+    const float span = hi - lo;
+    const bool bucketed = span > 0.f && span < INFINITY;
+    const float to_bucket = bucketed ? 256.f / span : 0.f;
+    // fast path: histogram of score values, exact ranking inside the boundary bucket
+    uint32_t B = 0, r = 0, cnt = 0xffffffffu;
+    if (bucketed) {
+      for (int i = tid; i < n; i += kSelThreads)
+        atomicAdd(&hist[bucket_of(sc[b0 + i], lo, to_bucket)], 1u);
       __syncthreads();
-      const uint32_t c = tid < 256 ? hist[255 - tid] : 0u;
+      const uint32_t c = tid < 256 ? hist[255 - tid] : 0u;  // thread 0: the highest bucket
       const uint32_t cge = block_scan_incl(c, tmp);
       const uint32_t cgt = cge - c;
-      if (tid < 256 && cgt < remaining && cge >= remaining) {
+      if (tid < 256 && cgt < kk && cge >= kk) {
         sel_digit = 255u - (uint32_t)tid;
-        sel_remaining = remaining - cgt;
+        sel_remaining = kk - cgt;
+        sel_count = c;
       }
       __syncthreads();
-      prefix |= sel_digit << shift;
-      mask |= 255u << shift;
-      remaining = sel_remaining;
+      B = sel_digit;
+      r = sel_remaining;
+      cnt = sel_count;
+    }
+    if (cnt <= (uint32_t)kMaxCand) {
+      for (int i = tid; i < n; i += kSelThreads) {
+        const uint32_t b = (uint32_t)bucket_of(sc[b0 + i], lo, to_bucket);
+        if (b > B) flag[b0 + i] |= kSelected;
+        if (b == B) {
+          const uint32_t pos = atomicAdd(&ncand, 1u);
+          cand_key[pos] = order_key(sc[b0 + i]);
+          cand_idx[pos] = i;
+        }
+      }
+      __syncthreads();
+      for (uint32_t c = tid; c < cnt; c += kSelThreads) {
+        const uint32_t key = cand_key[c];
+        const int idx = cand_idx[c];
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < cnt; ++j) {
+          const uint32_t kj = cand_key[j];
+          rank += kj > key || (kj == key && cand_idx[j] < idx);
+        }
+        if (rank < r) flag[b0 + idx] |= kSelected;
+      }
+      __syncthreads();
+    } else {
+      // General path: exact radix select of the kk-th largest key, 8 bits per pass.
+      uint32_t prefix = 0, mask = 0, remaining = kk;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        if (tid < 256) hist[tid] = 0;
+        __syncthreads();
+        for (int i = tid; i < n; i += kSelThreads) {
+          const uint32_t kv = order_key(sc[b0 + i]);
+          if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        const uint32_t c = tid < 256 ? hist[255 - tid] : 0u;
+        const uint32_t cge = block_scan_incl(c, tmp);
+        const uint32_t cgt = cge - c;
+        if (tid < 256 && cgt < remaining && cge >= remaining) {
+          sel_digit = 255u - (uint32_t)tid;
+          sel_remaining = remaining - cgt;
+        }
+        __syncthreads();
+        prefix |= sel_digit << shift;
+        mask |= 255u << shift;
+        remaining = sel_remaining;
+        __syncthreads();
+      }
+      const uint32_t thr = prefix;         // the kk-th largest key
+      const uint32_t take_eq = remaining;  // keys equal to thr that are selected
+      const int per = (n + kSelThreads - 1) / kSelThreads;
+      const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
+      uint32_t ties = 0;
+      for (int i = i0; i < i1; ++i) ties += order_key(sc[b0 + i]) == thr;
+      const uint32_t tie_base = block_scan_incl(ties, tmp) - ties;
+      uint32_t seen = 0;
+      for (int i = i0; i < i1; ++i) {
+        const uint32_t kv = order_key(sc[b0 + i]);
+        bool sel = kv > thr;
+        if (kv == thr) { sel = tie_base + seen < take_eq; ++seen; }
+        if (sel) flag[b0 + i] |= kSelected;
+      }
       __syncthreads();
     }
-    const uint32_t thr = prefix;         // the ks-th largest key
-    const uint32_t take_eq = remaining;  // keys equal to thr that are selected
-    const int per = (nb + kSelThreads - 1) / kSelThreads;
-    const int i0 = min(nb, tid * per), i1 = min(nb, i0 + per);
-    uint32_t ties = 0;
-    for (int i = i0; i < i1; ++i) ties += order_key(sc[i]) == thr;
-    const uint32_t tie_base = block_scan_incl(ties, tmp) - ties;
-    uint32_t seen = 0;
-    for (int i = i0; i < i1; ++i) {
-      const uint32_t kv = order_key(sc[i]);
-      bool sel = kv > thr;
-      if (kv == thr) { sel = tie_base + seen < take_eq; ++seen; }
-      if (sel) flag[i] |= kSelected;
-    }
-    __syncthreads();
-  }
+  };
 
-  // ascending compaction of the selected blocks, split by residency.  The offloaded list
-  // is assembled in LDS (over the scores, no longer needed) and then written out with
+  int n = nb;        // positions the final selection runs over
+  bool cand = false; // positions hold the pieces' candidates (block index in bk)
+  if (!alone) {
+    // 3. hand-over: this piece's top min(k, rows), ascending, to the workspace
+    topk(r0, r1 - r0, min(ks, (uint32_t)(r1 - r0)), lo, hi);
+    const int per = (r1 - r0 + kSelThreads - 1) / kSelThreads;
+    const int i0 = min(r1, r0 + tid * per), i1 = min(r1, i0 + per);
+    uint32_t mine = 0;
+    for (int i = i0; i < i1; ++i) mine += flag[i] & kSelected;
+    uint32_t pos = block_scan_incl(mine, tmp) - mine;
+    const size_t row0 = (size_t)pair * max_blocks;
+    for (int i = i0; i < i1; ++i) {
+      if (flag[i] & kSelected) {
+        const size_t at = row0 + r0 + pos++;
+        store_device(xs.score + at, __float_as_uint(sc[i]));
+        store_device(xs.page + at, (uint32_t)pg[i]);
+        store_device(xs.blk + at, (uint32_t)i);
+      }
+    }
+    if (tid == kSelThreads - 1)
+      store_device(xs.n + (size_t)pair * nchunk + ck, pos);  // (the last thread's end = count)
+    __builtin_amdgcn_s_waitcnt(0);  // every store of this thread has completed
+    __syncthreads();                // ... and of every thread of the workgroup
+    if (tid == 0)
+      arrived = __hip_atomic_fetch_add(xs.count + pair, 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrived != (uint32_t)(live - 1)) return;  // (uniform) another piece comes later
+    // the last piece: every other piece's candidates are in memory; gather them in piece
+    // order (ascending by block) into positions 0 .. n
+    if (tid == 0) store_device(xs.count + pair, 0u);
+    n = 0;
+    lo = INFINITY;
+    hi = -INFINITY;
+    for (int c = 0; c < live; ++c) {
+      // (a count read back is clamped to the piece and to the positions left)
+      const int nc = min(min((int)load_device(xs.n + (size_t)pair * nchunk + c), chunk),
+                         max_blocks - n);
+      const size_t src = row0 + (size_t)c * chunk;
+      for (int j = tid; j < nc; j += kSelThreads) {
+        const float v = __uint_as_float(load_device(xs.score + src + j));
+        const int32_t e = (int32_t)load_device(xs.page + src + j);
+        const uint32_t b = load_device(xs.blk + src + j);
+        sc[n + j] = v;
+        pg[n + j] = e;
+        bk[n + j] = (uint16_t)min(b, (uint32_t)(max_blocks - 1));
+        flag[n + j] = e >= 0 ? kResident : 0;
+        lo = fminf(lo, v);
+        hi = fmaxf(hi, v);
+      }
+      n += nc;
+    }
+    cand = true;
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lane == 0) { red_lo[wave] = lo; red_hi[wave] = hi; }
+    __syncthreads();
+    lo = red_lo[0];
+    hi = red_hi[0];
+    for (int w = 1; w < kSelWaves; ++w) { lo = fminf(lo, red_lo[w]); hi = fmaxf(hi, red_hi[w]); }
+  }
+  topk(0, n, ks, lo, hi);
+
+  // 4. ascending compaction of the selected positions, split by residency.  The offloaded
+  // list is assembled in LDS (over the scores, no longer needed) and then written out with
   // coalesced stores, to device memory and, when given, straight into the host mirror
   // (coherent page-locked host memory, which the device writes through without caching,
   // so the values are in host memory once the kernel has completed): the hand-off needs
   // no copy.
-  const int per = (nb + kSelThreads - 1) / kSelThreads;
-  const int i0 = min(nb, tid * per), i1 = min(nb, i0 + per);
+  const int per = (n + kSelThreads - 1) / kSelThreads;
+  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
   uint32_t cnt_res = 0, cnt_off = 0;
   for (int i = i0; i < i1; ++i) {
     const uint8_t f = flag[i];
@@ -375,22 +519,24 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
   const uint32_t packed = cnt_res | (cnt_off << 16);
   const uint32_t incl = block_scan_incl(packed, tmp);
   uint32_t pos_res = (incl - packed) & 0xffffu, pos_off = (incl - packed) >> 16;
-  if (tid == kSelThreads - 1) { tot_res = incl & 0xffffu; tot_off = incl >> 16; }
+  if (tid == kSelThreads - 1) { tot_a = incl & 0xffffu; tot_b = incl >> 16; }
   int32_t* grow = gpu_blocks + (size_t)pair * top_k;
   int32_t* prow = gpu_pages ? gpu_pages + (size_t)pair * top_k : nullptr;
   int32_t* off_lds = reinterpret_cast<int32_t*>(sc);  // [top_k] <= [max_blocks]
+  __syncthreads();  // (every score read before off_lds overwrites them)
   for (int i = i0; i < i1; ++i) {
     const uint8_t f = flag[i];
+    const int32_t blk = cand ? (int32_t)bk[i] : i;
     if (f == (kSelected | kResident)) {
-      grow[pos_res] = i;
+      grow[pos_res] = blk;
       if (prow) prow[pos_res] = pg[i];
       ++pos_res;
     } else if (f == kSelected) {
-      off_lds[pos_off++] = i;
+      off_lds[pos_off++] = blk;
     }
   }
   __syncthreads();
-  const int nr = (int)tot_res, no = (int)tot_off;
+  const int nr = (int)tot_a, no = (int)tot_b;
   for (int j = nr + tid; j < top_k; j += kSelThreads) {
     grow[j] = -1;
     if (prow) prow[j] = -1;
@@ -410,35 +556,70 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_kernel(
 }
 
 template <typename T, int D>
-hipError_t select_typed(const Shape& s, bool minmax, const QParts& q, const void* dig,
-                        const int32_t* lens, int top_k, const int32_t* table, int32_t* gb,
-                        int32_t* ng, int32_t* cb, int32_t* nc, float* scores, int32_t* cbh,
-                        int32_t* nch, int32_t* gp, hipStream_t st) {
-  // scores, flags (padded to a float boundary) and, when pages are written, table entries
-  const size_t lds = (size_t)(s.max_blocks + (s.max_blocks + 3) / 4) * sizeof(float) +
-                     (gp ? (size_t)s.max_blocks * sizeof(int32_t) : 0);
-  const dim3 grid(s.B * s.Hkv), block(kSelThreads);
+hipError_t select_typed(const Shape& s, const SelectPlan& p, bool minmax, const QParts& q,
+                        const void* dig, const int32_t* lens, int top_k, const int32_t* table,
+                        int32_t* gb, int32_t* ng, int32_t* cb, int32_t* nc, float* scores,
+                        int32_t* cbh, int32_t* nch, int32_t* gp, void* ws, hipStream_t st,
+                        hipEvent_t e0, hipEvent_t e1) {
+  // per position: score, table entry, block index (16 bits), flags
+  const size_t lds = (size_t)s.max_blocks * (sizeof(float) + sizeof(int32_t) + 2 + 1);
+  const size_t pairs = (size_t)s.B * s.Hkv, rows = pairs * s.max_blocks;
+  Handover xs{};
+  if (p.split > 0 && p.nchunk > 1) {
+    xs.score = static_cast<uint32_t*>(ws);
+    xs.page = xs.score + rows;
+    xs.blk = xs.page + rows;
+    xs.n = xs.blk + rows;
+    xs.count = xs.n + pairs * p.nchunk;
+  }
+  const dim3 grid(p.whole + p.split * p.nchunk), block(kSelThreads);
+  // hipExtLaunchKernelGGL records the (optional) events at the kernel's own start and end
   if (minmax)
-    hipLaunchKernelGGL((select_kernel<T, D, true>), grid, block, lds, st, q, (const T*)dig,
-                       lens, s.Hkv, s.G, s.bs, s.max_blocks, top_k, table, gb, ng, cb, nc,
-                       scores, cbh, nch, gp);
+    hipExtLaunchKernelGGL((select_kernel<T, D, true>), grid, block, lds, st, e0, e1, 0, q,
+                          (const T*)dig, lens, s.Hkv, s.G, s.bs, s.max_blocks, top_k, p.whole,
+                          p.split, p.chunk, p.nchunk, table, gb, ng, cb, nc, scores, cbh, nch,
+                          gp, xs);
   else
-    hipLaunchKernelGGL((select_kernel<T, D, false>), grid, block, lds, st, q, (const T*)dig,
-                       lens, s.Hkv, s.G, s.bs, s.max_blocks, top_k, table, gb, ng, cb, nc,
-                       scores, cbh, nch, gp);
+    hipExtLaunchKernelGGL((select_kernel<T, D, false>), grid, block, lds, st, e0, e1, 0, q,
+                          (const T*)dig, lens, s.Hkv, s.G, s.bs, s.max_blocks, top_k, p.whole,
+                          p.split, p.chunk, p.nchunk, table, gb, ng, cb, nc, scores, cbh, nch,
+                          gp, xs);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_select(const Shape& s, bool minmax, const QParts& q, const void* digests,
-                         const int32_t* seq_lens, int top_k, const int32_t* block_table,
-                         int32_t* gpu_blocks, int32_t* n_gpu, int32_t* cpu_blocks,
-                         int32_t* n_cpu, float* scores_or_null, int32_t* cpu_blocks_host,
-                         int32_t* n_cpu_host, int32_t* gpu_pages, hipStream_t stream) {
-#define SA_SEL_ARGS s, minmax, q, digests, seq_lens, top_k, block_table, gpu_blocks, n_gpu, \
-                    cpu_blocks, n_cpu, scores_or_null, cpu_blocks_host, n_cpu_host, gpu_pages, \
-                    stream
+SelectPlan select_plan(const Shape& s, bool) {
+  SelectPlan p;
+  const int pairs = s.B * s.Hkv;
+  // whole pairs: as many full rounds of one per CU as there are (a pair's rows must fit
+  // the table registers of one workgroup)
+  p.whole = s.max_blocks <= kMaxRows ? pairs / kCUs * kCUs : 0;
+  p.split = pairs - p.whole;
+  // the other pairs in pieces, about one piece per CU in all
+  const int pieces = p.split > 0 ? std::max(1, (kCUs + p.split - 1) / p.split) : 1;
+  int rows = (s.max_blocks + pieces - 1) / pieces;
+  rows = std::min(std::max(rows, kMinChunkRows), kMaxRows);
+  p.chunk = rows;
+  p.nchunk = p.split > 0 ? (s.max_blocks + rows - 1) / rows : 1;
+  // hand-over candidates (score, table entry, block) [pairs][max_blocks], their counts
+  // [pairs][nchunk], then the counters [pairs]
+  p.ws_bytes = p.split > 0 && p.nchunk > 1
+                   ? (size_t)pairs * (3 * (size_t)s.max_blocks + p.nchunk + 1) * sizeof(uint32_t)
+                   : 0;
+  return p;
+}
+
+hipError_t launch_select(const Shape& s, const SelectPlan& plan, bool minmax, const QParts& q,
+                         const void* digests, const int32_t* seq_lens, int top_k,
+                         const int32_t* block_table, int32_t* gpu_blocks, int32_t* n_gpu,
+                         int32_t* cpu_blocks, int32_t* n_cpu, float* scores_or_null,
+                         int32_t* cpu_blocks_host, int32_t* n_cpu_host, int32_t* gpu_pages,
+                         void* ws, hipStream_t stream, hipEvent_t ev_start,
+                         hipEvent_t ev_stop) {
+#define SA_SEL_ARGS s, plan, minmax, q, digests, seq_lens, top_k, block_table, gpu_blocks, \
+                    n_gpu, cpu_blocks, n_cpu, scores_or_null, cpu_blocks_host, n_cpu_host, \
+                    gpu_pages, ws, stream, ev_start, ev_stop
   if (s.bf16)
     return s.d == 128 ? select_typed<uint16_t, 128>(SA_SEL_ARGS)
                       : select_typed<uint16_t, 64>(SA_SEL_ARGS);

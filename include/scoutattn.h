@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 10
+#define SA_ABI_VERSION 11
 
 typedef enum {
   SA_OK = 0,
@@ -173,7 +173,11 @@ sa_status sa_predict_query(int32_t m, int32_t n, int32_t k, const void* x,
 
 /* ---------------------------------------------------------------------------------------
  * Workspace of sa_select_blocks + sa_sparse_decode (+ sa_decode_attend_merge) for a shape
- * and a top_k (a decode call uses list_stride == top_k).
+ * and a top_k (a decode call uses list_stride == top_k).  Its first part holds the
+ * selection's hand-over buffers and arrival counters: the caller fills the workspace with
+ * zeros once, before its first use (hipMemset, or a zero-filled allocation), and every call
+ * leaves the counters zero again.  Calls that share one workspace must not overlap in time
+ * (same stream, or ordered with events).
  * ------------------------------------------------------------------------------------- */
 size_t sa_workspace_bytes(const sa_dims* dims, int32_t top_k);
 
@@ -296,7 +300,8 @@ sa_status sa_host_partial_attention(const sa_dims* dims, int32_t host_pages,
  * side_stream NULL (or equal to `stream`) every step runs in order on `stream`.  All layers share dims, digest kind, hidden, top_k, scale and seq_lens.  `layers`
  * is a host array of num_layers descriptors (read during the call only).  Before returning,
  * `stream` waits for everything enqueued on side_stream, so a graph captured from `stream`
- * is closed.  ws: sa_step_workspace_bytes(dims, hidden, top_k).
+ * is closed.  ws: sa_step_workspace_bytes(dims, hidden, top_k), zero-filled before its first
+ * use (it holds the selection's arrival counters, which every step leaves zero again).
  * ------------------------------------------------------------------------------------- */
 typedef struct {
   const void* x;            /* X^i [B][hidden] bf16                                       */
@@ -479,14 +484,25 @@ sa_status sa_recall_blocks(const sa_dims* dims, int32_t list_stride, int32_t max
                            size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
- * sa_profile_attention -- kernel timing of the attention stage (GPUATTN).  After this call
- * the next n attention-kernel launches made by the calling thread (from sa_sparse_decode,
- * sa_decode_attend_merge or sa_decode_step) record start[i] when the i-th launch begins
- * executing and stop[i] when it ends, so hipEventElapsedTime(start[i], stop[i]) is that
- * kernel's duration.  Events are created by the caller and must stay valid until those
- * launches have completed; the handle arrays are copied.  Launches beyond n record
- * nothing; n = 0 turns the hook off.  Not for use while a stream is being captured.
+ * sa_profile_kernels -- kernel timing of one stage: the attention kernel (GPUATTN), the
+ * selection kernel (scoring + top-k + split) or the query GEMM kernel.  After this call the
+ * next n launches of that stage's kernel made by the calling thread (from any call that
+ * runs it, the decode step included) record start[i] when the i-th launch begins executing
+ * and stop[i] when it ends, so hipEventElapsedTime(start[i], stop[i]) is that kernel's
+ * duration (the GEMM's slice sum, a kernel of its own, is not included).  Events are
+ * created by the caller and must stay valid until those launches have completed; the handle
+ * arrays are copied.  Launches beyond n record nothing; n = 0 turns the hook off.  Not for
+ * use while a stream is being captured.  sa_profile_attention(...) is
+ * sa_profile_kernels(SA_PROFILE_ATTENTION, ...).
  * ------------------------------------------------------------------------------------- */
+typedef enum {
+  SA_PROFILE_ATTENTION = 0,
+  SA_PROFILE_SELECT = 1,
+  SA_PROFILE_GEMM = 2,
+  SA_PROFILE_STAGES = 3
+} sa_profile_stage;
+sa_status sa_profile_kernels(sa_profile_stage stage, const hipEvent_t* start,
+                             const hipEvent_t* stop, int32_t n);
 sa_status sa_profile_attention(const hipEvent_t* start, const hipEvent_t* stop, int32_t n);
 
 #ifdef __cplusplus

@@ -48,8 +48,27 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.sa_abi_version() == B.ABI_VERSION == 10
+    assert lib.sa_abi_version() == B.ABI_VERSION == 11
     assert lib.sa_status_string(B.SA_ERR_WORKSPACE) == b"SA_ERR_WORKSPACE"
+
+
+def test_workspace_holds_the_selection_handover(lib):
+    """With several chunk workgroups per pair, the workspace starts with the selection's
+    hand-over buffers: a score and a table entry per (pair, block), and a counter per pair."""
+    big = dims(batch=40, num_q_heads=40, num_kv_heads=8, max_blocks=2048, num_pages=40960)
+    pairs = 40 * 8
+    assert lib.sa_workspace_bytes(ctypes.byref(big), 64) >= pairs * (2 * 2048 + 1) * 4
+    # one chunk per pair (a tiny shape): no hand-over region beyond the attention partials
+    tiny = dims(batch=1, num_q_heads=4, num_kv_heads=1, max_blocks=8, num_pages=8)
+    assert lib.sa_workspace_bytes(ctypes.byref(tiny), 4) < 64 * 1024
+
+
+def test_profile_hook_validation(lib):
+    assert lib.sa_profile_kernels(7, None, None, 0) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_profile_kernels(1, None, None, -1) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_profile_kernels(2, None, None, 3) == B.SA_ERR_INVALID_ARG
+    for stage in range(3):
+        assert lib.sa_profile_kernels(stage, None, None, 0) == B.SA_OK
 
 
 # The calls below must all fail validation; on a machine with a GPU they are skipped so
