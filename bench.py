@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the single-layer workloads (the Qwen3-8B and Qwen3-14B layers "
+                         "and the ragged batch), each kernel timed after a cache flush")
     ap.add_argument("--offload", action="store_true",
                     help="after the GPU path, also time the step with its CPU side computed "
                          "by host tasks (sa_decode_step_offload), reported as \"offload\"")
@@ -259,17 +262,34 @@ def cpu_baseline(wl_full, budget_s):
             olayers_by_pair[(0, h)].append(dict(X=X64, W=W32, digest=digh, resident=resident,
                                                 K=Kl, V=Vl, seq_len=nb * bs, host=host))
     # time whole (sequence, layer) units: all KV heads of the sequence through one layer
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        for h in range(wl.num_kv_heads):
-            so.decode_step_pair(olayers_by_pair[(0, h)], 0, h, G, d, bs, wl.top_k, wl.scale)
-        done += wl.layers
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
+    def run(seconds):
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            for h in range(wl.num_kv_heads):
+                so.decode_step_pair(olayers_by_pair[(0, h)], 0, h, G, d, bs, wl.top_k, wl.scale)
+            done += wl.layers
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return done, el
+
+    done, el = run(budget_s)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        done1, el1 = run(budget_s / 2)
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": done / el, "unit": "seq-layers/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "os_cpu_count": os.cpu_count(),
+            "one_thread": {"value": done1 / el1, "unit": "seq-layers/s", "cores": 1,
+                           "sample": f"{done1} seq-layers in {el1:.1f} s"},
             "sample": f"{done} seq-layers: 1 sequence x {wl.layers} layers of the step "
                       f"(all {wl.num_kv_heads} KV heads, Algorithm 1 end to end in float64), "
                       f"repeated for {el:.1f} s; same shapes and recipe as the GPU workload"}
@@ -658,6 +678,163 @@ def timed_multi(torch, B, counts, fn):
     return {stage: [a.elapsed_time(b) for a, b in zip(*ev[stage])] for stage in ev}
 
 
+def attention_bytes_exact(wl, lens, gb, ng):
+    """GPUATTN bytes of one layer with ragged lengths: the valid K and V rows of every
+    resident selected block, q, and the (o, m, l) result."""
+    import numpy as np
+    bs, d = wl.block_size, wl.head_dim
+    el = 2 if wl.kv_dtype == "bf16" else 4
+    g, n = gb.cpu().numpy(), ng.cpu().numpy()
+    L = lens.cpu().numpy().astype(np.int64)
+    tokens = 0
+    for p in range(g.shape[0]):
+        blocks = g[p, :max(0, int(n[p]))].astype(np.int64)
+        tokens += int(np.minimum(bs, L[p // wl.num_kv_heads] - blocks * bs).sum())
+    Hq = wl.num_q_heads
+    return tokens * d * 2 * el + wl.batch * Hq * d * 4 + wl.batch * Hq * (d + 2) * 4
+
+
+def evict(flush):
+    """Read a 1 GiB buffer: it displaces the L2 caches and the 256 MB last-level cache with
+    clean lines (a write would leave dirty lines that the timed kernel then has to write
+    back while it reads)."""
+    return flush.amax()
+
+
+def layer_leg(wl, kind, torch, B, wk, flush, reps=20):
+    """One single-layer workload end to end on the GPU -- digests built from the full key
+    cache (a0), the query (a1: W_Q X, or drawn), the selection (a3 + a4), and the attention
+    (a5) over the resident selected blocks -- with residency chosen from the GPU's own
+    selection by the workload recipe.  Each kernel is timed per repetition from its own
+    start to its end, after a 1 GiB read that evicts the L2 caches and the 256 MB
+    last-level cache, so every byte comes from HBM."""
+    import numpy as np
+    dev = "cuda"
+    Bsz, Hq, Hkv, d, bs, k, mb = (wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                  wl.block_size, wl.top_k, wl.max_blocks)
+    pairs = Bsz * Hkv
+    el = 2 if wl.kv_dtype == "bf16" else 4
+    lens = wk.seq_lens(wl)
+    lens_d = lens.to(dev)
+    kv = wk.draw_kv_pages(wl, lens, dev)
+    P_full = kv["K"].shape[0]
+    SAK = B.SA_BF16 if wl.kv_dtype == "bf16" else B.SA_F32
+    dims_full = B.Dims(Bsz, Hq, Hkv, d, bs, mb, P_full, SAK)
+    k_full = B.pack_k_pages(dims_full, kv["K"])
+    per = 2 if kind == "minmax" else 1
+    dig = torch.zeros((Bsz, Hkv, mb, per, d), dtype=wl.torch_kv_dtype, device=dev)
+
+    def each(stage, fn, n=reps):
+        out = []
+        for _ in range(n):
+            evict(flush)
+            out += timed_multi(torch, B, {stage: 1}, fn)[stage]
+        return out
+
+    # a0: the digest build (one launch; timed with events around the call)
+    dig_ms = []
+    for _ in range(5):
+        evict(flush)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        B.sa_build_digests(dims_full, kind, k_full, kv["table"], lens_d, dig)
+        e1.record()
+        torch.cuda.synchronize()
+        dig_ms.append(e0.elapsed_time(e1))
+    ntok = int(lens.sum()) * Hkv
+    nblk = sum(wk.blocks_of(lens, bs)) * Hkv
+    dig_bytes = ntok * d * el + nblk * per * d * el
+    del k_full
+    out = {"workload": wl.name, "digest": kind}
+    st = spread(dig_ms)
+    out["digest_build"] = dict(time=st, bytes=dig_bytes, gbs=round(dig_bytes / (st["median_us"] * 1e-6) / 1e9, 1),
+                               frac=round(dig_bytes / (st["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))
+    # a1: the query
+    if wl.hidden:
+        qin = wk.draw_queries(wl, dev)
+        w_packed = B.pack_weight(qin["W"])
+        q = torch.empty((Bsz, Hq * d), dtype=torch.float32, device=dev)
+        gws = B.workspace(B.sa_predict_query_workspace_bytes(Bsz, Hq * d, wl.hidden))
+        B.sa_predict_query(qin["X"], w_packed, q, gws)
+        g_ms = each("gemm", lambda: B.sa_predict_query(qin["X"], w_packed, q, gws))
+        st = spread(g_ms)
+        gb_ = gemm_bytes(Bsz, Hq * d, wl.hidden)
+        flops = 2.0 * Bsz * Hq * d * wl.hidden
+        out["gemm"] = dict(time=st, bytes=gb_, gbs=round(gb_ / (st["median_us"] * 1e-6) / 1e9, 1),
+                           frac=round(gb_ / (st["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                           tflops=round(flops / (st["median_us"] * 1e-6) / 1e12, 1))
+        q = q.view(Bsz, Hq, d)
+    else:
+        q = wk.draw_queries(wl, dev)["Q"].contiguous()
+    # residency from the GPU's own selection over every block, by the workload recipe
+    gb = torch.empty((pairs, k), dtype=torch.int32, device=dev)
+    cb, ng, nc = torch.empty_like(gb), torch.empty(pairs, dtype=torch.int32, device=dev), \
+        torch.empty(pairs, dtype=torch.int32, device=dev)
+    ws = B.workspace(B.sa_workspace_bytes(dims_full, k))
+    B.sa_select_blocks(dims_full, kind, q, dig, lens_d, k, kv["table"], gb, ng, cb, nc, None, ws)
+    g, n = gb.cpu().numpy(), ng.cpu().numpy()
+    sel = [[np.sort(g[s * Hkv + h, :n[s * Hkv + h]]) for h in range(Hkv)] for s in range(Bsz)]
+    R = wk.choose_resident(wl, sel, lens)
+    pool = wk.build_pool(wl, R, kv["K"], kv["V"], kv["table"], k)
+    del kv
+    dims = B.Dims(Bsz, Hq, Hkv, d, bs, mb, pool["K"].shape[0], SAK)
+    kp, vp = B.pack_k_pages(dims, pool["K"]), B.pack_v_pages(dims, pool["V"])
+    bt = pool["block_table"]
+    del pool
+    ws = B.workspace(B.sa_workspace_bytes(dims, k))
+    run_sel = lambda: B.sa_select_blocks(dims, kind, q, dig, lens_d, k, bt, gb, ng, cb, nc,
+                                         None, ws)
+    run_sel()
+    s_ms = each("select", run_sel)
+    st = spread(s_ms)
+    sb = select_bytes(wl, kind, lens)
+    out["select"] = dict(time=st, bytes=sb, gbs=round(sb / (st["median_us"] * 1e-6) / 1e9, 1),
+                         frac=round(sb / (st["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))
+    torch.cuda.synchronize()
+    o = torch.empty((Bsz * Hq, d), dtype=torch.float32, device=dev)
+    hp = wk.draw_host_partials(wl, 0, dev)
+    run_att = lambda: B.sa_decode_attend_merge(dims, q, kp, vp, bt, lens_d, gb, ng, k, wl.scale,
+                                               hp["o"], hp["m"], hp["l"], nc, o, ws=ws)
+    run_att()
+    a_ms = each("attention", run_att)
+    st = spread(a_ms)
+    ab = attention_bytes_exact(wl, lens, gb, ng)
+    out["attention"] = dict(time=st, bytes=ab, gbs=round(ab / (st["median_us"] * 1e-6) / 1e9, 1),
+                            frac=round(ab / (st["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))
+    out["resident_selected_blocks"] = int(ng.sum())
+    out["offloaded_selected_blocks"] = int(nc.sum())
+    log(f"leg {wl.name}/{kind}: select {out['select']['time']['median_us']:.1f} us "
+        f"({out['select']['frac']:.2f}), attention {out['attention']['time']['median_us']:.1f} us "
+        f"({out['attention']['frac']:.2f})" +
+        (f", GEMM {out['gemm']['time']['median_us']:.1f} us" if "gemm" in out else ""))
+    del kp, vp, dig
+    torch.cuda.empty_cache()
+    return out
+
+
+def copy_ceiling(torch, n_bytes=1 << 30, reps=10):
+    """A plain device-to-device copy of 1 GiB (read once, written once), timed with events:
+    the bandwidth a streaming kernel can reach on this machine."""
+    a = torch.empty(n_bytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    st = spread(ms)
+    gbs = 2 * n_bytes / (st["median_us"] * 1e-6) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return {"bytes_moved": 2 * n_bytes, "time": st, "gbs": round(gbs, 1),
+            "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def select_alone(wl, dims, lens, layers, kind, torch, B, passes=2):
     """The selection kernel (scoring + top-k + split) launched by itself for every layer,
     each with the query the step selects it with (Q_pred^i = W_Q^i X^{i-1}; Q^0 for layer
@@ -888,6 +1065,8 @@ def main():
     }
     result["gemm"] = gemm_measure(wl, layers, torch, B)
     result["gemm"]["in_step_kernel"] = gemm_step
+    result["copy_ceiling"] = copy_ceiling(torch)
+    log(f"copy ceiling: {result['copy_ceiling']['gbs']:.0f} GB/s")
     if args.dense:
         result["dense"] = dense_measure(wl, args, torch, B, wk, iso_avg_ms * 1e3)
     store = host_store(wl, args, B, wk) if (args.recall or args.drift_steps) else None
@@ -920,6 +1099,19 @@ def main():
     if args.drift_steps:
         result["drift"] = drift_measure(wl, dims, lens, layers, ws, side_stream, store, args,
                                         torch, B)
+    if not args.no_legs:
+        # the single-layer workloads, after the step's buffers are released
+        del layers, ws, store
+        graph = run = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        result["layer_workloads"] = [
+            layer_leg(w, kd, torch, B, wk, flush)
+            for w, kd in ((wk.QWEN3_8B_LAYER, "mean"), (wk.QWEN3_14B_LAYER, "minmax"),
+                          (wk.RAGGED, "mean"), (wk.RAGGED, "minmax"))]
+        del flush
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
