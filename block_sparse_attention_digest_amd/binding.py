@@ -83,6 +83,8 @@ SIGNATURES = {
     "sa_merge": (ctypes.c_int, [_I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sa_decode_attend_merge": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _I, _F, _P, _P,
                                               _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "sa_decode_attend_merge_noalloc": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _I, _F,
+                                                      _P, _P, _P, _P, _P, _P, _P, _P]),
     "sa_step_workspace_bytes": (_Z, [_D, _I, _I]),
     "sa_decode_step": (ctypes.c_int, [_D, ctypes.c_int, _I, _I, _F, _P, _I,
                                       ctypes.POINTER(sa_layer), _P, _Z, _P, _P]),
@@ -385,6 +387,25 @@ def sa_decode_attend_merge(dims: Dims, q, k_pool, v_pool, block_table, seq_lens,
         _ptr(o, torch.float32, rows * dims.head_dim, "o"),
         _ptr(m, torch.float32, rows, "m"), _ptr(l, torch.float32, rows, "l"),
         _ptr(ws, torch.uint8, name="ws"), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def sa_decode_attend_merge_noalloc(dims: Dims, q, k_pool, v_pool, block_table, seq_lens,
+                                   gpu_blocks, n_gpu, list_stride: int, scale: float, host_o,
+                                   host_m, host_l, n_cpu, o, m=None, l=None, stream=None):
+    """sa_decode_attend_merge with its attention partials in the library's per-GPU scratch
+    instead of a caller workspace (no allocation anywhere in the call)."""
+    rows = dims.batch * dims.num_q_heads
+    _check(lib().sa_decode_attend_merge_noalloc(
+        ctypes.byref(dims.c()), _ptr(q, torch.float32, rows * dims.head_dim, "q"),
+        _ptr(k_pool, dims.kv_torch, name="k_pool"), _ptr(v_pool, dims.kv_torch, name="v_pool"),
+        _ptr(block_table, torch.int32, name="block_table"),
+        _ptr(seq_lens, torch.int32, dims.batch, "seq_lens"),
+        _ptr(gpu_blocks, torch.int32, name="gpu_blocks"), _ptr(n_gpu, torch.int32, name="n_gpu"),
+        list_stride, scale, _ptr(host_o, torch.float32, rows * dims.head_dim, "host_o"),
+        _ptr(host_m, torch.float32, rows, "host_m"), _ptr(host_l, torch.float32, rows, "host_l"),
+        _ptr(n_cpu, torch.int32, name="n_cpu"),
+        _ptr(o, torch.float32, rows * dims.head_dim, "o"),
+        _ptr(m, torch.float32, rows, "m"), _ptr(l, torch.float32, rows, "l"), _stream(stream)))
 
 
 def sa_merge(o_a, m_a, l_a, o_b, m_b, l_b, o, m, l, stream=None):

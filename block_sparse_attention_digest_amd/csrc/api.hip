@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <memory>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -179,6 +180,39 @@ sa_status run_select(const sa::Shape& s, bool minmax, const sa::QParts& q, const
   return SA_OK;
 }
 
+}  // namespace
+
+// The attention partials of sa_decode_attend_merge_noalloc live here, not in a caller
+// workspace: kScratchBytes per GPU, which every GPU the library runs on holds (zero-filled
+// when the code object loads) until the process ends.  In host code `scratch` is only a
+// stand-in for the symbol, never a device address: the address each GPU's copy has is
+// looked up once per device (scratch_address) and only that is passed to kernels.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current GPU's scratch (looked up on this device's first call).
+sa_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(SA_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SA_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -358,13 +392,16 @@ sa_status sa_select_blocks(const sa_dims* dims, sa_digest_kind kind, const float
   return ok();
 }
 
+// The attention stage with its merge: every argument is checked on the host, then the
+// partials go to `ws` (a caller workspace laid out as Layout says), or, with noalloc, to the
+// current GPU's scratch, which must hold them.
 static sa_status decode_common(const sa_dims* dims, const float* q, const void* k_pool,
                                const void* v_pool, const int32_t* block_table,
                                const int32_t* seq_lens, const int32_t* gpu_blocks,
                                const int32_t* n_gpu, int32_t list_stride, float scale,
                                const float* host_o, const float* host_m, const float* host_l,
                                const int32_t* n_cpu, float* o, float* m, float* l, void* ws,
-                               size_t ws_bytes, hipStream_t stream) {
+                               size_t ws_bytes, hipStream_t stream, bool noalloc = false) {
   sa::Shape s;
   SA_CHECK(check_dims(dims, &s));
   SA_NOT_NULL(q);
@@ -380,9 +417,21 @@ static sa_status decode_common(const sa_dims* dims, const float* q, const void* 
     return fail(SA_ERR_INVALID_ARG, "list_stride %d outside [1, max_blocks = %d]", list_stride,
                 s.max_blocks);
   const Layout L = layout(s, list_stride);
-  if (!ws || ws_bytes < L.total)
-    return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, L.total);
-  float* parts = (float*)((char*)ws + L.parts);
+  float* parts = nullptr;
+  if (noalloc) {
+    if (L.plan.ws_bytes > kScratchBytes)
+      return fail(SA_ERR_WORKSPACE,
+                  "the attention partials of this shape need %zu bytes, more than the %zu "
+                  "bytes of scratch the library holds per GPU (use sa_decode_attend_merge)",
+                  L.plan.ws_bytes, kScratchBytes);
+    void* ptr = nullptr;
+    SA_CHECK(scratch_address(&ptr));
+    parts = static_cast<float*>(ptr);
+  } else {
+    if (!ws || ws_bytes < L.total)
+      return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, L.total);
+    parts = (float*)((char*)ws + L.parts);
+  }
   hipEvent_t e0, e1;
   next_profile_events(&e0, &e1);
   SA_HIP(sa::launch_attention(s, L.plan, sa::plain_query(q, s.Hq * s.d), k_pool, v_pool,
@@ -419,6 +468,22 @@ sa_status sa_decode_attend_merge(const sa_dims* dims, const float* q, const void
   return decode_common(dims, q, k_pool, v_pool, block_table, seq_lens, gpu_blocks, n_gpu,
                        list_stride, scale, host_o, host_m, host_l, n_cpu, o, m, l, ws,
                        ws_bytes, stream);
+}
+
+sa_status sa_decode_attend_merge_noalloc(const sa_dims* dims, const float* q,
+                                         const void* k_pool, const void* v_pool,
+                                         const int32_t* block_table, const int32_t* seq_lens,
+                                         const int32_t* gpu_blocks, const int32_t* n_gpu,
+                                         int32_t list_stride, float scale, const float* host_o,
+                                         const float* host_m, const float* host_l,
+                                         const int32_t* n_cpu, float* o, float* m, float* l,
+                                         hipStream_t stream) {
+  SA_NOT_NULL(host_o);
+  SA_NOT_NULL(host_m);
+  SA_NOT_NULL(host_l);
+  return decode_common(dims, q, k_pool, v_pool, block_table, seq_lens, gpu_blocks, n_gpu,
+                       list_stride, scale, host_o, host_m, host_l, n_cpu, o, m, l, nullptr, 0,
+                       stream, true);
 }
 
 sa_status sa_merge(int32_t rows, int32_t d, const float* o_a, const float* m_a,

@@ -484,6 +484,25 @@ sa_status sa_recall_blocks(const sa_dims* dims, int32_t list_stride, int32_t max
                            size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * sa_decode_attend_merge_noalloc -- sa_decode_attend_merge for callers that cannot allocate
+ * (code under stream capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments without the workspace, the same kernels and results.  The attention
+ * partials go to a 16 MiB scratch array the library holds on every GPU it runs on, until
+ * the process ends; the call itself allocates nothing.  A shape whose partials need more
+ * (about (2048 + B*Hkv) * G * (d + 2) * 4 bytes) is refused with SA_ERR_WORKSPACE before
+ * anything is launched.  All calls on one GPU share its scratch: calls that overlap in time
+ * on one GPU (different streams, not ordered by events) race and give wrong results.
+ * ------------------------------------------------------------------------------------- */
+sa_status sa_decode_attend_merge_noalloc(const sa_dims* dims, const float* q,
+                                         const void* k_pool, const void* v_pool,
+                                         const int32_t* block_table, const int32_t* seq_lens,
+                                         const int32_t* gpu_blocks, const int32_t* n_gpu,
+                                         int32_t list_stride, float scale, const float* host_o,
+                                         const float* host_m, const float* host_l,
+                                         const int32_t* n_cpu, float* o, float* m, float* l,
+                                         hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * sa_profile_kernels -- kernel timing of one stage: the attention kernel (GPUATTN), the
  * selection kernel (scoring + top-k + split) or the query GEMM kernel.  After this call the
  * next n launches of that stage's kernel made by the calling thread (from any call that

@@ -90,6 +90,21 @@ def select(lib, d, top_k=8, ws_bytes=1 << 30, q=FAKE, kind=0):
 
 
 @no_gpu
+def test_noalloc_refuses_partials_beyond_scratch(lib):
+    """8192 pairs of 8 query heads need about 42 MB of attention partials, more than the
+    16 MiB of per-GPU scratch of sa_decode_attend_merge_noalloc: refused on the host."""
+    d = dims(batch=1024, num_q_heads=64, num_kv_heads=8, max_blocks=64, num_pages=1024)
+    st = lib.sa_decode_attend_merge_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, 8, 0.1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            None, None, None)
+    assert st == B.SA_ERR_WORKSPACE
+    assert b"scratch" in lib.sa_last_error()
+    assert lib.sa_decode_attend_merge_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                              FAKE, FAKE, 8, 0.1, None, FAKE, FAKE, FAKE,
+                                              FAKE, None, None, None) == B.SA_ERR_INVALID_ARG
+
+
+@no_gpu
 def test_dims_validation(lib):
     assert select(lib, dims(head_dim=96)) == B.SA_ERR_UNSUPPORTED
     assert b"head_dim" in lib.sa_last_error()
