@@ -55,8 +55,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager steps instead of replays of the step captured as a graph")
     ap.add_argument("--profile-steps", type=int, default=3,
-                    help="eager steps after the timed region whose attention launches are "
-                         "timed with kernel-precise HIP events")
+                    help="eager steps (at least 1) after the timed region whose attention, "
+                         "selection and GEMM launches are timed with kernel-precise HIP "
+                         "events")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -85,14 +86,17 @@ def parse():
                          "\"drift\"")
     ap.add_argument("--drift-rho", type=float, default=0.97)
     ap.add_argument("--beta", type=float, default=0.12)
-    ap.add_argument("--block-size", type=int, default=None, choices=(16, 32),
+    ap.add_argument("--block-size", type=int, default=None, choices=(16, 32, 64),
                     help="KV block size instead of the workload's 32, with the token budget "
                          "and the resident pool kept in tokens (a study of the digest "
                          "granularity; not the headline workload)")
     ap.add_argument("--pool-blocks", type=int, default=None,
                     help="resident pool blocks per (sequence, KV head) instead of the "
                          "workload's 128 (a study of the CPU share; not the headline workload)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.profile_steps < 1:
+        ap.error("--profile-steps must be at least 1 (the roofline figures come from them)")
+    return args
 
 
 def source_hash(path):
@@ -895,9 +899,9 @@ def main():
     if args.pool_blocks is not None:
         wl = wl.scaled(pool_blocks=args.pool_blocks)
     if args.block_size is not None and args.block_size != wl.block_size:
-        f = wl.block_size // args.block_size  # budget and pool kept in tokens
-        wl = wl.scaled(block_size=args.block_size, top_k=wl.top_k * f,
-                       pool_blocks=wl.pool_blocks * f)
+        bs0, bs1 = wl.block_size, args.block_size  # budget and pool kept in tokens
+        wl = wl.scaled(block_size=bs1, top_k=wl.top_k * bs0 // bs1,
+                       pool_blocks=wl.pool_blocks * bs0 // bs1)
     log(f"workload {wl.name}: setup")
     dims, lens, layers, ws = setup(wl, torch, B, wk)
     side_stream = torch.cuda.Stream()

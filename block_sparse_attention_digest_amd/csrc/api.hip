@@ -89,8 +89,8 @@ sa_status check_dims(const sa_dims* d, sa::Shape* s) {
   if (G > 8) return fail(SA_ERR_UNSUPPORTED, "query heads per KV head %d > 8", G);
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(SA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", d->head_dim);
-  if (d->block_size != 16 && d->block_size != 32)
-    return fail(SA_ERR_UNSUPPORTED, "block_size %d not in {16, 32}", d->block_size);
+  if (d->block_size != 16 && d->block_size != 32 && d->block_size != 64)
+    return fail(SA_ERR_UNSUPPORTED, "block_size %d not in {16, 32, 64}", d->block_size);
   if (d->max_blocks > kMaxBlocks)
     return fail(SA_ERR_UNSUPPORTED, "max_blocks %d > %d", d->max_blocks, kMaxBlocks);
   if ((long)d->batch * d->num_kv_heads > kMaxPairs)

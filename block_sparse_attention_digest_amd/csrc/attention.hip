@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     float* __restrict__ ws) {
   constexpr int KS = D / 32;          // MFMA k-steps over the head dimension (S = K Q^T)
   constexpr int CG = D / 16;          // 16-channel groups of the output (O^T += V^T P)
-  constexpr int HPB = BS / kStep;     // 16-token steps per block (1 or 2)
+  constexpr int HPB = BS / kStep;     // 16-token steps per block (1, 2 or 4)
 
   extern __shared__ int pfx[];        // [npairs + 1]
   __shared__ float q_lds[kQStage * G * D];
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
         open = true;
       }
     };
-    // HPB steps per block; a second half holding no valid token is fully masked.  Three
+    // HPB steps per block; a step past the block's valid tokens is fully masked.  Three
     // steps per iteration, the two after the one being computed in flight (so a wave keeps
     // the memory busy on its own once its SIMD neighbour has finished); the scheduling
     // barriers keep the compiler from sinking the loads to their use.
@@ -893,12 +893,13 @@ hipError_t launch_attention(const Shape& s, const AttnPlan& plan, const QParts& 
   const float sl2 = scale * kLog2e;
 #define SA_ARGS plan, q, k_pool, v_pool, block_table, seq_lens, gpu_blocks, gpu_pages, n_gpu, \
                 list_stride, sl2, partials, stream, ev_start, ev_stop
-  if (s.bf16) {
-    if (s.d == 128) return s.bs == 32 ? attn_bf16_g<128, 32>(s, SA_ARGS) : attn_bf16_g<128, 16>(s, SA_ARGS);
-    return s.bs == 32 ? attn_bf16_g<64, 32>(s, SA_ARGS) : attn_bf16_g<64, 16>(s, SA_ARGS);
-  }
-  if (s.d == 128) return s.bs == 32 ? attn_f32<128, 32>(s, SA_ARGS) : attn_f32<128, 16>(s, SA_ARGS);
-  return s.bs == 32 ? attn_f32<64, 32>(s, SA_ARGS) : attn_f32<64, 16>(s, SA_ARGS);
+#define SA_BY_BS(FN, D)                                   \
+  (s.bs == 64   ? FN<D, 64>(s, SA_ARGS)                    \
+   : s.bs == 32 ? FN<D, 32>(s, SA_ARGS)                    \
+                : FN<D, 16>(s, SA_ARGS))
+  if (s.bf16) return s.d == 128 ? SA_BY_BS(attn_bf16_g, 128) : SA_BY_BS(attn_bf16_g, 64);
+  return s.d == 128 ? SA_BY_BS(attn_f32, 128) : SA_BY_BS(attn_f32, 64);
+#undef SA_BY_BS
 #undef SA_ARGS
 }
 

@@ -74,17 +74,34 @@ __device__ __forceinline__ void store_mean1(uint16_t* dst, double v) {
 }
 __device__ __forceinline__ void store_mean1(float* dst, double v) { *dst = (float)v; }
 
-// One block's digest from its page, already in registers (raw), written to slot gidx.
+// Page geometry of one instantiation.  A lane holds CGS x TG loads of 16 bytes at a time:
+// the whole page when that is at most 8 loads, else the page in SL channel slabs of CGS
+// chunk groups each (channels are digested independently, so a slab is a unit of its own;
+// two slabs in flight per wave keep the registers within reach of two waves per SIMD).
+template <typename T, int D, int BS>
+struct PageGeom {
+  static constexpr int VEC = Vec<T>::N;  // elements per 16-byte chunk
+  static constexpr int NC = D / VEC;     // chunks per token
+  static constexpr int CG = NC / 8;      // chunk groups: 8 chunks per load instruction
+  static constexpr int TG = BS / 8;      // token groups: 8 tokens (one 128-byte line) per chunk
+  static constexpr int SL = CG * TG > 8 ? CG * TG / 8 : 1;    // channel slabs per page
+  static constexpr int CGS = CG / SL;                          // chunk groups per slab
+  static_assert(NC % 8 == 0 && BS % 8 == 0 && CG % SL == 0, "page shape");
+};
+
+// The digest of slab `slab` of one block, from its loads already in registers (raw),
+// written to slot gidx.
 template <typename T, int D, int BS, bool MINMAX>
-__device__ __forceinline__ void digest_block(const uint4 (&raw)[D / Vec<T>::N / 8][BS / 8],
-                                             int nvalid, T* __restrict__ dig, long gidx,
-                                             int cl, int tl) {
-  constexpr int VEC = Vec<T>::N;
-  constexpr int CG = D / VEC / 8, TG = BS / 8;
+__device__ __forceinline__ void digest_block(
+    const uint4 (&raw)[PageGeom<T, D, BS>::CGS][BS / 8], int nvalid, T* __restrict__ dig,
+    long gidx, int cl, int tl, int slab) {
+  using PG = PageGeom<T, D, BS>;
+  constexpr int VEC = PG::VEC, CGS = PG::CGS, TG = PG::TG;
   const int e = tl * VEC / 8;                          // this lane's element of its chunk
   const bool writer = (tl * VEC) % 8 == 0;             // one lane per element
 #pragma unroll
-  for (int cg = 0; cg < CG; ++cg) {
+  for (int cs = 0; cs < CGS; ++cs) {
+    const int cg = CGS * slab + cs;
     const int ch = (8 * cg + cl) * VEC + e;            // this lane's channel
     if constexpr (MINMAX) {
       float mn[VEC], mx[VEC];
@@ -94,7 +111,7 @@ __device__ __forceinline__ void digest_block(const uint4 (&raw)[D / Vec<T>::N / 
       for (int tg = 0; tg < TG; ++tg) {  // tokens past the valid ones are left out
         const bool ok = 8 * tg + tl < nvalid;
         float f[VEC];
-        Vec<T>::widen(raw[cg][tg], f);
+        Vec<T>::widen(raw[cs][tg], f);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
           mn[i] = fminf(mn[i], ok ? f[i] : INFINITY);
@@ -116,7 +133,7 @@ __device__ __forceinline__ void digest_block(const uint4 (&raw)[D / Vec<T>::N / 
 #pragma unroll
         for (int tg = 0; tg < TG; ++tg) {
           float f[VEC];
-          Vec<T>::widen(raw[cg][tg], f);
+          Vec<T>::widen(raw[cs][tg], f);
 #pragma unroll
           for (int i = 0; i < VEC; ++i) acc[i] += (double)f[i];
         }
@@ -125,7 +142,7 @@ __device__ __forceinline__ void digest_block(const uint4 (&raw)[D / Vec<T>::N / 
         for (int tg = 0; tg < TG; ++tg) {  // tokens past the valid ones add 0
           const bool ok = 8 * tg + tl < nvalid;
           float f[VEC];
-          Vec<T>::widen(raw[cg][tg], f);
+          Vec<T>::widen(raw[cs][tg], f);
 #pragma unroll
           for (int i = 0; i < VEC; ++i) acc[i] += (double)(ok ? f[i] : 0.f);
         }
@@ -149,26 +166,23 @@ __global__ __launch_bounds__(256) void digest_kernel(const T* __restrict__ k_poo
                                                      T* __restrict__ dig, int Hkv,
                                                      int max_blocks, int P, long total,
                                                      long per) {
-  constexpr int VEC = Vec<T>::N;  // elements per 16-byte chunk
-  constexpr int NC = D / VEC;     // chunks per token
-  constexpr int CG = NC / 8;      // chunk groups: 8 chunks per load instruction
-  constexpr int TG = BS / 8;      // token groups: 8 tokens (one 128-byte line) per chunk
-  static_assert(NC % 8 == 0 && BS % 8 == 0, "page shape");
+  using PG = PageGeom<T, D, BS>;
+  constexpr int VEC = PG::VEC, CGS = PG::CGS, TG = PG::TG, SL = PG::SL;
   const int lane = threadIdx.x % kWave;
   const long gw = (long)blockIdx.x * (blockDim.x / kWave) +
                   __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const long i0 = gw * per, i1 = min(total, i0 + per);
   const int cl = lane / 8, tl = lane % 8;  // chunk within the group, token within the group
 
-  // the whole page in flight at once (CG * TG <= 16 loads of 16 bytes per lane)
-  auto load_page = [&](int page, uint4 (&raw)[CG][TG]) {
+  // one slab of a page at once (CGS * TG <= 8 loads of 16 bytes per lane)
+  auto load_slab = [&](int page, int slab, uint4 (&raw)[CGS][TG]) {
     const T* src = k_pool + (size_t)page * BS * D;
 #pragma unroll
-    for (int cg = 0; cg < CG; ++cg)
+    for (int cs = 0; cs < CGS; ++cs)
 #pragma unroll
       for (int tg = 0; tg < TG; ++tg)
-        raw[cg][tg] = *reinterpret_cast<const uint4*>(
-            src + ((size_t)(8 * cg + cl) * BS + 8 * tg + tl) * VEC);
+        raw[cs][tg] = *reinterpret_cast<const uint4*>(
+            src + ((size_t)(8 * (CGS * slab + cs) + cl) * BS + 8 * tg + tl) * VEC);
   };
 
   for (long w0 = i0; w0 < i1; w0 += kWave) {
@@ -180,25 +194,32 @@ __global__ __launch_bounds__(256) void digest_kernel(const T* __restrict__ k_poo
     const int nval_l = min(BS, len - b * BS);
     uint64_t mask = __ballot(live);
     if (mask == 0) continue;
-    // resident blocks of the window in order; the next one's page is loaded before the
-    // current one is reduced (past the last, the last is loaded again: cached lines)
+    // the slabs of the window's resident blocks in order; the next slab is loaded before
+    // the current one is reduced (past the last, the last is loaded again: cached lines)
     int j = __builtin_ctzll(mask);
     mask &= mask - 1;
-    uint4 cur[CG][TG], nxt[CG][TG];
-    load_page(__builtin_amdgcn_readlane(page_l, j), cur);
+    int sl = 0;
+    uint4 cur[CGS][TG], nxt[CGS][TG];
+    load_slab(__builtin_amdgcn_readlane(page_l, j), 0, cur);
     while (true) {
-      const int jn = mask ? __builtin_ctzll(mask) : j;
-      load_page(__builtin_amdgcn_readlane(page_l, jn), nxt);
+      int jn = j, sn = sl + 1;
+      const bool last = sn == SL && !mask;
+      if (sn == SL) {
+        sn = last ? sl : 0;
+        jn = last ? j : __builtin_ctzll(mask);
+      }
+      load_slab(__builtin_amdgcn_readlane(page_l, jn), sn, nxt);
       __builtin_amdgcn_sched_barrier(0);
       digest_block<T, D, BS, MINMAX>(cur, __builtin_amdgcn_readlane(nval_l, j), dig, w0 + j,
-                                     cl, tl);
-      if (!mask) break;
-      mask &= mask - 1;
+                                     cl, tl, sl);
+      if (last) break;
+      if (sn == 0) mask &= mask - 1;  // block jn begins
       j = jn;
+      sl = sn;
 #pragma unroll
-      for (int cg = 0; cg < CG; ++cg)
+      for (int cs = 0; cs < CGS; ++cs)
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg) cur[cg][tg] = nxt[cg][tg];
+        for (int tg = 0; tg < TG; ++tg) cur[cs][tg] = nxt[cs][tg];
     }
   }
 }
@@ -213,8 +234,8 @@ __global__ __launch_bounds__(256) void refresh_kernel(const T* __restrict__ k_po
                                                       const int32_t* __restrict__ seq_lens,
                                                       T* __restrict__ dig, int Hkv, int npairs,
                                                       int max_blocks, int P) {
-  constexpr int VEC = Vec<T>::N;
-  constexpr int CG = D / VEC / 8, TG = BS / 8;
+  using PG = PageGeom<T, D, BS>;
+  constexpr int VEC = PG::VEC, CGS = PG::CGS, TG = PG::TG;
   const int lane = threadIdx.x % kWave;
   const int pair = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (pair >= npairs) return;
@@ -224,16 +245,19 @@ __global__ __launch_bounds__(256) void refresh_kernel(const T* __restrict__ k_po
   const int page = table[(size_t)pair * max_blocks + b];
   if (page < 0 || page >= P) return;
   const int cl = lane / 8, tl = lane % 8;
-  uint4 raw[CG][TG];
   const T* src = k_pool + (size_t)page * BS * D;
 #pragma unroll
-  for (int cg = 0; cg < CG; ++cg)
+  for (int sl = 0; sl < PG::SL; ++sl) {
+    uint4 raw[CGS][TG];
 #pragma unroll
-    for (int tg = 0; tg < TG; ++tg)
-      raw[cg][tg] = *reinterpret_cast<const uint4*>(
-          src + ((size_t)(8 * cg + cl) * BS + 8 * tg + tl) * VEC);
-  digest_block<T, D, BS, MINMAX>(raw, min(BS, len - b * BS), dig,
-                                 (long)pair * max_blocks + b, cl, tl);
+    for (int cs = 0; cs < CGS; ++cs)
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg)
+        raw[cs][tg] = *reinterpret_cast<const uint4*>(
+            src + ((size_t)(8 * (CGS * sl + cs) + cl) * BS + 8 * tg + tl) * VEC);
+    digest_block<T, D, BS, MINMAX>(raw, min(BS, len - b * BS), dig,
+                                   (long)pair * max_blocks + b, cl, tl, sl);
+  }
 }
 
 // Waves the device holds at once for this instantiation (all CUs at full occupancy), found
@@ -279,11 +303,11 @@ hipError_t launch_typed(const Shape& s, bool minmax, const void* k_pool, const i
 template <typename T>
 hipError_t launch_dtype(const Shape& s, bool minmax, const void* k, const int32_t* t,
                         const int32_t* l, void* dig, hipStream_t st) {
-  if (s.d == 128)
-    return s.bs == 32 ? launch_typed<T, 128, 32>(s, minmax, k, t, l, dig, st)
-                      : launch_typed<T, 128, 16>(s, minmax, k, t, l, dig, st);
-  return s.bs == 32 ? launch_typed<T, 64, 32>(s, minmax, k, t, l, dig, st)
-                    : launch_typed<T, 64, 16>(s, minmax, k, t, l, dig, st);
+#define SA_BY_BS(FN, D)                                                  \
+  (s.bs == 64   ? FN<T, D, 64>(s, minmax, k, t, l, dig, st)               \
+   : s.bs == 32 ? FN<T, D, 32>(s, minmax, k, t, l, dig, st)               \
+                : FN<T, D, 16>(s, minmax, k, t, l, dig, st))
+  return s.d == 128 ? SA_BY_BS(launch_typed, 128) : SA_BY_BS(launch_typed, 64);
 }
 
 template <typename T, int D, int BS>
@@ -303,11 +327,8 @@ hipError_t refresh_typed(const Shape& s, bool minmax, const void* k, const int32
 template <typename T>
 hipError_t refresh_dtype(const Shape& s, bool minmax, const void* k, const int32_t* t,
                          const int32_t* l, void* dig, hipStream_t st) {
-  if (s.d == 128)
-    return s.bs == 32 ? refresh_typed<T, 128, 32>(s, minmax, k, t, l, dig, st)
-                      : refresh_typed<T, 128, 16>(s, minmax, k, t, l, dig, st);
-  return s.bs == 32 ? refresh_typed<T, 64, 32>(s, minmax, k, t, l, dig, st)
-                    : refresh_typed<T, 64, 16>(s, minmax, k, t, l, dig, st);
+  return s.d == 128 ? SA_BY_BS(refresh_typed, 128) : SA_BY_BS(refresh_typed, 64);
+#undef SA_BY_BS
 }
 
 }  // namespace

@@ -77,6 +77,25 @@ LAYER_CASES = [
     ("bf16-poisoned-tails-host-worker",
      wk.RAGGED.scaled(batch=3, ctx_min=100, ctx_max=700, top_k=44), "mean",
      dict(poison_tails=True, resident_override="none", host_worker=True)),
+    # blocks of 64 tokens: four 16-token attention steps per block, digests of a page taken
+    # in channel slabs, every dtype and head dimension, ragged tails
+    ("bf16-d128-bs64", wk.QWEN3_8B_LAYER.scaled(batch=2, context=3000 + 7, block_size=64,
+                                                top_k=32), "mean", {}),
+    ("bf16-d128-bs64-minmax-ragged", wk.RAGGED.scaled(batch=4, ctx_min=1, ctx_max=3000,
+                                                      block_size=64, top_k=16), "minmax", {}),
+    ("bf16-d64-bs64-host-worker", wk.RAGGED.scaled(batch=3, num_q_heads=6, num_kv_heads=2,
+                                                   head_dim=64, ctx_min=100, ctx_max=2500,
+                                                   block_size=64, top_k=12), "mean",
+     dict(host_worker=True)),
+    ("f32-d128-bs64", wk.TINY.scaled(num_q_heads=10, num_kv_heads=2, head_dim=128,
+                                     block_size=64, context=1000, top_k=6), "mean", {}),
+    ("f32-d64-bs64-minmax", wk.TINY.scaled(block_size=64, context=1000 + 33, top_k=5,
+                                           n_lowest=2), "minmax", {}),
+    ("bf16-poisoned-tails-bs64", wk.RAGGED.scaled(batch=3, ctx_min=100, ctx_max=700,
+                                                  block_size=64, top_k=11),
+     "minmax", dict(poison_tails=True, resident_override="all")),
+    ("f32-poisoned-tails-bs64", TINY.scaled(context=1000, block_size=64), "mean",
+     dict(poison_tails=True, resident_override="all", top_k=16)),
 ]
 
 
@@ -87,7 +106,7 @@ def test_layer_parity(name, wl, kind, kw):
 
 
 @pytest.mark.parametrize("kv,d,bs", [("bf16", 128, 32), ("bf16", 64, 16), ("f32", 128, 16),
-                                     ("f32", 64, 32)])
+                                     ("f32", 64, 32), ("bf16", 128, 64), ("f32", 64, 64)])
 def test_pack_v_pages_layout(kv, d, bs):
     """The V page layout, bit for bit: [P][bs][d] viewed as [P][bs/16][16][d] with the two
     inner axes swapped."""
@@ -104,7 +123,7 @@ def test_pack_v_pages_layout(kv, d, bs):
 
 
 @pytest.mark.parametrize("kv,d,bs", [("bf16", 128, 32), ("bf16", 64, 16), ("f32", 128, 16),
-                                     ("f32", 64, 32)])
+                                     ("f32", 64, 32), ("bf16", 128, 64), ("f32", 64, 64)])
 def test_pack_k_pages_layout(kv, d, bs):
     """The chunk-major K layout, bit for bit: [P][bs][d] viewed as [P][bs][d/x][x] with the
     two middle axes swapped (x = 16 bytes of elements)."""
@@ -149,7 +168,9 @@ def test_predict_query_parity(m, n, k):
 
 
 @pytest.mark.parametrize("kind,kv,d,bs", [("mean", "bf16", 128, 32), ("minmax", "bf16", 64, 16),
-                                          ("mean", "f32", 64, 16), ("minmax", "f32", 128, 32)])
+                                          ("mean", "f32", 64, 16), ("minmax", "f32", 128, 32),
+                                          ("mean", "bf16", 128, 64), ("minmax", "bf16", 64, 64),
+                                          ("mean", "f32", 128, 64), ("minmax", "f32", 128, 64)])
 def test_refresh_last_digests(kind, kv, d, bs):
     """Decode-time digest maintenance: after one more token per sequence, refreshing the
     last blocks gives exactly what a full rebuild gives (and what the oracle gives), for a
@@ -297,15 +318,17 @@ def test_step_offload_parity_one_stream_one_thread():
     assert r["cpu_ratio"] > 0.1
 
 
-@pytest.mark.parametrize("pool,max_recall,ragged", [(6, 64, False), (12, 2, False),
-                                                     (12, 64, False), (6, 64, True)])
-def test_recall_parity(pool, max_recall, ragged):
+@pytest.mark.parametrize("pool,max_recall,ragged,bs", [(6, 64, False, 32), (12, 2, False, 32),
+                                                        (12, 64, False, 32), (6, 64, True, 32),
+                                                        (4, 64, True, 64)])
+def test_recall_parity(pool, max_recall, ragged, bs):
     """Periodic recall of every layer after a step: tables, moved pages and untouched pages
     against the oracle bit for bit, then the next step over the new residency."""
-    H.log(f"[case] recall pool={pool} max_recall={max_recall} ragged={ragged}")
+    H.log(f"[case] recall pool={pool} max_recall={max_recall} ragged={ragged} bs={bs}")
     import harness_recall as HR
     wl = wk.QWEN3_14B_STEP.scaled(batch=3, num_q_heads=10, num_kv_heads=2, context=2000,
-                                  layers=2, pool_blocks=pool, hidden=512, top_k=8)
+                                  layers=2, pool_blocks=pool, hidden=512, top_k=8 * 32 // bs,
+                                  block_size=bs)
     if ragged:
         wl = wl.scaled(batch=4, context=0, ctx_min=1, ctx_max=2000)
     r = HR.run_recall(wl, max_recall)
@@ -340,6 +363,16 @@ def test_step_recall_overlap_matches_join():
     assert moved > 0
 
 
+def test_step_offload_parity_bs64():
+    """The offload step on blocks of 64 tokens, ragged, with the host worker."""
+    H.log("[case] step offload bs64")
+    import harness_step as HS
+    HS.run_step(wk.QWEN3_14B_STEP.scaled(batch=3, num_q_heads=10, num_kv_heads=2, context=0,
+                                         ctx_min=1, ctx_max=3000, layers=3, pool_blocks=6,
+                                         hidden=512, top_k=5, block_size=64),
+                gen_device="cpu", side=False, offload=True)
+
+
 def test_step_parity_minmax_no_handoff():
     H.log("[case] step minmax")
     import harness_step as HS
@@ -355,6 +388,9 @@ def test_step_parity_minmax_no_handoff():
     ("bf16-ragged-bs32", wk.RAGGED.scaled(batch=4, ctx_min=40, ctx_max=3000, block_size=32,
                                           top_k=64), 0.0),
     ("bf16-some-blocks-without-page", wk.RAGGED.scaled(batch=5, ctx_min=1, ctx_max=1500), 0.3),
+    ("bf16-ragged-bs64", wk.RAGGED.scaled(batch=4, ctx_min=1, ctx_max=3000, block_size=64,
+                                          top_k=32), 0.1),
+    ("f32-bs64", wk.TINY.scaled(block_size=64, context=1000 + 9), 0.0),
 ])
 def test_dense_parity(name, wl, drop):
     """FullKV (sa_dense_decode) against the oracle's dense attention over the whole context;

@@ -217,7 +217,7 @@ def random_case(rng):
     Hkv = rng.choice([1, 2, 8])
     G = rng.choice([1, 3, 5, 8])
     D = rng.choice([64, 128])
-    BS = rng.choice([16, 32])
+    BS = rng.choice([16, 32, 64])
     B = rng.randint(1, 6)
     mb = rng.randint(1, 40)
     stride = rng.randint(1, 20)
