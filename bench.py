@@ -47,6 +47,15 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# The single-layer workloads timed after the step (name -> workload, digest kind).
+LEGS = {
+    "qwen3-8b-layer-mean": ("QWEN3_8B_LAYER", "mean"),
+    "qwen3-14b-layer-minmax": ("QWEN3_14B_LAYER", "minmax"),
+    "ragged-mean": ("RAGGED", "mean"),
+    "ragged-minmax": ("RAGGED", "minmax"),
+}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -61,6 +70,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--leg", choices=sorted(LEGS), default=None,
+                    help="run only this single-layer workload (no step, no oracle baseline) "
+                         "and print its figures as the JSON line: the unit a per-workload "
+                         "profile covers")
     ap.add_argument("--no-legs", action="store_true",
                     help="skip the single-layer workloads (the Qwen3-8B and Qwen3-14B layers "
                          "and the ragged batch), each kernel timed after a cache flush")
@@ -101,6 +114,25 @@ def parse():
 
 def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(wl, kind, kernel):
+    """HBM bytes per launch of `kernel` from the committed PMC measurement of this workload
+    (rocprofv3 FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's counts), or None when the
+    measurement is of another workload or the kernel's source has changed since."""
+    path = os.path.join(ROOT, "profiles", "kernel_traffic.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    w = t.get("workload", {})
+    if (w.get("name"), w.get("block_size"), w.get("resident_pool_blocks"), w.get("digest")) != \
+            (wl.name, wl.block_size, wl.pool_blocks, kind):
+        return None
+    for name, k in t.get("kernels", {}).items():
+        if name.startswith(kernel + "<") and \
+                k.get("source_sha256_16") == source_hash(os.path.join(ROOT, k["source"])):
+            return k["hbm_bytes_per_launch"]
+    return None
 
 
 # ---------------------------------------------------------------------------------------
@@ -607,9 +639,12 @@ def offload_measure(wl, dims, lens, layers, ws, side_stream, ms_gpu, args, torch
     log(f"offload: host store of {args.host_pages} pages ready ({time.time() - t0:.1f} s), "
         f"{threads} host threads")
 
+    handoff = "host_func"
+
     def step():
         B.sa_decode_step_offload(dims, "mean", wl.hidden, k, wl.scale, lens, layers, ws, plan,
-                                 host_stream, side_stream=side_stream)
+                                 host_stream if handoff == "host_func" else None,
+                                 side_stream=side_stream)
 
     def timed(run, n):
         torch.cuda.synchronize()
@@ -647,6 +682,34 @@ def offload_measure(wl, dims, lens, layers, ws, side_stream, ms_gpu, args, torch
             log(f"offload step: graph capture unavailable ({e})")
         torch.cuda.synchronize()
         del graph
+        # the same step with the flag hand-off (the plan's dispatcher thread and bounded GPU
+        # waits on flags in page-locked memory), eager and replayed from a graph
+        handoff = "flags"
+        plan.set_handoff("flags", gpu_wait_ms=30000)
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        ms_flags, host_ms_f = timed(step, args.offload_steps)
+        log(f"offload step (flag hand-off, eager): {ms_flags:.2f} ms/step")
+        out["ms_per_step_flags_eager"] = round(ms_flags, 3)
+        if ms_flags < ms_off:
+            ms_off, mode, host_ms = ms_flags, "eager, flag hand-off", host_ms_f
+        graph = None
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            torch.cuda.synchronize()
+            ms_fg, host_ms_fg = timed(graph.replay, args.offload_steps)
+            log(f"offload step (flag hand-off, hip-graph): {ms_fg:.2f} ms/step")
+            out["ms_per_step_flags_graph"] = round(ms_fg, 3)
+            if ms_fg < ms_off:
+                ms_off, mode, host_ms = ms_fg, "hip-graph, flag hand-off", host_ms_fg
+        except Exception as e:  # noqa: BLE001
+            log(f"offload step (flag hand-off): graph capture unavailable ({e})")
+        torch.cuda.synchronize()
+        del graph
+        plan.set_handoff("host_func")
         out.update({
             "ms_per_step": round(ms_off, 3), "launch": mode,
             "seq_layers_per_s": round(wl.batch * wl.layers / (ms_off * 1e-3), 1),
@@ -895,6 +958,13 @@ def main():
     B.lib()
     torch.cuda.set_device(0)
 
+    if args.leg is not None:
+        name, kd = LEGS[args.leg]
+        flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        out = layer_leg(getattr(wk, name), kd, torch, B, wk, flush)
+        print(json.dumps({"leg": args.leg, **out}), flush=True)
+        return
+
     wl = wk.QWEN3_14B_STEP
     if args.pool_blocks is not None:
         wl = wl.scaled(pool_blocks=args.pool_blocks)
@@ -1000,13 +1070,8 @@ def main():
     total_bytes = step_bytes(wl, n_gpu_sums)
     log(f"attention: {attn_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s algorithmic")
 
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", "attention_traffic.json")
-    if os.path.exists(tpath):
-        t = json.load(open(tpath))
-        src = os.path.join(ROOT, "block_sparse_attention_digest_amd", "csrc", "attention.hip")
-        if t.get("attention_source_sha256_16") == source_hash(src):
-            traffic = t.get("hbm_bytes_per_launch")
+    traffic = measured_traffic(wl, kind, "attn_bf16_kernel")
+    sel_traffic = measured_traffic(wl, kind, "select_kernel")
 
     value = wl.batch * wl.layers / (ms_step * 1e-3)
     result = {
@@ -1055,7 +1120,7 @@ def main():
             "achieved": round(sbytes / (sel_step["median_us"] * 1e-6) / 1e9, 1),
             "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(sbytes / (sel_step["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-            "traffic": None, "time": sel_step, "algorithmic_bytes_per_launch": sbytes,
+            "traffic": sel_traffic, "time": sel_step, "algorithmic_bytes_per_launch": sbytes,
             "measured": f"{n_sel} launches in {args.profile_steps} eager steps, HIP events at "
                         "each kernel's start and end; median",
             "shares_hbm_with": "the previous layer's attention on the main stream"},
@@ -1110,10 +1175,8 @@ def main():
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
-        result["layer_workloads"] = [
-            layer_leg(w, kd, torch, B, wk, flush)
-            for w, kd in ((wk.QWEN3_8B_LAYER, "mean"), (wk.QWEN3_14B_LAYER, "minmax"),
-                          (wk.RAGGED, "mean"), (wk.RAGGED, "minmax"))]
+        result["layer_workloads"] = [layer_leg(getattr(wk, name), kd, torch, B, wk, flush)
+                                     for name, kd in LEGS.values()]
         del flush
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libscoutattn.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = 0, -1, -2, -3, -4
 SA_F32, SA_BF16 = 0, 1
 SA_DIGEST_MEAN, SA_DIGEST_MINMAX = 0, 1
-ABI_VERSION = 11
+ABI_VERSION = 12
 
 KIND = {"mean": SA_DIGEST_MEAN, "minmax": SA_DIGEST_MINMAX}
 
@@ -109,7 +109,12 @@ SIGNATURES = {
                                                _Z, _I]),
     "sa_host_partial_attention": (ctypes.c_int, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _I, _F,
                                                  _P, _P, _P, _I]),
+    "sa_host_plan_set_handoff": (ctypes.c_int, [_P, ctypes.c_int, _P, _I]),
+    "sa_stream_signal": (ctypes.c_int, [_P, _P]),
+    "sa_stream_wait": (ctypes.c_int, [_P, _P, _I, _P, _P]),
 }
+
+HANDOFF = {"host_func": 0, "flags": 1}
 
 _lib = None
 
@@ -579,6 +584,19 @@ class HostPlan:
                                              _ptr(ws, torch.uint8, name="ws"), ws.numel(),
                                              1 if overlap else 0))
 
+    def set_handoff(self, mode: str, flags=None, gpu_wait_ms: int = 30000):
+        """sa_host_plan_set_handoff: "host_func" (HIP host functions, the default) or
+        "flags" (a dispatcher thread and flags in memory both sides see).  flags: an int32
+        CPU tensor of 2 * layers + 1 words (default: a new page-locked coherent one),
+        zeroed by the call and kept alive here."""
+        if mode == "flags" and flags is None:
+            flags = pinned_empty((2 * len(self.layers) + 1,), torch.int32)
+        ptr = None
+        if mode == "flags":
+            ptr = _ptr(flags, torch.int32, 2 * len(self.layers) + 1, "flags", device=False)
+        _check(lib().sa_host_plan_set_handoff(self.handle, HANDOFF[mode], ptr, gpu_wait_ms))
+        self.flags = flags if mode == "flags" else None
+
     def run(self, layer: int):
         """Layer `layer`'s host task now, on this thread and the plan's workers."""
         _check(lib().sa_host_plan_run(self.handle, layer))
@@ -605,7 +623,25 @@ def sa_decode_step_offload(dims: Dims, kind: str, hidden: int, top_k: int, scale
         _ptr(seq_lens, torch.int32, dims.batch, "seq_lens"), len(layers), arr,
         _ptr(ws, torch.uint8, name="ws"), ws.numel(), _stream(stream),
         None if side_stream is None else _stream(side_stream), plan.handle,
-        _stream(host_stream), None if recall_stream is None else _stream(recall_stream)))
+        None if host_stream is None else _stream(host_stream),
+        None if recall_stream is None else _stream(recall_stream)))
+
+
+def _word(t, name):
+    return _ptr(t, torch.int32, 1, name, device=t.is_cuda)
+
+
+def sa_stream_signal(counter, stream=None):
+    """*counter += 1 once the stream's earlier work is done (counter: a one-element int32
+    tensor in page-locked host memory or on the GPU)."""
+    _check(lib().sa_stream_signal(_word(counter, "counter"), _stream(stream)))
+
+
+def sa_stream_wait(flag, counter, wait_ms: int, timeouts, stream=None):
+    """Hold the stream until *flag == *counter, for at most about wait_ms ms; on giving up,
+    *timeouts = 1."""
+    _check(lib().sa_stream_wait(_word(flag, "flag"), _word(counter, "counter"), wait_ms,
+                                _word(timeouts, "timeouts"), _stream(stream)))
 
 
 PROFILE_STAGE = {"attention": 0, "select": 1, "gemm": 2}

@@ -24,7 +24,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libscoutattn.so")
 
 SOURCES = ["api.hip", "layout.hip", "digest.hip", "gemm.hip", "select.hip", "attention.hip",
-           "recall.hip", "dense.hip", "host_attention.cpp"]
+           "recall.hip", "dense.hip", "handoff.hip", "host_attention.cpp", "host_handoff.cpp"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -8,6 +8,7 @@
 #include <chrono>
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <memory>
 #include <mutex>
@@ -701,10 +702,23 @@ struct sa_host_plan {
   bool recall_overlap = false;
   std::vector<hipEvent_t> recall_done;
   std::vector<char> recall_pending;
+  // flag hand-off (sa_host_plan_set_handoff): the dispatcher thread, and the GPU wait bound
+  std::unique_ptr<sa::FlagDispatcher> flags;
+  uint32_t wait_rounds = 0;
   ~sa_host_plan() {
+    flags.reset();  // joins the dispatcher before the tasks and the pool it uses go
     for (hipEvent_t e : recall_done) hipEventDestroy(e);
   }
 };
+
+// The empty partial of a layer: o = 0, m = -inf, l = 0 for every row.
+static void empty_partial(const sa_host_plan& P, int layer) {
+  const sa_host_layer& H = P.layers[layer];
+  const size_t rows = (size_t)P.s.B * P.s.Hq;
+  std::fill(H.o_host, H.o_host + rows * P.s.d, 0.f);
+  std::fill(H.m_host, H.m_host + rows, -INFINITY);
+  std::fill(H.l_host, H.l_host + rows, 0.f);
+}
 
 // A layer's host task: A_cpu on the plan's workers; false if no worker could run (the
 // partial is then the empty one).
@@ -719,10 +733,7 @@ static bool host_task(const sa_host_plan::Task& t) {
   const bool done = P.pool->run(a);
   if (!done) {
     P.failed = true;
-    const size_t rows = (size_t)P.s.B * P.s.Hq;
-    std::fill(H.o_host, H.o_host + rows * P.s.d, 0.f);
-    std::fill(H.m_host, H.m_host + rows, -INFINITY);
-    std::fill(H.l_host, H.l_host + rows, 0.f);
+    empty_partial(P, t.layer);
   }
   const auto dt = std::chrono::steady_clock::now() - t0;
   P.busy_ns += std::chrono::duration_cast<std::chrono::nanoseconds>(dt).count();
@@ -830,17 +841,70 @@ sa_status sa_host_plan_set_recall(sa_host_plan* plan, int32_t max_recall, float 
   return ok();
 }
 
+sa_status sa_host_plan_set_handoff(sa_host_plan* plan, sa_handoff mode, uint32_t* flags,
+                                   int32_t gpu_wait_ms) {
+  SA_NOT_NULL(plan);
+  if (mode != SA_HANDOFF_HOST_FUNC && mode != SA_HANDOFF_FLAGS)
+    return fail(SA_ERR_INVALID_ARG, "handoff mode %d is neither SA_HANDOFF_HOST_FUNC nor "
+                "SA_HANDOFF_FLAGS", (int)mode);
+  if (mode == SA_HANDOFF_FLAGS) {
+    SA_NOT_NULL(flags);
+    if ((uintptr_t)flags % alignof(uint32_t) != 0)
+      return fail(SA_ERR_INVALID_ARG, "flags is not 4-byte aligned");
+    if (gpu_wait_ms < 1) return fail(SA_ERR_INVALID_ARG, "gpu_wait_ms %d < 1", gpu_wait_ms);
+  }
+  plan->flags.reset();  // (serves or closes the layers still raised)
+  if (mode == SA_HANDOFF_HOST_FUNC) return ok();
+  try {
+    sa_host_plan* P = plan;
+    plan->flags = std::make_unique<sa::FlagDispatcher>(
+        flags, (int)plan->layers.size(), [P](int layer) { return host_task(P->tasks[layer]); },
+        [P](int layer) { empty_partial(*P, layer); });
+  } catch (const std::exception& e) {  // thread creation
+    return fail(SA_ERR_INVALID_ARG, "handoff dispatcher: %s", e.what());
+  }
+  plan->wait_rounds = sa::wait_rounds(gpu_wait_ms);
+  return ok();
+}
+
+sa_status sa_stream_signal(uint32_t* counter, hipStream_t stream) {
+  SA_NOT_NULL(counter);
+  if ((uintptr_t)counter % alignof(uint32_t) != 0)
+    return fail(SA_ERR_INVALID_ARG, "counter is not 4-byte aligned");
+  SA_HIP(sa::launch_signal(counter, stream), "signal kernel");
+  return ok();
+}
+
+sa_status sa_stream_wait(const uint32_t* flag, const uint32_t* counter, int32_t wait_ms,
+                         uint32_t* timeouts, hipStream_t stream) {
+  SA_NOT_NULL(flag);
+  SA_NOT_NULL(counter);
+  SA_NOT_NULL(timeouts);
+  if ((uintptr_t)flag % alignof(uint32_t) != 0 || (uintptr_t)counter % alignof(uint32_t) != 0 ||
+      (uintptr_t)timeouts % alignof(uint32_t) != 0)
+    return fail(SA_ERR_INVALID_ARG, "flag, counter or timeouts is not 4-byte aligned");
+  if (wait_ms < 1) return fail(SA_ERR_INVALID_ARG, "wait_ms %d < 1", wait_ms);
+  SA_HIP(sa::launch_wait(flag, counter, sa::wait_rounds(wait_ms), timeouts, stream),
+         "wait kernel");
+  return ok();
+}
+
 sa_status sa_host_plan_destroy(sa_host_plan* plan) {
-  delete plan;  // joins the workers
+  delete plan;  // joins the dispatcher and the workers
   return ok();
 }
 
 sa_status sa_host_plan_stats(const sa_host_plan* plan, int64_t* tasks, double* busy_seconds) {
   SA_NOT_NULL(plan);
+  const sa::FlagDispatcher* D = plan->flags.get();
+  if (D) D->drain();
   if (tasks) *tasks = plan->runs.load();
   if (busy_seconds) *busy_seconds = 1e-9 * (double)plan->busy_ns.load();
   if (plan->failed.load())
     return fail(SA_ERR_HIP, "a host task could not run (out of memory); its partial is empty");
+  if (D && D->gpu_timed_out())
+    return fail(SA_ERR_HIP, "a GPU wait for a done flag timed out; that layer's merge read "
+                "its host partial before it was complete");
   return ok();
 }
 
@@ -928,7 +992,7 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
         (int)plan->layers.size() != num_layers)
       return fail(SA_ERR_INVALID_ARG,
                   "the host plan was made for another top_k, scale or number of layers");
-    if (!host_stream || host_stream == stream || host_stream == side_stream)
+    if (!plan->flags && (!host_stream || host_stream == stream || host_stream == side_stream))
       return fail(SA_ERR_INVALID_ARG, "host_stream must be a stream of its own");
     if (!plan->recall.empty() &&
         (!recall_stream || recall_stream == stream || recall_stream == side_stream ||
@@ -938,6 +1002,7 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
   }
   const bool recalls = plan && !plan->recall.empty();
   const bool overlap = recalls && plan->recall_overlap;
+  sa::FlagDispatcher* flags = plan ? plan->flags.get() : nullptr;
   if (overlap) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     SA_HIP(hipStreamIsCapturing(stream, &cs), "hipStreamIsCapturing");
@@ -985,9 +1050,16 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
   // the CPU side of layer j, once its lists are selected on `from`: the query it attends
   // with goes to the plan's host buffer, then a host task on host_stream computes A_cpu^j
   std::vector<hipEvent_t> host_done(plan ? num_layers : 0, nullptr);
+  // (only the query heads of pairs that offloaded something: the host reads no other)
   auto spawn_host = [&](int j, const sa::QParts& q, hipStream_t from) -> sa_status {
     const sa_host_layer& H = plan->layers[j];
-    SA_HIP(sa::launch_gather_query(q, s.B, n, H.q_host, from), "query gather kernel");
+    SA_HIP(sa::launch_gather_query(q, s.B, n, H.q_host, from, layers[j].n_cpu, s.G * s.d,
+                                   s.Hkv),
+           "query gather kernel");
+    if (flags) {  // advance ready[j] once the lists and the query are written
+      SA_HIP(sa::launch_signal(flags->flags() + j, from), "signal kernel");
+      return SA_OK;
+    }
     SA_CHECK(order(from, host_stream));
     SA_HIP(hipLaunchHostFunc(host_stream, run_host_task, &plan->tasks[j]), "hipLaunchHostFunc");
     SA_CHECK(new_event(&host_done[j]));
@@ -1094,7 +1166,11 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
     const float* hm = L.host_m;
     const float* hl = L.host_l;
     if (plan) {  // layer i's CPU side, spawned one layer earlier (layer 0: just now)
-      if (hipStreamWaitEvent(stream, host_done[i], 0) != hipSuccess) {
+      if (flags) {
+        e = sa::launch_wait(flags->flags() + num_layers + i, flags->flags() + i,
+                            plan->wait_rounds, flags->flags() + 2 * num_layers, stream);
+        if (e != hipSuccess) { st = hip_fail(e, "wait kernel"); break; }
+      } else if (hipStreamWaitEvent(stream, host_done[i], 0) != hipSuccess) {
         st = fail(SA_ERR_HIP, "hipStreamWaitEvent failed");
         break;
       }
@@ -1134,7 +1210,7 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
     sa_status j = order(side_stream, stream);
     if (st == SA_OK) st = j;
   }
-  if (plan) {
+  if (plan && !flags) {  // (with flags, each merge has already waited for its job)
     sa_status j = order(host_stream, stream);
     if (st == SA_OK) st = j;
   }

@@ -702,7 +702,9 @@ __global__ __launch_bounds__(256) void reduce_kernel(
   const int pair = s * Hkv + qh / G, g = qh % G;
   const PartialView part = partial_view(const_cast<float*>(ws), npairs, W, G, D);
 
-  // first loads: the pair's block count and prefix, and the host partial
+  // first loads: the pair's block count and prefix, its offloaded count and the host
+  // partial's (m, l); the host o vector (possibly over the host link) is read in the second
+  // round, and only for a pair with something offloaded
   const int ng = clamp_count(n_gpu[pair], cap);
   const int P = part.pfx[pair];
   const int T = part.pfx[npairs];
@@ -715,12 +717,14 @@ __global__ __launch_bounds__(256) void reduce_kernel(
   if (host_ptr) {
     mh = host_m[row] * kLog2e;
     lh = host_l[row];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) ho[i] = host_o[(size_t)row * D + lane + kWave * i];
     if (n_cpu) nc = n_cpu[pair];
   }
   // an empty host partial, or one for a pair with nothing offloaded, contributes nothing
   if (!host_ptr || nc <= 0 || !(lh > 0.f)) mh = -INFINITY;
+  if (mh != -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) ho[i] = host_o[(size_t)row * D + lane + kWave * i];
+  }
 
   int w_lo = 0, nslot = 0;
   if (ng > 0) {

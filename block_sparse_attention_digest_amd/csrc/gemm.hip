@@ -284,12 +284,16 @@ hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void
 // One float4 of one row per thread: the k-slice partials summed in slice order.  `out` may be
 // page-locked host memory the device addresses (the query handed to the CPU side).
 __global__ __launch_bounds__(256) void gather_query_kernel(QParts q, int rows, int n,
+                                                           const int32_t* __restrict__ n_cpu,
+                                                           int group_cols, int Hkv,
                                                            float* __restrict__ out) {
   const long i4 = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const int n4 = n / 4;
   if (i4 >= (long)rows * n4) return;
   const int row = (int)(i4 / n4);
   const int col = (int)(i4 % n4) * 4;
+  // with n_cpu, only the query heads of (row, KV head) pairs that offloaded something
+  if (n_cpu && n_cpu[(size_t)row * Hkv + col / group_cols] <= 0) return;
   const float* src = q.base + (size_t)row * q.row_stride + col;
   float4 s = *reinterpret_cast<const float4*>(src);
   for (int p = 1; p < q.parts; ++p) {
@@ -299,11 +303,12 @@ __global__ __launch_bounds__(256) void gather_query_kernel(QParts q, int rows, i
   *reinterpret_cast<float4*>(out + (size_t)row * n + col) = s;
 }
 
-hipError_t launch_gather_query(const QParts& q, int rows, int n, float* out, hipStream_t stream) {
+hipError_t launch_gather_query(const QParts& q, int rows, int n, float* out, hipStream_t stream,
+                               const int32_t* n_cpu, int group_cols, int Hkv) {
   const long total4 = (long)rows * (n / 4);
   if (total4 == 0) return hipSuccess;
   hipLaunchKernelGGL(gather_query_kernel, dim3((unsigned)((total4 + 255) / 256)), dim3(256), 0,
-                     stream, q, rows, n, out);
+                     stream, q, rows, n, n_cpu, group_cols, Hkv, out);
   return hipGetLastError();
 }
 

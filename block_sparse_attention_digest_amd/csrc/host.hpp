@@ -5,6 +5,7 @@
 #include <condition_variable>
 #include <cstddef>
 #include <cstdint>
+#include <functional>
 #include <mutex>
 #include <thread>
 #include <vector>
@@ -59,6 +60,42 @@ class HostPool {
   std::atomic<int> next_{0};
   std::vector<float> own_buf_;  // the block buffers of the thread that calls run()
   std::vector<std::thread> workers_;
+};
+
+// The flag hand-off of the offload step: a host thread that serves each layer whose ready
+// flag the GPU has advanced -- it runs the layer's task, then sets the layer's done flag to
+// the ready value it served -- while a bounded wait on the GPU holds the layer's merge until
+// done equals ready.  The flags are caller-owned words both sides see (page-locked, coherent
+// memory): ready[0, L) (advanced only by the GPU), done[L, 2L) (written only here), and word
+// 2L, where the GPU's wait records a timeout.  Every ready value seen gets its done flag
+// written: after the task, or after a failed task (the layer's partial then empty), and at
+// shutdown for a layer raised but not yet served (partial empty).  The thread needs no job
+// posted by the host, so a step may be replayed from a graph.  Pending layers are served in
+// cyclic layer order from the last one served.
+class FlagDispatcher {
+ public:
+  using Task = std::function<bool(int)>;   // runs the layer's CPU side; false: it failed
+  using Empty = std::function<void(int)>;  // writes the layer's empty partial
+  FlagDispatcher(uint32_t* flags, int layers, Task task, Empty empty);  // zeroes the flags
+  ~FlagDispatcher();
+  FlagDispatcher(const FlagDispatcher&) = delete;
+  FlagDispatcher& operator=(const FlagDispatcher&) = delete;
+  // waits until every layer's done flag equals its ready flag
+  void drain() const;
+  int64_t failures() const { return failures_.load(); }
+  bool gpu_timed_out() const;
+  uint32_t* flags() const { return flags_; }
+  int layers() const { return layers_; }
+
+ private:
+  void loop();
+  uint32_t* flags_;
+  int layers_;
+  Task task_;
+  Empty empty_;
+  std::atomic<bool> stop_{false};
+  std::atomic<int64_t> failures_{0};
+  std::thread thread_;
 };
 
 }  // namespace sa

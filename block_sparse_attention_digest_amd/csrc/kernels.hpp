@@ -77,8 +77,11 @@ hipError_t launch_recall(const Shape& s, int list_stride, int max_recall, const 
                          long threshold, hipStream_t stream);
 
 // q_out[r][c] = the sum of the parts of q, for rows r < rows and columns c < n (n a multiple of
-// 4); q_out may be device-addressable host memory
-hipError_t launch_gather_query(const QParts& q, int rows, int n, float* q_out, hipStream_t stream);
+// 4); q_out may be device-addressable host memory.  With n_cpu ([rows][Hkv]), only the columns
+// of KV heads h (columns [h * group_cols, (h + 1) * group_cols), a multiple of 4) whose
+// n_cpu[r][h] > 0 are written.
+hipError_t launch_gather_query(const QParts& q, int rows, int n, float* q_out, hipStream_t stream,
+                               const int32_t* n_cpu = nullptr, int group_cols = 1, int Hkv = 1);
 
 // ---- selection: scores, top-k and the resident split --------------------------------------
 // Pairs [0, whole) get one workgroup each; the other `split` pairs are cut into nchunk
@@ -122,6 +125,16 @@ hipError_t launch_reduce(const Shape& s, const AttnPlan& plan, const int32_t* n_
                          const float* partials, const float* host_o, const float* host_m,
                          const float* host_l, const int32_t* n_cpu, float* o, float* m,
                          float* l, hipStream_t stream);
+
+// ---- flags shared with the host (page-locked, coherent memory) -----------------------------
+// *ready += 1 after everything before it on the stream (only the device writes *ready)
+hipError_t launch_signal(uint32_t* ready, hipStream_t stream);
+// holds the stream until *done == *ready (as read when the wait starts), for at most
+// `rounds` polling rounds; on giving up it writes 1 to *timeouts and returns
+hipError_t launch_wait(const uint32_t* done, const uint32_t* ready, uint32_t rounds,
+                       uint32_t* timeouts, hipStream_t stream);
+// polling rounds of launch_wait that last at least `ms` milliseconds
+uint32_t wait_rounds(int ms);
 
 // ---- merge of two normalised partials ------------------------------------------------------
 hipError_t launch_merge(int rows, int d, const float* o_a, const float* m_a, const float* l_a,

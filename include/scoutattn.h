@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 11
+#define SA_ABI_VERSION 12
 
 typedef enum {
   SA_OK = 0,
@@ -407,14 +407,56 @@ sa_status sa_host_plan_set_recall(sa_host_plan* plan, int32_t max_recall, float 
 sa_status sa_host_plan_destroy(sa_host_plan* plan);
 sa_status sa_host_plan_stats(const sa_host_plan* plan, int64_t* tasks, double* busy_seconds);
 
+/* sa_host_plan_set_handoff -- how sa_decode_step_offload hands each layer's CPU side over
+ * ([HTML Sec. 3.3]: the CPU attends layer i's offloaded blocks while the GPU works one layer
+ * ahead; the GPU merges the two partials at layer i).
+ *   SA_HANDOFF_HOST_FUNC (the default): a HIP host function per layer on host_stream, and an
+ *     event the merge waits for.
+ *   SA_HANDOFF_FLAGS: flags in memory both sides see.  flags: 2 * num_layers + 1 uint32
+ *     words, page-locked and coherent (hipHostMalloc with hipHostMallocCoherent), owned by the
+ *     caller and kept while the plan uses them; the call zeroes them.  Words [0, L) are the
+ *     layers' ready counters, [L, 2L) their done flags, word 2L the GPU's timeout record.
+ *     Per layer and step, a one-lane kernel advances ready[i] once the selection's lists and
+ *     the gathered query are written; the plan's dispatcher thread, seeing ready[i] !=
+ *     done[i], runs the layer's task and then sets done[i] = the ready value it served; a
+ *     one-lane kernel before the merge holds `stream` until done[i] == ready[i].  Every
+ *     ready value the dispatcher sees gets its done flag: after the task, after a failed
+ *     task (partial empty), and, when the plan is destroyed or switched, for a layer raised
+ *     but not served (partial empty).  The GPU wait gives up after about gpu_wait_ms (it then
+ *     writes 1 to word 2L, the merge reads a partial that may be incomplete, and
+ *     sa_host_plan_stats reports it), so no wait is left unresolved whatever the host does.
+ *     gpu_wait_ms >= 1, well above the longest layer task.  No value comes from the host, so
+ *     a step may be captured in a HIP graph and replayed.  host_stream is not used (it may be
+ *     NULL).
+ * Call it while no step of the plan is in flight.  With SA_HANDOFF_FLAGS, sa_host_plan_stats
+ * first waits until every raised layer has been served (call it after the step's stream has
+ * been synchronised), and fails (SA_ERR_HIP) if a GPU wait has timed out. */
+typedef enum { SA_HANDOFF_HOST_FUNC = 0, SA_HANDOFF_FLAGS = 1 } sa_handoff;
+sa_status sa_host_plan_set_handoff(sa_host_plan* plan, sa_handoff mode, uint32_t* flags,
+                                   int32_t gpu_wait_ms);
+
+/* sa_stream_signal / sa_stream_wait -- the two kernels of the flag hand-off, on their own.
+ * counter, flag, timeouts: words in page-locked coherent host memory (or device memory).
+ * sa_stream_signal: *counter += 1 once everything before it on `stream` has finished (only
+ * the device may write *counter).  sa_stream_wait: holds `stream` until *flag equals
+ * *counter (read when the wait starts), polling for at most about wait_ms milliseconds
+ * (wait_ms >= 1); if they are still unequal then, it writes 1 to *timeouts and lets the
+ * stream go on.  Its wave always ends. */
+sa_status sa_stream_signal(uint32_t* counter, hipStream_t stream);
+sa_status sa_stream_wait(const uint32_t* flag, const uint32_t* counter, int32_t wait_ms,
+                         uint32_t* timeouts, hipStream_t stream);
+
 /* sa_decode_step_offload -- sa_decode_step with the CPU side computed, not given.  The
  * arguments are those of sa_decode_step, with the plan's shape, top_k, scale and num_layers;
  * in `layers`, host_o/host_m/host_l and the host mirrors are not used (the plan's buffers
  * take their place).  For each layer i, once B^i is selected (layer 0 on `stream`, the
  * others one layer ahead on side_stream), the step writes the query the CPU attends with
- * into q_host and the lists into the plan's mirrors, then enqueues on host_stream a host
+ * into q_host (the query heads of the pairs with offloaded blocks; the other rows are left
+ * as they are) and the lists into the plan's mirrors, then enqueues on host_stream a host
  * task that computes A_cpu^i with the plan's workers (as sa_host_partial_attention does)
- * into o_host/m_host/l_host; layer i's merge on `stream` waits for that task.  host_stream
+ * into o_host/m_host/l_host; layer i's merge on `stream` waits for that task.  (With the
+ * plan's SA_HANDOFF_FLAGS hand-off the task is run by the plan's dispatcher thread instead,
+ * see sa_host_plan_set_handoff.)  host_stream
  * must be a stream of its own (not `stream`, not side_stream): each task holds it while it
  * runs.  Layer 0 has no layer before it, so its merge waits for its own CPU side.  Before
  * returning, `stream` waits for host_stream, side_stream and (unless the plan's recalls

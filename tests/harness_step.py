@@ -112,13 +112,16 @@ def host_side(wl, data, store="full", host_pages=32768):
 
 
 def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs_to_check=None,
-             side=True, offload=False, host_threads=4, store="full", host_pages=32768):
+             side=True, offload=False, host_threads=4, store="full", host_pages=32768,
+             flags=False, steps=1):
     """handoff: give every layer host mirrors of its offloaded lists; side: run the
     layer-ahead work on a side stream; offload: compute the CPU side with host tasks
     (sa_decode_step_offload) from a host store of every block, instead of merging the
     drawn host partials.  store: "full" gives every block its own host page
     (draw_host_store); "aliased" maps every block into one pool of host_pages pages shared by
-    all layers (draw_host_store_aliased), for shapes whose offloaded KV would not fit."""
+    all layers (draw_host_store_aliased), for shapes whose offloaded KV would not fit.
+    flags: the offload step hands its CPU side over with flags (SA_HANDOFF_FLAGS) instead of
+    HIP host functions; steps: how many times the step runs before the check (same inputs)."""
     dev = "cuda"
     B_, Hkv, Hq, G, d, bs, k = (wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.group,
                                 wl.head_dim, wl.block_size, wl.top_k)
@@ -139,13 +142,24 @@ def run_step(wl: wk.Workload, gen_device="cpu", handoff=True, kind="mean", pairs
     if offload:
         stores, host_layers = host_side(wl, data, store, host_pages)
         plan = B.HostPlan(dims, k, wl.scale, lens.clone(), host_layers, threads=host_threads)
-        host_stream = torch.cuda.Stream()
-        B.sa_decode_step_offload(dims, kind, wl.hidden, k, wl.scale, lens_d, dev_layers, ws,
-                                 plan, host_stream, side_stream=side_stream)
-        torch.cuda.synchronize()
+        host_stream = None
+        if flags:
+            plan.set_handoff("flags", gpu_wait_ms=30000)
+        else:
+            host_stream = torch.cuda.Stream()
+        for rep in range(steps):
+            if rep:  # the host partials are written again by the next step's tasks
+                for hl in host_layers:
+                    hl["o_host"].fill_(float("nan"))
+            B.sa_decode_step_offload(dims, kind, wl.hidden, k, wl.scale, lens_d, dev_layers, ws,
+                                     plan, host_stream, side_stream=side_stream)
+            torch.cuda.synchronize()
         tasks, secs = plan.stats()
+        if flags:
+            fl = plan.flags.view(torch.int32)
+            assert fl[:2 * L].tolist() == [steps] * (2 * L) and fl[2 * L].item() == 0, fl
         plan.close()
-        assert tasks == L, (tasks, L)
+        assert tasks == L * steps, (tasks, L, steps)
         H.log(f"  HIP step with host tasks done ({tasks} tasks, {secs * 1e3:.2f} ms on the host)")
     else:
         B.sa_decode_step(dims, kind, wl.hidden, k, wl.scale, lens_d, dev_layers, ws,
@@ -271,7 +285,9 @@ def check_step(wl, data, dev_layers, lens, pairs_to_check=None, kind="mean", off
                 W64 = wk.f64(data[i]["W"])[h * G * d:(h + 1) * G * d]
                 q_want = so.predict_query(X64, W64).reshape(G, d)
                 q_got = host_layers[i]["q_host"][s, h * G:(h + 1) * G].double().numpy()
-                assert np.max(np.abs(q_got - q_want)) <= 1e-3 * max(1.0, np.max(np.abs(q_want)))
+                if nc > 0:  # (handed over only where something is offloaded)
+                    assert np.max(np.abs(q_got - q_want)) <= \
+                        1e-3 * max(1.0, np.max(np.abs(q_want)))
                 hl_ = host_layers[i]
                 for j in range(G):  # (the empty partial where nothing is offloaded)
                     max_err = max(max_err, H.compare_partial(

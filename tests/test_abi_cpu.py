@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.sa_abi_version() == B.ABI_VERSION == 11
+    assert lib.sa_abi_version() == B.ABI_VERSION == 12
     assert lib.sa_status_string(B.SA_ERR_WORKSPACE) == b"SA_ERR_WORKSPACE"
 
 

@@ -363,6 +363,55 @@ def test_step_recall_overlap_matches_join():
     assert moved > 0
 
 
+@pytest.mark.parametrize("side", [True, False])
+def test_step_offload_parity_flag_handoff(side):
+    """The offload step with its CPU side handed over through flags (a signal kernel per layer,
+    the plan's dispatcher thread, a bounded wait kernel before each merge), three steps in a
+    row: flags, host partials and merged outputs against the oracle."""
+    H.log(f"[case] step offload, flag hand-off, side={side}")
+    import harness_step as HS
+    r = HS.run_step(wk.QWEN3_14B_STEP.scaled(batch=3, num_q_heads=10, num_kv_heads=2,
+                                             context=0, ctx_min=1, ctx_max=2000, layers=4,
+                                             pool_blocks=6, hidden=512, top_k=8),
+                    gen_device="cpu", side=side, offload=True, flags=True, steps=3)
+    assert r["cpu_ratio"] > 0.1
+
+
+def test_stream_flags_signal_wait_and_bounded_timeout():
+    """sa_stream_signal / sa_stream_wait on page-locked flags: a wait on a flag that already
+    equals the counter passes without a timeout; a wait passes when the host sets the flag
+    later; a wait on a flag nobody sets gives up after its bound, records the timeout, and
+    its stream goes on."""
+    import threading
+    import time
+    H.log("[case] stream flags")
+    f = B.pinned_empty((4,), torch.int32).zero_()
+    ctr, flag, tmo = f[0:1], f[1:2], f[3:4]
+    s = torch.cuda.Stream()
+    B.sa_stream_signal(ctr, s)  # counter 1
+    s.synchronize()
+    assert f[0].item() == 1
+    flag.fill_(1)
+    B.sa_stream_wait(flag, ctr, 1000, tmo, s)
+    s.synchronize()
+    assert f[3].item() == 0
+    # the counter advances on the stream; the host sets the flag 50 ms later
+    B.sa_stream_signal(ctr, s)  # counter 2
+    B.sa_stream_wait(flag, ctr, 10000, tmo, s)
+    t = threading.Timer(0.05, lambda: f.__setitem__(1, 2))
+    t0 = time.monotonic()
+    t.start()
+    s.synchronize()
+    t.join()
+    assert f[0].item() == 2 and f[3].item() == 0 and time.monotonic() - t0 < 5
+    # never set: the wait ends by itself after about 20 ms, and later work still runs
+    B.sa_stream_signal(ctr, s)  # counter 3
+    B.sa_stream_wait(flag, ctr, 20, tmo, s)
+    B.sa_stream_signal(ctr, s)  # counter 4
+    s.synchronize()
+    assert f[3].item() == 1 and f[0].item() == 4 and f[1].item() == 2
+
+
 def test_step_offload_parity_bs64():
     """The offload step on blocks of 64 tokens, ragged, with the host worker."""
     H.log("[case] step offload bs64")

@@ -50,16 +50,27 @@ def poison(layers, host_layers):
 
 
 def same(a, b):
-    return all(torch.equal(x, y) for x, y in zip(a, b)) and len(a) == len(b)
+    """Bit for bit, NaN matching NaN (query rows of pairs with nothing offloaded are not
+    handed over, so they keep the poison)."""
+    def eq(x, y):
+        if x.is_floating_point():
+            return x.shape == y.shape and torch.equal(x.isnan(), y.isnan()) and \
+                torch.equal(x.nan_to_num(0.0).view(torch.int32), y.nan_to_num(0.0).view(torch.int32))
+        return torch.equal(x, y)
+    return all(eq(x, y) for x, y in zip(a, b)) and len(a) == len(b)
 
 
-@pytest.mark.parametrize("offload,recall", [(False, False), (True, False), (True, True)],
-                         ids=["step", "step-with-host-tasks", "step-with-host-tasks-and-recall"])
-def test_step_graph_replays_match_eager(offload, recall):
+@pytest.mark.parametrize("offload,recall,flags",
+                         [(False, False, False), (True, False, False), (True, True, False),
+                          (True, False, True)],
+                         ids=["step", "step-with-host-tasks", "step-with-host-tasks-and-recall",
+                              "step-with-flag-handoff"])
+def test_step_graph_replays_match_eager(offload, recall, flags):
     """With recall (beta 0), the first eager step recalls every offloaded selected block it
     can, and the state is then stable: later steps find nothing due, on the device, inside
-    the graph as well."""
-    H.log(f"[case] graph replay, offload={offload} recall={recall}")
+    the graph as well.  With the flag hand-off, every replay advances each layer's counter
+    once and the plan's dispatcher serves it."""
+    H.log(f"[case] graph replay, offload={offload} recall={recall} flags={flags}")
     data = HS.prepare_step(WL, "cpu")
     lens = wk.seq_lens(WL)
     lens_d = lens.to("cuda")
@@ -79,6 +90,9 @@ def test_step_graph_replays_match_eager(offload, recall):
                     h[n] = pinned
         plan = B.HostPlan(dims, WL.top_k, WL.scale, lens.clone(), host_layers, threads=3)
         host_stream = torch.cuda.Stream()
+        if flags:
+            plan.set_handoff("flags", gpu_wait_ms=30000)
+            host_stream = None
         if recall:
             pairs = WL.batch * WL.num_kv_heads
             plan.set_recall(dims, 64, 0.0, [
@@ -133,6 +147,9 @@ def test_step_graph_replays_match_eager(offload, recall):
             tasks, _ = plan.stats()
             # the capture enqueues no task; each eager step and each replay runs one per layer
             assert tasks == WL.layers * (8 if recall else 7), tasks
+            if flags:  # ready and done of every layer: 7 steps, no GPU timeout
+                fl = plan.flags.view(torch.int32).tolist()
+                assert fl == [7] * (2 * WL.layers) + [0], fl
     finally:
         if plan is not None:
             torch.cuda.synchronize()
