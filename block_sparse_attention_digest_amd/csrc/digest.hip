@@ -18,6 +18,8 @@
 namespace sa {
 namespace {
 
+constexpr int kDigestWaves = 4;  // waves per workgroup of the build
+
 template <typename T>
 struct Vec;
 template <>
@@ -153,25 +155,71 @@ __device__ __forceinline__ void digest_block(
   }
 }
 
-// Persistent waves over the (pair, block) slots: wave w owns slots [w per, (w + 1) per) and
-// walks them in windows of 64.  Lane j reads window slot j's table entry and its sequence
-// length (one coalesced round); the resident blocks of the window are then digested in
-// order, the next one's page loads in flight while the current one is reduced.  Slots that
-// are not resident (or name a page outside the pool) or lie past their sequence are skipped
-// (their digests are not written).
+// Block count of each (sequence, KV head) pair, nb = ceil(len / BS) clamped into
+// [0, max_blocks] (a negative or oversize length folded in before the division), and their
+// exclusive prefix over the pairs into LDS pfx[0..npairs] (pfx[npairs] = the blocks of all
+// sequences).  Every thread of the workgroup takes part; ends with a barrier.
+template <int BS>
+__device__ void block_count_prefix(const int32_t* __restrict__ seq_lens, int Hkv, int npairs,
+                                   int max_blocks, int* pfx, int* wave_tot) {
+  const int nt = blockDim.x, tid = threadIdx.x;
+  const int lane = tid % kWave, wave = tid / kWave, nw = nt / kWave;
+  const int per = (npairs + nt - 1) / nt;
+  const int p0 = min(npairs, tid * per), p1 = min(npairs, p0 + per);
+  auto nb_of = [&](int p) {
+    const int len = min(max(seq_lens[p / Hkv], 0), max_blocks * BS);
+    return (len + BS - 1) / BS;
+  };
+  int local = 0;
+  for (int p = p0; p < p1; ++p) local += nb_of(p);
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
+  }
+  if (lane == kWave - 1) wave_tot[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wave_tot[w];
+  int run = base + incl - local;
+  for (int p = p0; p < p1; ++p) {
+    pfx[p] = run;
+    run += nb_of(p);
+  }
+  if (tid == nt - 1) {
+    int tot = 0;
+    for (int w = 0; w < nw; ++w) tot += wave_tot[w];
+    pfx[npairs] = tot;
+  }
+  __syncthreads();
+}
+
+// Persistent waves over the blocks inside the sequences: the blocks of all (sequence, KV
+// head) pairs laid end to end (Nb of them, by the prefix of the pairs' block counts), wave w
+// of W takes [w Nb / W, (w + 1) Nb / W), so every wave has the same number of blocks whatever
+// the sequence lengths (slots past a sequence's end are never visited).  It walks its range
+// in windows of 64: lane j finds window block j's pair by a short forward scan of the prefix
+// and reads its table entry and sequence length (one coalesced round); the resident blocks of
+// the window are then digested in order, the next unit's page loads in flight while the
+// current one is reduced.  Blocks without a page in the pool are skipped (their digests are
+// not written).
 template <typename T, int D, int BS, bool MINMAX>
 __global__ __launch_bounds__(256) void digest_kernel(const T* __restrict__ k_pool,
                                                      const int32_t* __restrict__ table,
                                                      const int32_t* __restrict__ seq_lens,
-                                                     T* __restrict__ dig, int Hkv,
-                                                     int max_blocks, int P, long total,
-                                                     long per) {
+                                                     T* __restrict__ dig, int Hkv, int npairs,
+                                                     int max_blocks, int P, int W) {
   using PG = PageGeom<T, D, BS>;
   constexpr int VEC = PG::VEC, CGS = PG::CGS, TG = PG::TG, SL = PG::SL;
+  extern __shared__ int pfx[];  // [npairs + 1]
+  __shared__ int wave_tot[kDigestWaves];
+  block_count_prefix<BS>(seq_lens, Hkv, npairs, max_blocks, pfx, wave_tot);
+  const int Nb = pfx[npairs];
   const int lane = threadIdx.x % kWave;
-  const long gw = (long)blockIdx.x * (blockDim.x / kWave) +
-                  __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const long i0 = gw * per, i1 = min(total, i0 + per);
+  const int gw = blockIdx.x * kDigestWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int i0 = (int)((long)gw * Nb / W), i1 = (int)((long)(gw + 1) * Nb / W);
+  if (i0 >= i1) return;
   const int cl = lane / 8, tl = lane % 8;  // chunk within the group, token within the group
 
   // one slab of a page at once (CGS * TG <= 8 loads of 16 bytes per lane)
@@ -185,13 +233,27 @@ __global__ __launch_bounds__(256) void digest_kernel(const T* __restrict__ k_poo
             src + ((size_t)(8 * (CGS * slab + cs) + cl) * BS + 8 * tg + tl) * VEC);
   };
 
-  for (long w0 = i0; w0 < i1; w0 += kWave) {
-    const long idx = min(w0 + lane, i1 - 1);
-    const int page_l = table[idx];
-    const int pair = (int)(idx / max_blocks), b = (int)(idx % max_blocks);
-    const int len = seq_lens[pair / Hkv];
-    const bool live = w0 + lane < i1 && page_l >= 0 && page_l < P && b * BS < len;
-    const int nval_l = min(BS, len - b * BS);
+  // the pair of the wave's first block (pairs without blocks are passed over)
+  int p = 0;
+  {
+    int lo = 0, hi = npairs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pfx[mid] <= i0) lo = mid; else hi = mid - 1;
+    }
+    p = __builtin_amdgcn_readfirstlane(lo);
+  }
+  for (int w0 = i0; w0 < i1; w0 += kWave) {
+    const int g = min(w0 + lane, i1 - 1);
+    int pj = p;
+    while (pfx[pj + 1] <= g) ++pj;  // ends: pfx[npairs] = Nb > g
+    const int b = g - pfx[pj];      // < the pair's block count <= max_blocks
+    const int slot = pj * max_blocks + b;
+    const int page_l = table[slot];
+    const int len = seq_lens[pj / Hkv];
+    const bool live = w0 + lane < i1 && page_l >= 0 && page_l < P;
+    const int nval_l = min(BS, len - b * BS);  // >= 1: b < ceil(len / BS)
+    p = __builtin_amdgcn_readlane(pj, kWave - 1);
     uint64_t mask = __ballot(live);
     if (mask == 0) continue;
     // the slabs of the window's resident blocks in order; the next slab is loaded before
@@ -210,8 +272,8 @@ __global__ __launch_bounds__(256) void digest_kernel(const T* __restrict__ k_poo
       }
       load_slab(__builtin_amdgcn_readlane(page_l, jn), sn, nxt);
       __builtin_amdgcn_sched_barrier(0);
-      digest_block<T, D, BS, MINMAX>(cur, __builtin_amdgcn_readlane(nval_l, j), dig, w0 + j,
-                                     cl, tl, sl);
+      digest_block<T, D, BS, MINMAX>(cur, __builtin_amdgcn_readlane(nval_l, j), dig,
+                                     __builtin_amdgcn_readlane(slot, j), cl, tl, sl);
       if (last) break;
       if (sn == 0) mask &= mask - 1;  // block jn begins
       j = jn;
@@ -260,36 +322,31 @@ __global__ __launch_bounds__(256) void refresh_kernel(const T* __restrict__ k_po
   }
 }
 
-// Waves the device holds at once for this instantiation (all CUs at full occupancy), found
-// once per instantiation.
+// Waves the device holds at once for this kernel with `lds` bytes of dynamic LDS per
+// workgroup (all CUs at full occupancy).
 template <typename K>
-long resident_waves(K kernel, int block) {
-  static const long n = [&] {
-    int per_cu = 0, cus = 0, dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess ||
-        per_cu < 1 || cus < 1)
-      return 2048L;  // the grid only has to cover the slots; this size always does
-    return (long)per_cu * cus * (block / kWave);
-  }();
-  return n;
+int resident_waves(K kernel, int block, size_t lds) {
+  int per_cu = 0, cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, lds) != hipSuccess ||
+      per_cu < 1 || cus < 1)
+    return 2048;  // any grid covers the blocks; this one keeps the chip busy
+  return per_cu * cus * (block / kWave);
 }
 
 template <typename T, int D, int BS, bool MINMAX>
 hipError_t launch_kind(const Shape& s, const void* k_pool, const int32_t* table,
                        const int32_t* lens, void* dig, hipStream_t stream) {
-  const long total = (long)s.B * s.Hkv * s.max_blocks;
-  const int waves_per_wg = 4, block = waves_per_wg * kWave;
+  const int npairs = s.B * s.Hkv;
+  const int block = kDigestWaves * kWave;
+  const size_t lds = (size_t)(npairs + 1) * sizeof(int);
   auto kernel = digest_kernel<T, D, BS, MINMAX>;
-  // every wave resident at once, each a contiguous share of the slots
-  const long waves =
-      std::max(1L, std::min((total + kWave - 1) / kWave, resident_waves(kernel, block)));
-  const long per = (total + waves - 1) / waves;
-  const long nw = (total + per - 1) / per;
-  const dim3 grid((unsigned)((nw + waves_per_wg - 1) / waves_per_wg));
-  hipLaunchKernelGGL(kernel, grid, dim3(block), 0, stream, (const T*)k_pool, table, lens,
-                     (T*)dig, s.Hkv, s.max_blocks, s.P, total, per);
+  // every wave resident at once (the block count is on the device: waves past it exit)
+  const int waves = resident_waves(kernel, block, lds);
+  const dim3 grid((unsigned)((waves + kDigestWaves - 1) / kDigestWaves));
+  hipLaunchKernelGGL(kernel, grid, dim3(block), lds, stream, (const T*)k_pool, table, lens,
+                     (T*)dig, s.Hkv, npairs, s.max_blocks, s.P, (int)grid.x * kDigestWaves);
   return hipGetLastError();
 }
 

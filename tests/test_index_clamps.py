@@ -179,26 +179,47 @@ def trace_select(c, check, waves=8, threads=512, batch=8, tbl_run=8):
 
 
 def trace_digest(c, check):
-    """digest_kernel: each slot's table entry, and the page reads of live slots only (a page
-    outside [0, P) or a block past its sequence is not live)."""
+    """digest.hip block_count_prefix + digest_kernel: the pairs' block counts from the
+    (clamped) lengths, each wave's balanced range of blocks, each lane's pair by a forward
+    scan, its table entry and length, and the page reads and digest writes of resident
+    blocks only (a page outside [0, P) is not resident)."""
     Hkv, mb, P, BS, D = c["Hkv"], c["max_blocks"], c["P"], c["BS"], c["D"]
-    total = c["B"] * Hkv * mb
-    waves = c["digest_waves"]
-    per = (total + waves - 1) // waves
-    for gw in range(waves):
-        i0, i1 = gw * per, min(total, gw * per + per)
+    npairs = c["B"] * Hkv
+    lens = c["seq_lens"]
+    pfx = [0]
+    for p in range(npairs):
+        check("seq_lens", p // Hkv)
+        L = clamp(lens[p // Hkv], 0, mb * BS)
+        pfx.append(pfx[-1] + (L + BS - 1) // BS)
+    Nb = pfx[npairs]
+    W = c["digest_waves"]
+    for gw in range(W):
+        i0, i1 = gw * Nb // W, (gw + 1) * Nb // W
+        if i0 >= i1:
+            continue
+        p = pair_of(pfx, npairs, i0)
         for w0 in range(i0, i1, WAVE):
+            last_pj = p
             for lane in range(WAVE):
-                idx = min(w0 + lane, i1 - 1)
-                check("table", idx)
-                page = c["table"][idx]
-                pair, b = divmod(idx, mb)
-                check("seq_lens", pair // Hkv)
-                L = c["seq_lens"][pair // Hkv]
-                live = w0 + lane < i1 and 0 <= page < P and b * BS < L
-                if live:
+                g = min(w0 + lane, i1 - 1)
+                pj = p
+                while pfx[pj + 1] <= g:
+                    pj += 1
+                    assert pj < npairs
+                b = g - pfx[pj]
+                assert 0 <= b < mb
+                slot = pj * mb + b
+                check("table", slot)
+                check("seq_lens", pj // Hkv)
+                page = c["table"][slot]
+                L = lens[pj // Hkv]
+                assert min(BS, L - b * BS) >= 1
+                if w0 + lane < i1 and 0 <= page < P:
+                    check("k_pool", page * BS * D)
                     check("k_pool", page * BS * D + BS * D - 1)
-                    check("digests", idx * c["per"] * D + c["per"] * D - 1)
+                    check("digests", slot * c["per"] * D + c["per"] * D - 1)
+                last_pj = pj
+            p = last_pj
 
 
 def bad_int(rng, lo, hi):
@@ -227,7 +248,7 @@ def random_case(rng):
     W = waves_per_wg * rng.randint(1, 12)
     c = dict(B=B, Hkv=Hkv, G=G, D=D, BS=BS, max_blocks=mb, stride=stride, P=P, npairs=npairs,
              W=W, k=stride, per=rng.choice([1, 2]), parts=rng.randint(1, 5),
-             digest_waves=rng.randint(1, 9), use_pages=rng.random() < 0.5)
+             digest_waves=rng.randint(1, 40), use_pages=rng.random() < 0.5)
     c["row_stride"] = Hkv * G * D
     c["part_stride"] = B * c["row_stride"]
     c["n_gpu"] = [bad_int(rng, 0, stride + 1) for _ in range(npairs)]
