@@ -55,6 +55,11 @@ LAYER_CASES = [
     # workgroup ranges that cross more pairs than it stages queries for
     ("bf16-many-pairs", wk.RAGGED.scaled(batch=72, ctx_min=1, ctx_max=300, top_k=4), "mean", {}),
     ("bf16-512-pairs", wk.RAGGED.scaled(batch=64, ctx_min=1, ctx_max=300, top_k=4), "mean", {}),
+    # the most pairs the library takes (8192): the digest build's and attention's prefixes of
+    # 8192 counts in LDS, and more selection workgroups than CUs
+    ("bf16-8192-pairs", wk.RAGGED.scaled(batch=1024, ctx_min=1, ctx_max=48, top_k=2), "mean", {}),
+    ("bf16-8192-pairs-minmax", wk.RAGGED.scaled(batch=1024, ctx_min=1, ctx_max=48, top_k=2,
+                                                seed=1), "minmax", {}),
     # one block per pair and more blocks than waves: attention workgroups whose block ranges
     # cross more pairs than they stage queries for (those are summed from global memory)
     ("bf16-one-block-pairs", wk.RAGGED.scaled(batch=300, ctx_min=1, ctx_max=16, top_k=1), "mean",
