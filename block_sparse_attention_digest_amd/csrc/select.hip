@@ -60,6 +60,7 @@ constexpr int kTblRun = 8;       // block-table entries a thread holds in regist
 constexpr int kMaxRows = kTblRun * kSelThreads;  // rows of one item: its entries fit them
 constexpr int kMinChunkRows = 64;
 constexpr int kCUs = 256;        // compute units of the chip (one round of whole pairs)
+constexpr size_t kWholeBytes = 192 << 10;  // digest bytes of a pair one CU takes whole
 constexpr int kMaxGroup = 8;     // query heads per KV head
 // two workgroups per CU at once (a whole pair's beside a piece's): 4 waves per SIMD
 constexpr int kSelWavesPerSimd = 4;
@@ -589,12 +590,18 @@ hipError_t select_typed(const Shape& s, const SelectPlan& p, bool minmax, const 
 
 }  // namespace
 
-SelectPlan select_plan(const Shape& s, bool) {
+SelectPlan select_plan(const Shape& s, bool minmax) {
   SelectPlan p;
   const int pairs = s.B * s.Hkv;
   // whole pairs: as many full rounds of one per CU as there are (a pair's rows must fit
-  // the table registers of one workgroup)
-  p.whole = s.max_blocks <= kMaxRows ? pairs / kCUs * kCUs : 0;
+  // the table registers of one workgroup).  With no more pairs than CUs and small pairs, all
+  // of them whole: one CU streams such a pair (at most kWholeBytes of digests) in about the
+  // time a piece's hand-over takes.
+  const size_t pair_bytes = (size_t)s.max_blocks * s.d * (s.bf16 ? 2 : 4) * (minmax ? 2 : 1);
+  if (s.max_blocks <= kMaxRows && pairs <= kCUs && pair_bytes <= kWholeBytes)
+    p.whole = pairs;
+  else
+    p.whole = s.max_blocks <= kMaxRows ? pairs / kCUs * kCUs : 0;
   p.split = pairs - p.whole;
   // the other pairs in pieces, about one piece per CU in all
   const int pieces = p.split > 0 ? std::max(1, (kCUs + p.split - 1) / p.split) : 1;

@@ -39,6 +39,9 @@ LAYER_CASES = [
     ("cfg2-scaled", CFG2_S, "mean", {}),
     ("cfg3-scaled-minmax", CFG3_S, "minmax", {}),
     ("cfg5-scaled-mean", CFG5_S, "mean", {}),
+    # pairs too large to take whole (more than 192 KiB of digests each): each cut into pieces
+    # whose top candidates are handed over; mean digests, ragged last block
+    ("bf16-mean-pieces", wk.QWEN3_8B_LAYER.scaled(batch=2, context=30000 + 11), "mean", {}),
     ("cfg5-scaled-minmax", CFG5_S, "minmax", {}),
     ("bf16-g1-d64-bs16", wk.RAGGED.scaled(batch=2, num_q_heads=2, num_kv_heads=2, head_dim=64,
                                           ctx_min=300, ctx_max=900, top_k=12), "mean", {}),
@@ -415,6 +418,16 @@ def test_stream_flags_signal_wait_and_bounded_timeout():
     B.sa_stream_signal(ctr, s)  # counter 4
     s.synchronize()
     assert f[3].item() == 1 and f[0].item() == 4 and f[1].item() == 2
+
+
+def test_step_parity_selection_in_pieces():
+    """The step with pairs large enough that the selection cuts them into pieces (the hand-over
+    of each piece's candidates through device-coherent memory), side stream and host mirrors."""
+    H.log("[case] step, selection in pieces")
+    import harness_step as HS
+    HS.run_step(wk.QWEN3_14B_STEP.scaled(batch=2, num_q_heads=8, num_kv_heads=2, context=26000,
+                                         layers=2, pool_blocks=12, hidden=256, top_k=16),
+                gen_device="cpu", handoff=True, side=True)
 
 
 def test_step_offload_parity_bs64():
