@@ -419,13 +419,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     const uint16_t* src = k_pool + (size_t)page * BS * D + ((size_t)kq * BS + kStep * hh + c16) * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      R.k[ks] = *reinterpret_cast<const uint4*>(src + (size_t)ks * 4 * BS * 8);
+      R.k[ks] = load_stream16(src + (size_t)ks * 4 * BS * 8);
     // V half-page hh is [D][16]: channel 16 cg + c16, tokens 4 kq .. + 3 (8 bytes); the 64
     // lanes of one tile read 512 contiguous bytes
     const uint16_t* vsrc = v_pool + ((size_t)page * HPB + hh) * D * kStep + c16 * kStep + 4 * kq;
 #pragma unroll
     for (int cg = 0; cg < CG; ++cg)
-      R.v[cg] = *reinterpret_cast<const uint2*>(vsrc + (size_t)cg * 16 * kStep);
+      R.v[cg] = load_stream8(vsrc + (size_t)cg * 16 * kStep);
   };
 
   auto compute_step = [&](const StepRegs& R) {
@@ -645,8 +645,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
     for (int i = lane; i < BS * D; i += kWave) {
       // K is chunk-major: element i is channel 4 (i / 4BS) + i % 4 of token (i / 4) % BS;
       // V is [BS/16][D][16]: element i is channel (i / 16) % D of token 16 (i / 16D) + i % 16
-      ks[(i / 4) % BS][4 * (i / (4 * BS)) + i % 4] = k_pool[(size_t)page * BS * D + i];
-      vs[16 * (i / (16 * D)) + i % 16][(i / 16) % D] = v_pool[(size_t)page * BS * D + i];
+      ks[(i / 4) % BS][4 * (i / (4 * BS)) + i % 4] =
+          __builtin_nontemporal_load(k_pool + (size_t)page * BS * D + i);
+      vs[16 * (i / (16 * D)) + i % 16][(i / 16) % D] =
+          __builtin_nontemporal_load(v_pool + (size_t)page * BS * D + i);
     }
     __syncthreads();
     for (int i = lane; i < G * BS; i += kWave) {

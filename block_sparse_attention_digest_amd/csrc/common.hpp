@@ -14,6 +14,19 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));  // four bf16 MFMA op
 
 // ---- bfloat16 <-> float ------------------------------------------------------------------
 // A 32-bit word holds two bf16 values: element 0 in the low half, element 1 in the high half.
+// Loads of data read once per pass (K/V pages, digests), marked non-temporal so that they
+// are kept out of the caches' working set in favour of data that is read again.
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_stream8(const void* p) {
+  typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+  const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
+  return make_uint2(v.x, v.y);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

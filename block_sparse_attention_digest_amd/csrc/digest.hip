@@ -229,8 +229,8 @@ __global__ __launch_bounds__(256) void digest_kernel(const T* __restrict__ k_poo
     for (int cs = 0; cs < CGS; ++cs)
 #pragma unroll
       for (int tg = 0; tg < TG; ++tg)
-        raw[cs][tg] = *reinterpret_cast<const uint4*>(
-            src + ((size_t)(8 * (CGS * slab + cs) + cl) * BS + 8 * tg + tl) * VEC);
+        raw[cs][tg] =
+            load_stream16(src + ((size_t)(8 * (CGS * slab + cs) + cl) * BS + 8 * tg + tl) * VEC);
   };
 
   // the pair of the wave's first block (pairs without blocks are passed over)
@@ -315,8 +315,8 @@ __global__ __launch_bounds__(256) void refresh_kernel(const T* __restrict__ k_po
     for (int cs = 0; cs < CGS; ++cs)
 #pragma unroll
       for (int tg = 0; tg < TG; ++tg)
-        raw[cs][tg] = *reinterpret_cast<const uint4*>(
-            src + ((size_t)(8 * (CGS * sl + cs) + cl) * BS + 8 * tg + tl) * VEC);
+        raw[cs][tg] =
+            load_stream16(src + ((size_t)(8 * (CGS * sl + cs) + cl) * BS + 8 * tg + tl) * VEC);
     digest_block<T, D, BS, MINMAX>(raw, min(BS, len - b * BS), dig,
                                    (long)pair * max_blocks + b, cl, tl, sl);
   }

@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kSelThreads, kSelWavesPerSimd) void select_kernel(
       const int b = max(min(b_first + u * BPI + bi, r1 - 1), 0);
 #pragma unroll
       for (int r = 0; r < LPB; ++r)
-        buf[u * LPB + r] = *reinterpret_cast<const uint4*>(base + (size_t)b * ROW + r * D);
+        buf[u * LPB + r] = load_stream16(base + (size_t)b * ROW + r * D);
     }
   };
   // the first two batches of a wave are fixed; later ones come from next_row
