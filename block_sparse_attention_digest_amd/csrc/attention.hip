@@ -409,11 +409,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     int nval;
   };
   int w_page = 0, w_nval = 0;  // lane j: page and valid tokens of block (window start + j)
-  // Every load is issued unconditionally (rows clamped into the page), so the number of
-  // loads in flight is the same on every path and the compiler waits only for the step
-  // being computed, never for the one in flight.
-  auto load_step = [&](int j, int hh, StepRegs& R) {
-    const int page = __builtin_amdgcn_readlane(w_page, j);
+  // Every load is issued unconditionally, so the number of loads in flight is the same on
+  // every path and the compiler waits only for the step being computed, never for the one
+  // in flight.  The K/V of a step are read once (non-temporal loads); a padding step past a
+  // window's end reads the first step of pool page 0 instead, the same lines for every wave,
+  // so that after the first they come from the cache rather than from HBM.
+  auto load_step = [&](int j, int hh, StepRegs& R, bool pad) {
+    const int page = pad ? 0 : __builtin_amdgcn_readlane(w_page, j);
+    hh = pad ? 0 : hh;
     R.nval = __builtin_amdgcn_readlane(w_nval, j) - kStep * hh;  // valid tokens of the step
     // chunk 4 ks + kq (channels 32 ks + 8 kq .. + 7) of token kStep hh + c16
     const uint16_t* src = k_pool + (size_t)page * BS * D + ((size_t)kq * BS + kStep * hh + c16) * 8;
@@ -499,13 +502,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     return pp;
   };
   // A window's pages and valid-token counts go to lane registers and the loads of its first
-  // two steps are issued.  The steps past the window's end re-read its last step (lines that
-  // are still cached), so every path has the same loads in flight.
+  // two steps are issued.  The steps past the window's end are padding loads (see
+  // load_step), so every path has the same loads in flight.
   StepRegs ra, rb, rc;
   int nw = 1, nst = 1;
   auto ld = [&](int st, StepRegs& R) {
     const int sc = min(st, nst - 1);
-    load_step(sc / HPB, sc % HPB, R);
+    load_step(sc / HPB, sc % HPB, R, st >= nst);
   };
   auto open_window = [&](int wb) {
     nw = max(1, min(kWave, b1 - wb));

@@ -222,8 +222,12 @@ __global__ __launch_bounds__(256) void digest_kernel(const T* __restrict__ k_poo
   if (i0 >= i1) return;
   const int cl = lane / 8, tl = lane % 8;  // chunk within the group, token within the group
 
-  // one slab of a page at once (CGS * TG <= 8 loads of 16 bytes per lane)
-  auto load_slab = [&](int page, int slab, uint4 (&raw)[CGS][TG]) {
+  // one slab of a page at once (CGS * TG <= 8 loads of 16 bytes per lane), read once
+  // (non-temporal loads); the padding load after a window's last slab reads slab 0 of pool
+  // page 0, the same lines for every wave, so that after the first they come from the cache
+  auto load_slab = [&](int page, int slab, uint4 (&raw)[CGS][TG], bool pad) {
+    page = pad ? 0 : page;
+    slab = pad ? 0 : slab;
     const T* src = k_pool + (size_t)page * BS * D;
 #pragma unroll
     for (int cs = 0; cs < CGS; ++cs)
@@ -257,12 +261,12 @@ __global__ __launch_bounds__(256) void digest_kernel(const T* __restrict__ k_poo
     uint64_t mask = __ballot(live);
     if (mask == 0) continue;
     // the slabs of the window's resident blocks in order; the next slab is loaded before
-    // the current one is reduced (past the last, the last is loaded again: cached lines)
+    // the current one is reduced (past the last, a padding load)
     int j = __builtin_ctzll(mask);
     mask &= mask - 1;
     int sl = 0;
     uint4 cur[CGS][TG], nxt[CGS][TG];
-    load_slab(__builtin_amdgcn_readlane(page_l, j), 0, cur);
+    load_slab(__builtin_amdgcn_readlane(page_l, j), 0, cur, false);
     while (true) {
       int jn = j, sn = sl + 1;
       const bool last = sn == SL && !mask;
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(256) void digest_kernel(const T* __restrict__ k_poo
         sn = last ? sl : 0;
         jn = last ? j : __builtin_ctzll(mask);
       }
-      load_slab(__builtin_amdgcn_readlane(page_l, jn), sn, nxt);
+      load_slab(__builtin_amdgcn_readlane(page_l, jn), sn, nxt, last);
       __builtin_amdgcn_sched_barrier(0);
       digest_block<T, D, BS, MINMAX>(cur, __builtin_amdgcn_readlane(nval_l, j), dig,
                                      __builtin_amdgcn_readlane(slot, j), cl, tl, sl);
