@@ -112,6 +112,11 @@ def trace_attention(c, waves_per_wg, check):
             # every pair the range touches gets a partial in slot gw + pair
             if b0 < b1:
                 for pair in range(pair_of(pfx, npairs, b0), pair_of(pfx, npairs, b1 - 1) + 1):
+                    if pfx[pair + 1] <= pfx[pair]:
+                        continue  # (no block of the pair in the range)
+                    written = c.setdefault("written", {})
+                    assert gw + pair not in written, (gw, pair)  # one partial per slot
+                    written[gw + pair] = pair
                     for g in range(G):
                         check("partial_o", ((gw + pair) * G + g) * D + D - 1)
                         check("partial_ml", ((gw + pair) * G + g) * 2 + 1)
@@ -119,12 +124,16 @@ def trace_attention(c, waves_per_wg, check):
 
 def trace_reduce(c, check):
     """reduce_kernel: the covering waves' slots of every row, with the count clamped and the
-    preloaded o vectors' slot index clamped into the covering range."""
+    preloaded o vectors' slot index clamped into the covering range.  Beyond the addresses,
+    the partials it combines (the covering slots of live waves) are exactly those the
+    attention waves wrote for the pair."""
     npairs, stride, G, D, W = c["npairs"], c["stride"], c["G"], c["D"], c["W"]
     pfx = pair_prefix(c["n_gpu"], stride)
     T = pfx[npairs]
     kpre = 16
+    written = c.get("written", {})
     for pair in range(npairs):
+        check("n_gpu", pair)
         ng = clamp(c["n_gpu"][pair], 0, stride)
         w_lo = nslot = 0
         if ng > 0:
@@ -137,6 +146,11 @@ def trace_reduce(c, check):
             for j in range(nslot):  # (m, l) of the covering slots, then their o vectors
                 check("partial_ml", ((w_lo + j + pair) * G + g) * 2 + 1)
                 check("partial_o", ((w_lo + j + pair) * G + g) * D + D - 1)
+        # a covering wave with an empty range (possible when W > T) wrote nothing
+        live = {w_lo + j + pair for j in range(nslot)
+                if W <= T or wave_start(w_lo + j, T, W) < wave_start(w_lo + j + 1, T, W)}
+        want = {slot for slot, p in written.items() if p == pair}
+        assert live == want, (pair, sorted(live), sorted(want))
 
 
 def trace_select(c, check, waves=8, threads=512, batch=8, tbl_run=8):
@@ -234,24 +248,27 @@ def bad_int(rng, lo, hi):
     return rng.randint(hi, 1 << 30)
 
 
-def random_case(rng):
-    Hkv = rng.choice([1, 2, 8])
+def random_case(rng, long_lists=False):
+    """long_lists: few pairs with long, mostly full lists, so that a pair's blocks span
+    more waves than the reduce preloads, both with more waves than blocks and with fewer."""
+    Hkv = rng.choice([1, 2, 8]) if not long_lists else 1
     G = rng.choice([1, 3, 5, 8])
     D = rng.choice([64, 128])
     BS = rng.choice([16, 32, 64])
-    B = rng.randint(1, 6)
-    mb = rng.randint(1, 40)
-    stride = rng.randint(1, 20)
+    B = rng.randint(1, 6) if not long_lists else rng.randint(1, 3)
+    mb = rng.randint(1, 40) if not long_lists else rng.randint(60, 100)
+    stride = rng.randint(1, 20) if not long_lists else rng.randint(40, mb)
     P = rng.randint(1, 60)
     npairs = B * Hkv
     waves_per_wg = 4
-    W = waves_per_wg * rng.randint(1, 12)
+    W = waves_per_wg * rng.randint(1, 12) if not long_lists else waves_per_wg * rng.randint(8, 40)
     c = dict(B=B, Hkv=Hkv, G=G, D=D, BS=BS, max_blocks=mb, stride=stride, P=P, npairs=npairs,
              W=W, k=stride, per=rng.choice([1, 2]), parts=rng.randint(1, 5),
              digest_waves=rng.randint(1, 40), use_pages=rng.random() < 0.5)
     c["row_stride"] = Hkv * G * D
     c["part_stride"] = B * c["row_stride"]
-    c["n_gpu"] = [bad_int(rng, 0, stride + 1) for _ in range(npairs)]
+    c["n_gpu"] = [bad_int(rng, 0, stride + 1) if not long_lists or rng.random() < 0.2
+                  else rng.randint(stride // 2, stride) for _ in range(npairs)]
     c["gpu_blocks"] = [bad_int(rng, -1, mb) for _ in range(npairs * stride)]
     c["gpu_pages"] = [bad_int(rng, -1, P) for _ in range(npairs * stride)]
     c["table"] = [bad_int(rng, -1, P) for _ in range(npairs * mb)]
@@ -280,6 +297,33 @@ def test_kernel_addresses_stay_in_bounds_on_bad_contents():
         trace_select(c, check)
         trace_digest(c, check)
         assert not bad, bad[:5]
+
+
+def test_pairs_spanning_many_waves_stay_in_bounds_and_match():
+    """Long lists: pairs whose blocks span more than 16 waves (the reduce's preload), with
+    more waves than blocks (empty waves among the covering ones) and with fewer."""
+    rng = random.Random(77)
+    bad = []
+    seen = dict(ge=0, lt=0)
+    for trial in range(60):
+        c, sizes, wpg = random_case(rng, long_lists=True)
+        pfx = pair_prefix(c["n_gpu"], c["stride"])
+        T, W = pfx[-1], c["W"]
+        for p in range(c["npairs"]):
+            ng = pfx[p + 1] - pfx[p]
+            if ng and T:
+                n = wave_of(pfx[p] + ng - 1, T, W) - wave_of(pfx[p], T, W) + 1
+                if n > 16:
+                    seen["ge" if W >= T else "lt"] += 1
+
+        def check(buf, i, c=c, trial=trial):
+            if not 0 <= i < sizes[buf]:
+                bad.append((trial, buf, i, sizes[buf]))
+
+        trace_attention(c, wpg, check)
+        trace_reduce(c, check)
+        assert not bad, bad[:5]
+    assert seen["ge"] > 0 and seen["lt"] > 0, seen
 
 
 def test_bad_contents_exercise_the_clamps():
