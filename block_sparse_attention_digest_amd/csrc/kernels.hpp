@@ -47,8 +47,8 @@ inline QParts plain_query(const float* q, int n) { return QParts{q, 1, 0, (size_
 struct GemmPlan {
   int ksplit;        // K slices (equal; k / ksplit is a multiple of 64)
   int kslice;        // columns of K per slice
-  int tpw;           // 16-column tiles per workgroup (divides n_total / 16)
-  int kpw;           // waves per tile, each streaming 1/kpw of the k-slice
+  int tpw;           // 16-column tiles per workgroup and wave (divides n_total / 16)
+  int kpw;           // waves per workgroup, each streaming 1/kpw of the k-slice
   size_t ws_bytes;   // float partials [ksplit][m][n_total] when ksplit > 1
 };
 GemmPlan gemm_plan(int m, int n_total, int k);
