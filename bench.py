@@ -1046,7 +1046,8 @@ def main():
     sbytes = select_bytes(wl, kind)
     sel_step = spread(in_step["select"])
     gemm_step = spread(in_step["gemm"])
-    log(f"selection in the step: {sel_step['median_us']:.1f} us median; query GEMM in the step: "
+    log(f"selection in the step: {sel_step['mean_us']:.1f} us mean (median "
+        f"{sel_step['median_us']:.1f}); query GEMM in the step: "
         f"{gemm_step['median_us']:.1f} us median")
 
     rows = wl.batch * wl.num_q_heads
@@ -1117,12 +1118,14 @@ def main():
         "roofline_select": {
             "kernel": "select_kernel (digest scoring + top-k + resident split), in the step",
             "bound": "hbm",
-            "achieved": round(sbytes / (sel_step["median_us"] * 1e-6) / 1e9, 1),
+            "achieved": round(sbytes / (sel_step["mean_us"] * 1e-6) / 1e9, 1),
             "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(sbytes / (sel_step["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "frac": round(sbytes / (sel_step["mean_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "traffic": sel_traffic, "time": sel_step, "algorithmic_bytes_per_launch": sbytes,
             "measured": f"{n_sel} launches in {args.profile_steps} eager steps, HIP events at "
-                        "each kernel's start and end; median",
+                        "each kernel's start and end; mean (in these eager steps a launch "
+                        "either overlaps the attention beside it, about 80 us, or runs after "
+                        "it, about 40 us, so the median jumps between the two)",
             "shares_hbm_with": "the previous layer's attention on the main stream"},
         "roofline_select_isolated": {
             "kernel": "select_kernel, launched alone (each layer's digests once per pass)",
