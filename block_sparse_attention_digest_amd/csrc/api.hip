@@ -153,6 +153,12 @@ sa_status check_gemm_shape(int32_t m, int32_t n, int32_t k) {
   } while (0)
 #define SA_NOT_NULL(p) \
   do { if (!(p)) return fail(SA_ERR_INVALID_ARG, "%s is NULL", #p); } while (0)
+// buffers the kernels read or write with 16-byte vector accesses
+#define SA_ALIGNED16(p)                                                              \
+  do {                                                                               \
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0)                                    \
+      return fail(SA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p);               \
+  } while (0)
 #define SA_HIP(expr, what)                       \
   do {                                           \
     hipError_t e_ = (expr);                      \
@@ -262,6 +268,8 @@ sa_status sa_pack_k_pages(const sa_dims* dims, const void* k_rows, void* k_pool,
   SA_CHECK(check_dims(dims, &s));
   SA_NOT_NULL(k_rows);
   SA_NOT_NULL(k_pool);
+  SA_ALIGNED16(k_rows);
+  SA_ALIGNED16(k_pool);
   const size_t bytes = (size_t)s.P * s.bs * s.d * (s.bf16 ? 2 : 4);
   const char* a = (const char*)k_rows;
   const char* b = (const char*)k_pool;
@@ -276,6 +284,8 @@ sa_status sa_pack_v_pages(const sa_dims* dims, const void* v_rows, void* v_pool,
   SA_CHECK(check_dims(dims, &s));
   SA_NOT_NULL(v_rows);
   SA_NOT_NULL(v_pool);
+  SA_ALIGNED16(v_rows);
+  SA_ALIGNED16(v_pool);
   const size_t bytes = (size_t)s.P * s.bs * s.d * (s.bf16 ? 2 : 4);
   const char* a = (const char*)v_rows;
   const char* b = (const char*)v_pool;
@@ -291,6 +301,8 @@ sa_status sa_pack_weight(int32_t n, int32_t k, const void* w, void* w_packed,
     return fail(SA_ERR_UNSUPPORTED, "weight n (%d) must be a multiple of 16 and k (%d) of 32", n, k);
   SA_NOT_NULL(w);
   SA_NOT_NULL(w_packed);
+  SA_ALIGNED16(w);
+  SA_ALIGNED16(w_packed);
   const size_t bytes = (size_t)n * k * 2;
   const char* a = (const char*)w;
   const char* b = (const char*)w_packed;
@@ -309,6 +321,8 @@ sa_status sa_build_digests(const sa_dims* dims, sa_digest_kind kind, const void*
   SA_NOT_NULL(block_table);
   SA_NOT_NULL(seq_lens);
   SA_NOT_NULL(digests);
+  SA_ALIGNED16(k_pool);
+  SA_ALIGNED16(digests);
   SA_HIP(sa::launch_build_digests(s, kind == SA_DIGEST_MINMAX, k_pool, block_table, seq_lens,
                                   digests, stream),
          "digest kernel");
@@ -325,6 +339,8 @@ sa_status sa_refresh_last_digests(const sa_dims* dims, sa_digest_kind kind,
   SA_NOT_NULL(block_table);
   SA_NOT_NULL(seq_lens);
   SA_NOT_NULL(digests);
+  SA_ALIGNED16(k_pool);
+  SA_ALIGNED16(digests);
   SA_HIP(sa::launch_refresh_digests(s, kind == SA_DIGEST_MINMAX, k_pool, block_table,
                                     seq_lens, digests, stream),
          "digest refresh kernel");
@@ -344,6 +360,10 @@ sa_status sa_predict_query(int32_t m, int32_t n, int32_t k, const void* x,
   SA_NOT_NULL(w_packed);
   const void* w = w_packed;
   SA_NOT_NULL(q);
+  SA_ALIGNED16(x);
+  SA_ALIGNED16(w_packed);
+  SA_ALIGNED16(q);
+  SA_ALIGNED16(ws);
   const sa::GemmPlan plan = sa::gemm_plan(m, n, k);
   if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes))
     return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, plan.ws_bytes);
@@ -381,6 +401,9 @@ sa_status sa_select_blocks(const sa_dims* dims, sa_digest_kind kind, const float
   SA_NOT_NULL(n_gpu);
   SA_NOT_NULL(cpu_blocks);
   SA_NOT_NULL(n_cpu);
+  SA_ALIGNED16(q);
+  SA_ALIGNED16(digests);
+  SA_ALIGNED16(ws);
   if (top_k < 1 || top_k > s.max_blocks)
     return fail(SA_ERR_INVALID_ARG, "top_k %d outside [1, max_blocks = %d]", top_k, s.max_blocks);
   const Layout L = layout(s, top_k);
@@ -414,6 +437,10 @@ static sa_status decode_common(const sa_dims* dims, const float* q, const void* 
   SA_NOT_NULL(n_gpu);
   SA_NOT_NULL(o);
   SA_CHECK(check_scale(scale));
+  SA_ALIGNED16(q);
+  SA_ALIGNED16(k_pool);
+  SA_ALIGNED16(v_pool);
+  SA_ALIGNED16(ws);
   if (list_stride < 1 || list_stride > s.max_blocks)
     return fail(SA_ERR_INVALID_ARG, "list_stride %d outside [1, max_blocks = %d]", list_stride,
                 s.max_blocks);
@@ -532,6 +559,10 @@ sa_status sa_dense_decode(const sa_dims* dims, const float* q, const void* k_poo
   SA_NOT_NULL(block_table);
   SA_NOT_NULL(seq_lens);
   SA_NOT_NULL(o);
+  SA_ALIGNED16(q);
+  SA_ALIGNED16(k_pool);
+  SA_ALIGNED16(v_pool);
+  SA_ALIGNED16(ws);
   const size_t need = sa_dense_workspace_bytes(dims);
   if (!ws || ws_bytes < need)
     return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
@@ -597,6 +628,11 @@ sa_status sa_recall_blocks(const sa_dims* dims, int32_t list_stride, int32_t max
   SA_NOT_NULL(k_pool);
   SA_NOT_NULL(v_pool);
   SA_NOT_NULL(n_recalled);
+  SA_ALIGNED16(k_host);
+  SA_ALIGNED16(v_host);
+  SA_ALIGNED16(k_pool);
+  SA_ALIGNED16(v_pool);
+  SA_ALIGNED16(ws);
   const size_t need = sa_recall_workspace_bytes(dims, max_recall);
   if (!ws || ws_bytes < need)
     return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
@@ -975,6 +1011,10 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
     if (!L.x || !L.w_q || !L.digests || !L.block_table || !L.k_pool || !L.v_pool ||
         !L.gpu_blocks || !L.n_gpu || !L.cpu_blocks || !L.n_cpu || !L.out_o)
       return fail(SA_ERR_INVALID_ARG, "layer %d: a required pointer is NULL", i);
+    for (const void* v : {L.x, L.w_q, L.digests, L.k_pool, L.v_pool})
+      if (reinterpret_cast<uintptr_t>(v) % 16 != 0)
+        return fail(SA_ERR_INVALID_ARG,
+                    "layer %d: x, w_q, digests, k_pool and v_pool must be 16-byte aligned", i);
     if (plan) continue;  // the plan's host buffers take the place of the rest
     if (!L.host_o || !L.host_m || !L.host_l)
       return fail(SA_ERR_INVALID_ARG, "layer %d: a host partial pointer is NULL", i);
@@ -1013,6 +1053,7 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
   const StepLayout SL = step_layout(s, hidden, top_k);
   if (!ws || ws_bytes < SL.total)
     return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, SL.total);
+  SA_ALIGNED16(ws);
 
   char* base = (char*)ws;
   float* q_true = (float*)(base + SL.q_true);

@@ -28,6 +28,12 @@
  *     described here.
  *   - Layouts are row-major, innermost index last.  "KV dtype" is sa_dims.kv_dtype:
  *     SA_F32 (float) or SA_BF16 (bfloat16 bit patterns, uint16).
+ *   - Alignment: every buffer is aligned to its element size, and the buffers the kernels
+ *     move with 16-byte accesses to 16 bytes: the K/V pages and rows (k_pool, v_pool,
+ *     k_rows, v_rows, k_host, v_host), digests, the GEMM's x, w and w_packed, the query q
+ *     of the GEMM, selection and attention calls, and every workspace `ws`.  (hipMalloc and
+ *     PyTorch allocations are 256-byte aligned.)  A call given one of these at another
+ *     address returns SA_ERR_INVALID_ARG.
  *
  * Shapes: B sequences; Hq query heads; Hkv KV heads with G = Hq / Hkv query heads per KV
  * head (query head g uses KV head g / G); head dimension d; block size bs; P pages in the
