@@ -511,6 +511,53 @@ def pin_sparse_equals_attention_over_selection():
     assert len(r.cpu_blocks) == 0 and len(r.gpu_blocks) == k
 
 
+def pin_split_partials_indicator_hand():
+    """The GPU partial covers exactly the resident selected blocks and the host partial the
+    offloaded ones (Algorithm 1: A_gpu over B_gpu, A_cpu over B_cpu; R6).  Hand case with
+    zero keys, so every attended token has logit 0 and weight 1: then m = 0, l = the number
+    of attended tokens, and o = the mean of their values.  Values are one-hot per block
+    (block b's rows all e_b), so o[b] = (tokens of b attended) / l, which shows which blocks
+    each partial read.  Six blocks of 4 tokens, the last one 3 tokens long (T = 23); digests
+    chosen so that the selecting query picks blocks 5, 1, 3, 4 (k = 4); blocks 1, 4 and 2
+    resident.  Selection uses the selecting query, attention the other (Algorithm 1)."""
+    bs, T, nb = 4, 23, 6
+    K = np.zeros((T, nb))
+    V = np.zeros((T, nb))
+    for b in range(nb):
+        V[b * bs:min((b + 1) * bs, T), b] = 1.0
+    q = np.ones((1, nb))
+    dig = np.array([[0.0] * nb, [5.0] + [0.0] * (nb - 1), [1.0] + [0.0] * (nb - 1),
+                    [4.0] + [0.0] * (nb - 1), [3.0] + [0.0] * (nb - 1),
+                    [9.0] + [0.0] * (nb - 1)])   # scores 0, 5, 1, 4, 3, 9
+    res = np.array([False, True, True, False, True, False])
+    # the attention query differs from the selecting one (it would pick the lowest scores);
+    # with zero keys it does not change any partial
+    r = so.forward_pair(q, -q, K, V, T, bs, dig, "mean", 4, res, 1.0)
+    assert sorted(r.selected.tolist()) == [1, 3, 4, 5]
+    assert r.gpu_blocks.tolist() == [1, 4] and r.cpu_blocks.tolist() == [3, 5]
+    g, h, o = r.gpu[0], r.host[0], r.out[0]
+    assert g.m == 0.0 and g.l == 8.0                       # blocks 1 and 4: 4 + 4 tokens
+    assert np.array_equal(g.o, [0, 0.5, 0, 0, 0.5, 0])
+    assert h.m == 0.0 and h.l == 7.0                       # blocks 3 and 5: 4 + 3 tokens
+    _close(h.o, [0, 0, 0, 4 / 7, 0, 3 / 7], 1e-15, "host partial")
+    assert o.m == 0.0 and o.l == 15.0                      # the union: 15 tokens
+    _close(o.o, [0, 4 / 15, 0, 4 / 15, 4 / 15, 3 / 15], 1e-15, "merged")
+
+
+def pin_dense_attention_indicator_hand():
+    """FullKV over the first seq_len tokens: with zero keys and one-hot values per token
+    position group, o is the token-count share of each group and l = seq_len (HTML Sec. 4,
+    the FullKV baseline).  T = 10 tokens, groups of 3 (the last group 1 token)."""
+    T, d = 10, 4
+    K = np.zeros((12, d))
+    V = np.zeros((12, d))
+    for t in range(12):
+        V[t, t // 3] = 1.0
+    p = so.dense_attention(np.ones(d), K, V, T, 1.0)
+    assert p.m == 0.0 and p.l == 10.0
+    _close(p.o, [0.3, 0.3, 0.3, 0.1], 1e-15, "dense indicator")
+
+
 def pin_layer_ahead_selection_hand():
     """Algorithm 1: layer 1 selects with Q_pred^1 = W_Q^1 X^0, not with its own Q^1, and
     attends with Q^1; layer 0 selects with Q^0.  Hand case: hidden = d = 2, one head,

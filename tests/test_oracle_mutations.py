@@ -218,7 +218,99 @@ def _step_always_mean(layers, s, h, group, head_dim, block_size, top_k, scale, k
                                      "mean")
 
 
+def _block_view_drops_tail(K, seq_len, block_size):
+    full, _ = _orig["_block_view"](K, seq_len, block_size)
+    return full, None
+
+
+def _block_view_tail_one_short(K, seq_len, block_size):
+    full, tail = _orig["_block_view"](K, seq_len, block_size)
+    return full, (tail[:-1] if tail is not None and len(tail) > 1 else tail)
+
+
+def _gather_tokens_first_only(X, blocks, seq_len, block_size):
+    return _orig["gather_tokens"](X, list(blocks)[:1], seq_len, block_size)
+
+
+def _gather_tokens_drop_last_row(X, blocks, seq_len, block_size):
+    rows = _orig["gather_tokens"](X, blocks, seq_len, block_size)
+    return rows[:-1] if len(rows) > 1 else rows
+
+
+def _attend_blocks_by_position(q, K, V, blocks, seq_len, block_size, scale):
+    # attends the first len(blocks) blocks instead of the listed ones
+    return _orig["attend_blocks"](q, K, V, list(range(len(list(blocks)))), seq_len, block_size,
+                                  scale)
+
+
+def _select_pair_swaps_split(q_sel_group, digest, kind, top_k, resident):
+    sigma, sel, g, c = _orig["select_pair"](q_sel_group, digest, kind, top_k, resident)
+    return sigma, sel, c, g
+
+
+def _select_pair_unsorted_scores(q_sel_group, digest, kind, top_k, resident):
+    sigma, sel, g, c = _orig["select_pair"](q_sel_group, digest, kind, top_k, resident)
+    return sigma[::-1].copy(), sel, g, c
+
+
+def _attend_selection_no_host(q_att_group, K, V, seq_len, block_size, sigma, selected,
+                              resident, scale, host=None):
+    r = _orig["attend_selection"](q_att_group, K, V, seq_len, block_size, sigma, selected,
+                                  resident, scale, host)
+    r.out = list(r.gpu)
+    return r
+
+
+def _attend_selection_all_on_gpu(q_att_group, K, V, seq_len, block_size, sigma, selected,
+                                 resident, scale, host=None):
+    every = np.ones(len(np.asarray(resident)), dtype=bool)
+    return _orig["attend_selection"](q_att_group, K, V, seq_len, block_size, sigma, selected,
+                                     every, scale, host)
+
+
+def _dense_one_token_short(q, K, V, seq_len, scale):
+    return _orig["dense_attention"](q, K, V, max(1, seq_len - 1), scale)
+
+
+def _empty_partial_zero_max(d):
+    return so.Partial(np.zeros(d, dtype=np.float64), 0.0, 0.0)
+
+
+def _forward_pair_selects_with_q_att(q_sel_group, q_att_group, K, V, seq_len, block_size,
+                                     digest, kind, top_k, resident, scale, host=None):
+    return _orig["forward_pair"](q_att_group, q_att_group, K, V, seq_len, block_size, digest,
+                                 kind, top_k, resident, scale, host)
+
+
+def _num_blocks_floor(seq_len, block_size):
+    return int(seq_len) // int(block_size)
+
+
+def _recall_due_at_or_above(n_cpu_per_pair, top_k, beta):
+    n = np.asarray(n_cpu_per_pair, dtype=np.int64)
+    return float(n.sum()) / (len(n) * top_k) >= beta
+
+
+def _recall_due_per_pair_max(n_cpu_per_pair, top_k, beta):
+    return float(np.max(np.asarray(n_cpu_per_pair))) / top_k > beta
+
+
 MUTATIONS = {
+    "empty partial has running max 0": ("empty_partial", _empty_partial_zero_max),
+    "one layer selects with the attention query": ("forward_pair", _forward_pair_selects_with_q_att),
+    "block count rounds down": ("num_blocks", _num_blocks_floor),
+    "recall due at the threshold itself": ("recall_due", _recall_due_at_or_above),
+    "recall due on the worst pair's share": ("recall_due", _recall_due_per_pair_max),
+    "block view drops the partial last block": ("_block_view", _block_view_drops_tail),
+    "block view's partial last block one token short": ("_block_view", _block_view_tail_one_short),
+    "gathered tokens of the first block only": ("gather_tokens", _gather_tokens_first_only),
+    "gathered tokens miss the last row": ("gather_tokens", _gather_tokens_drop_last_row),
+    "blocks attended by list position": ("attend_blocks", _attend_blocks_by_position),
+    "selection returns the split swapped": ("select_pair", _select_pair_swaps_split),
+    "selection returns the scores reversed": ("select_pair", _select_pair_unsorted_scores),
+    "attention of a selection drops the host partial": ("attend_selection", _attend_selection_no_host),
+    "attention of a selection ignores residency": ("attend_selection", _attend_selection_all_on_gpu),
+    "dense attention one token short": ("dense_attention", _dense_one_token_short),
     "bf16 double rounding via f32": ("round_to_bf16", _bf16_via_f32),
     "bf16 ties away from zero": ("round_to_bf16", _bf16_ties_away),
     "Q_pred transposed operand": ("predict_query", _qpred_transposed),
