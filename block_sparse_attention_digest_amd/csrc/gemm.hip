@@ -8,8 +8,9 @@
 // an x operand (the v_mfma_f32_16x16x32_bf16 A operand: 16 rows x 32 k-values, 16 bytes a
 // lane) is loaded once per wave and used for every tile.  Both operands go straight from
 // memory into registers -- x rows as A operands, W (packed by launch_pack_w: the B operand
-// of one tile and one 32-wide k-step is a contiguous kilobyte) as B operands -- three k-steps
-// ahead of the matrix cores, so no wave waits for another before its first product.  The
+// of one tile and one 32-wide k-step is a contiguous kilobyte) as B operands -- five k-steps
+// (four with 64 rows) ahead of the matrix cores, so no wave waits for another before its
+// first product.  The
 // kpw parts of each tile are then summed in LDS in part order, and each workgroup writes
 // its slice's float32 partial.  The partials are summed in slice order -- by a second kernel
 // in the stand-alone call, by the kernels that read the query in the decode step -- so
