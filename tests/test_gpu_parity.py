@@ -162,7 +162,8 @@ def test_pack_weight_layout(n, k):
 
 @pytest.mark.parametrize("m,n,k", [(1, 64, 64), (8, 4096, 4096), (40, 5120, 5120),
                                    (65, 256, 320), (256, 128, 1024), (40, 320, 640),
-                                   (3, 960, 192), (17, 192, 8192)])
+                                   (3, 960, 192), (17, 192, 8192), (64, 5120, 5120),
+                                   (256, 640, 2560)])
 def test_predict_query_parity(m, n, k):
     H.log(f"[case] gemm {m}x{n}x{k}")
     g = torch.Generator().manual_seed(m * 7 + n + k)
