@@ -3,20 +3,22 @@
 // skinny GEMM q[m][n] = x[m][k] . w[n][k]^T with bf16 operands and float32 accumulation.
 //
 // m is the batch (8..40 rows), so the product is bound by streaming W from memory, not by
-// the matrix cores.  A workgroup owns tpw 16-column tiles and one k-slice; its kpw waves
-// split the k-slice into kpw parts, and each wave multiplies its part for all tpw tiles, so
+// the matrix cores.  A workgroup owns TPW 16-column tiles and one k-slice; its kpw waves
+// split the k-slice into kpw parts, and each wave multiplies its part for all TPW tiles, so
 // an x operand (the v_mfma_f32_16x16x32_bf16 A operand: 16 rows x 32 k-values, 16 bytes a
 // lane) is loaded once per wave and used for every tile.  Both operands go straight from
 // memory into registers -- x rows as A operands, W (packed by launch_pack_w: the B operand
 // of one tile and one 32-wide k-step is a contiguous kilobyte) as B operands -- five k-steps
 // (four with 64 rows) ahead of the matrix cores, so no wave waits for another before its
-// first product.  The
-// kpw parts of each tile are then summed in LDS in part order, and each workgroup writes
-// its slice's float32 partial.  The partials are summed in slice order -- by a second kernel
-// in the stand-alone call, by the kernels that read the query in the decode step -- so
-// results are deterministic.  The plan sizes the grid to about one workgroup per CU, so the
-// whole product is one round of short-lived waves.  Two weight matrices that share x (Q^i
-// and Q_pred^{i+1}) can run as one launch.
+// first product.  The tile count is a template parameter, so the product loop has no
+// branches.  At the end each wave writes its part of the workgroup's output block
+// row-major into LDS; the parts are summed in part order, and the workgroup stores its
+// block (its slice's float32 partial) as whole rows of float4.  The partials are summed in
+// slice order -- by a second kernel in the stand-alone call, by the kernels that read the
+// query in the decode step -- so results are deterministic.  The plan sizes the grid to
+// about one workgroup of four waves per CU, so the whole product is one round of
+// short-lived waves, one per SIMD.  Two weight matrices that share x (Q^i and
+// Q_pred^{i+1}) can run as one launch.
 #include <hip/hip_ext.h>
 
 #include <algorithm>
@@ -27,29 +29,37 @@
 namespace sa {
 namespace {
 
-// waves per workgroup: small workgroups leave room on every CU for an attention or
-// selection workgroup running beside them
-constexpr int kMaxWpg = 5;
+// waves per workgroup: one per SIMD of a CU; small workgroups also leave room on every CU
+// for an attention or selection workgroup running beside them.  The kernel is built for two
+// waves per SIMD (at most 256 registers a wave): with more, the compiler keeps values in the
+// accumulation registers and copies them inside the product loop.
+constexpr int kMaxWpg = 4;
 constexpr int kMaxTpw = 5;           // 16-column tiles per workgroup (and per wave)
 constexpr int kCUs = 256;
 
-template <int MT>
-__global__ __launch_bounds__(kMaxWpg * kWave) void gemm_kernel(const uint16_t* __restrict__ x,
+// floats per row of a wave's part in LDS: the block's 16 TPW columns and 4 more, so the four
+// row quads a store instruction writes fall in different banks
+constexpr int red_stride(int tpw) { return 16 * tpw + 4; }
+
+template <int MT, int TPW>
+__global__ __launch_bounds__(kMaxWpg * kWave, 2) void gemm_kernel(const uint16_t* __restrict__ x,
                                                     const uint16_t* __restrict__ w0,
                                                     const uint16_t* __restrict__ w1, int m,
                                                     int n, int k, int kslice, int tiles,
-                                                    int tpw, float* __restrict__ out0,
+                                                    float* __restrict__ out0,
                                                     float* __restrict__ out1, int ksplit,
                                                     float* __restrict__ partials) {
-  extern __shared__ floatx4 red[];  // [kpw][tpw][MT][64 lanes]: every part's sums
+  extern __shared__ float4 red4[];  // [kpw][16 MT][RS] floats: every part's sums, row-major
+  constexpr int RS = red_stride(TPW);
   const int lane = threadIdx.x % kWave;
   const int kpw = blockDim.x / kWave;  // waves per workgroup: the parts of the k-slice
-  const int kpart = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // scalar branches
-  const int groups = tiles / tpw;
+  const int kpart = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int groups = tiles / TPW;
   const int ks = blockIdx.x / groups;        // the k-slice
-  const int tile0 = (blockIdx.x % groups) * tpw;
+  const int tile0 = (blockIdx.x % groups) * TPW;
   const int n_total = tiles * 16;
   const int row0 = blockIdx.y * 16 * MT;
+  const int mr = min(16 * MT, m - row0);     // rows of this row group
   const int nsteps = kslice / 32 / kpw;      // this wave's k-steps
   const int kk0 = ks * kslice + kpart * nsteps * 32;  // its first k
 
@@ -61,31 +71,31 @@ __global__ __launch_bounds__(kMaxWpg * kWave) void gemm_kernel(const uint16_t* _
   for (int t = 0; t < MT; ++t)
     xa[t] = x + (size_t)min(row0 + 16 * t + lane % 16, m - 1) * k + kk0 + 8 * (lane / 16);
   // B operand of tile tt, k-step s: the packed kilobyte (tile, k-step), lane l's 8 values
-  const uint16_t* wb[kMaxTpw];
+  const uint16_t* wb[TPW];
 #pragma unroll
-  for (int tt = 0; tt < kMaxTpw; ++tt) {
-    const int tile = tile0 + min(tt, tpw - 1);
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int tile = tile0 + tt;
     const int prob = tile * 16 >= n ? 1 : 0;  // (16 | n: the same for the tile's columns)
     const uint16_t* w = prob ? w1 : w0;
     wb[tt] = w + ((size_t)(tile - prob * n / 16) * (k / 32) + kk0 / 32) * 512 + lane * 8;
   }
 
-  floatx4 acc[kMaxTpw][MT];
+  floatx4 acc[TPW][MT];
 #pragma unroll
-  for (int tt = 0; tt < kMaxTpw; ++tt)
+  for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[tt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // kAhead register sets rotate, each holding one k-step's operands; a set is refilled
   // right after it is multiplied, while the k-steps of the other sets are in flight.  Loads
-  // are unconditional (k-steps past the part clamp to its last step, tiles past tpw to the
-  // last tile; the B operands of such steps are zeroed), so the loop has the same loads in
-  // flight on every path and the compiler waits only for the set being multiplied; the
-  // scheduling barriers keep it from sinking loads.  The last round issues no loads.
+  // are unconditional (k-steps past the part clamp to its last step; the B operands of such
+  // steps are zeroed), so the loop has the same loads in flight on every path and the
+  // compiler waits only for the set being multiplied; the scheduling barriers keep it from
+  // sinking loads.  The last round issues no loads.
   constexpr int kAhead = MT >= 4 ? 4 : 5;
   struct Set {
     uint4 a[MT];
-    uint4 b[kMaxTpw];
+    uint4 b[TPW];
   };
   Set rs[kAhead];
   auto load = [&](Set& r, int st) {
@@ -93,13 +103,11 @@ __global__ __launch_bounds__(kMaxWpg * kWave) void gemm_kernel(const uint16_t* _
 #pragma unroll
     for (int t = 0; t < MT; ++t) r.a[t] = *reinterpret_cast<const uint4*>(xa[t] + 32 * sc);
 #pragma unroll
-    for (int tt = 0; tt < kMaxTpw; ++tt)
-      r.b[tt] = *reinterpret_cast<const uint4*>(wb[tt] + 512 * sc);
+    for (int tt = 0; tt < TPW; ++tt) r.b[tt] = *reinterpret_cast<const uint4*>(wb[tt] + 512 * sc);
   };
   auto mma = [&](const Set& r, int st) {
 #pragma unroll
-    for (int tt = 0; tt < kMaxTpw; ++tt) {
-      if (tt >= tpw) continue;  // (uniform)
+    for (int tt = 0; tt < TPW; ++tt) {
       const uint4 bw = st < nsteps ? r.b[tt] : make_uint4(0, 0, 0, 0);
       const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
 #pragma unroll
@@ -124,47 +132,36 @@ __global__ __launch_bounds__(kMaxWpg * kWave) void gemm_kernel(const uint16_t* _
   for (int u = 0; u < kAhead; ++u)
     if (s0 + u < nsteps) mma(rs[u], s0 + u);  // (uniform)
 
-  // sum the kpw parts of each tile in LDS, in part order (deterministic); wave w then writes
-  // the tiles w, w + kpw, ...
-  if (kpw > 1) {
+  // acc[tt][t][r] holds row 16t + 4 (lane / 16) + r of the block, column 16 tt + lane % 16:
+  // the wave writes its part row-major, every row (rows past mr hold sums of the repeated
+  // last row and are never read; writing them keeps the stores unpredicated)
+  float* red = reinterpret_cast<float*>(red4);
+  float* mine = red + (size_t)kpart * 16 * MT * RS;
 #pragma unroll
-    for (int tt = 0; tt < kMaxTpw; ++tt) {
-      if (tt >= tpw) continue;  // (uniform)
+  for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-      for (int t = 0; t < MT; ++t) red[((kpart * tpw + tt) * MT + t) * kWave + lane] = acc[tt][t];
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        mine[(16 * t + 4 * (lane / 16) + r) * RS + 16 * tt + lane % 16] = acc[tt][t][r];
+  __syncthreads();
+  // the block, mr rows x 4 TPW float4: each sums the kpw parts in part order (deterministic)
+  // and stores whole rows
+  const int units = mr * 4 * TPW;
+  for (int u = threadIdx.x; u < units; u += blockDim.x) {
+    const int row = u / (4 * TPW), c4 = u % (4 * TPW);
+    float4 s = red4[(row * RS) / 4 + c4];
+    for (int p = 1; p < kpw; ++p) {
+      const float4 v = red4[((p * 16 * MT + row) * RS) / 4 + c4];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
     }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int tt = 0; tt < kMaxTpw; ++tt) {
-    if (tt >= tpw || tt % kpw != kpart) continue;  // (uniform)
-    floatx4 sum[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) sum[t] = acc[tt][t];
-    if (kpw > 1) {
-#pragma unroll
-      for (int t = 0; t < MT; ++t) sum[t] = red[(tt * MT + t) * kWave + lane];
-      for (int p = 1; p < kpw; ++p)
-#pragma unroll
-        for (int t = 0; t < MT; ++t) sum[t] += red[((p * tpw + tt) * MT + t) * kWave + lane];
-    }
-    // sum[t][r] holds row row0 + 16t + 4 (lane / 16) + r, column (tile0 + tt) * 16 + lane % 16
-    const int col_g = (tile0 + tt) * 16 + lane % 16;  // in [0, n_total)
-    const int prob = col_g >= n ? 1 : 0;
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = row0 + 16 * t + 4 * (lane / 16) + r;
-        if (row < m) {
-          if (ksplit == 1) {
-            float* out = prob ? out1 : out0;
-            out[(size_t)row * n + col_g - prob * n] = sum[t][r];
-          } else {
-            partials[((size_t)ks * m + row) * n_total + col_g] = sum[t][r];
-          }
-        }
-      }
+    const int col_g = tile0 * 16 + 4 * c4;  // in [0, n_total); a float4 stays in one tile
+    if (ksplit == 1) {
+      const int prob = col_g >= n ? 1 : 0;
+      float* out = prob ? out1 : out0;
+      *reinterpret_cast<float4*>(out + (size_t)(row0 + row) * n + col_g - prob * n) = s;
+    } else {
+      *reinterpret_cast<float4*>(partials + ((size_t)ks * m + row0 + row) * n_total + col_g) = s;
     }
   }
 }
@@ -245,24 +242,34 @@ hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void
   const int n_total = n * nprob;
   const int mt = row_tiles(m);
   const int tiles = n_total / 16;
-  const dim3 grid(tiles / plan.tpw * plan.ksplit, (m + 63) / 64);
+  const dim3 grid(tiles / plan.tpw * plan.ksplit, (m + 16 * mt - 1) / (16 * mt));
   const dim3 block(plan.kpw * kWave);
-  const size_t lds = plan.kpw > 1 ? (size_t)plan.kpw * plan.tpw * mt * kWave * 16 : 0;
+  // every wave's part of the block, all 16 mt rows
+  const size_t lds = (size_t)plan.kpw * 16 * mt * red_stride(plan.tpw) * sizeof(float);
   const uint16_t* X = (const uint16_t*)x;
   const uint16_t* W0 = (const uint16_t*)w0;
   const uint16_t* W1 = (const uint16_t*)(nprob > 1 ? w1 : w0);
   float* Q1 = nprob > 1 ? q1 : q0;
   // hipExtLaunchKernelGGL records the (optional) events at the kernel's own start and end
-#define SA_GEMM_CASE(MT)                                                                    \
-  case MT:                                                                                  \
-    hipExtLaunchKernelGGL(gemm_kernel<MT>, grid, block, lds, stream, ev_start, ev_stop, 0,  \
-                          X, W0, W1, m, n, k, plan.kslice, tiles, plan.tpw, q0, Q1,         \
-                          plan.ksplit, ws);                                                 \
-    break;
-  switch (mt) {
-    SA_GEMM_CASE(1) SA_GEMM_CASE(2) SA_GEMM_CASE(3) default: SA_GEMM_CASE(4)
+#define SA_GEMM_LAUNCH(MT, TPW)                                                             \
+  hipExtLaunchKernelGGL((gemm_kernel<MT, TPW>), grid, block, lds, stream, ev_start, ev_stop, \
+                        0, X, W0, W1, m, n, k, plan.kslice, tiles, q0, Q1, plan.ksplit, ws)
+#define SA_GEMM_TPW(MT)                                       \
+  switch (plan.tpw) {                                         \
+    case 1: SA_GEMM_LAUNCH(MT, 1); break;                     \
+    case 2: SA_GEMM_LAUNCH(MT, 2); break;                     \
+    case 3: SA_GEMM_LAUNCH(MT, 3); break;                     \
+    case 4: SA_GEMM_LAUNCH(MT, 4); break;                     \
+    default: SA_GEMM_LAUNCH(MT, 5); break;                    \
   }
-#undef SA_GEMM_CASE
+  switch (mt) {
+    case 1: SA_GEMM_TPW(1) break;
+    case 2: SA_GEMM_TPW(2) break;
+    case 3: SA_GEMM_TPW(3) break;
+    default: SA_GEMM_TPW(4) break;
+  }
+#undef SA_GEMM_TPW
+#undef SA_GEMM_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.ksplit == 1 || !sum_slices) return e;
   const long total4 = (long)m * n_total / 4;
