@@ -207,11 +207,11 @@ GemmPlan gemm_plan(int m, int n_total, int k) {
   const int tiles = n_total / 16;
   const int ksteps64 = k / 64;
   const int row_groups = (m + 63) / 64;
-  // tiles per workgroup: the largest divisor of the tile count up to kMaxTpw
-  int tpw = 1;
-  for (int v = 1; v <= kMaxTpw; ++v)
-    if (tiles % v == 0) tpw = v;
-  const int groups = tiles / tpw;
+  // tiles per workgroup: 5 when they divide the tile count, else 4 (the entry points take
+  // n % 64 == 0, so the tile count is a multiple of 4; any other count gets tpw = 0, which
+  // launch_gemm refuses)
+  const int tpw = tiles % kMaxTpw == 0 ? kMaxTpw : tiles % 4 == 0 ? 4 : 0;
+  const int groups = tpw ? tiles / tpw : 1;
   // fewest k-slices (a divisor of k/64, so slices are equal) that give about one workgroup
   // per CU, and at most kMaxSplit of them (the consumers sum the slices' partials)
   constexpr int kMaxSplit = 16;
@@ -240,6 +240,7 @@ hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void
                        hipStream_t stream, bool sum_slices, hipEvent_t ev_start,
                        hipEvent_t ev_stop) {
   const int n_total = n * nprob;
+  if (plan.tpw != 4 && plan.tpw != kMaxTpw) return hipErrorInvalidValue;
   const int mt = row_tiles(m);
   const int tiles = n_total / 16;
   const dim3 grid(tiles / plan.tpw * plan.ksplit, (m + 16 * mt - 1) / (16 * mt));
@@ -254,13 +255,11 @@ hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void
 #define SA_GEMM_LAUNCH(MT, TPW)                                                             \
   hipExtLaunchKernelGGL((gemm_kernel<MT, TPW>), grid, block, lds, stream, ev_start, ev_stop, \
                         0, X, W0, W1, m, n, k, plan.kslice, tiles, q0, Q1, plan.ksplit, ws)
-#define SA_GEMM_TPW(MT)                                       \
-  switch (plan.tpw) {                                         \
-    case 1: SA_GEMM_LAUNCH(MT, 1); break;                     \
-    case 2: SA_GEMM_LAUNCH(MT, 2); break;                     \
-    case 3: SA_GEMM_LAUNCH(MT, 3); break;                     \
-    case 4: SA_GEMM_LAUNCH(MT, 4); break;                     \
-    default: SA_GEMM_LAUNCH(MT, 5); break;                    \
+#define SA_GEMM_TPW(MT)    \
+  if (plan.tpw == 4) {     \
+    SA_GEMM_LAUNCH(MT, 4); \
+  } else {                 \
+    SA_GEMM_LAUNCH(MT, 5); \
   }
   switch (mt) {
     case 1: SA_GEMM_TPW(1) break;

@@ -177,6 +177,25 @@ def test_predict_query_parity(m, n, k):
     assert err <= H.TOL_GEMM, err
 
 
+def test_predict_query_shared_workspace():
+    """One workspace, sized for the largest, serves GEMMs of several shapes in a row (k-split
+    or not, the same shape again): every result matches the oracle, so nothing a call leaves
+    in the workspace changes the next one's result."""
+    shapes = [(40, 5120, 5120), (8, 4096, 4096), (1, 64, 64), (256, 640, 2560),
+              (40, 5120, 5120), (17, 192, 8192), (3, 960, 192), (40, 5120, 5120)]
+    ws = B.workspace(max(B.sa_predict_query_workspace_bytes(*s) for s in shapes))
+    for i, (m, n, k) in enumerate(shapes):
+        H.log(f"[case] shared workspace gemm {m}x{n}x{k} (call {i})")
+        g = torch.Generator().manual_seed(1000 + i)
+        X = torch.randn(m, k, generator=g).to(torch.bfloat16)
+        W = (torch.randn(n, k, generator=g) / math.sqrt(k)).to(torch.bfloat16)
+        want = so.predict_query(wk.f64(X), wk.f64(W))
+        q = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+        B.sa_predict_query(X.cuda(), B.pack_weight(W.cuda()), q, ws)
+        err = float(np.max(np.abs(q.cpu().double().numpy() - want)))
+        assert err <= H.TOL_GEMM, (m, n, k, err)
+
+
 @pytest.mark.parametrize("kind,kv,d,bs", [("mean", "bf16", 128, 32), ("minmax", "bf16", 64, 16),
                                           ("mean", "f32", 64, 16), ("minmax", "f32", 128, 32),
                                           ("mean", "bf16", 128, 64), ("minmax", "bf16", 64, 64),
