@@ -1121,7 +1121,8 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
     return SA_OK;
   };
   sa_status st = SA_OK;
-  hipEvent_t sel_done = nullptr;  // side stream: the selection of the coming layer is done
+  hipEvent_t sel_done = nullptr;  // side stream: the selection of this layer is done
+  hipEvent_t sel_next = nullptr;  // ... and of the coming layer
   for (int i = 0; i < num_layers && st == SA_OK; ++i) {
     const sa_layer& L = layers[i];
     const bool has_next = i + 1 < num_layers;
@@ -1182,6 +1183,13 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
                         N.gpu_blocks, N.n_gpu, N.cpu_blocks, N.n_cpu, nullptr,
                         mirror_blocks(i + 1), mirror_n(i + 1), pages[(i + 1) & 1], sel_ws,
                         sel_stream);
+      // the next layer's attention needs its lists only: the event is recorded before the
+      // host hand-off (query gather, signal), which then runs beside this layer's attention
+      if (st == SA_OK && side_stream) {
+        st = new_event(&sel_next);
+        if (st == SA_OK && hipEventRecord(sel_next, side_stream) != hipSuccess)
+          st = fail(SA_ERR_HIP, "hipEventRecord failed");
+      }
       if (st == SA_OK && plan) st = spawn_host(i + 1, q_next, sel_stream);
       if (st != SA_OK) break;
     }
@@ -1190,12 +1198,7 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
       st = fail(SA_ERR_HIP, "hipStreamWaitEvent failed");
       break;
     }
-    if (has_next && side_stream) {
-      st = new_event(&sel_done);
-      if (st == SA_OK && hipEventRecord(sel_done, side_stream) != hipSuccess)
-        st = fail(SA_ERR_HIP, "hipEventRecord failed");
-      if (st != SA_OK) break;
-    }
+    sel_done = sel_next;
     // 5. GPU attention of layer i, merged with its host partial
     hipEvent_t e0, e1;
     next_profile_events(&e0, &e1);
