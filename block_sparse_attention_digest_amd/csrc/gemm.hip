@@ -29,11 +29,12 @@
 namespace sa {
 namespace {
 
-// waves per workgroup: one per SIMD of a CU; small workgroups also leave room on every CU
-// for an attention or selection workgroup running beside them.  The kernel is built for two
-// waves per SIMD (at most 256 registers a wave): with more, the compiler keeps values in the
-// accumulation registers and copies them inside the product loop.
-constexpr int kMaxWpg = 4;
+// waves per workgroup: up to five (the plan takes four unless told otherwise: one per SIMD
+// of a CU); small workgroups also leave room on every CU for an attention or selection
+// workgroup running beside them.  The kernel is built for two waves per SIMD (at most 256
+// registers a wave): with more, the compiler keeps values in the accumulation registers and
+// copies them inside the product loop.
+constexpr int kMaxWpg = 5;
 constexpr int kMaxTpw = 5;           // 16-column tiles per workgroup (and per wave)
 constexpr int kCUs = 256;
 
@@ -203,7 +204,7 @@ int row_tiles(int m) { return m >= 64 ? 4 : (m + 15) / 16; }
 
 }  // namespace
 
-GemmPlan gemm_plan(int m, int n_total, int k) {
+GemmPlan gemm_plan(int m, int n_total, int k, int max_waves) {
   const int tiles = n_total / 16;
   const int ksteps64 = k / 64;
   const int row_groups = (m + 63) / 64;
@@ -221,10 +222,10 @@ GemmPlan gemm_plan(int m, int n_total, int k) {
     ksplit = d;
     if ((long)groups * row_groups * d >= kCUs) break;
   }
-  // waves per workgroup: the most, up to kMaxWpg, that split the slice's k-steps evenly
+  // waves per workgroup: the most, up to max_waves, that split the slice's k-steps evenly
   const int steps = k / ksplit / 32;
   int kpw = 1;
-  for (int v = 2; v <= kMaxWpg; ++v)
+  for (int v = 2; v <= std::min(max_waves, kMaxWpg); ++v)
     if (steps % v == 0) kpw = v;
   GemmPlan p;
   p.ksplit = ksplit;

@@ -51,7 +51,8 @@ struct GemmPlan {
   int kpw;           // waves per workgroup, each streaming 1/kpw of the k-slice
   size_t ws_bytes;   // float partials [ksplit][m][n_total] when ksplit > 1
 };
-GemmPlan gemm_plan(int m, int n_total, int k);
+// max_waves: waves per workgroup at most (1..5)
+GemmPlan gemm_plan(int m, int n_total, int k, int max_waves = 4);
 // sum_slices: also launch the slice sum into q0 / q1 (when ksplit > 1).  Without it the
 // result of problem `prob` is left as gemm_result(...) describes, for a consumer to sum.
 hipError_t launch_gemm(int m, int n, int k, const void* x, int nprob, const void* w0,

@@ -461,6 +461,18 @@ def test_step_offload_parity_bs64():
                 gen_device="cpu", side=False, offload=True)
 
 
+def test_step_parity_five_wave_gemm():
+    """Blocks of 16 with a selection that streams more than the attention (125 blocks a pair
+    against a budget of 3): the step's GEMMs run five waves a workgroup, each over two of a
+    k-slice's ten k-steps (hidden 5120 in 16 slices); side stream and host hand-off."""
+    H.log("[case] step, five-wave GEMM")
+    import harness_step as HS
+    HS.run_step(wk.QWEN3_14B_STEP.scaled(batch=3, num_q_heads=10, num_kv_heads=2, context=2000,
+                                         layers=3, pool_blocks=6, hidden=5120, top_k=3,
+                                         block_size=16),
+                gen_device="cpu", handoff=True, side=True)
+
+
 def test_step_parity_minmax_no_handoff():
     H.log("[case] step minmax")
     import harness_step as HS
