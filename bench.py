@@ -103,6 +103,9 @@ def parse():
                     help="KV block size instead of the workload's 32, with the token budget "
                          "and the resident pool kept in tokens (a study of the digest "
                          "granularity; not the headline workload)")
+    ap.add_argument("--digest", choices=("mean", "minmax"), default="mean",
+                    help="digests of the 40-layer step: mean keys (the default) or Quest's "
+                         "per-channel min/max (the GPU step only)")
     ap.add_argument("--pool-blocks", type=int, default=None,
                     help="resident pool blocks per (sequence, KV head) instead of the "
                          "workload's 128 (a study of the CPU share; not the headline workload)")
@@ -139,7 +142,7 @@ def measured_traffic(wl, kind, kernel):
 # workload setup (untimed)
 # ---------------------------------------------------------------------------------------
 
-def setup(wl, torch, B, wk):
+def setup(wl, torch, B, wk, kind="mean"):
     dev = "cuda"
     L, Bsz, Hkv, Hq, d, k = (wl.layers, wl.batch, wl.num_kv_heads, wl.num_q_heads,
                              wl.head_dim, wl.top_k)
@@ -162,10 +165,10 @@ def setup(wl, torch, B, wk):
     t0 = time.time()
     for i in range(L):
         off = wk.layer_offsets(wl, i, dev)
-        dig = wk.draw_layer_digests(wl, i, off, dev)
+        dig = wk.draw_layer_digests(wl, i, off, dev, kind)
         w_packed = B.pack_weight(ins[i]["W"])  # once, at weight load
         B.sa_predict_query(ins[i]["X"], w_packed, q, gemm_ws)
-        B.sa_select_blocks(dims, "mean", q, dig, lens, kp, table_none, gb, ng, cb, nc, None,
+        B.sa_select_blocks(dims, kind, q, dig, lens, kp, table_none, gb, ng, cb, nc, None,
                            sel_ws)
         sets = [[None] * Hkv for _ in range(Bsz)]
         cbh = cb.cpu().numpy()
@@ -175,7 +178,7 @@ def setup(wl, torch, B, wk):
         k_pool = B.pack_k_pages(dims, pool["K"])  # K pages in the chunk-major layout
         v_pool = B.pack_v_pages(dims, pool["V"])  # V pages as [P][bs/16][d][16]
         del pool["K"], pool["V"]
-        B.sa_build_digests(dims, "mean", k_pool, pool["block_table"], lens, dig)
+        B.sa_build_digests(dims, kind, k_pool, pool["block_table"], lens, dig)
         hp = wk.draw_host_partials(wl, i, dev)
         del off
         layers.append(dict(
@@ -238,13 +241,15 @@ def spread(ms):
             "launches": len(v)}
 
 
-def step_bytes(wl, n_gpu_sums):
+def step_bytes(wl, n_gpu_sums, kind="mean"):
     """Algorithmic bytes of one whole step (every stage of every layer)."""
     Bsz, Hkv, Hq, d, k, L = (wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim,
                              wl.top_k, wl.layers)
     n, hid = Hq * d, wl.hidden
     gemm = lambda: n * hid * 2 + Bsz * hid * 2 + Bsz * n * 4
-    score = Bsz * Hkv * wl.max_blocks * d * 2 + Bsz * Hq * d * 4 + Bsz * Hkv * (2 * k + 2) * 4
+    per = 2 if kind == "minmax" else 1  # digest rows per block
+    score = (Bsz * Hkv * wl.max_blocks * per * d * 2 + Bsz * Hq * d * 4 +
+             Bsz * Hkv * (2 * k + 2) * 4)
     merge = 3 * Bsz * Hq * (d + 2) * 4
     total = 0
     for i in range(L):
@@ -258,7 +263,7 @@ def step_bytes(wl, n_gpu_sums):
 # CPU baseline: the oracle on a bounded sample of the same workload
 # ---------------------------------------------------------------------------------------
 
-def cpu_baseline(wl_full, budget_s):
+def cpu_baseline(wl_full, budget_s, kind="mean"):
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -273,12 +278,12 @@ def cpu_baseline(wl_full, budget_s):
     olayers_by_pair = {(0, h): [] for h in range(wl.num_kv_heads)}
     for i in range(wl.layers):
         off = wk.layer_offsets(wl, i, "cpu")
-        dig = wk.draw_layer_digests(wl, i, off, "cpu")
+        dig = wk.draw_layer_digests(wl, i, off, "cpu", kind)
         X64 = ins[i]["X"].float().numpy().astype(np.float64)
         W32 = ins[i]["W"].float().numpy()
         Q = so.query_heads(so.predict_query(X64, W32), wl.num_q_heads, d)
         dig64 = dig.float().numpy().astype(np.float64)
-        sets = [[so.select_topk(so.score_mean(Q[0, h * G:(h + 1) * G], dig64[0, h]),
+        sets = [[so.select_topk(so.score_blocks(Q[0, h * G:(h + 1) * G], dig64[0, h], kind),
                                 wl.pool_blocks) for h in range(wl.num_kv_heads)]]
         pool = wk.draw_layer_pool(wl, i, off, sets)
         hp = wk.draw_host_partials(wl, i, "cpu")
@@ -292,7 +297,9 @@ def cpu_baseline(wl_full, budget_s):
                 Vl[b * bs:(b + 1) * bs] = pool["V"][int(bt[b])].float().numpy()
             digh = dig64[0, h].copy()
             res_b = np.nonzero(resident)[0]
-            digh[res_b] = so.digest_mean(Kl, nb * bs, bs, "bf16")[res_b]
+            built = (so.digest_minmax(Kl, nb * bs, bs) if kind == "minmax"
+                     else so.digest_mean(Kl, nb * bs, bs, "bf16"))
+            digh[res_b] = built[res_b]
             host = [so.Partial(hp["o"][0, h * G + j].double().numpy(), float(hp["m"][0, h * G + j]),
                                float(hp["l"][0, h * G + j])) for j in range(G)]
             olayers_by_pair[(0, h)].append(dict(X=X64, W=W32, digest=digh, resident=resident,
@@ -303,7 +310,8 @@ def cpu_baseline(wl_full, budget_s):
         t0 = time.perf_counter()
         while True:
             for h in range(wl.num_kv_heads):
-                so.decode_step_pair(olayers_by_pair[(0, h)], 0, h, G, d, bs, wl.top_k, wl.scale)
+                so.decode_step_pair(olayers_by_pair[(0, h)], 0, h, G, d, bs, wl.top_k, wl.scale,
+                                    kind=kind)
             done += wl.layers
             el = time.perf_counter() - t0
             if el >= seconds:
@@ -327,7 +335,8 @@ def cpu_baseline(wl_full, budget_s):
             "one_thread": {"value": done1 / el1, "unit": "seq-layers/s", "cores": 1,
                            "sample": f"{done1} seq-layers in {el1:.1f} s"},
             "sample": f"{done} seq-layers: 1 sequence x {wl.layers} layers of the step "
-                      f"(all {wl.num_kv_heads} KV heads, Algorithm 1 end to end in float64), "
+                      f"(all {wl.num_kv_heads} KV heads, Algorithm 1 end to end in float64, "
+                      f"{kind} digests), "
                       f"repeated for {el:.1f} s; same shapes and recipe as the GPU workload"}
 
 
@@ -972,10 +981,14 @@ def main():
         bs0, bs1 = wl.block_size, args.block_size  # budget and pool kept in tokens
         wl = wl.scaled(block_size=bs1, top_k=wl.top_k * bs0 // bs1,
                        pool_blocks=wl.pool_blocks * bs0 // bs1)
-    log(f"workload {wl.name}: setup")
-    dims, lens, layers, ws = setup(wl, torch, B, wk)
+    kind = args.digest
+    if kind != "mean" and (args.offload or args.recall or args.drift_steps):
+        print("--digest minmax times the GPU step (and the single-layer workloads); the "
+              "offload, recall and drift studies run with mean digests", file=sys.stderr)
+        sys.exit(2)
+    log(f"workload {wl.name}: setup ({kind} digests)")
+    dims, lens, layers, ws = setup(wl, torch, B, wk, kind)
     side_stream = torch.cuda.Stream()
-    kind = "mean"
 
     def step():
         B.sa_decode_step(dims, kind, wl.hidden, wl.top_k, wl.scale, lens, layers, ws,
@@ -1068,7 +1081,7 @@ def main():
     iso_achieved = iso_bytes_avg / (iso_avg_ms * 1e-3) / 1e9
     log(f"attention alone: {iso_avg_ms * 1e3:.1f} us avg, {iso_achieved:.0f} GB/s")
     sel_alone = select_alone(wl, dims, lens, layers, kind, torch, B)
-    total_bytes = step_bytes(wl, n_gpu_sums)
+    total_bytes = step_bytes(wl, n_gpu_sums, kind)
     log(f"attention: {attn_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s algorithmic")
 
     traffic = measured_traffic(wl, kind, "attn_bf16_kernel")
@@ -1184,7 +1197,7 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, kind)
     print(json.dumps(result), flush=True)
 
 

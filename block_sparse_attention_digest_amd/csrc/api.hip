@@ -1054,13 +1054,14 @@ static sa_status step_impl(const sa_dims* dims, sa_digest_kind kind, int32_t hid
   if (!ws || ws_bytes < SL.total)
     return fail(SA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, SL.total);
   SA_ALIGNED16(ws);
-  // The GEMMs share the CUs with the selection and the attention.  Where the selection
-  // streams at least as many bytes per layer as the attention (its digests against the K and
-  // V of the selected blocks) it sets the step's pace, and five-wave GEMM workgroups leave it
-  // more room than four (measured on the 40-layer step: 5.24 against 5.55 ms with blocks of
-  // 16; with blocks of 32 and 64, where the attention streams more, four waves are 2-3 %
-  // faster).  The wave count does not change the workspace.
-  if ((long)s.max_blocks * (kind == SA_DIGEST_MINMAX ? 2 : 1) >= 2L * top_k * s.bs) {
+  // The GEMMs share the CUs with the selection and the attention.  Where the selection ranks
+  // 4096 blocks or more per (sequence, KV head) it sets the step's pace, and five-wave GEMM
+  // workgroups leave it more room than four.  Measured on the 40-layer step: blocks of 16
+  // (4096 a pair) 5.24 against 5.55 ms; blocks of 32 (2048 a pair) 4.29 against 4.42 ms
+  // with mean digests and 4.50 against 4.63-4.68 ms with min/max digests (which stream as
+  // many bytes as blocks of 16) in favour of four; blocks of 64, four.  The wave count does
+  // not change the workspace.
+  if (s.max_blocks >= 4096) {
     SL.plan_dual = sa::gemm_plan(s.B, 2 * s.Hq * s.d, hidden, 5);
     SL.plan_single = sa::gemm_plan(s.B, s.Hq * s.d, hidden, 5);
   }

@@ -278,13 +278,40 @@ def layer_offsets(wl: Workload, layer: int, device) -> torch.Tensor:
                    generator(wl, f"offset{layer}", device), device, std=wl.offset_std)
 
 
-def draw_layer_digests(wl: Workload, layer: int, offsets: torch.Tensor, device) -> torch.Tensor:
-    """Stand-in digests for blocks whose keys are never materialised: offset + N(0, 1/bs)
-    (the law of the mean of bs unit-normal keys around the offset), stored in the KV
-    dtype, [B][Hkv][max_blocks][d]."""
-    noise = _normal(tuple(offsets.shape), generator(wl, f"digest_noise{layer}", device),
-                    device, std=1.0 / math.sqrt(wl.block_size))
-    return (offsets + noise).to(wl.torch_kv_dtype)
+def _largest_normal_moments(n: int):
+    """Mean and standard deviation of the largest of n independent N(0, 1) draws, by
+    quadrature of its density n phi(x) Phi(x)^(n-1) over [-8, 8]."""
+    x = np.linspace(-8.0, 8.0, 16001)
+    phi = np.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+    cdf = 0.5 * (1.0 + np.array([math.erf(v / math.sqrt(2.0)) for v in x]))
+    pdf = n * phi * cdf ** (n - 1)
+    dx = x[1] - x[0]
+    mean = float(np.sum(x * pdf) * dx)
+    return mean, math.sqrt(float(np.sum((x - mean) ** 2 * pdf) * dx))
+
+
+def draw_layer_digests(wl: Workload, layer: int, offsets: torch.Tensor, device,
+                       kind: str = "mean") -> torch.Tensor:
+    """Stand-in digests for blocks whose keys are never materialised, stored in the KV dtype.
+
+    mean: offset + N(0, 1/bs), the law of the mean of bs unit-normal keys around the offset;
+    [B][Hkv][max_blocks][d].
+    minmax: [B][Hkv][max_blocks][2][d], [..][0] = offset - E1 and [..][1] = offset + E2,
+    where E1, E2 are drawn from the normal law with the mean and spread of the largest of bs
+    unit normals (the per-channel extremes of bs keys around the offset, taken apart)."""
+    if kind == "mean":
+        noise = _normal(tuple(offsets.shape), generator(wl, f"digest_noise{layer}", device),
+                        device, std=1.0 / math.sqrt(wl.block_size))
+        return (offsets + noise).to(wl.torch_kv_dtype)
+    if kind != "minmax":
+        raise ValueError(f"digest kind {kind!r}")
+    mean, sd = _largest_normal_moments(wl.block_size)
+    shape = tuple(offsets.shape)
+    lo = offsets - (_normal(shape, generator(wl, f"digest_lo{layer}", device), device, std=sd)
+                    + mean)
+    hi = offsets + (_normal(shape, generator(wl, f"digest_hi{layer}", device), device, std=sd)
+                    + mean)
+    return torch.stack([lo, hi], dim=3).to(wl.torch_kv_dtype)
 
 
 def draw_layer_pool(wl: Workload, layer: int, offsets: torch.Tensor, pool_sets) -> dict:

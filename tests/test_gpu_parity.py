@@ -462,14 +462,14 @@ def test_step_offload_parity_bs64():
 
 
 def test_step_parity_five_wave_gemm():
-    """Blocks of 16 with a selection that streams more than the attention (125 blocks a pair
-    against a budget of 3): the step's GEMMs run five waves a workgroup, each over two of a
-    k-slice's ten k-steps (hidden 5120 in 16 slices); side stream and host hand-off."""
+    """A selection over 4096 blocks a pair (64K tokens in blocks of 16): the step's GEMMs run
+    five waves a workgroup, each over two of a k-slice's ten k-steps (hidden 5120 in 16
+    slices); side stream and host hand-off.  One sequence, one KV head group, two layers."""
     H.log("[case] step, five-wave GEMM")
     import harness_step as HS
-    HS.run_step(wk.QWEN3_14B_STEP.scaled(batch=3, num_q_heads=10, num_kv_heads=2, context=2000,
-                                         layers=3, pool_blocks=6, hidden=5120, top_k=3,
-                                         block_size=16),
+    HS.run_step(wk.QWEN3_14B_STEP.scaled(batch=1, num_q_heads=10, num_kv_heads=2,
+                                         context=65536, layers=2, pool_blocks=6, hidden=5120,
+                                         top_k=3, block_size=16),
                 gen_device="cpu", handoff=True, side=True)
 
 

@@ -113,3 +113,33 @@ def test_step_pool_keys_carry_the_block_offsets():
     assert float((k.mean(0) - off[0, 1, 2]).abs().max()) < 5.0 / math.sqrt(32)
     hp = wk.draw_host_partials(wl, 0, "cpu")
     assert float(hp["l"].min()) >= 1.0 and float(hp["l"].max()) <= wl.block_size * wl.top_k
+
+
+def test_largest_normal_moments_match_closed_forms_and_sampling():
+    """The law the min/max stand-in digests draw from: the largest of n unit normals.  n = 1
+    is N(0, 1); n = 2 has mean 1/sqrt(pi) and variance 1 - 1/pi; n = 32 against a seeded
+    sample of 200,000 maxima."""
+    m1, s1 = wk._largest_normal_moments(1)
+    assert abs(m1) < 1e-9 and abs(s1 - 1.0) < 1e-6
+    m2, s2 = wk._largest_normal_moments(2)
+    assert abs(m2 - 1.0 / math.sqrt(math.pi)) < 1e-6
+    assert abs(s2 - math.sqrt(1.0 - 1.0 / math.pi)) < 1e-6
+    m32, s32 = wk._largest_normal_moments(32)
+    mx = np.random.default_rng(5).standard_normal((200_000, 32)).max(axis=1)
+    assert abs(m32 - mx.mean()) < 0.01 and abs(s32 - mx.std()) < 0.01
+
+
+def test_minmax_stand_in_digests_bracket_the_offsets():
+    """min/max stand-ins: [B][Hkv][max_blocks][2][d] in the KV dtype, minimum below the block's
+    offset and maximum above it, each about E[max of bs unit normals] away."""
+    wl = wk.QWEN3_14B_STEP.scaled(batch=2, num_q_heads=10, num_kv_heads=2, context=4096,
+                                  layers=2, pool_blocks=4, hidden=256)
+    off = wk.layer_offsets(wl, 1, "cpu")
+    dig = wk.draw_layer_digests(wl, 1, off, "cpu", "minmax")
+    assert dig.dtype == torch.bfloat16 and dig.shape == (2, 2, 128, 2, 128)
+    lo, hi = dig[..., 0, :].float(), dig[..., 1, :].float()
+    assert bool((lo < hi).all())
+    mean, _ = wk._largest_normal_moments(wl.block_size)
+    assert abs(float((hi - off).mean()) - mean) < 0.02
+    assert abs(float((off - lo).mean()) - mean) < 0.02
+    assert torch.equal(dig, wk.draw_layer_digests(wl, 1, off, "cpu", "minmax"))
