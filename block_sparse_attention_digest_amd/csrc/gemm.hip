@@ -16,9 +16,9 @@
 // block (its slice's float32 partial) as whole rows of float4.  The partials are summed in
 // slice order -- by a second kernel in the stand-alone call, by the kernels that read the
 // query in the decode step -- so results are deterministic.  The plan sizes the grid to
-// about one workgroup of four waves per CU, so the whole product is one round of
-// short-lived waves, one per SIMD.  Two weight matrices that share x (Q^i and
-// Q_pred^{i+1}) can run as one launch.
+// about one workgroup per CU, of four waves (one per SIMD) unless the caller asks for up to
+// five, so the whole product is one round of short-lived waves.  Two weight matrices that
+// share x (Q^i and Q_pred^{i+1}) can run as one launch.
 #include <hip/hip_ext.h>
 
 #include <algorithm>
