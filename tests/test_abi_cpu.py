@@ -175,6 +175,31 @@ def test_gemm_validation(lib):
 
 
 @no_gpu
+def test_gemm_split_plan(lib):
+    """The GEMM's k-split, seen through its workspace (ksplit float32 partials of m x n): the
+    fewest equal slices (a divisor of k / 64, at most 16) that give about one workgroup per
+    CU, with 5 column tiles of 16 a workgroup where they divide the tiles, else 4."""
+    def ws(m, n, k):
+        return lib.sa_predict_query_workspace_bytes(m, n, k)
+    # 320 tiles -> 64 groups of 5: 4 slices fill 256 CUs
+    assert ws(40, 5120, 5120) == 4 * 40 * 5120 * 4
+    # 64 rows still one row group of 64
+    assert ws(64, 5120, 5120) == 4 * 64 * 5120 * 4
+    # 256 tiles -> 64 groups of 4
+    assert ws(8, 4096, 4096) == 4 * 8 * 4096 * 4
+    # 40 tiles -> 8 groups of 5, 4 row groups of 64: 8 slices
+    assert ws(256, 640, 2560) == 8 * 256 * 640 * 4
+    # 12 tiles -> 3 groups of 4: 16 slices at most (k / 64 = 128 has the divisor 16)
+    assert ws(17, 192, 8192) == 16 * 17 * 192 * 4
+    # k / 64 = 5: the divisors are 1 and 5
+    assert ws(3, 960, 320) == 5 * 3 * 960 * 4
+    # 1024 tiles -> 256 groups of 4: one slice, no partials
+    assert ws(8, 16384, 4096) == 0
+    # k / 64 = 1: nothing to split
+    assert ws(1, 64, 64) == 0
+
+
+@no_gpu
 def test_alignment_validation(lib):
     """Buffers the kernels move with 16-byte accesses are refused on the host when they are
     not 16-byte aligned (the rest of each call's arguments valid)."""
