@@ -58,6 +58,17 @@ def test_step_fullsize():
     assert 0.0 < r["cpu_ratio"] < 0.5
 
 
+def test_step_fullsize_bs16():
+    """The benchmark's step with blocks of 16 tokens, budget and pool kept in tokens (k = 128,
+    a pool of 256 blocks, as bench.py --block-size 16): the selection ranks 4096 blocks a
+    pair, so the step's GEMMs run five waves a workgroup; four layers, sampled pairs."""
+    wl = wk.QWEN3_14B_STEP.scaled(block_size=16, top_k=128, pool_blocks=256, layers=4)
+    H.log(f"[case] full size step {wl.name} bs16")
+    import harness_step as HS
+    r = HS.run_step(wl, gen_device="cuda", handoff=True, pairs_to_check=sample_pairs(wl, 4, 7))
+    assert 0.0 < r["cpu_ratio"] < 0.5
+
+
 def test_step_offload_fullsize():
     """The benchmark's step with its CPU side computed by host tasks one layer ahead, from an
     aliased host store (as bench.py --offload), sampled pairs through every layer: the query
