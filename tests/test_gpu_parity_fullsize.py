@@ -69,6 +69,18 @@ def test_step_fullsize_bs16():
     assert 0.0 < r["cpu_ratio"] < 0.5
 
 
+def test_step_fullsize_minmax():
+    """The benchmark's step shape with min/max digests (as bench.py --digest minmax), side
+    stream and host hand-off; four layers, sampled pairs.  The pool holds 48 blocks, fewer
+    than the budget of 64, so every pair offloads and the host mirrors carry real lists."""
+    wl = wk.QWEN3_14B_STEP.scaled(layers=4, pool_blocks=48, digest_kinds=("minmax",))
+    H.log(f"[case] full size step {wl.name} minmax")
+    import harness_step as HS
+    r = HS.run_step(wl, gen_device="cuda", handoff=True, kind="minmax",
+                    pairs_to_check=sample_pairs(wl, 4, 13))
+    assert 0.0 < r["cpu_ratio"] < 1.0
+
+
 def test_step_offload_fullsize():
     """The benchmark's step with its CPU side computed by host tasks one layer ahead, from an
     aliased host store (as bench.py --offload), sampled pairs through every layer: the query
