@@ -54,6 +54,10 @@ LAYER_CASES = [
     ("f32-d128-bs32", wk.TINY.scaled(num_q_heads=10, num_kv_heads=2, head_dim=128,
                                      block_size=32, context=1000, top_k=6), "minmax", {}),
     ("bf16-short-seqs", wk.RAGGED.scaled(batch=5, ctx_min=1, ctx_max=40, top_k=3), "mean", {}),
+    # few resident blocks (5-10 % of each selection): many more attention waves than blocks,
+    # so waves with empty ranges, and reduce slots of covering waves that wrote nothing
+    ("bf16-few-resident", wk.RAGGED.scaled(batch=4, ctx_min=2000, ctx_max=4000, top_k=64,
+                                           resident_frac=(0.05, 0.1)), "mean", {}),
     # more than 512 (sequence, KV head) pairs: attention's workgroup-wide prefix scan, and
     # workgroup ranges that cross more pairs than it stages queries for
     ("bf16-many-pairs", wk.RAGGED.scaled(batch=72, ctx_min=1, ctx_max=300, top_k=4), "mean", {}),
